@@ -1,0 +1,39 @@
+"""CPU oracle for speculative verify-and-accept and the P-EAGLE draft batch.
+
+TEST INFRASTRUCTURE ONLY.  Plain, slow, fp64 numpy, one sequence at a time.
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it; the product path (``draft_verification_vocab_amd``
+and its HIP library) never does, and this package imports nothing from it.
+
+What each function follows (the pages cited are the three source pages:
+"Project 14 - speculative decoding inference server" (ai-engineering.com.cn),
+the P-EAGLE / TorchSpec blog summary (blog.hotdry.top), and the rskf.cn survey
+of Eagle / MTP / DFlash / DSPark):
+
+* ``verify.target_distribution``  softmax of a logit row at temperature T.
+  Pinned by closed forms and scipy (tests/test_oracle_softmax.py).
+* ``verify.verify_greedy``        argmax-match prefix, then the target argmax.
+  Pinned by the argmax-chain property and brute force.
+* ``verify.verify_sample``        p/q acceptance, first-rejection prefix,
+  residual max(0, p - q) resample or bonus draw from p.  Pinned by exact
+  enumeration of the output law on tiny vocabularies, chi-square and binomial
+  tests, closed forms for the acceptance rate and mean accepted length, and
+  special cases (q = p, q one-hot on a zero of p, disjoint supports).
+* ``peagle.build_draft_batch``    the P-EAGLE drafter batch.  Pinned by the
+  invariants the P-EAGLE summary fixes (K-1 MASK rows per sequence, slot -1
+  exactly on rejected tokens, h_shared on the MASK rows, the new token paired
+  with h_context) and by brute-force checks of the slot formula.  The row
+  order inside a sequence (accepted, NTP, MASK, rejected) is a reading the
+  pages leave open: that ordering is parity unpinned by the pages.
+"""
+from . import peagle, verify  # noqa: F401
+from .peagle import PADDING_SLOT_ID, build_draft_batch  # noqa: F401
+from .verify import (  # noqa: F401
+    decode_logits,
+    first_argmax,
+    sample_outcomes,
+    target_distribution,
+    verify_greedy,
+    verify_sample,
+    verify_sample_seq,
+)
