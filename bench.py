@@ -1,0 +1,264 @@
+"""Benchmark: one decode round's verify + P-EAGLE batch build on one MI355X.
+
+A step is one pass of the whole path over one batch: spec_verify_sample on
+B=1024 sequences with K=7 drafts over a V=151936 bf16 vocabulary (logits
+2.49 GB, draft probabilities 4.36 GB, both resident in HBM), then
+peagle_build_draft_batch (H=2048 bf16) fed by the verify outputs on the same
+stream.  The greedy variant of the same step is timed too and reported in
+"greedy_step".
+
+Prints one JSON line.  `value` is verified logit rows per second, B*(K+1)
+rows per step.  `roofline` covers the dominant kernel (the sampled verify),
+timed with HIP events on the stream it runs on; `cpu_baseline` times the
+fp64 CPU oracle on the host over as much of the same batch as fits a time
+budget.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_verify_sample_fused_b1024.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--no-greedy", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run only this many untimed steps (for rocprofv3) and exit")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources the timed kernels are built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "draft_verification_vocab_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def verify_bytes(B, K, V, zsize, acc, sample=True):
+    """Algorithmic HBM bytes of a verify call, split as (row kernel, draw kernel).
+
+    Row kernel: every logit row once, the draft tokens, the outputs, and for
+    sampling the q(d) / z(d) gathers, the test uniforms and p_k(d_k).  Draw
+    kernel (sampling): the drafter's row a_b of each sequence that rejects a
+    draft and the final uniforms; reading logit row a again is not counted."""
+    n = B * (K + 1) * V * zsize                      # logits, every row once
+    n += B * K * 4                                   # draft tokens
+    n += B * (K + 1) * 4 + B * 4                     # out_tokens, num_accepted
+    if not sample:
+        return n, 0
+    n += B * K * 4 * 2                               # q(d) and z(d) gathers
+    n += B * K * 4                                   # uniforms of the tests
+    n += B * K * 4                                   # p_k(d_k) output
+    draw = int((acc < K).sum()) * V * 4 + B * 4      # q row a_b of rejecting sequences, u[:, K]
+    return n, draw
+
+
+def build_bytes(B, K, H, hsize):
+    """Algorithmic HBM bytes of one build launch: every verify hidden row read
+    once, h_shared, the 2K output rows per sequence and their metadata."""
+    n = B * (K + 1) * H * hsize + H * hsize + B * 2 * K * H * hsize
+    n += B * ((K + 1) * 4 + 4 + K * 4 + 8 + 8)      # verify outputs, draft tokens, L, table reads
+    n += B * 2 * K * (4 + 8 + 8) + B * K * 4         # ids, positions, slots, sample rows
+    return n
+
+
+def cpu_baseline(vi, bi, budget_s):
+    """The oracle as it stands, one thread, over the batch until the budget runs out."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    K = vi.spec.K
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        done = _oracle_loop(oracle, np, vi, bi, K, t0, budget_s)
+        dt = time.perf_counter() - t0
+    rows = done * (K + 1)
+    return {"value": rows / dt, "unit": "verified logit rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {vi.spec.B} sequences of the same batch "
+                      f"(sampled verify + P-EAGLE build per sequence, fp64 numpy), {dt:.1f} s"}
+
+
+def _oracle_loop(oracle, np, vi, bi, K, t0, budget_s):
+    done = 0
+    for b in range(vi.spec.B):
+        z = oracle.decode_logits(vi.logits[b], "bf16")
+        tr = oracle.verify_sample_seq(z, vi.draft_probs[b], vi.draft_tokens[b], vi.uniforms[b],
+                                      vi.temperature)
+        oracle.build_draft_batch(tr.out_tokens[None], np.array([tr.a], np.int32),
+                                 vi.draft_tokens[b:b + 1], bi.start_pos[b:b + 1],
+                                 bi.block_table[b:b + 1], bi.spec.block_size,
+                                 bi.target_hidden[b * (K + 1):(b + 1) * (K + 1)], bi.h_shared,
+                                 bi.mask_token_id)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    return done
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import synth
+
+    # inputs are drawn before anything touches the GPU
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+    log("drawing inputs")
+    vi, bi = synth.make_fused_inputs()
+    log("inputs ready; uploading")
+    B, K, V = vi.spec.B, vi.spec.K, vi.spec.V
+    H = bi.spec.H
+
+    import torch
+    import draft_verification_vocab_amd as sv
+    sv.require_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    z, q, d, u = up(vi.logits), up(vi.draft_probs), up(vi.draft_tokens), up(vi.uniforms)
+    L, bt, hid, hs = up(bi.start_pos), up(bi.block_table), up(bi.target_hidden), up(bi.h_shared)
+    out_t = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    acc_t = torch.empty(B, dtype=torch.int32, device=dev)
+    pd_t = torch.empty((B, K), dtype=torch.float32, device=dev)
+    ws = torch.zeros(sv.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    bouts = {"input_ids": torch.empty(B * 2 * K, dtype=torch.int32, device=dev),
+             "positions": torch.empty(B * 2 * K, dtype=torch.int64, device=dev),
+             "slot_mapping": torch.empty(B * 2 * K, dtype=torch.int64, device=dev),
+             "hidden": torch.empty((B * 2 * K, H), dtype=torch.bfloat16, device=dev),
+             "sample_rows": torch.empty((B, K), dtype=torch.int32, device=dev)}
+
+    def step(sample=True):
+        if sample:
+            sv.spec_verify_sample(z, q, d, u, vi.temperature, out_tokens=out_t,
+                                  out_num_accepted=acc_t, out_draft_target_prob=pd_t, workspace=ws)
+        else:
+            sv.spec_verify_greedy(z, d, out_tokens=out_t, out_num_accepted=acc_t, workspace=ws)
+
+    def build():
+        sv.peagle_build_draft_batch(out_t, acc_t, d, L, bt, bi.spec.block_size, hid, hs,
+                                    bi.mask_token_id, outputs=bouts)
+
+    if args.profile_steps:
+        for i in range(args.profile_steps):
+            step(True); build(); step(False); build()
+        torch.cuda.synchronize()
+        print(f"profiled {args.profile_steps} sampled and greedy steps", flush=True)
+        return
+
+    def timed(sample):
+        for _ in range(args.warmup):
+            step(sample); build()
+        torch.cuda.synchronize()
+        sv.trace_begin(3 * args.steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(sample)
+            build()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = {}
+        for name, ms in sv.trace_read():
+            per.setdefault(name, []).append(ms)
+        sv.trace_end()
+        acc = acc_t.cpu().numpy()
+        return wall / args.steps, {k: float(np.mean(v)) for k, v in per.items()}, acc
+
+    sec_sample, kms, acc = timed(True)
+    vb_rows, vb_draw = verify_bytes(B, K, V, 2, acc, sample=True)
+    bb = build_bytes(B, K, H, 2)
+    rows = B * (K + 1)
+
+    def kinfo(name, nbytes, note=None):
+        ms = kms[name]
+        d = {"avg_ms": ms, "algorithmic_bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+             "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if note:
+            d["note"] = note
+        return d
+
+    res = {
+        "metric": "verified logit rows/sec and achieved HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": rows / sec_sample,
+        "unit": "verified logit rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": sec_sample * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "fused high-concurrency step: sampled verify B=1024 K=7 "
+                               "V=151936 bf16 logits T=0.7 + P-EAGLE build H=2048 bf16",
+                   "B": B, "K": K, "V": V, "H": H, "logits": "bf16", "draft_probs": "f32",
+                   "temperature": vi.temperature, "mode": "sample"},
+        "step_hbm_gbs": (vb_rows + vb_draw + bb) / sec_sample / 1e9,
+        "step_hbm_frac": (vb_rows + vb_draw + bb) / sec_sample / 1e9 / HBM_PEAK_GBS,
+        "step_bytes": vb_rows + vb_draw + bb,
+        "kernels": {
+            "verify_sample_rows": kinfo("verify_sample_rows", vb_rows),
+            "verify_sample_draw": kinfo("verify_sample_draw", vb_draw,
+                                        "algorithmic bytes count the drafter rows only; the "
+                                        "kernel also re-reads logit row a"),
+            "peagle_build": kinfo("peagle_build", bb),
+        },
+        "acceptance": {"mean_accepted": float(acc.mean()),
+                       "rate": float(acc.sum() / np.minimum(acc + 1, K).sum())},
+    }
+    rk = res["kernels"]["verify_sample_rows"]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == kernel_source_hash():
+            traffic = tr.get("hbm_bytes_per_launch")
+    res["roofline"] = {"bound": "hbm", "achieved": rk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": rk["frac"], "traffic": traffic, "kernel": "verify_sample_rows",
+                       "algorithmic_bytes": vb_rows, "avg_ms": rk["avg_ms"]}
+    log("sampled step timed")
+    if not args.no_greedy:
+        sec_g, kmsg, accg = timed(False)
+        vbg, _ = verify_bytes(B, K, V, 2, accg, sample=False)
+        g_ms = kmsg["verify_greedy"]
+        res["greedy_step"] = {"value": rows / sec_g, "unit": "verified logit rows/s",
+                              "ms_per_step": sec_g * 1e3,
+                              "verify_greedy": {"avg_ms": g_ms, "algorithmic_bytes": vbg,
+                                                "gbs": vbg / (g_ms * 1e-3) / 1e9,
+                                                "frac": vbg / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                              "peagle_build_ms": kmsg["peagle_build"],
+                              "step_hbm_gbs": (vbg + bb) / sec_g / 1e9,
+                              "step_hbm_frac": (vbg + bb) / sec_g / 1e9 / HBM_PEAK_GBS}
+    if args.cpu_budget > 0:
+        log("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(vi, bi, args.cpu_budget)
+    res["kernel_source_hash"] = kernel_source_hash()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,297 @@
+"""Speculative verify-and-accept and the P-EAGLE draft batch on MI355X.
+
+Thin Python binding over ``libspecverify.so`` (C ABI in include/spec_verify.h).
+The functions here only marshal arguments: they check tensor shapes, dtypes
+and devices, allocate outputs with torch when the caller passes none, and call
+the library on the current HIP stream.  All computation runs in the library's
+HIP kernels; there is no other implementation to fall back to, and every call
+raises if the library is missing or returns an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "require_library", "library_path", "sv_status_string", "spec_verify_workspace_bytes",
+    "spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
+    "SpecVerifyError", "SV_F32", "SV_BF16", "SV_F16", "PADDING_SLOT_ID",
+    "trace_begin", "trace_read", "trace_end",
+    "DEVERR_DRAFT_TOKEN", "DEVERR_ACCEPT_COUNT", "DEVERR_BLOCK_TABLE",
+]
+
+SV_F32, SV_BF16, SV_F16 = 0, 1, 2
+PADDING_SLOT_ID = -1
+DEVERR_DRAFT_TOKEN, DEVERR_ACCEPT_COUNT, DEVERR_BLOCK_TABLE = 1, 2, 4
+MAX_K = 63
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+_lib = None
+_lock = threading.Lock()
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_SIGS = {
+    "sv_status_string": (ctypes.c_char_p, [_i]),
+    "spec_verify_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
+    "spec_verify_greedy": (_i, [_p, _i, _p, _i, _i, _i, _p, _p, _p, ctypes.c_size_t, _p, _p]),
+    "spec_verify_sample": (_i, [_p, _i, _p, _p, _p, ctypes.c_float, _i, _i, _i, _p, _p, _p, _p,
+                                ctypes.c_size_t, _p, _p]),
+    "peagle_build_draft_batch": (_i, [_p, _p, _p, _p, _p, _i, _i, _p, _p, _i, ctypes.c_int32,
+                                      _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
+    "sv_kernel_name": (ctypes.c_char_p, [_i]),
+    "sv_trace_begin": (_i, [_i]),
+    "sv_trace_count": (_i, []),
+    "sv_trace_read": (_i, [_i, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)]),
+    "sv_trace_end": (None, []),
+}
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def require_library():
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise SpecVerifyError(
+                    f"{_LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+            lib = ctypes.CDLL(_LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def sv_status_string(status: int) -> str:
+    return require_library().sv_status_string(status).decode()
+
+
+def spec_verify_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(require_library().spec_verify_workspace_bytes(B, K, V))
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise SpecVerifyError(f"{what}: {sv_status_string(status)} (status {status})")
+
+
+# ---------------------------------------------------------------- tracing
+def trace_begin(capacity: int):
+    """Start kernel tracing on this host thread for up to `capacity` launches."""
+    _check(require_library().sv_trace_begin(int(capacity)), "sv_trace_begin")
+
+
+def trace_read():
+    """[(kernel name, duration ms)] of the launches traced so far (waits for them)."""
+    lib = require_library()
+    out = []
+    kid, ms = ctypes.c_int(), ctypes.c_float()
+    for i in range(lib.sv_trace_count()):
+        _check(lib.sv_trace_read(i, ctypes.byref(kid), ctypes.byref(ms)), "sv_trace_read")
+        out.append((lib.sv_kernel_name(kid.value).decode(), float(ms.value)))
+    return out
+
+
+def trace_end():
+    require_library().sv_trace_end()
+
+
+# ---------------------------------------------------------------- helpers
+_DTYPES = {torch.float32: SV_F32, torch.bfloat16: SV_BF16, torch.float16: SV_F16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_ws_cache = {}
+
+
+def _workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-filled workspace per device.  The kernels leave it zero-filled,
+    so it is reused without clearing; calls on one device must share a stream."""
+    key = (device.type, device.index)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------- verify
+def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                       out_tokens: Optional[torch.Tensor] = None,
+                       out_num_accepted: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       device_error: Optional[torch.Tensor] = None):
+    """Greedy verify; see spec_verify_greedy in include/spec_verify.h.
+
+    target_logits [B, K+1, V] float32/bfloat16, draft_tokens [B, K] int32.
+    Returns (out_tokens [B, K+1] int32, num_accepted [B] int32).
+    """
+    lib = require_library()
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    _dev(target_logits, "target_logits")
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("target_logits must be float32 or bfloat16")
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if out_tokens is None \
+        else _dev(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+    out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev) if out_num_accepted is None \
+        else _dev(out_num_accepted, "out_num_accepted", torch.int32, (B,), dev)
+    need = spec_verify_workspace_bytes(B, K, V)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    _dev(workspace, "workspace", device=dev)
+    if device_error is not None:
+        _dev(device_error, "device_error", torch.int32, (1,), dev)
+    st = lib.spec_verify_greedy(_ptr(target_logits), _DTYPES[target_logits.dtype], _ptr(draft_tokens),
+                                B, K, V, _ptr(out_tokens), _ptr(out_num_accepted), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _ptr(device_error),
+                                _stream(dev))
+    _check(st, "spec_verify_greedy")
+    return out_tokens, out_num_accepted
+
+
+def spec_verify_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor,
+                       draft_tokens: torch.Tensor, uniforms: torch.Tensor, temperature: float,
+                       out_tokens: Optional[torch.Tensor] = None,
+                       out_num_accepted: Optional[torch.Tensor] = None,
+                       out_draft_target_prob: Optional[torch.Tensor] = None,
+                       want_draft_target_prob: bool = False,
+                       workspace: Optional[torch.Tensor] = None,
+                       device_error: Optional[torch.Tensor] = None):
+    """Rejection-sampling verify; see spec_verify_sample in include/spec_verify.h.
+
+    Returns (out_tokens, num_accepted, draft_target_prob or None).
+    """
+    lib = require_library()
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    _dev(target_logits, "target_logits")
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("target_logits must be float32 or bfloat16")
+    _dev(draft_probs, "draft_probs", torch.float32, (B, K, V), dev)
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _dev(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if out_tokens is None \
+        else _dev(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+    out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev) if out_num_accepted is None \
+        else _dev(out_num_accepted, "out_num_accepted", torch.int32, (B,), dev)
+    if out_draft_target_prob is None and want_draft_target_prob:
+        out_draft_target_prob = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if out_draft_target_prob is not None:
+        _dev(out_draft_target_prob, "out_draft_target_prob", torch.float32, (B, K), dev)
+    need = spec_verify_workspace_bytes(B, K, V)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    _dev(workspace, "workspace", device=dev)
+    if device_error is not None:
+        _dev(device_error, "device_error", torch.int32, (1,), dev)
+    st = lib.spec_verify_sample(_ptr(target_logits), _DTYPES[target_logits.dtype], _ptr(draft_probs),
+                                _ptr(draft_tokens), _ptr(uniforms), float(temperature), B, K, V,
+                                _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_draft_target_prob),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _ptr(device_error), _stream(dev))
+    _check(st, "spec_verify_sample")
+    return out_tokens, out_num_accepted, out_draft_target_prob
+
+
+# ---------------------------------------------------------------- P-EAGLE
+def peagle_build_draft_batch(verify_out_tokens: torch.Tensor, num_accepted: torch.Tensor,
+                             draft_tokens: torch.Tensor, start_pos: torch.Tensor,
+                             block_table: torch.Tensor, block_size: int,
+                             target_hidden: torch.Tensor, h_shared: torch.Tensor,
+                             mask_token_id: int, outputs: Optional[dict] = None,
+                             want_sample_rows: bool = True,
+                             device_error: Optional[torch.Tensor] = None) -> dict:
+    """P-EAGLE drafter batch; see peagle_build_draft_batch in include/spec_verify.h.
+
+    Returns a dict of input_ids [B*2K] int32, positions [B*2K] int64,
+    slot_mapping [B*2K] int64, hidden [B*2K, H], sample_rows [B, K] int32.
+    """
+    lib = require_library()
+    B, K = draft_tokens.shape
+    dev = draft_tokens.device
+    H = target_hidden.shape[-1]
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _dev(verify_out_tokens, "verify_out_tokens", torch.int32, (B, K + 1), dev)
+    _dev(num_accepted, "num_accepted", torch.int32, (B,), dev)
+    _dev(start_pos, "start_pos", torch.int64, (B,), dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    _dev(block_table, "block_table", torch.int32, device=dev)
+    if target_hidden.dtype not in _DTYPES:
+        raise TypeError("hidden states must be bfloat16, float16 or float32")
+    _dev(target_hidden, "target_hidden", shape=(B * (K + 1), H), device=dev)
+    _dev(h_shared, "h_shared", target_hidden.dtype, (H,), dev)
+    o = dict(outputs or {})
+    n = B * 2 * K
+    if "input_ids" not in o:
+        o["input_ids"] = torch.empty(n, dtype=torch.int32, device=dev)
+    if "positions" not in o:
+        o["positions"] = torch.empty(n, dtype=torch.int64, device=dev)
+    if "slot_mapping" not in o:
+        o["slot_mapping"] = torch.empty(n, dtype=torch.int64, device=dev)
+    if "hidden" not in o:
+        o["hidden"] = torch.empty((n, H), dtype=target_hidden.dtype, device=dev)
+    if "sample_rows" not in o and want_sample_rows:
+        o["sample_rows"] = torch.empty((B, K), dtype=torch.int32, device=dev)
+    _dev(o["input_ids"], "input_ids", torch.int32, (n,), dev)
+    _dev(o["positions"], "positions", torch.int64, (n,), dev)
+    _dev(o["slot_mapping"], "slot_mapping", torch.int64, (n,), dev)
+    _dev(o["hidden"], "hidden", target_hidden.dtype, (n, H), dev)
+    if o.get("sample_rows") is not None:
+        _dev(o["sample_rows"], "sample_rows", torch.int32, (B, K), dev)
+    if device_error is not None:
+        _dev(device_error, "device_error", torch.int32, (1,), dev)
+    st = lib.peagle_build_draft_batch(
+        _ptr(verify_out_tokens), _ptr(num_accepted), _ptr(draft_tokens), _ptr(start_pos),
+        _ptr(block_table), block_table.shape[1], int(block_size), _ptr(target_hidden), _ptr(h_shared),
+        _DTYPES[target_hidden.dtype], int(mask_token_id), B, K, H, _ptr(o["input_ids"]),
+        _ptr(o["positions"]), _ptr(o["slot_mapping"]), _ptr(o["hidden"]), _ptr(o.get("sample_rows")),
+        _ptr(device_error), _stream(dev))
+    _check(st, "peagle_build_draft_batch")
+    return o

@@ -1,0 +1,241 @@
+// C ABI of libspecverify: host-side validation, then the call's kernel
+// launches.  Nothing here reads device memory or synchronises (except
+// sv_trace_read, which waits for the traced launch it reports); on any
+// validation error a call returns before touching the GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+// ---------------------------------------------------------------- tracing
+namespace {
+struct Tracer {
+  bool on = false;
+  int cap = 0, count = 0;
+  std::vector<hipEvent_t> ev;     // 2 per traced launch
+  std::vector<int> ids;
+  void destroy() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    ev.clear();
+    ids.clear();
+    on = false;
+    cap = count = 0;
+  }
+  ~Tracer() { destroy(); }
+};
+thread_local Tracer tracer;
+}  // namespace
+
+void trace_before(hipStream_t stream) {
+  if (tracer.on && tracer.count < tracer.cap)
+    (void)hipEventRecord(tracer.ev[2 * tracer.count], stream);
+}
+
+void trace_after(hipStream_t stream, int kernel_id) {
+  if (tracer.on && tracer.count < tracer.cap) {
+    (void)hipEventRecord(tracer.ev[2 * tracer.count + 1], stream);
+    tracer.ids[tracer.count++] = kernel_id;
+  }
+}
+
+}  // namespace sv
+
+namespace {
+
+inline bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+constexpr long kMaxB = 1L << 20;   // sequences per call
+
+sv_status check_verify_shape(int B, int K, int V) {
+  if (B < 0 || B > kMaxB || K < 0 || K > SV_MAX_K || V < 1 || V > SV_MAX_V) return SV_ERR_SHAPE;
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+SV_API const char* sv_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_NULL: return "a required pointer is NULL";
+    case SV_ERR_SHAPE: return "shape argument out of range";
+    case SV_ERR_DTYPE: return "unsupported dtype";
+    case SV_ERR_VALUE: return "scalar argument out of range";
+    case SV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SV_ERR_ALIGN: return "pointer not aligned to its element size";
+    case SV_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+SV_API const char* sv_kernel_name(int kernel_id) {
+  switch (kernel_id) {
+    case SV_KERNEL_VERIFY_GREEDY: return "verify_greedy";
+    case SV_KERNEL_VERIFY_SAMPLE_ROWS: return "verify_sample_rows";
+    case SV_KERNEL_VERIFY_SAMPLE_DRAW: return "verify_sample_draw";
+    case SV_KERNEL_PEAGLE_BUILD: return "peagle_build";
+    default: return "unknown";
+  }
+}
+
+SV_API sv_status sv_trace_begin(int capacity) {
+  if (capacity < 1) return SV_ERR_VALUE;
+  sv::tracer.destroy();
+  sv::tracer.ev.resize(2 * (size_t)capacity);
+  for (auto& e : sv::tracer.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      sv::tracer.destroy();
+      return SV_ERR_HIP;
+    }
+  }
+  sv::tracer.ids.assign(capacity, -1);
+  sv::tracer.cap = capacity;
+  sv::tracer.count = 0;
+  sv::tracer.on = true;
+  return SV_OK;
+}
+
+SV_API int sv_trace_count(void) { return sv::tracer.count; }
+
+SV_API sv_status sv_trace_read(int i, int* kernel_id, float* ms) {
+  if (!kernel_id || !ms) return SV_ERR_NULL;
+  if (i < 0 || i >= sv::tracer.count) return SV_ERR_VALUE;
+  hipEvent_t e0 = sv::tracer.ev[2 * i], e1 = sv::tracer.ev[2 * i + 1];
+  if (hipEventSynchronize(e1) != hipSuccess) return SV_ERR_HIP;
+  if (hipEventElapsedTime(ms, e0, e1) != hipSuccess) return SV_ERR_HIP;
+  *kernel_id = sv::tracer.ids[i];
+  return SV_OK;
+}
+
+SV_API void sv_trace_end(void) { sv::tracer.destroy(); }
+
+SV_API size_t spec_verify_workspace_bytes(int B, int K, int V) {
+  if (check_verify_shape(B, K, V) != SV_OK) return 0;
+  if (B == 0) return 0;
+  return sv::verify_workspace_bytes(B, K, V);
+}
+
+static sv_status verify_common(const void* logits, int dtype, const float* draft_probs,
+                               const int32_t* draft_tokens, const float* uniforms,
+                               float temperature, int sample, int B, int K, int V,
+                               int32_t* out_tokens, int32_t* out_num_accepted, float* out_p_draft,
+                               void* workspace, size_t workspace_bytes, int32_t* device_error,
+                               void* stream) {
+  sv_status st = check_verify_shape(B, K, V);
+  if (st != SV_OK) return st;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (sample && !(temperature > 0.0f && isfinite(temperature))) return SV_ERR_VALUE;
+  if (B == 0) return SV_OK;
+  if (!logits || !out_tokens || !out_num_accepted || (K > 0 && !draft_tokens)) return SV_ERR_NULL;
+  if (sample && (!uniforms || (K > 0 && !draft_probs))) return SV_ERR_NULL;
+  if (!workspace) return SV_ERR_WORKSPACE;
+  if (workspace_bytes < sv::verify_workspace_bytes(B, K, V)) return SV_ERR_WORKSPACE;
+  const size_t esz = dtype == SV_BF16 ? 2 : 4;
+  if (!aligned(logits, esz) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+      (draft_tokens && !aligned(draft_tokens, 4)) || !aligned(workspace, 16) ||
+      (device_error && !aligned(device_error, 4)))
+    return SV_ERR_ALIGN;
+  if (sample && (!aligned(uniforms, 4) || (draft_probs && !aligned(draft_probs, 4)) ||
+                 (out_p_draft && !aligned(out_p_draft, 4))))
+    return SV_ERR_ALIGN;
+  if ((long)B * (K + 1) * sv::verify_splits(B, K, V) > 0x7fffffffL) return SV_ERR_SHAPE;
+
+  sv::VerifyLaunch L;
+  L.logits = logits;
+  L.draft_probs = draft_probs;
+  L.draft_tokens = draft_tokens;
+  L.uniforms = uniforms;
+  L.temperature = temperature;
+  L.B = B; L.K = K; L.V = V;
+  L.bf16 = dtype == SV_BF16;
+  L.sample = sample;
+  L.vec = (V % 8 == 0) && aligned(logits, 16) && (!sample || !draft_probs || aligned(draft_probs, 16));
+  L.out_tokens = out_tokens;
+  L.out_num_accepted = out_num_accepted;
+  L.out_p_draft = sample ? out_p_draft : nullptr;
+  L.workspace = workspace;
+  L.device_error = device_error;
+  return sv::launch_verify(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
+                                    const int32_t* draft_tokens, int B, int K, int V,
+                                    int32_t* out_tokens, int32_t* out_num_accepted,
+                                    void* workspace, size_t workspace_bytes,
+                                    int32_t* device_error, void* stream) {
+  return verify_common(target_logits, logits_dtype, nullptr, draft_tokens, nullptr, 1.0f, 0, B, K,
+                       V, out_tokens, out_num_accepted, nullptr, workspace, workspace_bytes,
+                       device_error, stream);
+}
+
+SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
+                                    const float* draft_probs, const int32_t* draft_tokens,
+                                    const float* uniforms, float temperature, int B, int K, int V,
+                                    int32_t* out_tokens, int32_t* out_num_accepted,
+                                    float* out_draft_target_prob, void* workspace,
+                                    size_t workspace_bytes, int32_t* device_error, void* stream) {
+  return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, uniforms,
+                       temperature, 1, B, K, V, out_tokens, out_num_accepted,
+                       out_draft_target_prob, workspace, workspace_bytes, device_error, stream);
+}
+
+SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,
+                                          const int32_t* num_accepted, const int32_t* draft_tokens,
+                                          const int64_t* start_pos, const int32_t* block_table,
+                                          int max_blocks_per_seq, int block_size,
+                                          const void* target_hidden, const void* h_shared,
+                                          int hidden_dtype, int32_t mask_token_id, int B, int K,
+                                          int H, int32_t* out_input_ids, int64_t* out_positions,
+                                          int64_t* out_slot_mapping, void* out_hidden,
+                                          int32_t* out_sample_rows, int32_t* device_error,
+                                          void* stream) {
+  if (B < 0 || B > kMaxB || K < 1 || K > SV_MAX_K || H < 1 || block_size < 1 ||
+      max_blocks_per_seq < 1)
+    return SV_ERR_SHAPE;
+  if (hidden_dtype != SV_F32 && hidden_dtype != SV_BF16 && hidden_dtype != SV_F16)
+    return SV_ERR_DTYPE;
+  if (B == 0) return SV_OK;
+  if (!verify_out_tokens || !num_accepted || !draft_tokens || !start_pos || !block_table ||
+      !target_hidden || !h_shared || !out_input_ids || !out_positions || !out_slot_mapping ||
+      !out_hidden)
+    return SV_ERR_NULL;
+  const int esz = hidden_dtype == SV_F32 ? 4 : 2;
+  if (!aligned(verify_out_tokens, 4) || !aligned(num_accepted, 4) || !aligned(draft_tokens, 4) ||
+      !aligned(start_pos, 8) || !aligned(block_table, 4) || !aligned(target_hidden, esz) ||
+      !aligned(h_shared, esz) || !aligned(out_input_ids, 4) || !aligned(out_positions, 8) ||
+      !aligned(out_slot_mapping, 8) || !aligned(out_hidden, esz) ||
+      (out_sample_rows && !aligned(out_sample_rows, 4)) ||
+      (device_error && !aligned(device_error, 4)))
+    return SV_ERR_ALIGN;
+  const long row_bytes = (long)H * esz;
+  sv::BuildLaunch L;
+  L.verify_out_tokens = verify_out_tokens;
+  L.num_accepted = num_accepted;
+  L.draft_tokens = draft_tokens;
+  L.start_pos = start_pos;
+  L.block_table = block_table;
+  L.max_blocks = max_blocks_per_seq;
+  L.block_size = block_size;
+  L.target_hidden = target_hidden;
+  L.h_shared = h_shared;
+  L.elem_bytes = esz;
+  L.vec = row_bytes % 16 == 0 && aligned(target_hidden, 16) && aligned(h_shared, 16) &&
+          aligned(out_hidden, 16);
+  L.mask_token_id = mask_token_id;
+  L.B = B; L.K = K; L.H = H;
+  L.out_input_ids = out_input_ids;
+  L.out_positions = out_positions;
+  L.out_slot_mapping = out_slot_mapping;
+  L.out_hidden = out_hidden;
+  L.out_sample_rows = out_sample_rows;
+  L.device_error = device_error;
+  return sv::launch_build(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Host-side launch descriptors shared by the C ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/spec_verify.h"
+
+namespace sv {
+
+struct VerifyLaunch {
+  const void* logits;
+  const float* draft_probs;      // sampling only
+  const int32_t* draft_tokens;
+  const float* uniforms;         // sampling only
+  float temperature;             // sampling only
+  int B, K, V;
+  int bf16;                      // logits are bf16 (else fp32)
+  int sample;                    // rejection sampling (else greedy)
+  int vec;                       // 16-byte vector loads are legal for every row
+  int32_t* out_tokens;
+  int32_t* out_num_accepted;
+  float* out_p_draft;            // may be NULL
+  void* workspace;
+  int32_t* device_error;         // may be NULL
+};
+
+struct BuildLaunch {
+  const int32_t* verify_out_tokens;
+  const int32_t* num_accepted;
+  const int32_t* draft_tokens;
+  const int64_t* start_pos;
+  const int32_t* block_table;
+  int max_blocks, block_size;
+  const void* target_hidden;
+  const void* h_shared;
+  int elem_bytes;                // 2 or 4
+  int vec;                       // rows are 16-byte aligned multiples of 16 bytes
+  int32_t mask_token_id;
+  int B, K, H;
+  int32_t* out_input_ids;
+  int64_t* out_positions;
+  int64_t* out_slot_mapping;
+  void* out_hidden;
+  int32_t* out_sample_rows;      // may be NULL
+  int32_t* device_error;         // may be NULL
+};
+
+int verify_splits(int B, int K, int V);
+
+// Kernel tracing (per host thread): bracket a launch with events on its stream.
+void trace_before(hipStream_t stream);
+void trace_after(hipStream_t stream, int kernel_id);
+size_t verify_workspace_bytes(int B, int K, int V);
+hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream);
+hipError_t launch_build(const BuildLaunch& L, hipStream_t stream);
+
+}  // namespace sv

@@ -1,0 +1,697 @@
+// Batched speculative verify-and-accept for gfx950.
+//
+// Kernel 1 (verify_rows): one workgroup per (sequence b, logit row k,
+// vocabulary split s), sequence-major.  Each workgroup streams its slice of
+// row k from HBM once and reduces it to a partial: the max and its lowest
+// index (greedy), or the max and the sum of exponentials relative to it
+// (sampling).  The last workgroup of a sequence to arrive (a per-sequence
+// ticket) combines the partials of the K+1 rows, tests every draft in
+// parallel (one lane per row), takes the first rejection from a wave ballot
+// and writes the accepted prefix.  Greedy: it also writes the argmax of row a
+// and the step is done.  Sampling: it leaves (a, max, sum) of row a for
+// kernel 2.
+//
+// Kernel 2 (verify_draw, sampling only): C workgroups per sequence each take
+// a contiguous chunk of row a, compute the mass r = max(0, p_a - q_a) (or p_K
+// for the bonus token) of each 512-element tile in it, and publish the tile
+// masses and the chunk total.  The last chunk to arrive finds the chunk, then
+// the tile, whose running total first exceeds u * S, rescans that one tile
+// and writes the token.
+//
+// The verify flow is that of "Project 14 - speculative decoding inference
+// server", section 架构 (architecture): accept the prefix, resample the
+// rejected suffix.  The bitmask form of the accept scan follows the rskf.cn
+// survey, section 3.3 (DFlash): one bit per draft instead of a branch per
+// draft; here the bits come from a wave64 ballot.
+#include <math.h>
+
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+struct Partial {
+  float m;       // max of the slice (-inf if every element is -inf)
+  int g;         // greedy: lowest index attaining m
+  double acc;    // sampling: sum over the slice of 2^((z - m) * c)
+};
+
+struct DrawInfo {  // row a of a sequence, handed from kernel 1 to kernel 2
+  int a;
+  float M;         // max of row a
+  double s;        // sum over row a of 2^((z - M) * c)
+};
+
+constexpr int kThreads = 256;           // 4 waves
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxTiles = SV_MAX_V / kTile;
+constexpr int kTileUnroll = 4;          // draw: tiles per wave per step
+
+enum Mode { GREEDY = 0, SAMPLE = 1 };
+
+// ---------------------------------------------------------------- workspace
+// tickets [B] | tickets2 [B] | info [B] | chunk sums [B][C] | tile sums [B][T] | partials [B][K+1][S]
+struct Layout {
+  size_t tickets, tickets2, info, chunk, tile, partials, total;
+  int S, C, T;
+};
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int verify_splits(int B, int K, int V) {
+  const long rows = (long)B * (K + 1);
+  const long octets = (V + 7) / 8;
+  long s = (2048 + rows - 1) / rows;
+  s = s < 16 ? s : 16;
+  long cap = octets / 256;
+  if (s > cap) s = cap;
+  return s < 1 ? 1 : (int)s;
+}
+
+static int draw_chunks(int B, int V) {
+  const long tiles = (V + kTile - 1) / kTile;
+  long c = (4096 + B - 1) / B;
+  if (c > tiles) c = tiles;
+  return c < 1 ? 1 : (int)c;
+}
+
+static Layout layout(int B, int K, int V) {
+  Layout L;
+  L.S = verify_splits(B, K, V);
+  L.C = draw_chunks(B, V);
+  L.T = (V + kTile - 1) / kTile;
+  size_t off = 0;
+  L.tickets = off;  off = align256(off + (size_t)B * sizeof(int));
+  L.tickets2 = off; off = align256(off + (size_t)B * sizeof(int));
+  L.info = off;     off = align256(off + (size_t)B * sizeof(DrawInfo));
+  L.chunk = off;    off = align256(off + (size_t)B * L.C * sizeof(double));
+  L.tile = off;     off = align256(off + (size_t)B * L.T * sizeof(float));
+  L.partials = off; off = align256(off + (size_t)B * (K + 1) * L.S * sizeof(Partial));
+  L.total = off;
+  return L;
+}
+
+size_t verify_workspace_bytes(int B, int K, int V) { return layout(B, K, V).total; }
+
+struct RowsArgs {
+  const void* logits;
+  const float* draft_probs;
+  const int32_t* draft_tokens;
+  const float* uniforms;
+  float c;                 // log2(e) / T   (sampling)
+  int B, K, V, S;
+  long octets;             // ceil(V / 8)
+  int32_t* out_tokens;
+  int32_t* out_num_accepted;
+  float* out_p_draft;
+  Partial* partials;       // [B][K+1][S]
+  int* tickets;            // [B]
+  DrawInfo* info;          // [B]
+  int32_t* device_error;
+};
+
+struct DrawArgs {
+  const void* logits;
+  const float* draft_probs;
+  const float* uniforms;
+  float c;
+  int B, K, V, C, T;
+  int32_t* out_tokens;
+  DrawInfo* info;          // [B]
+  int* tickets2;           // [B]
+  double* chunk_sums;      // [B][C]
+  float* tile_sums;        // [B][T]
+};
+
+// ---------------------------------------------------------------- raw octets
+// One octet in the registers it was loaded into, so that a step can issue all
+// of its loads before converting any of them.
+template <typename LT> struct Raw;
+template <> struct Raw<uint16_t> { u32x4 w; };
+template <> struct Raw<float> { u32x4 a, b; };
+
+template <bool NT>
+__device__ __forceinline__ void raw_load(const uint16_t* row, long o, Raw<uint16_t>& r) {
+  r.w = ld16<NT>(row + o * 8);
+}
+template <bool NT>
+__device__ __forceinline__ void raw_load(const float* row, long o, Raw<float>& r) {
+  r.a = ld16<NT>(row + o * 8);
+  r.b = ld16<NT>(row + o * 8 + 4);
+}
+__device__ __forceinline__ void unpack(const Raw<uint16_t>& r, float v[8]) {
+  v[0] = bf16_lo(r.w.x); v[1] = bf16_hi(r.w.x); v[2] = bf16_lo(r.w.y); v[3] = bf16_hi(r.w.y);
+  v[4] = bf16_lo(r.w.z); v[5] = bf16_hi(r.w.z); v[6] = bf16_lo(r.w.w); v[7] = bf16_hi(r.w.w);
+}
+__device__ __forceinline__ void unpack(const Raw<float>& r, float v[8]) {
+  v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
+  v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
+  v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+  v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+}
+
+// ---------------------------------------------------------------- row-slice state
+struct SliceState {
+  float best = -INFINITY;   // greedy: running max ...
+  int idx = INT32_MAX;      // ... and the lowest index attaining it
+  float mref = -INFINITY;   // sampling: running max ...
+  float R = -1e30f;         // ... its exponent mref*c (log2 units, fp32) ...
+  double acc = 0.0;         // ... and the sum of 2^(z*c - R) so far
+};
+
+__device__ __forceinline__ float tree_sum8(const float e[8]) {
+  return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+}
+
+// Fold N octets (at octet indices o0, o0 + ostride, ...) into the state.  The
+// octets arrive in increasing index order, so "strictly greater" keeps the
+// lowest index of a maximum.
+template <int MODE, int N>
+__device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, long ostride,
+                                     long V, float c) {
+  float mt = v[0][0];
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mt = fmaxf(mt, v[u][j]);
+  if constexpr (MODE == GREEDY) {
+    if (mt > s.best || s.idx == INT32_MAX) {
+      int found = INT32_MAX;
+#pragma unroll
+      for (int u = N - 1; u >= 0; --u)
+#pragma unroll
+        for (int j = 7; j >= 0; --j) {
+          const long e = (o0 + (long)u * ostride) * 8 + j;
+          if (e < V && v[u][j] == mt) found = (int)e;
+        }
+      if (found != INT32_MAX) { s.best = mt; s.idx = found; }
+    }
+  } else {
+    if (mt > s.mref) {
+      const float Rn = mt * c;
+      s.acc *= (double)__builtin_amdgcn_exp2f(s.R - Rn);
+      s.R = Rn;
+      s.mref = mt;
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(v[u][j], c, -s.R));
+      part += tree_sum8(e);
+    }
+    s.acc += (double)part;
+  }
+}
+
+// Phase 1: one slice [o_lo, o_hi) of octets of one row -> one Partial
+// (returned by thread 0).  VEC: V is a multiple of 8 and the rows are 16-byte
+// aligned, so the steady-state loop has no branches and issues all of a
+// step's loads before using any.
+template <typename LT, int MODE, bool VEC>
+__device__ Partial slice_stats(const LT* row, long o_lo, long o_hi, long V, float c,
+                               float* sm_f, int* sm_i, double* sm_d) {
+  constexpr int U = 16 / sizeof(LT);    // octets per step: 128 bytes in flight per thread
+  const int t = threadIdx.x;
+  SliceState st;
+  long base = o_lo + t;
+  if constexpr (VEC) {
+    for (; base + (long)(U - 1) * kThreads < o_hi; base += (long)U * kThreads) {
+      Raw<LT> raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) raw_load<false>(row, base + (long)u * kThreads, raw[u]);
+      float v[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) unpack(raw[u], v[u]);
+      fold<MODE, U>(st, v, base, kThreads, V, c);
+    }
+    for (; base < o_hi; base += kThreads) {
+      Raw<LT> raw;
+      raw_load<false>(row, base, raw);
+      float v[1][8];
+      unpack(raw, v[0]);
+      fold<MODE, 1>(st, v, base, kThreads, V, c);
+    }
+  } else {
+    for (; base < o_hi; base += kThreads) {
+      float v[1][8];
+      load_octet<false>(row, base, V, false, -INFINITY, v[0]);
+      fold<MODE, 1>(st, v, base, kThreads, V, c);
+    }
+  }
+
+  Partial P{-INFINITY, INT32_MAX, 0.0};
+  const int w = t / kWave, l = lane_id();
+  if constexpr (MODE == GREEDY) {
+    float best = st.best;
+    int idx = st.idx;
+    wave_argmax(best, idx);
+    if (l == 0) { sm_f[w] = best; sm_i[w] = idx; }
+    __syncthreads();
+    if (t == 0) {
+      P.m = sm_f[0];
+      P.g = sm_i[0];
+      for (int i = 1; i < kWaves; ++i) argmax_combine(P.m, P.g, sm_f[i], sm_i[i]);
+    }
+  } else {
+    float M = wave_max(st.mref);
+    if (l == 0) sm_f[w] = M;
+    __syncthreads();
+    M = sm_f[0];
+    for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sm_f[i]);
+    // rescale this thread's sum from its reference R to M*c (fp64)
+    const double mine = st.acc == 0.0 ? 0.0 : st.acc * exp2((double)st.R - (double)M * (double)c);
+    const double ws = wave_sum(mine);
+    if (l == 0) sm_d[w] = ws;
+    __syncthreads();
+    if (t == 0) {
+      double s = sm_d[0];
+      for (int i = 1; i < kWaves; ++i) s += sm_d[i];
+      P.m = M; P.g = 0; P.acc = s;
+    }
+  }
+  return P;
+}
+
+// ----------------------------------------------------------------------------
+template <typename LT, int MODE, bool VEC>
+__global__ __launch_bounds__(kThreads) void verify_rows(RowsArgs A) {
+  __shared__ float sm_f[kWaves];
+  __shared__ int sm_i[kWaves];
+  __shared__ double sm_d[kWaves];
+  __shared__ int sm_last;
+
+  const int K = A.K, S = A.S;
+  const long V = A.V;
+  const long unit = blockIdx.x;                 // ((b * (K+1)) + k) * S + s
+  const int s = (int)(unit % S);
+  const long rowi = unit / S;                   // b * (K+1) + k
+  const int b = (int)(rowi / (K + 1));
+  const LT* row = static_cast<const LT*>(A.logits) + rowi * V;
+  const long o_lo = (long)s * A.octets / S, o_hi = (long)(s + 1) * A.octets / S;
+
+  const Partial P = slice_stats<LT, MODE, VEC>(row, o_lo, o_hi, V, A.c, sm_f, sm_i, sm_d);
+
+  // ---- publish the partial, then take the per-sequence ticket
+  if (threadIdx.x == 0) {
+    Partial* dst = &A.partials[unit];
+    st_coherent(&dst->m, P.m);
+    st_coherent(&dst->g, P.g);
+    st_coherent(&dst->acc, P.acc);
+    wait_stores_performed();
+    const int prev = take_ticket(&A.tickets[b]);
+    sm_last = (prev == (K + 1) * S - 1);
+  }
+  __syncthreads();
+  if (!sm_last || threadIdx.x >= kWave) return;
+
+  // ---- the last workgroup of sequence b (one wave): combine, test, scan, write
+  const int l = lane_id();
+  Partial* Pb = A.partials + (long)b * (K + 1) * S;
+  const int k = l;
+  float M = -INFINITY;
+  int g = INT32_MAX;
+  double s_k = 0.0;
+  if (k <= K) {
+    if constexpr (MODE == GREEDY) {
+      for (int j = 0; j < S; ++j) {
+        const float pm = ld_coherent(&Pb[k * S + j].m);
+        const int pg = ld_coherent(&Pb[k * S + j].g);
+        if (j == 0 || pm > M) { M = pm; g = pg; }
+      }
+    } else {
+      for (int j = 0; j < S; ++j) M = fmaxf(M, ld_coherent(&Pb[k * S + j].m));
+      for (int j = 0; j < S; ++j) {
+        const float pm = ld_coherent(&Pb[k * S + j].m);
+        const double pacc = ld_coherent(&Pb[k * S + j].acc);
+        if (pacc != 0.0) s_k += pacc * exp2(((double)pm - (double)M) * (double)A.c);
+      }
+    }
+    // the partials are consumed: clear them so the workspace ends all zero
+    for (int j = 0; j < S; ++j) {
+      st_coherent(&Pb[k * S + j].m, 0.f);
+      st_coherent(&Pb[k * S + j].g, 0);
+      st_coherent(&Pb[k * S + j].acc, 0.0);
+    }
+  }
+  int d = -1;
+  bool rej = false;
+  if (k < K) {
+    d = A.draft_tokens[(long)b * K + k];
+    const bool valid = d >= 0 && d < V;
+    if (!valid) flag_error(A.device_error, SV_DEVERR_DRAFT_TOKEN);
+    if constexpr (MODE == GREEDY) {
+      rej = !(valid && d == g);
+    } else {
+      double px = 0.0;
+      if (valid) {
+        const LT* zr = static_cast<const LT*>(A.logits) + ((long)b * (K + 1) + k) * V;
+        const float zx = logit_at(zr, d);
+        px = exp2(((double)zx - (double)M) * (double)A.c) / s_k;
+        const double qx = (double)A.draft_probs[((long)b * K + k) * V + d];
+        const double ratio = qx > 0.0 ? px / qx : (px > 0.0 ? INFINITY : 0.0);
+        rej = !((double)A.uniforms[(long)b * (K + 1) + k] < ratio);
+      } else {
+        rej = true;
+      }
+      if (A.out_p_draft) A.out_p_draft[(long)b * K + k] = (float)px;
+    }
+  }
+  const unsigned long long rejmask = __ballot(k < K && rej);
+  const int a = rejmask ? __ffsll((long long)rejmask) - 1 : K;
+  const int gA = __shfl(g, a);
+  const float Ma = __shfl(M, a);
+  const double sa = __shfl(s_k, a);
+  if (k <= K) {
+    const int tok = k < a ? d : (k == a && MODE == GREEDY ? gA : -1);
+    A.out_tokens[(long)b * (K + 1) + k] = tok;
+  }
+  if (l == 0) {
+    A.out_num_accepted[b] = a;
+    if constexpr (MODE == SAMPLE) A.info[b] = DrawInfo{a, Ma, sa};
+    st_coherent(&A.tickets[b], 0);     // leave the ticket cleared for the next call
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Residual / bonus mass of one octet: r = max(0, p - q) or p, p = 2^(z c - Mc) * inv_s.
+__device__ __forceinline__ void mass_octet(const float z[8], const float q[8], bool residual,
+                                           float c, float Mc, float inv_s, float r[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(z[j], c, -Mc)) * inv_s;
+    r[j] = residual ? fmaxf(0.f, p - q[j]) : p;
+  }
+}
+
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Mass of octet o of the draw row (z: logits row, q: drafter row or null).
+// With VEC the address is clamped into the row and the values past V are
+// masked, so the loads carry no branch.
+template <typename LT, bool VEC>
+__device__ __forceinline__ void octet_mass(const LT* zrow, const float* qrow, long o, long V,
+                                           long nocts, bool residual, float c, float Mc,
+                                           float inv_s, float r[8]) {
+  float z[8], q[8];
+  if constexpr (VEC) {
+    const bool in = o < nocts;
+    const long oc = in ? o : nocts - 1;
+    Raw<LT> rz;
+    raw_load<false>(zrow, oc, rz);
+    unpack(rz, z);
+    if (residual) {
+      Raw<float> rq;
+      raw_load<false>(qrow, oc, rq);
+      unpack(rq, q);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = 0.f;
+    }
+    if (!in) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { z[j] = -INFINITY; q[j] = 0.f; }
+    }
+  } else {
+    load_octet<false>(zrow, o, V, false, -INFINITY, z);
+    if (residual) load_octet<false>(qrow, o, V, false, 0.f, q);
+    else
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = 0.f;
+  }
+  mass_octet(z, q, residual, c, Mc, inv_s, r);
+}
+
+// Tile masses of tiles [t_lo, t_hi) of the draw row, computed by the whole
+// workgroup (kTileUnroll tiles per wave per step) and published with
+// agent-coherent stores; their sum in tile order is returned to thread 0.
+template <typename LT, bool VEC>
+__device__ double tile_masses(const LT* zrow, const float* qrow, long V, int t_lo, int t_hi,
+                              bool residual, float c, float Mc, float inv_s, float* tsum_g,
+                              float* tsum_l) {
+  const int w = threadIdx.x / kWave, l = lane_id();
+  const long nocts = (V + 7) / 8;
+  for (int t0 = t_lo + w * kTileUnroll; t0 < t_hi; t0 += kWaves * kTileUnroll) {
+    float ls[kTileUnroll];
+#pragma unroll
+    for (int j = 0; j < kTileUnroll; ++j) {
+      float r[8];
+      octet_mass<LT, VEC>(zrow, qrow, (long)(t0 + j) * kWave + l, V, nocts, residual, c, Mc,
+                          inv_s, r);
+      ls[j] = tree_sum8(r);
+    }
+#pragma unroll
+    for (int j = 0; j < kTileUnroll; ++j) {
+      const float ts = wave_sum_f(ls[j]);
+      if (l == 0 && t0 + j < t_hi) {
+        tsum_l[t0 + j - t_lo] = ts;
+        st_coherent(&tsum_g[t0 + j], ts);
+      }
+    }
+  }
+  // every wave's tile stores are performed before thread 0 takes a ticket
+  wait_stores_performed();
+  __syncthreads();
+  double sum = 0.0;
+  if (threadIdx.x == 0)
+    for (int i = 0; i < t_hi - t_lo; ++i) sum += (double)tsum_l[i];
+  __syncthreads();
+  return sum;
+}
+
+template <typename LT, bool VEC>
+__global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
+  __shared__ float tsum_l[kMaxTiles];
+  __shared__ int sm_last;
+  __shared__ int sm_pick;
+  __shared__ int sm_redo;
+
+  const int C = A.C, T = A.T, K = A.K;
+  const int b = blockIdx.x / C, cidx = blockIdx.x % C;
+  const long V = A.V;
+  const DrawInfo di = A.info[b];
+  const int a = di.a;
+  const LT* zrow = static_cast<const LT*>(A.logits) + ((long)b * (K + 1) + a) * V;
+  const float* qrow = a < K ? A.draft_probs + ((long)b * K + a) * V : nullptr;
+  const float c = A.c;
+  // p = 2^(z*c - M*c) / s.  Mc32 is M*c rounded to fp32; the rounding is
+  // folded into the scale so that p keeps the fp64 reference exactly.
+  const float Mc32 = di.M * c;
+  const float inv_s = (float)(exp2((double)Mc32 - (double)di.M * (double)c) / di.s);
+  float* tsum_g = A.tile_sums + (long)b * T;
+  double* csum_g = A.chunk_sums + (long)b * C;
+  bool residual = qrow != nullptr;
+
+  const int t_lo = (int)((long)cidx * T / C), t_hi = (int)((long)(cidx + 1) * T / C);
+  const double mine = tile_masses<LT, VEC>(zrow, qrow, V, t_lo, t_hi, residual, c, Mc32, inv_s,
+                                           tsum_g, tsum_l);
+  if (threadIdx.x == 0) {
+    st_coherent(&csum_g[cidx], mine);
+    wait_stores_performed();
+    sm_last = take_ticket(&A.tickets2[b]) == C - 1;
+  }
+  __syncthreads();
+  if (!sm_last) return;
+
+  // ---- the last chunk of sequence b: total, locate, rescan
+  const int w = threadIdx.x / kWave, l = lane_id();
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    if (w == 0) {
+      const int per = (C + kWave - 1) / kWave;
+      double part = 0.0;
+      for (int i = l * per; i < min(C, (l + 1) * per); ++i) part += ld_coherent(&csum_g[i]);
+      const double incl = wave_inclusive_scan(part);
+      const double S = __shfl(incl, kWave - 1);
+      if (l == 0) sm_redo = residual && !(S > 0.0);
+    }
+    __syncthreads();
+    if (!sm_redo) break;
+    // r sums to 0 (only when the drafter's row sums to more than p): draw
+    // from p_a instead; this workgroup recomputes every tile of the row
+    residual = false;
+    for (int ci = 0; ci < C; ++ci) {
+      const int lo = (int)((long)ci * T / C), hi = (int)((long)(ci + 1) * T / C);
+      const double cs = tile_masses<LT, VEC>(zrow, nullptr, V, lo, hi, false, c, Mc32, inv_s,
+                                             tsum_g, tsum_l);
+      if (threadIdx.x == 0) st_coherent(&csum_g[ci], cs);
+    }
+    if (threadIdx.x == 0) wait_stores_performed();
+    __syncthreads();
+  }
+
+  if (w == 0) {
+    // chunk that holds u * S (lanes own contiguous runs of chunks)
+    const int per = (C + kWave - 1) / kWave;
+    const int lo = l * per, hi = min(C, (l + 1) * per);
+    double part = 0.0;
+    for (int i = lo; i < hi; ++i) part += ld_coherent(&csum_g[i]);
+    const double incl = wave_inclusive_scan(part);
+    const double S = __shfl(incl, kWave - 1);
+    const double target = (double)A.uniforms[(long)b * (K + 1) + K] * S;
+    double run = __shfl_up(incl, 1);
+    if (l == 0) run = 0.0;
+    int hit = -1;
+    double pre = 0.0;
+    for (int i = lo; i < hi; ++i) {
+      const double nxt = run + ld_coherent(&csum_g[i]);
+      if (nxt > target) { hit = i; pre = run; break; }
+      run = nxt;
+    }
+    unsigned long long any = __ballot(hit >= 0);
+    int chunk;
+    bool fallback = false;
+    if (any) {
+      const int src = __ffsll((long long)any) - 1;
+      chunk = __shfl(hit, src);
+      pre = __shfl(pre, src);
+    } else {
+      // rounding left u*S at or past the total: last chunk with positive mass
+      int last = -1;
+      for (int i = lo; i < hi; ++i) if (ld_coherent(&csum_g[i]) > 0.0) last = i;
+      const unsigned long long anyp = __ballot(last >= 0);
+      chunk = anyp ? __shfl(last, 63 - __clzll((long long)anyp)) : 0;
+      fallback = true;
+    }
+    // tile inside the chunk (lanes own contiguous runs of its tiles)
+    const int clo = (int)((long)chunk * T / C), chi = (int)((long)(chunk + 1) * T / C);
+    const int n = chi - clo;
+    const int tper = (n + kWave - 1) / kWave;
+    const int tlo = clo + l * tper, thi = min(chi, clo + (l + 1) * tper);
+    double tpart = 0.0;
+    for (int i = tlo; i < thi; ++i) tpart += (double)ld_coherent(&tsum_g[i]);
+    const double tincl = wave_inclusive_scan(tpart);
+    double trun = __shfl_up(tincl, 1);
+    if (l == 0) trun = 0.0;
+    trun += pre;
+    int thit = -1, tlast = -1;
+    double tpre = 0.0;
+    for (int i = tlo; i < thi; ++i) {
+      const float ts = ld_coherent(&tsum_g[i]);
+      if (ts > 0.f) tlast = i;
+      const double nxt = trun + (double)ts;
+      if (!fallback && thit < 0 && nxt > target) { thit = i; tpre = trun; }
+      trun = nxt;
+    }
+    any = __ballot(thit >= 0);
+    int tile;
+    if (any) {
+      const int src = __ffsll((long long)any) - 1;
+      tile = __shfl(thit, src);
+      tpre = __shfl(tpre, src);
+    } else {
+      const unsigned long long anyp = __ballot(tlast >= 0);
+      tile = anyp ? __shfl(tlast, 63 - __clzll((long long)anyp)) : clo;
+      fallback = true;
+    }
+    // rescan the tile: one octet per lane
+    const long o = (long)tile * kWave + l;
+    float r[8];
+    octet_mass<LT, VEC>(zrow, qrow, o, V, (V + 7) / 8, residual, c, Mc32, inv_s, r);
+    const double ls = (double)tree_sum8(r);
+    const double lincl = wave_inclusive_scan(ls);
+    double lexcl = __shfl_up(lincl, 1);
+    if (l == 0) lexcl = 0.0;
+    int pick = -1;
+    if (!fallback) {
+      double lrun = tpre + lexcl;
+      const unsigned long long cross = __ballot(tpre + lincl > target);
+      const int src = cross ? __ffsll((long long)cross) - 1 : -1;
+      if (l == src) {
+        for (int j = 0; j < 8; ++j) {
+          lrun += (double)r[j];
+          if (r[j] > 0.f && lrun > target) { pick = (int)(o * 8 + j); break; }
+        }
+        if (pick < 0)
+          for (int j = 7; j >= 0; --j) if (r[j] > 0.f) { pick = (int)(o * 8 + j); break; }
+      }
+      const unsigned long long got = __ballot(pick >= 0);
+      if (got) pick = __shfl(pick, __ffsll((long long)got) - 1);
+    }
+    if (pick < 0) {
+      // last element of the tile with positive mass
+      int lastj = -1;
+      for (int j = 7; j >= 0; --j) if (r[j] > 0.f) { lastj = (int)(o * 8 + j); break; }
+      const unsigned long long anyp = __ballot(lastj >= 0);
+      pick = anyp ? __shfl(lastj, 63 - __clzll((long long)anyp)) : 0;
+    }
+    if (l == 0) sm_pick = pick;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) A.out_tokens[(long)b * (K + 1) + a] = sm_pick;
+  // leave this sequence's part of the workspace cleared
+  for (int i = threadIdx.x; i < T; i += kThreads) st_coherent(&tsum_g[i], 0.f);
+  for (int i = threadIdx.x; i < C; i += kThreads) st_coherent(&csum_g[i], 0.0);
+  if (threadIdx.x == 0) {
+    st_coherent(&A.tickets2[b], 0);
+    A.info[b] = DrawInfo{0, 0.f, 0.0};
+  }
+}
+
+// ----------------------------------------------------------------------------
+hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
+  const Layout lay = layout(L.B, L.K, L.V);
+  char* ws = static_cast<char*>(L.workspace);
+  const float c = L.sample ? (float)(1.4426950408889634 / (double)L.temperature) : 1.0f;
+
+  RowsArgs R;
+  R.logits = L.logits;
+  R.draft_probs = L.draft_probs;
+  R.draft_tokens = L.draft_tokens;
+  R.uniforms = L.uniforms;
+  R.c = c;
+  R.B = L.B; R.K = L.K; R.V = L.V; R.S = lay.S;
+  R.octets = (L.V + 7) / 8;
+  R.out_tokens = L.out_tokens;
+  R.out_num_accepted = L.out_num_accepted;
+  R.out_p_draft = L.out_p_draft;
+  R.partials = reinterpret_cast<Partial*>(ws + lay.partials);
+  R.tickets = reinterpret_cast<int*>(ws + lay.tickets);
+  R.info = reinterpret_cast<DrawInfo*>(ws + lay.info);
+  R.device_error = L.device_error;
+  const dim3 grid1((unsigned)((long)L.B * (L.K + 1) * lay.S)), block(kThreads);
+  const int kid1 = L.sample ? SV_KERNEL_VERIFY_SAMPLE_ROWS : SV_KERNEL_VERIFY_GREEDY;
+  trace_before(stream);
+#define SV_ROWS(LT, MODE, VEC) hipLaunchKernelGGL((verify_rows<LT, MODE, VEC>), grid1, block, 0, stream, R)
+  if (L.bf16) {
+    if (L.sample) { if (L.vec) SV_ROWS(uint16_t, SAMPLE, true); else SV_ROWS(uint16_t, SAMPLE, false); }
+    else { if (L.vec) SV_ROWS(uint16_t, GREEDY, true); else SV_ROWS(uint16_t, GREEDY, false); }
+  } else {
+    if (L.sample) { if (L.vec) SV_ROWS(float, SAMPLE, true); else SV_ROWS(float, SAMPLE, false); }
+    else { if (L.vec) SV_ROWS(float, GREEDY, true); else SV_ROWS(float, GREEDY, false); }
+  }
+#undef SV_ROWS
+  hipError_t err = hipGetLastError();
+  trace_after(stream, kid1);
+  if (err != hipSuccess || !L.sample) return err;
+
+  DrawArgs D;
+  D.logits = L.logits;
+  D.draft_probs = L.draft_probs;
+  D.uniforms = L.uniforms;
+  D.c = c;
+  D.B = L.B; D.K = L.K; D.V = L.V; D.C = lay.C; D.T = lay.T;
+  D.out_tokens = L.out_tokens;
+  D.info = R.info;
+  D.tickets2 = reinterpret_cast<int*>(ws + lay.tickets2);
+  D.chunk_sums = reinterpret_cast<double*>(ws + lay.chunk);
+  D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
+  const dim3 grid2((unsigned)((long)L.B * lay.C));
+  trace_before(stream);
+  if (L.bf16) {
+    if (L.vec) hipLaunchKernelGGL((verify_draw<uint16_t, true>), grid2, block, 0, stream, D);
+    else hipLaunchKernelGGL((verify_draw<uint16_t, false>), grid2, block, 0, stream, D);
+  } else {
+    if (L.vec) hipLaunchKernelGGL((verify_draw<float, true>), grid2, block, 0, stream, D);
+    else hipLaunchKernelGGL((verify_draw<float, false>), grid2, block, 0, stream, D);
+  }
+  err = hipGetLastError();
+  trace_after(stream, SV_KERNEL_VERIFY_SAMPLE_DRAW);
+  return err;
+}
+
+}  // namespace sv

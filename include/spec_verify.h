@@ -1,0 +1,211 @@
+/*
+ * spec_verify.h - C ABI of the speculative-decoding hot path on one MI355X.
+ *
+ * Two steps of a decode round with draft tokens:
+ *   1. verify-and-accept: per sequence, softmax over the target's K+1 logit
+ *      rows, the greedy argmax-match or p/q rejection test on the K drafts,
+ *      the first-rejection prefix length, then the residual max(0, p - q)
+ *      resample or the bonus token.  Source: "Project 14 - speculative
+ *      decoding inference server" (ai-engineering.com.cn), section 架构
+ *      (architecture): the target checks the k drafts in one forward, keeps
+ *      the accepted prefix and resamples the rejected suffix; section 概念
+ *      (concepts): an accepted prefix replaces the greedy path.
+ *   2. the P-EAGLE parallel-draft batch: MASK rows for the multi-token
+ *      prediction positions 2..K, remapped positions, h_shared broadcast into
+ *      the MASK rows, PADDING_SLOT_ID = -1 for the KV slots of rejected
+ *      tokens.  Source: the P-EAGLE / TorchSpec blog summary
+ *      (blog.hotdry.top), sections 并行架构的核心创新 (parallel architecture)
+ *      and TorchSpec 集成与工程优化 (engineering).
+ *
+ * Conventions shared by every call
+ *   - Every tensor argument is a DEVICE pointer on the current HIP device,
+ *     owned by the caller; the library allocates no device memory, keeps no
+ *     state between calls (the optional kernel tracer at the end of this
+ *     file aside) and never synchronises.  All work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) in issue order.
+ *   - Arrays are dense and row-major with the shapes given below.
+ *   - Arguments are validated on the host before anything is enqueued: on an
+ *     error the call returns a nonzero sv_status and touches no memory.
+ *     SV_ERR_HIP means a launch was rejected by the runtime; faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - `device_error` (optional, may be NULL) is one int32 in device memory;
+ *     kernels OR SV_DEVERR_* bits into it when they meet data that breaks a
+ *     precondition.  Such data is handled safely as documented per bit.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs on every run (no floating-point atomics).
+ *   - Calls on one stream run in order; calls that share a workspace must not
+ *     run concurrently on different streams.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_API __attribute__((visibility("default")))
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  SV_ERR_SHAPE = 2,     /* B, K, V, H, block sizes or table width out of range */
+  SV_ERR_DTYPE = 3,     /* dtype code not supported by this call               */
+  SV_ERR_VALUE = 4,     /* scalar out of range (temperature <= 0 or not finite)*/
+  SV_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required             */
+  SV_ERR_ALIGN = 6,     /* pointer not aligned to its element size             */
+  SV_ERR_HIP = 7        /* the HIP runtime rejected a launch                   */
+} sv_status;
+
+typedef enum {
+  SV_F32 = 0,   /* IEEE binary32                                            */
+  SV_BF16 = 1,  /* bfloat16 (upper half of a binary32)                      */
+  SV_F16 = 2    /* IEEE binary16: accepted where data is only copied (hidden) */
+} sv_dtype;
+
+/* Bits OR-ed into *device_error. */
+#define SV_DEVERR_DRAFT_TOKEN 1   /* a draft token outside [0, V): that draft is rejected
+                                     (greedy: mismatch; sampling: ratio 0) and its
+                                     out_draft_target_prob entry is 0                  */
+#define SV_DEVERR_ACCEPT_COUNT 2  /* num_accepted outside [0, K]: clamped into range    */
+#define SV_DEVERR_BLOCK_TABLE 4   /* a position past the block table, or a negative
+                                     block id: that row gets slot -1                   */
+
+/* Limits. */
+#define SV_MAX_K 63               /* drafts per sequence (K+1 rows fit one wavefront) */
+#define SV_MAX_V (1 << 19)        /* vocabulary size                                  */
+#define SV_PADDING_SLOT_ID (-1)   /* slot of rows that must not write the KV cache    */
+
+/* Human-readable name of a status code (static storage; never NULL). */
+SV_API const char* sv_status_string(int status);
+
+/* Bytes of device workspace spec_verify_greedy / spec_verify_sample need for
+ * this (B, K, V).  The workspace must be zero-filled once after allocation;
+ * every call leaves it zero-filled again, so it can be reused (and captured
+ * in a graph) without clearing.  Returns 0 for invalid shapes. */
+SV_API size_t spec_verify_workspace_bytes(int B, int K, int V);
+
+/*
+ * Greedy verify.  For sequence b, g_k = the lowest index of the maximum of
+ * logit row k.  a_b = the first k < K with draft_tokens[b][k] != g_k, or K.
+ * Emitted tokens: the a_b accepted drafts, then c_b = g_{a_b}.
+ *
+ *   target_logits    [B][K+1][V], dtype SV_F32 or SV_BF16; row k is the
+ *                    target's distribution for the token after verify slot k
+ *                    (slot 0 = last committed token, slot i = draft i-1).
+ *   draft_tokens     [B][K] int32.
+ *   out_tokens       [B][K+1] int32: d[0..a-1], c, then -1 up to K.
+ *   out_num_accepted [B] int32, in [0, K].
+ *   workspace        spec_verify_workspace_bytes(B, K, V) bytes (see above).
+ * Ties: the lowest index wins.  NaN logits, or a row of only -inf, give an
+ * unspecified but in-range token.  B = 0 is a no-op.  1 <= V <= SV_MAX_V,
+ * 0 <= K <= SV_MAX_K.
+ */
+SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
+                                    const int32_t* draft_tokens,
+                                    int B, int K, int V,
+                                    int32_t* out_tokens, int32_t* out_num_accepted,
+                                    void* workspace, size_t workspace_bytes,
+                                    int32_t* device_error, void* stream);
+
+/*
+ * Sampled verify (rejection sampling against the drafter's distribution).
+ * p_k = softmax(row k / T); q_k = draft_probs[b][k] used as given.
+ * Draft k is accepted iff u[b][k] < p_k(x)/q_k(x), x = draft_tokens[b][k]
+ * (q_k(x) = 0: accepted iff p_k(x) > 0).  a_b = the first rejected k, or K.
+ * If a_b < K the new token is drawn from r = max(0, p_a - q_a) (from p_a if
+ * r sums to 0); if a_b = K it is the bonus token drawn from p_K.  The draw is
+ * the smallest v whose running total of r in vocabulary order exceeds
+ * u[b][K] * sum(r) (inverse CDF with the last uniform).
+ *
+ *   target_logits    [B][K+1][V], SV_F32 or SV_BF16.
+ *   draft_probs      [B][K][V] fp32, the drafter's probabilities of each draft.
+ *   draft_tokens     [B][K] int32, d[b][k] drawn from draft_probs[b][k].
+ *   uniforms         [B][K+1] fp32 in [0, 1): [:, k<K] tests, [:, K] the draw.
+ *   temperature      > 0 and finite; applies to the target logits only.
+ *   out_tokens, out_num_accepted: as for spec_verify_greedy.
+ *   out_draft_target_prob  optional [B][K] fp32: p_k(d[b][k]) for every k
+ *                    (NULL = not written).
+ * Arithmetic: fp32 exponentials, fp64 accumulation of every sum and of the
+ * acceptance ratio; results agree with an fp64 evaluation except when a
+ * decision lies within ~1e-6 of its threshold.  Two kernels are enqueued:
+ * row statistics with the accept scan, then the draw of the new token.
+ */
+SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
+                                    const float* draft_probs,
+                                    const int32_t* draft_tokens,
+                                    const float* uniforms, float temperature,
+                                    int B, int K, int V,
+                                    int32_t* out_tokens, int32_t* out_num_accepted,
+                                    float* out_draft_target_prob,
+                                    void* workspace, size_t workspace_bytes,
+                                    int32_t* device_error, void* stream);
+
+/*
+ * P-EAGLE drafter batch.  Each sequence b owns the 2K rows [2Kb, 2Kb+2K).
+ * With a = num_accepted[b], c = verify_out_tokens[b][a], L = start_pos[b]
+ * (position of verify slot 0) and h[i] = target_hidden row b*(K+1)+i (the
+ * target's hidden state at verify slot i):
+ *
+ *   row a' = 0..a-1   id verify_out_tokens[b][r]   pos L+r     hidden h[r]      slot(L+r)
+ *   row a             id c (the new token)         pos L+a     hidden h[a]      slot(L+a)
+ *   row a+m, m=1..K-1 id mask_token_id             pos L+a+m   hidden h_shared  slot(L+a+m)
+ *   row a+K+j,        id draft_tokens[b][a+j]      pos L+a+1+j hidden h[a+1+j]  -1
+ *     j=0..K-a-1
+ *
+ * slot(p) = block_table[b][p / block_size] * block_size + p % block_size.
+ * out_sample_rows[b][k] = 2Kb + a + k: the NTP row and the K-1 MASK rows whose
+ * drafter outputs are the next K drafts.
+ *
+ *   verify_out_tokens [B][K+1] int32 and num_accepted [B] int32, as written by
+ *                    spec_verify_* (they may still be in flight on `stream`).
+ *   draft_tokens     [B][K] int32.        start_pos [B] int64.
+ *   block_table      [B][max_blocks_per_seq] int32 page ids.
+ *   target_hidden    [B*(K+1)][H], h_shared [H]: elements of hidden_dtype
+ *                    (SV_BF16, SV_F16 or SV_F32), copied bit for bit.
+ *   out_input_ids [B*2K] int32, out_positions [B*2K] int64,
+ *   out_slot_mapping [B*2K] int64, out_hidden [B*2K][H], out_sample_rows
+ *   optional [B][K] int32.
+ * 1 <= K <= SV_MAX_K, H >= 1, block_size >= 1, max_blocks_per_seq >= 1.
+ */
+SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,
+                                          const int32_t* num_accepted,
+                                          const int32_t* draft_tokens,
+                                          const int64_t* start_pos,
+                                          const int32_t* block_table,
+                                          int max_blocks_per_seq, int block_size,
+                                          const void* target_hidden, const void* h_shared,
+                                          int hidden_dtype, int32_t mask_token_id,
+                                          int B, int K, int H,
+                                          int32_t* out_input_ids, int64_t* out_positions,
+                                          int64_t* out_slot_mapping, void* out_hidden,
+                                          int32_t* out_sample_rows,
+                                          int32_t* device_error, void* stream);
+
+/*
+ * Kernel tracing, a profiling aid.  While tracing is on for the calling host
+ * thread, every kernel the library enqueues is bracketed by two HIP timing
+ * events recorded on the kernel's own stream, for up to `capacity` launches
+ * (later launches are not traced).  After the stream has completed, entry i
+ * gives the kernel's id and its duration in milliseconds.  sv_trace_begin
+ * creates the events (it may be called again to start over); sv_trace_end
+ * destroys them.  Tracing adds two event records per launch and nothing else.
+ */
+#define SV_KERNEL_VERIFY_GREEDY 0       /* spec_verify_greedy                         */
+#define SV_KERNEL_VERIFY_SAMPLE_ROWS 1  /* spec_verify_sample: row stats, accept scan */
+#define SV_KERNEL_VERIFY_SAMPLE_DRAW 2  /* spec_verify_sample: residual / bonus draw  */
+#define SV_KERNEL_PEAGLE_BUILD 3        /* peagle_build_draft_batch                   */
+
+SV_API const char* sv_kernel_name(int kernel_id);
+SV_API sv_status sv_trace_begin(int capacity);       /* SV_ERR_VALUE if capacity < 1   */
+SV_API int sv_trace_count(void);                     /* launches traced so far         */
+SV_API sv_status sv_trace_read(int i, int* kernel_id, float* ms);  /* waits for entry i */
+SV_API void sv_trace_end(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

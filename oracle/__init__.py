@@ -23,8 +23,9 @@ of Eagle / MTP / DFlash / DSPark):
   invariants the P-EAGLE summary fixes (K-1 MASK rows per sequence, slot -1
   exactly on rejected tokens, h_shared on the MASK rows, the new token paired
   with h_context) and by brute-force checks of the slot formula.  The row
-  order inside a sequence (accepted, NTP, MASK, rejected) is a reading the
-  pages leave open: that ordering is parity unpinned by the pages.
+  order inside a sequence (accepted, NTP, MASK, rejected) and the content of
+  the rejected padding rows are readings the pages leave open: those two
+  aspects are parity unpinned by the pages.
 """
 from . import peagle, verify  # noqa: F401
 from .peagle import PADDING_SLOT_ID, build_draft_batch  # noqa: F401

@@ -22,3 +22,13 @@ def gpu():
     import draft_verification_vocab_amd as sv
     sv.require_library()
     return sv
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stderr before it runs, so a failure that takes the
+    process down still says which case was running."""
+    if request.node.get_closest_marker("gpu"):
+        sys.__stderr__.write(f"[gpu-case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

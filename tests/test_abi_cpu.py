@@ -1,0 +1,180 @@
+"""The C-ABI library without a GPU: it loads, exports every function the header
+declares, and rejects bad arguments on the host before any launch.
+
+Every call below fails validation, so nothing reaches the HIP runtime; the
+pointers are never dereferenced (fake, but aligned unless the test is about
+alignment)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EVALUE, EWS, EALIGN, EHIP = range(8)
+FAKE = 0x7F0000000000          # 256-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import draft_verification_vocab_amd as sv
+    if not os.path.exists(sv.library_path()):
+        from draft_verification_vocab_amd import _build
+        _build.build()
+    return sv.require_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"SV_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
+              "spec_verify_workspace_bytes", "sv_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    import draft_verification_vocab_amd as sv
+    out = subprocess.run(["nm", "-D", "--defined-only", sv.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in declared_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+    # nothing else leaks out of the C ABI
+    assert all(not e.startswith("_ZN2sv") for e in exported)
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.sv_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.sv_status_string(OK) == b"ok"
+    assert lib.sv_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.spec_verify_workspace_bytes(0, 7, 100) == 0
+    assert lib.spec_verify_workspace_bytes(1, -1, 100) == 0
+    assert lib.spec_verify_workspace_bytes(1, 64, 100) == 0
+    assert lib.spec_verify_workspace_bytes(1, 3, 0) == 0
+    assert lib.spec_verify_workspace_bytes(1, 3, (1 << 19) + 1) == 0
+    small = lib.spec_verify_workspace_bytes(1, 3, 32)
+    big = lib.spec_verify_workspace_bytes(1024, 7, 151936)
+    assert 0 < small < big
+    # grows with the batch
+    assert lib.spec_verify_workspace_bytes(2048, 7, 151936) > big
+
+
+def greedy(lib, logits=FAKE, dtype=1, d=FAKE, B=2, K=3, V=64, out=FAKE, acc=FAKE,
+           ws=FAKE, wsb=None, err=None):
+    if wsb is None:
+        wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(K, 0), max(V, 1))
+    return lib.spec_verify_greedy(logits, dtype, d, B, K, V, out, acc, ws, wsb, err, None)
+
+
+def sample(lib, logits=FAKE, dtype=0, q=FAKE, d=FAKE, u=FAKE, T=1.0, B=2, K=3, V=64, out=FAKE,
+           acc=FAKE, pd=None, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(K, 0), max(V, 1))
+    return lib.spec_verify_sample(logits, dtype, q, d, u, T, B, K, V, out, acc, pd, ws, wsb,
+                                  None, None)
+
+
+def test_verify_validation(lib):
+    # shapes
+    assert greedy(lib, B=-1) == ESHAPE
+    assert greedy(lib, K=-1) == ESHAPE
+    assert greedy(lib, K=64) == ESHAPE
+    assert greedy(lib, V=0) == ESHAPE
+    assert greedy(lib, V=(1 << 19) + 1) == ESHAPE
+    assert greedy(lib, B=(1 << 20) + 1) == ESHAPE
+    # dtype
+    assert greedy(lib, dtype=2) == EDTYPE
+    assert greedy(lib, dtype=7) == EDTYPE
+    # empty batch is a no-op that needs no pointers
+    assert greedy(lib, B=0, logits=None, d=None, out=None, acc=None, ws=None, wsb=0) == OK
+    # nulls
+    assert greedy(lib, logits=None) == ENULL
+    assert greedy(lib, d=None) == ENULL
+    assert greedy(lib, out=None) == ENULL
+    assert greedy(lib, acc=None) == ENULL
+    # workspace
+    assert greedy(lib, ws=None) == EWS
+    assert greedy(lib, wsb=16) == EWS
+    # alignment
+    assert greedy(lib, logits=FAKE + 1) == EALIGN
+    assert greedy(lib, out=FAKE + 2) == EALIGN
+    assert greedy(lib, ws=FAKE + 8) == EALIGN
+    assert greedy(lib, err=FAKE + 1) == EALIGN
+    # sampling: temperature and its extra inputs
+    assert sample(lib, T=0.0) == EVALUE
+    assert sample(lib, T=-1.0) == EVALUE
+    assert sample(lib, T=float("inf")) == EVALUE
+    assert sample(lib, T=float("nan")) == EVALUE
+    assert sample(lib, q=None) == ENULL
+    assert sample(lib, u=None) == ENULL
+    assert sample(lib, u=FAKE + 2) == EALIGN
+    assert sample(lib, pd=FAKE + 1) == EALIGN
+    assert sample(lib, dtype=0, logits=FAKE + 2) == EALIGN      # fp32 needs 4-byte alignment
+    assert sample(lib, B=0, T=0.5, logits=None, q=None, d=None, u=None, out=None, acc=None,
+                  ws=None, wsb=0) == OK
+
+
+def build(lib, **kw):
+    a = dict(vo=FAKE, acc=FAKE, d=FAKE, L=FAKE, bt=FAKE, maxb=4, bs=16, th=FAKE, hs=FAKE,
+             hdt=1, mask=99, B=2, K=3, H=64, ids=FAKE, pos=FAKE, slots=FAKE, hid=FAKE,
+             sr=None, err=None)
+    a.update(kw)
+    return lib.peagle_build_draft_batch(a["vo"], a["acc"], a["d"], a["L"], a["bt"], a["maxb"],
+                                        a["bs"], a["th"], a["hs"], a["hdt"], a["mask"], a["B"],
+                                        a["K"], a["H"], a["ids"], a["pos"], a["slots"], a["hid"],
+                                        a["sr"], a["err"], None)
+
+
+def test_build_validation(lib):
+    assert build(lib, K=0) == ESHAPE
+    assert build(lib, K=64) == ESHAPE
+    assert build(lib, H=0) == ESHAPE
+    assert build(lib, bs=0) == ESHAPE
+    assert build(lib, maxb=0) == ESHAPE
+    assert build(lib, B=-3) == ESHAPE
+    assert build(lib, hdt=5) == EDTYPE
+    assert build(lib, B=0, vo=None, acc=None) == OK
+    for k in ("vo", "acc", "d", "L", "bt", "th", "hs", "ids", "pos", "slots", "hid"):
+        assert build(lib, **{k: None}) == ENULL, k
+    assert build(lib, L=FAKE + 4) == EALIGN            # int64 needs 8 bytes
+    assert build(lib, pos=FAKE + 4) == EALIGN
+    assert build(lib, slots=FAKE + 4) == EALIGN
+    assert build(lib, th=FAKE + 1) == EALIGN
+    assert build(lib, hdt=0, hid=FAKE + 2) == EALIGN   # fp32 hidden needs 4 bytes
+    assert build(lib, sr=FAKE + 2) == EALIGN
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    import draft_verification_vocab_amd as sv
+    z = torch.zeros(1, 4, 32)
+    d = torch.zeros(1, 3, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sv.spec_verify_greedy(z, d)
+
+
+def test_tracer_host_paths(lib):
+    import ctypes
+    assert lib.sv_trace_begin(0) == EVALUE          # rejected before any HIP call
+    assert lib.sv_trace_begin(-4) == EVALUE
+    assert lib.sv_trace_count() == 0
+    kid, ms = ctypes.c_int(), ctypes.c_float()
+    assert lib.sv_trace_read(0, ctypes.byref(kid), ctypes.byref(ms)) == EVALUE
+    assert lib.sv_trace_read(0, None, None) == ENULL
+    names = [lib.sv_kernel_name(i) for i in range(4)]
+    assert names == [b"verify_greedy", b"verify_sample_rows", b"verify_sample_draw", b"peagle_build"]
+    assert lib.sv_kernel_name(17) == b"unknown"
+    lib.sv_trace_end()                              # harmless when tracing is off
