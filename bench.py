@@ -38,7 +38,13 @@ def parse():
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
-                    help="run only this many untimed steps (for rocprofv3) and exit")
+                    help="run only this many untimed steps (for rocprofv3) and exit; inputs are "
+                         "then drawn in this process (no worker processes under a profiler)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE runs of --profile-steps) into the traffic record and exit")
+    ap.add_argument("--workers", type=int, default=None,
+                    help="processes drawing the synthetic inputs (default: one per core, up to 16)")
     return ap.parse_args()
 
 
@@ -114,8 +120,66 @@ def _oracle_loop(oracle, np, vi, bi, K, t0, budget_s):
     return done
 
 
+COPY_BYTES = 1 << 30           # the calibration copy of --profile-steps
+
+
+def ingest_counters(fetch_csv, write_csv):
+    """Per-kernel HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the 1 GiB copy
+    in the same run; writes the traffic record and a markdown summary."""
+    import csv
+    import collections
+
+    def load(path, counter):
+        per = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                per[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)
+        return per
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k][0]
+    f_scale = COPY_BYTES / max(fetch[copy])
+    w_scale = COPY_BYTES / max(write[copy])
+    kernels = {}
+    for name in fetch:
+        if not name.startswith(("void sv::", "sv::")):
+            continue
+        f = sum(fetch[name]) / len(fetch[name]) * f_scale
+        w = sum(write.get(name, [0.0])) / max(1, len(write.get(name, []))) * w_scale
+        kernels[name] = {"fetch_bytes": f, "write_bytes": w, "hbm_bytes_per_launch": f + w,
+                         "dispatches": len(fetch[name])}
+    dom = [k for k in kernels if "verify_rows<unsigned short, 1, true>" in k][0]
+    rec = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernel": dom, "hbm_bytes_per_launch": kernels[dom]["hbm_bytes_per_launch"],
+           "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    md = os.path.join(ROOT, "profiles", "hbm_counters_fused_b1024.md")
+    lines = ["# HBM bytes per launch from rocprofv3 counters: fused step, B=1024 K=7 V=151936 bf16, H=2048\n",
+             "Commands (one counter per run, from /tmp with TMPDIR=/tmp; profiler output under gpurun_out/):\n",
+             "```",
+             "timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $GRAFT_REPO_ROOT/gpurun_out/pmc_fetch -o fetch -- python3 $GRAFT_REPO_ROOT/bench.py --profile-steps 2",
+             "timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $GRAFT_REPO_ROOT/gpurun_out/pmc_write -o write -- python3 $GRAFT_REPO_ROOT/bench.py --profile-steps 2",
+             "python bench.py --ingest-counters gpurun_out/pmc_fetch/fetch_counter_collection.csv gpurun_out/pmc_write/write_counter_collection.csv",
+             "```\n",
+             f"Calibration (a plain 1 GiB device copy in the same runs): FETCH_SIZE x {f_scale:.4f}, "
+             f"WRITE_SIZE x {w_scale:.4f} give bytes.  Kernel source hash `{rec['source_hash']}`.\n",
+             "| kernel | dispatches | HBM read (GB) | HBM write (GB) | total (GB) |", "|---|---|---|---|---|"]
+    for name, k in kernels.items():
+        lines.append(f"| `{name}` | {k['dispatches']} | {k['fetch_bytes'] / 1e9:.4f} | "
+                     f"{k['write_bytes'] / 1e9:.4f} | {k['hbm_bytes_per_launch'] / 1e9:.4f} |")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"traffic_file": TRAFFIC_FILE, "summary": md,
+                      "dominant_hbm_bytes_per_launch": rec["hbm_bytes_per_launch"]}))
+
+
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence with no exchange; see DESIGN.md)", file=sys.stderr)
@@ -127,7 +191,8 @@ def main():
     # inputs are drawn before anything touches the GPU
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
     log("drawing inputs")
-    vi, bi = synth.make_fused_inputs()
+    workers = 1 if args.profile_steps else args.workers
+    vi, bi = synth.make_fused_inputs(workers=workers)
     log("inputs ready; uploading")
     B, K, V = vi.spec.B, vi.spec.K, vi.spec.V
     H = bi.spec.H
@@ -170,7 +235,12 @@ def main():
         for i in range(args.profile_steps):
             step(True); build(); step(False); build()
         torch.cuda.synchronize()
-        print(f"profiled {args.profile_steps} sampled and greedy steps", flush=True)
+        # calibration for HBM byte counters: one plain copy of 1 GiB
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"profiled {args.profile_steps} sampled and greedy steps and a 1 GiB copy", flush=True)
         return
 
     def timed(sample):
