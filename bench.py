@@ -59,22 +59,21 @@ def kernel_source_hash() -> str:
 
 
 def verify_bytes(B, K, V, zsize, acc, sample=True):
-    """Algorithmic HBM bytes of a verify call, split as (row kernel, draw kernel).
+    """Algorithmic HBM bytes of a verify call, split as (row kernel, scan kernel).
 
-    Row kernel: every logit row once, the draft tokens, the outputs, and for
-    sampling the q(d) / z(d) gathers, the test uniforms and p_k(d_k).  Draw
-    kernel (sampling): the drafter's row a_b of each sequence that rejects a
-    draft and the final uniforms; reading logit row a again is not counted."""
-    n = B * (K + 1) * V * zsize                      # logits, every row once
-    n += B * K * 4                                   # draft tokens
-    n += B * (K + 1) * 4 + B * 4                     # out_tokens, num_accepted
-    if not sample:
-        return n, 0
-    n += B * K * 4 * 2                               # q(d) and z(d) gathers
-    n += B * K * 4                                   # uniforms of the tests
-    n += B * K * 4                                   # p_k(d_k) output
-    draw = int((acc < K).sum()) * V * 4 + B * 4      # q row a_b of rejecting sequences, u[:, K]
-    return n, draw
+    Row kernel: every logit row once.  Scan kernel: the draft tokens, the
+    outputs, and for sampling the q(d) / z(d) gathers, the uniforms,
+    p_k(d_k) and the drafter's row a_b of each sequence that rejects a draft.
+    The draw's second read of logit row a is not counted: the method reads
+    every logit once."""
+    rows = B * (K + 1) * V * zsize
+    scan = B * K * 4 + B * (K + 1) * 4 + B * 4          # draft tokens, out_tokens, num_accepted
+    if sample:
+        scan += B * K * 4 * 2                           # q(d) and z(d) gathers
+        scan += B * (K + 1) * 4                         # uniforms
+        scan += B * K * 4                               # p_k(d_k) output
+        scan += int((acc < K).sum()) * V * 4            # q row a_b of rejecting sequences
+    return rows, scan
 
 
 def build_bytes(B, K, H, hsize):
@@ -247,7 +246,7 @@ def main():
         for _ in range(args.warmup):
             step(sample); build()
         torch.cuda.synchronize()
-        sv.trace_begin(3 * args.steps)
+        sv.trace_begin(4 * args.steps)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -293,8 +292,8 @@ def main():
         "kernels": {
             "verify_sample_rows": kinfo("verify_sample_rows", vb_rows),
             "verify_sample_draw": kinfo("verify_sample_draw", vb_draw,
-                                        "algorithmic bytes count the drafter rows only; the "
-                                        "kernel also re-reads logit row a"),
+                                        "accept scan + draw; algorithmic bytes count the drafter "
+                                        "rows and gathers; the kernel also re-reads logit row a"),
             "peagle_build": kinfo("peagle_build", bb),
         },
         "acceptance": {"mean_accepted": float(acc.mean()),
@@ -313,16 +312,17 @@ def main():
     log("sampled step timed")
     if not args.no_greedy:
         sec_g, kmsg, accg = timed(False)
-        vbg, _ = verify_bytes(B, K, V, 2, accg, sample=False)
-        g_ms = kmsg["verify_greedy"]
+        vg_rows, vg_scan = verify_bytes(B, K, V, 2, accg, sample=False)
+        g_ms = kmsg["verify_greedy_rows"]
         res["greedy_step"] = {"value": rows / sec_g, "unit": "verified logit rows/s",
                               "ms_per_step": sec_g * 1e3,
-                              "verify_greedy": {"avg_ms": g_ms, "algorithmic_bytes": vbg,
-                                                "gbs": vbg / (g_ms * 1e-3) / 1e9,
-                                                "frac": vbg / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                              "verify_greedy_rows": {"avg_ms": g_ms, "algorithmic_bytes": vg_rows,
+                                                     "gbs": vg_rows / (g_ms * 1e-3) / 1e9,
+                                                     "frac": vg_rows / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                              "verify_greedy_accept_ms": kmsg["verify_greedy_accept"],
                               "peagle_build_ms": kmsg["peagle_build"],
-                              "step_hbm_gbs": (vbg + bb) / sec_g / 1e9,
-                              "step_hbm_frac": (vbg + bb) / sec_g / 1e9 / HBM_PEAK_GBS}
+                              "step_hbm_gbs": (vg_rows + vg_scan + bb) / sec_g / 1e9,
+                              "step_hbm_frac": (vg_rows + vg_scan + bb) / sec_g / 1e9 / HBM_PEAK_GBS}
     if args.cpu_budget > 0:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(vi, bi, args.cpu_budget)

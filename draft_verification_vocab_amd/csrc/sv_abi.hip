@@ -75,10 +75,11 @@ SV_API const char* sv_status_string(int status) {
 
 SV_API const char* sv_kernel_name(int kernel_id) {
   switch (kernel_id) {
-    case SV_KERNEL_VERIFY_GREEDY: return "verify_greedy";
+    case SV_KERNEL_VERIFY_GREEDY_ROWS: return "verify_greedy_rows";
     case SV_KERNEL_VERIFY_SAMPLE_ROWS: return "verify_sample_rows";
     case SV_KERNEL_VERIFY_SAMPLE_DRAW: return "verify_sample_draw";
     case SV_KERNEL_PEAGLE_BUILD: return "peagle_build";
+    case SV_KERNEL_VERIFY_GREEDY_ACCEPT: return "verify_greedy_accept";
     default: return "unknown";
   }
 }

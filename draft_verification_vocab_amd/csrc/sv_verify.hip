@@ -1,22 +1,20 @@
 // Batched speculative verify-and-accept for gfx950.
 //
-// Kernel 1 (verify_rows): one workgroup per (sequence b, logit row k,
-// vocabulary split s), sequence-major.  Each workgroup streams its slice of
-// row k from HBM once and reduces it to a partial: the max and its lowest
-// index (greedy), or the max and the sum of exponentials relative to it
-// (sampling).  The last workgroup of a sequence to arrive (a per-sequence
-// ticket) combines the partials of the K+1 rows, tests every draft in
-// parallel (one lane per row), takes the first rejection from a wave ballot
-// and writes the accepted prefix.  Greedy: it also writes the argmax of row a
-// and the step is done.  Sampling: it leaves (a, max, sum) of row a for
-// kernel 2.
+// verify_rows: one workgroup per (sequence b, logit row k, vocabulary split
+// s).  Each workgroup streams its slice of row k from HBM once and reduces it
+// to a partial: the max and its lowest index (greedy), or the max and the sum
+// of exponentials relative to it (sampling).  Nothing else: no workgroup of
+// this kernel waits for or hands anything to another.
 //
-// Kernel 2 (verify_draw, sampling only): C workgroups per sequence each take
-// a contiguous chunk of row a, compute the mass r = max(0, p_a - q_a) (or p_K
-// for the bonus token) of each 512-element tile in it, and publish the tile
-// masses and the chunk total.  The last chunk to arrive finds the chunk, then
-// the tile, whose running total first exceeds u * S, rescans that one tile
-// and writes the token.
+// The accept scan (one wave per sequence, one lane per row) combines a
+// sequence's partials, tests every draft in parallel and takes the first
+// rejection from a wave ballot.  Greedy: verify_accept runs it and writes the
+// argmax of row a as the new token.  Sampling: each of the C workgroups of
+// verify_draw that share a sequence runs it (a few dozen loads), then takes a
+// contiguous chunk of row a and computes the mass r = max(0, p_a - q_a) (or
+// p_K for the bonus token) of each 512-element tile in it.  The last chunk to
+// arrive (a per-sequence ticket) finds the chunk, then the tile, whose running
+// total first exceeds u * S, rescans that one tile and writes the token.
 //
 // The verify flow is that of "Project 14 - speculative decoding inference
 // server", section 架构 (architecture): accept the prefix, resample the
@@ -36,10 +34,11 @@ struct Partial {
   double acc;    // sampling: sum over the slice of 2^((z - m) * c)
 };
 
-struct DrawInfo {  // row a of a sequence, handed from kernel 1 to kernel 2
-  int a;
-  float M;         // max of row a
-  double s;        // sum over row a of 2^((z - M) * c)
+struct ScanResult {  // outcome of a sequence's accept scan
+  int a;             // accepted drafts
+  int g_a;           // greedy: argmax of row a
+  float M_a;         // max of row a
+  double s_a;        // sampling: sum over row a of 2^((z - M_a) * c)
 };
 
 constexpr int kThreads = 256;           // 4 waves
@@ -50,9 +49,9 @@ constexpr int kTileUnroll = 4;          // draw: tiles per wave per step
 enum Mode { GREEDY = 0, SAMPLE = 1 };
 
 // ---------------------------------------------------------------- workspace
-// tickets [B] | tickets2 [B] | info [B] | chunk sums [B][C] | tile sums [B][T] | partials [B][K+1][S]
+// tickets [B] | chunk sums [B][C] | tile sums [B][T] | partials [B][K+1][S]
 struct Layout {
-  size_t tickets, tickets2, info, chunk, tile, partials, total;
+  size_t tickets, chunk, tile, partials, total;
   int S, C, T;
 };
 
@@ -82,8 +81,6 @@ static Layout layout(int B, int K, int V) {
   L.T = (V + kTile - 1) / kTile;
   size_t off = 0;
   L.tickets = off;  off = align256(off + (size_t)B * sizeof(int));
-  L.tickets2 = off; off = align256(off + (size_t)B * sizeof(int));
-  L.info = off;     off = align256(off + (size_t)B * sizeof(DrawInfo));
   L.chunk = off;    off = align256(off + (size_t)B * L.C * sizeof(double));
   L.tile = off;     off = align256(off + (size_t)B * L.T * sizeof(float));
   L.partials = off; off = align256(off + (size_t)B * (K + 1) * L.S * sizeof(Partial));
@@ -95,30 +92,30 @@ size_t verify_workspace_bytes(int B, int K, int V) { return layout(B, K, V).tota
 
 struct RowsArgs {
   const void* logits;
+  float c;                 // log2(e) / T   (sampling)
+  int K, V, S;
+  long octets;             // ceil(V / 8)
+  Partial* partials;       // [B][K+1][S]
+};
+
+struct ScanArgs {          // what an accept scan reads and writes
+  const void* logits;
   const float* draft_probs;
   const int32_t* draft_tokens;
   const float* uniforms;
-  float c;                 // log2(e) / T   (sampling)
+  float c;
   int B, K, V, S;
-  long octets;             // ceil(V / 8)
+  Partial* partials;       // [B][K+1][S]
   int32_t* out_tokens;
   int32_t* out_num_accepted;
   float* out_p_draft;
-  Partial* partials;       // [B][K+1][S]
-  int* tickets;            // [B]
-  DrawInfo* info;          // [B]
   int32_t* device_error;
 };
 
 struct DrawArgs {
-  const void* logits;
-  const float* draft_probs;
-  const float* uniforms;
-  float c;
-  int B, K, V, C, T;
-  int32_t* out_tokens;
-  DrawInfo* info;          // [B]
-  int* tickets2;           // [B]
+  ScanArgs sc;
+  int C, T;
+  int* tickets;            // [B]
   double* chunk_sums;      // [B][C]
   float* tile_sums;        // [B][T]
 };
@@ -280,67 +277,54 @@ __global__ __launch_bounds__(kThreads) void verify_rows(RowsArgs A) {
   __shared__ float sm_f[kWaves];
   __shared__ int sm_i[kWaves];
   __shared__ double sm_d[kWaves];
-  __shared__ int sm_last;
 
-  const int K = A.K, S = A.S;
+  const int S = A.S;
   const long V = A.V;
   const long unit = blockIdx.x;                 // ((b * (K+1)) + k) * S + s
   const int s = (int)(unit % S);
   const long rowi = unit / S;                   // b * (K+1) + k
-  const int b = (int)(rowi / (K + 1));
   const LT* row = static_cast<const LT*>(A.logits) + rowi * V;
   const long o_lo = (long)s * A.octets / S, o_hi = (long)(s + 1) * A.octets / S;
 
   const Partial P = slice_stats<LT, MODE, VEC>(row, o_lo, o_hi, V, A.c, sm_f, sm_i, sm_d);
+  if (threadIdx.x == 0) A.partials[unit] = P;   // read by the next kernel
+}
 
-  // ---- publish the partial, then take the per-sequence ticket
-  if (threadIdx.x == 0) {
-    Partial* dst = &A.partials[unit];
-    st_coherent(&dst->m, P.m);
-    st_coherent(&dst->g, P.g);
-    st_coherent(&dst->acc, P.acc);
-    wait_stores_performed();
-    const int prev = take_ticket(&A.tickets[b]);
-    sm_last = (prev == (K + 1) * S - 1);
-  }
-  __syncthreads();
-  if (!sm_last || threadIdx.x >= kWave) return;
-
-  // ---- the last workgroup of sequence b (one wave): combine, test, scan, write
-  const int l = lane_id();
-  Partial* Pb = A.partials + (long)b * (K + 1) * S;
-  const int k = l;
+// ----------------------------------------------------------------------------
+// Accept scan of sequence b by one full wave (lane k holds row k <= K).
+// Combines the S partials of each row, tests every draft, finds the first
+// rejection with a ballot.  With `write` it writes the accepted prefix, the
+// -1 padding, num_accepted and p_k(d_k); the new token is written by the
+// caller (greedy: g_a; sampling: the draw).
+template <typename LT, int MODE>
+__device__ ScanResult accept_scan(const ScanArgs& A, int b, bool write) {
+  const int K = A.K, S = A.S;
+  const long V = A.V;
+  const int k = lane_id();
+  const Partial* Pb = A.partials + (long)b * (K + 1) * S;
   float M = -INFINITY;
   int g = INT32_MAX;
   double s_k = 0.0;
   if (k <= K) {
     if constexpr (MODE == GREEDY) {
       for (int j = 0; j < S; ++j) {
-        const float pm = ld_coherent(&Pb[k * S + j].m);
-        const int pg = ld_coherent(&Pb[k * S + j].g);
-        if (j == 0 || pm > M) { M = pm; g = pg; }
+        const Partial p = Pb[k * S + j];
+        if (j == 0 || p.m > M) { M = p.m; g = p.g; }
       }
     } else {
-      for (int j = 0; j < S; ++j) M = fmaxf(M, ld_coherent(&Pb[k * S + j].m));
+      for (int j = 0; j < S; ++j) M = fmaxf(M, Pb[k * S + j].m);
       for (int j = 0; j < S; ++j) {
-        const float pm = ld_coherent(&Pb[k * S + j].m);
-        const double pacc = ld_coherent(&Pb[k * S + j].acc);
-        if (pacc != 0.0) s_k += pacc * exp2(((double)pm - (double)M) * (double)A.c);
+        const Partial p = Pb[k * S + j];
+        if (p.acc != 0.0) s_k += p.acc * exp2(((double)p.m - (double)M) * (double)A.c);
       }
-    }
-    // the partials are consumed: clear them so the workspace ends all zero
-    for (int j = 0; j < S; ++j) {
-      st_coherent(&Pb[k * S + j].m, 0.f);
-      st_coherent(&Pb[k * S + j].g, 0);
-      st_coherent(&Pb[k * S + j].acc, 0.0);
     }
   }
   int d = -1;
   bool rej = false;
+  float pdraft = 0.f;
   if (k < K) {
     d = A.draft_tokens[(long)b * K + k];
     const bool valid = d >= 0 && d < V;
-    if (!valid) flag_error(A.device_error, SV_DEVERR_DRAFT_TOKEN);
     if constexpr (MODE == GREEDY) {
       rej = !(valid && d == g);
     } else {
@@ -355,23 +339,35 @@ __global__ __launch_bounds__(kThreads) void verify_rows(RowsArgs A) {
       } else {
         rej = true;
       }
-      if (A.out_p_draft) A.out_p_draft[(long)b * K + k] = (float)px;
+      pdraft = (float)px;
     }
+    if (write && !valid) flag_error(A.device_error, SV_DEVERR_DRAFT_TOKEN);
   }
   const unsigned long long rejmask = __ballot(k < K && rej);
-  const int a = rejmask ? __ffsll((long long)rejmask) - 1 : K;
-  const int gA = __shfl(g, a);
-  const float Ma = __shfl(M, a);
-  const double sa = __shfl(s_k, a);
-  if (k <= K) {
-    const int tok = k < a ? d : (k == a && MODE == GREEDY ? gA : -1);
-    A.out_tokens[(long)b * (K + 1) + k] = tok;
+  ScanResult r;
+  r.a = rejmask ? __ffsll((long long)rejmask) - 1 : K;
+  r.g_a = __shfl(g, r.a);
+  r.M_a = __shfl(M, r.a);
+  r.s_a = __shfl(s_k, r.a);
+  if (write) {
+    if (k <= K && k != r.a) A.out_tokens[(long)b * (K + 1) + k] = k < r.a ? d : -1;
+    if (k == 0) A.out_num_accepted[b] = r.a;
+    if (MODE == SAMPLE && k < K && A.out_p_draft) A.out_p_draft[(long)b * K + k] = pdraft;
   }
-  if (l == 0) {
-    A.out_num_accepted[b] = a;
-    if constexpr (MODE == SAMPLE) A.info[b] = DrawInfo{a, Ma, sa};
-    st_coherent(&A.tickets[b], 0);     // leave the ticket cleared for the next call
-  }
+  return r;
+}
+
+// Greedy: one wave per sequence runs the accept scan and writes g_a.
+template <typename LT>
+__global__ __launch_bounds__(kThreads) void verify_accept(ScanArgs A) {
+  const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (b >= A.B) return;
+  const ScanResult r = accept_scan<LT, GREEDY>(A, b, true);
+  const int l = lane_id();
+  if (l == 0) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
+  // the partials are consumed: clear them so the workspace ends all zero
+  Partial* Pb = A.partials + (long)b * (A.K + 1) * A.S;
+  for (int i = l; i < (A.K + 1) * A.S; i += kWave) Pb[i] = Partial{0.f, 0, 0.0};
 }
 
 // ----------------------------------------------------------------------------
@@ -470,19 +466,26 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
   __shared__ int sm_last;
   __shared__ int sm_pick;
   __shared__ int sm_redo;
+  __shared__ ScanResult sm_scan;
 
-  const int C = A.C, T = A.T, K = A.K;
+  const int C = A.C, T = A.T, K = A.sc.K;
   const int b = blockIdx.x / C, cidx = blockIdx.x % C;
-  const long V = A.V;
-  const DrawInfo di = A.info[b];
-  const int a = di.a;
-  const LT* zrow = static_cast<const LT*>(A.logits) + ((long)b * (K + 1) + a) * V;
-  const float* qrow = a < K ? A.draft_probs + ((long)b * K + a) * V : nullptr;
-  const float c = A.c;
+  const long V = A.sc.V;
+  // every chunk of the sequence runs the accept scan; chunk 0 writes its outputs
+  if (threadIdx.x < kWave) {
+    const ScanResult r = accept_scan<LT, SAMPLE>(A.sc, b, cidx == 0);
+    if (threadIdx.x == 0) sm_scan = r;
+  }
+  __syncthreads();
+  const int a = sm_scan.a;
+  const LT* zrow = static_cast<const LT*>(A.sc.logits) + ((long)b * (K + 1) + a) * V;
+  const float* qrow = a < K ? A.sc.draft_probs + ((long)b * K + a) * V : nullptr;
+  const float c = A.sc.c;
   // p = 2^(z*c - M*c) / s.  Mc32 is M*c rounded to fp32; the rounding is
   // folded into the scale so that p keeps the fp64 reference exactly.
-  const float Mc32 = di.M * c;
-  const float inv_s = (float)(exp2((double)Mc32 - (double)di.M * (double)c) / di.s);
+  const float M = sm_scan.M_a;
+  const float Mc32 = M * c;
+  const float inv_s = (float)(exp2((double)Mc32 - (double)M * (double)c) / sm_scan.s_a);
   float* tsum_g = A.tile_sums + (long)b * T;
   double* csum_g = A.chunk_sums + (long)b * C;
   bool residual = qrow != nullptr;
@@ -493,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
   if (threadIdx.x == 0) {
     st_coherent(&csum_g[cidx], mine);
     wait_stores_performed();
-    sm_last = take_ticket(&A.tickets2[b]) == C - 1;
+    sm_last = take_ticket(&A.tickets[b]) == C - 1;
   }
   __syncthreads();
   if (!sm_last) return;
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
     for (int i = lo; i < hi; ++i) part += ld_coherent(&csum_g[i]);
     const double incl = wave_inclusive_scan(part);
     const double S = __shfl(incl, kWave - 1);
-    const double target = (double)A.uniforms[(long)b * (K + 1) + K] * S;
+    const double target = (double)A.sc.uniforms[(long)b * (K + 1) + K] * S;
     double run = __shfl_up(incl, 1);
     if (l == 0) run = 0.0;
     int hit = -1;
@@ -622,14 +625,14 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
     if (l == 0) sm_pick = pick;
   }
   __syncthreads();
-  if (threadIdx.x == 0) A.out_tokens[(long)b * (K + 1) + a] = sm_pick;
-  // leave this sequence's part of the workspace cleared
+  if (threadIdx.x == 0) A.sc.out_tokens[(long)b * (K + 1) + a] = sm_pick;
+  // leave this sequence's part of the workspace cleared (every chunk has
+  // already read the partials: it took its ticket after its accept scan)
+  Partial* Pb = A.sc.partials + (long)b * (K + 1) * A.sc.S;
+  for (int i = threadIdx.x; i < (K + 1) * A.sc.S; i += kThreads) Pb[i] = Partial{0.f, 0, 0.0};
   for (int i = threadIdx.x; i < T; i += kThreads) st_coherent(&tsum_g[i], 0.f);
   for (int i = threadIdx.x; i < C; i += kThreads) st_coherent(&csum_g[i], 0.0);
-  if (threadIdx.x == 0) {
-    st_coherent(&A.tickets2[b], 0);
-    A.info[b] = DrawInfo{0, 0.f, 0.0};
-  }
+  if (threadIdx.x == 0) st_coherent(&A.tickets[b], 0);
 }
 
 // ----------------------------------------------------------------------------
@@ -637,24 +640,16 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   const Layout lay = layout(L.B, L.K, L.V);
   char* ws = static_cast<char*>(L.workspace);
   const float c = L.sample ? (float)(1.4426950408889634 / (double)L.temperature) : 1.0f;
+  Partial* partials = reinterpret_cast<Partial*>(ws + lay.partials);
+  const dim3 block(kThreads);
 
   RowsArgs R;
   R.logits = L.logits;
-  R.draft_probs = L.draft_probs;
-  R.draft_tokens = L.draft_tokens;
-  R.uniforms = L.uniforms;
   R.c = c;
-  R.B = L.B; R.K = L.K; R.V = L.V; R.S = lay.S;
+  R.K = L.K; R.V = L.V; R.S = lay.S;
   R.octets = (L.V + 7) / 8;
-  R.out_tokens = L.out_tokens;
-  R.out_num_accepted = L.out_num_accepted;
-  R.out_p_draft = L.out_p_draft;
-  R.partials = reinterpret_cast<Partial*>(ws + lay.partials);
-  R.tickets = reinterpret_cast<int*>(ws + lay.tickets);
-  R.info = reinterpret_cast<DrawInfo*>(ws + lay.info);
-  R.device_error = L.device_error;
-  const dim3 grid1((unsigned)((long)L.B * (L.K + 1) * lay.S)), block(kThreads);
-  const int kid1 = L.sample ? SV_KERNEL_VERIFY_SAMPLE_ROWS : SV_KERNEL_VERIFY_GREEDY;
+  R.partials = partials;
+  const dim3 grid1((unsigned)((long)L.B * (L.K + 1) * lay.S));
   trace_before(stream);
 #define SV_ROWS(LT, MODE, VEC) hipLaunchKernelGGL((verify_rows<LT, MODE, VEC>), grid1, block, 0, stream, R)
   if (L.bf16) {
@@ -666,18 +661,36 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   }
 #undef SV_ROWS
   hipError_t err = hipGetLastError();
-  trace_after(stream, kid1);
-  if (err != hipSuccess || !L.sample) return err;
+  trace_after(stream, L.sample ? SV_KERNEL_VERIFY_SAMPLE_ROWS : SV_KERNEL_VERIFY_GREEDY_ROWS);
+  if (err != hipSuccess) return err;
+
+  ScanArgs sc;
+  sc.logits = L.logits;
+  sc.draft_probs = L.draft_probs;
+  sc.draft_tokens = L.draft_tokens;
+  sc.uniforms = L.uniforms;
+  sc.c = c;
+  sc.B = L.B; sc.K = L.K; sc.V = L.V; sc.S = lay.S;
+  sc.partials = partials;
+  sc.out_tokens = L.out_tokens;
+  sc.out_num_accepted = L.out_num_accepted;
+  sc.out_p_draft = L.out_p_draft;
+  sc.device_error = L.device_error;
+
+  if (!L.sample) {
+    const dim3 grid2((unsigned)((L.B + kWaves - 1) / kWaves));
+    trace_before(stream);
+    if (L.bf16) hipLaunchKernelGGL((verify_accept<uint16_t>), grid2, block, 0, stream, sc);
+    else hipLaunchKernelGGL((verify_accept<float>), grid2, block, 0, stream, sc);
+    err = hipGetLastError();
+    trace_after(stream, SV_KERNEL_VERIFY_GREEDY_ACCEPT);
+    return err;
+  }
 
   DrawArgs D;
-  D.logits = L.logits;
-  D.draft_probs = L.draft_probs;
-  D.uniforms = L.uniforms;
-  D.c = c;
-  D.B = L.B; D.K = L.K; D.V = L.V; D.C = lay.C; D.T = lay.T;
-  D.out_tokens = L.out_tokens;
-  D.info = R.info;
-  D.tickets2 = reinterpret_cast<int*>(ws + lay.tickets2);
+  D.sc = sc;
+  D.C = lay.C; D.T = lay.T;
+  D.tickets = reinterpret_cast<int*>(ws + lay.tickets);
   D.chunk_sums = reinterpret_cast<double*>(ws + lay.chunk);
   D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
   const dim3 grid2((unsigned)((long)L.B * lay.C));

@@ -101,7 +101,8 @@ SV_API size_t spec_verify_workspace_bytes(int B, int K, int V);
  *   workspace        spec_verify_workspace_bytes(B, K, V) bytes (see above).
  * Ties: the lowest index wins.  NaN logits, or a row of only -inf, give an
  * unspecified but in-range token.  B = 0 is a no-op.  1 <= V <= SV_MAX_V,
- * 0 <= K <= SV_MAX_K.
+ * 0 <= K <= SV_MAX_K.  Two kernels are enqueued: row statistics, then the
+ * accept scan.
  */
 SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
                                     const int32_t* draft_tokens,
@@ -131,7 +132,7 @@ SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
  * Arithmetic: fp32 exponentials, fp64 accumulation of every sum and of the
  * acceptance ratio; results agree with an fp64 evaluation except when a
  * decision lies within ~1e-6 of its threshold.  Two kernels are enqueued:
- * row statistics with the accept scan, then the draw of the new token.
+ * row statistics, then the accept scan with the draw of the new token.
  */
 SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
                                     const float* draft_probs,
@@ -193,10 +194,11 @@ SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,
  * creates the events (it may be called again to start over); sv_trace_end
  * destroys them.  Tracing adds two event records per launch and nothing else.
  */
-#define SV_KERNEL_VERIFY_GREEDY 0       /* spec_verify_greedy                         */
-#define SV_KERNEL_VERIFY_SAMPLE_ROWS 1  /* spec_verify_sample: row stats, accept scan */
-#define SV_KERNEL_VERIFY_SAMPLE_DRAW 2  /* spec_verify_sample: residual / bonus draw  */
-#define SV_KERNEL_PEAGLE_BUILD 3        /* peagle_build_draft_batch                   */
+#define SV_KERNEL_VERIFY_GREEDY_ROWS 0   /* spec_verify_greedy: row max / argmax         */
+#define SV_KERNEL_VERIFY_SAMPLE_ROWS 1   /* spec_verify_sample: row max / sum of exp     */
+#define SV_KERNEL_VERIFY_SAMPLE_DRAW 2   /* spec_verify_sample: accept scan + draw       */
+#define SV_KERNEL_PEAGLE_BUILD 3         /* peagle_build_draft_batch                     */
+#define SV_KERNEL_VERIFY_GREEDY_ACCEPT 4 /* spec_verify_greedy: accept scan              */
 
 SV_API const char* sv_kernel_name(int kernel_id);
 SV_API sv_status sv_trace_begin(int capacity);       /* SV_ERR_VALUE if capacity < 1   */

@@ -174,7 +174,8 @@ def test_tracer_host_paths(lib):
     kid, ms = ctypes.c_int(), ctypes.c_float()
     assert lib.sv_trace_read(0, ctypes.byref(kid), ctypes.byref(ms)) == EVALUE
     assert lib.sv_trace_read(0, None, None) == ENULL
-    names = [lib.sv_kernel_name(i) for i in range(4)]
-    assert names == [b"verify_greedy", b"verify_sample_rows", b"verify_sample_draw", b"peagle_build"]
+    names = [lib.sv_kernel_name(i) for i in range(5)]
+    assert names == [b"verify_greedy_rows", b"verify_sample_rows", b"verify_sample_draw",
+                     b"peagle_build", b"verify_greedy_accept"]
     assert lib.sv_kernel_name(17) == b"unknown"
     lib.sv_trace_end()                              # harmless when tracing is off
