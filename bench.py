@@ -246,7 +246,7 @@ def main():
         for _ in range(args.warmup):
             step(sample); build()
         torch.cuda.synchronize()
-        sv.trace_begin(4 * args.steps)
+        sv.trace_begin(5 * args.steps)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -291,9 +291,10 @@ def main():
         "step_bytes": vb_rows + vb_draw + bb,
         "kernels": {
             "verify_sample_rows": kinfo("verify_sample_rows", vb_rows),
-            "verify_sample_draw": kinfo("verify_sample_draw", vb_draw,
-                                        "accept scan + draw; algorithmic bytes count the drafter "
-                                        "rows and gathers; the kernel also re-reads logit row a"),
+            "verify_sample_accept": kinfo("verify_sample_accept", vb_draw - int((acc < K).sum()) * V * 4),
+            "verify_sample_draw": kinfo("verify_sample_draw", int((acc < K).sum()) * V * 4,
+                                        "algorithmic bytes count the drafter rows a_b; the kernel "
+                                        "also re-reads logit row a"),
             "peagle_build": kinfo("peagle_build", bb),
         },
         "acceptance": {"mean_accepted": float(acc.mean()),

@@ -80,6 +80,7 @@ SV_API const char* sv_kernel_name(int kernel_id) {
     case SV_KERNEL_VERIFY_SAMPLE_DRAW: return "verify_sample_draw";
     case SV_KERNEL_PEAGLE_BUILD: return "peagle_build";
     case SV_KERNEL_VERIFY_GREEDY_ACCEPT: return "verify_greedy_accept";
+    case SV_KERNEL_VERIFY_SAMPLE_ACCEPT: return "verify_sample_accept";
     default: return "unknown";
   }
 }

@@ -1,113 +1,184 @@
 // P-EAGLE parallel-draft batch construction for gfx950.
 //
-// One wavefront per output row of the drafter batch (2K rows per sequence),
-// four rows per workgroup.  Every lane derives the row's role from the
-// sequence's accept count (a handful of scalar loads that hit the same
-// addresses), lane 0 writes the row's token id, position and KV slot, and the
-// whole wave copies the row's hidden state (a target hidden row, or h_shared
-// for MASK rows) with 16-byte loads and stores.  Fusing the metadata rebuild
-// with the hidden copy is one launch instead of the separate copy / scatter /
-// insert / pad / mask / remap operations and the dedicated broadcast copy that
-// the P-EAGLE / TorchSpec blog summary describes (section TorchSpec 集成与工程优化).
-// Row layout (per sequence, a = accepted drafts, K drafts):
+// Per sequence (a accepted drafts, K drafts, new token c, verify slot 0 at
+// position L) the drafter batch has 2K rows:
 //   0..a-1 accepted, a NTP, a+1..a+K-1 MASK, a+K..2K-1 rejected (slot -1).
+// Every target hidden row h[i] (i = 0..K) lands in exactly one output row:
+// row i when i <= a (accepted or NTP), row i+K-1 when i > a (rejected), and
+// in every case at position L+i.  h_shared fills the K-1 MASK rows.
+//
+// One wavefront per source row (b, i), four per workgroup.  The wave starts
+// loading h[i] (and h_shared when 1 <= i <= K-1) before it knows a, so the
+// hidden-row loads overlap the metadata loads; then it stores h[i] into its
+// output row and, for 1 <= i <= K-1, h_shared into MASK row a+i, and lanes 0
+// and 1 write those rows' token id, position and KV slot.  Fusing the
+// metadata rebuild with the hidden copy is one launch instead of the separate
+// copy / scatter / insert / pad / mask / remap operations and the dedicated
+// broadcast copy that the P-EAGLE / TorchSpec blog summary describes (section
+// TorchSpec 集成与工程优化).
 #include "sv_device.h"
 #include "sv_internal.h"
 
 namespace sv {
 
 constexpr int kBuildThreads = 256;
-constexpr int kRowsPerBlock = kBuildThreads / kWave;
+constexpr int kWavesPerBlock = kBuildThreads / kWave;
+constexpr int kCopyUnroll = 8;          // 16-byte vectors per lane per step
 
 struct BuildArgs {
   BuildLaunch L;
-  long rows;   // B * 2K
+  long units;   // B * (K+1) source rows
 };
 
-__device__ __forceinline__ void copy_row(const void* src, void* dst, long row_bytes, bool vec,
-                                         int elem_bytes) {
-  const int l = lane_id();
-  if (vec) {
-    const u32x4* s = static_cast<const u32x4*>(src);
-    u32x4* d = static_cast<u32x4*>(dst);
-    const long n = row_bytes / 16;
-    for (long i = l; i < n; i += kWave) d[i] = s[i];
-  } else if (elem_bytes == 4) {
-    const uint32_t* s = static_cast<const uint32_t*>(src);
-    uint32_t* d = static_cast<uint32_t*>(dst);
-    for (long i = l; i < row_bytes / 4; i += kWave) d[i] = s[i];
-  } else {
-    const uint16_t* s = static_cast<const uint16_t*>(src);
-    uint16_t* d = static_cast<uint16_t*>(dst);
-    for (long i = l; i < row_bytes / 2; i += kWave) d[i] = s[i];
-  }
+__device__ __forceinline__ int64_t kv_slot(const BuildLaunch& L, int b, int64_t pos) {
+  const int64_t blk = pos / L.block_size;
+  const bool ok = pos >= 0 && blk < L.max_blocks;
+  const int32_t page = ok ? L.block_table[(long)b * L.max_blocks + blk] : -1;
+  if (ok && page >= 0) return (int64_t)page * L.block_size + pos % L.block_size;
+  flag_error(L.device_error, SV_DEVERR_BLOCK_TABLE);
+  return SV_PADDING_SLOT_ID;
 }
 
 __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs A) {
   const BuildLaunch& L = A.L;
-  const long row = (long)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-  if (row >= A.rows) return;
+  const long unit = (long)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (unit >= A.units) return;
   const int K = L.K;
-  const int b = (int)(row / (2 * K));
-  const int i = (int)(row % (2 * K));
+  const int b = (int)(unit / (K + 1));
+  const int i = (int)(unit % (K + 1));
+  const int l = lane_id();
+  const bool mask_row = i >= 1 && i <= K - 1;   // this wave also writes MASK row a+i
+  const long row_bytes = (long)L.H * L.elem_bytes;
+  const char* src = static_cast<const char*>(L.target_hidden) + unit * row_bytes;
+  const char* hs = static_cast<const char*>(L.h_shared);
+  char* out = static_cast<char*>(L.out_hidden);
+  const long base_row = (long)b * 2 * K;
+
+  if (L.vec) {
+    const long nvec = row_bytes / 16;
+    const u32x4* s = reinterpret_cast<const u32x4*>(src);
+    const u32x4* h = reinterpret_cast<const u32x4*>(hs);
+    // first step's loads go out before the accept count is known
+    u32x4 vs[kCopyUnroll], vh[kCopyUnroll];
+#pragma unroll
+    for (int j = 0; j < kCopyUnroll; ++j) {
+      const long e = l + (long)j * kWave;
+      if (e < nvec) {
+        vs[j] = s[e];
+        if (mask_row) vh[j] = h[e];
+      }
+    }
+    int a = L.num_accepted[b];
+    if (a < 0 || a > K) {
+      if (l == 0 && i == 0) flag_error(L.device_error, SV_DEVERR_ACCEPT_COUNT);
+      a = a < 0 ? 0 : K;
+    }
+    const long dst_row = base_row + (i <= a ? i : i + K - 1);
+    u32x4* d = reinterpret_cast<u32x4*>(out + dst_row * row_bytes);
+    u32x4* dm = reinterpret_cast<u32x4*>(out + (base_row + a + i) * row_bytes);
+    for (long e0 = 0;; e0 += (long)kCopyUnroll * kWave) {
+#pragma unroll
+      for (int j = 0; j < kCopyUnroll; ++j) {
+        const long e = e0 + l + (long)j * kWave;
+        if (e < nvec) {
+          d[e] = vs[j];
+          if (mask_row) dm[e] = vh[j];
+        }
+      }
+      const long next = e0 + (long)kCopyUnroll * kWave;
+      if (next >= nvec) break;
+#pragma unroll
+      for (int j = 0; j < kCopyUnroll; ++j) {
+        const long e = next + l + (long)j * kWave;
+        if (e < nvec) {
+          vs[j] = s[e];
+          if (mask_row) vh[j] = h[e];
+        }
+      }
+    }
+    if (l < 2) {
+      // lanes 0 / 1: metadata of the source row / of the MASK row
+      const int64_t Lpos = L.start_pos[b];
+      if (l == 0) {
+        int token;
+        int64_t slot;
+        if (i <= a) {
+          token = L.verify_out_tokens[(long)b * (K + 1) + i];
+          slot = kv_slot(L, b, Lpos + i);
+        } else {
+          token = L.draft_tokens[(long)b * K + i - 1];
+          slot = SV_PADDING_SLOT_ID;
+        }
+        L.out_input_ids[dst_row] = token;
+        L.out_positions[dst_row] = Lpos + i;
+        L.out_slot_mapping[dst_row] = slot;
+      } else if (mask_row) {
+        const long mrow = base_row + a + i;
+        L.out_input_ids[mrow] = L.mask_token_id;
+        L.out_positions[mrow] = Lpos + a + i;
+        L.out_slot_mapping[mrow] = kv_slot(L, b, Lpos + a + i);
+      }
+    }
+    if (L.out_sample_rows && i == 0 && l < K)
+      L.out_sample_rows[(long)b * K + l] = (int32_t)(base_row + a + l);
+    return;
+  }
+
+  // element-wise path (rows not a multiple of 16 bytes, or unaligned)
   int a = L.num_accepted[b];
   if (a < 0 || a > K) {
-    if (lane_id() == 0 && i == 0) flag_error(L.device_error, SV_DEVERR_ACCEPT_COUNT);
+    if (l == 0 && i == 0) flag_error(L.device_error, SV_DEVERR_ACCEPT_COUNT);
     a = a < 0 ? 0 : K;
   }
-  const int64_t Lpos = L.start_pos[b];
-  // role of row i
-  int token;
-  int64_t pos;
-  int hslot;        // verify slot whose hidden row is copied; -1 = h_shared
-  bool pad = false;
-  if (i < a) {
-    token = L.verify_out_tokens[(long)b * (K + 1) + i];
-    pos = Lpos + i;
-    hslot = i;
-  } else if (i == a) {
-    token = L.verify_out_tokens[(long)b * (K + 1) + a];
-    pos = Lpos + a;
-    hslot = a;
-  } else if (i < a + K) {
-    token = L.mask_token_id;
-    pos = Lpos + i;
-    hslot = -1;
-  } else {
-    const int j = i - a - K;
-    token = L.draft_tokens[(long)b * K + a + j];
-    pos = Lpos + a + 1 + j;
-    hslot = a + 1 + j;
-    pad = true;
-  }
-  if (lane_id() == 0) {
-    int64_t slot = SV_PADDING_SLOT_ID;
-    if (!pad) {
-      const int64_t blk = pos / L.block_size;
-      bool okb = pos >= 0 && blk < L.max_blocks;
-      int32_t page = okb ? L.block_table[(long)b * L.max_blocks + blk] : -1;
-      if (okb && page >= 0) slot = (int64_t)page * L.block_size + pos % L.block_size;
-      else flag_error(L.device_error, SV_DEVERR_BLOCK_TABLE);
+  const long dst_row = base_row + (i <= a ? i : i + K - 1);
+  const long mrow = base_row + a + i;
+  if (L.elem_bytes == 4) {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+    const uint32_t* h = reinterpret_cast<const uint32_t*>(hs);
+    uint32_t* d = reinterpret_cast<uint32_t*>(out + dst_row * row_bytes);
+    uint32_t* dm = reinterpret_cast<uint32_t*>(out + mrow * row_bytes);
+    for (long e = l; e < L.H; e += kWave) {
+      d[e] = s[e];
+      if (mask_row) dm[e] = h[e];
     }
-    L.out_input_ids[row] = token;
-    L.out_positions[row] = pos;
-    L.out_slot_mapping[row] = slot;
+  } else {
+    const uint16_t* s = reinterpret_cast<const uint16_t*>(src);
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(hs);
+    uint16_t* d = reinterpret_cast<uint16_t*>(out + dst_row * row_bytes);
+    uint16_t* dm = reinterpret_cast<uint16_t*>(out + mrow * row_bytes);
+    for (long e = l; e < L.H; e += kWave) {
+      d[e] = s[e];
+      if (mask_row) dm[e] = h[e];
+    }
   }
-  if (L.out_sample_rows && i == 0 && lane_id() < K)
-    L.out_sample_rows[(long)b * K + lane_id()] = (int32_t)(row + a + lane_id());
-  const long row_bytes = (long)L.H * L.elem_bytes;
-  const char* src = hslot < 0
-      ? static_cast<const char*>(L.h_shared)
-      : static_cast<const char*>(L.target_hidden) + ((long)b * (K + 1) + hslot) * row_bytes;
-  char* dst = static_cast<char*>(L.out_hidden) + row * row_bytes;
-  copy_row(src, dst, row_bytes, L.vec != 0, L.elem_bytes);
+  const int64_t Lpos = L.start_pos[b];
+  if (l == 0) {
+    int token;
+    int64_t slot;
+    if (i <= a) {
+      token = L.verify_out_tokens[(long)b * (K + 1) + i];
+      slot = kv_slot(L, b, Lpos + i);
+    } else {
+      token = L.draft_tokens[(long)b * K + i - 1];
+      slot = SV_PADDING_SLOT_ID;
+    }
+    L.out_input_ids[dst_row] = token;
+    L.out_positions[dst_row] = Lpos + i;
+    L.out_slot_mapping[dst_row] = slot;
+  } else if (l == 1 && mask_row) {
+    L.out_input_ids[mrow] = L.mask_token_id;
+    L.out_positions[mrow] = Lpos + a + i;
+    L.out_slot_mapping[mrow] = kv_slot(L, b, Lpos + a + i);
+  }
+  if (L.out_sample_rows && i == 0 && l < K)
+    L.out_sample_rows[(long)b * K + l] = (int32_t)(base_row + a + l);
 }
 
 hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
   BuildArgs A;
   A.L = L;
-  A.rows = (long)L.B * 2 * L.K;
-  const unsigned blocks = (unsigned)((A.rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  A.units = (long)L.B * (L.K + 1);
+  const unsigned blocks = (unsigned)((A.units + kWavesPerBlock - 1) / kWavesPerBlock);
   trace_before(stream);
   hipLaunchKernelGGL(build_kernel, dim3(blocks), dim3(kBuildThreads), 0, stream, A);
   const hipError_t err = hipGetLastError();

@@ -6,15 +6,15 @@
 // of exponentials relative to it (sampling).  Nothing else: no workgroup of
 // this kernel waits for or hands anything to another.
 //
-// The accept scan (one wave per sequence, one lane per row) combines a
+// verify_accept: one wave per sequence (one lane per row) combines the
 // sequence's partials, tests every draft in parallel and takes the first
-// rejection from a wave ballot.  Greedy: verify_accept runs it and writes the
-// argmax of row a as the new token.  Sampling: each of the C workgroups of
-// verify_draw that share a sequence runs it (a few dozen loads), then takes a
-// contiguous chunk of row a and computes the mass r = max(0, p_a - q_a) (or
-// p_K for the bonus token) of each 512-element tile in it.  The last chunk to
-// arrive (a per-sequence ticket) finds the chunk, then the tile, whose running
-// total first exceeds u * S, rescans that one tile and writes the token.
+// rejection from a wave ballot.  Greedy: it writes the argmax of row a as the
+// new token.  Sampling: it leaves (a, max and sum of row a) for verify_draw,
+// whose C workgroups per sequence each take a contiguous chunk of row a and
+// compute the mass r = max(0, p_a - q_a) (or p_K for the bonus token) of each
+// 512-element tile in it.  The last chunk to arrive (a per-sequence ticket)
+// finds the chunk, then the tile, whose running total first exceeds u * S,
+// rescans that one tile and writes the token.
 //
 // The verify flow is that of "Project 14 - speculative decoding inference
 // server", section 架构 (architecture): accept the prefix, resample the
@@ -43,15 +43,17 @@ struct ScanResult {  // outcome of a sequence's accept scan
 
 constexpr int kThreads = 256;           // 4 waves
 constexpr int kWaves = kThreads / kWave;
-constexpr int kMaxTiles = SV_MAX_V / kTile;
-constexpr int kTileUnroll = 4;          // draw: tiles per wave per step
+constexpr int kTileLoads = 4;           // draw: wave-wide 512-element loads per CDF tile
+constexpr int kTileElems = kTile * kTileLoads;
+constexpr int kMaxTiles = SV_MAX_V / kTileElems;
+constexpr int kTileUnroll = 1;          // draw: tiles per wave per step
 
 enum Mode { GREEDY = 0, SAMPLE = 1 };
 
 // ---------------------------------------------------------------- workspace
-// tickets [B] | chunk sums [B][C] | tile sums [B][T] | partials [B][K+1][S]
+// tickets [B] | scan results [B] | chunk sums [B][C] | tile sums [B][T] | partials [B][K+1][S]
 struct Layout {
-  size_t tickets, chunk, tile, partials, total;
+  size_t tickets, info, chunk, tile, partials, total;
   int S, C, T;
 };
 
@@ -68,7 +70,7 @@ int verify_splits(int B, int K, int V) {
 }
 
 static int draw_chunks(int B, int V) {
-  const long tiles = (V + kTile - 1) / kTile;
+  const long tiles = (V + kTileElems - 1) / kTileElems;
   long c = (4096 + B - 1) / B;
   if (c > tiles) c = tiles;
   return c < 1 ? 1 : (int)c;
@@ -78,9 +80,10 @@ static Layout layout(int B, int K, int V) {
   Layout L;
   L.S = verify_splits(B, K, V);
   L.C = draw_chunks(B, V);
-  L.T = (V + kTile - 1) / kTile;
+  L.T = (V + kTileElems - 1) / kTileElems;
   size_t off = 0;
   L.tickets = off;  off = align256(off + (size_t)B * sizeof(int));
+  L.info = off;     off = align256(off + (size_t)B * sizeof(ScanResult));
   L.chunk = off;    off = align256(off + (size_t)B * L.C * sizeof(double));
   L.tile = off;     off = align256(off + (size_t)B * L.T * sizeof(float));
   L.partials = off; off = align256(off + (size_t)B * (K + 1) * L.S * sizeof(Partial));
@@ -106,6 +109,7 @@ struct ScanArgs {          // what an accept scan reads and writes
   float c;
   int B, K, V, S;
   Partial* partials;       // [B][K+1][S]
+  ScanResult* info;        // [B] sampling: handed to verify_draw
   int32_t* out_tokens;
   int32_t* out_num_accepted;
   float* out_p_draft;
@@ -205,7 +209,8 @@ __device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, l
 // Phase 1: one slice [o_lo, o_hi) of octets of one row -> one Partial
 // (returned by thread 0).  VEC: V is a multiple of 8 and the rows are 16-byte
 // aligned, so the steady-state loop has no branches and issues all of a
-// step's loads before using any.
+// step's loads before using any.  The loads are non-temporal: every logit is
+// read exactly once here (measured 10% faster than cached loads on gfx950).
 template <typename LT, int MODE, bool VEC>
 __device__ Partial slice_stats(const LT* row, long o_lo, long o_hi, long V, float c,
                                float* sm_f, int* sm_i, double* sm_d) {
@@ -217,7 +222,7 @@ __device__ Partial slice_stats(const LT* row, long o_lo, long o_hi, long V, floa
     for (; base + (long)(U - 1) * kThreads < o_hi; base += (long)U * kThreads) {
       Raw<LT> raw[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) raw_load<false>(row, base + (long)u * kThreads, raw[u]);
+      for (int u = 0; u < U; ++u) raw_load<true>(row, base + (long)u * kThreads, raw[u]);
       float v[U][8];
 #pragma unroll
       for (int u = 0; u < U; ++u) unpack(raw[u], v[u]);
@@ -357,14 +362,18 @@ __device__ ScanResult accept_scan(const ScanArgs& A, int b, bool write) {
   return r;
 }
 
-// Greedy: one wave per sequence runs the accept scan and writes g_a.
-template <typename LT>
+// One wave per sequence runs the accept scan.  Greedy: writes g_a as the new
+// token.  Sampling: hands (a, M_a, s_a) to verify_draw.
+template <typename LT, int MODE>
 __global__ __launch_bounds__(kThreads) void verify_accept(ScanArgs A) {
   const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
   if (b >= A.B) return;
-  const ScanResult r = accept_scan<LT, GREEDY>(A, b, true);
+  const ScanResult r = accept_scan<LT, MODE>(A, b, true);
   const int l = lane_id();
-  if (l == 0) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
+  if (l == 0) {
+    if constexpr (MODE == GREEDY) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
+    else A.info[b] = r;
+  }
   // the partials are consumed: clear them so the workspace ends all zero
   Partial* Pb = A.partials + (long)b * (A.K + 1) * A.S;
   for (int i = l; i < (A.K + 1) * A.S; i += kWave) Pb[i] = Partial{0.f, 0, 0.0};
@@ -399,7 +408,8 @@ __device__ __forceinline__ void octet_mass(const LT* zrow, const float* qrow, lo
     const bool in = o < nocts;
     const long oc = in ? o : nocts - 1;
     Raw<LT> rz;
-    raw_load<false>(zrow, oc, rz);
+    raw_load<true>(zrow, oc, rz);      // non-temporal: measured faster for the logits
+                                        // (not for the drafter rows)
     unpack(rz, z);
     if (residual) {
       Raw<float> rq;
@@ -424,8 +434,11 @@ __device__ __forceinline__ void octet_mass(const LT* zrow, const float* qrow, lo
 }
 
 // Tile masses of tiles [t_lo, t_hi) of the draw row, computed by the whole
-// workgroup (kTileUnroll tiles per wave per step) and published with
-// agent-coherent stores; their sum in tile order is returned to thread 0.
+// workgroup and published with agent-coherent stores; their sum in tile order
+// is returned to thread 0.  A tile is kTileLoads consecutive 512-element
+// wave loads; each lane sums its octets of the tile first, so one wave
+// reduction serves kTileLoads loads.  Each wave takes kTileUnroll tiles per
+// step, all of whose loads are issued before any is used.
 template <typename LT, bool VEC>
 __device__ double tile_masses(const LT* zrow, const float* qrow, long V, int t_lo, int t_hi,
                               bool residual, float c, float Mc, float inv_s, float* tsum_g,
@@ -436,10 +449,14 @@ __device__ double tile_masses(const LT* zrow, const float* qrow, long V, int t_l
     float ls[kTileUnroll];
 #pragma unroll
     for (int j = 0; j < kTileUnroll; ++j) {
-      float r[8];
-      octet_mass<LT, VEC>(zrow, qrow, (long)(t0 + j) * kWave + l, V, nocts, residual, c, Mc,
-                          inv_s, r);
-      ls[j] = tree_sum8(r);
+      ls[j] = 0.f;
+#pragma unroll
+      for (int sl = 0; sl < kTileLoads; ++sl) {
+        float r[8];
+        const long o = ((long)(t0 + j) * kTileLoads + sl) * kWave + l;
+        octet_mass<LT, VEC>(zrow, qrow, o, V, nocts, residual, c, Mc, inv_s, r);
+        ls[j] += tree_sum8(r);
+      }
     }
 #pragma unroll
     for (int j = 0; j < kTileUnroll; ++j) {
@@ -466,26 +483,20 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
   __shared__ int sm_last;
   __shared__ int sm_pick;
   __shared__ int sm_redo;
-  __shared__ ScanResult sm_scan;
 
   const int C = A.C, T = A.T, K = A.sc.K;
   const int b = blockIdx.x / C, cidx = blockIdx.x % C;
   const long V = A.sc.V;
-  // every chunk of the sequence runs the accept scan; chunk 0 writes its outputs
-  if (threadIdx.x < kWave) {
-    const ScanResult r = accept_scan<LT, SAMPLE>(A.sc, b, cidx == 0);
-    if (threadIdx.x == 0) sm_scan = r;
-  }
-  __syncthreads();
-  const int a = sm_scan.a;
+  const ScanResult scan = A.sc.info[b];       // written by verify_accept
+  const int a = scan.a;
   const LT* zrow = static_cast<const LT*>(A.sc.logits) + ((long)b * (K + 1) + a) * V;
   const float* qrow = a < K ? A.sc.draft_probs + ((long)b * K + a) * V : nullptr;
   const float c = A.sc.c;
   // p = 2^(z*c - M*c) / s.  Mc32 is M*c rounded to fp32; the rounding is
   // folded into the scale so that p keeps the fp64 reference exactly.
-  const float M = sm_scan.M_a;
+  const float M = scan.M_a;
   const float Mc32 = M * c;
-  const float inv_s = (float)(exp2((double)Mc32 - (double)M * (double)c) / sm_scan.s_a);
+  const float inv_s = (float)(exp2((double)Mc32 - (double)M * (double)c) / scan.s_a);
   float* tsum_g = A.tile_sums + (long)b * T;
   double* csum_g = A.chunk_sums + (long)b * C;
   bool residual = qrow != nullptr;
@@ -591,48 +602,57 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
       tile = anyp ? __shfl(tlast, 63 - __clzll((long long)anyp)) : clo;
       fallback = true;
     }
-    // rescan the tile: one octet per lane
-    const long o = (long)tile * kWave + l;
-    float r[8];
-    octet_mass<LT, VEC>(zrow, qrow, o, V, (V + 7) / 8, residual, c, Mc32, inv_s, r);
-    const double ls = (double)tree_sum8(r);
-    const double lincl = wave_inclusive_scan(ls);
-    double lexcl = __shfl_up(lincl, 1);
-    if (l == 0) lexcl = 0.0;
+    // rescan the tile, one 512-element wave load at a time (one octet per lane)
+    const long nocts = (V + 7) / 8;
     int pick = -1;
-    if (!fallback) {
-      double lrun = tpre + lexcl;
-      const unsigned long long cross = __ballot(tpre + lincl > target);
-      const int src = cross ? __ffsll((long long)cross) - 1 : -1;
-      if (l == src) {
-        for (int j = 0; j < 8; ++j) {
-          lrun += (double)r[j];
-          if (r[j] > 0.f && lrun > target) { pick = (int)(o * 8 + j); break; }
-        }
-        if (pick < 0)
-          for (int j = 7; j >= 0; --j) if (r[j] > 0.f) { pick = (int)(o * 8 + j); break; }
-      }
-      const unsigned long long got = __ballot(pick >= 0);
-      if (got) pick = __shfl(pick, __ffsll((long long)got) - 1);
-    }
-    if (pick < 0) {
-      // last element of the tile with positive mass
+    int lastpos = -1;               // last element of the tile with positive mass so far
+    double lrun0 = tpre;            // running total before the current wave load
+    for (int sl = 0; sl < kTileLoads && pick < 0; ++sl) {
+      const long o = ((long)tile * kTileLoads + sl) * kWave + l;
+      float r[8];
+      octet_mass<LT, VEC>(zrow, qrow, o, V, nocts, residual, c, Mc32, inv_s, r);
       int lastj = -1;
       for (int j = 7; j >= 0; --j) if (r[j] > 0.f) { lastj = (int)(o * 8 + j); break; }
       const unsigned long long anyp = __ballot(lastj >= 0);
-      pick = anyp ? __shfl(lastj, 63 - __clzll((long long)anyp)) : 0;
+      if (anyp) lastpos = __shfl(lastj, 63 - __clzll((long long)anyp));
+      if (fallback) continue;
+      const double ls = (double)tree_sum8(r);
+      const double lincl = wave_inclusive_scan(ls);
+      double lexcl = __shfl_up(lincl, 1);
+      if (l == 0) lexcl = 0.0;
+      const unsigned long long cross = __ballot(lrun0 + lincl > target);
+      if (cross) {
+        const int src = __ffsll((long long)cross) - 1;
+        int mine = -1;
+        if (l == src) {
+          double lrun = lrun0 + lexcl;
+          for (int j = 0; j < 8; ++j) {
+            lrun += (double)r[j];
+            if (r[j] > 0.f && lrun > target) { mine = (int)(o * 8 + j); break; }
+          }
+          if (mine < 0)
+            for (int j = 7; j >= 0; --j) if (r[j] > 0.f) { mine = (int)(o * 8 + j); break; }
+        }
+        const unsigned long long got = __ballot(mine >= 0);
+        pick = got ? __shfl(mine, __ffsll((long long)got) - 1) : lastpos;
+        if (pick < 0) pick = 0;
+      }
+      lrun0 += __shfl(lincl, kWave - 1);
     }
+    // rounding left u*S at or past the tile's total: its last positive element
+    if (pick < 0) pick = lastpos >= 0 ? lastpos : 0;
     if (l == 0) sm_pick = pick;
   }
   __syncthreads();
   if (threadIdx.x == 0) A.sc.out_tokens[(long)b * (K + 1) + a] = sm_pick;
-  // leave this sequence's part of the workspace cleared (every chunk has
-  // already read the partials: it took its ticket after its accept scan)
-  Partial* Pb = A.sc.partials + (long)b * (K + 1) * A.sc.S;
-  for (int i = threadIdx.x; i < (K + 1) * A.sc.S; i += kThreads) Pb[i] = Partial{0.f, 0, 0.0};
+  // leave this sequence's part of the workspace cleared (every chunk read
+  // its scan result before it took its ticket)
   for (int i = threadIdx.x; i < T; i += kThreads) st_coherent(&tsum_g[i], 0.f);
   for (int i = threadIdx.x; i < C; i += kThreads) st_coherent(&csum_g[i], 0.0);
-  if (threadIdx.x == 0) st_coherent(&A.tickets[b], 0);
+  if (threadIdx.x == 0) {
+    st_coherent(&A.tickets[b], 0);
+    A.sc.info[b] = ScanResult{0, 0, 0.f, 0.0};
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -677,15 +697,19 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   sc.out_p_draft = L.out_p_draft;
   sc.device_error = L.device_error;
 
-  if (!L.sample) {
-    const dim3 grid2((unsigned)((L.B + kWaves - 1) / kWaves));
-    trace_before(stream);
-    if (L.bf16) hipLaunchKernelGGL((verify_accept<uint16_t>), grid2, block, 0, stream, sc);
-    else hipLaunchKernelGGL((verify_accept<float>), grid2, block, 0, stream, sc);
-    err = hipGetLastError();
-    trace_after(stream, SV_KERNEL_VERIFY_GREEDY_ACCEPT);
-    return err;
+  sc.info = reinterpret_cast<ScanResult*>(ws + lay.info);
+  const dim3 grid_acc((unsigned)((L.B + kWaves - 1) / kWaves));
+  trace_before(stream);
+  if (L.bf16) {
+    if (L.sample) hipLaunchKernelGGL((verify_accept<uint16_t, SAMPLE>), grid_acc, block, 0, stream, sc);
+    else hipLaunchKernelGGL((verify_accept<uint16_t, GREEDY>), grid_acc, block, 0, stream, sc);
+  } else {
+    if (L.sample) hipLaunchKernelGGL((verify_accept<float, SAMPLE>), grid_acc, block, 0, stream, sc);
+    else hipLaunchKernelGGL((verify_accept<float, GREEDY>), grid_acc, block, 0, stream, sc);
   }
+  err = hipGetLastError();
+  trace_after(stream, L.sample ? SV_KERNEL_VERIFY_SAMPLE_ACCEPT : SV_KERNEL_VERIFY_GREEDY_ACCEPT);
+  if (err != hipSuccess || !L.sample) return err;
 
   DrawArgs D;
   D.sc = sc;

@@ -131,8 +131,8 @@ SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
  *                    (NULL = not written).
  * Arithmetic: fp32 exponentials, fp64 accumulation of every sum and of the
  * acceptance ratio; results agree with an fp64 evaluation except when a
- * decision lies within ~1e-6 of its threshold.  Two kernels are enqueued:
- * row statistics, then the accept scan with the draw of the new token.
+ * decision lies within ~1e-6 of its threshold.  Three kernels are enqueued:
+ * row statistics, the accept scan, the draw of the new token.
  */
 SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
                                     const float* draft_probs,
@@ -196,9 +196,10 @@ SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,
  */
 #define SV_KERNEL_VERIFY_GREEDY_ROWS 0   /* spec_verify_greedy: row max / argmax         */
 #define SV_KERNEL_VERIFY_SAMPLE_ROWS 1   /* spec_verify_sample: row max / sum of exp     */
-#define SV_KERNEL_VERIFY_SAMPLE_DRAW 2   /* spec_verify_sample: accept scan + draw       */
+#define SV_KERNEL_VERIFY_SAMPLE_DRAW 2   /* spec_verify_sample: residual / bonus draw    */
 #define SV_KERNEL_PEAGLE_BUILD 3         /* peagle_build_draft_batch                     */
 #define SV_KERNEL_VERIFY_GREEDY_ACCEPT 4 /* spec_verify_greedy: accept scan              */
+#define SV_KERNEL_VERIFY_SAMPLE_ACCEPT 5 /* spec_verify_sample: accept scan              */
 
 SV_API const char* sv_kernel_name(int kernel_id);
 SV_API sv_status sv_trace_begin(int capacity);       /* SV_ERR_VALUE if capacity < 1   */

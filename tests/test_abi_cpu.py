@@ -174,8 +174,8 @@ def test_tracer_host_paths(lib):
     kid, ms = ctypes.c_int(), ctypes.c_float()
     assert lib.sv_trace_read(0, ctypes.byref(kid), ctypes.byref(ms)) == EVALUE
     assert lib.sv_trace_read(0, None, None) == ENULL
-    names = [lib.sv_kernel_name(i) for i in range(5)]
+    names = [lib.sv_kernel_name(i) for i in range(6)]
     assert names == [b"verify_greedy_rows", b"verify_sample_rows", b"verify_sample_draw",
-                     b"peagle_build", b"verify_greedy_accept"]
+                     b"peagle_build", b"verify_greedy_accept", b"verify_sample_accept"]
     assert lib.sv_kernel_name(17) == b"unknown"
     lib.sv_trace_end()                              # harmless when tracing is off
