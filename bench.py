@@ -243,10 +243,13 @@ def main():
         return
 
     def timed(sample):
+        """Wall time per step with only the dominant kernel traced (two events
+        per step), then per-kernel times from a second loop tracing all."""
+        dom = "verify_sample_rows" if sample else "verify_greedy_rows"
         for _ in range(args.warmup):
             step(sample); build()
         torch.cuda.synchronize()
-        sv.trace_begin(5 * args.steps)
+        sv.trace_begin(args.steps, [dom])
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -254,9 +257,15 @@ def main():
             build()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = {}
+        per = {dom: [ms for _, ms in sv.trace_read()]}
+        sv.trace_begin(8 * args.steps)
+        for _ in range(args.steps):
+            step(sample)
+            build()
+        torch.cuda.synchronize()
         for name, ms in sv.trace_read():
-            per.setdefault(name, []).append(ms)
+            if name != dom:
+                per.setdefault(name, []).append(ms)
         sv.trace_end()
         acc = acc_t.cpu().numpy()
         return wall / args.steps, {k: float(np.mean(v)) for k, v in per.items()}, acc
@@ -295,6 +304,7 @@ def main():
             "verify_sample_draw": kinfo("verify_sample_draw", int((acc < K).sum()) * V * 4,
                                         "algorithmic bytes count the drafter rows a_b; the kernel "
                                         "also re-reads logit row a"),
+            "verify_sample_locate": kinfo("verify_sample_locate", B * 4),
             "peagle_build": kinfo("peagle_build", bb),
         },
         "acceptance": {"mean_accepted": float(acc.mean()),

@@ -45,7 +45,7 @@ _SIGS = {
     "peagle_build_draft_batch": (_i, [_p, _p, _p, _p, _p, _i, _i, _p, _p, _i, ctypes.c_int32,
                                       _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
     "sv_kernel_name": (ctypes.c_char_p, [_i]),
-    "sv_trace_begin": (_i, [_i]),
+    "sv_trace_begin": (_i, [_i, ctypes.c_uint]),
     "sv_trace_count": (_i, []),
     "sv_trace_read": (_i, [_i, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)]),
     "sv_trace_end": (None, []),
@@ -91,9 +91,16 @@ def _check(status: int, what: str):
 
 
 # ---------------------------------------------------------------- tracing
-def trace_begin(capacity: int):
-    """Start kernel tracing on this host thread for up to `capacity` launches."""
-    _check(require_library().sv_trace_begin(int(capacity)), "sv_trace_begin")
+KERNEL_IDS = {"verify_greedy_rows": 0, "verify_sample_rows": 1, "verify_sample_draw": 2,
+              "peagle_build": 3, "verify_greedy_accept": 4, "verify_sample_accept": 5,
+              "verify_sample_locate": 6}
+
+
+def trace_begin(capacity: int, kernels=None):
+    """Start kernel tracing on this host thread for up to `capacity` launches
+    of the named kernels (all kernels when `kernels` is None)."""
+    mask = 0xFFFFFFFF if kernels is None else sum(1 << KERNEL_IDS[k] for k in kernels)
+    _check(require_library().sv_trace_begin(int(capacity), mask), "sv_trace_begin")
 
 
 def trace_read():

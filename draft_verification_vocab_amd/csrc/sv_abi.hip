@@ -15,6 +15,8 @@ namespace sv {
 namespace {
 struct Tracer {
   bool on = false;
+  bool pending = false;           // trace_before recorded an event for the next launch
+  unsigned mask = ~0u;
   int cap = 0, count = 0;
   std::vector<hipEvent_t> ev;     // 2 per traced launch
   std::vector<int> ids;
@@ -22,7 +24,7 @@ struct Tracer {
     for (hipEvent_t e : ev) (void)hipEventDestroy(e);
     ev.clear();
     ids.clear();
-    on = false;
+    on = pending = false;
     cap = count = 0;
   }
   ~Tracer() { destroy(); }
@@ -30,15 +32,16 @@ struct Tracer {
 thread_local Tracer tracer;
 }  // namespace
 
-void trace_before(hipStream_t stream) {
-  if (tracer.on && tracer.count < tracer.cap)
-    (void)hipEventRecord(tracer.ev[2 * tracer.count], stream);
+void trace_before(hipStream_t stream, int kernel_id) {
+  tracer.pending = tracer.on && tracer.count < tracer.cap && ((tracer.mask >> kernel_id) & 1u);
+  if (tracer.pending) (void)hipEventRecord(tracer.ev[2 * tracer.count], stream);
 }
 
 void trace_after(hipStream_t stream, int kernel_id) {
-  if (tracer.on && tracer.count < tracer.cap) {
+  if (tracer.pending) {
     (void)hipEventRecord(tracer.ev[2 * tracer.count + 1], stream);
     tracer.ids[tracer.count++] = kernel_id;
+    tracer.pending = false;
   }
 }
 
@@ -81,11 +84,12 @@ SV_API const char* sv_kernel_name(int kernel_id) {
     case SV_KERNEL_PEAGLE_BUILD: return "peagle_build";
     case SV_KERNEL_VERIFY_GREEDY_ACCEPT: return "verify_greedy_accept";
     case SV_KERNEL_VERIFY_SAMPLE_ACCEPT: return "verify_sample_accept";
+    case SV_KERNEL_VERIFY_SAMPLE_LOCATE: return "verify_sample_locate";
     default: return "unknown";
   }
 }
 
-SV_API sv_status sv_trace_begin(int capacity) {
+SV_API sv_status sv_trace_begin(int capacity, unsigned kernel_mask) {
   if (capacity < 1) return SV_ERR_VALUE;
   sv::tracer.destroy();
   sv::tracer.ev.resize(2 * (size_t)capacity);
@@ -99,6 +103,7 @@ SV_API sv_status sv_trace_begin(int capacity) {
   sv::tracer.ids.assign(capacity, -1);
   sv::tracer.cap = capacity;
   sv::tracer.count = 0;
+  sv::tracer.mask = kernel_mask;
   sv::tracer.on = true;
   return SV_OK;
 }

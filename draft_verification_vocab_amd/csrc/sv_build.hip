@@ -179,7 +179,7 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
   A.L = L;
   A.units = (long)L.B * (L.K + 1);
   const unsigned blocks = (unsigned)((A.units + kWavesPerBlock - 1) / kWavesPerBlock);
-  trace_before(stream);
+  trace_before(stream, SV_KERNEL_PEAGLE_BUILD);
   hipLaunchKernelGGL(build_kernel, dim3(blocks), dim3(kBuildThreads), 0, stream, A);
   const hipError_t err = hipGetLastError();
   trace_after(stream, SV_KERNEL_PEAGLE_BUILD);

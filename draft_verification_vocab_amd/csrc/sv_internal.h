@@ -50,7 +50,7 @@ struct BuildLaunch {
 int verify_splits(int B, int K, int V);
 
 // Kernel tracing (per host thread): bracket a launch with events on its stream.
-void trace_before(hipStream_t stream);
+void trace_before(hipStream_t stream, int kernel_id);
 void trace_after(hipStream_t stream, int kernel_id);
 size_t verify_workspace_bytes(int B, int K, int V);
 hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream);

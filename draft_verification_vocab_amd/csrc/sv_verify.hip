@@ -9,12 +9,14 @@
 // verify_accept: one wave per sequence (one lane per row) combines the
 // sequence's partials, tests every draft in parallel and takes the first
 // rejection from a wave ballot.  Greedy: it writes the argmax of row a as the
-// new token.  Sampling: it leaves (a, max and sum of row a) for verify_draw,
-// whose C workgroups per sequence each take a contiguous chunk of row a and
-// compute the mass r = max(0, p_a - q_a) (or p_K for the bonus token) of each
-// 512-element tile in it.  The last chunk to arrive (a per-sequence ticket)
-// finds the chunk, then the tile, whose running total first exceeds u * S,
-// rescans that one tile and writes the token.
+// new token.  Sampling: it leaves (a, max and sum of row a) for the draw.
+//
+// verify_draw (sampling): C workgroups per sequence each take a contiguous
+// chunk of row a and store the mass r = max(0, p_a - q_a) (or p_K for the
+// bonus token) of each 2048-element tile in it, and the chunk's total.
+// verify_locate: one wave per sequence finds the chunk, then the tile, whose
+// running total first exceeds u * S, rescans that one tile and writes the
+// token.  Every hand-off between workgroups goes through a kernel boundary.
 //
 // The verify flow is that of "Project 14 - speculative decoding inference
 // server", section 架构 (architecture): accept the prefix, resample the
@@ -51,9 +53,9 @@ constexpr int kTileUnroll = 1;          // draw: tiles per wave per step
 enum Mode { GREEDY = 0, SAMPLE = 1 };
 
 // ---------------------------------------------------------------- workspace
-// tickets [B] | scan results [B] | chunk sums [B][C] | tile sums [B][T] | partials [B][K+1][S]
+// scan results [B] | chunk sums [B][C] | tile sums [B][T] | partials [B][K+1][S]
 struct Layout {
-  size_t tickets, info, chunk, tile, partials, total;
+  size_t info, chunk, tile, partials, total;
   int S, C, T;
 };
 
@@ -82,7 +84,6 @@ static Layout layout(int B, int K, int V) {
   L.C = draw_chunks(B, V);
   L.T = (V + kTileElems - 1) / kTileElems;
   size_t off = 0;
-  L.tickets = off;  off = align256(off + (size_t)B * sizeof(int));
   L.info = off;     off = align256(off + (size_t)B * sizeof(ScanResult));
   L.chunk = off;    off = align256(off + (size_t)B * L.C * sizeof(double));
   L.tile = off;     off = align256(off + (size_t)B * L.T * sizeof(float));
@@ -119,7 +120,6 @@ struct ScanArgs {          // what an accept scan reads and writes
 struct DrawArgs {
   ScanArgs sc;
   int C, T;
-  int* tickets;            // [B]
   double* chunk_sums;      // [B][C]
   float* tile_sums;        // [B][T]
 };
@@ -433,226 +433,229 @@ __device__ __forceinline__ void octet_mass(const LT* zrow, const float* qrow, lo
   mass_octet(z, q, residual, c, Mc, inv_s, r);
 }
 
-// Tile masses of tiles [t_lo, t_hi) of the draw row, computed by the whole
-// workgroup and published with agent-coherent stores; their sum in tile order
-// is returned to thread 0.  A tile is kTileLoads consecutive 512-element
-// wave loads; each lane sums its octets of the tile first, so one wave
-// reduction serves kTileLoads loads.  Each wave takes kTileUnroll tiles per
-// step, all of whose loads are issued before any is used.
+// Everything the draw needs about sequence b's row a.
+template <typename LT>
+struct DrawRow {
+  const LT* zrow;
+  const float* qrow;       // null for the bonus draw (a = K)
+  float c, Mc32, inv_s;
+  int a;
+};
+
+template <typename LT>
+__device__ __forceinline__ DrawRow<LT> draw_row(const DrawArgs& A, int b) {
+  const ScanResult scan = A.sc.info[b];       // written by verify_accept
+  DrawRow<LT> r;
+  r.a = scan.a;
+  r.zrow = static_cast<const LT*>(A.sc.logits) + ((long)b * (A.sc.K + 1) + scan.a) * A.sc.V;
+  r.qrow = scan.a < A.sc.K ? A.sc.draft_probs + ((long)b * A.sc.K + scan.a) * A.sc.V : nullptr;
+  r.c = A.sc.c;
+  // p = 2^(z*c - M*c) / s.  Mc32 is M*c rounded to fp32; the rounding is
+  // folded into the scale so that p keeps the fp64 reference exactly.
+  r.Mc32 = scan.M_a * r.c;
+  r.inv_s = (float)(exp2((double)r.Mc32 - (double)scan.M_a * (double)r.c) / scan.s_a);
+  return r;
+}
+
+// Mass of tile t seen by one lane: the sum of its kTileLoads octets.
 template <typename LT, bool VEC>
-__device__ double tile_masses(const LT* zrow, const float* qrow, long V, int t_lo, int t_hi,
-                              bool residual, float c, float Mc, float inv_s, float* tsum_g,
-                              float* tsum_l) {
-  const int w = threadIdx.x / kWave, l = lane_id();
+__device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool residual, int t, long V,
+                                                long nocts) {
+  float ls = 0.f;
+#pragma unroll
+  for (int sl = 0; sl < kTileLoads; ++sl) {
+    float r[8];
+    const long o = ((long)t * kTileLoads + sl) * kWave + lane_id();
+    octet_mass<LT, VEC>(R.zrow, R.qrow, o, V, nocts, residual, R.c, R.Mc32, R.inv_s, r);
+    ls += tree_sum8(r);
+  }
+  return ls;
+}
+
+// verify_draw: chunk cidx of sequence b stores the mass of each of its tiles
+// and the chunk total (tile order).  A tile is kTileLoads consecutive
+// 512-element wave loads; each lane sums its octets of the tile before one
+// wave reduction.
+template <typename LT, bool VEC>
+__global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
+  __shared__ float tsum_l[kMaxTiles];
+  const int C = A.C, T = A.T;
+  const int b = blockIdx.x / C, cidx = blockIdx.x % C;
+  const long V = A.sc.V;
   const long nocts = (V + 7) / 8;
+  const DrawRow<LT> R = draw_row<LT>(A, b);
+  const bool residual = R.qrow != nullptr;
+  float* tsum_g = A.tile_sums + (long)b * T;
+  const int t_lo = (int)((long)cidx * T / C), t_hi = (int)((long)(cidx + 1) * T / C);
+  const int w = threadIdx.x / kWave, l = lane_id();
   for (int t0 = t_lo + w * kTileUnroll; t0 < t_hi; t0 += kWaves * kTileUnroll) {
     float ls[kTileUnroll];
 #pragma unroll
-    for (int j = 0; j < kTileUnroll; ++j) {
-      ls[j] = 0.f;
-#pragma unroll
-      for (int sl = 0; sl < kTileLoads; ++sl) {
-        float r[8];
-        const long o = ((long)(t0 + j) * kTileLoads + sl) * kWave + l;
-        octet_mass<LT, VEC>(zrow, qrow, o, V, nocts, residual, c, Mc, inv_s, r);
-        ls[j] += tree_sum8(r);
-      }
-    }
+    for (int j = 0; j < kTileUnroll; ++j) ls[j] = lane_tile_mass<LT, VEC>(R, residual, t0 + j, V, nocts);
 #pragma unroll
     for (int j = 0; j < kTileUnroll; ++j) {
       const float ts = wave_sum_f(ls[j]);
       if (l == 0 && t0 + j < t_hi) {
         tsum_l[t0 + j - t_lo] = ts;
-        st_coherent(&tsum_g[t0 + j], ts);
+        tsum_g[t0 + j] = ts;                  // read by verify_locate
       }
     }
   }
-  // every wave's tile stores are performed before thread 0 takes a ticket
-  wait_stores_performed();
   __syncthreads();
-  double sum = 0.0;
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0) {
+    double sum = 0.0;
     for (int i = 0; i < t_hi - t_lo; ++i) sum += (double)tsum_l[i];
-  __syncthreads();
-  return sum;
+    A.chunk_sums[(long)b * C + cidx] = sum;
+  }
 }
 
+// verify_locate: one wave per sequence draws the token from the tile masses.
 template <typename LT, bool VEC>
-__global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
-  __shared__ float tsum_l[kMaxTiles];
-  __shared__ int sm_last;
-  __shared__ int sm_pick;
-  __shared__ int sm_redo;
-
+__global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
+  const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (b >= A.sc.B) return;
   const int C = A.C, T = A.T, K = A.sc.K;
-  const int b = blockIdx.x / C, cidx = blockIdx.x % C;
   const long V = A.sc.V;
-  const ScanResult scan = A.sc.info[b];       // written by verify_accept
-  const int a = scan.a;
-  const LT* zrow = static_cast<const LT*>(A.sc.logits) + ((long)b * (K + 1) + a) * V;
-  const float* qrow = a < K ? A.sc.draft_probs + ((long)b * K + a) * V : nullptr;
-  const float c = A.sc.c;
-  // p = 2^(z*c - M*c) / s.  Mc32 is M*c rounded to fp32; the rounding is
-  // folded into the scale so that p keeps the fp64 reference exactly.
-  const float M = scan.M_a;
-  const float Mc32 = M * c;
-  const float inv_s = (float)(exp2((double)Mc32 - (double)M * (double)c) / scan.s_a);
+  const long nocts = (V + 7) / 8;
+  const int l = lane_id();
+  const DrawRow<LT> R = draw_row<LT>(A, b);
+  bool residual = R.qrow != nullptr;
   float* tsum_g = A.tile_sums + (long)b * T;
   double* csum_g = A.chunk_sums + (long)b * C;
-  bool residual = qrow != nullptr;
+  const int per = (C + kWave - 1) / kWave;
+  const int lo = l * per, hi = min(C, (l + 1) * per);
 
-  const int t_lo = (int)((long)cidx * T / C), t_hi = (int)((long)(cidx + 1) * T / C);
-  const double mine = tile_masses<LT, VEC>(zrow, qrow, V, t_lo, t_hi, residual, c, Mc32, inv_s,
-                                           tsum_g, tsum_l);
-  if (threadIdx.x == 0) {
-    st_coherent(&csum_g[cidx], mine);
-    wait_stores_performed();
-    sm_last = take_ticket(&A.tickets[b]) == C - 1;
-  }
-  __syncthreads();
-  if (!sm_last) return;
-
-  // ---- the last chunk of sequence b: total, locate, rescan
-  const int w = threadIdx.x / kWave, l = lane_id();
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    if (w == 0) {
-      const int per = (C + kWave - 1) / kWave;
-      double part = 0.0;
-      for (int i = l * per; i < min(C, (l + 1) * per); ++i) part += ld_coherent(&csum_g[i]);
-      const double incl = wave_inclusive_scan(part);
-      const double S = __shfl(incl, kWave - 1);
-      if (l == 0) sm_redo = residual && !(S > 0.0);
-    }
-    __syncthreads();
-    if (!sm_redo) break;
+  // the masses are read with agent-coherent loads: the rare path below
+  // rewrites them from this wave and reads them back
+  double part = 0.0;
+  for (int i = lo; i < hi; ++i) part += ld_coherent(&csum_g[i]);
+  double incl = wave_inclusive_scan(part);
+  double S = __shfl(incl, kWave - 1);
+  if (residual && !(S > 0.0)) {
     // r sums to 0 (only when the drafter's row sums to more than p): draw
-    // from p_a instead; this workgroup recomputes every tile of the row
+    // from p_a instead; this wave recomputes every tile and chunk mass
     residual = false;
     for (int ci = 0; ci < C; ++ci) {
-      const int lo = (int)((long)ci * T / C), hi = (int)((long)(ci + 1) * T / C);
-      const double cs = tile_masses<LT, VEC>(zrow, nullptr, V, lo, hi, false, c, Mc32, inv_s,
-                                             tsum_g, tsum_l);
-      if (threadIdx.x == 0) st_coherent(&csum_g[ci], cs);
+      const int clo = (int)((long)ci * T / C), chi = (int)((long)(ci + 1) * T / C);
+      double cs = 0.0;
+      for (int t = clo; t < chi; ++t) {
+        const float ts = wave_sum_f(lane_tile_mass<LT, VEC>(R, false, t, V, nocts));
+        if (l == 0) st_coherent(&tsum_g[t], ts);
+        cs += (double)ts;
+      }
+      if (l == 0) st_coherent(&csum_g[ci], cs);
     }
-    if (threadIdx.x == 0) wait_stores_performed();
-    __syncthreads();
+    wait_stores_performed();
+    part = 0.0;
+    for (int i = lo; i < hi; ++i) part += ld_coherent(&csum_g[i]);
+    incl = wave_inclusive_scan(part);
+    S = __shfl(incl, kWave - 1);
+  }
+  const double target = (double)A.sc.uniforms[(long)b * (K + 1) + K] * S;
+
+  // chunk that holds u * S (lanes own contiguous runs of chunks)
+  double run = __shfl_up(incl, 1);
+  if (l == 0) run = 0.0;
+  int hit = -1;
+  double pre = 0.0;
+  for (int i = lo; i < hi; ++i) {
+    const double nxt = run + ld_coherent(&csum_g[i]);
+    if (nxt > target) { hit = i; pre = run; break; }
+    run = nxt;
+  }
+  unsigned long long any = __ballot(hit >= 0);
+  int chunk;
+  bool fallback = false;
+  if (any) {
+    const int src = __ffsll((long long)any) - 1;
+    chunk = __shfl(hit, src);
+    pre = __shfl(pre, src);
+  } else {
+    // rounding left u*S at or past the total: last chunk with positive mass
+    int last = -1;
+    for (int i = lo; i < hi; ++i) if (ld_coherent(&csum_g[i]) > 0.0) last = i;
+    const unsigned long long anyp = __ballot(last >= 0);
+    chunk = anyp ? __shfl(last, 63 - __clzll((long long)anyp)) : 0;
+    fallback = true;
+  }
+  // tile inside the chunk (lanes own contiguous runs of its tiles)
+  const int clo = (int)((long)chunk * T / C), chi = (int)((long)(chunk + 1) * T / C);
+  const int tper = (chi - clo + kWave - 1) / kWave;
+  const int tlo = clo + l * tper, thi = min(chi, clo + (l + 1) * tper);
+  double tpart = 0.0;
+  for (int i = tlo; i < thi; ++i) tpart += (double)ld_coherent(&tsum_g[i]);
+  const double tincl = wave_inclusive_scan(tpart);
+  double trun = __shfl_up(tincl, 1);
+  if (l == 0) trun = 0.0;
+  trun += pre;
+  int thit = -1, tlast = -1;
+  double tpre = 0.0;
+  for (int i = tlo; i < thi; ++i) {
+    const float ts = ld_coherent(&tsum_g[i]);
+    if (ts > 0.f) tlast = i;
+    const double nxt = trun + (double)ts;
+    if (!fallback && thit < 0 && nxt > target) { thit = i; tpre = trun; }
+    trun = nxt;
+  }
+  any = __ballot(thit >= 0);
+  int tile;
+  if (any) {
+    const int src = __ffsll((long long)any) - 1;
+    tile = __shfl(thit, src);
+    tpre = __shfl(tpre, src);
+  } else {
+    const unsigned long long anyp = __ballot(tlast >= 0);
+    tile = anyp ? __shfl(tlast, 63 - __clzll((long long)anyp)) : clo;
+    fallback = true;
   }
 
-  if (w == 0) {
-    // chunk that holds u * S (lanes own contiguous runs of chunks)
-    const int per = (C + kWave - 1) / kWave;
-    const int lo = l * per, hi = min(C, (l + 1) * per);
-    double part = 0.0;
-    for (int i = lo; i < hi; ++i) part += ld_coherent(&csum_g[i]);
-    const double incl = wave_inclusive_scan(part);
-    const double S = __shfl(incl, kWave - 1);
-    const double target = (double)A.sc.uniforms[(long)b * (K + 1) + K] * S;
-    double run = __shfl_up(incl, 1);
-    if (l == 0) run = 0.0;
-    int hit = -1;
-    double pre = 0.0;
-    for (int i = lo; i < hi; ++i) {
-      const double nxt = run + ld_coherent(&csum_g[i]);
-      if (nxt > target) { hit = i; pre = run; break; }
-      run = nxt;
-    }
-    unsigned long long any = __ballot(hit >= 0);
-    int chunk;
-    bool fallback = false;
-    if (any) {
-      const int src = __ffsll((long long)any) - 1;
-      chunk = __shfl(hit, src);
-      pre = __shfl(pre, src);
-    } else {
-      // rounding left u*S at or past the total: last chunk with positive mass
-      int last = -1;
-      for (int i = lo; i < hi; ++i) if (ld_coherent(&csum_g[i]) > 0.0) last = i;
-      const unsigned long long anyp = __ballot(last >= 0);
-      chunk = anyp ? __shfl(last, 63 - __clzll((long long)anyp)) : 0;
-      fallback = true;
-    }
-    // tile inside the chunk (lanes own contiguous runs of its tiles)
-    const int clo = (int)((long)chunk * T / C), chi = (int)((long)(chunk + 1) * T / C);
-    const int n = chi - clo;
-    const int tper = (n + kWave - 1) / kWave;
-    const int tlo = clo + l * tper, thi = min(chi, clo + (l + 1) * tper);
-    double tpart = 0.0;
-    for (int i = tlo; i < thi; ++i) tpart += (double)ld_coherent(&tsum_g[i]);
-    const double tincl = wave_inclusive_scan(tpart);
-    double trun = __shfl_up(tincl, 1);
-    if (l == 0) trun = 0.0;
-    trun += pre;
-    int thit = -1, tlast = -1;
-    double tpre = 0.0;
-    for (int i = tlo; i < thi; ++i) {
-      const float ts = ld_coherent(&tsum_g[i]);
-      if (ts > 0.f) tlast = i;
-      const double nxt = trun + (double)ts;
-      if (!fallback && thit < 0 && nxt > target) { thit = i; tpre = trun; }
-      trun = nxt;
-    }
-    any = __ballot(thit >= 0);
-    int tile;
-    if (any) {
-      const int src = __ffsll((long long)any) - 1;
-      tile = __shfl(thit, src);
-      tpre = __shfl(tpre, src);
-    } else {
-      const unsigned long long anyp = __ballot(tlast >= 0);
-      tile = anyp ? __shfl(tlast, 63 - __clzll((long long)anyp)) : clo;
-      fallback = true;
-    }
-    // rescan the tile, one 512-element wave load at a time (one octet per lane)
-    const long nocts = (V + 7) / 8;
-    int pick = -1;
-    int lastpos = -1;               // last element of the tile with positive mass so far
-    double lrun0 = tpre;            // running total before the current wave load
-    for (int sl = 0; sl < kTileLoads && pick < 0; ++sl) {
-      const long o = ((long)tile * kTileLoads + sl) * kWave + l;
-      float r[8];
-      octet_mass<LT, VEC>(zrow, qrow, o, V, nocts, residual, c, Mc32, inv_s, r);
-      int lastj = -1;
-      for (int j = 7; j >= 0; --j) if (r[j] > 0.f) { lastj = (int)(o * 8 + j); break; }
-      const unsigned long long anyp = __ballot(lastj >= 0);
-      if (anyp) lastpos = __shfl(lastj, 63 - __clzll((long long)anyp));
-      if (fallback) continue;
-      const double ls = (double)tree_sum8(r);
-      const double lincl = wave_inclusive_scan(ls);
-      double lexcl = __shfl_up(lincl, 1);
-      if (l == 0) lexcl = 0.0;
-      const unsigned long long cross = __ballot(lrun0 + lincl > target);
-      if (cross) {
-        const int src = __ffsll((long long)cross) - 1;
-        int mine = -1;
-        if (l == src) {
-          double lrun = lrun0 + lexcl;
-          for (int j = 0; j < 8; ++j) {
-            lrun += (double)r[j];
-            if (r[j] > 0.f && lrun > target) { mine = (int)(o * 8 + j); break; }
-          }
-          if (mine < 0)
-            for (int j = 7; j >= 0; --j) if (r[j] > 0.f) { mine = (int)(o * 8 + j); break; }
+  // rescan the tile: load its kTileLoads wave loads at once, then walk them
+  float r[kTileLoads][8];
+#pragma unroll
+  for (int sl = 0; sl < kTileLoads; ++sl) {
+    const long o = ((long)tile * kTileLoads + sl) * kWave + l;
+    octet_mass<LT, VEC>(R.zrow, R.qrow, o, V, nocts, residual, R.c, R.Mc32, R.inv_s, r[sl]);
+  }
+  int pick = -1, lastpos = -1;
+  double lrun0 = tpre;               // running total before the current wave load
+#pragma unroll
+  for (int sl = 0; sl < kTileLoads; ++sl) {
+    const long o = ((long)tile * kTileLoads + sl) * kWave + l;
+    int lastj = -1;
+    for (int j = 7; j >= 0; --j) if (r[sl][j] > 0.f) { lastj = (int)(o * 8 + j); break; }
+    const unsigned long long anyp = __ballot(lastj >= 0);
+    if (anyp) lastpos = __shfl(lastj, 63 - __clzll((long long)anyp));
+    if (fallback || pick >= 0) continue;
+    const double ls = (double)tree_sum8(r[sl]);
+    const double lincl = wave_inclusive_scan(ls);
+    double lexcl = __shfl_up(lincl, 1);
+    if (l == 0) lexcl = 0.0;
+    const unsigned long long cross = __ballot(lrun0 + lincl > target);
+    if (cross) {
+      const int src = __ffsll((long long)cross) - 1;
+      int mine = -1;
+      if (l == src) {
+        double lrun = lrun0 + lexcl;
+        for (int j = 0; j < 8; ++j) {
+          lrun += (double)r[sl][j];
+          if (r[sl][j] > 0.f && lrun > target) { mine = (int)(o * 8 + j); break; }
         }
-        const unsigned long long got = __ballot(mine >= 0);
-        pick = got ? __shfl(mine, __ffsll((long long)got) - 1) : lastpos;
-        if (pick < 0) pick = 0;
+        if (mine < 0)
+          for (int j = 7; j >= 0; --j) if (r[sl][j] > 0.f) { mine = (int)(o * 8 + j); break; }
       }
-      lrun0 += __shfl(lincl, kWave - 1);
+      const unsigned long long got = __ballot(mine >= 0);
+      pick = got ? __shfl(mine, __ffsll((long long)got) - 1) : lastpos;
+      if (pick < 0) pick = 0;
     }
-    // rounding left u*S at or past the tile's total: its last positive element
-    if (pick < 0) pick = lastpos >= 0 ? lastpos : 0;
-    if (l == 0) sm_pick = pick;
+    lrun0 += __shfl(lincl, kWave - 1);
   }
-  __syncthreads();
-  if (threadIdx.x == 0) A.sc.out_tokens[(long)b * (K + 1) + a] = sm_pick;
-  // leave this sequence's part of the workspace cleared (every chunk read
-  // its scan result before it took its ticket)
-  for (int i = threadIdx.x; i < T; i += kThreads) st_coherent(&tsum_g[i], 0.f);
-  for (int i = threadIdx.x; i < C; i += kThreads) st_coherent(&csum_g[i], 0.0);
-  if (threadIdx.x == 0) {
-    st_coherent(&A.tickets[b], 0);
-    A.sc.info[b] = ScanResult{0, 0, 0.f, 0.0};
-  }
+  // rounding left u*S at or past the tile's total: its last positive element
+  if (pick < 0) pick = lastpos >= 0 ? lastpos : 0;
+  if (l == 0) A.sc.out_tokens[(long)b * (K + 1) + R.a] = pick;
+  // leave this sequence's part of the workspace cleared
+  for (int i = l; i < T; i += kWave) st_coherent(&tsum_g[i], 0.f);
+  for (int i = l; i < C; i += kWave) st_coherent(&csum_g[i], 0.0);
+  if (l == 0) A.sc.info[b] = ScanResult{0, 0, 0.f, 0.0};
 }
 
 // ----------------------------------------------------------------------------
@@ -670,7 +673,7 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   R.octets = (L.V + 7) / 8;
   R.partials = partials;
   const dim3 grid1((unsigned)((long)L.B * (L.K + 1) * lay.S));
-  trace_before(stream);
+  trace_before(stream, L.sample ? SV_KERNEL_VERIFY_SAMPLE_ROWS : SV_KERNEL_VERIFY_GREEDY_ROWS);
 #define SV_ROWS(LT, MODE, VEC) hipLaunchKernelGGL((verify_rows<LT, MODE, VEC>), grid1, block, 0, stream, R)
   if (L.bf16) {
     if (L.sample) { if (L.vec) SV_ROWS(uint16_t, SAMPLE, true); else SV_ROWS(uint16_t, SAMPLE, false); }
@@ -699,7 +702,7 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
 
   sc.info = reinterpret_cast<ScanResult*>(ws + lay.info);
   const dim3 grid_acc((unsigned)((L.B + kWaves - 1) / kWaves));
-  trace_before(stream);
+  trace_before(stream, L.sample ? SV_KERNEL_VERIFY_SAMPLE_ACCEPT : SV_KERNEL_VERIFY_GREEDY_ACCEPT);
   if (L.bf16) {
     if (L.sample) hipLaunchKernelGGL((verify_accept<uint16_t, SAMPLE>), grid_acc, block, 0, stream, sc);
     else hipLaunchKernelGGL((verify_accept<uint16_t, GREEDY>), grid_acc, block, 0, stream, sc);
@@ -714,20 +717,30 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   DrawArgs D;
   D.sc = sc;
   D.C = lay.C; D.T = lay.T;
-  D.tickets = reinterpret_cast<int*>(ws + lay.tickets);
   D.chunk_sums = reinterpret_cast<double*>(ws + lay.chunk);
   D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
-  const dim3 grid2((unsigned)((long)L.B * lay.C));
-  trace_before(stream);
+  const dim3 grid3((unsigned)((long)L.B * lay.C));
+  trace_before(stream, SV_KERNEL_VERIFY_SAMPLE_DRAW);
   if (L.bf16) {
-    if (L.vec) hipLaunchKernelGGL((verify_draw<uint16_t, true>), grid2, block, 0, stream, D);
-    else hipLaunchKernelGGL((verify_draw<uint16_t, false>), grid2, block, 0, stream, D);
+    if (L.vec) hipLaunchKernelGGL((verify_draw<uint16_t, true>), grid3, block, 0, stream, D);
+    else hipLaunchKernelGGL((verify_draw<uint16_t, false>), grid3, block, 0, stream, D);
   } else {
-    if (L.vec) hipLaunchKernelGGL((verify_draw<float, true>), grid2, block, 0, stream, D);
-    else hipLaunchKernelGGL((verify_draw<float, false>), grid2, block, 0, stream, D);
+    if (L.vec) hipLaunchKernelGGL((verify_draw<float, true>), grid3, block, 0, stream, D);
+    else hipLaunchKernelGGL((verify_draw<float, false>), grid3, block, 0, stream, D);
   }
   err = hipGetLastError();
   trace_after(stream, SV_KERNEL_VERIFY_SAMPLE_DRAW);
+  if (err != hipSuccess) return err;
+  trace_before(stream, SV_KERNEL_VERIFY_SAMPLE_LOCATE);
+  if (L.bf16) {
+    if (L.vec) hipLaunchKernelGGL((verify_locate<uint16_t, true>), grid_acc, block, 0, stream, D);
+    else hipLaunchKernelGGL((verify_locate<uint16_t, false>), grid_acc, block, 0, stream, D);
+  } else {
+    if (L.vec) hipLaunchKernelGGL((verify_locate<float, true>), grid_acc, block, 0, stream, D);
+    else hipLaunchKernelGGL((verify_locate<float, false>), grid_acc, block, 0, stream, D);
+  }
+  err = hipGetLastError();
+  trace_after(stream, SV_KERNEL_VERIFY_SAMPLE_LOCATE);
   return err;
 }
 

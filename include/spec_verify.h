@@ -131,8 +131,9 @@ SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
  *                    (NULL = not written).
  * Arithmetic: fp32 exponentials, fp64 accumulation of every sum and of the
  * acceptance ratio; results agree with an fp64 evaluation except when a
- * decision lies within ~1e-6 of its threshold.  Three kernels are enqueued:
- * row statistics, the accept scan, the draw of the new token.
+ * decision lies within ~1e-6 of its threshold.  Four kernels are enqueued:
+ * row statistics, the accept scan, the residual / bonus masses of row a, and
+ * the draw of the new token from them.
  */
 SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
                                     const float* draft_probs,
@@ -187,22 +188,24 @@ SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,
 
 /*
  * Kernel tracing, a profiling aid.  While tracing is on for the calling host
- * thread, every kernel the library enqueues is bracketed by two HIP timing
- * events recorded on the kernel's own stream, for up to `capacity` launches
- * (later launches are not traced).  After the stream has completed, entry i
- * gives the kernel's id and its duration in milliseconds.  sv_trace_begin
- * creates the events (it may be called again to start over); sv_trace_end
- * destroys them.  Tracing adds two event records per launch and nothing else.
+ * thread, every kernel the library enqueues whose id is set in `kernel_mask`
+ * (bit i = kernel id i; ~0u = all) is bracketed by two HIP timing events
+ * recorded on the kernel's own stream, for up to `capacity` launches (later
+ * launches are not traced).  After the stream has completed, entry i gives
+ * the kernel's id and its duration in milliseconds.  sv_trace_begin creates
+ * the events (it may be called again to start over); sv_trace_end destroys
+ * them.  Tracing adds two event records per traced launch and nothing else.
  */
 #define SV_KERNEL_VERIFY_GREEDY_ROWS 0   /* spec_verify_greedy: row max / argmax         */
 #define SV_KERNEL_VERIFY_SAMPLE_ROWS 1   /* spec_verify_sample: row max / sum of exp     */
-#define SV_KERNEL_VERIFY_SAMPLE_DRAW 2   /* spec_verify_sample: residual / bonus draw    */
+#define SV_KERNEL_VERIFY_SAMPLE_DRAW 2   /* spec_verify_sample: residual / bonus masses  */
 #define SV_KERNEL_PEAGLE_BUILD 3         /* peagle_build_draft_batch                     */
 #define SV_KERNEL_VERIFY_GREEDY_ACCEPT 4 /* spec_verify_greedy: accept scan              */
 #define SV_KERNEL_VERIFY_SAMPLE_ACCEPT 5 /* spec_verify_sample: accept scan              */
+#define SV_KERNEL_VERIFY_SAMPLE_LOCATE 6 /* spec_verify_sample: locate the drawn token   */
 
 SV_API const char* sv_kernel_name(int kernel_id);
-SV_API sv_status sv_trace_begin(int capacity);       /* SV_ERR_VALUE if capacity < 1   */
+SV_API sv_status sv_trace_begin(int capacity, unsigned kernel_mask); /* SV_ERR_VALUE if capacity < 1 */
 SV_API int sv_trace_count(void);                     /* launches traced so far         */
 SV_API sv_status sv_trace_read(int i, int* kernel_id, float* ms);  /* waits for entry i */
 SV_API void sv_trace_end(void);

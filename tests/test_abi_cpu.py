@@ -168,14 +168,17 @@ def test_binding_refuses_cpu_tensors(lib):
 
 def test_tracer_host_paths(lib):
     import ctypes
-    assert lib.sv_trace_begin(0) == EVALUE          # rejected before any HIP call
-    assert lib.sv_trace_begin(-4) == EVALUE
+    assert lib.sv_trace_begin(0, 0xFFFFFFFF) == EVALUE      # rejected before any HIP call
+    assert lib.sv_trace_begin(-4, 1) == EVALUE
     assert lib.sv_trace_count() == 0
     kid, ms = ctypes.c_int(), ctypes.c_float()
     assert lib.sv_trace_read(0, ctypes.byref(kid), ctypes.byref(ms)) == EVALUE
     assert lib.sv_trace_read(0, None, None) == ENULL
-    names = [lib.sv_kernel_name(i) for i in range(6)]
+    import draft_verification_vocab_amd as sv
+    assert all(lib.sv_kernel_name(i).decode() == n for n, i in sv.KERNEL_IDS.items())
+    names = [lib.sv_kernel_name(i) for i in range(7)]
     assert names == [b"verify_greedy_rows", b"verify_sample_rows", b"verify_sample_draw",
-                     b"peagle_build", b"verify_greedy_accept", b"verify_sample_accept"]
+                     b"peagle_build", b"verify_greedy_accept", b"verify_sample_accept",
+                     b"verify_sample_locate"]
     assert lib.sv_kernel_name(17) == b"unknown"
     lib.sv_trace_end()                              # harmless when tracing is off
