@@ -16,6 +16,11 @@
 // copy / scatter / insert / pad / mask / remap operations and the dedicated
 // broadcast copy that the P-EAGLE / TorchSpec blog summary describes (section
 // TorchSpec 集成与工程优化).
+//
+// The hidden rows are written with non-temporal stores: the drafter reads
+// them in a later launch, and ordinary stores leave ~60 MB of dirty lines in
+// the memory-side cache that the next verify step's scattered row reads then
+// evict, which was measured to slow that step's residual-draw kernel by ~18%.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -81,8 +86,8 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs A) {
       for (int j = 0; j < kCopyUnroll; ++j) {
         const long e = e0 + l + (long)j * kWave;
         if (e < nvec) {
-          d[e] = vs[j];
-          if (mask_row) dm[e] = vh[j];
+          __builtin_nontemporal_store(vs[j], d + e);
+          if (mask_row) __builtin_nontemporal_store(vh[j], dm + e);
         }
       }
       const long next = e0 + (long)kCopyUnroll * kWave;
@@ -138,8 +143,8 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs A) {
     uint32_t* d = reinterpret_cast<uint32_t*>(out + dst_row * row_bytes);
     uint32_t* dm = reinterpret_cast<uint32_t*>(out + mrow * row_bytes);
     for (long e = l; e < L.H; e += kWave) {
-      d[e] = s[e];
-      if (mask_row) dm[e] = h[e];
+      __builtin_nontemporal_store(s[e], d + e);
+      if (mask_row) __builtin_nontemporal_store(h[e], dm + e);
     }
   } else {
     const uint16_t* s = reinterpret_cast<const uint16_t*>(src);
@@ -147,8 +152,8 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs A) {
     uint16_t* d = reinterpret_cast<uint16_t*>(out + dst_row * row_bytes);
     uint16_t* dm = reinterpret_cast<uint16_t*>(out + mrow * row_bytes);
     for (long e = l; e < L.H; e += kWave) {
-      d[e] = s[e];
-      if (mask_row) dm[e] = h[e];
+      __builtin_nontemporal_store(s[e], d + e);
+      if (mask_row) __builtin_nontemporal_store(h[e], dm + e);
     }
   }
   const int64_t Lpos = L.start_pos[b];
