@@ -19,6 +19,12 @@ of Eagle / MTP / DFlash / DSPark):
   enumeration of the output law on tiny vocabularies, chi-square and binomial
   tests, closed forms for the acceptance rate and mean accepted length, and
   special cases (q = p, q one-hot on a zero of p, disjoint supports).
+* ``draft.draft_sample``          the drafter's K prediction rows per sequence
+  -> draft tokens and draft probabilities q for the next verify (softmax at
+  the request's temperature, inverse-CDF draw; T = 0 drafts greedily).
+  Pinned by scipy's softmax, numpy's searchsorted, cell-midpoint brute force,
+  chi-square, and by the end-to-end law: drafting with it and verifying with
+  ``verify_sample`` emits tokens distributed as the target.
 * ``peagle.build_draft_batch``    the P-EAGLE drafter batch.  Pinned by the
   invariants the P-EAGLE summary fixes (K-1 MASK rows per sequence, slot -1
   exactly on rejected tokens, h_shared on the MASK rows, the new token paired
@@ -27,7 +33,8 @@ of Eagle / MTP / DFlash / DSPark):
   the rejected padding rows are readings the pages leave open: those two
   aspects are parity unpinned by the pages.
 """
-from . import peagle, verify  # noqa: F401
+from . import draft, peagle, verify  # noqa: F401
+from .draft import draft_distribution, draft_outcomes, draft_sample  # noqa: F401
 from .peagle import PADDING_SLOT_ID, build_draft_batch  # noqa: F401
 from .verify import (  # noqa: F401
     decode_logits,

@@ -13,6 +13,10 @@ from .workloads import (  # noqa: F401
     make_build_inputs,
     make_verify_inputs,
     make_fused_inputs,
+    DraftInputs,
+    DraftSpec,
+    DRAFT_CONFIGS,
+    make_draft_inputs,
     verify_config,
     build_config,
     CONFIG_NAMES,

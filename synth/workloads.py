@@ -116,7 +116,7 @@ def _global_rng(seed: int, tag: int = 1) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(tag,))))
 
 
-def _zipf_head(spec: VerifySpec) -> np.ndarray:
+def _zipf_head(spec) -> np.ndarray:
     """6 / rank(v) with rank from one seeded permutation of the vocabulary."""
     g = _global_rng(spec.seed)
     perm = g.permutation(spec.V)                 # perm[r] = token of rank r+1
@@ -280,3 +280,70 @@ def make_fused_inputs(workers: Optional[int] = None):
     bi.draft_tokens = vi.draft_tokens
     return vi, bi
 
+
+
+# ---------------------------------------------------------------- drafter outputs
+@dataclasses.dataclass(frozen=True)
+class DraftSpec:
+    """Drafter prediction rows to be sampled into the next verify's drafts.
+
+    rows_per_seq = K: the logits hold exactly the K prediction rows of each
+    sequence (row b*K + k).  rows_per_seq > K: the logits hold every row of
+    the drafter batch and ``row_index`` picks K distinct rows per sequence.
+    mixed: per-sequence temperatures from {0 (greedy), 0.5, 0.7, 1.0, 1.3}.
+    """
+    name: str
+    B: int
+    K: int
+    V: int
+    dtype: str
+    sigma: float
+    boost: str
+    temperature: float
+    rows_per_seq: int
+    mixed: bool
+    seed: int
+
+
+DRAFT_CONFIGS = {
+    "draft-tiny": DraftSpec("draft-tiny", 2, 3, 32, "f32", 2.0, "none", 1.0, 3, False, 11),
+    "draft-ragged": DraftSpec("draft-ragged", 5, 4, 30011, "bf16", 3.0, "zipf-head", 0.7, 8,
+                              True, 12),
+    "draft-mid": DraftSpec("draft-mid", 48, 7, 151936, "bf16", 3.0, "zipf-head", 0.7, 7, False, 13),
+}
+
+
+@dataclasses.dataclass
+class DraftInputs:
+    spec: DraftSpec
+    logits: np.ndarray                  # [B*rows_per_seq, V] float32 or uint16 bf16 bits
+    uniforms: np.ndarray                # [B, K] float32
+    row_index: Optional[np.ndarray]     # [B, K] int32, or None (row b*K + k)
+    temperatures: Optional[np.ndarray]  # [B] float32, or None (the scalar temperature)
+
+    @property
+    def temperature(self) -> float:
+        return self.spec.temperature
+
+
+def make_draft_inputs(spec: DraftSpec) -> DraftInputs:
+    B, K, V, R = spec.B, spec.K, spec.V, spec.rows_per_seq
+    head = _zipf_head(spec) if spec.boost == "zipf-head" else None
+    ldt = np.uint16 if spec.dtype == "bf16" else np.float32
+    logits = np.empty((B * R, V), dtype=ldt)
+    u = np.empty((B, K), dtype=np.float32)
+    rows = np.empty((B, K), dtype=np.int32) if R > K else None
+    temps = np.empty(B, dtype=np.float32) if spec.mixed else None
+    for b in range(B):
+        rng = _seq_rng(spec.seed, b, tag=4)
+        z = rng.standard_normal((R, V), dtype=np.float32)
+        z *= np.float32(spec.sigma)
+        if head is not None:
+            z += head[None, :]
+        logits[b * R:(b + 1) * R] = f32_to_bf16_bits(z) if spec.dtype == "bf16" else z
+        u[b] = rng.random(K, dtype=np.float32)
+        if rows is not None:
+            rows[b] = b * R + rng.choice(R, size=K, replace=False)
+        if temps is not None:
+            temps[b] = np.float32(rng.choice([0.0, 0.5, 0.7, 1.0, 1.3]))
+    return DraftInputs(spec, logits, u, rows, temps)

@@ -123,3 +123,31 @@ def test_build_mutant_fails_invariants(label, funcs, old, new):
         res = m.build_draft_batch(**case)
         check_invariants(res, case, K)
         check_slots_dense(res, case, K)
+
+
+DRAFT_MUTANTS = [
+    ("drafter temperature ignored", ["draft_distribution"], "target_distribution(z, T)",
+     "target_distribution(z, 1.0)"),
+    ("greedy drafting keeps the last maximum", ["draft_distribution"], "q[first_argmax(z)] = 1.0",
+     "q[len(z) - 1 - first_argmax(z[::-1])] = 1.0"),
+    ("draw with 1 - u", ["draft_sample_row"], "inverse_cdf(q, float(u))",
+     "inverse_cdf(q, 1.0 - float(u))"),
+    ("row index transposed", ["_rows"], "np.asarray(row_index, dtype=np.int64).reshape(B, K)",
+     "np.asarray(row_index, dtype=np.int64).reshape(K, B).T"),
+    ("per-sequence temperatures ignored", ["_temps"], "if temperatures is None:", "if True:"),
+    ("default rows shifted by one sequence", ["_rows"],
+     "np.arange(B * K, dtype=np.int64).reshape(B, K)",
+     "(np.arange(B * K, dtype=np.int64).reshape(B, K) + K) % (B * K)"),
+]
+
+
+@pytest.mark.parametrize("label,funcs,old,new", DRAFT_MUTANTS, ids=[m[0] for m in DRAFT_MUTANTS])
+def test_draft_mutant_fails_pins(label, funcs, old, new):
+    import oracle.draft as odraft
+    from tests.test_oracle_draft import check_module
+    m = _mutant_module(odraft, funcs, old, new)
+    try:
+        fails = check_module(m)
+    except (AssertionError, IndexError, ValueError):
+        fails = ["raised"]
+    assert fails, f"mutant '{label}' passed the drafter pins"

@@ -83,3 +83,24 @@ def test_build_inputs_shapes():
         a = bi.num_accepted[b]
         assert np.array_equal(bi.out_tokens[b, :a], bi.draft_tokens[b, :a])
         assert np.all(bi.out_tokens[b, a + 1:] == -1)
+
+
+def test_draft_inputs_shapes_and_determinism():
+    from synth.workloads import DRAFT_CONFIGS, make_draft_inputs
+    spec = DRAFT_CONFIGS["draft-ragged"]
+    a = make_draft_inputs(spec)
+    b = make_draft_inputs(spec)
+    B, K, V, R = spec.B, spec.K, spec.V, spec.rows_per_seq
+    assert a.logits.shape == (B * R, V) and a.logits.dtype == np.uint16
+    assert np.array_equal(a.logits, b.logits) and np.array_equal(a.uniforms, b.uniforms)
+    assert a.uniforms.shape == (B, K) and a.uniforms.dtype == np.float32
+    assert ((a.uniforms >= 0) & (a.uniforms < 1)).all()
+    # K distinct rows per sequence, all inside that sequence's block of rows
+    for s in range(B):
+        r = a.row_index[s]
+        assert len(set(r.tolist())) == K
+        assert ((r >= s * R) & (r < (s + 1) * R)).all()
+    assert set(a.temperatures.tolist()) <= {0.0, 0.5, 0.7, 1.0, 1.3}
+    assert a.temperatures.dtype == np.float32
+    t = make_draft_inputs(DRAFT_CONFIGS["draft-tiny"])
+    assert t.row_index is None and t.temperatures is None and t.logits.dtype == np.float32
