@@ -100,7 +100,7 @@ def test_draft_inputs_shapes_and_determinism():
         r = a.row_index[s]
         assert len(set(r.tolist())) == K
         assert ((r >= s * R) & (r < (s + 1) * R)).all()
-    assert set(a.temperatures.tolist()) <= {0.0, 0.5, 0.7, 1.0, 1.3}
+    assert set(a.temperatures.tolist()) <= set(np.float32([0.0, 0.5, 0.7, 1.0, 1.3]).tolist())
     assert a.temperatures.dtype == np.float32
     t = make_draft_inputs(DRAFT_CONFIGS["draft-tiny"])
     assert t.row_index is None and t.temperatures is None and t.logits.dtype == np.float32
