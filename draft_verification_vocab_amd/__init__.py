@@ -27,6 +27,7 @@ __all__ = [
 SV_F32, SV_BF16, SV_F16 = 0, 1, 2
 PADDING_SLOT_ID = -1
 DEVERR_DRAFT_TOKEN, DEVERR_ACCEPT_COUNT, DEVERR_BLOCK_TABLE = 1, 2, 4
+DEVERR_ROW_INDEX, DEVERR_TEMPERATURE = 8, 16
 MAX_K = 63
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +45,8 @@ _SIGS = {
                                 ctypes.c_size_t, _p, _p]),
     "peagle_build_draft_batch": (_i, [_p, _p, _p, _p, _p, _i, _i, _p, _p, _i, ctypes.c_int32,
                                       _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
+    "spec_draft_sample": (_i, [_p, _i, ctypes.c_int64, _p, _p, ctypes.c_float, _p, _i, _i, _i,
+                               _p, _p, _p, _p]),
     "sv_kernel_name": (ctypes.c_char_p, [_i]),
     "sv_trace_begin": (_i, [_i, ctypes.c_uint]),
     "sv_trace_count": (_i, []),
@@ -93,7 +96,7 @@ def _check(status: int, what: str):
 # ---------------------------------------------------------------- tracing
 KERNEL_IDS = {"verify_greedy_rows": 0, "verify_sample_rows": 1, "verify_sample_draw": 2,
               "peagle_build": 3, "verify_greedy_accept": 4, "verify_sample_accept": 5,
-              "verify_sample_locate": 6}
+              "verify_sample_locate": 6, "draft_sample": 7}
 
 
 def trace_begin(capacity: int, kernels=None):
@@ -302,3 +305,56 @@ def peagle_build_draft_batch(verify_out_tokens: torch.Tensor, num_accepted: torc
         _ptr(device_error), _stream(dev))
     _check(st, "peagle_build_draft_batch")
     return o
+
+
+# ---------------------------------------------------------------- drafter outputs
+def spec_draft_sample(drafter_logits: torch.Tensor, K: int, temperature: float,
+                      uniforms: Optional[torch.Tensor] = None,
+                      row_index: Optional[torch.Tensor] = None,
+                      temperatures: Optional[torch.Tensor] = None,
+                      out_draft_tokens: Optional[torch.Tensor] = None,
+                      out_draft_probs: Optional[torch.Tensor] = None,
+                      want_draft_probs: bool = True,
+                      device_error: Optional[torch.Tensor] = None):
+    """Sample the drafter's prediction rows; see spec_draft_sample in
+    include/spec_verify.h.  drafter_logits is [n_rows, V]; B is taken from
+    row_index ([B, K]) when given, else n_rows // K.
+
+    Returns (draft_tokens [B, K] int32, draft_probs [B, K, V] fp32 or None).
+    """
+    lib = require_library()
+    if drafter_logits.dim() != 2:
+        raise ValueError("drafter_logits must be [n_rows, V]")
+    n_rows, V = drafter_logits.shape
+    dev = drafter_logits.device
+    _dev(drafter_logits, "drafter_logits")
+    if drafter_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("drafter_logits must be float32 or bfloat16")
+    if row_index is not None:
+        if row_index.dim() != 2 or row_index.shape[1] != K:
+            raise ValueError("row_index must be [B, K]")
+        B = row_index.shape[0]
+        _dev(row_index, "row_index", torch.int32, (B, K), dev)
+    else:
+        if K < 1 or n_rows % K:
+            raise ValueError("without row_index, n_rows must be a multiple of K")
+        B = n_rows // K
+    if uniforms is not None:
+        _dev(uniforms, "uniforms", torch.float32, (B, K), dev)
+    if temperatures is not None:
+        _dev(temperatures, "temperatures", torch.float32, (B,), dev)
+    out_draft_tokens = torch.empty((B, K), dtype=torch.int32, device=dev) \
+        if out_draft_tokens is None else _dev(out_draft_tokens, "out_draft_tokens", torch.int32,
+                                             (B, K), dev)
+    if out_draft_probs is None and want_draft_probs:
+        out_draft_probs = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    if out_draft_probs is not None:
+        _dev(out_draft_probs, "out_draft_probs", torch.float32, (B, K, V), dev)
+    if device_error is not None:
+        _dev(device_error, "device_error", torch.int32, (1,), dev)
+    st = lib.spec_draft_sample(_ptr(drafter_logits), _DTYPES[drafter_logits.dtype], n_rows,
+                               _ptr(row_index), _ptr(uniforms), float(temperature),
+                               _ptr(temperatures), B, K, V, _ptr(out_draft_tokens),
+                               _ptr(out_draft_probs), _ptr(device_error), _stream(dev))
+    _check(st, "spec_draft_sample")
+    return out_draft_tokens, out_draft_probs

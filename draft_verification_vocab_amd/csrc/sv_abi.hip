@@ -85,6 +85,7 @@ SV_API const char* sv_kernel_name(int kernel_id) {
     case SV_KERNEL_VERIFY_GREEDY_ACCEPT: return "verify_greedy_accept";
     case SV_KERNEL_VERIFY_SAMPLE_ACCEPT: return "verify_sample_accept";
     case SV_KERNEL_VERIFY_SAMPLE_LOCATE: return "verify_sample_locate";
+    case SV_KERNEL_DRAFT_SAMPLE: return "draft_sample";
     default: return "unknown";
   }
 }
@@ -243,6 +244,46 @@ SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,
   L.out_sample_rows = out_sample_rows;
   L.device_error = device_error;
   return sv::launch_build(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype, int64_t n_rows,
+                                   const int32_t* row_index, const float* uniforms,
+                                   float temperature, const float* temperatures, int B, int K,
+                                   int V, int32_t* out_draft_tokens, float* out_draft_probs,
+                                   int32_t* device_error, void* stream) {
+  if (B < 0 || B > kMaxB || K < 1 || K > SV_MAX_K || V < 1 || V > SV_MAX_V || n_rows < 0 ||
+      n_rows > 0x7fffffffL)
+    return SV_ERR_SHAPE;
+  if (!row_index && n_rows < (int64_t)B * K) return SV_ERR_SHAPE;
+  if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (!(temperature >= 0.0f && isfinite(temperature))) return SV_ERR_VALUE;
+  if (temperature > 0.0f && !isfinite((float)(1.4426950408889634 / (double)temperature)))
+    return SV_ERR_VALUE;
+  if (B == 0) return SV_OK;
+  if (!drafter_logits || !out_draft_tokens) return SV_ERR_NULL;
+  if (!uniforms && (temperature != 0.0f || temperatures)) return SV_ERR_NULL;
+  const size_t esz = logits_dtype == SV_BF16 ? 2 : 4;
+  if (!aligned(drafter_logits, esz) || !aligned(out_draft_tokens, 4) ||
+      (row_index && !aligned(row_index, 4)) || (uniforms && !aligned(uniforms, 4)) ||
+      (temperatures && !aligned(temperatures, 4)) ||
+      (out_draft_probs && !aligned(out_draft_probs, 4)) ||
+      (device_error && !aligned(device_error, 4)))
+    return SV_ERR_ALIGN;
+  sv::DraftLaunch L;
+  L.logits = drafter_logits;
+  L.row_index = row_index;
+  L.n_rows = (long)n_rows;
+  L.uniforms = uniforms;
+  L.temperatures = temperatures;
+  L.temperature = temperature;
+  L.B = B; L.K = K; L.V = V;
+  L.bf16 = logits_dtype == SV_BF16;
+  L.vec = (V % 8 == 0) && aligned(drafter_logits, 16) &&
+          (!out_draft_probs || aligned(out_draft_probs, 16));
+  L.out_tokens = out_draft_tokens;
+  L.out_probs = out_draft_probs;
+  L.device_error = device_error;
+  return sv::launch_draft(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 }  // extern "C"

@@ -47,6 +47,21 @@ struct BuildLaunch {
   int32_t* device_error;         // may be NULL
 };
 
+struct DraftLaunch {
+  const void* logits;            // [n_rows][V]
+  const int32_t* row_index;      // [B*K] or NULL
+  long n_rows;
+  const float* uniforms;         // [B*K]
+  const float* temperatures;     // [B] or NULL
+  float temperature;
+  int B, K, V;
+  int bf16;
+  int vec;                       // 16-byte vector loads / stores are legal for every row
+  int32_t* out_tokens;
+  float* out_probs;              // may be NULL
+  int32_t* device_error;         // may be NULL
+};
+
 int verify_splits(int B, int K, int V);
 
 // Kernel tracing (per host thread): bracket a launch with events on its stream.
@@ -55,5 +70,6 @@ void trace_after(hipStream_t stream, int kernel_id);
 size_t verify_workspace_bytes(int B, int K, int V);
 hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream);
 hipError_t launch_build(const BuildLaunch& L, hipStream_t stream);
+hipError_t launch_draft(const DraftLaunch& L, hipStream_t stream);
 
 }  // namespace sv

@@ -72,6 +72,12 @@ typedef enum {
 #define SV_DEVERR_ACCEPT_COUNT 2  /* num_accepted outside [0, K]: clamped into range    */
 #define SV_DEVERR_BLOCK_TABLE 4   /* a position past the block table, or a negative
                                      block id: that row gets slot -1                   */
+#define SV_DEVERR_ROW_INDEX 8     /* spec_draft_sample: a row index outside
+                                     [0, n_rows): that draft gets token -1 and an
+                                     all-zero q row                                    */
+#define SV_DEVERR_TEMPERATURE 16  /* a per-sequence temperature that is negative, NaN,
+                                     infinite or too small for 1/T to be finite:
+                                     that sequence is treated as greedy (T = 0)        */
 
 /* Limits. */
 #define SV_MAX_K 63               /* drafts per sequence (K+1 rows fit one wavefront) */
@@ -187,6 +193,43 @@ SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,
                                           int32_t* device_error, void* stream);
 
 /*
+ * Drafter-output sampling: the P-EAGLE drafter's K prediction rows per
+ * sequence (the NTP row and the K-1 MASK rows, out_sample_rows above) become
+ * the K draft tokens and the drafter distribution q of the next verify.
+ * Source: the P-EAGLE / TorchSpec blog summary, section 并行架构的核心创新
+ * (one drafter forward predicts all K drafts); "Project 14", section 架构 (the
+ * drafter proposes k tokens that the target verifies).
+ * For draft k of sequence b, z = drafter_logits row row_index[b][k] (or row
+ * b*K + k when row_index is NULL) and T_b = temperatures[b] (or the scalar
+ * temperature when temperatures is NULL):
+ *   T_b > 0:  q = softmax(z / T_b); the token is the smallest v whose running
+ *             total of q in vocabulary order exceeds uniforms[b][k] * sum(q)
+ *             (inverse CDF, never a token with q = 0);
+ *   T_b = 0:  greedy drafting: the token is the lowest-index argmax of z and
+ *             q is one-hot at it.
+ *   drafter_logits   [n_rows][V], SV_F32 or SV_BF16.
+ *   row_index        optional [B][K] int32 in [0, n_rows), e.g. out_sample_rows
+ *                    of peagle_build_draft_batch; NULL needs n_rows >= B*K.
+ *   uniforms         [B][K] fp32 in [0, 1); may be NULL only when temperature
+ *                    is 0 and temperatures is NULL (every draft greedy).
+ *   temperature      finite, >= 0 (0 = greedy).
+ *   temperatures     optional [B] fp32 device array overriding `temperature`
+ *                    per sequence (bad values: SV_DEVERR_TEMPERATURE).
+ *   out_draft_tokens [B][K] int32, the draft_tokens of the next verify.
+ *   out_draft_probs  optional [B][K][V] fp32, the draft_probs of the next
+ *                    verify (NULL = not written).
+ * 1 <= K <= SV_MAX_K, 1 <= V <= SV_MAX_V; B = 0 is a no-op.  Arithmetic as in
+ * spec_verify_sample (fp32 exponentials, fp64 running totals).  One kernel is
+ * enqueued; no workspace is needed.
+ */
+SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype, int64_t n_rows,
+                                   const int32_t* row_index, const float* uniforms,
+                                   float temperature, const float* temperatures,
+                                   int B, int K, int V,
+                                   int32_t* out_draft_tokens, float* out_draft_probs,
+                                   int32_t* device_error, void* stream);
+
+/*
  * Kernel tracing, a profiling aid.  While tracing is on for the calling host
  * thread, every kernel the library enqueues whose id is set in `kernel_mask`
  * (bit i = kernel id i; ~0u = all) is bracketed by two HIP timing events
@@ -203,6 +246,7 @@ SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,
 #define SV_KERNEL_VERIFY_GREEDY_ACCEPT 4 /* spec_verify_greedy: accept scan              */
 #define SV_KERNEL_VERIFY_SAMPLE_ACCEPT 5 /* spec_verify_sample: accept scan              */
 #define SV_KERNEL_VERIFY_SAMPLE_LOCATE 6 /* spec_verify_sample: locate the drawn token   */
+#define SV_KERNEL_DRAFT_SAMPLE 7         /* spec_draft_sample                            */
 
 SV_API const char* sv_kernel_name(int kernel_id);
 SV_API sv_status sv_trace_begin(int capacity, unsigned kernel_mask); /* SV_ERR_VALUE if capacity < 1 */

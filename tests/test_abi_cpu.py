@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
-              "spec_verify_workspace_bytes", "sv_status_string"):
+              "spec_draft_sample", "spec_verify_workspace_bytes", "sv_status_string"):
         assert n in names
 
 
@@ -176,9 +176,41 @@ def test_tracer_host_paths(lib):
     assert lib.sv_trace_read(0, None, None) == ENULL
     import draft_verification_vocab_amd as sv
     assert all(lib.sv_kernel_name(i).decode() == n for n, i in sv.KERNEL_IDS.items())
-    names = [lib.sv_kernel_name(i) for i in range(7)]
+    names = [lib.sv_kernel_name(i) for i in range(8)]
     assert names == [b"verify_greedy_rows", b"verify_sample_rows", b"verify_sample_draw",
                      b"peagle_build", b"verify_greedy_accept", b"verify_sample_accept",
-                     b"verify_sample_locate"]
+                     b"verify_sample_locate", b"draft_sample"]
     assert lib.sv_kernel_name(17) == b"unknown"
     lib.sv_trace_end()                              # harmless when tracing is off
+
+
+def draft(lib, logits=FAKE, dtype=1, n_rows=6, ri=None, u=FAKE, T=0.7, temps=None, B=2, K=3,
+          V=64, tok=FAKE, probs=FAKE, err=None):
+    return lib.spec_draft_sample(logits, dtype, n_rows, ri, u, T, temps, B, K, V, tok, probs,
+                                 err, None)
+
+
+def test_draft_validation(lib):
+    assert draft(lib, K=0) == ESHAPE
+    assert draft(lib, K=64) == ESHAPE
+    assert draft(lib, V=0) == ESHAPE
+    assert draft(lib, V=(1 << 19) + 1) == ESHAPE
+    assert draft(lib, B=-1) == ESHAPE
+    assert draft(lib, n_rows=5) == ESHAPE             # fewer than B*K rows and no row index
+    assert draft(lib, n_rows=-1, ri=FAKE) == ESHAPE
+    assert draft(lib, dtype=2) == EDTYPE
+    for T in (-0.5, float("inf"), float("nan"), 1e-45):
+        assert draft(lib, T=T) == EVALUE, T
+    assert draft(lib, B=0, logits=None, u=None, tok=None, probs=None) == OK
+    assert draft(lib, logits=None) == ENULL
+    assert draft(lib, tok=None) == ENULL
+    assert draft(lib, u=None) == ENULL                 # sampled rows need uniforms
+    assert draft(lib, u=None, T=0.0, temps=FAKE) == ENULL
+    assert draft(lib, logits=FAKE + 1) == EALIGN
+    assert draft(lib, dtype=0, logits=FAKE + 2) == EALIGN
+    assert draft(lib, ri=FAKE + 2) == EALIGN
+    assert draft(lib, u=FAKE + 1) == EALIGN
+    assert draft(lib, temps=FAKE + 2) == EALIGN
+    assert draft(lib, probs=FAKE + 2) == EALIGN
+    assert draft(lib, tok=FAKE + 1) == EALIGN
+    assert draft(lib, err=FAKE + 1) == EALIGN
