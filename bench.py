@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-greedy", action="store_true")
+    ap.add_argument("--no-draft", action="store_true",
+                    help="skip timing the drafter-output sampling kernel")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run only this many untimed steps (for rocprofv3) and exit; inputs are "
                          "then drawn in this process (no worker processes under a profiler)")
@@ -219,6 +221,22 @@ def main():
              "hidden": torch.empty((B * 2 * K, H), dtype=torch.bfloat16, device=dev),
              "sample_rows": torch.empty((B, K), dtype=torch.int32, device=dev)}
 
+    # drafter-output sampling: K prediction rows per sequence.  The synthetic
+    # drafter rows are the first K logit rows of each sequence (same recipe:
+    # bf16, 3*N(0,1) + Zipf head), gathered through a row index as the drafter
+    # batch's sample_rows would be.
+    d_rows = (torch.arange(B, dtype=torch.int32, device=dev)[:, None] * (K + 1)
+              + torch.arange(K, dtype=torch.int32, device=dev)[None, :]).contiguous()
+    d_u = up(np.random.default_rng(7).random((B, K), dtype=np.float32))
+    d_tok = torch.empty((B, K), dtype=torch.int32, device=dev)
+    d_q = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    z_rows = z.view(B * (K + 1), V)
+
+    def draft(with_q=True):
+        sv.spec_draft_sample(z_rows, K, vi.temperature, uniforms=d_u, row_index=d_rows,
+                             out_draft_tokens=d_tok, out_draft_probs=d_q if with_q else None,
+                             want_draft_probs=with_q)
+
     def step(sample=True):
         if sample:
             sv.spec_verify_sample(z, q, d, u, vi.temperature, out_tokens=out_t,
@@ -232,7 +250,7 @@ def main():
 
     if args.profile_steps:
         for i in range(args.profile_steps):
-            step(True); build(); step(False); build()
+            step(True); build(); step(False); build(); draft()
         torch.cuda.synchronize()
         # calibration for HBM byte counters: one plain copy of 1 GiB
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -334,6 +352,27 @@ def main():
                               "peagle_build_ms": kmsg["peagle_build"],
                               "step_hbm_gbs": (vg_rows + vg_scan + bb) / sec_g / 1e9,
                               "step_hbm_frac": (vg_rows + vg_scan + bb) / sec_g / 1e9 / HBM_PEAK_GBS}
+    if not args.no_draft:
+        def timed_draft(with_q):
+            for _ in range(args.warmup):
+                draft(with_q)
+            torch.cuda.synchronize()
+            sv.trace_begin(args.steps, ["draft_sample"])
+            for _ in range(args.steps):
+                draft(with_q)
+            torch.cuda.synchronize()
+            ms = float(np.mean([m for _, m in sv.trace_read()]))
+            sv.trace_end()
+            nbytes = B * K * (V * 2 + (V * 4 if with_q else 0) + 12)
+            return {"avg_ms": ms, "rows_per_s": B * K / (ms * 1e-3), "algorithmic_bytes": nbytes,
+                    "gbs": nbytes / (ms * 1e-3) / 1e9,
+                    "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        res["draft_sample"] = {
+            "workload": f"drafter-output sampling B={B} K={K} V={V} bf16 T={vi.temperature}: "
+                        "K draft tokens per sequence and their fp32 distributions",
+            "with_probs": timed_draft(True),
+            "tokens_only": timed_draft(False)}
+        log("drafter sampling timed")
     if args.cpu_budget > 0:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(vi, bi, args.cpu_budget)

@@ -6,14 +6,17 @@
 // the target verifies).
 //
 // One workgroup per draft (b, k); no workgroup hands anything to another.
-//   sweep 1  streams the drafter logit row and reduces it to its max and sum
-//            of exponentials at the sequence's temperature, or to its
-//            lowest-index argmax when that temperature is 0 (greedy);
-//   sweep 2  streams the row again, writes q = softmax(z / T) as fp32 and
-//            keeps the mass of every 2048-element CDF tile in LDS;
-//   locate   one wave finds the tile whose running total first exceeds u * S,
-//            rescans that tile and writes the token.
-// Greedy rows skip sweep 2's loads: q is the one-hot of the argmax.
+//   sweep 1  streams the drafter logit row once and keeps, for every
+//            2048-element CDF tile, its max and its sum of exponentials at the
+//            sequence's temperature (LDS); the row's max and sum follow from
+//            them.  With temperature 0 (greedy) it finds the lowest-index
+//            argmax instead.
+//   sweep 2  only when q is requested: streams the row again and writes
+//            q = softmax(z / T) as fp32;
+//   locate   one wave finds the tile whose running mass first exceeds u,
+//            rescans that one tile and writes the token.
+// Without q the row is read once with one exponential per element.  Greedy
+// rows need no exponentials: q is the one-hot of the argmax.
 // The q rows are written with non-temporal stores: the next verify reads only
 // a few of their elements and one row per sequence.
 #include "sv_device.h"
@@ -22,8 +25,10 @@
 
 namespace sv {
 
-constexpr int kDraftThreads = 512;      // 8 waves
-constexpr int kDraftWaves = kDraftThreads / kWave;
+// Workgroup size: 512 threads when q is written (measured 1.49 vs 1.83 ms
+// with 256 at 1024 x 7 x 151936), 256 when only tokens are drawn.
+template <bool WQ> constexpr int draft_threads() { return WQ ? 512 : 256; }
+constexpr int kDraftTilesPerStep = 2;  // sweep 1: CDF tiles per wave in flight
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -96,9 +101,9 @@ __device__ __forceinline__ void store_q(float* qrow, long o, long V, const float
 }
 
 // Whole q row: the one-hot of g (g < 0: all zero), stores only.
-template <bool VEC>
+template <bool VEC, int THREADS>
 __device__ void store_one_hot(float* qrow, long V, long nocts, int g) {
-  for (long o = threadIdx.x; o < nocts; o += kDraftThreads) {
+  for (long o = threadIdx.x; o < nocts; o += THREADS) {
     float q[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) q[j] = (o * 8 + j == g) ? 1.f : 0.f;
@@ -106,20 +111,88 @@ __device__ void store_one_hot(float* qrow, long V, long nocts, int g) {
   }
 }
 
-template <typename LT, bool VEC>
-__global__ __launch_bounds__(kDraftThreads) void draft_sample_kernel(DraftArgs A) {
-  __shared__ float sm_f[kDraftWaves];
-  __shared__ int sm_i[kDraftWaves];
-  __shared__ double sm_d[kDraftWaves];
+// Sweep 1 of a sampled row: the max m_t and the sum s_t of 2^(z c - m_t c)
+// of every CDF tile, one wave per tile (kDraftTilesPerStep tiles in flight).
+// NT: non-temporal loads, for a row that is not read again (without q);
+// with q, sweep 2 reads the row again at once and cached loads serve it.
+template <typename LT, bool VEC, int WAVES, bool NT>
+__device__ __forceinline__ void tile_stats(const LT* zrow, long V, long nocts, int T_tiles, float c,
+                                           float* tile_m, float* tile_s) {
+  const int w = threadIdx.x / kWave, l = lane_id();
+  for (int t0 = w * kDraftTilesPerStep; t0 < T_tiles; t0 += WAVES * kDraftTilesPerStep) {
+    float z[kDraftTilesPerStep][kTileLoads][8];
+    if constexpr (VEC) {
+      Raw<LT> raw[kDraftTilesPerStep][kTileLoads];
+#pragma unroll
+      for (int j = 0; j < kDraftTilesPerStep; ++j)
+#pragma unroll
+        for (int sl = 0; sl < kTileLoads; ++sl) {
+          const long o = ((long)(t0 + j) * kTileLoads + sl) * kWave + l;
+          raw_load<NT>(zrow, o < nocts ? o : nocts - 1, raw[j][sl]);
+        }
+#pragma unroll
+      for (int j = 0; j < kDraftTilesPerStep; ++j)
+#pragma unroll
+        for (int sl = 0; sl < kTileLoads; ++sl) {
+          const long o = ((long)(t0 + j) * kTileLoads + sl) * kWave + l;
+          unpack(raw[j][sl], z[j][sl]);
+          if (o >= nocts)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[j][sl][e] = -INFINITY;
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kDraftTilesPerStep; ++j)
+#pragma unroll
+        for (int sl = 0; sl < kTileLoads; ++sl) {
+          const long o = ((long)(t0 + j) * kTileLoads + sl) * kWave + l;
+          load_octet<false>(zrow, o, V, false, -INFINITY, z[j][sl]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kDraftTilesPerStep; ++j) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int sl = 0; sl < kTileLoads; ++sl)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, z[j][sl][e]);
+      m = wave_max(m);
+      float ls = 0.f;
+      if (m != -INFINITY) {
+        const float R = m * c;
+#pragma unroll
+        for (int sl = 0; sl < kTileLoads; ++sl) {
+          float e8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) e8[e] = __builtin_amdgcn_exp2f(fmaf(z[j][sl][e], c, -R));
+          ls += tree_sum8(e8);
+        }
+      }
+      const float st = wave_sum_f(ls);
+      if (l == 0 && t0 + j < T_tiles) { tile_m[t0 + j] = m; tile_s[t0 + j] = st; }
+    }
+  }
+}
+
+// WQ: q is written (out_probs non-null).
+template <typename LT, bool VEC, bool WQ>
+__global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(DraftArgs A) {
+  constexpr int THREADS = draft_threads<WQ>();
+  constexpr int WAVES = THREADS / kWave;
+  __shared__ float sm_f[WAVES];
+  __shared__ int sm_i[WAVES];
+  __shared__ double sm_d[WAVES];
   __shared__ Partial stats;
-  __shared__ float tsum[kMaxTiles];
+  __shared__ float tile_m[kMaxTiles];
+  __shared__ float tile_s[kMaxTiles];
+  __shared__ double row_S;
 
   const long r = blockIdx.x;                    // b * K + k
   const int b = (int)(r / A.K);
   const long V = A.V;
   const long nocts = (V + 7) / 8;
   const int t = threadIdx.x, w = t / kWave, l = lane_id();
-  float* qrow = A.out_probs ? A.out_probs + r * V : nullptr;
+  float* qrow = WQ ? A.out_probs + r * V : nullptr;
 
   const long ri = A.row_index ? (long)A.row_index[r] : r;
   if (ri < 0 || ri >= A.n_rows) {
@@ -127,7 +200,7 @@ __global__ __launch_bounds__(kDraftThreads) void draft_sample_kernel(DraftArgs A
       flag_error(A.device_error, SV_DEVERR_ROW_INDEX);
       A.out_tokens[r] = -1;
     }
-    if (qrow) store_one_hot<VEC>(qrow, V, nocts, -1);
+    if constexpr (WQ) store_one_hot<VEC, THREADS>(qrow, V, nocts, -1);
     return;
   }
   const LT* zrow = static_cast<const LT*>(A.logits) + ri * V;
@@ -144,58 +217,77 @@ __global__ __launch_bounds__(kDraftThreads) void draft_sample_kernel(DraftArgs A
     }
   }
 
-  // sweep 1: row statistics (greedy -> argmax; sampling -> max, sum of 2^(zc - Mc))
-  Partial P;
-  if (greedy) P = slice_stats<LT, GREEDY, VEC, kDraftThreads>(zrow, 0, nocts, V, c, sm_f, sm_i, sm_d);
-  else P = slice_stats<LT, SAMPLE, VEC, kDraftThreads>(zrow, 0, nocts, V, c, sm_f, sm_i, sm_d);
-  if (t == 0) stats = P;
-  __syncthreads();
-  P = stats;
-
   if (greedy) {
-    const int g = P.g == INT32_MAX ? 0 : P.g;
+    // lowest-index argmax; q is its one-hot
+    const Partial P = slice_stats<LT, GREEDY, VEC, THREADS, !WQ>(zrow, 0, nocts, V, c, sm_f,
+                                                               sm_i, sm_d);
+    if (t == 0) stats = P;
+    __syncthreads();
+    const int g = stats.g == INT32_MAX ? 0 : stats.g;
     if (t == 0) A.out_tokens[r] = g;
-    if (qrow) store_one_hot<VEC>(qrow, V, nocts, g);
+    if constexpr (WQ) store_one_hot<VEC, THREADS>(qrow, V, nocts, g);
     return;
   }
 
-  // sweep 2: q and the CDF tile masses.  p = 2^(z c - Mc32) * inv_s, where
-  // Mc32 is M*c rounded to fp32 and inv_s folds that rounding back in.
-  const float Mc = P.m * c;
-  const float inv_s = (float)(exp2((double)Mc - (double)P.m * (double)c) / P.acc);
+  // sweep 1: per-tile max and sum of exponentials
   const int T_tiles = (int)((V + kTileElems - 1) / kTileElems);
-  for (int tile = w; tile < T_tiles; tile += kDraftWaves) {
-    float q[kTileLoads][8];
-    tile_q<LT, VEC>(zrow, tile, V, nocts, c, Mc, inv_s, q);
-    float ls = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < kTileLoads; ++sl) {
-      const long o = ((long)tile * kTileLoads + sl) * kWave + l;
-      if (qrow && o < nocts) store_q<VEC>(qrow, o, V, q[sl]);
-      ls += tree_sum8(q[sl]);
+  tile_stats<LT, VEC, WAVES, !WQ>(zrow, V, nocts, T_tiles, c, tile_m, tile_s);
+  __syncthreads();
+  // row max M; tile masses w_t = s_t 2^(m_t c - M c) replace s_t; row sum S
+  if (w == 0) {
+    float M = -INFINITY;
+    for (int i = l; i < T_tiles; i += kWave) M = fmaxf(M, tile_m[i]);
+    M = wave_max(M);
+    double part = 0.0;
+    for (int i = l; i < T_tiles; i += kWave) {
+      const float mt = tile_m[i];
+      const float wt = mt == -INFINITY ? 0.f
+          : (float)((double)tile_s[i] * exp2((double)(mt * c) - (double)M * (double)c));
+      tile_s[i] = wt;
+      part += (double)wt;
     }
-    const float ts = wave_sum_f(ls);
-    if (l == 0) tsum[tile] = ts;
+    const double S = wave_sum(part);
+    if (l == 0) { row_S = S; stats.m = M; }
   }
   __syncthreads();
+  const float M = stats.m;
+  const double S = row_S;
+  // p = 2^(z c - Mc32) * inv_s, where Mc32 is M*c rounded to fp32 and inv_s
+  // folds that rounding back in
+  const float Mc = M * c;
+  const float inv_s = (float)(exp2((double)Mc - (double)M * (double)c) / S);
+
+  // sweep 2 (only when q is requested): write q
+  if constexpr (WQ) {
+    for (int tile = w; tile < T_tiles; tile += WAVES) {
+      float q[kTileLoads][8];
+      tile_q<LT, VEC>(zrow, tile, V, nocts, c, Mc, inv_s, q);
+#pragma unroll
+      for (int sl = 0; sl < kTileLoads; ++sl) {
+        const long o = ((long)tile * kTileLoads + sl) * kWave + l;
+        if (o < nocts) store_q<VEC>(qrow, o, V, q[sl]);
+      }
+    }
+  }
   if (w != 0) return;
 
-  // locate: the tile holding u * S (lanes own contiguous runs of tiles) ...
+  // locate, in units of q (tile masses / S): the tile holding u (lanes own
+  // contiguous runs of tiles), then the element inside it from the q values
   const int per = (T_tiles + kWave - 1) / kWave;
   const int lo = min(T_tiles, l * per), hi = min(T_tiles, (l + 1) * per);
+  const double invS = 1.0 / S;
   double part = 0.0;
-  for (int i = lo; i < hi; ++i) part += (double)tsum[i];
+  for (int i = lo; i < hi; ++i) part += (double)tile_s[i] * invS;
   const double incl = wave_inclusive_scan(part);
-  const double S = __shfl(incl, kWave - 1);
-  const double target = (double)A.uniforms[r] * S;
+  const double target = (double)A.uniforms[r] * __shfl(incl, kWave - 1);
   double run = __shfl_up(incl, 1);
   if (l == 0) run = 0.0;
   int hit = -1, last = -1;
   double pre = 0.0;
   for (int i = lo; i < hi; ++i) {
-    const float ts = tsum[i];
-    if (ts > 0.f) last = i;
-    const double nxt = run + (double)ts;
+    const double wt = (double)tile_s[i] * invS;
+    if (wt > 0.0) last = i;
+    const double nxt = run + wt;
     if (hit < 0 && nxt > target) { hit = i; pre = run; }
     run = nxt;
   }
@@ -207,12 +299,11 @@ __global__ __launch_bounds__(kDraftThreads) void draft_sample_kernel(DraftArgs A
     tile = __shfl(hit, src);
     pre = __shfl(pre, src);
   } else {
-    // rounding left u*S at or past the total: the last tile with positive mass
+    // rounding left the target at or past the total: the last tile with mass
     const unsigned long long anyp = __ballot(last >= 0);
     tile = anyp ? __shfl(last, 63 - __clzll((long long)anyp)) : 0;
     fallback = true;
   }
-  // ... then the element inside it, from the same q values
   float q[kTileLoads][8];
   tile_q<LT, VEC>(zrow, tile, V, nocts, c, Mc, inv_s, q);
   const int pick = pick_in_tile(q, tile, pre, target, fallback);
@@ -231,15 +322,20 @@ hipError_t launch_draft(const DraftLaunch& L, hipStream_t stream) {
   A.out_tokens = L.out_tokens;
   A.out_probs = L.out_probs;
   A.device_error = L.device_error;
-  const dim3 grid((unsigned)((long)L.B * L.K)), block(kDraftThreads);
+  const dim3 grid((unsigned)((long)L.B * L.K));
+  const bool wq = L.out_probs != nullptr;
+  const dim3 block(wq ? draft_threads<true>() : draft_threads<false>());
   trace_before(stream, SV_KERNEL_DRAFT_SAMPLE);
+#define SV_DRAFT(LT, VEC, WQ) \
+  hipLaunchKernelGGL((draft_sample_kernel<LT, VEC, WQ>), grid, block, 0, stream, A)
   if (L.bf16) {
-    if (L.vec) hipLaunchKernelGGL((draft_sample_kernel<uint16_t, true>), grid, block, 0, stream, A);
-    else hipLaunchKernelGGL((draft_sample_kernel<uint16_t, false>), grid, block, 0, stream, A);
+    if (L.vec) { if (wq) SV_DRAFT(uint16_t, true, true); else SV_DRAFT(uint16_t, true, false); }
+    else { if (wq) SV_DRAFT(uint16_t, false, true); else SV_DRAFT(uint16_t, false, false); }
   } else {
-    if (L.vec) hipLaunchKernelGGL((draft_sample_kernel<float, true>), grid, block, 0, stream, A);
-    else hipLaunchKernelGGL((draft_sample_kernel<float, false>), grid, block, 0, stream, A);
+    if (L.vec) { if (wq) SV_DRAFT(float, true, true); else SV_DRAFT(float, true, false); }
+    else { if (wq) SV_DRAFT(float, false, true); else SV_DRAFT(float, false, false); }
   }
+#undef SV_DRAFT
   const hipError_t err = hipGetLastError();
   trace_after(stream, SV_KERNEL_DRAFT_SAMPLE);
   return err;
