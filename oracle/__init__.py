@@ -25,6 +25,11 @@ of Eagle / MTP / DFlash / DSPark):
   Pinned by scipy's softmax, numpy's searchsorted, cell-midpoint brute force,
   chi-square, and by the end-to-end law: drafting with it and verifying with
   ``verify_sample`` emits tokens distributed as the target.
+* ``mixed.verify_mixed``          a verify batch with a temperature per
+  sequence (0 = greedy).  Pinned by per-group chi-square against scipy's
+  softmax at each group's temperature, the exact greedy argmax chain inside a
+  mixed batch, the fp32 boundary of invalid temperatures, and reduction to
+  ``verify_sample`` / ``verify_greedy`` for uniform batches.
 * ``peagle.build_draft_batch``    the P-EAGLE drafter batch.  Pinned by the
   invariants the P-EAGLE summary fixes (K-1 MASK rows per sequence, slot -1
   exactly on rejected tokens, h_shared on the MASK rows, the new token paired
@@ -33,7 +38,8 @@ of Eagle / MTP / DFlash / DSPark):
   the rejected padding rows are readings the pages leave open: those two
   aspects are parity unpinned by the pages.
 """
-from . import draft, peagle, verify  # noqa: F401
+from . import draft, mixed, peagle, verify  # noqa: F401
+from .mixed import verify_mixed  # noqa: F401
 from .draft import draft_distribution, draft_outcomes, draft_sample  # noqa: F401
 from .peagle import PADDING_SLOT_ID, build_draft_batch  # noqa: F401
 from .verify import (  # noqa: F401

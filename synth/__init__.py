@@ -17,6 +17,8 @@ from .workloads import (  # noqa: F401
     DraftSpec,
     DRAFT_CONFIGS,
     make_draft_inputs,
+    make_temperatures,
+    MIXED_TEMPERATURES,
     verify_config,
     build_config,
     CONFIG_NAMES,

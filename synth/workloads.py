@@ -347,3 +347,18 @@ def make_draft_inputs(spec: DraftSpec) -> DraftInputs:
         if temps is not None:
             temps[b] = np.float32(rng.choice([0.0, 0.5, 0.7, 1.0, 1.3]))
     return DraftInputs(spec, logits, u, rows, temps)
+
+
+# ---------------------------------------------------------------- mixed batches
+MIXED_TEMPERATURES = (0.0, 0.5, 0.7, 1.0, 1.3)
+
+
+def make_temperatures(B: int, seed: int,
+                      choices: Sequence[float] = MIXED_TEMPERATURES) -> np.ndarray:
+    """Per-sequence temperatures [B] fp32 for a mixed serving batch: each
+    sequence draws one of ``choices`` (0 = a greedy request) from its own
+    stream, key (5, b)."""
+    out = np.empty(B, dtype=np.float32)
+    for b in range(B):
+        out[b] = np.float32(_seq_rng(seed, b, tag=5).choice(np.asarray(choices, np.float64)))
+    return out

@@ -151,3 +151,26 @@ def test_draft_mutant_fails_pins(label, funcs, old, new):
     except (AssertionError, IndexError, ValueError):
         fails = ["raised"]
     assert fails, f"mutant '{label}' passed the drafter pins"
+
+
+MIXED_MUTANTS = [
+    ("first sequence's temperature for all", ["verify_mixed"], "uniforms[b], temperatures[b])",
+     "uniforms[b], temperatures[0])"),
+    ("NaN temperature sampled", ["is_greedy"], "if not (T32 > 0.0 and np.isfinite(T32)):",
+     "if T32 < 0.0:"),
+    ("greedy p_draft always 1", ["verify_mixed_seq"],
+     "1.0 if int(d[k]) == first_argmax(z_rows[k]) else 0.0", "1.0"),
+    ("overflowing 1/T sampled", ["is_greedy"], "return not np.isfinite(c)", "return False"),
+]
+
+
+@pytest.mark.parametrize("label,funcs,old,new", MIXED_MUTANTS, ids=[m[0] for m in MIXED_MUTANTS])
+def test_mixed_mutant_fails_pins(label, funcs, old, new):
+    import oracle.mixed as omixed
+    from tests.test_oracle_mixed import check_module
+    m = _mutant_module(omixed, funcs, old, new)
+    try:
+        fails = check_module(m)
+    except (AssertionError, IndexError, ValueError, FloatingPointError):
+        fails = ["raised"]
+    assert fails, f"mutant '{label}' passed the mixed-batch pins"

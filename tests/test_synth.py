@@ -104,3 +104,11 @@ def test_draft_inputs_shapes_and_determinism():
     assert a.temperatures.dtype == np.float32
     t = make_draft_inputs(DRAFT_CONFIGS["draft-tiny"])
     assert t.row_index is None and t.temperatures is None and t.logits.dtype == np.float32
+
+
+def test_mixed_temperatures():
+    from synth import MIXED_TEMPERATURES, make_temperatures
+    t = make_temperatures(200, 9)
+    assert t.dtype == np.float32 and t.shape == (200,)
+    assert set(t.tolist()) == set(np.float32(MIXED_TEMPERATURES).tolist())
+    assert np.array_equal(t[:50], make_temperatures(50, 9))
