@@ -45,6 +45,8 @@ _SIGS = {
                                 ctypes.c_size_t, _p, _p]),
     "peagle_build_draft_batch": (_i, [_p, _p, _p, _p, _p, _i, _i, _p, _p, _i, ctypes.c_int32,
                                       _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
+    "spec_verify_mixed": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p,
+                               ctypes.c_size_t, _p, _p]),
     "spec_draft_sample": (_i, [_p, _i, ctypes.c_int64, _p, _p, ctypes.c_float, _p, _i, _i, _i,
                                _p, _p, _p, _p]),
     "sv_kernel_name": (ctypes.c_char_p, [_i]),
@@ -96,7 +98,8 @@ def _check(status: int, what: str):
 # ---------------------------------------------------------------- tracing
 KERNEL_IDS = {"verify_greedy_rows": 0, "verify_sample_rows": 1, "verify_sample_draw": 2,
               "peagle_build": 3, "verify_greedy_accept": 4, "verify_sample_accept": 5,
-              "verify_sample_locate": 6, "draft_sample": 7}
+              "verify_sample_locate": 6, "draft_sample": 7, "verify_mixed_rows": 8,
+              "verify_mixed_accept": 9}
 
 
 def trace_begin(capacity: int, kernels=None):
@@ -246,6 +249,56 @@ def spec_verify_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor,
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _ptr(device_error), _stream(dev))
     _check(st, "spec_verify_sample")
+    return out_tokens, out_num_accepted, out_draft_target_prob
+
+
+def spec_verify_mixed(target_logits: torch.Tensor, draft_probs: torch.Tensor,
+                      draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                      temperatures: torch.Tensor,
+                      out_tokens: Optional[torch.Tensor] = None,
+                      out_num_accepted: Optional[torch.Tensor] = None,
+                      out_draft_target_prob: Optional[torch.Tensor] = None,
+                      want_draft_target_prob: bool = False,
+                      workspace: Optional[torch.Tensor] = None,
+                      device_error: Optional[torch.Tensor] = None):
+    """Verify with a temperature per sequence (0 = greedy); see
+    spec_verify_mixed in include/spec_verify.h.
+
+    Returns (out_tokens, num_accepted, draft_target_prob or None).
+    """
+    lib = require_library()
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    _dev(target_logits, "target_logits")
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("target_logits must be float32 or bfloat16")
+    _dev(draft_probs, "draft_probs", torch.float32, (B, K, V), dev)
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _dev(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    _dev(temperatures, "temperatures", torch.float32, (B,), dev)
+    out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if out_tokens is None \
+        else _dev(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+    out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev) if out_num_accepted is None \
+        else _dev(out_num_accepted, "out_num_accepted", torch.int32, (B,), dev)
+    if out_draft_target_prob is None and want_draft_target_prob:
+        out_draft_target_prob = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if out_draft_target_prob is not None:
+        _dev(out_draft_target_prob, "out_draft_target_prob", torch.float32, (B, K), dev)
+    need = spec_verify_workspace_bytes(B, K, V)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    _dev(workspace, "workspace", device=dev)
+    if device_error is not None:
+        _dev(device_error, "device_error", torch.int32, (1,), dev)
+    st = lib.spec_verify_mixed(_ptr(target_logits), _DTYPES[target_logits.dtype], _ptr(draft_probs),
+                               _ptr(draft_tokens), _ptr(uniforms), _ptr(temperatures), B, K, V,
+                               _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_draft_target_prob),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _ptr(device_error), _stream(dev))
+    _check(st, "spec_verify_mixed")
     return out_tokens, out_num_accepted, out_draft_target_prob
 
 

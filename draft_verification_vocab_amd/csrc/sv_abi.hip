@@ -86,6 +86,8 @@ SV_API const char* sv_kernel_name(int kernel_id) {
     case SV_KERNEL_VERIFY_SAMPLE_ACCEPT: return "verify_sample_accept";
     case SV_KERNEL_VERIFY_SAMPLE_LOCATE: return "verify_sample_locate";
     case SV_KERNEL_DRAFT_SAMPLE: return "draft_sample";
+    case SV_KERNEL_VERIFY_MIXED_ROWS: return "verify_mixed_rows";
+    case SV_KERNEL_VERIFY_MIXED_ACCEPT: return "verify_mixed_accept";
     default: return "unknown";
   }
 }
@@ -129,17 +131,22 @@ SV_API size_t spec_verify_workspace_bytes(int B, int K, int V) {
   return sv::verify_workspace_bytes(B, K, V);
 }
 
+// sample: 0 greedy, 1 one temperature, 2 per-sequence temperatures (mixed)
 static sv_status verify_common(const void* logits, int dtype, const float* draft_probs,
                                const int32_t* draft_tokens, const float* uniforms,
-                               float temperature, int sample, int B, int K, int V,
-                               int32_t* out_tokens, int32_t* out_num_accepted, float* out_p_draft,
-                               void* workspace, size_t workspace_bytes, int32_t* device_error,
-                               void* stream) {
+                               float temperature, const float* temperatures, int sample, int B,
+                               int K, int V, int32_t* out_tokens, int32_t* out_num_accepted,
+                               float* out_p_draft, void* workspace, size_t workspace_bytes,
+                               int32_t* device_error, void* stream) {
   sv_status st = check_verify_shape(B, K, V);
   if (st != SV_OK) return st;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
-  if (sample && !(temperature > 0.0f && isfinite(temperature))) return SV_ERR_VALUE;
+  if (sample == 1 && !(temperature > 0.0f && isfinite(temperature) &&
+                       isfinite((float)(1.4426950408889634 / (double)temperature))))
+    return SV_ERR_VALUE;
   if (B == 0) return SV_OK;
+  if (sample == 2 && !temperatures) return SV_ERR_NULL;
+  if (temperatures && !aligned(temperatures, 4)) return SV_ERR_ALIGN;
   if (!logits || !out_tokens || !out_num_accepted || (K > 0 && !draft_tokens)) return SV_ERR_NULL;
   if (sample && (!uniforms || (K > 0 && !draft_probs))) return SV_ERR_NULL;
   if (!workspace) return SV_ERR_WORKSPACE;
@@ -162,7 +169,9 @@ static sv_status verify_common(const void* logits, int dtype, const float* draft
   L.temperature = temperature;
   L.B = B; L.K = K; L.V = V;
   L.bf16 = dtype == SV_BF16;
-  L.sample = sample;
+  L.sample = sample != 0;
+  L.mixed = sample == 2;
+  L.temperatures = sample == 2 ? temperatures : nullptr;
   L.vec = (V % 8 == 0) && aligned(logits, 16) && (!sample || !draft_probs || aligned(draft_probs, 16));
   L.out_tokens = out_tokens;
   L.out_num_accepted = out_num_accepted;
@@ -177,9 +186,9 @@ SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
                                     int32_t* out_tokens, int32_t* out_num_accepted,
                                     void* workspace, size_t workspace_bytes,
                                     int32_t* device_error, void* stream) {
-  return verify_common(target_logits, logits_dtype, nullptr, draft_tokens, nullptr, 1.0f, 0, B, K,
-                       V, out_tokens, out_num_accepted, nullptr, workspace, workspace_bytes,
-                       device_error, stream);
+  return verify_common(target_logits, logits_dtype, nullptr, draft_tokens, nullptr, 1.0f, nullptr,
+                       0, B, K, V, out_tokens, out_num_accepted, nullptr, workspace,
+                       workspace_bytes, device_error, stream);
 }
 
 SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
@@ -189,7 +198,18 @@ SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
                                     float* out_draft_target_prob, void* workspace,
                                     size_t workspace_bytes, int32_t* device_error, void* stream) {
   return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, uniforms,
-                       temperature, 1, B, K, V, out_tokens, out_num_accepted,
+                       temperature, nullptr, 1, B, K, V, out_tokens, out_num_accepted,
+                       out_draft_target_prob, workspace, workspace_bytes, device_error, stream);
+}
+
+SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
+                                   const float* draft_probs, const int32_t* draft_tokens,
+                                   const float* uniforms, const float* temperatures, int B, int K,
+                                   int V, int32_t* out_tokens, int32_t* out_num_accepted,
+                                   float* out_draft_target_prob, void* workspace,
+                                   size_t workspace_bytes, int32_t* device_error, void* stream) {
+  return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, uniforms, 1.0f,
+                       temperatures, 2, B, K, V, out_tokens, out_num_accepted,
                        out_draft_target_prob, workspace, workspace_bytes, device_error, stream);
 }
 

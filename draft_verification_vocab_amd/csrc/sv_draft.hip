@@ -205,17 +205,11 @@ __global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(Draft
   }
   const LT* zrow = static_cast<const LT*>(A.logits) + ri * V;
 
-  float T = A.temperatures ? A.temperatures[b] : A.temperature;
-  float c = 1.f;
-  bool greedy = T == 0.f;
-  if (!greedy) {
-    c = (float)(1.4426950408889634 / (double)T);
-    if (!(T > 0.f) || !isfinite(T) || !isfinite(c)) {
-      if (t == 0) flag_error(A.device_error, SV_DEVERR_TEMPERATURE);
-      greedy = true;
-      c = 1.f;
-    }
-  }
+  bool bad;
+  float c = seq_scale(A.temperatures ? A.temperatures[b] : A.temperature, bad);
+  if (bad && t == 0) flag_error(A.device_error, SV_DEVERR_TEMPERATURE);
+  const bool greedy = c == 0.f;
+  if (greedy) c = 1.f;
 
   if (greedy) {
     // lowest-index argmax; q is its one-hot

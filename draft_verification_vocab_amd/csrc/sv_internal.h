@@ -18,6 +18,8 @@ struct VerifyLaunch {
   int B, K, V;
   int bf16;                      // logits are bf16 (else fp32)
   int sample;                    // rejection sampling (else greedy)
+  int mixed;                     // per-sequence temperatures (overrides sample)
+  const float* temperatures;     // mixed: [B]
   int vec;                       // 16-byte vector loads are legal for every row
   int32_t* out_tokens;
   int32_t* out_num_accepted;

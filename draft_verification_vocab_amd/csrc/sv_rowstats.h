@@ -16,7 +16,21 @@ struct Partial {
   double acc;    // sampling: sum over the slice of 2^((z - m) * c)
 };
 
-enum Mode { GREEDY = 0, SAMPLE = 1 };
+enum Mode { GREEDY = 0, SAMPLE = 1, MIXED = 2 };   // MIXED: per-sequence temperature
+
+// Exponent scale c = log2(e) / T of a sequence's temperature T, or 0 for a
+// greedy sequence: T = 0, or a temperature that is negative, NaN, infinite or
+// so small that 1/T overflows fp32 (`bad` is then set).
+__device__ __forceinline__ float seq_scale(float T, bool& bad) {
+  bad = false;
+  if (T == 0.f) return 0.f;
+  const float c = (float)(1.4426950408889634 / (double)T);
+  if (!(T > 0.f) || !isfinite(T) || !isfinite(c)) {
+    bad = true;
+    return 0.f;
+  }
+  return c;
+}
 
 constexpr int kTileLoads = 4;           // wave-wide 512-element loads per CDF tile
 constexpr int kTileElems = kTile * kTileLoads;

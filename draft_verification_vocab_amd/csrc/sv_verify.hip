@@ -35,6 +35,7 @@ struct ScanResult {  // outcome of a sequence's accept scan
   int a;             // accepted drafts
   int g_a;           // greedy: argmax of row a
   float M_a;         // max of row a
+  float c;           // the sequence's exponent scale; 0 = greedy (nothing to draw)
   double s_a;        // sampling: sum over row a of 2^((z - M_a) * c)
 };
 
@@ -86,6 +87,7 @@ size_t verify_workspace_bytes(int B, int K, int V) { return layout(B, K, V).tota
 
 struct RowsArgs {
   const void* logits;
+  const float* temperatures;  // mixed: [B] per-sequence temperatures
   float c;                 // log2(e) / T   (sampling)
   int K, V, S;
   long octets;             // ceil(V / 8)
@@ -94,6 +96,7 @@ struct RowsArgs {
 
 struct ScanArgs {          // what an accept scan reads and writes
   const void* logits;
+  const float* temperatures;  // mixed: [B]
   const float* draft_probs;
   const int32_t* draft_tokens;
   const float* uniforms;
@@ -129,7 +132,16 @@ __global__ __launch_bounds__(kThreads) void verify_rows(RowsArgs A) {
   const LT* row = static_cast<const LT*>(A.logits) + rowi * V;
   const long o_lo = (long)s * A.octets / S, o_hi = (long)(s + 1) * A.octets / S;
 
-  const Partial P = slice_stats<LT, MODE, VEC, kThreads>(row, o_lo, o_hi, V, A.c, sm_f, sm_i, sm_d);
+  Partial P;
+  if constexpr (MODE == MIXED) {
+    // the sequence's own rule; uniform across the workgroup
+    bool bad;
+    const float c = seq_scale(A.temperatures[rowi / (A.K + 1)], bad);
+    if (c == 0.f) P = slice_stats<LT, GREEDY, VEC, kThreads>(row, o_lo, o_hi, V, 1.f, sm_f, sm_i, sm_d);
+    else P = slice_stats<LT, SAMPLE, VEC, kThreads>(row, o_lo, o_hi, V, c, sm_f, sm_i, sm_d);
+  } else {
+    P = slice_stats<LT, MODE, VEC, kThreads>(row, o_lo, o_hi, V, A.c, sm_f, sm_i, sm_d);
+  }
   if (threadIdx.x == 0) A.partials[unit] = P;   // read by the next kernel
 }
 
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void verify_rows(RowsArgs A) {
 // -1 padding, num_accepted and p_k(d_k); the new token is written by the
 // caller (greedy: g_a; sampling: the draw).
 template <typename LT, int MODE>
-__device__ ScanResult accept_scan(const ScanArgs& A, int b, bool write) {
+__device__ ScanResult accept_scan(const ScanArgs& A, int b, bool write, float c) {
   const int K = A.K, S = A.S;
   const long V = A.V;
   const int k = lane_id();
@@ -158,7 +170,7 @@ __device__ ScanResult accept_scan(const ScanArgs& A, int b, bool write) {
       for (int j = 0; j < S; ++j) M = fmaxf(M, Pb[k * S + j].m);
       for (int j = 0; j < S; ++j) {
         const Partial p = Pb[k * S + j];
-        if (p.acc != 0.0) s_k += p.acc * exp2(((double)p.m - (double)M) * (double)A.c);
+        if (p.acc != 0.0) s_k += p.acc * exp2(((double)p.m - (double)M) * (double)c);
       }
     }
   }
@@ -170,12 +182,13 @@ __device__ ScanResult accept_scan(const ScanArgs& A, int b, bool write) {
     const bool valid = d >= 0 && d < V;
     if constexpr (MODE == GREEDY) {
       rej = !(valid && d == g);
+      pdraft = rej ? 0.f : 1.f;           // the T -> 0 limit of p_k(d_k)
     } else {
       double px = 0.0;
       if (valid) {
         const LT* zr = static_cast<const LT*>(A.logits) + ((long)b * (K + 1) + k) * V;
         const float zx = logit_at(zr, d);
-        px = exp2(((double)zx - (double)M) * (double)A.c) / s_k;
+        px = exp2(((double)zx - (double)M) * (double)c) / s_k;
         const double qx = (double)A.draft_probs[((long)b * K + k) * V + d];
         const double ratio = qx > 0.0 ? px / qx : (px > 0.0 ? INFINITY : 0.0);
         rej = !((double)A.uniforms[(long)b * (K + 1) + k] < ratio);
@@ -192,10 +205,11 @@ __device__ ScanResult accept_scan(const ScanArgs& A, int b, bool write) {
   r.g_a = __shfl(g, r.a);
   r.M_a = __shfl(M, r.a);
   r.s_a = __shfl(s_k, r.a);
+  r.c = MODE == SAMPLE ? c : 0.f;
   if (write) {
     if (k <= K && k != r.a) A.out_tokens[(long)b * (K + 1) + k] = k < r.a ? d : -1;
     if (k == 0) A.out_num_accepted[b] = r.a;
-    if (MODE == SAMPLE && k < K && A.out_p_draft) A.out_p_draft[(long)b * K + k] = pdraft;
+    if (k < K && A.out_p_draft) A.out_p_draft[(long)b * K + k] = pdraft;
   }
   return r;
 }
@@ -206,11 +220,23 @@ template <typename LT, int MODE>
 __global__ __launch_bounds__(kThreads) void verify_accept(ScanArgs A) {
   const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
   if (b >= A.B) return;
-  const ScanResult r = accept_scan<LT, MODE>(A, b, true);
   const int l = lane_id();
-  if (l == 0) {
-    if constexpr (MODE == GREEDY) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
-    else A.info[b] = r;
+  if constexpr (MODE == MIXED) {
+    bool bad;
+    const float c = seq_scale(A.temperatures[b], bad);
+    if (bad && l == 0) flag_error(A.device_error, SV_DEVERR_TEMPERATURE);
+    const ScanResult r = c == 0.f ? accept_scan<LT, GREEDY>(A, b, true, 1.f)
+                                  : accept_scan<LT, SAMPLE>(A, b, true, c);
+    if (l == 0) {
+      if (c == 0.f) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
+      A.info[b] = r;                      // c = 0 tells the draw to skip it
+    }
+  } else {
+    const ScanResult r = accept_scan<LT, MODE>(A, b, true, A.c);
+    if (l == 0) {
+      if constexpr (MODE == GREEDY) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
+      else A.info[b] = r;
+    }
   }
   // the partials are consumed: clear them so the workspace ends all zero
   Partial* Pb = A.partials + (long)b * (A.K + 1) * A.S;
@@ -271,11 +297,12 @@ __device__ __forceinline__ DrawRow<LT> draw_row(const DrawArgs& A, int b) {
   r.a = scan.a;
   r.zrow = static_cast<const LT*>(A.sc.logits) + ((long)b * (A.sc.K + 1) + scan.a) * A.sc.V;
   r.qrow = scan.a < A.sc.K ? A.sc.draft_probs + ((long)b * A.sc.K + scan.a) * A.sc.V : nullptr;
-  r.c = A.sc.c;
+  r.c = scan.c;                               // 0: a greedy sequence of a mixed batch
   // p = 2^(z*c - M*c) / s.  Mc32 is M*c rounded to fp32; the rounding is
   // folded into the scale so that p keeps the fp64 reference exactly.
   r.Mc32 = scan.M_a * r.c;
-  r.inv_s = (float)(exp2((double)r.Mc32 - (double)scan.M_a * (double)r.c) / scan.s_a);
+  r.inv_s = r.c == 0.f ? 0.f
+      : (float)(exp2((double)r.Mc32 - (double)scan.M_a * (double)r.c) / scan.s_a);
   return r;
 }
 
@@ -306,6 +333,7 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
   const long V = A.sc.V;
   const long nocts = (V + 7) / 8;
   const DrawRow<LT> R = draw_row<LT>(A, b);
+  if (R.c == 0.f) return;                     // greedy: its token is already written
   const bool residual = R.qrow != nullptr;
   float* tsum_g = A.tile_sums + (long)b * T;
   const int t_lo = (int)((long)cidx * T / C), t_hi = (int)((long)(cidx + 1) * T / C);
@@ -341,6 +369,10 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
   const long nocts = (V + 7) / 8;
   const int l = lane_id();
   const DrawRow<LT> R = draw_row<LT>(A, b);
+  if (R.c == 0.f) {                           // greedy: nothing to draw
+    if (l == 0) A.sc.info[b] = ScanResult{0, 0, 0.f, 0.f, 0.0};
+    return;
+  }
   bool residual = R.qrow != nullptr;
   float* tsum_g = A.tile_sums + (long)b * T;
   double* csum_g = A.chunk_sums + (long)b * C;
@@ -443,40 +475,52 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
   // leave this sequence's part of the workspace cleared
   for (int i = l; i < T; i += kWave) st_coherent(&tsum_g[i], 0.f);
   for (int i = l; i < C; i += kWave) st_coherent(&csum_g[i], 0.0);
-  if (l == 0) A.sc.info[b] = ScanResult{0, 0, 0.f, 0.0};
+  if (l == 0) A.sc.info[b] = ScanResult{0, 0, 0.f, 0.f, 0.0};
 }
 
 // ----------------------------------------------------------------------------
 hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   const Layout lay = layout(L.B, L.K, L.V);
   char* ws = static_cast<char*>(L.workspace);
-  const float c = L.sample ? (float)(1.4426950408889634 / (double)L.temperature) : 1.0f;
+  const int mode = L.mixed ? MIXED : (L.sample ? SAMPLE : GREEDY);
+  const float c = mode == SAMPLE ? (float)(1.4426950408889634 / (double)L.temperature) : 1.0f;
   Partial* partials = reinterpret_cast<Partial*>(ws + lay.partials);
   const dim3 block(kThreads);
+  const int rows_id = mode == MIXED ? SV_KERNEL_VERIFY_MIXED_ROWS
+                    : mode == SAMPLE ? SV_KERNEL_VERIFY_SAMPLE_ROWS : SV_KERNEL_VERIFY_GREEDY_ROWS;
+  const int accept_id = mode == MIXED ? SV_KERNEL_VERIFY_MIXED_ACCEPT
+                      : mode == SAMPLE ? SV_KERNEL_VERIFY_SAMPLE_ACCEPT
+                                       : SV_KERNEL_VERIFY_GREEDY_ACCEPT;
 
   RowsArgs R;
   R.logits = L.logits;
+  R.temperatures = L.temperatures;
   R.c = c;
   R.K = L.K; R.V = L.V; R.S = lay.S;
   R.octets = (L.V + 7) / 8;
   R.partials = partials;
   const dim3 grid1((unsigned)((long)L.B * (L.K + 1) * lay.S));
-  trace_before(stream, L.sample ? SV_KERNEL_VERIFY_SAMPLE_ROWS : SV_KERNEL_VERIFY_GREEDY_ROWS);
-#define SV_ROWS(LT, MODE, VEC) hipLaunchKernelGGL((verify_rows<LT, MODE, VEC>), grid1, block, 0, stream, R)
-  if (L.bf16) {
-    if (L.sample) { if (L.vec) SV_ROWS(uint16_t, SAMPLE, true); else SV_ROWS(uint16_t, SAMPLE, false); }
-    else { if (L.vec) SV_ROWS(uint16_t, GREEDY, true); else SV_ROWS(uint16_t, GREEDY, false); }
-  } else {
-    if (L.sample) { if (L.vec) SV_ROWS(float, SAMPLE, true); else SV_ROWS(float, SAMPLE, false); }
-    else { if (L.vec) SV_ROWS(float, GREEDY, true); else SV_ROWS(float, GREEDY, false); }
-  }
-#undef SV_ROWS
+  trace_before(stream, rows_id);
+#define SV_ROWS(LT, MODE) \
+  do { \
+    if (L.vec) hipLaunchKernelGGL((verify_rows<LT, MODE, true>), grid1, block, 0, stream, R); \
+    else hipLaunchKernelGGL((verify_rows<LT, MODE, false>), grid1, block, 0, stream, R); \
+  } while (0)
+#define SV_BY_MODE(M, LT) \
+  do { \
+    if (mode == MIXED) M(LT, MIXED); \
+    else if (mode == SAMPLE) M(LT, SAMPLE); \
+    else M(LT, GREEDY); \
+  } while (0)
+  if (L.bf16) SV_BY_MODE(SV_ROWS, uint16_t);
+  else SV_BY_MODE(SV_ROWS, float);
   hipError_t err = hipGetLastError();
-  trace_after(stream, L.sample ? SV_KERNEL_VERIFY_SAMPLE_ROWS : SV_KERNEL_VERIFY_GREEDY_ROWS);
+  trace_after(stream, rows_id);
   if (err != hipSuccess) return err;
 
   ScanArgs sc;
   sc.logits = L.logits;
+  sc.temperatures = L.temperatures;
   sc.draft_probs = L.draft_probs;
   sc.draft_tokens = L.draft_tokens;
   sc.uniforms = L.uniforms;
@@ -490,17 +534,16 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
 
   sc.info = reinterpret_cast<ScanResult*>(ws + lay.info);
   const dim3 grid_acc((unsigned)((L.B + kWaves - 1) / kWaves));
-  trace_before(stream, L.sample ? SV_KERNEL_VERIFY_SAMPLE_ACCEPT : SV_KERNEL_VERIFY_GREEDY_ACCEPT);
-  if (L.bf16) {
-    if (L.sample) hipLaunchKernelGGL((verify_accept<uint16_t, SAMPLE>), grid_acc, block, 0, stream, sc);
-    else hipLaunchKernelGGL((verify_accept<uint16_t, GREEDY>), grid_acc, block, 0, stream, sc);
-  } else {
-    if (L.sample) hipLaunchKernelGGL((verify_accept<float, SAMPLE>), grid_acc, block, 0, stream, sc);
-    else hipLaunchKernelGGL((verify_accept<float, GREEDY>), grid_acc, block, 0, stream, sc);
-  }
+  trace_before(stream, accept_id);
+#define SV_ACCEPT(LT, MODE) hipLaunchKernelGGL((verify_accept<LT, MODE>), grid_acc, block, 0, stream, sc)
+  if (L.bf16) SV_BY_MODE(SV_ACCEPT, uint16_t);
+  else SV_BY_MODE(SV_ACCEPT, float);
+#undef SV_ACCEPT
+#undef SV_BY_MODE
+#undef SV_ROWS
   err = hipGetLastError();
-  trace_after(stream, L.sample ? SV_KERNEL_VERIFY_SAMPLE_ACCEPT : SV_KERNEL_VERIFY_GREEDY_ACCEPT);
-  if (err != hipSuccess || !L.sample) return err;
+  trace_after(stream, accept_id);
+  if (err != hipSuccess || mode == GREEDY) return err;
 
   DrawArgs D;
   D.sc = sc;

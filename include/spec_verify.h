@@ -131,7 +131,8 @@ SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
  *   draft_probs      [B][K][V] fp32, the drafter's probabilities of each draft.
  *   draft_tokens     [B][K] int32, d[b][k] drawn from draft_probs[b][k].
  *   uniforms         [B][K+1] fp32 in [0, 1): [:, k<K] tests, [:, K] the draw.
- *   temperature      > 0 and finite; applies to the target logits only.
+ *   temperature      > 0 and finite, with 1/T finite in fp32; applies to the
+ *                    target logits only.
  *   out_tokens, out_num_accepted: as for spec_verify_greedy.
  *   out_draft_target_prob  optional [B][K] fp32: p_k(d[b][k]) for every k
  *                    (NULL = not written).
@@ -150,6 +151,35 @@ SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
                                     float* out_draft_target_prob,
                                     void* workspace, size_t workspace_bytes,
                                     int32_t* device_error, void* stream);
+
+/*
+ * Verify of a mixed serving batch: sequence b follows the greedy rule of
+ * spec_verify_greedy when temperatures[b] = 0, and the rejection sampling of
+ * spec_verify_sample at temperature temperatures[b] when it is > 0, all in
+ * one launch sequence.  Source: "Project 14", section 架构 (one server
+ * verifies every running request's drafts in a single target pass, each
+ * request with its own sampling settings) and section 概念 (the greedy path).
+ *   target_logits, draft_probs, draft_tokens, uniforms, out_tokens,
+ *   out_num_accepted, workspace: as for spec_verify_sample; the draft_probs
+ *                    rows and uniforms of greedy sequences are not read.
+ *   temperatures     [B] fp32 device array.  A value that is negative, NaN,
+ *                    infinite or too small for 1/T to be finite sets
+ *                    SV_DEVERR_TEMPERATURE and verifies that sequence greedily.
+ *   out_draft_target_prob  optional [B][K]: p_k(d[b][k]) for sampled
+ *                    sequences; for greedy ones 1 where d[b][k] is row k's
+ *                    lowest-index argmax and 0 elsewhere (the T -> 0 limit).
+ * Results equal those of spec_verify_greedy / spec_verify_sample on each
+ * sequence alone.  The same four kernels as spec_verify_sample are enqueued;
+ * the draw skips greedy sequences.
+ */
+SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
+                                   const float* draft_probs, const int32_t* draft_tokens,
+                                   const float* uniforms, const float* temperatures,
+                                   int B, int K, int V,
+                                   int32_t* out_tokens, int32_t* out_num_accepted,
+                                   float* out_draft_target_prob,
+                                   void* workspace, size_t workspace_bytes,
+                                   int32_t* device_error, void* stream);
 
 /*
  * P-EAGLE drafter batch.  Each sequence b owns the 2K rows [2Kb, 2Kb+2K).
@@ -247,6 +277,9 @@ SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype,
 #define SV_KERNEL_VERIFY_SAMPLE_ACCEPT 5 /* spec_verify_sample: accept scan              */
 #define SV_KERNEL_VERIFY_SAMPLE_LOCATE 6 /* spec_verify_sample: locate the drawn token   */
 #define SV_KERNEL_DRAFT_SAMPLE 7         /* spec_draft_sample                            */
+#define SV_KERNEL_VERIFY_MIXED_ROWS 8    /* spec_verify_mixed: row statistics            */
+#define SV_KERNEL_VERIFY_MIXED_ACCEPT 9  /* spec_verify_mixed: accept scan (its draw and
+                                            locate kernels carry ids 2 and 6)            */
 
 SV_API const char* sv_kernel_name(int kernel_id);
 SV_API sv_status sv_trace_begin(int capacity, unsigned kernel_mask); /* SV_ERR_VALUE if capacity < 1 */

@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
-              "spec_draft_sample", "spec_verify_workspace_bytes", "sv_status_string"):
+              "spec_draft_sample", "spec_verify_mixed", "spec_verify_workspace_bytes",
+              "sv_status_string"):
         assert n in names
 
 
@@ -118,6 +119,7 @@ def test_verify_validation(lib):
     assert sample(lib, T=-1.0) == EVALUE
     assert sample(lib, T=float("inf")) == EVALUE
     assert sample(lib, T=float("nan")) == EVALUE
+    assert sample(lib, T=1e-45) == EVALUE           # 1/T overflows fp32
     assert sample(lib, q=None) == ENULL
     assert sample(lib, u=None) == ENULL
     assert sample(lib, u=FAKE + 2) == EALIGN
@@ -176,10 +178,11 @@ def test_tracer_host_paths(lib):
     assert lib.sv_trace_read(0, None, None) == ENULL
     import draft_verification_vocab_amd as sv
     assert all(lib.sv_kernel_name(i).decode() == n for n, i in sv.KERNEL_IDS.items())
-    names = [lib.sv_kernel_name(i) for i in range(8)]
+    names = [lib.sv_kernel_name(i) for i in range(10)]
     assert names == [b"verify_greedy_rows", b"verify_sample_rows", b"verify_sample_draw",
                      b"peagle_build", b"verify_greedy_accept", b"verify_sample_accept",
-                     b"verify_sample_locate", b"draft_sample"]
+                     b"verify_sample_locate", b"draft_sample", b"verify_mixed_rows",
+                     b"verify_mixed_accept"]
     assert lib.sv_kernel_name(17) == b"unknown"
     lib.sv_trace_end()                              # harmless when tracing is off
 
@@ -214,3 +217,25 @@ def test_draft_validation(lib):
     assert draft(lib, probs=FAKE + 2) == EALIGN
     assert draft(lib, tok=FAKE + 1) == EALIGN
     assert draft(lib, err=FAKE + 1) == EALIGN
+
+
+def mixed(lib, logits=FAKE, dtype=1, q=FAKE, d=FAKE, u=FAKE, temps=FAKE, B=2, K=3, V=64,
+          out=FAKE, acc=FAKE, pd=None, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(K, 0), max(V, 1))
+    return lib.spec_verify_mixed(logits, dtype, q, d, u, temps, B, K, V, out, acc, pd, ws, wsb,
+                                 None, None)
+
+
+def test_mixed_validation(lib):
+    assert mixed(lib, K=64) == ESHAPE
+    assert mixed(lib, V=0) == ESHAPE
+    assert mixed(lib, dtype=2) == EDTYPE
+    assert mixed(lib, B=0, logits=None, q=None, d=None, u=None, temps=None, out=None, acc=None,
+                 ws=None, wsb=0) == OK
+    assert mixed(lib, temps=None) == ENULL
+    assert mixed(lib, q=None) == ENULL
+    assert mixed(lib, u=None) == ENULL
+    assert mixed(lib, temps=FAKE + 2) == EALIGN
+    assert mixed(lib, ws=None) == EWS
+    assert mixed(lib, wsb=8) == EWS

@@ -104,3 +104,56 @@ def test_fused_sample_then_build(gpu, fused):
     rate = (acc.sum() / np.minimum(acc + 1, vi.spec.K).sum())
     print(f"[fused] acceptance rate {rate:.3f}, mean accepted {acc.mean():.3f}", flush=True)
     assert 0.3 < rate < 0.8
+
+
+def test_fused_mixed_then_build(gpu, fused):
+    """The same batch as a mixed serving batch: per-sequence temperatures from
+    {0, 0.5, 0.7, 1.0, 1.3}, one verify launch sequence, then the build."""
+    vi, bi, t, picks = fused
+    temps = synth.make_temperatures(vi.spec.B, 15)
+    out_t, acc_t, pd_t = gpu.spec_verify_mixed(t["z"], t["q"], t["d"], t["u"], dev(temps),
+                                               want_draft_target_prob=True)
+    res = _build(gpu, bi, t, out_t, acc_t)
+    torch.cuda.synchronize()
+    out, acc, pd = out_t.cpu().numpy(), acc_t.cpu().numpy(), pd_t.cpu().numpy()
+    _well_formed(vi, out, acc)
+    for b in picks:
+        z64 = oracle.decode_logits(vi.logits[b], "bf16")
+        if temps[b] == 0:
+            w_out, w_acc, w_pd = oracle.verify_mixed(vi.logits[b:b + 1], "bf16",
+                                                     vi.draft_probs[b:b + 1],
+                                                     vi.draft_tokens[b:b + 1],
+                                                     vi.uniforms[b:b + 1], temps[b:b + 1])
+            assert acc[b] == w_acc[0] and np.array_equal(out[b], w_out[0]), b
+            assert np.array_equal(pd[b], w_pd[0].astype(np.float32)), b
+        else:
+            check_sample_sequence(z64, vi.draft_probs[b], vi.draft_tokens[b], vi.uniforms[b],
+                                  float(temps[b]), out[b], acc[b], pd[b])
+    _check_build_rows(vi, bi, res, out, acc, picks)
+
+
+def test_fused_draft_sample(gpu, fused):
+    """Drafter-output sampling at the bench shape: the first K logit rows of
+    each sequence stand in for the drafter rows, gathered through a row index;
+    sampled drafts checked against the oracle."""
+    vi, bi, t, picks = fused
+    B, K, V = vi.spec.B, vi.spec.K, vi.spec.V
+    rows = (np.arange(B, dtype=np.int32)[:, None] * (K + 1) + np.arange(K, dtype=np.int32)).copy()
+    u = np.random.default_rng(7).random((B, K), dtype=np.float32)
+    tok_t, q_t = gpu.spec_draft_sample(t["z"].view(B * (K + 1), V), K, vi.temperature,
+                                       uniforms=dev(u), row_index=dev(rows))
+    tok2_t, _ = gpu.spec_draft_sample(t["z"].view(B * (K + 1), V), K, vi.temperature,
+                                      uniforms=dev(u), row_index=dev(rows),
+                                      want_draft_probs=False)
+    torch.cuda.synchronize()
+    tok = tok_t.cpu().numpy()
+    assert np.array_equal(tok, tok2_t.cpu().numpy())
+    assert np.all((tok >= 0) & (tok < V))
+    for b in picks:
+        qb = q_t[b].cpu().numpy()
+        for k in range(K):
+            z64 = oracle.decode_logits(vi.logits[b, k], "bf16")
+            d, q = oracle.draft.draft_sample_row(z64, float(np.float32(vi.temperature)), u[b, k])
+            assert np.allclose(qb[k], q, rtol=1e-5, atol=1e-30), (b, k)
+            if tok[b, k] != d:
+                assert int(tok[b, k]) in oracle.draft_outcomes(z64, vi.temperature, u[b, k]), (b, k)

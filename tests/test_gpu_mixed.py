@@ -1,0 +1,90 @@
+"""GPU parity: spec_verify_mixed (a temperature per sequence, 0 = greedy).
+
+Greedy sequences are compared exactly (tokens, accept count, and the 0/1
+p_draft of the T -> 0 limit); sampled sequences as in the sampled-verify
+tests (decisions within 1e-6 of their threshold may go either way, p_k(d_k)
+within 1e-5).  A uniform batch must reproduce spec_verify_greedy or
+spec_verify_sample bit for bit; invalid temperatures are flagged and verified
+greedily.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import DEV, check_sample_sequence, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _mixed_parity(sv, vi, temps):
+    out, acc, pd = sv.spec_verify_mixed(dev(vi.logits), dev(vi.draft_probs), dev(vi.draft_tokens),
+                                        dev(vi.uniforms), dev(temps), want_draft_target_prob=True)
+    torch.cuda.synchronize()
+    out, acc, pd = out.cpu().numpy(), acc.cpu().numpy(), pd.cpu().numpy()
+    mism = flags = 0
+    for b in range(vi.spec.B):
+        z64 = oracle.decode_logits(vi.logits[b], vi.spec.dtype)
+        if oracle.mixed.is_greedy(temps[b]):
+            w_out, w_acc, w_pd = oracle.verify_mixed(vi.logits[b:b + 1], vi.spec.dtype,
+                                                     vi.draft_probs[b:b + 1],
+                                                     vi.draft_tokens[b:b + 1],
+                                                     vi.uniforms[b:b + 1], temps[b:b + 1])
+            assert acc[b] == w_acc[0] and np.array_equal(out[b], w_out[0]), b
+            assert np.array_equal(pd[b], w_pd[0].astype(np.float32)), b
+        else:
+            same, f = check_sample_sequence(z64, vi.draft_probs[b], vi.draft_tokens[b],
+                                            vi.uniforms[b], float(temps[b]), out[b], acc[b], pd[b])
+            mism += not same
+            flags += f
+    assert mism <= flags
+    return out, acc, pd
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_mixed_workloads(gpu, cfg):
+    vi = synth.make_verify_inputs(synth.verify_config(cfg))
+    temps = synth.make_temperatures(vi.spec.B, 100 + cfg)
+    if cfg == 1:
+        temps[:] = 0.7
+    _mixed_parity(gpu, vi, temps)
+
+
+def test_every_sequence_mode_in_one_batch(gpu):
+    # workload 2 has 8 sequences: give them every kind of temperature
+    vi = synth.make_verify_inputs(synth.verify_config(2))
+    temps = np.array([0.0, 0.5, 1.0, 0.0, 1.3, 0.7, 0.0, 2.0], dtype=np.float32)
+    _mixed_parity(gpu, vi, temps)
+
+
+def test_uniform_batches_match_single_mode_calls(gpu):
+    vi = synth.make_verify_inputs(synth.verify_config(4))
+    B = vi.spec.B
+    z, q, d, u = dev(vi.logits), dev(vi.draft_probs), dev(vi.draft_tokens), dev(vi.uniforms)
+    o1, a1, p1 = gpu.spec_verify_mixed(z, q, d, u, torch.full((B,), vi.temperature, device=DEV),
+                                       want_draft_target_prob=True)
+    o2, a2, p2 = gpu.spec_verify_sample(z, q, d, u, vi.temperature, want_draft_target_prob=True)
+    o3, a3, p3 = gpu.spec_verify_mixed(z, q, d, u, torch.zeros(B, device=DEV),
+                                       want_draft_target_prob=True)
+    o4, a4 = gpu.spec_verify_greedy(z, d)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(a1, a2)
+    assert torch.equal(p1.view(torch.int32), p2.view(torch.int32))
+    assert torch.equal(o3, o4) and torch.equal(a3, a4)
+
+
+def test_invalid_temperatures_are_greedy_and_flagged(gpu):
+    vi = synth.make_verify_inputs(synth.verify_config(2))
+    temps = np.array([0.7, -1.0, np.nan, np.inf, 1e-39, 1e-38, 0.0, 1.0], dtype=np.float32)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, acc, _ = gpu.spec_verify_mixed(dev(vi.logits), dev(vi.draft_probs), dev(vi.draft_tokens),
+                                        dev(vi.uniforms), dev(temps), device_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == gpu.DEVERR_TEMPERATURE
+    out, acc = out.cpu().numpy(), acc.cpu().numpy()
+    w_out, w_acc = oracle.verify_greedy(vi.logits, vi.spec.dtype, vi.draft_tokens)
+    for b in (1, 2, 3, 4, 6):
+        assert acc[b] == w_acc[b] and np.array_equal(out[b], w_out[b]), b
+    # the clean workspace: a sampled call afterwards is unaffected
+    _mixed_parity(gpu, vi, np.full(vi.spec.B, 0.9, np.float32))
