@@ -237,8 +237,15 @@ def main():
                              out_draft_tokens=d_tok, out_draft_probs=d_q if with_q else None,
                              want_draft_probs=with_q)
 
+    # a mixed serving batch: per-sequence temperatures from {0, 0.5, 0.7, 1.0, 1.3}
+    temps_np = synth.make_temperatures(B, 15)
+    temps = up(temps_np)
+
     def step(sample=True):
-        if sample:
+        if sample == "mixed":
+            sv.spec_verify_mixed(z, q, d, u, temps, out_tokens=out_t, out_num_accepted=acc_t,
+                                 out_draft_target_prob=pd_t, workspace=ws)
+        elif sample:
             sv.spec_verify_sample(z, q, d, u, vi.temperature, out_tokens=out_t,
                                   out_num_accepted=acc_t, out_draft_target_prob=pd_t, workspace=ws)
         else:
@@ -263,7 +270,8 @@ def main():
     def timed(sample):
         """Wall time per step with only the dominant kernel traced (two events
         per step), then per-kernel times from a second loop tracing all."""
-        dom = "verify_sample_rows" if sample else "verify_greedy_rows"
+        dom = {"mixed": "verify_mixed_rows", True: "verify_sample_rows",
+               False: "verify_greedy_rows"}[sample]
         for _ in range(args.warmup):
             step(sample); build()
         torch.cuda.synchronize()
@@ -352,6 +360,23 @@ def main():
                               "peagle_build_ms": kmsg["peagle_build"],
                               "step_hbm_gbs": (vg_rows + vg_scan + bb) / sec_g / 1e9,
                               "step_hbm_frac": (vg_rows + vg_scan + bb) / sec_g / 1e9 / HBM_PEAK_GBS}
+    if not args.no_greedy:
+        sec_m, kmsm, accm = timed("mixed")
+        sampled = temps_np > 0
+        vm_rows, _ = verify_bytes(B, K, V, 2, accm, sample=True)
+        # scan bytes: greedy sequences as in greedy mode, sampled ones as in sampling
+        ns = int(sampled.sum())
+        vm_draw = (B * K * 4 + B * (K + 1) * 4 + B * 4 + B * 4
+                   + ns * (K * 4 * 3 + (K + 1) * 4)
+                   + int(((accm < K) & sampled).sum()) * V * 4)
+        res["mixed_step"] = {
+            "value": rows / sec_m, "unit": "verified logit rows/s", "ms_per_step": sec_m * 1e3,
+            "workload": "the fused batch with per-sequence temperatures "
+                        f"({int((~sampled).sum())} greedy, {int(sampled.sum())} sampled), + build",
+            "kernels_ms": {k: v for k, v in kmsm.items()},
+            "step_hbm_gbs": (vm_rows + vm_draw + bb) / sec_m / 1e9,
+            "step_hbm_frac": (vm_rows + vm_draw + bb) / sec_m / 1e9 / HBM_PEAK_GBS}
+        log("mixed step timed")
     if not args.no_draft:
         def timed_draft(with_q):
             for _ in range(args.warmup):

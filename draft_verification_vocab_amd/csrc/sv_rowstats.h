@@ -125,7 +125,7 @@ __device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, l
 // step's loads before using any.  NT: non-temporal loads, for data read
 // exactly once (measured 10% faster than cached loads on gfx950).
 template <typename LT, int MODE, bool VEC, int THREADS, bool NT = true>
-__device__ Partial slice_stats(const LT* row, long o_lo, long o_hi, long V, float c,
+__device__ __forceinline__ Partial slice_stats(const LT* row, long o_lo, long o_hi, long V, float c,
                                float* sm_f, int* sm_i, double* sm_d) {
   constexpr int U = 16 / sizeof(LT);    // octets per step: 128 bytes in flight per thread
   const int t = threadIdx.x;

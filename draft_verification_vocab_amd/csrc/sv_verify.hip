@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void verify_rows(RowsArgs A) {
 // -1 padding, num_accepted and p_k(d_k); the new token is written by the
 // caller (greedy: g_a; sampling: the draw).
 template <typename LT, int MODE>
-__device__ ScanResult accept_scan(const ScanArgs& A, int b, bool write, float c) {
+__device__ __forceinline__ ScanResult accept_scan(const ScanArgs& A, int b, bool write, float c) {
   const int K = A.K, S = A.S;
   const long V = A.V;
   const int k = lane_id();
