@@ -30,6 +30,11 @@ of Eagle / MTP / DFlash / DSPark):
   softmax at each group's temperature, the exact greedy argmax chain inside a
   mixed batch, the fp32 boundary of invalid temperatures, and reduction to
   ``verify_sample`` / ``verify_greedy`` for uniform batches.
+* ``metrics.counters`` / ``rates``  acceptance counters of verify calls and the
+  acceptance length, tokens per round, draft acceptance rate and conditional
+  per-position rates.  Pinned by a hand-counted example, the closed forms of
+  independent acceptance (truncated geometric), and the verify oracle's
+  all-accept / all-reject cases.
 * ``peagle.build_draft_batch``    the P-EAGLE drafter batch.  Pinned by the
   invariants the P-EAGLE summary fixes (K-1 MASK rows per sequence, slot -1
   exactly on rejected tokens, h_shared on the MASK rows, the new token paired
@@ -38,7 +43,7 @@ of Eagle / MTP / DFlash / DSPark):
   the rejected padding rows are readings the pages leave open: those two
   aspects are parity unpinned by the pages.
 """
-from . import draft, mixed, peagle, verify  # noqa: F401
+from . import draft, metrics, mixed, peagle, verify  # noqa: F401
 from .mixed import verify_mixed  # noqa: F401
 from .draft import draft_distribution, draft_outcomes, draft_sample  # noqa: F401
 from .peagle import PADDING_SLOT_ID, build_draft_batch  # noqa: F401

@@ -174,3 +174,26 @@ def test_mixed_mutant_fails_pins(label, funcs, old, new):
     except (AssertionError, IndexError, ValueError, FloatingPointError):
         fails = ["raised"]
     assert fails, f"mutant '{label}' passed the mixed-batch pins"
+
+
+METRICS_MUTANTS = [
+    ("emitted without the new token", ["counters"], '"emitted": int(a.sum()) + int(a.size)',
+     '"emitted": int(a.sum())'),
+    ("histogram shifted", ["counters"], "hist[x] += 1", "hist[max(x - 1, 0)] += 1"),
+    ("conditional rate over all rounds", ["rates"], "passed / np.maximum(reached, 1)",
+     "passed / max(c['rounds'], 1)"),
+    ("steps not summed", ["accumulate"], 'for k in ("steps", "rounds"', 'for k in ("rounds"'),
+]
+
+
+@pytest.mark.parametrize("label,funcs,old,new", METRICS_MUTANTS,
+                         ids=[m[0] for m in METRICS_MUTANTS])
+def test_metrics_mutant_fails_pins(label, funcs, old, new):
+    import oracle.metrics as ometrics
+    from tests.test_oracle_metrics import check_module
+    m = _mutant_module(ometrics, funcs, old, new)
+    try:
+        fails = check_module(m)
+    except (AssertionError, IndexError, KeyError, ValueError):
+        fails = ["raised"]
+    assert fails, f"mutant '{label}' passed the metrics pins"
