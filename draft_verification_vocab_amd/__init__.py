@@ -49,6 +49,11 @@ _SIGS = {
                                ctypes.c_size_t, _p, _p]),
     "spec_draft_sample": (_i, [_p, _i, ctypes.c_int64, _p, _p, ctypes.c_float, _p, _i, _i, _i,
                                _p, _p, _p, _p]),
+    "spec_accept_metrics_words": (ctypes.c_size_t, [_i]),
+    "spec_accept_metrics": (_i, [_p, _i, _i, _p, _p, _p]),
+    "sv_step_graph_create": (_i, [_p, _p]),
+    "sv_step_graph_launch": (_i, [_p, _p]),
+    "sv_step_graph_destroy": (None, [_p]),
     "sv_kernel_name": (ctypes.c_char_p, [_i]),
     "sv_trace_begin": (_i, [_i, ctypes.c_uint]),
     "sv_trace_count": (_i, []),
@@ -99,7 +104,7 @@ def _check(status: int, what: str):
 KERNEL_IDS = {"verify_greedy_rows": 0, "verify_sample_rows": 1, "verify_sample_draw": 2,
               "peagle_build": 3, "verify_greedy_accept": 4, "verify_sample_accept": 5,
               "verify_sample_locate": 6, "draft_sample": 7, "verify_mixed_rows": 8,
-              "verify_mixed_accept": 9}
+              "verify_mixed_accept": 9, "accept_metrics": 10}
 
 
 def trace_begin(capacity: int, kernels=None):
@@ -411,3 +416,169 @@ def spec_draft_sample(drafter_logits: torch.Tensor, K: int, temperature: float,
                                _ptr(out_draft_probs), _ptr(device_error), _stream(dev))
     _check(st, "spec_draft_sample")
     return out_draft_tokens, out_draft_probs
+
+
+# ---------------------------------------------------------------- acceptance metrics
+METRICS_STEPS, METRICS_ROUNDS, METRICS_PROPOSED, METRICS_ACCEPTED, METRICS_EMITTED, \
+    METRICS_HIST = range(6)
+
+
+def accept_metrics_buffer(K: int, device) -> torch.Tensor:
+    """A zeroed counter array for spec_accept_metrics (int64 storage of the
+    uint64 counters)."""
+    n = require_library().spec_accept_metrics_words(int(K))
+    if n == 0:
+        raise ValueError(f"K={K} out of range")
+    return torch.zeros(n, dtype=torch.int64, device=device)
+
+
+def spec_accept_metrics(num_accepted: torch.Tensor, K: int, metrics: torch.Tensor,
+                        device_error: Optional[torch.Tensor] = None):
+    """Add one verify call's counts to `metrics`; see spec_accept_metrics in
+    include/spec_verify.h."""
+    lib = require_library()
+    if num_accepted.dim() != 1:
+        raise ValueError("num_accepted must be [B]")
+    B = num_accepted.shape[0]
+    dev = num_accepted.device
+    _dev(num_accepted, "num_accepted", torch.int32, (B,), dev)
+    _dev(metrics, "metrics", torch.int64, (lib.spec_accept_metrics_words(int(K)),), dev)
+    if device_error is not None:
+        _dev(device_error, "device_error", torch.int32, (1,), dev)
+    _check(lib.spec_accept_metrics(_ptr(num_accepted), B, int(K), _ptr(metrics),
+                                   _ptr(device_error), _stream(dev)), "spec_accept_metrics")
+    return metrics
+
+
+def acceptance_summary(metrics: torch.Tensor) -> dict:
+    """Host-side view of the counters (synchronises): the counts and the
+    acceptance length, tokens per round and draft acceptance rate."""
+    m = [int(x) for x in metrics.cpu().tolist()]
+    rounds, proposed, accepted, emitted = (m[METRICS_ROUNDS], m[METRICS_PROPOSED],
+                                           m[METRICS_ACCEPTED], m[METRICS_EMITTED])
+    return {"steps": m[METRICS_STEPS], "rounds": rounds, "proposed": proposed,
+            "accepted": accepted, "emitted": emitted, "hist": m[METRICS_HIST:],
+            "acceptance_length": accepted / rounds if rounds else float("nan"),
+            "tokens_per_round": emitted / rounds if rounds else float("nan"),
+            "draft_acceptance_rate": accepted / proposed if proposed else float("nan")}
+
+
+# ---------------------------------------------------------------- step graphs
+STEP_GREEDY, STEP_SAMPLE, STEP_MIXED = 0, 1, 2
+
+
+class _StepDesc(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("target_logits", _p), ("logits_dtype", ctypes.c_int),
+                ("draft_probs", _p), ("draft_tokens", _p), ("uniforms", _p),
+                ("temperature", ctypes.c_float), ("temperatures", _p),
+                ("B", ctypes.c_int), ("K", ctypes.c_int), ("V", ctypes.c_int),
+                ("out_tokens", _p), ("out_num_accepted", _p), ("out_draft_target_prob", _p),
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+                ("start_pos", _p), ("block_table", _p), ("max_blocks_per_seq", ctypes.c_int),
+                ("block_size", ctypes.c_int), ("target_hidden", _p), ("h_shared", _p),
+                ("hidden_dtype", ctypes.c_int), ("mask_token_id", ctypes.c_int32),
+                ("H", ctypes.c_int), ("out_input_ids", _p), ("out_positions", _p),
+                ("out_slot_mapping", _p), ("out_hidden", _p), ("out_sample_rows", _p),
+                ("metrics", _p), ("device_error", _p)]
+
+
+class StepGraph:
+    """One decode step (verify, then optionally the P-EAGLE build and the
+    acceptance metrics) captured as a HIP graph; see sv_step_graph_create in
+    include/spec_verify.h.  Every tensor is fixed at capture and kept alive
+    by this object; ``launch()`` replays the step on the current stream with
+    whatever the tensors hold.
+
+    verify: dict with target_logits, draft_tokens, out_tokens,
+      out_num_accepted, workspace, and for sampling draft_probs, uniforms and
+      temperature (mode "sample") or temperatures (mode "mixed"); optional
+      out_draft_target_prob.
+    build: None, or dict with start_pos, block_table, block_size,
+      target_hidden, h_shared, mask_token_id and outputs (as returned by
+      peagle_build_draft_batch or preallocated).
+    metrics: None, or a counter array from accept_metrics_buffer.
+    """
+
+    def __init__(self, mode: str, verify: dict, build: Optional[dict] = None,
+                 metrics: Optional[torch.Tensor] = None,
+                 device_error: Optional[torch.Tensor] = None):
+        lib = require_library()
+        z = verify["target_logits"]
+        if z.dim() != 3:
+            raise ValueError("target_logits must be [B, K+1, V]")
+        B, K1, V = z.shape
+        K = K1 - 1
+        dev = z.device
+        d = _StepDesc()
+        d.mode = {"greedy": STEP_GREEDY, "sample": STEP_SAMPLE, "mixed": STEP_MIXED}[mode]
+        keep = [z]
+
+        def ptr(t, name, dtype=None, shape=None):
+            if t is None:
+                return None
+            _dev(t, name, dtype, shape, dev)
+            keep.append(t)
+            return t.data_ptr()
+
+        d.target_logits = ptr(z, "target_logits")
+        d.logits_dtype = _DTYPES[z.dtype]
+        d.draft_tokens = ptr(verify["draft_tokens"], "draft_tokens", torch.int32, (B, K))
+        if mode != "greedy":
+            d.draft_probs = ptr(verify["draft_probs"], "draft_probs", torch.float32, (B, K, V))
+            d.uniforms = ptr(verify["uniforms"], "uniforms", torch.float32, (B, K + 1))
+        if mode == "sample":
+            d.temperature = float(verify["temperature"])
+        if mode == "mixed":
+            d.temperatures = ptr(verify["temperatures"], "temperatures", torch.float32, (B,))
+        d.B, d.K, d.V = B, K, V
+        d.out_tokens = ptr(verify["out_tokens"], "out_tokens", torch.int32, (B, K + 1))
+        d.out_num_accepted = ptr(verify["out_num_accepted"], "out_num_accepted", torch.int32, (B,))
+        d.out_draft_target_prob = ptr(verify.get("out_draft_target_prob"), "out_draft_target_prob",
+                                      torch.float32, (B, K))
+        ws = verify["workspace"]
+        d.workspace = ptr(ws, "workspace")
+        d.workspace_bytes = ws.numel() * ws.element_size()
+        if build is not None:
+            h = build["target_hidden"]
+            H = h.shape[1]
+            o = build["outputs"]
+            d.start_pos = ptr(build["start_pos"], "start_pos", torch.int64, (B,))
+            bt = build["block_table"]
+            d.block_table = ptr(bt, "block_table", torch.int32)
+            d.max_blocks_per_seq = bt.shape[1]
+            d.block_size = int(build["block_size"])
+            d.target_hidden = ptr(h, "target_hidden", None, (B * (K + 1), H))
+            d.h_shared = ptr(build["h_shared"], "h_shared", h.dtype, (H,))
+            d.hidden_dtype = _DTYPES[h.dtype]
+            d.mask_token_id = int(build["mask_token_id"])
+            d.H = H
+            d.out_input_ids = ptr(o["input_ids"], "input_ids", torch.int32, (B * 2 * K,))
+            d.out_positions = ptr(o["positions"], "positions", torch.int64, (B * 2 * K,))
+            d.out_slot_mapping = ptr(o["slot_mapping"], "slot_mapping", torch.int64, (B * 2 * K,))
+            d.out_hidden = ptr(o["hidden"], "hidden", h.dtype, (B * 2 * K, H))
+            d.out_sample_rows = ptr(o.get("sample_rows"), "sample_rows", torch.int32, (B, K))
+        if metrics is not None:
+            d.metrics = ptr(metrics, "metrics", torch.int64)
+        if device_error is not None:
+            d.device_error = ptr(device_error, "device_error", torch.int32, (1,))
+        self._keep = keep
+        self._desc = d
+        self._lib = lib
+        self._dev = dev
+        self._g = ctypes.c_void_p()
+        _check(lib.sv_step_graph_create(ctypes.byref(d), ctypes.byref(self._g)),
+               "sv_step_graph_create")
+
+    def launch(self):
+        _check(self._lib.sv_step_graph_launch(self._g, _stream(self._dev)), "sv_step_graph_launch")
+
+    def close(self):
+        if self._g:
+            self._lib.sv_step_graph_destroy(self._g)
+            self._g = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

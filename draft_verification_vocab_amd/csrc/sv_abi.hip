@@ -37,6 +37,9 @@ void trace_before(hipStream_t stream, int kernel_id) {
   if (tracer.pending) (void)hipEventRecord(tracer.ev[2 * tracer.count], stream);
 }
 
+TracePause::TracePause() : was_on(tracer.on) { tracer.on = false; }
+TracePause::~TracePause() { tracer.on = was_on; }
+
 void trace_after(hipStream_t stream, int kernel_id) {
   if (tracer.pending) {
     (void)hipEventRecord(tracer.ev[2 * tracer.count + 1], stream);
@@ -88,6 +91,7 @@ SV_API const char* sv_kernel_name(int kernel_id) {
     case SV_KERNEL_DRAFT_SAMPLE: return "draft_sample";
     case SV_KERNEL_VERIFY_MIXED_ROWS: return "verify_mixed_rows";
     case SV_KERNEL_VERIFY_MIXED_ACCEPT: return "verify_mixed_accept";
+    case SV_KERNEL_ACCEPT_METRICS: return "accept_metrics";
     default: return "unknown";
   }
 }
@@ -304,6 +308,116 @@ SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype,
   L.out_probs = out_draft_probs;
   L.device_error = device_error;
   return sv::launch_draft(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+SV_API size_t spec_accept_metrics_words(int K) {
+  if (K < 1 || K > SV_MAX_K) return 0;
+  return (size_t)SV_METRICS_HIST + K + 1;
+}
+
+SV_API sv_status spec_accept_metrics(const int32_t* num_accepted, int B, int K, uint64_t* metrics,
+                                     int32_t* device_error, void* stream) {
+  if (B < 0 || B > kMaxB || K < 1 || K > SV_MAX_K) return SV_ERR_SHAPE;
+  if (B == 0) return SV_OK;
+  if (!num_accepted || !metrics) return SV_ERR_NULL;
+  if (!aligned(num_accepted, 4) || !aligned(metrics, 8) ||
+      (device_error && !aligned(device_error, 4)))
+    return SV_ERR_ALIGN;
+  return sv::launch_metrics(num_accepted, B, K, metrics, device_error,
+                            static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- step graphs
+struct sv_step_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+  hipStream_t capture_stream;
+};
+
+namespace {
+
+// The calls of one step, in order, on stream s (each validates its arguments).
+sv_status enqueue_step(const sv_step_desc* d, hipStream_t s) {
+  sv_status st;
+  switch (d->mode) {
+    case SV_STEP_GREEDY:
+      st = spec_verify_greedy(d->target_logits, d->logits_dtype, d->draft_tokens, d->B, d->K,
+                              d->V, d->out_tokens, d->out_num_accepted, d->workspace,
+                              d->workspace_bytes, d->device_error, s);
+      break;
+    case SV_STEP_SAMPLE:
+      st = spec_verify_sample(d->target_logits, d->logits_dtype, d->draft_probs, d->draft_tokens,
+                              d->uniforms, d->temperature, d->B, d->K, d->V, d->out_tokens,
+                              d->out_num_accepted, d->out_draft_target_prob, d->workspace,
+                              d->workspace_bytes, d->device_error, s);
+      break;
+    default:
+      st = spec_verify_mixed(d->target_logits, d->logits_dtype, d->draft_probs, d->draft_tokens,
+                             d->uniforms, d->temperatures, d->B, d->K, d->V, d->out_tokens,
+                             d->out_num_accepted, d->out_draft_target_prob, d->workspace,
+                             d->workspace_bytes, d->device_error, s);
+      break;
+  }
+  if (st != SV_OK) return st;
+  if (d->out_hidden) {
+    st = peagle_build_draft_batch(d->out_tokens, d->out_num_accepted, d->draft_tokens,
+                                  d->start_pos, d->block_table, d->max_blocks_per_seq,
+                                  d->block_size, d->target_hidden, d->h_shared, d->hidden_dtype,
+                                  d->mask_token_id, d->B, d->K, d->H, d->out_input_ids,
+                                  d->out_positions, d->out_slot_mapping, d->out_hidden,
+                                  d->out_sample_rows, d->device_error, s);
+    if (st != SV_OK) return st;
+  }
+  if (d->metrics)
+    st = spec_accept_metrics(d->out_num_accepted, d->B, d->K, d->metrics, d->device_error, s);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+SV_API sv_status sv_step_graph_create(const sv_step_desc* desc, sv_step_graph** out) {
+  if (!desc || !out) return SV_ERR_NULL;
+  *out = nullptr;
+  if (desc->mode != SV_STEP_GREEDY && desc->mode != SV_STEP_SAMPLE && desc->mode != SV_STEP_MIXED)
+    return SV_ERR_VALUE;
+  if (desc->metrics && (desc->K < 1 || desc->K > SV_MAX_K)) return SV_ERR_SHAPE;
+  hipStream_t s = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return SV_ERR_HIP;
+  sv::TracePause pause;
+  if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipStreamDestroy(s);
+    return SV_ERR_HIP;
+  }
+  const sv_status st = enqueue_step(desc, s);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(s, &g);
+  hipGraphExec_t x = nullptr;
+  if (st != SV_OK || e != hipSuccess || !g ||
+      hipGraphInstantiate(&x, g, nullptr, nullptr, 0) != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    (void)hipStreamDestroy(s);
+    return st != SV_OK ? st : SV_ERR_HIP;
+  }
+  *out = new sv_step_graph{g, x, s};
+  return SV_OK;
+}
+
+SV_API sv_status sv_step_graph_launch(sv_step_graph* graph, void* stream) {
+  if (!graph) return SV_ERR_NULL;
+  return hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK
+                                                                                     : SV_ERR_HIP;
+}
+
+SV_API void sv_step_graph_destroy(sv_step_graph* graph) {
+  if (!graph) return;
+  (void)hipGraphExecDestroy(graph->exec);
+  (void)hipGraphDestroy(graph->graph);
+  (void)hipStreamDestroy(graph->capture_stream);
+  delete graph;
 }
 
 }  // extern "C"

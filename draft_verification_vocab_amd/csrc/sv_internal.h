@@ -73,5 +73,15 @@ size_t verify_workspace_bytes(int B, int K, int V);
 hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream);
 hipError_t launch_build(const BuildLaunch& L, hipStream_t stream);
 hipError_t launch_draft(const DraftLaunch& L, hipStream_t stream);
+hipError_t launch_metrics(const int32_t* num_accepted, int B, int K, uint64_t* metrics,
+                          int32_t* device_error, hipStream_t stream);
+
+// Pause kernel tracing on this host thread for the lifetime of the object
+// (graph capture records no timing events).
+struct TracePause {
+  TracePause();
+  ~TracePause();
+  bool was_on;
+};
 
 }  // namespace sv

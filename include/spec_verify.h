@@ -260,6 +260,90 @@ SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype,
                                    int32_t* device_error, void* stream);
 
 /*
+ * Acceptance metrics, accumulated on the device.  `metrics` is an array of
+ * spec_accept_metrics_words(K) uint64 counters in device memory, zeroed by the
+ * caller once; every call adds one verify call's counts:
+ *   [SV_METRICS_STEPS]     calls
+ *   [SV_METRICS_ROUNDS]    rounds (one sequence in one call)
+ *   [SV_METRICS_PROPOSED]  drafts proposed (K per round)
+ *   [SV_METRICS_ACCEPTED]  drafts accepted (sum of num_accepted)
+ *   [SV_METRICS_EMITTED]   tokens emitted (accepted + the new token per round)
+ *   [SV_METRICS_HIST + a]  rounds that accepted exactly a drafts, a = 0..K
+ * Acceptance length (mean accepted drafts per round, P-EAGLE / TorchSpec blog
+ * summary, section 监控与调优建议) = ACCEPTED / ROUNDS; tokens per round =
+ * EMITTED / ROUNDS; draft acceptance rate = ACCEPTED / PROPOSED ("Project 14",
+ * section 使用它, reports acceptance rate and accepted tokens per step); the
+ * histogram gives the acceptance rate at each draft position.  Counts are
+ * integers added with atomics, so totals are exact and order-independent.
+ * num_accepted [B] int32 as written by spec_verify_* (values outside [0, K]
+ * set SV_DEVERR_ACCEPT_COUNT and are clamped).  1 <= K <= SV_MAX_K.  B = 0 is a
+ * no-op.  One kernel is enqueued.
+ */
+#define SV_METRICS_STEPS 0
+#define SV_METRICS_ROUNDS 1
+#define SV_METRICS_PROPOSED 2
+#define SV_METRICS_ACCEPTED 3
+#define SV_METRICS_EMITTED 4
+#define SV_METRICS_HIST 5
+SV_API size_t spec_accept_metrics_words(int K);  /* SV_METRICS_HIST + K + 1; 0 if K is invalid */
+SV_API sv_status spec_accept_metrics(const int32_t* num_accepted, int B, int K, uint64_t* metrics,
+                                     int32_t* device_error, void* stream);
+
+/*
+ * One decode step captured once as a HIP graph and replayed with a single
+ * launch: the verify call (greedy, sampled or mixed), then, optionally, the
+ * P-EAGLE build from its outputs and the acceptance metrics.  Every buffer and
+ * shape is fixed at capture (static maximum shapes, as serving engines
+ * capture their graphs per batch size and extend the capture range by
+ * K x max_num_seqs for the drafter batch: P-EAGLE / TorchSpec blog summary,
+ * section TorchSpec 集成与工程优化); each replay reads whatever the buffers
+ * hold at that time.  The buffers must stay allocated while the graph exists.
+ * Fields mirror the arguments of the calls above; the build is skipped when
+ * out_hidden is NULL and the metrics when metrics is NULL.  Argument errors
+ * of the captured calls are returned by sv_step_graph_create, which then
+ * creates nothing.  Kernel tracing is paused during capture.
+ */
+#define SV_STEP_GREEDY 0
+#define SV_STEP_SAMPLE 1
+#define SV_STEP_MIXED 2
+typedef struct sv_step_desc {
+  int mode;                               /* SV_STEP_*                          */
+  const void* target_logits;
+  int logits_dtype;
+  const float* draft_probs;               /* sample / mixed                      */
+  const int32_t* draft_tokens;
+  const float* uniforms;                  /* sample / mixed                      */
+  float temperature;                      /* sample                              */
+  const float* temperatures;              /* mixed                               */
+  int B, K, V;
+  int32_t* out_tokens;
+  int32_t* out_num_accepted;
+  float* out_draft_target_prob;           /* optional                            */
+  void* workspace;
+  size_t workspace_bytes;
+  const int64_t* start_pos;               /* build                               */
+  const int32_t* block_table;
+  int max_blocks_per_seq, block_size;
+  const void* target_hidden;
+  const void* h_shared;
+  int hidden_dtype;
+  int32_t mask_token_id;
+  int H;
+  int32_t* out_input_ids;
+  int64_t* out_positions;
+  int64_t* out_slot_mapping;
+  void* out_hidden;                       /* NULL: no build                      */
+  int32_t* out_sample_rows;               /* optional                            */
+  uint64_t* metrics;                      /* NULL: no metrics                    */
+  int32_t* device_error;                  /* optional                            */
+} sv_step_desc;
+
+typedef struct sv_step_graph sv_step_graph;   /* opaque */
+SV_API sv_status sv_step_graph_create(const sv_step_desc* desc, sv_step_graph** out);
+SV_API sv_status sv_step_graph_launch(sv_step_graph* graph, void* stream);
+SV_API void sv_step_graph_destroy(sv_step_graph* graph);
+
+/*
  * Kernel tracing, a profiling aid.  While tracing is on for the calling host
  * thread, every kernel the library enqueues whose id is set in `kernel_mask`
  * (bit i = kernel id i; ~0u = all) is bracketed by two HIP timing events
@@ -280,6 +364,7 @@ SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype,
 #define SV_KERNEL_VERIFY_MIXED_ROWS 8    /* spec_verify_mixed: row statistics            */
 #define SV_KERNEL_VERIFY_MIXED_ACCEPT 9  /* spec_verify_mixed: accept scan (its draw and
                                             locate kernels carry ids 2 and 6)            */
+#define SV_KERNEL_ACCEPT_METRICS 10      /* spec_accept_metrics                          */
 
 SV_API const char* sv_kernel_name(int kernel_id);
 SV_API sv_status sv_trace_begin(int capacity, unsigned kernel_mask); /* SV_ERR_VALUE if capacity < 1 */

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
               "spec_draft_sample", "spec_verify_mixed", "spec_verify_workspace_bytes",
-              "sv_status_string"):
+              "sv_status_string", "spec_accept_metrics", "spec_accept_metrics_words",
+              "sv_step_graph_create", "sv_step_graph_launch", "sv_step_graph_destroy"):
         assert n in names
 
 
@@ -178,11 +179,11 @@ def test_tracer_host_paths(lib):
     assert lib.sv_trace_read(0, None, None) == ENULL
     import draft_verification_vocab_amd as sv
     assert all(lib.sv_kernel_name(i).decode() == n for n, i in sv.KERNEL_IDS.items())
-    names = [lib.sv_kernel_name(i) for i in range(10)]
+    names = [lib.sv_kernel_name(i) for i in range(11)]
     assert names == [b"verify_greedy_rows", b"verify_sample_rows", b"verify_sample_draw",
                      b"peagle_build", b"verify_greedy_accept", b"verify_sample_accept",
                      b"verify_sample_locate", b"draft_sample", b"verify_mixed_rows",
-                     b"verify_mixed_accept"]
+                     b"verify_mixed_accept", b"accept_metrics"]
     assert lib.sv_kernel_name(17) == b"unknown"
     lib.sv_trace_end()                              # harmless when tracing is off
 
@@ -239,3 +240,56 @@ def test_mixed_validation(lib):
     assert mixed(lib, temps=FAKE + 2) == EALIGN
     assert mixed(lib, ws=None) == EWS
     assert mixed(lib, wsb=8) == EWS
+
+
+def test_metrics_and_graph_validation(lib):
+    assert lib.spec_accept_metrics_words(0) == 0
+    assert lib.spec_accept_metrics_words(64) == 0
+    assert lib.spec_accept_metrics_words(7) == 5 + 8
+    am = lambda na=FAKE, B=4, K=7, m=FAKE, err=None: lib.spec_accept_metrics(na, B, K, m, err, None)
+    assert am(B=-1) == ESHAPE
+    assert am(K=0) == ESHAPE
+    assert am(K=64) == ESHAPE
+    assert am(B=0, na=None, m=None) == OK
+    assert am(na=None) == ENULL
+    assert am(m=None) == ENULL
+    assert am(m=FAKE + 4) == EALIGN
+    assert am(na=FAKE + 2) == EALIGN
+    # graph: argument checks that come before any HIP call
+    import draft_verification_vocab_amd as sv
+    g = ctypes.c_void_p()
+    assert lib.sv_step_graph_create(None, ctypes.byref(g)) == ENULL
+    d = sv._StepDesc()
+    assert lib.sv_step_graph_create(ctypes.byref(d), None) == ENULL
+    d.mode = 7
+    assert lib.sv_step_graph_create(ctypes.byref(d), ctypes.byref(g)) == EVALUE
+    d.mode, d.metrics, d.K = 1, FAKE, 0
+    assert lib.sv_step_graph_create(ctypes.byref(d), ctypes.byref(g)) == ESHAPE
+    assert lib.sv_step_graph_launch(None, None) == ENULL
+    lib.sv_step_graph_destroy(None)
+
+
+def test_step_desc_layout_matches_header():
+    """The ctypes mirror of sv_step_desc has the C struct's size and offsets:
+    compile a probe with the host compiler that prints them."""
+    import shutil
+    import tempfile
+    import draft_verification_vocab_amd as sv
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f for f, _ in sv._StepDesc._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"spec_verify.h\"\nint main(void){\n"
+    src += 'printf("%zu\\n", sizeof(sv_step_desc));\n'
+    for f in fields:
+        src += f'printf("%zu\\n", offsetof(sv_step_desc, {f}));\n'
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as t:
+        c = os.path.join(t, "probe.c")
+        exe = os.path.join(t, "probe")
+        open(c, "w").write(src)
+        subprocess.run([cc, "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        out = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                              check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(sv._StepDesc)
+    assert out[1:] == [getattr(sv._StepDesc, f).offset for f in fields]

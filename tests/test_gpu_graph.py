@@ -1,0 +1,159 @@
+"""GPU: on-device acceptance metrics and the captured decode-step graph.
+
+* spec_accept_metrics against oracle.metrics.counters, over several calls
+  and more sequences than one workgroup covers, with out-of-range accept
+  counts flagged and clamped.
+* A step graph (verify, build, metrics) replayed several times with new
+  inputs copied into its buffers and eager calls on other buffers in
+  between: every replay must equal the eager step on the same inputs bit for
+  bit, and the metrics must equal the oracle's counters of all replays.
+  Greedy, sampled and mixed graphs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.workloads import BuildSpec
+from tests.gpu_util import DEV, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_metrics_match_oracle(gpu):
+    rng = np.random.default_rng(71)
+    K = 7
+    m = gpu.accept_metrics_buffer(K, DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    want = None
+    for B in (1, 1000, 70_000):
+        a = rng.integers(0, K + 1, size=B).astype(np.int32)
+        gpu.spec_accept_metrics(dev(a), K, m, device_error=err)
+        c = oracle.metrics.counters(a, K)
+        want = c if want is None else oracle.metrics.accumulate(want, c)
+    torch.cuda.synchronize()
+    got = m.cpu().numpy()
+    assert int(err.item()) == 0
+    assert got[gpu.METRICS_STEPS] == want["steps"] == 3
+    assert got[gpu.METRICS_ROUNDS] == want["rounds"]
+    assert got[gpu.METRICS_PROPOSED] == want["proposed"]
+    assert got[gpu.METRICS_ACCEPTED] == want["accepted"]
+    assert got[gpu.METRICS_EMITTED] == want["emitted"]
+    assert np.array_equal(got[gpu.METRICS_HIST:], want["hist"])
+    s = gpu.acceptance_summary(m)
+    r = oracle.metrics.rates(want)
+    assert s["acceptance_length"] == r["acceptance_length"]
+    assert s["draft_acceptance_rate"] == r["draft_acceptance_rate"]
+    # out-of-range counts: flagged, clamped into [0, K]
+    m2 = gpu.accept_metrics_buffer(3, DEV)
+    gpu.spec_accept_metrics(dev(np.array([-2, 1, 5, 3], np.int32)), 3, m2, device_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == gpu.DEVERR_ACCEPT_COUNT
+    assert m2.cpu().numpy()[gpu.METRICS_HIST:].tolist() == [1, 1, 0, 2]
+
+
+def _build_inputs(B, K, V):
+    bi = synth.make_build_inputs(BuildSpec(0, B, K, 512, V, 16, 700, 16, 77, False))
+    return dict(start_pos=dev(bi.start_pos), block_table=dev(bi.block_table),
+                block_size=bi.spec.block_size, target_hidden=dev(bi.target_hidden),
+                h_shared=dev(bi.h_shared), mask_token_id=bi.mask_token_id)
+
+
+def _outputs(B, K, V, H):
+    return dict(tok=torch.empty((B, K + 1), dtype=torch.int32, device=DEV),
+                acc=torch.empty(B, dtype=torch.int32, device=DEV),
+                pd=torch.empty((B, K), dtype=torch.float32, device=DEV),
+                build={"input_ids": torch.empty(B * 2 * K, dtype=torch.int32, device=DEV),
+                       "positions": torch.empty(B * 2 * K, dtype=torch.int64, device=DEV),
+                       "slot_mapping": torch.empty(B * 2 * K, dtype=torch.int64, device=DEV),
+                       "hidden": torch.empty((B * 2 * K, H), dtype=torch.bfloat16, device=DEV),
+                       "sample_rows": torch.empty((B, K), dtype=torch.int32, device=DEV)})
+
+
+def _eager(sv, mode, inp, b, o, ws, m):
+    if mode == "greedy":
+        sv.spec_verify_greedy(inp["z"], inp["d"], out_tokens=o["tok"], out_num_accepted=o["acc"],
+                              workspace=ws)
+    elif mode == "sample":
+        sv.spec_verify_sample(inp["z"], inp["q"], inp["d"], inp["u"], inp["T"],
+                              out_tokens=o["tok"], out_num_accepted=o["acc"],
+                              out_draft_target_prob=o["pd"], workspace=ws)
+    else:
+        sv.spec_verify_mixed(inp["z"], inp["q"], inp["d"], inp["u"], inp["temps"],
+                             out_tokens=o["tok"], out_num_accepted=o["acc"],
+                             out_draft_target_prob=o["pd"], workspace=ws)
+    sv.peagle_build_draft_batch(o["tok"], o["acc"], inp["d"], b["start_pos"], b["block_table"],
+                                b["block_size"], b["target_hidden"], b["h_shared"],
+                                b["mask_token_id"], outputs=o["build"])
+    sv.spec_accept_metrics(o["acc"], inp["d"].shape[1], m)
+
+
+@pytest.mark.parametrize("mode", ["sample", "greedy", "mixed"])
+def test_step_graph_replays_match_eager(gpu, mode):
+    vi = synth.make_verify_inputs(synth.verify_config(2))
+    B, K, V = vi.spec.B, vi.spec.K, vi.spec.V
+    rng = np.random.default_rng(72)
+    temps = np.array([0.0, 0.5, 1.0, 0.0, 1.3, 0.7, 0.0, 2.0], dtype=np.float32)
+    inp = dict(z=dev(vi.logits), q=dev(vi.draft_probs), d=dev(vi.draft_tokens),
+               u=dev(vi.uniforms), T=vi.temperature, temps=dev(temps))
+    b = _build_inputs(B, K, V)
+    og, oe = _outputs(B, K, V, 512), _outputs(B, K, V, 512)
+    ws_g = torch.zeros(gpu.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=DEV)
+    ws_e = torch.zeros_like(ws_g)
+    mg, me = gpu.accept_metrics_buffer(K, DEV), gpu.accept_metrics_buffer(K, DEV)
+    verify = dict(target_logits=inp["z"], draft_tokens=inp["d"], out_tokens=og["tok"],
+                  out_num_accepted=og["acc"], workspace=ws_g)
+    if mode != "greedy":
+        verify.update(draft_probs=inp["q"], uniforms=inp["u"], out_draft_target_prob=og["pd"])
+    if mode == "sample":
+        verify["temperature"] = vi.temperature
+    if mode == "mixed":
+        verify["temperatures"] = inp["temps"]
+    graph = gpu.StepGraph(mode, verify, dict(b, outputs=og["build"]), metrics=mg)
+    accs = []
+    for rep in range(4):
+        # new inputs in the captured buffers: fresh uniforms and drafts
+        u_new = rng.random((B, K + 1), dtype=np.float32)
+        d_new = vi.draft_tokens.copy()
+        if rep % 2:
+            d_new[:, rep % K] = rng.integers(0, V, size=B)
+        inp["u"].copy_(dev(u_new))
+        inp["d"].copy_(dev(d_new))
+        graph.launch()
+        _eager(gpu, mode, inp, b, oe, ws_e, me)
+        torch.cuda.synchronize()
+        assert torch.equal(og["tok"], oe["tok"]) and torch.equal(og["acc"], oe["acc"]), rep
+        if mode != "greedy":
+            assert torch.equal(og["pd"].view(torch.int32), oe["pd"].view(torch.int32)), rep
+        for k in og["build"]:
+            assert torch.equal(og["build"][k], oe["build"][k]), (rep, k)
+        accs.append(oe["acc"].cpu().numpy())
+    want = oracle.metrics.counters(accs[0], K)
+    for a in accs[1:]:
+        want = oracle.metrics.accumulate(want, oracle.metrics.counters(a, K))
+    assert torch.equal(mg, me)
+    got = mg.cpu().numpy()
+    assert got[gpu.METRICS_ACCEPTED] == want["accepted"] and got[gpu.METRICS_STEPS] == 4
+    assert np.array_equal(got[gpu.METRICS_HIST:], want["hist"])
+    graph.close()
+
+
+def test_step_graph_argument_errors(gpu):
+    z = torch.zeros((2, 4, 64), dtype=torch.float32, device=DEV)
+    d = torch.zeros((2, 3), dtype=torch.int32, device=DEV)
+    verify = dict(target_logits=z, draft_tokens=d,
+                  out_tokens=torch.empty((2, 4), dtype=torch.int32, device=DEV),
+                  out_num_accepted=torch.empty(2, dtype=torch.int32, device=DEV),
+                  workspace=torch.zeros(16, dtype=torch.uint8, device=DEV))    # too small
+    with pytest.raises(gpu.SpecVerifyError):
+        gpu.StepGraph("greedy", verify)
+    verify["workspace"] = torch.zeros(gpu.spec_verify_workspace_bytes(2, 3, 64),
+                                      dtype=torch.uint8, device=DEV)
+    g = gpu.StepGraph("greedy", verify)
+    g.launch()
+    torch.cuda.synchronize()
+    # all-zero logits: every argmax is token 0, so all-zero drafts are all accepted
+    assert verify["out_num_accepted"].cpu().tolist() == [3, 3]
+    assert verify["out_tokens"].cpu().tolist() == [[0, 0, 0, 0], [0, 0, 0, 0]]
+    g.close()
