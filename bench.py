@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-greedy", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the captured step graph")
     ap.add_argument("--no-draft", action="store_true",
                     help="skip timing the drafter-output sampling kernel")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -174,6 +176,55 @@ def ingest_counters(fetch_csv, write_csv):
         f.write("\n".join(lines) + "\n")
     print(json.dumps({"traffic_file": TRAFFIC_FILE, "summary": md,
                       "dominant_hbm_bytes_per_launch": rec["hbm_bytes_per_launch"]}))
+
+
+def graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt, hid, hs, out_t, acc_t,
+                pd_t, ws, bouts):
+    """The fused sampled step (verify, build, acceptance metrics) replayed as
+    one captured HIP graph vs the same calls launched one by one, at the full
+    batch and at a small batch (the first 16 sequences) where launches
+    dominate; the metrics counters give the acceptance figures."""
+    def run(nb):
+        zz, qq, dd, uu = z[:nb], q[:nb], d[:nb], u[:nb]
+        oo = {k: (v[:nb * 2 * K] if k != "sample_rows" else v[:nb]) for k, v in bouts.items()}
+        m_e, m_g = sv.accept_metrics_buffer(K, z.device), sv.accept_metrics_buffer(K, z.device)
+        build = dict(start_pos=L[:nb], block_table=bt[:nb], block_size=bi.spec.block_size,
+                     target_hidden=hid[:nb * (K + 1)], h_shared=hs,
+                     mask_token_id=bi.mask_token_id, outputs=oo)
+
+        def eager():
+            sv.spec_verify_sample(zz, qq, dd, uu, vi.temperature, out_tokens=out_t[:nb],
+                                  out_num_accepted=acc_t[:nb], out_draft_target_prob=pd_t[:nb],
+                                  workspace=ws)
+            sv.peagle_build_draft_batch(out_t[:nb], acc_t[:nb], dd, build["start_pos"],
+                                        build["block_table"], build["block_size"],
+                                        build["target_hidden"], hs, bi.mask_token_id, outputs=oo)
+            sv.spec_accept_metrics(acc_t[:nb], K, m_e)
+
+        g = sv.StepGraph("sample", dict(target_logits=zz, draft_probs=qq, draft_tokens=dd,
+                                        uniforms=uu, temperature=vi.temperature,
+                                        out_tokens=out_t[:nb], out_num_accepted=acc_t[:nb],
+                                        out_draft_target_prob=pd_t[:nb], workspace=ws),
+                         build, metrics=m_g)
+        out = {"B": nb}
+        for name, fn in (("eager", eager), ("graph", g.launch)):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            out[f"{name}_ms_per_step"] = (time.perf_counter() - t0) / args.steps * 1e3
+        g.close()
+        summ = sv.acceptance_summary(m_g)
+        out["rows_per_s_graph"] = nb * (K + 1) / (out["graph_ms_per_step"] * 1e-3)
+        out["device_metrics"] = {k: summ[k] for k in ("steps", "acceptance_length",
+                                                      "tokens_per_round",
+                                                      "draft_acceptance_rate")}
+        return out
+    return {"note": "verify_sample + P-EAGLE build + acceptance metrics per step",
+            "full": run(B), "small": run(16)}
 
 
 def main():
@@ -377,6 +428,10 @@ def main():
             "step_hbm_gbs": (vm_rows + vm_draw + bb) / sec_m / 1e9,
             "step_hbm_frac": (vm_rows + vm_draw + bb) / sec_m / 1e9 / HBM_PEAK_GBS}
         log("mixed step timed")
+    if not args.no_graph:
+        res["graph_step"] = graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt,
+                                        hid, hs, out_t, acc_t, pd_t, ws, bouts)
+        log("graph step timed")
     if not args.no_draft:
         def timed_draft(with_q):
             for _ in range(args.warmup):
