@@ -35,6 +35,12 @@ of Eagle / MTP / DFlash / DSPark):
   per-position rates.  Pinned by a hand-counted example, the closed forms of
   independent acceptance (truncated geometric), and the verify oracle's
   all-accept / all-reject cases.
+* ``tree.verify_tree_*``          verification of a draft tree (greedy argmax
+  walk; recursive rejection over independently drafted children).  Pinned
+  by reduction to the chain verify when every node has one child, the exact
+  law of the first emitted token on star trees (bisection over the uniforms,
+  equal to the target softmax), chi-square on two-level trees, and a brute
+  force check of the greedy walk.
 * ``peagle.build_draft_batch``    the P-EAGLE drafter batch.  Pinned by the
   invariants the P-EAGLE summary fixes (K-1 MASK rows per sequence, slot -1
   exactly on rejected tokens, h_shared on the MASK rows, the new token paired
@@ -43,7 +49,7 @@ of Eagle / MTP / DFlash / DSPark):
   the rejected padding rows are readings the pages leave open: those two
   aspects are parity unpinned by the pages.
 """
-from . import draft, metrics, mixed, peagle, verify  # noqa: F401
+from . import draft, metrics, mixed, peagle, tree, verify  # noqa: F401
 from .mixed import verify_mixed  # noqa: F401
 from .draft import draft_distribution, draft_outcomes, draft_sample  # noqa: F401
 from .peagle import PADDING_SLOT_ID, build_draft_batch  # noqa: F401

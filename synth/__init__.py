@@ -18,6 +18,11 @@ from .workloads import (  # noqa: F401
     DRAFT_CONFIGS,
     make_draft_inputs,
     make_temperatures,
+    TreeInputs,
+    TreeSpec,
+    TREE_CONFIGS,
+    make_tree_inputs,
+    static_tree_parents,
     MIXED_TEMPERATURES,
     verify_config,
     build_config,

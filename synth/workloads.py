@@ -362,3 +362,112 @@ def make_temperatures(B: int, seed: int,
     for b in range(B):
         out[b] = np.float32(_seq_rng(seed, b, tag=5).choice(np.asarray(choices, np.float64)))
     return out
+
+
+# ---------------------------------------------------------------- draft trees
+@dataclasses.dataclass(frozen=True)
+class TreeSpec:
+    """Draft trees of N nodes per sequence (node 0 = the root).
+
+    shape "chain": node i's parent is i-1; "static": one branching shape for
+    every sequence, widths per depth; "random": per sequence, node i picks
+    its parent uniformly among the last few nodes.  Children are drawn
+    independently from their parent's draft row.
+    """
+    name: str
+    B: int
+    N: int
+    V: int
+    dtype: str
+    sigma: float
+    boost: str
+    temperature: float
+    draft_noise: float
+    draft_temperature: float
+    shape: str
+    widths: tuple
+    seed: int
+
+
+TREE_CONFIGS = {
+    "tree-tiny": TreeSpec("tree-tiny", 3, 6, 32, "f32", 2.0, "none", 1.0, 0.5, 1.0, "random", (),
+                          21),
+    "tree-mid": TreeSpec("tree-mid", 16, 15, 32000, "f32", 3.0, "one-token", 1.0, 1.0, 1.0,
+                         "static", (3, 2, 1), 22),
+    "tree-large": TreeSpec("tree-large", 64, 15, 151936, "bf16", 3.0, "zipf-head", 0.7, 1.0, 0.7,
+                           "static", (3, 2, 1), 23),
+}
+
+
+def static_tree_parents(widths: Sequence[int]) -> np.ndarray:
+    """Parents of a tree in which every node at depth d has widths[d] children
+    (breadth-first numbering; node 0 is the root)."""
+    parents, level = [], [0]
+    for w in widths:
+        nxt = []
+        for p in level:
+            for _ in range(w):
+                parents.append(p)
+                nxt.append(len(parents))
+        level = nxt
+    return np.asarray(parents, dtype=np.int32)
+
+
+@dataclasses.dataclass
+class TreeInputs:
+    spec: TreeSpec
+    logits: np.ndarray        # [B, N+1, V] float32 or uint16 bf16 bits
+    draft_probs: np.ndarray   # [B, N+1, V] float32: row n drafted node n's children
+    parents: np.ndarray       # [B, N] int32
+    tokens: np.ndarray        # [B, N] int32
+    uniforms: np.ndarray      # [B, N+1] float32: [:, i] tests node i, [:, 0] the final draw
+
+    @property
+    def temperature(self) -> float:
+        return self.spec.temperature
+
+
+def make_tree_inputs(spec: TreeSpec) -> TreeInputs:
+    B, N, V = spec.B, spec.N, spec.V
+    head = _zipf_head(spec) if spec.boost == "zipf-head" else None
+    ldt = np.uint16 if spec.dtype == "bf16" else np.float32
+    logits = np.empty((B, N + 1, V), dtype=ldt)
+    q = np.empty((B, N + 1, V), dtype=np.float32)
+    parents = np.empty((B, N), dtype=np.int32)
+    tokens = np.empty((B, N), dtype=np.int32)
+    u = np.empty((B, N + 1), dtype=np.float32)
+    static = static_tree_parents(spec.widths) if spec.shape == "static" else None
+    if static is not None:
+        assert static.size == N, (static.size, N)
+    for b in range(B):
+        rng = _seq_rng(spec.seed, b, tag=6)
+        z = rng.standard_normal((N + 1, V), dtype=np.float32)
+        z *= np.float32(spec.sigma)
+        if spec.boost == "one-token":
+            z[np.arange(N + 1), rng.integers(0, V, size=N + 1)] += np.float32(6.0)
+        elif head is not None:
+            z += head[None, :]
+        if spec.dtype == "bf16":
+            stored = f32_to_bf16_bits(z)
+            seen = bf16_bits_to_f32(stored).astype(np.float64)
+        else:
+            stored = z
+            seen = z.astype(np.float64)
+        logits[b] = stored
+        noise = rng.standard_normal((N + 1, V), dtype=np.float32).astype(np.float64)
+        x = (seen + spec.draft_noise * noise) / spec.draft_temperature
+        x -= x.max(axis=1, keepdims=True)
+        np.exp(x, out=x)
+        x /= x.sum(axis=1, keepdims=True)
+        q[b] = x.astype(np.float32)
+        if spec.shape == "chain":
+            par = np.arange(N, dtype=np.int32)
+        elif static is not None:
+            par = static
+        else:
+            par = np.array([int(rng.integers(max(0, i - 3), i)) for i in range(1, N + 1)],
+                           dtype=np.int32)
+        parents[b] = par
+        tokens[b] = [rng.choice(V, p=x[par[i]]) for i in range(N)]
+        u[b] = rng.random(N + 1, dtype=np.float32)
+    return TreeInputs(spec, logits, q, parents, tokens, u)

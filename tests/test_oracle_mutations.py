@@ -197,3 +197,31 @@ def test_metrics_mutant_fails_pins(label, funcs, old, new):
     except (AssertionError, IndexError, KeyError, ValueError):
         fails = ["raised"]
     assert fails, f"mutant '{label}' passed the metrics pins"
+
+
+TREE_MUTANTS = [
+    ("residual not renormalised", ["verify_tree_sample_seq"], "r, mass = res / S, res",
+     "r, mass = res, res"),
+    ("siblings tested from the last", ["children"],
+     "return [i for i in range(1, len(parent) + 1) if int(parent[i - 1]) == n]",
+     "return [i for i in range(len(parent), 0, -1) if int(parent[i - 1]) == n]"),
+    ("draw from p after rejections", ["verify_tree_sample_seq"],
+     "c, _, _ = inverse_cdf(mass, float(u[0]))", "c, _, _ = inverse_cdf(p, float(u[0]))"),
+    ("test against p after a rejection", ["verify_tree_sample_seq"], "ratio = r[x] / q[cur, x]",
+     "ratio = p[x] / q[cur, x]"),
+    ("greedy takes the last matching child", ["verify_tree_greedy_seq"],
+     "nxt = next((i for i in children(parent, cur) if int(token[i - 1]) == g), None)",
+     "nxt = next((i for i in reversed(children(parent, cur)) if int(token[i - 1]) == g), None)"),
+]
+
+
+@pytest.mark.parametrize("label,funcs,old,new", TREE_MUTANTS, ids=[m[0] for m in TREE_MUTANTS])
+def test_tree_mutant_fails_pins(label, funcs, old, new):
+    import oracle.tree as otree
+    from tests.test_oracle_tree import check_module
+    m = _mutant_module(otree, funcs, old, new)
+    try:
+        fails = check_module(m)
+    except (AssertionError, IndexError, KeyError, ValueError, ZeroDivisionError):
+        fails = ["raised"]
+    assert fails, f"mutant '{label}' passed the tree pins"

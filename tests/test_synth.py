@@ -112,3 +112,19 @@ def test_mixed_temperatures():
     assert t.dtype == np.float32 and t.shape == (200,)
     assert set(t.tolist()) == set(np.float32(MIXED_TEMPERATURES).tolist())
     assert np.array_equal(t[:50], make_temperatures(50, 9))
+
+
+def test_tree_inputs():
+    from synth import TREE_CONFIGS, make_tree_inputs, static_tree_parents
+    assert static_tree_parents((3, 2, 1)).tolist() == [0, 0, 0, 1, 1, 2, 2, 3, 3,
+                                                       4, 5, 6, 7, 8, 9]
+    for name in ("tree-tiny", "tree-mid"):
+        ti = make_tree_inputs(TREE_CONFIGS[name])
+        s = ti.spec
+        assert ti.logits.shape == (s.B, s.N + 1, s.V) and ti.uniforms.shape == (s.B, s.N + 1)
+        for b in range(s.B):
+            assert all(0 <= ti.parents[b, i] <= i for i in range(s.N))   # parent of node i+1
+        assert ((ti.tokens >= 0) & (ti.tokens < s.V)).all()
+        assert np.allclose(ti.draft_probs.sum(axis=2), 1.0, atol=1e-5)
+        again = make_tree_inputs(s)
+        assert np.array_equal(again.tokens, ti.tokens) and np.array_equal(again.logits, ti.logits)
