@@ -27,7 +27,7 @@ __all__ = [
 SV_F32, SV_BF16, SV_F16 = 0, 1, 2
 PADDING_SLOT_ID = -1
 DEVERR_DRAFT_TOKEN, DEVERR_ACCEPT_COUNT, DEVERR_BLOCK_TABLE = 1, 2, 4
-DEVERR_ROW_INDEX, DEVERR_TEMPERATURE = 8, 16
+DEVERR_ROW_INDEX, DEVERR_TEMPERATURE, DEVERR_TREE = 8, 16, 32
 MAX_K = 63
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,6 +49,8 @@ _SIGS = {
                                ctypes.c_size_t, _p, _p]),
     "spec_draft_sample": (_i, [_p, _i, ctypes.c_int64, _p, _p, ctypes.c_float, _p, _i, _i, _i,
                                _p, _p, _p, _p]),
+    "spec_verify_tree": (_i, [_p, _i, _p, _p, _p, _p, ctypes.c_float, _i, _i, _i, _p, _p, _p, _p,
+                              ctypes.c_size_t, _p, _p]),
     "spec_accept_metrics_words": (ctypes.c_size_t, [_i]),
     "spec_accept_metrics": (_i, [_p, _i, _i, _p, _p, _p]),
     "sv_step_graph_create": (_i, [_p, _p]),
@@ -104,7 +106,7 @@ def _check(status: int, what: str):
 KERNEL_IDS = {"verify_greedy_rows": 0, "verify_sample_rows": 1, "verify_sample_draw": 2,
               "peagle_build": 3, "verify_greedy_accept": 4, "verify_sample_accept": 5,
               "verify_sample_locate": 6, "draft_sample": 7, "verify_mixed_rows": 8,
-              "verify_mixed_accept": 9, "accept_metrics": 10}
+              "verify_mixed_accept": 9, "accept_metrics": 10, "tree_rows": 11, "tree_walk": 12}
 
 
 def trace_begin(capacity: int, kernels=None):
@@ -416,6 +418,56 @@ def spec_draft_sample(drafter_logits: torch.Tensor, K: int, temperature: float,
                                _ptr(out_draft_probs), _ptr(device_error), _stream(dev))
     _check(st, "spec_draft_sample")
     return out_draft_tokens, out_draft_probs
+
+
+# ---------------------------------------------------------------- draft trees
+def spec_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor,
+                     temperature: float = 0.0, draft_probs: Optional[torch.Tensor] = None,
+                     uniforms: Optional[torch.Tensor] = None,
+                     out_tokens: Optional[torch.Tensor] = None,
+                     out_path: Optional[torch.Tensor] = None,
+                     out_num_accepted: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     device_error: Optional[torch.Tensor] = None):
+    """Verify a draft tree per sequence (temperature 0 = greedy); see
+    spec_verify_tree in include/spec_verify.h.
+
+    Returns (out_tokens [B, N+1], out_path [B, N+1], num_accepted [B])."""
+    lib = require_library()
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, N+1, V]")
+    B, N1, V = target_logits.shape
+    N = N1 - 1
+    dev = target_logits.device
+    _dev(target_logits, "target_logits")
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("target_logits must be float32 or bfloat16")
+    _dev(parents, "parents", torch.int32, (B, N), dev)
+    _dev(tokens, "tokens", torch.int32, (B, N), dev)
+    if temperature > 0:
+        _dev(draft_probs, "draft_probs", torch.float32, (B, N + 1, V), dev)
+        _dev(uniforms, "uniforms", torch.float32, (B, N + 1), dev)
+    out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev) if out_tokens is None \
+        else _dev(out_tokens, "out_tokens", torch.int32, (B, N + 1), dev)
+    out_path = torch.empty((B, N + 1), dtype=torch.int32, device=dev) if out_path is None \
+        else _dev(out_path, "out_path", torch.int32, (B, N + 1), dev)
+    out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev) if out_num_accepted is None \
+        else _dev(out_num_accepted, "out_num_accepted", torch.int32, (B,), dev)
+    need = spec_verify_workspace_bytes(B, N, V)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    _dev(workspace, "workspace", device=dev)
+    if device_error is not None:
+        _dev(device_error, "device_error", torch.int32, (1,), dev)
+    st = lib.spec_verify_tree(_ptr(target_logits), _DTYPES[target_logits.dtype],
+                              _ptr(draft_probs if temperature > 0 else None), _ptr(parents),
+                              _ptr(tokens), _ptr(uniforms if temperature > 0 else None),
+                              float(temperature), B, N, V, _ptr(out_tokens), _ptr(out_path),
+                              _ptr(out_num_accepted), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(device_error),
+                              _stream(dev))
+    _check(st, "spec_verify_tree")
+    return out_tokens, out_path, out_num_accepted
 
 
 # ---------------------------------------------------------------- acceptance metrics

@@ -92,6 +92,8 @@ SV_API const char* sv_kernel_name(int kernel_id) {
     case SV_KERNEL_VERIFY_MIXED_ROWS: return "verify_mixed_rows";
     case SV_KERNEL_VERIFY_MIXED_ACCEPT: return "verify_mixed_accept";
     case SV_KERNEL_ACCEPT_METRICS: return "accept_metrics";
+    case SV_KERNEL_TREE_ROWS: return "tree_rows";
+    case SV_KERNEL_TREE_WALK: return "tree_walk";
     default: return "unknown";
   }
 }
@@ -308,6 +310,50 @@ SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype,
   L.out_probs = out_draft_probs;
   L.device_error = device_error;
   return sv::launch_draft(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+SV_API sv_status spec_verify_tree(const void* target_logits, int logits_dtype,
+                                  const float* draft_probs, const int32_t* parents,
+                                  const int32_t* tokens, const float* uniforms, float temperature,
+                                  int B, int N, int V, int32_t* out_tokens, int32_t* out_path,
+                                  int32_t* out_num_accepted, void* workspace,
+                                  size_t workspace_bytes, int32_t* device_error, void* stream) {
+  sv_status st = check_verify_shape(B, N, V);
+  if (st != SV_OK) return st;
+  if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (!(temperature >= 0.0f && isfinite(temperature))) return SV_ERR_VALUE;
+  const bool sample = temperature > 0.0f;
+  if (sample && !isfinite((float)(1.4426950408889634 / (double)temperature))) return SV_ERR_VALUE;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !out_tokens || !out_path || !out_num_accepted) return SV_ERR_NULL;
+  if (N > 0 && (!parents || !tokens)) return SV_ERR_NULL;
+  if (sample && (!draft_probs || !uniforms)) return SV_ERR_NULL;
+  if (!workspace || workspace_bytes < sv::verify_workspace_bytes(B, N, V)) return SV_ERR_WORKSPACE;
+  const size_t esz = logits_dtype == SV_BF16 ? 2 : 4;
+  if (!aligned(target_logits, esz) || !aligned(out_tokens, 4) || !aligned(out_path, 4) ||
+      !aligned(out_num_accepted, 4) || !aligned(workspace, 16) ||
+      (parents && !aligned(parents, 4)) || (tokens && !aligned(tokens, 4)) ||
+      (draft_probs && !aligned(draft_probs, 4)) || (uniforms && !aligned(uniforms, 4)) ||
+      (device_error && !aligned(device_error, 4)))
+    return SV_ERR_ALIGN;
+  if ((long)B * (N + 1) * sv::verify_splits(B, N, V) > 0x7fffffffL) return SV_ERR_SHAPE;
+  sv::TreeLaunch L;
+  L.logits = target_logits;
+  L.draft_probs = sample ? draft_probs : nullptr;
+  L.parents = parents;
+  L.tokens = tokens;
+  L.uniforms = uniforms;
+  L.temperature = temperature;
+  L.B = B; L.N = N; L.V = V;
+  L.bf16 = logits_dtype == SV_BF16;
+  L.vec = (V % 8 == 0) && aligned(target_logits, 16) &&
+          (!sample || aligned(draft_probs, 16));
+  L.out_tokens = out_tokens;
+  L.out_path = out_path;
+  L.out_num_accepted = out_num_accepted;
+  L.workspace = workspace;
+  L.device_error = device_error;
+  return sv::launch_tree(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 SV_API size_t spec_accept_metrics_words(int K) {

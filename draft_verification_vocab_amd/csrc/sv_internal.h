@@ -64,7 +64,34 @@ struct DraftLaunch {
   int32_t* device_error;         // may be NULL
 };
 
+struct TreeLaunch {
+  const void* logits;            // [B][N+1][V]
+  const float* draft_probs;      // [B][N+1][V] (sampled)
+  const int32_t* parents;        // [B][N]
+  const int32_t* tokens;         // [B][N]
+  const float* uniforms;         // [B][N+1] (sampled)
+  float temperature;             // 0 = greedy
+  int B, N, V;
+  int bf16;
+  int vec;
+  int32_t* out_tokens;           // [B][N+1]
+  int32_t* out_path;             // [B][N+1]
+  int32_t* out_num_accepted;     // [B]
+  void* workspace;
+  int32_t* device_error;
+};
+
+// The row-statistics partials of a verify workspace: [B][K+1][S] entries.
+struct RowPartials {
+  void* partials;
+  int S;
+};
+
 int verify_splits(int B, int K, int V);
+RowPartials row_partials(void* workspace, int B, int K, int V);
+hipError_t launch_row_stats(const void* logits, int bf16, int vec, int sample, float c, int B,
+                            int K, int V, void* workspace, int trace_id, hipStream_t stream);
+hipError_t launch_tree(const TreeLaunch& L, hipStream_t stream);
 
 // Kernel tracing (per host thread): bracket a launch with events on its stream.
 void trace_before(hipStream_t stream, int kernel_id);

@@ -1,0 +1,265 @@
+// Draft-tree verification for gfx950.  "Project 14 - speculative decoding
+// inference server", section 概念: P-EAGLE's parallel speculation forms deeper
+// draft trees; the target verifies every node in one forward, giving one
+// logit row per node (row 0 = the root, the last committed token).
+//
+// Row statistics of all B * (N+1) rows come from the verify row kernel (one
+// pass over every logit).  Then one workgroup per sequence walks the tree:
+//   greedy   move to the lowest-index child whose token is the row's argmax;
+//            emit the argmax when none matches;
+//   sampled  test the children of the current node in index order against
+//            the residual r_m = max(0, p - w_m q) / S_m (w_0 = 0, S_0 = 1;
+//            after a rejection w_{m+1} = w_m + S_m and S_{m+1} is the mass of
+//            the new residual, one workgroup pass over the node's row) --
+//            the normalise-and-subtract recursion of rejection sampling over
+//            independently drafted candidates, written so that one pass per
+//            rejection suffices; an accepted child becomes the current node;
+//            when every child is rejected, or the node is a leaf, the new
+//            token is drawn from the residual by inverse CDF (tile masses in
+//            LDS, then the in-tile search the chain draw uses).
+// All threads of a workgroup take the same decisions from the same values,
+// so the workgroup-wide passes sit in uniform control flow.
+#include "sv_device.h"
+#include "sv_internal.h"
+#include "sv_rowstats.h"
+
+namespace sv {
+
+constexpr int kTreeThreads = 256;
+constexpr int kTreeWaves = kTreeThreads / kWave;
+
+struct TreeArgs {
+  TreeLaunch L;
+  Partial* partials;       // [B][N+1][S]
+  int S;
+  float c;                 // log2(e) / T (sampled)
+};
+
+// Residual masses of the kTileLoads octets of tile t seen by this lane:
+// max(0, p - w q) with p = 2^(z c - Mc) * inv_s (residual = false: p).
+template <typename LT, bool VEC>
+__device__ __forceinline__ void tile_residual(const LT* zrow, const float* qrow, bool residual,
+                                              int t, long V, long nocts, float c, float Mc,
+                                              float inv_s, float w, float (&r)[kTileLoads][8]) {
+  const int l = lane_id();
+#pragma unroll
+  for (int sl = 0; sl < kTileLoads; ++sl) {
+    const long o = ((long)t * kTileLoads + sl) * kWave + l;
+    float z[8], q[8];
+    if constexpr (VEC) {
+      const long oc = o < nocts ? o : nocts - 1;
+      Raw<LT> rz;
+      raw_load<false>(zrow, oc, rz);
+      unpack(rz, z);
+      if (residual) {
+        Raw<float> rq;
+        raw_load<false>(qrow, oc, rq);
+        unpack(rq, q);
+      }
+      if (o >= nocts)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[j] = -INFINITY;
+    } else {
+      load_octet<false>(zrow, o, V, false, -INFINITY, z);
+      if (residual) load_octet<false>(qrow, o, V, false, 0.f, q);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(z[j], c, -Mc)) * inv_s;
+      r[sl][j] = residual ? fmaxf(0.f, fmaf(-w, q[j], p)) : p;
+    }
+  }
+}
+
+// Tile masses of the residual into tsum (LDS); returns the fp64 total, the
+// same on every thread.  Called in uniform control flow.
+template <typename LT, bool VEC>
+__device__ __forceinline__ double residual_tiles(const LT* zrow, const float* qrow, bool residual, float w,
+                                 long V, long nocts, int T_tiles, float c, float Mc, float inv_s,
+                                 float* tsum, double* red) {
+  const int wv = threadIdx.x / kWave, l = lane_id();
+  double part = 0.0;
+  for (int t = wv; t < T_tiles; t += kTreeWaves) {
+    float r[kTileLoads][8];
+    tile_residual<LT, VEC>(zrow, qrow, residual, t, V, nocts, c, Mc, inv_s, w, r);
+    float ls = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kTileLoads; ++sl) ls += tree_sum8(r[sl]);
+    const float ts = wave_sum_f(ls);
+    if (l == 0) tsum[t] = ts;
+    part += (double)ts;
+  }
+  if (l == 0) red[wv] = part;
+  __syncthreads();
+  double tot = 0.0;
+  for (int i = 0; i < kTreeWaves; ++i) tot += red[i];
+  __syncthreads();
+  return tot;
+}
+
+template <typename LT, int MODE, bool VEC>
+__global__ __launch_bounds__(kTreeThreads) void tree_walk(TreeArgs A) {
+  __shared__ int s_par[SV_MAX_K + 1];
+  __shared__ int s_tok[SV_MAX_K + 1];
+  __shared__ float tsum[kMaxTiles];
+  __shared__ double red[kTreeWaves];
+
+  const TreeLaunch& L = A.L;
+  const int b = blockIdx.x, N = L.N, t = threadIdx.x, S = A.S;
+  const long V = L.V, nocts = (V + 7) / 8;
+  const int T_tiles = (int)((V + kTileElems - 1) / kTileElems);
+  if (t < N) {
+    // node i = t + 1: its parent must precede it and its token lie in [0, V)
+    const int par = L.parents[(long)b * N + t];
+    const int tok = L.tokens[(long)b * N + t];
+    const bool ok = par >= 0 && par <= t && tok >= 0 && tok < V;
+    if (!ok) flag_error(L.device_error, SV_DEVERR_TREE);
+    s_par[t + 1] = ok ? par : -1;          // an invalid node is nobody's child
+    s_tok[t + 1] = tok;
+  }
+  __syncthreads();
+
+  const LT* zb = static_cast<const LT*>(L.logits) + (long)b * (N + 1) * V;
+  Partial* Pb = A.partials + (long)b * (N + 1) * S;
+  int32_t* out = L.out_tokens + (long)b * (N + 1);
+  int32_t* path = L.out_path + (long)b * (N + 1);
+  const float c = A.c;
+  int cur = 0, depth = 0;
+  for (;;) {
+    // statistics of row cur from its S partials (same order on every thread)
+    float M = -INFINITY;
+    int g = INT32_MAX;
+    double s = 0.0;
+    if constexpr (MODE == GREEDY) {
+      for (int j = 0; j < S; ++j) {
+        const Partial p = Pb[cur * S + j];
+        if (j == 0 || p.m > M) { M = p.m; g = p.g; }
+      }
+    } else {
+      for (int j = 0; j < S; ++j) M = fmaxf(M, Pb[cur * S + j].m);
+      for (int j = 0; j < S; ++j) {
+        const Partial p = Pb[cur * S + j];
+        if (p.acc != 0.0) s += p.acc * exp2(((double)p.m - (double)M) * (double)c);
+      }
+    }
+    const LT* zrow = zb + (long)cur * V;
+    int nxt = -1;
+    if constexpr (MODE == GREEDY) {
+      if (g < 0 || g >= V) g = 0;          // a NaN row: any in-range token
+      for (int i = 1; i <= N; ++i)
+        if (s_par[i] == cur && s_tok[i] == g) { nxt = i; break; }
+      if (nxt < 0) {
+        if (t == 0) out[depth] = g;
+        break;
+      }
+    } else {
+      const float* qrow = L.draft_probs + ((long)b * (N + 1) + cur) * V;
+      // p = 2^(z c - Mc) * inv_s; Mc is M*c rounded to fp32, folded into inv_s
+      const float Mc = M * c;
+      const float inv_s = (float)(exp2((double)Mc - (double)M * (double)c) / s);
+      double w = 0.0, Sr = 1.0;            // residual r = max(0, p - w q) / Sr
+      bool tiles = false;                  // tsum holds the current residual's tiles
+      // one call site for the workgroup pass: after each rejection (the new
+      // residual's mass), and before the final draw when tsum is not current
+      for (int i = 1;; ++i) {
+        while (i <= N && s_par[i] != cur) ++i;
+        bool final_pass = false;
+        if (i <= N) {
+          const int x = s_tok[i];
+          const double px = exp2(((double)logit_at(zrow, x) - (double)M) * (double)c) / s;
+          const double qx = (double)qrow[x];
+          const double R = fmax(0.0, px - w * qx);
+          const double ratio = qx > 0.0 ? R / (Sr * qx) : (R > 0.0 ? INFINITY : 0.0);
+          if ((double)L.uniforms[(long)b * (N + 1) + i] < ratio) { nxt = i; break; }
+          w += Sr;
+        } else {
+          if (tiles) break;                // tsum already holds the residual
+          final_pass = true;               // w = 0 here: the tiles of p
+        }
+        const double tot = residual_tiles<LT, VEC>(zrow, qrow, w > 0.0, (float)w, V, nocts,
+                                                   T_tiles, c, Mc, inv_s, tsum, red);
+        if (final_pass) break;
+        Sr = tot;
+        tiles = true;
+        if (!(Sr > 0.0)) { w = 0.0; Sr = 1.0; tiles = false; }   // empty residual: back to p
+      }
+      if (nxt < 0) {
+        // final draw from the residual (p when w = 0) with u[0]
+        const bool residual = w > 0.0;
+        if (t < kWave) {
+          const int l = t;
+          const int per = (T_tiles + kWave - 1) / kWave;
+          const int lo = min(T_tiles, l * per), hi = min(T_tiles, (l + 1) * per);
+          double part = 0.0;
+          for (int k = lo; k < hi; ++k) part += (double)tsum[k];
+          const double incl = wave_inclusive_scan(part);
+          const double target = (double)L.uniforms[(long)b * (N + 1)] * __shfl(incl, kWave - 1);
+          double run = __shfl_up(incl, 1);
+          if (l == 0) run = 0.0;
+          int hit = -1, last = -1;
+          double pre = 0.0;
+          for (int k = lo; k < hi; ++k) {
+            const float ts = tsum[k];
+            if (ts > 0.f) last = k;
+            const double nx = run + (double)ts;
+            if (hit < 0 && nx > target) { hit = k; pre = run; }
+            run = nx;
+          }
+          int tile;
+          bool fallback = false;
+          const unsigned long long any = __ballot(hit >= 0);
+          if (any) {
+            const int src = __ffsll((long long)any) - 1;
+            tile = __shfl(hit, src);
+            pre = __shfl(pre, src);
+          } else {
+            const unsigned long long anyp = __ballot(last >= 0);
+            tile = anyp ? __shfl(last, 63 - __clzll((long long)anyp)) : 0;
+            fallback = true;
+          }
+          float r[kTileLoads][8];
+          tile_residual<LT, VEC>(zrow, qrow, residual, tile, V, nocts, c, Mc, inv_s, (float)w, r);
+          const int pick = pick_in_tile(r, tile, pre, target, fallback);
+          if (l == 0) out[depth] = pick;
+        }
+        break;
+      }
+    }
+    if (t == 0) {
+      out[depth] = s_tok[nxt];
+      path[depth] = nxt;
+    }
+    ++depth;
+    cur = nxt;
+  }
+  for (int j = depth + 1 + t; j <= N; j += kTreeThreads) out[j] = -1;
+  for (int j = depth + t; j <= N; j += kTreeThreads) path[j] = -1;
+  if (t == 0) L.out_num_accepted[b] = depth;
+  // the partials are consumed: clear them so the workspace ends all zero
+  for (int i = t; i < (N + 1) * S; i += kTreeThreads) Pb[i] = Partial{0.f, 0, 0.0};
+}
+
+hipError_t launch_tree(const TreeLaunch& L, hipStream_t stream) {
+  const bool sample = L.temperature > 0.f;
+  const float c = sample ? (float)(1.4426950408889634 / (double)L.temperature) : 1.0f;
+  hipError_t err = launch_row_stats(L.logits, L.bf16, L.vec, sample, c, L.B, L.N, L.V, L.workspace,
+                                    SV_KERNEL_TREE_ROWS, stream);
+  if (err != hipSuccess) return err;
+  const RowPartials rp = row_partials(L.workspace, L.B, L.N, L.V);
+  TreeArgs A{L, static_cast<Partial*>(rp.partials), rp.S, c};
+  const dim3 grid((unsigned)L.B), block(kTreeThreads);
+  trace_before(stream, SV_KERNEL_TREE_WALK);
+#define SV_TREE(LT, MODE) \
+  do { \
+    if (L.vec) hipLaunchKernelGGL((tree_walk<LT, MODE, true>), grid, block, 0, stream, A); \
+    else hipLaunchKernelGGL((tree_walk<LT, MODE, false>), grid, block, 0, stream, A); \
+  } while (0)
+  if (L.bf16) { if (sample) SV_TREE(uint16_t, SAMPLE); else SV_TREE(uint16_t, GREEDY); }
+  else { if (sample) SV_TREE(float, SAMPLE); else SV_TREE(float, GREEDY); }
+#undef SV_TREE
+  err = hipGetLastError();
+  trace_after(stream, SV_KERNEL_TREE_WALK);
+  return err;
+}
+
+}  // namespace sv

@@ -85,6 +85,11 @@ static Layout layout(int B, int K, int V) {
 
 size_t verify_workspace_bytes(int B, int K, int V) { return layout(B, K, V).total; }
 
+RowPartials row_partials(void* workspace, int B, int K, int V) {
+  const Layout lay = layout(B, K, V);
+  return RowPartials{reinterpret_cast<char*>(workspace) + lay.partials, lay.S};
+}
+
 struct RowsArgs {
   const void* logits;
   const float* temperatures;  // mixed: [B] per-sequence temperatures
@@ -479,6 +484,32 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
 }
 
 // ----------------------------------------------------------------------------
+hipError_t launch_row_stats(const void* logits, int bf16, int vec, int sample, float c, int B,
+                            int K, int V, void* workspace, int trace_id, hipStream_t stream) {
+  const Layout lay = layout(B, K, V);
+  RowsArgs R;
+  R.logits = logits;
+  R.temperatures = nullptr;
+  R.c = c;
+  R.K = K; R.V = V; R.S = lay.S;
+  R.octets = (V + 7) / 8;
+  R.partials = reinterpret_cast<Partial*>(static_cast<char*>(workspace) + lay.partials);
+  const dim3 grid1((unsigned)((long)B * (K + 1) * lay.S)), block(kThreads);
+  trace_before(stream, trace_id);
+#define SV_ROWS(LT, MODE, VEC) hipLaunchKernelGGL((verify_rows<LT, MODE, VEC>), grid1, block, 0, stream, R)
+  if (bf16) {
+    if (sample) { if (vec) SV_ROWS(uint16_t, SAMPLE, true); else SV_ROWS(uint16_t, SAMPLE, false); }
+    else { if (vec) SV_ROWS(uint16_t, GREEDY, true); else SV_ROWS(uint16_t, GREEDY, false); }
+  } else {
+    if (sample) { if (vec) SV_ROWS(float, SAMPLE, true); else SV_ROWS(float, SAMPLE, false); }
+    else { if (vec) SV_ROWS(float, GREEDY, true); else SV_ROWS(float, GREEDY, false); }
+  }
+#undef SV_ROWS
+  const hipError_t err = hipGetLastError();
+  trace_after(stream, trace_id);
+  return err;
+}
+
 hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   const Layout lay = layout(L.B, L.K, L.V);
   char* ws = static_cast<char*>(L.workspace);

@@ -75,6 +75,9 @@ typedef enum {
 #define SV_DEVERR_ROW_INDEX 8     /* spec_draft_sample: a row index outside
                                      [0, n_rows): that draft gets token -1 and an
                                      all-zero q row                                    */
+#define SV_DEVERR_TREE 32         /* spec_verify_tree: a node whose parent does not
+                                     precede it or whose token is outside [0, V): the
+                                     node is treated as absent                         */
 #define SV_DEVERR_TEMPERATURE 16  /* a per-sequence temperature that is negative, NaN,
                                      infinite or too small for 1/T to be finite:
                                      that sequence is treated as greedy (T = 0)        */
@@ -180,6 +183,45 @@ SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
                                    float* out_draft_target_prob,
                                    void* workspace, size_t workspace_bytes,
                                    int32_t* device_error, void* stream);
+
+/*
+ * Verification of a draft tree per sequence.  "Project 14", section 概念:
+ * P-EAGLE's parallel speculation forms deeper draft trees (the pages give no
+ * tree shape; any shape of up to SV_MAX_K nodes is accepted).  Node 0 is the
+ * root (the last committed token); nodes 1..N have parents[b][i-1] < i and
+ * tokens[b][i-1]; target logit row n (n = 0..N) is the target's distribution
+ * after node n.
+ *   temperature = 0 (greedy): from the root, move to the lowest-index child
+ *     whose token is the lowest-index argmax of the current row; when none
+ *     matches, emit that argmax.
+ *   temperature > 0 (sampled): draft_probs row n is the distribution node n's
+ *     children were drawn from, independently.  With r = softmax(row / T) of
+ *     the current node, its children are tested in index order: child x is
+ *     accepted iff uniforms[b][i] < r(x) / q(x) (q(x) = 0: iff r(x) > 0); a
+ *     rejection replaces r by max(0, r - q) normalised (by p if that is all
+ *     zero).  An accepted child becomes the current node; when every child is
+ *     rejected, or at a leaf, the new token is the inverse-CDF draw from r
+ *     with uniforms[b][0].  With one child per node this is spec_verify_sample.
+ *   target_logits    [B][N+1][V], SV_F32 or SV_BF16.
+ *   draft_probs      [B][N+1][V] fp32 (sampled; NULL allowed when greedy).
+ *   parents, tokens  [B][N] int32 (bad nodes: SV_DEVERR_TREE, treated as absent).
+ *   uniforms         [B][N+1] fp32 in [0, 1) (sampled).
+ *   out_tokens       [B][N+1]: the accepted path's tokens, the new token, -1.
+ *   out_path         [B][N+1]: the accepted node indices, then -1.
+ *   out_num_accepted [B]: the accepted path length.
+ *   workspace        spec_verify_workspace_bytes(B, N, V) bytes, zeroed once.
+ * 0 <= N <= SV_MAX_K.  Two kernels are enqueued: the row statistics of all
+ * B*(N+1) rows, then one workgroup per sequence walks its tree (each
+ * rejection costs that workgroup one pass over the node's row).
+ */
+SV_API sv_status spec_verify_tree(const void* target_logits, int logits_dtype,
+                                  const float* draft_probs, const int32_t* parents,
+                                  const int32_t* tokens, const float* uniforms, float temperature,
+                                  int B, int N, int V,
+                                  int32_t* out_tokens, int32_t* out_path,
+                                  int32_t* out_num_accepted,
+                                  void* workspace, size_t workspace_bytes,
+                                  int32_t* device_error, void* stream);
 
 /*
  * P-EAGLE drafter batch.  Each sequence b owns the 2K rows [2Kb, 2Kb+2K).
@@ -365,6 +407,8 @@ SV_API void sv_step_graph_destroy(sv_step_graph* graph);
 #define SV_KERNEL_VERIFY_MIXED_ACCEPT 9  /* spec_verify_mixed: accept scan (its draw and
                                             locate kernels carry ids 2 and 6)            */
 #define SV_KERNEL_ACCEPT_METRICS 10      /* spec_accept_metrics                          */
+#define SV_KERNEL_TREE_ROWS 11           /* spec_verify_tree: row statistics             */
+#define SV_KERNEL_TREE_WALK 12           /* spec_verify_tree: the walk down the tree     */
 
 SV_API const char* sv_kernel_name(int kernel_id);
 SV_API sv_status sv_trace_begin(int capacity, unsigned kernel_mask); /* SV_ERR_VALUE if capacity < 1 */

@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     for n in ("spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
               "spec_draft_sample", "spec_verify_mixed", "spec_verify_workspace_bytes",
               "sv_status_string", "spec_accept_metrics", "spec_accept_metrics_words",
-              "sv_step_graph_create", "sv_step_graph_launch", "sv_step_graph_destroy"):
+              "sv_step_graph_create", "sv_step_graph_launch", "sv_step_graph_destroy",
+              "spec_verify_tree"):
         assert n in names
 
 
@@ -179,11 +180,11 @@ def test_tracer_host_paths(lib):
     assert lib.sv_trace_read(0, None, None) == ENULL
     import draft_verification_vocab_amd as sv
     assert all(lib.sv_kernel_name(i).decode() == n for n, i in sv.KERNEL_IDS.items())
-    names = [lib.sv_kernel_name(i) for i in range(11)]
+    names = [lib.sv_kernel_name(i) for i in range(13)]
     assert names == [b"verify_greedy_rows", b"verify_sample_rows", b"verify_sample_draw",
                      b"peagle_build", b"verify_greedy_accept", b"verify_sample_accept",
                      b"verify_sample_locate", b"draft_sample", b"verify_mixed_rows",
-                     b"verify_mixed_accept", b"accept_metrics"]
+                     b"verify_mixed_accept", b"accept_metrics", b"tree_rows", b"tree_walk"]
     assert lib.sv_kernel_name(17) == b"unknown"
     lib.sv_trace_end()                              # harmless when tracing is off
 
@@ -293,3 +294,30 @@ def test_step_desc_layout_matches_header():
                                               check=True).stdout.split()]
     assert out[0] == ctypes.sizeof(sv._StepDesc)
     assert out[1:] == [getattr(sv._StepDesc, f).offset for f in fields]
+
+
+def tree(lib, logits=FAKE, dtype=1, q=FAKE, par=FAKE, tok=FAKE, u=FAKE, T=0.7, B=2, N=6, V=64,
+         out=FAKE, path=FAKE, acc=FAKE, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(N, 0), max(V, 1))
+    return lib.spec_verify_tree(logits, dtype, q, par, tok, u, T, B, N, V, out, path, acc, ws, wsb,
+                                None, None)
+
+
+def test_tree_validation(lib):
+    assert tree(lib, N=64) == ESHAPE
+    assert tree(lib, N=-1) == ESHAPE
+    assert tree(lib, V=0) == ESHAPE
+    assert tree(lib, dtype=2) == EDTYPE
+    for T in (-1.0, float("nan"), float("inf"), 1e-45):
+        assert tree(lib, T=T) == EVALUE, T
+    assert tree(lib, B=0, logits=None, q=None, par=None, tok=None, u=None, out=None, path=None,
+                acc=None, ws=None, wsb=0) == OK
+    assert tree(lib, par=None) == ENULL
+    assert tree(lib, path=None) == ENULL
+    assert tree(lib, q=None) == ENULL              # sampled trees need draft probs
+    assert tree(lib, u=None) == ENULL
+    assert tree(lib, ws=None) == EWS
+    assert tree(lib, wsb=8) == EWS
+    assert tree(lib, par=FAKE + 2) == EALIGN
+    assert tree(lib, dtype=0, logits=FAKE + 2) == EALIGN
