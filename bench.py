@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the captured step graph")
+    ap.add_argument("--no-tree", action="store_true",
+                    help="skip timing draft-tree verification")
     ap.add_argument("--no-draft", action="store_true",
                     help="skip timing the drafter-output sampling kernel")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -225,6 +227,57 @@ def graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt, hid, hs
         return out
     return {"note": "verify_sample + P-EAGLE build + acceptance metrics per step",
             "full": run(B), "small": run(16)}
+
+
+def tree_bench(sv, torch, np, synth, args):
+    """Draft-tree verification on B=256 trees of 15 nodes (3 children at the
+    root, 2 below each, 1 below those), V=151936 bf16 logits, T=0.7: one call
+    is the row statistics of all B*16 rows plus the walk down every tree."""
+    spec = synth.TREE_CONFIGS["tree-bench"]
+    ti = synth.make_tree_inputs(spec, workers=args.workers)
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    z, q, par, tok, u = (up(ti.logits), up(ti.draft_probs), up(ti.parents), up(ti.tokens),
+                         up(ti.uniforms))
+    B, N, V = spec.B, spec.N, spec.V
+    ws = torch.zeros(sv.spec_verify_workspace_bytes(B, N, V), dtype=torch.uint8, device=dev)
+    outs = (torch.empty((B, N + 1), dtype=torch.int32, device=dev),
+            torch.empty((B, N + 1), dtype=torch.int32, device=dev),
+            torch.empty(B, dtype=torch.int32, device=dev))
+    rows = B * (N + 1)
+    res = {"workload": f"B={B} trees of N={N} nodes (widths 3,2,1), V={V} bf16, T={spec.temperature}"}
+    for name, T in (("greedy", 0.0), ("sample", spec.temperature)):
+        def call():
+            sv.spec_verify_tree(z, par, tok, T, draft_probs=q, uniforms=u, out_tokens=outs[0],
+                                out_path=outs[1], out_num_accepted=outs[2], workspace=ws)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / args.steps
+        sv.trace_begin(4 * args.steps)
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        per = {}
+        for k, ms in sv.trace_read():
+            per.setdefault(k, []).append(ms)
+        sv.trace_end()
+        acc = outs[2].cpu().numpy()
+        rb = rows * V * 2
+        res[name] = {"ms_per_call": sec * 1e3, "rows_per_s": rows / sec,
+                     "logit_gbs": rb / sec / 1e9, "logit_frac": rb / sec / 1e9 / HBM_PEAK_GBS,
+                     "kernels_ms": {k: float(np.mean(v)) for k, v in per.items()},
+                     "mean_accepted": float(acc.mean())}
+    return res
 
 
 def main():
@@ -453,6 +506,9 @@ def main():
             "with_probs": timed_draft(True),
             "tokens_only": timed_draft(False)}
         log("drafter sampling timed")
+    if not args.no_tree:
+        res["tree_verify"] = tree_bench(sv, torch, np, synth, args)
+        log("tree verify timed")
     if args.cpu_budget > 0:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(vi, bi, args.cpu_budget)

@@ -396,6 +396,8 @@ TREE_CONFIGS = {
                          "static", (3, 2, 1), 22),
     "tree-large": TreeSpec("tree-large", 64, 15, 151936, "bf16", 3.0, "zipf-head", 0.7, 1.0, 0.7,
                            "static", (3, 2, 1), 23),
+    "tree-bench": TreeSpec("tree-bench", 256, 15, 151936, "bf16", 3.0, "zipf-head", 0.7, 1.0, 0.7,
+                           "static", (3, 2, 1), 24),
 }
 
 
@@ -427,47 +429,65 @@ class TreeInputs:
         return self.spec.temperature
 
 
-def make_tree_inputs(spec: TreeSpec) -> TreeInputs:
-    B, N, V = spec.B, spec.N, spec.V
+def _tree_seq(spec: TreeSpec, b: int, head: Optional[np.ndarray], static: Optional[np.ndarray]):
+    N, V = spec.N, spec.V
+    rng = _seq_rng(spec.seed, b, tag=6)
+    z = rng.standard_normal((N + 1, V), dtype=np.float32)
+    z *= np.float32(spec.sigma)
+    if spec.boost == "one-token":
+        z[np.arange(N + 1), rng.integers(0, V, size=N + 1)] += np.float32(6.0)
+    elif head is not None:
+        z += head[None, :]
+    if spec.dtype == "bf16":
+        stored = f32_to_bf16_bits(z)
+        seen = bf16_bits_to_f32(stored).astype(np.float64)
+    else:
+        stored = z
+        seen = z.astype(np.float64)
+    noise = rng.standard_normal((N + 1, V), dtype=np.float32).astype(np.float64)
+    x = (seen + spec.draft_noise * noise) / spec.draft_temperature
+    x -= x.max(axis=1, keepdims=True)
+    np.exp(x, out=x)
+    x /= x.sum(axis=1, keepdims=True)
+    if spec.shape == "chain":
+        par = np.arange(N, dtype=np.int32)
+    elif static is not None:
+        par = static
+    else:
+        par = np.array([int(rng.integers(max(0, i - 3), i)) for i in range(1, N + 1)],
+                       dtype=np.int32)
+    tok = np.array([rng.choice(V, p=x[par[i]]) for i in range(N)], dtype=np.int32)
+    u = rng.random(N + 1, dtype=np.float32)
+    return b, stored, x.astype(np.float32), par, tok, u
+
+
+def _tree_worker(args):
+    spec, seqs = args
     head = _zipf_head(spec) if spec.boost == "zipf-head" else None
+    static = static_tree_parents(spec.widths) if spec.shape == "static" else None
+    return [_tree_seq(spec, b, head, static) for b in seqs]
+
+
+def make_tree_inputs(spec: TreeSpec, workers: Optional[int] = None) -> TreeInputs:
+    """Draw the tree inputs of ``spec``; large draws use a pool of freshly
+    spawned processes (the values do not depend on the number of workers)."""
+    B, N, V = spec.B, spec.N, spec.V
+    if spec.shape == "static":
+        assert static_tree_parents(spec.widths).size == N
     ldt = np.uint16 if spec.dtype == "bf16" else np.float32
     logits = np.empty((B, N + 1, V), dtype=ldt)
     q = np.empty((B, N + 1, V), dtype=np.float32)
     parents = np.empty((B, N), dtype=np.int32)
     tokens = np.empty((B, N), dtype=np.int32)
     u = np.empty((B, N + 1), dtype=np.float32)
-    static = static_tree_parents(spec.widths) if spec.shape == "static" else None
-    if static is not None:
-        assert static.size == N, (static.size, N)
-    for b in range(B):
-        rng = _seq_rng(spec.seed, b, tag=6)
-        z = rng.standard_normal((N + 1, V), dtype=np.float32)
-        z *= np.float32(spec.sigma)
-        if spec.boost == "one-token":
-            z[np.arange(N + 1), rng.integers(0, V, size=N + 1)] += np.float32(6.0)
-        elif head is not None:
-            z += head[None, :]
-        if spec.dtype == "bf16":
-            stored = f32_to_bf16_bits(z)
-            seen = bf16_bits_to_f32(stored).astype(np.float64)
-        else:
-            stored = z
-            seen = z.astype(np.float64)
-        logits[b] = stored
-        noise = rng.standard_normal((N + 1, V), dtype=np.float32).astype(np.float64)
-        x = (seen + spec.draft_noise * noise) / spec.draft_temperature
-        x -= x.max(axis=1, keepdims=True)
-        np.exp(x, out=x)
-        x /= x.sum(axis=1, keepdims=True)
-        q[b] = x.astype(np.float32)
-        if spec.shape == "chain":
-            par = np.arange(N, dtype=np.int32)
-        elif static is not None:
-            par = static
-        else:
-            par = np.array([int(rng.integers(max(0, i - 3), i)) for i in range(1, N + 1)],
-                           dtype=np.int32)
-        parents[b] = par
-        tokens[b] = [rng.choice(V, p=x[par[i]]) for i in range(N)]
-        u[b] = rng.random(N + 1, dtype=np.float32)
+    nw = _workers(B, workers)
+    if nw == 1:
+        results = [_tree_worker((spec, list(range(B))))]
+    else:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(nw) as pool:
+            results = pool.map(_tree_worker, [(spec, list(range(i, B, nw))) for i in range(nw)])
+    for res in results:
+        for b, zs, qs, ps, ts, us in res:
+            logits[b], q[b], parents[b], tokens[b], u[b] = zs, qs, ps, ts, us
     return TreeInputs(spec, logits, q, parents, tokens, u)

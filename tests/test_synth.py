@@ -128,3 +128,11 @@ def test_tree_inputs():
         assert np.allclose(ti.draft_probs.sum(axis=2), 1.0, atol=1e-5)
         again = make_tree_inputs(s)
         assert np.array_equal(again.tokens, ti.tokens) and np.array_equal(again.logits, ti.logits)
+
+
+def test_tree_workers_do_not_change_values():
+    from synth import TREE_CONFIGS, make_tree_inputs
+    s = TREE_CONFIGS["tree-tiny"]
+    a, b = make_tree_inputs(s, workers=1), make_tree_inputs(s, workers=2)
+    for f in ("logits", "draft_probs", "parents", "tokens", "uniforms"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
