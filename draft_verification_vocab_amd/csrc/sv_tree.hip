@@ -25,8 +25,11 @@
 
 namespace sv {
 
-constexpr int kTreeThreads = 256;
-constexpr int kTreeWaves = kTreeThreads / kWave;
+// Workgroup size: the sampled walk spends its time in workgroup passes over
+// a row (at 256 trees x 16 rows x 151936: 119 us with 512 threads, 181 with
+// 256; 1024 would be 106 but spills registers); the greedy walk only reads
+// partials.
+template <int MODE> constexpr int tree_threads() { return MODE == SAMPLE ? 512 : 256; }
 
 struct TreeArgs {
   TreeLaunch L;
@@ -73,13 +76,13 @@ __device__ __forceinline__ void tile_residual(const LT* zrow, const float* qrow,
 
 // Tile masses of the residual into tsum (LDS); returns the fp64 total, the
 // same on every thread.  Called in uniform control flow.
-template <typename LT, bool VEC>
-__device__ __forceinline__ double residual_tiles(const LT* zrow, const float* qrow, bool residual, float w,
-                                 long V, long nocts, int T_tiles, float c, float Mc, float inv_s,
-                                 float* tsum, double* red) {
+template <typename LT, bool VEC, int WAVES>
+__device__ __forceinline__ double residual_tiles(const LT* zrow, const float* qrow, bool residual,
+                                                 float w, long V, long nocts, int T_tiles, float c,
+                                                 float Mc, float inv_s, float* tsum, double* red) {
   const int wv = threadIdx.x / kWave, l = lane_id();
   double part = 0.0;
-  for (int t = wv; t < T_tiles; t += kTreeWaves) {
+  for (int t = wv; t < T_tiles; t += WAVES) {
     float r[kTileLoads][8];
     tile_residual<LT, VEC>(zrow, qrow, residual, t, V, nocts, c, Mc, inv_s, w, r);
     float ls = 0.f;
@@ -92,17 +95,19 @@ __device__ __forceinline__ double residual_tiles(const LT* zrow, const float* qr
   if (l == 0) red[wv] = part;
   __syncthreads();
   double tot = 0.0;
-  for (int i = 0; i < kTreeWaves; ++i) tot += red[i];
+  for (int i = 0; i < WAVES; ++i) tot += red[i];
   __syncthreads();
   return tot;
 }
 
 template <typename LT, int MODE, bool VEC>
-__global__ __launch_bounds__(kTreeThreads) void tree_walk(TreeArgs A) {
+__global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
+  constexpr int THREADS = tree_threads<MODE>();
+  constexpr int WAVES = THREADS / kWave;
   __shared__ int s_par[SV_MAX_K + 1];
   __shared__ int s_tok[SV_MAX_K + 1];
   __shared__ float tsum[kMaxTiles];
-  __shared__ double red[kTreeWaves];
+  __shared__ double red[WAVES];
 
   const TreeLaunch& L = A.L;
   const int b = blockIdx.x, N = L.N, t = threadIdx.x, S = A.S;
@@ -176,8 +181,8 @@ __global__ __launch_bounds__(kTreeThreads) void tree_walk(TreeArgs A) {
           if (tiles) break;                // tsum already holds the residual
           final_pass = true;               // w = 0 here: the tiles of p
         }
-        const double tot = residual_tiles<LT, VEC>(zrow, qrow, w > 0.0, (float)w, V, nocts,
-                                                   T_tiles, c, Mc, inv_s, tsum, red);
+        const double tot = residual_tiles<LT, VEC, WAVES>(zrow, qrow, w > 0.0, (float)w, V,
+                                                          nocts, T_tiles, c, Mc, inv_s, tsum, red);
         if (final_pass) break;
         Sr = tot;
         tiles = true;
@@ -232,11 +237,11 @@ __global__ __launch_bounds__(kTreeThreads) void tree_walk(TreeArgs A) {
     ++depth;
     cur = nxt;
   }
-  for (int j = depth + 1 + t; j <= N; j += kTreeThreads) out[j] = -1;
-  for (int j = depth + t; j <= N; j += kTreeThreads) path[j] = -1;
+  for (int j = depth + 1 + t; j <= N; j += THREADS) out[j] = -1;
+  for (int j = depth + t; j <= N; j += THREADS) path[j] = -1;
   if (t == 0) L.out_num_accepted[b] = depth;
   // the partials are consumed: clear them so the workspace ends all zero
-  for (int i = t; i < (N + 1) * S; i += kTreeThreads) Pb[i] = Partial{0.f, 0, 0.0};
+  for (int i = t; i < (N + 1) * S; i += THREADS) Pb[i] = Partial{0.f, 0, 0.0};
 }
 
 hipError_t launch_tree(const TreeLaunch& L, hipStream_t stream) {
@@ -247,7 +252,7 @@ hipError_t launch_tree(const TreeLaunch& L, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const RowPartials rp = row_partials(L.workspace, L.B, L.N, L.V);
   TreeArgs A{L, static_cast<Partial*>(rp.partials), rp.S, c};
-  const dim3 grid((unsigned)L.B), block(kTreeThreads);
+  const dim3 grid((unsigned)L.B), block(sample ? tree_threads<SAMPLE>() : tree_threads<GREEDY>());
   trace_before(stream, SV_KERNEL_TREE_WALK);
 #define SV_TREE(LT, MODE) \
   do { \
