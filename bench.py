@@ -16,6 +16,8 @@ budget.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import hashlib
 import json
 import os
@@ -29,10 +31,23 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_verify_sample_fused_b1024.json")
 
 
+@contextlib.contextmanager
+def quiet_host():
+    """A timed region without Python garbage collection: a full collection
+    over the objects torch and the input generators leave behind takes tens
+    of milliseconds, long enough to stall the enqueue of a short timed loop."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
@@ -213,11 +228,12 @@ def graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt, hid, hs
             for _ in range(args.warmup):
                 fn()
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(args.steps):
-                fn()
-            torch.cuda.synchronize()
-            out[f"{name}_ms_per_step"] = (time.perf_counter() - t0) / args.steps * 1e3
+            with quiet_host():
+                t0 = time.perf_counter()
+                for _ in range(args.steps):
+                    fn()
+                torch.cuda.synchronize()
+                out[f"{name}_ms_per_step"] = (time.perf_counter() - t0) / args.steps * 1e3
         g.close()
         summ = sv.acceptance_summary(m_g)
         out["rows_per_s_graph"] = nb * (K + 1) / (out["graph_ms_per_step"] * 1e-3)
@@ -258,11 +274,12 @@ def tree_bench(sv, torch, np, synth, args):
         for _ in range(args.warmup):
             call()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            call()
-        torch.cuda.synchronize()
-        sec = (time.perf_counter() - t0) / args.steps
+        with quiet_host():
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                call()
+            torch.cuda.synchronize()
+            sec = (time.perf_counter() - t0) / args.steps
         sv.trace_begin(4 * args.steps)
         for _ in range(args.steps):
             call()
@@ -381,12 +398,13 @@ def main():
         torch.cuda.synchronize()
         sv.trace_begin(args.steps, [dom])
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step(sample)
-            build()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        with quiet_host():
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                step(sample)
+                build()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
         per = {dom: [ms for _, ms in sv.trace_read()]}
         sv.trace_begin(8 * args.steps)
         for _ in range(args.steps):
