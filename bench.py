@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the captured step graph")
+    ap.add_argument("--no-round", action="store_true",
+                    help="skip timing the decode round on the two q interfaces")
     ap.add_argument("--no-tree", action="store_true",
                     help="skip timing draft-tree verification")
     ap.add_argument("--no-draft", action="store_true",
@@ -243,6 +245,61 @@ def graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt, hid, hs
         return out
     return {"note": "verify_sample + P-EAGLE build + acceptance metrics per step",
             "full": run(B), "small": run(16)}
+
+
+def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, out_t, acc_t,
+                pd_t, ws, bouts):
+    """One decode round of the path on the two ways of handing the drafter's
+    distributions to the verify: drafter sampling that writes dense fp32 q +
+    spec_verify_sample, vs drafter sampling that writes only tokens and row
+    descriptors + spec_verify_sample_lq; both followed by the P-EAGLE build.
+    Stand-in drafter rows: the first K logit rows of the sequence B/2 places
+    away (same recipe, distinct memory), gathered through a row index."""
+    dev = z.device
+    zr = z.view(B * (K + 1), V)
+    seq = (torch.arange(B, dtype=torch.int32, device=dev) + B // 2) % B
+    rows = (seq[:, None] * (K + 1) + torch.arange(K, dtype=torch.int32, device=dev)[None, :]).contiguous()
+    ud = torch.from_numpy(np.random.default_rng(8).random((B, K), dtype=np.float32)).to(dev)
+    tok = torch.empty((B, K), dtype=torch.int32, device=dev)
+    q = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    desc = torch.empty((B, K, 4), dtype=torch.int32, device=dev)
+    T = vi.temperature
+
+    def build():
+        sv.peagle_build_draft_batch(out_t, acc_t, tok, L, bt, bi.spec.block_size, hid, hs,
+                                    bi.mask_token_id, outputs=bouts)
+
+    def dense():
+        sv.spec_draft_sample(zr, K, T, uniforms=ud, row_index=rows, out_draft_tokens=tok,
+                             out_draft_probs=q)
+        sv.spec_verify_sample(z, q, tok, u, T, out_tokens=out_t, out_num_accepted=acc_t,
+                              out_draft_target_prob=pd_t, workspace=ws)
+        build()
+
+    def lq():
+        sv.spec_draft_sample(zr, K, T, uniforms=ud, row_index=rows, out_draft_tokens=tok,
+                             want_draft_probs=False, out_row_desc=desc)
+        sv.spec_verify_sample_lq(z, zr, desc, tok, u, T, drafter_rows=rows, out_tokens=out_t,
+                                 out_num_accepted=acc_t, out_draft_target_prob=pd_t, workspace=ws)
+        build()
+
+    res = {"workload": f"B={B} K={K} V={V} bf16: drafter sampling + sampled verify + P-EAGLE build"}
+    outs = {}
+    for name, fn in (("dense_q", dense), ("logit_q", lq)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        with quiet_host():
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            res[f"{name}_ms_per_round"] = (time.perf_counter() - t0) / args.steps * 1e3
+        outs[name] = (out_t.clone(), acc_t.clone())
+    res["speedup"] = res["dense_q_ms_per_round"] / res["logit_q_ms_per_round"]
+    res["identical_outputs"] = bool(torch.equal(outs["dense_q"][0], outs["logit_q"][0]) and
+                                    torch.equal(outs["dense_q"][1], outs["logit_q"][1]))
+    return res
 
 
 def tree_bench(sv, torch, np, synth, args):
@@ -524,6 +581,10 @@ def main():
             "with_probs": timed_draft(True),
             "tokens_only": timed_draft(False)}
         log("drafter sampling timed")
+    if not args.no_round:
+        res["decode_round"] = round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt,
+                                          hid, hs, out_t, acc_t, pd_t, ws, bouts)
+        log("decode round timed")
     if not args.no_tree:
         res["tree_verify"] = tree_bench(sv, torch, np, synth, args)
         log("tree verify timed")

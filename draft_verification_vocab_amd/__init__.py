@@ -48,7 +48,9 @@ _SIGS = {
     "spec_verify_mixed": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p,
                                ctypes.c_size_t, _p, _p]),
     "spec_draft_sample": (_i, [_p, _i, ctypes.c_int64, _p, _p, ctypes.c_float, _p, _i, _i, _i,
-                               _p, _p, _p, _p]),
+                               _p, _p, _p, _p, _p]),
+    "spec_verify_sample_lq": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, ctypes.c_float,
+                                   _i, _i, _i, _p, _p, _p, _p, ctypes.c_size_t, _p, _p]),
     "spec_verify_tree": (_i, [_p, _i, _p, _p, _p, _p, ctypes.c_float, _i, _i, _i, _p, _p, _p, _p,
                               ctypes.c_size_t, _p, _p]),
     "spec_accept_metrics_words": (ctypes.c_size_t, [_i]),
@@ -375,12 +377,16 @@ def spec_draft_sample(drafter_logits: torch.Tensor, K: int, temperature: float,
                       out_draft_tokens: Optional[torch.Tensor] = None,
                       out_draft_probs: Optional[torch.Tensor] = None,
                       want_draft_probs: bool = True,
-                      device_error: Optional[torch.Tensor] = None):
+                      device_error: Optional[torch.Tensor] = None,
+                      out_row_desc: Optional[torch.Tensor] = None,
+                      want_row_desc: bool = False):
     """Sample the drafter's prediction rows; see spec_draft_sample in
     include/spec_verify.h.  drafter_logits is [n_rows, V]; B is taken from
     row_index ([B, K]) when given, else n_rows // K.
 
-    Returns (draft_tokens [B, K] int32, draft_probs [B, K, V] fp32 or None).
+    Returns (draft_tokens [B, K] int32, draft_probs [B, K, V] fp32 or None),
+    plus the row descriptors ([B, K, 4] int32 holding sv_draft_row) as a third
+    element when want_row_desc or out_row_desc is given.
     """
     lib = require_library()
     if drafter_logits.dim() != 2:
@@ -412,12 +418,74 @@ def spec_draft_sample(drafter_logits: torch.Tensor, K: int, temperature: float,
         _dev(out_draft_probs, "out_draft_probs", torch.float32, (B, K, V), dev)
     if device_error is not None:
         _dev(device_error, "device_error", torch.int32, (1,), dev)
+    with_desc = want_row_desc or out_row_desc is not None
+    if out_row_desc is None and want_row_desc:
+        out_row_desc = torch.empty((B, K, 4), dtype=torch.int32, device=dev)
+    if out_row_desc is not None:
+        _dev(out_row_desc, "out_row_desc", torch.int32, (B, K, 4), dev)
     st = lib.spec_draft_sample(_ptr(drafter_logits), _DTYPES[drafter_logits.dtype], n_rows,
                                _ptr(row_index), _ptr(uniforms), float(temperature),
                                _ptr(temperatures), B, K, V, _ptr(out_draft_tokens),
-                               _ptr(out_draft_probs), _ptr(device_error), _stream(dev))
+                               _ptr(out_draft_probs), _ptr(out_row_desc), _ptr(device_error),
+                               _stream(dev))
     _check(st, "spec_draft_sample")
+    if with_desc:
+        return out_draft_tokens, out_draft_probs, out_row_desc
     return out_draft_tokens, out_draft_probs
+
+
+def spec_verify_sample_lq(target_logits: torch.Tensor, drafter_logits: torch.Tensor,
+                          drafter_desc: torch.Tensor, draft_tokens: torch.Tensor,
+                          uniforms: torch.Tensor, temperature: float,
+                          drafter_rows: Optional[torch.Tensor] = None,
+                          out_tokens: Optional[torch.Tensor] = None,
+                          out_num_accepted: Optional[torch.Tensor] = None,
+                          out_draft_target_prob: Optional[torch.Tensor] = None,
+                          want_draft_target_prob: bool = False,
+                          workspace: Optional[torch.Tensor] = None,
+                          device_error: Optional[torch.Tensor] = None):
+    """Sampled verify with q recomputed from the drafter logits and the row
+    descriptors of spec_draft_sample; see spec_verify_sample_lq in
+    include/spec_verify.h.  Returns (out_tokens, num_accepted, draft_target_prob
+    or None)."""
+    lib = require_library()
+    if target_logits.dim() != 3 or drafter_logits.dim() != 2:
+        raise ValueError("target_logits must be [B, K+1, V] and drafter_logits [n_rows, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    _dev(target_logits, "target_logits")
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("target_logits must be float32 or bfloat16")
+    _dev(drafter_logits, "drafter_logits", target_logits.dtype, (drafter_logits.shape[0], V), dev)
+    _dev(drafter_desc, "drafter_desc", torch.int32, (B, K, 4), dev)
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _dev(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    if drafter_rows is not None:
+        _dev(drafter_rows, "drafter_rows", torch.int32, (B, K), dev)
+    out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if out_tokens is None \
+        else _dev(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+    out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev) if out_num_accepted is None \
+        else _dev(out_num_accepted, "out_num_accepted", torch.int32, (B,), dev)
+    if out_draft_target_prob is None and want_draft_target_prob:
+        out_draft_target_prob = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if out_draft_target_prob is not None:
+        _dev(out_draft_target_prob, "out_draft_target_prob", torch.float32, (B, K), dev)
+    need = spec_verify_workspace_bytes(B, K, V)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    _dev(workspace, "workspace", device=dev)
+    if device_error is not None:
+        _dev(device_error, "device_error", torch.int32, (1,), dev)
+    st = lib.spec_verify_sample_lq(_ptr(target_logits), _DTYPES[target_logits.dtype],
+                                   _ptr(drafter_logits), drafter_logits.shape[0],
+                                   _ptr(drafter_rows), _ptr(drafter_desc), _ptr(draft_tokens),
+                                   _ptr(uniforms), float(temperature), B, K, V, _ptr(out_tokens),
+                                   _ptr(out_num_accepted), _ptr(out_draft_target_prob),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _ptr(device_error), _stream(dev))
+    _check(st, "spec_verify_sample_lq")
+    return out_tokens, out_num_accepted, out_draft_target_prob
 
 
 # ---------------------------------------------------------------- draft trees

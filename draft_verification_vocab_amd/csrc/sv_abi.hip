@@ -178,6 +178,10 @@ static sv_status verify_common(const void* logits, int dtype, const float* draft
   L.sample = sample != 0;
   L.mixed = sample == 2;
   L.temperatures = sample == 2 ? temperatures : nullptr;
+  L.dlogits = nullptr;
+  L.d_rows = 0;
+  L.drows = nullptr;
+  L.ddesc = nullptr;
   L.vec = (V % 8 == 0) && aligned(logits, 16) && (!sample || !draft_probs || aligned(draft_probs, 16));
   L.out_tokens = out_tokens;
   L.out_num_accepted = out_num_accepted;
@@ -206,6 +210,65 @@ SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
   return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, uniforms,
                        temperature, nullptr, 1, B, K, V, out_tokens, out_num_accepted,
                        out_draft_target_prob, workspace, workspace_bytes, device_error, stream);
+}
+
+SV_API sv_status spec_verify_sample_lq(const void* target_logits, int logits_dtype,
+                                       const void* drafter_logits, int64_t n_drafter_rows,
+                                       const int32_t* drafter_rows,
+                                       const sv_draft_row* drafter_desc,
+                                       const int32_t* draft_tokens, const float* uniforms,
+                                       float temperature, int B, int K, int V,
+                                       int32_t* out_tokens, int32_t* out_num_accepted,
+                                       float* out_draft_target_prob, void* workspace,
+                                       size_t workspace_bytes, int32_t* device_error,
+                                       void* stream) {
+  sv_status st = check_verify_shape(B, K, V);
+  if (st != SV_OK) return st;
+  if (n_drafter_rows < 0 || n_drafter_rows > 0x7fffffffL) return SV_ERR_SHAPE;
+  if (!drafter_rows && n_drafter_rows < (int64_t)B * K) return SV_ERR_SHAPE;
+  if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (!(temperature > 0.0f && isfinite(temperature) &&
+        isfinite((float)(1.4426950408889634 / (double)temperature))))
+    return SV_ERR_VALUE;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !out_tokens || !out_num_accepted || !uniforms) return SV_ERR_NULL;
+  if (K > 0 && (!draft_tokens || !drafter_logits || !drafter_desc)) return SV_ERR_NULL;
+  if (!workspace || workspace_bytes < sv::verify_workspace_bytes(B, K, V)) return SV_ERR_WORKSPACE;
+  const size_t esz = logits_dtype == SV_BF16 ? 2 : 4;
+  if (!aligned(target_logits, esz) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+      !aligned(uniforms, 4) || !aligned(workspace, 16) ||
+      (draft_tokens && !aligned(draft_tokens, 4)) ||
+      (drafter_logits && !aligned(drafter_logits, esz)) ||
+      (drafter_rows && !aligned(drafter_rows, 4)) ||
+      (drafter_desc && !aligned(drafter_desc, 16)) ||
+      (out_draft_target_prob && !aligned(out_draft_target_prob, 4)) ||
+      (device_error && !aligned(device_error, 4)))
+    return SV_ERR_ALIGN;
+  if ((long)B * (K + 1) * sv::verify_splits(B, K, V) > 0x7fffffffL) return SV_ERR_SHAPE;
+  sv::VerifyLaunch L;
+  L.logits = target_logits;
+  L.draft_probs = nullptr;
+  L.draft_tokens = draft_tokens;
+  L.uniforms = uniforms;
+  L.temperature = temperature;
+  L.B = B; L.K = K; L.V = V;
+  L.bf16 = logits_dtype == SV_BF16;
+  L.sample = 1;
+  L.mixed = 0;
+  L.temperatures = nullptr;
+  // a valid pointer for K = 0 (nothing is read from it then)
+  L.dlogits = drafter_logits ? drafter_logits : target_logits;
+  L.d_rows = (long)n_drafter_rows;
+  L.drows = drafter_rows;
+  L.ddesc = drafter_desc;
+  L.vec = (V % 8 == 0) && aligned(target_logits, 16) &&
+          (!drafter_logits || aligned(drafter_logits, 16));
+  L.out_tokens = out_tokens;
+  L.out_num_accepted = out_num_accepted;
+  L.out_p_draft = out_draft_target_prob;
+  L.workspace = workspace;
+  L.device_error = device_error;
+  return sv::launch_verify(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
@@ -276,7 +339,8 @@ SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype,
                                    const int32_t* row_index, const float* uniforms,
                                    float temperature, const float* temperatures, int B, int K,
                                    int V, int32_t* out_draft_tokens, float* out_draft_probs,
-                                   int32_t* device_error, void* stream) {
+                                   sv_draft_row* out_row_desc, int32_t* device_error,
+                                   void* stream) {
   if (B < 0 || B > kMaxB || K < 1 || K > SV_MAX_K || V < 1 || V > SV_MAX_V || n_rows < 0 ||
       n_rows > 0x7fffffffL)
     return SV_ERR_SHAPE;
@@ -293,7 +357,7 @@ SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype,
       (row_index && !aligned(row_index, 4)) || (uniforms && !aligned(uniforms, 4)) ||
       (temperatures && !aligned(temperatures, 4)) ||
       (out_draft_probs && !aligned(out_draft_probs, 4)) ||
-      (device_error && !aligned(device_error, 4)))
+      (out_row_desc && !aligned(out_row_desc, 16)) || (device_error && !aligned(device_error, 4)))
     return SV_ERR_ALIGN;
   sv::DraftLaunch L;
   L.logits = drafter_logits;
@@ -308,6 +372,7 @@ SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype,
           (!out_draft_probs || aligned(out_draft_probs, 16));
   L.out_tokens = out_draft_tokens;
   L.out_probs = out_draft_probs;
+  L.out_desc = out_row_desc;
   L.device_error = device_error;
   return sv::launch_draft(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

@@ -42,6 +42,7 @@ struct DraftArgs {
   int B, K, V;
   int32_t* out_tokens;         // [B*K]
   float* out_probs;            // [B*K][V] or null
+  sv_draft_row* out_desc;      // [B*K] or null
   int32_t* device_error;
 };
 
@@ -199,6 +200,7 @@ __global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(Draft
     if (t == 0) {
       flag_error(A.device_error, SV_DEVERR_ROW_INDEX);
       A.out_tokens[r] = -1;
+      if (A.out_desc) A.out_desc[r] = sv_draft_row{0.f, 0.f, 0.f, -1};   // q = 0
     }
     if constexpr (WQ) store_one_hot<VEC, THREADS>(qrow, V, nocts, -1);
     return;
@@ -218,7 +220,10 @@ __global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(Draft
     if (t == 0) stats = P;
     __syncthreads();
     const int g = stats.g == INT32_MAX ? 0 : stats.g;
-    if (t == 0) A.out_tokens[r] = g;
+    if (t == 0) {
+      A.out_tokens[r] = g;
+      if (A.out_desc) A.out_desc[r] = sv_draft_row{0.f, 0.f, 0.f, g};      // q = one-hot(g)
+    }
     if constexpr (WQ) store_one_hot<VEC, THREADS>(qrow, V, nocts, g);
     return;
   }
@@ -250,6 +255,7 @@ __global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(Draft
   // folds that rounding back in
   const float Mc = M * c;
   const float inv_s = (float)(exp2((double)Mc - (double)M * (double)c) / S);
+  if (t == 0 && A.out_desc) A.out_desc[r] = sv_draft_row{c, Mc, inv_s, -1};
 
   // sweep 2 (only when q is requested): write q
   if constexpr (WQ) {
@@ -315,6 +321,7 @@ hipError_t launch_draft(const DraftLaunch& L, hipStream_t stream) {
   A.B = L.B; A.K = L.K; A.V = L.V;
   A.out_tokens = L.out_tokens;
   A.out_probs = L.out_probs;
+  A.out_desc = L.out_desc;
   A.device_error = L.device_error;
   const dim3 grid((unsigned)((long)L.B * L.K));
   const bool wq = L.out_probs != nullptr;

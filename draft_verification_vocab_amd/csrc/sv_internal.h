@@ -20,6 +20,11 @@ struct VerifyLaunch {
   int sample;                    // rejection sampling (else greedy)
   int mixed;                     // per-sequence temperatures (overrides sample)
   const float* temperatures;     // mixed: [B]
+  // q from the drafter logits (sampling only): dlogits != NULL
+  const void* dlogits;           // [d_rows][V], same dtype as logits
+  long d_rows;
+  const int32_t* drows;          // [B*K] or NULL (row b*K + k)
+  const sv_draft_row* ddesc;     // [B*K]
   int vec;                       // 16-byte vector loads are legal for every row
   int32_t* out_tokens;
   int32_t* out_num_accepted;
@@ -61,6 +66,7 @@ struct DraftLaunch {
   int vec;                       // 16-byte vector loads / stores are legal for every row
   int32_t* out_tokens;
   float* out_probs;              // may be NULL
+  sv_draft_row* out_desc;        // may be NULL
   int32_t* device_error;         // may be NULL
 };
 

@@ -205,6 +205,13 @@ __device__ __forceinline__ void mass_octet(const float z[8], const float q[8], b
   }
 }
 
+// q(x) of a drafted row from its drafter logit z(x) and its descriptor: the
+// fp32 operations the drafter kernel uses to write q.
+__device__ __forceinline__ float drafter_q(const sv_draft_row& d, float z, long e) {
+  return d.c > 0.f ? __builtin_amdgcn_exp2f(fmaf(z, d.c, -d.mc)) * d.inv_s
+                   : (e == (long)d.argmax ? 1.f : 0.f);
+}
+
 // The token drawn inside one CDF tile.  Lane l holds the masses r[sl][0..7]
 // of octet (tile * kTileLoads + sl) * 64 + l; tpre is the running total before
 // the tile and target = u * S.  Returns (on every lane) the first element

@@ -102,6 +102,10 @@ struct RowsArgs {
 struct ScanArgs {          // what an accept scan reads and writes
   const void* logits;
   const float* temperatures;  // mixed: [B]
+  const void* dlogits;        // q from the drafter logits: [d_rows][V]
+  long d_rows;
+  const int32_t* drows;       // [B*K] or null (row b*K + k)
+  const sv_draft_row* ddesc;  // [B*K]
   const float* draft_probs;
   const int32_t* draft_tokens;
   const float* uniforms;
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void verify_rows(RowsArgs A) {
 // rejection with a ballot.  With `write` it writes the accepted prefix, the
 // -1 padding, num_accepted and p_k(d_k); the new token is written by the
 // caller (greedy: g_a; sampling: the draw).
-template <typename LT, int MODE>
+template <typename LT, int MODE, bool QL = false>
 __device__ __forceinline__ ScanResult accept_scan(const ScanArgs& A, int b, bool write, float c) {
   const int K = A.K, S = A.S;
   const long V = A.V;
@@ -194,7 +198,20 @@ __device__ __forceinline__ ScanResult accept_scan(const ScanArgs& A, int b, bool
         const LT* zr = static_cast<const LT*>(A.logits) + ((long)b * (K + 1) + k) * V;
         const float zx = logit_at(zr, d);
         px = exp2(((double)zx - (double)M) * (double)c) / s_k;
-        const double qx = (double)A.draft_probs[((long)b * K + k) * V + d];
+        double qx;
+        if constexpr (QL) {
+          // q_k(x) recomputed from drafter row r with the drafter's operations
+          const long j = (long)b * K + k;
+          const long r = A.drows ? (long)A.drows[j] : j;
+          if (r >= 0 && r < A.d_rows) {
+            qx = (double)drafter_q(A.ddesc[j], logit_at(static_cast<const LT*>(A.dlogits) + r * V, d), d);
+          } else {
+            qx = 0.0;
+            if (write) flag_error(A.device_error, SV_DEVERR_ROW_INDEX);
+          }
+        } else {
+          qx = (double)A.draft_probs[((long)b * K + k) * V + d];
+        }
         const double ratio = qx > 0.0 ? px / qx : (px > 0.0 ? INFINITY : 0.0);
         rej = !((double)A.uniforms[(long)b * (K + 1) + k] < ratio);
       } else {
@@ -221,7 +238,7 @@ __device__ __forceinline__ ScanResult accept_scan(const ScanArgs& A, int b, bool
 
 // One wave per sequence runs the accept scan.  Greedy: writes g_a as the new
 // token.  Sampling: hands (a, M_a, s_a) to verify_draw.
-template <typename LT, int MODE>
+template <typename LT, int MODE, bool QL>
 __global__ __launch_bounds__(kThreads) void verify_accept(ScanArgs A) {
   const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
   if (b >= A.B) return;
@@ -231,13 +248,13 @@ __global__ __launch_bounds__(kThreads) void verify_accept(ScanArgs A) {
     const float c = seq_scale(A.temperatures[b], bad);
     if (bad && l == 0) flag_error(A.device_error, SV_DEVERR_TEMPERATURE);
     const ScanResult r = c == 0.f ? accept_scan<LT, GREEDY>(A, b, true, 1.f)
-                                  : accept_scan<LT, SAMPLE>(A, b, true, c);
+                                  : accept_scan<LT, SAMPLE, QL>(A, b, true, c);
     if (l == 0) {
       if (c == 0.f) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
       A.info[b] = r;                      // c = 0 tells the draw to skip it
     }
   } else {
-    const ScanResult r = accept_scan<LT, MODE>(A, b, true, A.c);
+    const ScanResult r = accept_scan<LT, MODE, QL>(A, b, true, A.c);
     if (l == 0) {
       if constexpr (MODE == GREEDY) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
       else A.info[b] = r;
@@ -249,59 +266,42 @@ __global__ __launch_bounds__(kThreads) void verify_accept(ScanArgs A) {
 }
 
 // ----------------------------------------------------------------------------
-// Mass of octet o of the draw row (z: logits row, q: drafter row or null).
-// With VEC the address is clamped into the row and the values past V are
-// masked, so the loads carry no branch.
-template <typename LT, bool VEC>
-__device__ __forceinline__ void octet_mass(const LT* zrow, const float* qrow, long o, long V,
-                                           long nocts, bool residual, float c, float Mc,
-                                           float inv_s, float r[8]) {
-  float z[8], q[8];
-  if constexpr (VEC) {
-    const bool in = o < nocts;
-    const long oc = in ? o : nocts - 1;
-    Raw<LT> rz;
-    raw_load<true>(zrow, oc, rz);      // non-temporal: measured faster for the logits
-                                        // (not for the drafter rows)
-    unpack(rz, z);
-    if (residual) {
-      Raw<float> rq;
-      raw_load<false>(qrow, oc, rq);
-      unpack(rq, q);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = 0.f;
-    }
-    if (!in) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) { z[j] = -INFINITY; q[j] = 0.f; }
-    }
-  } else {
-    load_octet<false>(zrow, o, V, false, -INFINITY, z);
-    if (residual) load_octet<false>(qrow, o, V, false, 0.f, q);
-    else
-#pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = 0.f;
-  }
-  mass_octet(z, q, residual, c, Mc, inv_s, r);
-}
-
 // Everything the draw needs about sequence b's row a.
 template <typename LT>
 struct DrawRow {
   const LT* zrow;
-  const float* qrow;       // null for the bonus draw (a = K)
+  const float* qrow;       // dense q row a (null for the bonus draw or with QL)
+  const LT* dzrow;         // QL: drafter logit row of draft a (null: q = 0)
+  sv_draft_row desc;       // QL: its descriptor
+  bool residual;           // a < K: draw from max(0, p - q); else the bonus from p
   float c, Mc32, inv_s;
   int a;
 };
 
-template <typename LT>
+template <typename LT, bool QL>
 __device__ __forceinline__ DrawRow<LT> draw_row(const DrawArgs& A, int b) {
   const ScanResult scan = A.sc.info[b];       // written by verify_accept
+  const int K = A.sc.K;
+  const long V = A.sc.V;
   DrawRow<LT> r;
   r.a = scan.a;
-  r.zrow = static_cast<const LT*>(A.sc.logits) + ((long)b * (A.sc.K + 1) + scan.a) * A.sc.V;
-  r.qrow = scan.a < A.sc.K ? A.sc.draft_probs + ((long)b * A.sc.K + scan.a) * A.sc.V : nullptr;
+  r.zrow = static_cast<const LT*>(A.sc.logits) + ((long)b * (K + 1) + scan.a) * V;
+  r.residual = scan.a < K;
+  r.qrow = nullptr;
+  r.dzrow = nullptr;
+  r.desc = sv_draft_row{0.f, 0.f, 0.f, -1};
+  if (r.residual) {
+    const long j = (long)b * K + scan.a;
+    if constexpr (QL) {
+      const long row = A.sc.drows ? (long)A.sc.drows[j] : j;
+      if (row >= 0 && row < A.sc.d_rows) {
+        r.dzrow = static_cast<const LT*>(A.sc.dlogits) + row * V;
+        r.desc = A.sc.ddesc[j];
+      }
+    } else {
+      r.qrow = A.sc.draft_probs + j * V;
+    }
+  }
   r.c = scan.c;                               // 0: a greedy sequence of a mixed batch
   // p = 2^(z*c - M*c) / s.  Mc32 is M*c rounded to fp32; the rounding is
   // folded into the scale so that p keeps the fp64 reference exactly.
@@ -311,8 +311,66 @@ __device__ __forceinline__ DrawRow<LT> draw_row(const DrawArgs& A, int b) {
   return r;
 }
 
+// Mass of octet o of the draw row: max(0, p - q) (residual) or p.  q comes
+// from the dense q row, or (QL) from the drafter logit row and descriptor.
+// With VEC the address is clamped into the row and the values past V are
+// masked, so the loads carry no branch.
+template <typename LT, bool VEC, bool QL>
+__device__ __forceinline__ void octet_mass(const DrawRow<LT>& R, long o, long V, long nocts,
+                                           bool residual, float r[8]) {
+  float z[8], q[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) q[j] = 0.f;
+  if constexpr (VEC) {
+    const bool in = o < nocts;
+    const long oc = in ? o : nocts - 1;
+    Raw<LT> rz;
+    raw_load<true>(R.zrow, oc, rz);    // non-temporal: measured faster for the logits
+                                        // (not for the drafter rows)
+    unpack(rz, z);
+    if (residual) {
+      if constexpr (QL) {
+        if (R.dzrow) {
+          Raw<LT> rd;
+          raw_load<false>(R.dzrow, oc, rd);
+          float dz[8];
+          unpack(rd, dz);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) q[j] = drafter_q(R.desc, dz[j], oc * 8 + j);
+        }
+      } else {
+        Raw<float> rq;
+        raw_load<false>(R.qrow, oc, rq);
+        unpack(rq, q);
+      }
+    }
+    if (!in) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { z[j] = -INFINITY; q[j] = 0.f; }
+    }
+  } else {
+    load_octet<false>(R.zrow, o, V, false, -INFINITY, z);
+    if (residual) {
+      if constexpr (QL) {
+        if (R.dzrow) {
+          float dz[8];
+          load_octet<false>(R.dzrow, o, V, false, 0.f, dz);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const long e = o * 8 + j;
+            q[j] = e < V ? drafter_q(R.desc, dz[j], e) : 0.f;
+          }
+        }
+      } else {
+        load_octet<false>(R.qrow, o, V, false, 0.f, q);
+      }
+    }
+  }
+  mass_octet(z, q, residual, R.c, R.Mc32, R.inv_s, r);
+}
+
 // Mass of tile t seen by one lane: the sum of its kTileLoads octets.
-template <typename LT, bool VEC>
+template <typename LT, bool VEC, bool QL>
 __device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool residual, int t, long V,
                                                 long nocts) {
   float ls = 0.f;
@@ -320,7 +378,7 @@ __device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool resid
   for (int sl = 0; sl < kTileLoads; ++sl) {
     float r[8];
     const long o = ((long)t * kTileLoads + sl) * kWave + lane_id();
-    octet_mass<LT, VEC>(R.zrow, R.qrow, o, V, nocts, residual, R.c, R.Mc32, R.inv_s, r);
+    octet_mass<LT, VEC, QL>(R, o, V, nocts, residual, r);
     ls += tree_sum8(r);
   }
   return ls;
@@ -330,23 +388,24 @@ __device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool resid
 // and the chunk total (tile order).  A tile is kTileLoads consecutive
 // 512-element wave loads; each lane sums its octets of the tile before one
 // wave reduction.
-template <typename LT, bool VEC>
+template <typename LT, bool VEC, bool QL>
 __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
   __shared__ float tsum_l[kMaxTiles];
   const int C = A.C, T = A.T;
   const int b = blockIdx.x / C, cidx = blockIdx.x % C;
   const long V = A.sc.V;
   const long nocts = (V + 7) / 8;
-  const DrawRow<LT> R = draw_row<LT>(A, b);
+  const DrawRow<LT> R = draw_row<LT, QL>(A, b);
   if (R.c == 0.f) return;                     // greedy: its token is already written
-  const bool residual = R.qrow != nullptr;
+  const bool residual = R.residual;
   float* tsum_g = A.tile_sums + (long)b * T;
   const int t_lo = (int)((long)cidx * T / C), t_hi = (int)((long)(cidx + 1) * T / C);
   const int w = threadIdx.x / kWave, l = lane_id();
   for (int t0 = t_lo + w * kTileUnroll; t0 < t_hi; t0 += kWaves * kTileUnroll) {
     float ls[kTileUnroll];
 #pragma unroll
-    for (int j = 0; j < kTileUnroll; ++j) ls[j] = lane_tile_mass<LT, VEC>(R, residual, t0 + j, V, nocts);
+    for (int j = 0; j < kTileUnroll; ++j)
+      ls[j] = lane_tile_mass<LT, VEC, QL>(R, residual, t0 + j, V, nocts);
 #pragma unroll
     for (int j = 0; j < kTileUnroll; ++j) {
       const float ts = wave_sum_f(ls[j]);
@@ -365,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
 }
 
 // verify_locate: one wave per sequence draws the token from the tile masses.
-template <typename LT, bool VEC>
+template <typename LT, bool VEC, bool QL>
 __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
   const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
   if (b >= A.sc.B) return;
@@ -373,12 +432,12 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
   const long V = A.sc.V;
   const long nocts = (V + 7) / 8;
   const int l = lane_id();
-  const DrawRow<LT> R = draw_row<LT>(A, b);
+  const DrawRow<LT> R = draw_row<LT, QL>(A, b);
   if (R.c == 0.f) {                           // greedy: nothing to draw
     if (l == 0) A.sc.info[b] = ScanResult{0, 0, 0.f, 0.f, 0.0};
     return;
   }
-  bool residual = R.qrow != nullptr;
+  bool residual = R.residual;
   float* tsum_g = A.tile_sums + (long)b * T;
   double* csum_g = A.chunk_sums + (long)b * C;
   const int per = (C + kWave - 1) / kWave;
@@ -398,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
       const int clo = (int)((long)ci * T / C), chi = (int)((long)(ci + 1) * T / C);
       double cs = 0.0;
       for (int t = clo; t < chi; ++t) {
-        const float ts = wave_sum_f(lane_tile_mass<LT, VEC>(R, false, t, V, nocts));
+        const float ts = wave_sum_f(lane_tile_mass<LT, VEC, QL>(R, false, t, V, nocts));
         if (l == 0) st_coherent(&tsum_g[t], ts);
         cs += (double)ts;
       }
@@ -473,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
 #pragma unroll
   for (int sl = 0; sl < kTileLoads; ++sl) {
     const long o = ((long)tile * kTileLoads + sl) * kWave + l;
-    octet_mass<LT, VEC>(R.zrow, R.qrow, o, V, nocts, residual, R.c, R.Mc32, R.inv_s, r[sl]);
+    octet_mass<LT, VEC, QL>(R, o, V, nocts, residual, r[sl]);
   }
   const int pick = pick_in_tile(r, tile, tpre, target, fallback);
   if (l == 0) A.sc.out_tokens[(long)b * (K + 1) + R.a] = pick;
@@ -549,9 +608,14 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   trace_after(stream, rows_id);
   if (err != hipSuccess) return err;
 
+  const bool ql = L.dlogits != nullptr;       // q from the drafter logits (sampling)
   ScanArgs sc;
   sc.logits = L.logits;
   sc.temperatures = L.temperatures;
+  sc.dlogits = L.dlogits;
+  sc.d_rows = L.d_rows;
+  sc.drows = L.drows;
+  sc.ddesc = L.ddesc;
   sc.draft_probs = L.draft_probs;
   sc.draft_tokens = L.draft_tokens;
   sc.uniforms = L.uniforms;
@@ -566,9 +630,15 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   sc.info = reinterpret_cast<ScanResult*>(ws + lay.info);
   const dim3 grid_acc((unsigned)((L.B + kWaves - 1) / kWaves));
   trace_before(stream, accept_id);
-#define SV_ACCEPT(LT, MODE) hipLaunchKernelGGL((verify_accept<LT, MODE>), grid_acc, block, 0, stream, sc)
-  if (L.bf16) SV_BY_MODE(SV_ACCEPT, uint16_t);
-  else SV_BY_MODE(SV_ACCEPT, float);
+#define SV_ACCEPT(LT, MODE) hipLaunchKernelGGL((verify_accept<LT, MODE, false>), grid_acc, block, 0, stream, sc)
+  if (ql) {
+    if (L.bf16) hipLaunchKernelGGL((verify_accept<uint16_t, SAMPLE, true>), grid_acc, block, 0, stream, sc);
+    else hipLaunchKernelGGL((verify_accept<float, SAMPLE, true>), grid_acc, block, 0, stream, sc);
+  } else if (L.bf16) {
+    SV_BY_MODE(SV_ACCEPT, uint16_t);
+  } else {
+    SV_BY_MODE(SV_ACCEPT, float);
+  }
 #undef SV_ACCEPT
 #undef SV_BY_MODE
 #undef SV_ROWS
@@ -582,25 +652,28 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   D.chunk_sums = reinterpret_cast<double*>(ws + lay.chunk);
   D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
   const dim3 grid3((unsigned)((long)L.B * lay.C));
+#define SV_DRAW_KERNELS(KERNEL, GRID) \
+  do { \
+    if (L.bf16) { \
+      if (L.vec) { if (ql) hipLaunchKernelGGL((KERNEL<uint16_t, true, true>), GRID, block, 0, stream, D); \
+                   else hipLaunchKernelGGL((KERNEL<uint16_t, true, false>), GRID, block, 0, stream, D); } \
+      else { if (ql) hipLaunchKernelGGL((KERNEL<uint16_t, false, true>), GRID, block, 0, stream, D); \
+             else hipLaunchKernelGGL((KERNEL<uint16_t, false, false>), GRID, block, 0, stream, D); } \
+    } else { \
+      if (L.vec) { if (ql) hipLaunchKernelGGL((KERNEL<float, true, true>), GRID, block, 0, stream, D); \
+                   else hipLaunchKernelGGL((KERNEL<float, true, false>), GRID, block, 0, stream, D); } \
+      else { if (ql) hipLaunchKernelGGL((KERNEL<float, false, true>), GRID, block, 0, stream, D); \
+             else hipLaunchKernelGGL((KERNEL<float, false, false>), GRID, block, 0, stream, D); } \
+    } \
+  } while (0)
   trace_before(stream, SV_KERNEL_VERIFY_SAMPLE_DRAW);
-  if (L.bf16) {
-    if (L.vec) hipLaunchKernelGGL((verify_draw<uint16_t, true>), grid3, block, 0, stream, D);
-    else hipLaunchKernelGGL((verify_draw<uint16_t, false>), grid3, block, 0, stream, D);
-  } else {
-    if (L.vec) hipLaunchKernelGGL((verify_draw<float, true>), grid3, block, 0, stream, D);
-    else hipLaunchKernelGGL((verify_draw<float, false>), grid3, block, 0, stream, D);
-  }
+  SV_DRAW_KERNELS(verify_draw, grid3);
   err = hipGetLastError();
   trace_after(stream, SV_KERNEL_VERIFY_SAMPLE_DRAW);
   if (err != hipSuccess) return err;
   trace_before(stream, SV_KERNEL_VERIFY_SAMPLE_LOCATE);
-  if (L.bf16) {
-    if (L.vec) hipLaunchKernelGGL((verify_locate<uint16_t, true>), grid_acc, block, 0, stream, D);
-    else hipLaunchKernelGGL((verify_locate<uint16_t, false>), grid_acc, block, 0, stream, D);
-  } else {
-    if (L.vec) hipLaunchKernelGGL((verify_locate<float, true>), grid_acc, block, 0, stream, D);
-    else hipLaunchKernelGGL((verify_locate<float, false>), grid_acc, block, 0, stream, D);
-  }
+  SV_DRAW_KERNELS(verify_locate, grid_acc);
+#undef SV_DRAW_KERNELS
   err = hipGetLastError();
   trace_after(stream, SV_KERNEL_VERIFY_SAMPLE_LOCATE);
   return err;

@@ -87,6 +87,22 @@ typedef enum {
 #define SV_MAX_V (1 << 19)        /* vocabulary size                                  */
 #define SV_PADDING_SLOT_ID (-1)   /* slot of rows that must not write the KV cache    */
 
+/*
+ * How one drafted row's distribution q is recomputed from the drafter's
+ * logits z (see spec_draft_sample and spec_verify_sample_lq):
+ *   c > 0:  q(x) = exp2(fma(z(x), c, -mc)) * inv_s, evaluated in fp32 (c =
+ *           log2(e) / T, mc = max(z) * c, inv_s = 1 / sum of the exponentials);
+ *   c = 0:  q(x) = 1 if x == argmax else 0 (greedy drafting; argmax = -1: q = 0).
+ * These are the same fp32 operations spec_draft_sample uses to write q, so a
+ * recomputed q(x) equals the stored one bit for bit.
+ */
+typedef struct sv_draft_row {
+  float c;
+  float mc;
+  float inv_s;
+  int32_t argmax;
+} sv_draft_row;
+
 /* Human-readable name of a status code (static storage; never NULL). */
 SV_API const char* sv_status_string(int status);
 
@@ -154,6 +170,35 @@ SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
                                     float* out_draft_target_prob,
                                     void* workspace, size_t workspace_bytes,
                                     int32_t* device_error, void* stream);
+
+/*
+ * Sampled verify that takes the drafter's distributions as its logits plus a
+ * per-row descriptor (from spec_draft_sample) instead of a dense [B][K][V]
+ * q: q_k(x) is recomputed where the method needs it -- at each draft token
+ * and along row a for the residual draw.  Results are those of
+ * spec_verify_sample with draft_probs = the q that spec_draft_sample would
+ * have written (bit for bit).  It spares the dense q's write and halves the
+ * draw's drafter-row read (bf16 logits instead of fp32 q).
+ *   drafter_logits   [n_drafter_rows][V], same dtype as target_logits.
+ *   drafter_rows     optional [B][K] int32: the drafter row of draft k of
+ *                    sequence b (NULL: row b*K + k, needs n_drafter_rows >= B*K);
+ *                    a row outside [0, n_drafter_rows) sets SV_DEVERR_ROW_INDEX
+ *                    and counts as q = 0.
+ *   drafter_desc     [B][K] sv_draft_row, as written by spec_draft_sample for
+ *                    the same rows (desc b*K+k describes draft k of sequence b).
+ *   Other arguments as for spec_verify_sample.  Four kernels are enqueued.
+ */
+SV_API sv_status spec_verify_sample_lq(const void* target_logits, int logits_dtype,
+                                       const void* drafter_logits, int64_t n_drafter_rows,
+                                       const int32_t* drafter_rows,
+                                       const sv_draft_row* drafter_desc,
+                                       const int32_t* draft_tokens,
+                                       const float* uniforms, float temperature,
+                                       int B, int K, int V,
+                                       int32_t* out_tokens, int32_t* out_num_accepted,
+                                       float* out_draft_target_prob,
+                                       void* workspace, size_t workspace_bytes,
+                                       int32_t* device_error, void* stream);
 
 /*
  * Verify of a mixed serving batch: sequence b follows the greedy rule of
@@ -290,6 +335,9 @@ SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,
  *   out_draft_tokens [B][K] int32, the draft_tokens of the next verify.
  *   out_draft_probs  optional [B][K][V] fp32, the draft_probs of the next
  *                    verify (NULL = not written).
+ *   out_row_desc     optional [B][K] sv_draft_row: what spec_verify_sample_lq
+ *                    needs to recompute q from the drafter logits instead of
+ *                    reading a dense q (NULL = not written).
  * 1 <= K <= SV_MAX_K, 1 <= V <= SV_MAX_V; B = 0 is a no-op.  Arithmetic as in
  * spec_verify_sample (fp32 exponentials, fp64 running totals).  One kernel is
  * enqueued; no workspace is needed.
@@ -299,6 +347,7 @@ SV_API sv_status spec_draft_sample(const void* drafter_logits, int logits_dtype,
                                    float temperature, const float* temperatures,
                                    int B, int K, int V,
                                    int32_t* out_draft_tokens, float* out_draft_probs,
+                                   sv_draft_row* out_row_desc,
                                    int32_t* device_error, void* stream);
 
 /*

@@ -96,3 +96,17 @@ def draft_outcomes(z_row: np.ndarray, T: float, u: float, tol: float = 1e-6) -> 
     if T == 0.0:
         return [int(np.argmax(q))]
     return _draw_candidates(q, float(u), tol)
+
+
+def draft_probs(logits: np.ndarray, dtype: str, temperature: float, B: int, K: int,
+                row_index: Optional[np.ndarray] = None,
+                temperatures: Optional[np.ndarray] = None) -> np.ndarray:
+    """q [B, K, V] fp64 of the drafter rows (D1, D2, D4), without drawing."""
+    rows = _rows(B, K, row_index)
+    Ts = _temps(B, temperature, temperatures)
+    V = logits.shape[-1]
+    q = np.empty((B, K, V), dtype=np.float64)
+    for b in range(B):
+        for k in range(K):
+            q[b, k] = draft_distribution(decode_logits(logits[rows[b, k]], dtype), Ts[b])
+    return q

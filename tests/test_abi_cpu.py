@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
               "spec_draft_sample", "spec_verify_mixed", "spec_verify_workspace_bytes",
               "sv_status_string", "spec_accept_metrics", "spec_accept_metrics_words",
               "sv_step_graph_create", "sv_step_graph_launch", "sv_step_graph_destroy",
-              "spec_verify_tree"):
+              "spec_verify_tree", "spec_verify_sample_lq"):
         assert n in names
 
 
@@ -190,9 +190,9 @@ def test_tracer_host_paths(lib):
 
 
 def draft(lib, logits=FAKE, dtype=1, n_rows=6, ri=None, u=FAKE, T=0.7, temps=None, B=2, K=3,
-          V=64, tok=FAKE, probs=FAKE, err=None):
+          V=64, tok=FAKE, probs=FAKE, desc=None, err=None):
     return lib.spec_draft_sample(logits, dtype, n_rows, ri, u, T, temps, B, K, V, tok, probs,
-                                 err, None)
+                                 desc, err, None)
 
 
 def test_draft_validation(lib):
@@ -219,6 +219,7 @@ def test_draft_validation(lib):
     assert draft(lib, probs=FAKE + 2) == EALIGN
     assert draft(lib, tok=FAKE + 1) == EALIGN
     assert draft(lib, err=FAKE + 1) == EALIGN
+    assert draft(lib, desc=FAKE + 8) == EALIGN        # descriptors are 16-byte records
 
 
 def mixed(lib, logits=FAKE, dtype=1, q=FAKE, d=FAKE, u=FAKE, temps=FAKE, B=2, K=3, V=64,
@@ -321,3 +322,29 @@ def test_tree_validation(lib):
     assert tree(lib, wsb=8) == EWS
     assert tree(lib, par=FAKE + 2) == EALIGN
     assert tree(lib, dtype=0, logits=FAKE + 2) == EALIGN
+
+
+def lq(lib, logits=FAKE, dtype=1, dl=FAKE, n_rows=6, rows=None, desc=FAKE, d=FAKE, u=FAKE, T=0.7,
+       B=2, K=3, V=64, out=FAKE, acc=FAKE, pd=None, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(K, 0), max(V, 1))
+    return lib.spec_verify_sample_lq(logits, dtype, dl, n_rows, rows, desc, d, u, T, B, K, V, out,
+                                     acc, pd, ws, wsb, None, None)
+
+
+def test_sample_lq_validation(lib):
+    assert lq(lib, K=64) == ESHAPE
+    assert lq(lib, n_rows=5) == ESHAPE                 # fewer than B*K rows, no row index
+    assert lq(lib, n_rows=-1, rows=FAKE) == ESHAPE
+    assert lq(lib, dtype=2) == EDTYPE
+    for T in (0.0, -1.0, float("nan"), 1e-45):
+        assert lq(lib, T=T) == EVALUE, T
+    assert lq(lib, B=0, logits=None, dl=None, desc=None, d=None, u=None, out=None, acc=None,
+              ws=None, wsb=0) == OK
+    assert lq(lib, dl=None) == ENULL
+    assert lq(lib, desc=None) == ENULL
+    assert lq(lib, u=None) == ENULL
+    assert lq(lib, ws=None) == EWS
+    assert lq(lib, desc=FAKE + 8) == EALIGN
+    assert lq(lib, dl=FAKE + 1) == EALIGN
+    assert lq(lib, rows=FAKE + 2) == EALIGN

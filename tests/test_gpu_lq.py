@@ -1,0 +1,107 @@
+"""GPU: the sampled verify that recomputes q from the drafter logits.
+
+spec_draft_sample writes, for each drafted row, the dense q and the row
+descriptor; spec_verify_sample on the dense q and spec_verify_sample_lq on
+the drafter logits + descriptors must then agree bit for bit (tokens, accept
+counts, p_k(d_k)).  The lq results are also checked against the oracle: q from
+oracle.draft.draft_probs, then the sampled-verify oracle with its near-tie
+tolerance.  Covered: the 151936-token bf16 shape, ragged fp32 rows gathered
+through a row index with greedy-drafted sequences, and invalid drafter rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.workloads import DRAFT_CONFIGS, make_draft_inputs
+from tests.gpu_util import DEV, check_sample_sequence, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _chain(sv, z, zd, K, Td, T, u_draft, u_verify, rows=None, temps=None):
+    tok, q, desc = sv.spec_draft_sample(zd, K, Td, uniforms=u_draft, row_index=rows,
+                                        temperatures=temps, want_row_desc=True)
+    dense = sv.spec_verify_sample(z, q, tok, u_verify, T, want_draft_target_prob=True)
+    lq = sv.spec_verify_sample_lq(z, zd, desc, tok, u_verify, T, drafter_rows=rows,
+                                  want_draft_target_prob=True)
+    torch.cuda.synchronize()
+    return tok, q, desc, dense, lq
+
+
+def _same(dense, lq):
+    assert torch.equal(dense[0], lq[0]) and torch.equal(dense[1], lq[1])
+    assert torch.equal(dense[2].view(torch.int32), lq[2].view(torch.int32))
+
+
+def test_lq_matches_dense_and_oracle_large_vocab(gpu):
+    vi = synth.make_verify_inputs(synth.verify_config(5), seqs=range(48))
+    di = make_draft_inputs(DRAFT_CONFIGS["draft-mid"])           # B=48, K=7, V=151936 bf16
+    B, K, V = 48, 7, 151936
+    tok, q, desc, dense, lq = _chain(gpu, dev(vi.logits), dev(di.logits), K, di.temperature,
+                                     vi.temperature, dev(di.uniforms), dev(vi.uniforms))
+    _same(dense, lq)
+    out, acc, pd = (x.cpu().numpy() for x in lq)
+    tok = tok.cpu().numpy()
+    oq = oracle.draft.draft_probs(di.logits, "bf16", di.temperature, B, K)
+    checked = 0
+    for b in range(B):
+        od = [oracle.draft.draft_sample_row(oracle.decode_logits(di.logits[b * K + k], "bf16"),
+                                            float(np.float32(di.temperature)), di.uniforms[b, k])[0]
+              for k in range(K)]
+        if list(tok[b]) != od:
+            continue                      # a flagged near tie in the draft itself
+        z64 = oracle.decode_logits(vi.logits[b], "bf16")
+        check_sample_sequence(z64, oq[b], tok[b], vi.uniforms[b], vi.temperature, out[b], acc[b],
+                              pd[b])
+        checked += 1
+    assert checked >= B - 2
+
+
+def test_lq_gathered_rows_greedy_drafts_and_bad_rows(gpu):
+    di = make_draft_inputs(DRAFT_CONFIGS["draft-ragged"])         # fp32-free: bf16, V=30011
+    s = di.spec
+    B, K, V = s.B, s.K, s.V
+    rng = np.random.default_rng(91)
+    z = synth.f32_to_bf16_bits((3.0 * rng.standard_normal((B, K + 1, V))).astype(np.float32))
+    uv = rng.random((B, K + 1), dtype=np.float32)
+    temps = di.temperatures.copy()
+    temps[0] = 0.0                                                # a greedy-drafted sequence
+    tok, q, desc, dense, lq = _chain(gpu, dev(z), dev(di.logits), K, s.temperature, 0.9,
+                                     dev(di.uniforms), dev(uv), rows=dev(di.row_index),
+                                     temps=dev(temps))
+    _same(dense, lq)
+    d = desc.cpu().numpy()
+    assert np.all(d[0, :, 0] == 0) and np.all(d[0, :, 3] == tok.cpu().numpy()[0])
+    # a drafter row outside the logits: flagged, and counted as q = 0 (the
+    # dense path sees the all-zero q row that spec_draft_sample writes for it)
+    rows = di.row_index.copy()
+    rows[2, 1] = B * s.rows_per_seq + 3
+    err_d = torch.zeros(1, dtype=torch.int32, device=DEV)
+    err_v = torch.zeros(1, dtype=torch.int32, device=DEV)
+    tok2, q2, desc2 = gpu.spec_draft_sample(dev(di.logits), K, s.temperature,
+                                            uniforms=dev(di.uniforms), row_index=dev(rows),
+                                            temperatures=dev(temps), want_row_desc=True,
+                                            device_error=err_d)
+    tok2[2, 1] = 5                                                # a valid token for the test
+    a1 = gpu.spec_verify_sample(dev(z), q2, tok2, dev(uv), 0.9, want_draft_target_prob=True)
+    a2 = gpu.spec_verify_sample_lq(dev(z), dev(di.logits), desc2, tok2, dev(uv), 0.9,
+                                   drafter_rows=dev(rows), want_draft_target_prob=True,
+                                   device_error=err_v)
+    torch.cuda.synchronize()
+    assert int(err_d.item()) == gpu.DEVERR_ROW_INDEX
+    assert int(err_v.item()) == gpu.DEVERR_ROW_INDEX
+    _same(a1, a2)
+
+
+def test_lq_without_drafts(gpu):
+    z = dev((2.0 * np.random.default_rng(3).standard_normal((3, 1, 64))).astype(np.float32))
+    u = dev(np.random.default_rng(4).random((3, 1), dtype=np.float32))
+    zd = torch.zeros((0, 64), dtype=torch.float32, device=DEV)
+    desc = torch.zeros((3, 0, 4), dtype=torch.int32, device=DEV)
+    d = torch.zeros((3, 0), dtype=torch.int32, device=DEV)
+    o1, a1, _ = gpu.spec_verify_sample_lq(z, zd, desc, d, u, 1.0)
+    o2, a2, _ = gpu.spec_verify_sample(z, torch.zeros((3, 0, 64), device=DEV), d, u, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(a1, a2)
