@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run only this many untimed steps (for rocprofv3) and exit; inputs are "
                          "then drawn in this process (no worker processes under a profiler)")
+    ap.add_argument("--hash-out", default=None,
+                    help="with --profile-steps: write the kernel source hash of this run here")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE runs of --profile-steps) into the traffic record and exit")
@@ -148,7 +150,17 @@ COPY_BYTES = 1 << 30           # the calibration copy of --profile-steps
 def ingest_counters(fetch_csv, write_csv):
     """Per-kernel HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the 1 GiB copy
-    in the same run; writes the traffic record and a markdown summary."""
+    in the same run; writes the traffic record and a markdown summary.  Both
+    profiled runs must have recorded (--hash-out source_hash.txt next to their
+    CSV) the kernel source hash of the current sources."""
+    here = kernel_source_hash()
+    for csv in (fetch_csv, write_csv):
+        hp = os.path.join(os.path.dirname(csv), "source_hash.txt")
+        if not os.path.exists(hp):
+            sys.exit(f"{hp} is missing: cannot tell which kernels these counters measured")
+        got = open(hp).read().strip()
+        if got != here:
+            sys.exit(f"counters in {csv} were taken on kernel sources {got}, not the current {here}")
     import csv
     import collections
 
@@ -178,12 +190,17 @@ def ingest_counters(fetch_csv, write_csv):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
     md = os.path.join(ROOT, "profiles", "hbm_counters_fused_b1024.md")
+    # the commands that made the two CSVs: one counter per profiler run, output
+    # in the directory holding each CSV
+    fdir, wdir = os.path.dirname(fetch_csv), os.path.dirname(write_csv)
+    fo = os.path.basename(fetch_csv).split("_counter_collection")[0]
+    wo = os.path.basename(write_csv).split("_counter_collection")[0]
     lines = ["# HBM bytes per launch from rocprofv3 counters: fused step, B=1024 K=7 V=151936 bf16, H=2048\n",
-             "Commands (one counter per run, from /tmp with TMPDIR=/tmp; profiler output under gpurun_out/):\n",
+             "Commands (one counter per run, from /tmp with TMPDIR=/tmp; REPO = the repository root):\n",
              "```",
-             "timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $GRAFT_REPO_ROOT/gpurun_out/pmc_fetch -o fetch -- python3 $GRAFT_REPO_ROOT/bench.py --profile-steps 2",
-             "timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $GRAFT_REPO_ROOT/gpurun_out/pmc_write -o write -- python3 $GRAFT_REPO_ROOT/bench.py --profile-steps 2",
-             "python bench.py --ingest-counters gpurun_out/pmc_fetch/fetch_counter_collection.csv gpurun_out/pmc_write/write_counter_collection.csv",
+             f"timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{fdir} -o {fo} -- python3 $REPO/bench.py --profile-steps 2 --hash-out $REPO/{fdir}/source_hash.txt",
+             f"timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{wdir} -o {wo} -- python3 $REPO/bench.py --profile-steps 2 --hash-out $REPO/{wdir}/source_hash.txt",
+             f"python bench.py --ingest-counters {fetch_csv} {write_csv}",
              "```\n",
              f"Calibration (a plain 1 GiB device copy in the same runs): FETCH_SIZE x {f_scale:.4f}, "
              f"WRITE_SIZE x {w_scale:.4f} give bytes.  Kernel source hash `{rec['source_hash']}`.\n",
@@ -361,7 +378,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the path shards by sequence with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -434,15 +451,41 @@ def main():
                                     bi.mask_token_id, outputs=bouts)
 
     if args.profile_steps:
+        # every kernel family once per step, for the profiler: sampled, greedy
+        # and mixed verify with the build, drafter sampling with q and with
+        # row descriptors, the verify from drafter logits, acceptance metrics,
+        # and (below) tree verification
+        d_desc = torch.empty((B, K, 4), dtype=torch.int32, device=dev)
+        mtr = sv.accept_metrics_buffer(K, dev)
         for i in range(args.profile_steps):
-            step(True); build(); step(False); build(); draft()
+            step(True); build(); step(False); build(); step("mixed"); build(); draft()
+            sv.spec_draft_sample(z_rows, K, vi.temperature, uniforms=d_u, row_index=d_rows,
+                                 out_draft_tokens=d_tok, want_draft_probs=False,
+                                 out_row_desc=d_desc)
+            sv.spec_verify_sample_lq(z, z_rows, d_desc, d_tok, u, vi.temperature,
+                                     drafter_rows=d_rows, out_tokens=out_t,
+                                     out_num_accepted=acc_t, workspace=ws)
+            sv.spec_accept_metrics(acc_t, K, mtr)
+        torch.cuda.synchronize()
+        ts = synth.TREE_CONFIGS["tree-large"]
+        ti = synth.make_tree_inputs(ts, workers=1)
+        tz, tq, tp, tt, tu = (up(ti.logits), up(ti.draft_probs), up(ti.parents), up(ti.tokens),
+                              up(ti.uniforms))
+        for i in range(args.profile_steps):
+            for T in (0.0, ts.temperature):
+                sv.spec_verify_tree(tz, tp, tt, T, draft_probs=tq, uniforms=tu)
         torch.cuda.synchronize()
         # calibration for HBM byte counters: one plain copy of 1 GiB
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(f"profiled {args.profile_steps} sampled and greedy steps and a 1 GiB copy", flush=True)
+        if args.hash_out:
+            os.makedirs(os.path.dirname(os.path.abspath(args.hash_out)), exist_ok=True)
+            with open(args.hash_out, "w") as f:
+                f.write(kernel_source_hash() + "\n")
+        print(f"profiled {args.profile_steps} steps of every kernel family and a 1 GiB copy",
+              flush=True)
         return
 
     def timed(sample):
