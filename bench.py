@@ -165,25 +165,30 @@ def ingest_counters(fetch_csv, write_csv):
     import collections
 
     def load(path, counter):
+        # per (kernel, grid size): one kernel serves several workloads
         per = collections.defaultdict(list)
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] == counter:
-                per[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)
+                per[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]) * 1024.0)
         return per
 
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
-    copy = [k for k in fetch if "copyBuffer" in k][0]
-    f_scale = COPY_BYTES / max(fetch[copy])
-    w_scale = COPY_BYTES / max(write[copy])
+    copy = [k for k in fetch if "copyBuffer" in k[0]]
+    f_scale = COPY_BYTES / max(max(fetch[k]) for k in copy)
+    w_scale = COPY_BYTES / max(max(write[k]) for k in copy)
     kernels = {}
-    for name in fetch:
+    for key in sorted(fetch, key=lambda k: (k[0], -k[1])):
+        name, grid = key
         if not name.startswith(("void sv::", "sv::")):
             continue
-        f = sum(fetch[name]) / len(fetch[name]) * f_scale
-        w = sum(write.get(name, [0.0])) / max(1, len(write.get(name, []))) * w_scale
-        kernels[name] = {"fetch_bytes": f, "write_bytes": w, "hbm_bytes_per_launch": f + w,
-                         "dispatches": len(fetch[name])}
-    dom = [k for k in kernels if "verify_rows<unsigned short, 1, true>" in k][0]
+        f = sum(fetch[key]) / len(fetch[key]) * f_scale
+        w = sum(write.get(key, [0.0])) / max(1, len(write.get(key, []))) * w_scale
+        kernels[f"{name} [grid {grid}]"] = {"fetch_bytes": f, "write_bytes": w,
+                                            "hbm_bytes_per_launch": f + w,
+                                            "dispatches": len(fetch[key]), "grid": grid}
+    # the sampled row kernel of the fused step: the largest grid of that kernel
+    dom = max((k for k in kernels if "verify_rows<unsigned short, 1, true>" in k),
+              key=lambda k: kernels[k]["grid"])
     rec = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
            "kernel": dom, "hbm_bytes_per_launch": kernels[dom]["hbm_bytes_per_launch"],
            "kernels": kernels}
@@ -204,7 +209,7 @@ def ingest_counters(fetch_csv, write_csv):
              "```\n",
              f"Calibration (a plain 1 GiB device copy in the same runs): FETCH_SIZE x {f_scale:.4f}, "
              f"WRITE_SIZE x {w_scale:.4f} give bytes.  Kernel source hash `{rec['source_hash']}`.\n",
-             "| kernel | dispatches | HBM read (GB) | HBM write (GB) | total (GB) |", "|---|---|---|---|---|"]
+             "| kernel [grid size in threads] | dispatches | HBM read (GB) | HBM write (GB) | total (GB) |", "|---|---|---|---|---|"]
     for name, k in kernels.items():
         lines.append(f"| `{name}` | {k['dispatches']} | {k['fetch_bytes'] / 1e9:.4f} | "
                      f"{k['write_bytes'] / 1e9:.4f} | {k['hbm_bytes_per_launch'] / 1e9:.4f} |")
