@@ -186,3 +186,14 @@ def test_draft_then_verify_on_gpu(gpu):
                               acc[b], pd[b])
         checked += 1
     assert checked >= B - 1
+
+
+def test_max_drafts_per_sequence(gpu):
+    """K = 63 drafts per sequence (the limit), rows gathered, mixed temperatures."""
+    rng = np.random.default_rng(63)
+    B, K, V = 2, 63, 1000
+    z = (2.0 * rng.standard_normal((B * K + 5, V))).astype(np.float32)
+    rows = rng.permutation(B * K + 5)[:B * K].astype(np.int32).reshape(B, K)
+    u = rng.random((B, K), dtype=np.float32)
+    temps = np.array([0.0, 0.8], np.float32)
+    _parity(gpu, z, "f32", u, 1.0, B, K, row_index=rows, temps=temps)

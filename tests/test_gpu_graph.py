@@ -157,3 +157,16 @@ def test_step_graph_argument_errors(gpu):
     assert verify["out_num_accepted"].cpu().tolist() == [3, 3]
     assert verify["out_tokens"].cpu().tolist() == [[0, 0, 0, 0], [0, 0, 0, 0]]
     g.close()
+
+
+def test_metrics_at_max_drafts(gpu):
+    rng = np.random.default_rng(73)
+    K = 63
+    a = rng.integers(0, K + 1, size=5000).astype(np.int32)
+    m = gpu.accept_metrics_buffer(K, DEV)
+    gpu.spec_accept_metrics(dev(a), K, m)
+    torch.cuda.synchronize()
+    want = oracle.metrics.counters(a, K)
+    got = m.cpu().numpy()
+    assert np.array_equal(got[gpu.METRICS_HIST:], want["hist"])
+    assert got[gpu.METRICS_ACCEPTED] == want["accepted"]

@@ -133,3 +133,12 @@ def test_determinism_and_clean_workspace(gpu):
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(r1, r2))
     assert int(ws.count_nonzero().item()) == 0
+
+
+def test_max_nodes_random_trees(gpu):
+    """N = 63 nodes (the limit) with a vocabulary that is not a multiple of 8."""
+    from synth.workloads import TreeSpec
+    spec = TreeSpec("tree-max", 3, 63, 4099, "f32", 2.0, "none", 1.0, 0.5, 1.0, "random", (), 25)
+    ti = make_tree_inputs(spec, workers=1)
+    _check_greedy(ti, *_run(gpu, ti, 0.0))
+    _check_sample(ti, 1.0, *_run(gpu, ti, 1.0))
