@@ -65,6 +65,9 @@ def parse():
                          "then drawn in this process (no worker processes under a profiler)")
     ap.add_argument("--hash-out", default=None,
                     help="with --profile-steps: write the kernel source hash of this run here")
+    ap.add_argument("--ingest-valu", default=None, metavar="VALU_CSV",
+                    help="write profiles/valu_counters_fused_b1024.md from a --pmc SQ_INSTS_VALU "
+                         "SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE run")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE runs of --profile-steps) into the traffic record and exit")
@@ -217,6 +220,51 @@ def ingest_counters(fetch_csv, write_csv):
         f.write("\n".join(lines) + "\n")
     print(json.dumps({"traffic_file": TRAFFIC_FILE, "summary": md,
                       "dominant_hbm_bytes_per_launch": rec["hbm_bytes_per_launch"]}))
+
+
+def ingest_valu(valu_csv):
+    """ALU load per kernel from instruction counters: VALU and fp32
+    transcendental wave instructions per dispatch, converted to SIMD cycles
+    (a wave64 instruction: 4 cycles on a 16-lane SIMD without packed fp32; a
+    transcendental: 16, a quarter rate) and set against the SIMD cycles of the
+    kernel's duration at 2.4 GHz (durations of the same dispatches, from the
+    counter run's timestamps)."""
+    import csv
+    import collections
+    hp = os.path.join(os.path.dirname(valu_csv), "source_hash.txt")
+    if not os.path.exists(hp) or open(hp).read().strip() != kernel_source_hash():
+        sys.exit(f"{valu_csv}: counters not taken on the current kernel sources")
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    span = collections.defaultdict(dict)       # dispatch -> duration (us)
+    for r in csv.DictReader(open(valu_csv)):
+        key = (r["Kernel_Name"], int(r["Grid_Size"]))
+        per[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        span[key][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    simd_cycles_per_us = 256 * 4 * 2400.0
+    lines = ["# ALU load from instruction counters: fused-step kernels (B=1024, K=7, V=151936 bf16)\n",
+             "Command (REPO = the repository root):\n", "```",
+             f"timeout -s KILL 300 rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE --output-format csv -d $REPO/{os.path.dirname(valu_csv)} -o valu -- python3 $REPO/bench.py --profile-steps 2 --hash-out $REPO/{os.path.dirname(valu_csv)}/source_hash.txt",
+             f"python bench.py --ingest-valu {valu_csv}", "```\n",
+             "Counts are wave instructions per dispatch.  SIMD cycles: 4 per VALU instruction of a wave64 "
+             "on a 16-lane SIMD (fp32 without packed math), 16 per transcendental (quarter rate).  "
+             "Load = those cycles / (1024 SIMDs x duration x 2.4 GHz), durations from the "
+             "counter run's own dispatch timestamps; exp/s counts lanes.\n",
+             f"Kernel source hash `{kernel_source_hash()}`.\n",
+             "| kernel [grid] | VALU instr | of which exp (fp32 transcendental) | duration µs | exp/s | ALU load at 2.4 GHz |",
+             "|---|---|---|---|---|---|"]
+    for (name, grid), c in sorted(per.items()):
+        if not name.startswith(("void sv::", "sv::")) or not c["SQ_INSTS_VALU"]:
+            continue
+        valu = sum(c["SQ_INSTS_VALU"]) / len(c["SQ_INSTS_VALU"])
+        tr = sum(c["SQ_INSTS_VALU_TRANS_F32"]) / max(1, len(c["SQ_INSTS_VALU_TRANS_F32"]))
+        us = sum(span[(name, grid)].values()) / len(span[(name, grid)])
+        cycles = (valu - tr) * 4 + tr * 16
+        lines.append(f"| `{name} [{grid}]` | {valu:.3e} | {tr:.3e} | {us:.1f} | "
+                     f"{tr * 64 / (us * 1e-6):.2e} | {100 * cycles / (simd_cycles_per_us * us):.0f}% |")
+    md = os.path.join(ROOT, "profiles", "valu_counters_fused_b1024.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(md)
 
 
 def graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt, hid, hs, out_t, acc_t,
@@ -380,6 +428,9 @@ def main():
     args = parse()
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
+        return
+    if args.ingest_valu:
+        ingest_valu(args.ingest_valu)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
