@@ -13,10 +13,10 @@
 //
 // verify_draw (sampling): C workgroups per sequence each take a contiguous
 // chunk of row a and store the mass r = max(0, p_a - q_a) (or p_K for the
-// bonus token) of each 2048-element tile in it, and the chunk's total.
-// verify_locate: one wave per sequence finds the chunk, then the tile, whose
-// running total first exceeds u * S, rescans that one tile and writes the
-// token.  Every hand-off between workgroups goes through a kernel boundary.
+// bonus token) of each 2048-element tile in it.
+// verify_locate: one wave per sequence finds the tile whose running total
+// first exceeds u * S, rescans that one tile and writes the token.  Every
+// hand-off between workgroups goes through a kernel boundary.
 //
 // The verify flow is that of "Project 14 - speculative decoding inference
 // server", section 架构 (architecture): accept the prefix, resample the
@@ -44,9 +44,9 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kTileUnroll = 1;          // draw: tiles per wave per step
 
 // ---------------------------------------------------------------- workspace
-// scan results [B] | chunk sums [B][C] | tile sums [B][T] | partials [B][K+1][S]
+// scan results [B] | tile sums [B][T] | partials [B][K+1][S]
 struct Layout {
-  size_t info, chunk, tile, partials, total;
+  size_t info, tile, partials, total;
   int S, C, T;
 };
 
@@ -76,7 +76,6 @@ static Layout layout(int B, int K, int V) {
   L.T = (V + kTileElems - 1) / kTileElems;
   size_t off = 0;
   L.info = off;     off = align256(off + (size_t)B * sizeof(ScanResult));
-  L.chunk = off;    off = align256(off + (size_t)B * L.C * sizeof(double));
   L.tile = off;     off = align256(off + (size_t)B * L.T * sizeof(float));
   L.partials = off; off = align256(off + (size_t)B * (K + 1) * L.S * sizeof(Partial));
   L.total = off;
@@ -122,7 +121,6 @@ struct ScanArgs {          // what an accept scan reads and writes
 struct DrawArgs {
   ScanArgs sc;
   int C, T;
-  double* chunk_sums;      // [B][C]
   float* tile_sums;        // [B][T]
 };
 
@@ -384,13 +382,11 @@ __device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool resid
   return ls;
 }
 
-// verify_draw: chunk cidx of sequence b stores the mass of each of its tiles
-// and the chunk total (tile order).  A tile is kTileLoads consecutive
-// 512-element wave loads; each lane sums its octets of the tile before one
-// wave reduction.
+// verify_draw: chunk cidx of sequence b stores the mass of each of its
+// tiles.  A tile is kTileLoads consecutive 512-element wave loads; each lane
+// sums its octets of the tile before one wave reduction.
 template <typename LT, bool VEC, bool QL>
 __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
-  __shared__ float tsum_l[kMaxTiles];
   const int C = A.C, T = A.T;
   const int b = blockIdx.x / C, cidx = blockIdx.x % C;
   const long V = A.sc.V;
@@ -409,121 +405,86 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
 #pragma unroll
     for (int j = 0; j < kTileUnroll; ++j) {
       const float ts = wave_sum_f(ls[j]);
-      if (l == 0 && t0 + j < t_hi) {
-        tsum_l[t0 + j - t_lo] = ts;
-        tsum_g[t0 + j] = ts;                  // read by verify_locate
-      }
+      if (l == 0 && t0 + j < t_hi) tsum_g[t0 + j] = ts;   // read by verify_locate
     }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double sum = 0.0;
-    for (int i = 0; i < t_hi - t_lo; ++i) sum += (double)tsum_l[i];
-    A.chunk_sums[(long)b * C + cidx] = sum;
   }
 }
 
 // verify_locate: one wave per sequence draws the token from the tile masses.
 template <typename LT, bool VEC, bool QL>
 __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
+  constexpr int kPer = kMaxTiles / kWave;     // tiles per lane at most
   const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
   if (b >= A.sc.B) return;
-  const int C = A.C, T = A.T, K = A.sc.K;
+  const int T = A.T, K = A.sc.K;
   const long V = A.sc.V;
   const long nocts = (V + 7) / 8;
   const int l = lane_id();
+  float* tsum_g = A.tile_sums + (long)b * T;
+  // this sequence's tile masses, lanes owning contiguous runs of tiles; the
+  // loads go out before the scan result is read.  They are agent-coherent
+  // loads: the rare path below rewrites the masses from this wave and reads
+  // them back.
+  const int per = (T + kWave - 1) / kWave;
+  const int lo = min(T, l * per), hi = min(T, (l + 1) * per);
+  float ts[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) ts[j] = lo + j < hi ? ld_coherent(&tsum_g[lo + j]) : 0.f;
   const DrawRow<LT> R = draw_row<LT, QL>(A, b);
   if (R.c == 0.f) {                           // greedy: nothing to draw
     if (l == 0) A.sc.info[b] = ScanResult{0, 0, 0.f, 0.f, 0.0};
     return;
   }
   bool residual = R.residual;
-  float* tsum_g = A.tile_sums + (long)b * T;
-  double* csum_g = A.chunk_sums + (long)b * C;
-  const int per = (C + kWave - 1) / kWave;
-  const int lo = l * per, hi = min(C, (l + 1) * per);
-
-  // the masses are read with agent-coherent loads: the rare path below
-  // rewrites them from this wave and reads them back
   double part = 0.0;
-  for (int i = lo; i < hi; ++i) part += ld_coherent(&csum_g[i]);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) part += (double)ts[j];
   double incl = wave_inclusive_scan(part);
   double S = __shfl(incl, kWave - 1);
   if (residual && !(S > 0.0)) {
     // r sums to 0 (only when the drafter's row sums to more than p): draw
-    // from p_a instead; this wave recomputes every tile and chunk mass
+    // from p_a instead; this wave recomputes every tile mass
     residual = false;
-    for (int ci = 0; ci < C; ++ci) {
-      const int clo = (int)((long)ci * T / C), chi = (int)((long)(ci + 1) * T / C);
-      double cs = 0.0;
-      for (int t = clo; t < chi; ++t) {
-        const float ts = wave_sum_f(lane_tile_mass<LT, VEC, QL>(R, false, t, V, nocts));
-        if (l == 0) st_coherent(&tsum_g[t], ts);
-        cs += (double)ts;
-      }
-      if (l == 0) st_coherent(&csum_g[ci], cs);
+    for (int t = 0; t < T; ++t) {
+      const float m = wave_sum_f(lane_tile_mass<LT, VEC, QL>(R, false, t, V, nocts));
+      if (l == 0) st_coherent(&tsum_g[t], m);
     }
     wait_stores_performed();
     part = 0.0;
-    for (int i = lo; i < hi; ++i) part += ld_coherent(&csum_g[i]);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      ts[j] = lo + j < hi ? ld_coherent(&tsum_g[lo + j]) : 0.f;
+      part += (double)ts[j];
+    }
     incl = wave_inclusive_scan(part);
     S = __shfl(incl, kWave - 1);
   }
   const double target = (double)A.sc.uniforms[(long)b * (K + 1) + K] * S;
 
-  // chunk that holds u * S (lanes own contiguous runs of chunks)
+  // the tile that holds u * S
   double run = __shfl_up(incl, 1);
   if (l == 0) run = 0.0;
-  int hit = -1;
+  int hit = -1, last = -1;
   double pre = 0.0;
-  for (int i = lo; i < hi; ++i) {
-    const double nxt = run + ld_coherent(&csum_g[i]);
-    if (nxt > target) { hit = i; pre = run; break; }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (lo + j >= hi) break;
+    if (ts[j] > 0.f) last = lo + j;
+    const double nxt = run + (double)ts[j];
+    if (hit < 0 && nxt > target) { hit = lo + j; pre = run; }
     run = nxt;
   }
-  unsigned long long any = __ballot(hit >= 0);
-  int chunk;
+  int tile;
   bool fallback = false;
+  const unsigned long long any = __ballot(hit >= 0);
   if (any) {
     const int src = __ffsll((long long)any) - 1;
-    chunk = __shfl(hit, src);
+    tile = __shfl(hit, src);
     pre = __shfl(pre, src);
   } else {
-    // rounding left u*S at or past the total: last chunk with positive mass
-    int last = -1;
-    for (int i = lo; i < hi; ++i) if (ld_coherent(&csum_g[i]) > 0.0) last = i;
+    // rounding left u*S at or past the total: the last tile with positive mass
     const unsigned long long anyp = __ballot(last >= 0);
-    chunk = anyp ? __shfl(last, 63 - __clzll((long long)anyp)) : 0;
-    fallback = true;
-  }
-  // tile inside the chunk (lanes own contiguous runs of its tiles)
-  const int clo = (int)((long)chunk * T / C), chi = (int)((long)(chunk + 1) * T / C);
-  const int tper = (chi - clo + kWave - 1) / kWave;
-  const int tlo = clo + l * tper, thi = min(chi, clo + (l + 1) * tper);
-  double tpart = 0.0;
-  for (int i = tlo; i < thi; ++i) tpart += (double)ld_coherent(&tsum_g[i]);
-  const double tincl = wave_inclusive_scan(tpart);
-  double trun = __shfl_up(tincl, 1);
-  if (l == 0) trun = 0.0;
-  trun += pre;
-  int thit = -1, tlast = -1;
-  double tpre = 0.0;
-  for (int i = tlo; i < thi; ++i) {
-    const float ts = ld_coherent(&tsum_g[i]);
-    if (ts > 0.f) tlast = i;
-    const double nxt = trun + (double)ts;
-    if (!fallback && thit < 0 && nxt > target) { thit = i; tpre = trun; }
-    trun = nxt;
-  }
-  any = __ballot(thit >= 0);
-  int tile;
-  if (any) {
-    const int src = __ffsll((long long)any) - 1;
-    tile = __shfl(thit, src);
-    tpre = __shfl(tpre, src);
-  } else {
-    const unsigned long long anyp = __ballot(tlast >= 0);
-    tile = anyp ? __shfl(tlast, 63 - __clzll((long long)anyp)) : clo;
+    tile = anyp ? __shfl(last, 63 - __clzll((long long)anyp)) : 0;
     fallback = true;
   }
 
@@ -534,11 +495,10 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
     const long o = ((long)tile * kTileLoads + sl) * kWave + l;
     octet_mass<LT, VEC, QL>(R, o, V, nocts, residual, r[sl]);
   }
-  const int pick = pick_in_tile(r, tile, tpre, target, fallback);
+  const int pick = pick_in_tile(r, tile, pre, target, fallback);
   if (l == 0) A.sc.out_tokens[(long)b * (K + 1) + R.a] = pick;
   // leave this sequence's part of the workspace cleared
   for (int i = l; i < T; i += kWave) st_coherent(&tsum_g[i], 0.f);
-  for (int i = l; i < C; i += kWave) st_coherent(&csum_g[i], 0.0);
   if (l == 0) A.sc.info[b] = ScanResult{0, 0, 0.f, 0.f, 0.0};
 }
 
@@ -649,7 +609,6 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   DrawArgs D;
   D.sc = sc;
   D.C = lay.C; D.T = lay.T;
-  D.chunk_sums = reinterpret_cast<double*>(ws + lay.chunk);
   D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
   const dim3 grid3((unsigned)((long)L.B * lay.C));
 #define SV_DRAW_KERNELS(KERNEL, GRID) \
