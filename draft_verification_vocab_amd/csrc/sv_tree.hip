@@ -30,6 +30,7 @@ namespace sv {
 // 256; 1024 would be 106 but spills registers); the greedy walk only reads
 // partials.
 template <int MODE> constexpr int tree_threads() { return MODE == SAMPLE ? 512 : 256; }
+constexpr int kTreeSplits = 16;        // workgroups per row at most (the row kernel's limit)
 
 struct TreeArgs {
   TreeLaunch L;
@@ -135,17 +136,23 @@ __global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
     float M = -INFINITY;
     int g = INT32_MAX;
     double s = 0.0;
+    // all of the row's partials loaded at once (at most kTreeSplits of them)
+    Partial pk[kTreeSplits];
+#pragma unroll
+    for (int j = 0; j < kTreeSplits; ++j)
+      if (j < S) pk[j] = Pb[cur * S + j];
     if constexpr (MODE == GREEDY) {
-      for (int j = 0; j < S; ++j) {
-        const Partial p = Pb[cur * S + j];
-        if (j == 0 || p.m > M) { M = p.m; g = p.g; }
-      }
+#pragma unroll
+      for (int j = 0; j < kTreeSplits; ++j)
+        if (j < S && (j == 0 || pk[j].m > M)) { M = pk[j].m; g = pk[j].g; }
     } else {
-      for (int j = 0; j < S; ++j) M = fmaxf(M, Pb[cur * S + j].m);
-      for (int j = 0; j < S; ++j) {
-        const Partial p = Pb[cur * S + j];
-        if (p.acc != 0.0) s += p.acc * exp2(((double)p.m - (double)M) * (double)c);
-      }
+#pragma unroll
+      for (int j = 0; j < kTreeSplits; ++j)
+        if (j < S) M = fmaxf(M, pk[j].m);
+#pragma unroll
+      for (int j = 0; j < kTreeSplits; ++j)
+        if (j < S && pk[j].acc != 0.0)
+          s += pk[j].acc * exp2(((double)pk[j].m - (double)M) * (double)c);
     }
     const LT* zrow = zb + (long)cur * V;
     int nxt = -1;

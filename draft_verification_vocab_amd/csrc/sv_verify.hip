@@ -41,6 +41,7 @@ struct ScanResult {  // outcome of a sequence's accept scan
 
 constexpr int kThreads = 256;           // 4 waves
 constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxSplits = 16;          // workgroups per logit row at most
 constexpr int kTileUnroll = 1;          // draw: tiles per wave per step
 
 // ---------------------------------------------------------------- workspace
@@ -56,7 +57,7 @@ int verify_splits(int B, int K, int V) {
   const long rows = (long)B * (K + 1);
   const long octets = (V + 7) / 8;
   long s = (2048 + rows - 1) / rows;
-  s = s < 16 ? s : 16;
+  s = s < kMaxSplits ? s : kMaxSplits;
   long cap = octets / 256;
   if (s > cap) s = cap;
   return s < 1 ? 1 : (int)s;
@@ -168,17 +169,24 @@ __device__ __forceinline__ ScanResult accept_scan(const ScanArgs& A, int b, bool
   int g = INT32_MAX;
   double s_k = 0.0;
   if (k <= K) {
+    // all of the row's partials are loaded at once (S <= kMaxSplits), so the
+    // scan waits for one load latency, not S of them
+    Partial pk[kMaxSplits];
+#pragma unroll
+    for (int j = 0; j < kMaxSplits; ++j)
+      if (j < S) pk[j] = Pb[k * S + j];
     if constexpr (MODE == GREEDY) {
-      for (int j = 0; j < S; ++j) {
-        const Partial p = Pb[k * S + j];
-        if (j == 0 || p.m > M) { M = p.m; g = p.g; }
-      }
+#pragma unroll
+      for (int j = 0; j < kMaxSplits; ++j)
+        if (j < S && (j == 0 || pk[j].m > M)) { M = pk[j].m; g = pk[j].g; }
     } else {
-      for (int j = 0; j < S; ++j) M = fmaxf(M, Pb[k * S + j].m);
-      for (int j = 0; j < S; ++j) {
-        const Partial p = Pb[k * S + j];
-        if (p.acc != 0.0) s_k += p.acc * exp2(((double)p.m - (double)M) * (double)c);
-      }
+#pragma unroll
+      for (int j = 0; j < kMaxSplits; ++j)
+        if (j < S) M = fmaxf(M, pk[j].m);
+#pragma unroll
+      for (int j = 0; j < kMaxSplits; ++j)
+        if (j < S && pk[j].acc != 0.0)
+          s_k += pk[j].acc * exp2(((double)pk[j].m - (double)M) * (double)c);
     }
   }
   int d = -1;
