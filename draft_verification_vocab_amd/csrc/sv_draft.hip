@@ -215,8 +215,8 @@ __global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(Draft
 
   if (greedy) {
     // lowest-index argmax; q is its one-hot
-    const Partial P = slice_stats<LT, GREEDY, VEC, THREADS, !WQ>(zrow, 0, nocts, V, c, sm_f,
-                                                               sm_i, sm_d);
+    const Partial P = slice_stats<LT, GREEDY, VEC, THREADS, !WQ, true>(zrow, 0, nocts, V, c,
+                                                                     sm_f, sm_i, sm_d);
     if (t == 0) stats = P;
     __syncthreads();
     const int g = stats.g == INT32_MAX ? 0 : stats.g;

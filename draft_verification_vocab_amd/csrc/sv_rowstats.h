@@ -76,12 +76,19 @@ __device__ __forceinline__ float tree_sum8(const float e[8]) {
   return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
 }
 
-// Fold N octets (at octet indices o0, o0 + ostride, ...) into the state.  The
+// Fold N octets (at octet indices o0, o0 + OSTRIDE, ...) into the state.  The
 // octets arrive in increasing index order, so "strictly greater" keeps the
-// lowest index of a maximum.
-template <int MODE, int N>
-__device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, long ostride,
-                                     long V, float c) {
+// lowest index of a maximum.  RANGED: some of the elements may lie at or past
+// V (padding of a ragged row) and must not be taken as the argmax.  Without
+// it every element is in the row and the greedy search names a candidate by
+// its slot u*8 + j in the step (< 64, so every select takes an inline
+// constant and no register), one independent compare/select chain per octet
+// joined by a minimum: one compare and one select per element.  The ranged
+// form adds a 64-bit index and bound test, ~3x the instructions, and a search
+// runs on most steps because some lane of the wave almost always finds a new
+// maximum.
+template <int MODE, int N, int OSTRIDE, bool RANGED = true>
+__device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, long V, float c) {
   float mt = v[0][0];
 #pragma unroll
   for (int u = 0; u < N; ++u)
@@ -90,13 +97,27 @@ __device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, l
   if constexpr (MODE == GREEDY) {
     if (mt > s.best || s.idx == INT32_MAX) {
       int found = INT32_MAX;
+      if constexpr (RANGED) {
 #pragma unroll
-      for (int u = N - 1; u >= 0; --u)
+        for (int u = N - 1; u >= 0; --u)
 #pragma unroll
-        for (int j = 7; j >= 0; --j) {
-          const long e = (o0 + (long)u * ostride) * 8 + j;
-          if (e < V && v[u][j] == mt) found = (int)e;
+          for (int j = 7; j >= 0; --j) {
+            const long e = (o0 + (long)u * OSTRIDE) * 8 + j;
+            if (e < V && v[u][j] == mt) found = (int)e;
+          }
+      } else {
+        static_assert(N * 8 <= 64, "slot numbers must stay inline constants");
+        int slot = 64;
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+          int su = 64;
+#pragma unroll
+          for (int j = 7; j >= 0; --j)
+            if (v[u][j] == mt) su = u * 8 + j;
+          slot = min(slot, su);
         }
+        if (slot < 64) found = (int)(o0 * 8) + (slot >> 3) * (OSTRIDE * 8) + (slot & 7);
+      }
       if (found != INT32_MAX) { s.best = mt; s.idx = found; }
     }
   } else {
@@ -123,8 +144,12 @@ __device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, l
 // entry per wave.  VEC: V is a multiple of 8 and the rows are 16-byte
 // aligned, so the steady-state loop has no branches and issues all of a
 // step's loads before using any.  NT: non-temporal loads, for data read
-// exactly once (measured 10% faster than cached loads on gfx950).
-template <typename LT, int MODE, bool VEC, int THREADS, bool NT = true>
+// exactly once (measured 10% faster than cached loads on gfx950).  RANGED:
+// keep the bound-tested greedy search under VEC as well (same result); the
+// drafter kernel uses it: with the short search its sampled path measured
+// 11% slower, although that path's instructions stay the same; only the
+// kernel's scalar register count changes (98 -> 74).
+template <typename LT, int MODE, bool VEC, int THREADS, bool NT = true, bool RANGED = false>
 __device__ __forceinline__ Partial slice_stats(const LT* row, long o_lo, long o_hi, long V, float c,
                                float* sm_f, int* sm_i, double* sm_d) {
   constexpr int U = 16 / sizeof(LT);    // octets per step: 128 bytes in flight per thread
@@ -139,20 +164,20 @@ __device__ __forceinline__ Partial slice_stats(const LT* row, long o_lo, long o_
       float v[U][8];
 #pragma unroll
       for (int u = 0; u < U; ++u) unpack(raw[u], v[u]);
-      fold<MODE, U>(st, v, base, THREADS, V, c);
+      fold<MODE, U, THREADS, RANGED>(st, v, base, V, c);
     }
     for (; base < o_hi; base += THREADS) {
       Raw<LT> raw;
       raw_load<false>(row, base, raw);
       float v[1][8];
       unpack(raw, v[0]);
-      fold<MODE, 1>(st, v, base, THREADS, V, c);
+      fold<MODE, 1, THREADS, RANGED>(st, v, base, V, c);
     }
   } else {
     for (; base < o_hi; base += THREADS) {
       float v[1][8];
       load_octet<false>(row, base, V, false, -INFINITY, v[0]);
-      fold<MODE, 1>(st, v, base, THREADS, V, c);
+      fold<MODE, 1, THREADS>(st, v, base, V, c);
     }
   }
 
