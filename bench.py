@@ -87,11 +87,12 @@ def kernel_source_hash() -> str:
 
 
 def verify_bytes(B, K, V, zsize, acc, sample=True):
-    """Algorithmic HBM bytes of a verify call, split as (row kernel, scan kernel).
+    """Algorithmic HBM bytes of a verify call, split as (row kernel, the rest).
 
-    Row kernel: every logit row once.  Scan kernel: the draft tokens, the
-    outputs, and for sampling the q(d) / z(d) gathers, the uniforms,
-    p_k(d_k) and the drafter's row a_b of each sequence that rejects a draft.
+    Row kernel: every logit row once.  The rest (accept scan, and for sampling
+    the draw): the draft tokens, the outputs, and for sampling the q(d) / z(d)
+    gathers, the uniforms, p_k(d_k) and the drafter's row a_b of each sequence
+    that rejects a draft.
     The draw's second read of logit row a is not counted: the method reads
     every logit once."""
     rows = B * (K + 1) * V * zsize
@@ -652,10 +653,11 @@ def main():
         "step_bytes": vb_rows + vb_draw + bb,
         "kernels": {
             "verify_sample_rows": kinfo("verify_sample_rows", vb_rows),
-            "verify_sample_accept": kinfo("verify_sample_accept", vb_draw - int((acc < K).sum()) * V * 4),
-            "verify_sample_draw": kinfo("verify_sample_draw", int((acc < K).sum()) * V * 4,
-                                        "algorithmic bytes count the drafter rows a_b; the kernel "
-                                        "also re-reads logit row a"),
+            "verify_sample_draw": kinfo("verify_sample_draw", vb_draw,
+                                        "the accept scan, then the residual tile masses; "
+                                        "algorithmic bytes count the scan's reads and writes "
+                                        "once and the drafter rows a_b; the kernel also "
+                                        "re-reads logit row a"),
             "verify_sample_locate": kinfo("verify_sample_locate", B * 4),
             "peagle_build": kinfo("peagle_build", bb),
         },

@@ -106,9 +106,9 @@ def _check(status: int, what: str):
 
 # ---------------------------------------------------------------- tracing
 KERNEL_IDS = {"verify_greedy_rows": 0, "verify_sample_rows": 1, "verify_sample_draw": 2,
-              "peagle_build": 3, "verify_greedy_accept": 4, "verify_sample_accept": 5,
-              "verify_sample_locate": 6, "draft_sample": 7, "verify_mixed_rows": 8,
-              "verify_mixed_accept": 9, "accept_metrics": 10, "tree_rows": 11, "tree_walk": 12}
+              "peagle_build": 3, "verify_greedy_accept": 4, "verify_sample_locate": 5,
+              "draft_sample": 6, "verify_mixed_rows": 7, "accept_metrics": 8, "tree_rows": 9,
+              "tree_walk": 10}
 
 
 def trace_begin(capacity: int, kernels=None):

@@ -86,11 +86,9 @@ SV_API const char* sv_kernel_name(int kernel_id) {
     case SV_KERNEL_VERIFY_SAMPLE_DRAW: return "verify_sample_draw";
     case SV_KERNEL_PEAGLE_BUILD: return "peagle_build";
     case SV_KERNEL_VERIFY_GREEDY_ACCEPT: return "verify_greedy_accept";
-    case SV_KERNEL_VERIFY_SAMPLE_ACCEPT: return "verify_sample_accept";
     case SV_KERNEL_VERIFY_SAMPLE_LOCATE: return "verify_sample_locate";
     case SV_KERNEL_DRAFT_SAMPLE: return "draft_sample";
     case SV_KERNEL_VERIFY_MIXED_ROWS: return "verify_mixed_rows";
-    case SV_KERNEL_VERIFY_MIXED_ACCEPT: return "verify_mixed_accept";
     case SV_KERNEL_ACCEPT_METRICS: return "accept_metrics";
     case SV_KERNEL_TREE_ROWS: return "tree_rows";
     case SV_KERNEL_TREE_WALK: return "tree_walk";

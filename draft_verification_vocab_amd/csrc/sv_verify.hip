@@ -112,7 +112,7 @@ struct ScanArgs {          // what an accept scan reads and writes
   float c;
   int B, K, V, S;
   Partial* partials;       // [B][K+1][S]
-  ScanResult* info;        // [B] sampling: handed to verify_draw
+  ScanResult* info;        // [B] written by verify_draw, read by verify_locate
   int32_t* out_tokens;
   int32_t* out_num_accepted;
   float* out_p_draft;
@@ -242,33 +242,48 @@ __device__ __forceinline__ ScanResult accept_scan(const ScanArgs& A, int b, bool
   return r;
 }
 
-// One wave per sequence runs the accept scan.  Greedy: writes g_a as the new
-// token.  Sampling: hands (a, M_a, s_a) to verify_draw.
-template <typename LT, int MODE, bool QL>
+// The row partials of sequence b are consumed: clear them (one wave), so the
+// workspace ends all zero.
+__device__ __forceinline__ void clear_partials(const ScanArgs& A, int b) {
+  Partial* Pb = A.partials + (long)b * (A.K + 1) * A.S;
+  for (int i = lane_id(); i < (A.K + 1) * A.S; i += kWave) Pb[i] = Partial{0.f, 0, 0.0};
+}
+
+// Greedy verify: one wave per sequence runs the accept scan and writes g_a as
+// the new token.  (Sampling and mixed batches run the scan inside verify_draw.)
+template <typename LT>
 __global__ __launch_bounds__(kThreads) void verify_accept(ScanArgs A) {
   const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
   if (b >= A.B) return;
   const int l = lane_id();
+  const ScanResult r = accept_scan<LT, GREEDY>(A, b, true, 1.f);
+  if (l == 0) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
+  clear_partials(A, b);
+}
+
+// The accept scan of sequence b as the draw needs it, by one full wave.  Every
+// draw workgroup of b runs it (it reads the row partials and two values per
+// draft, a few hundred bytes); the workgroup of chunk 0 (`write`) also writes
+// the accept outputs, the greedy token of a greedy sequence of a mixed batch,
+// and the result for verify_locate.
+template <typename LT, int MODE, bool QL>
+__device__ __forceinline__ ScanResult draw_scan(const ScanArgs& A, int b, bool write) {
+  ScanResult r;
   if constexpr (MODE == MIXED) {
     bool bad;
     const float c = seq_scale(A.temperatures[b], bad);
-    if (bad && l == 0) flag_error(A.device_error, SV_DEVERR_TEMPERATURE);
-    const ScanResult r = c == 0.f ? accept_scan<LT, GREEDY>(A, b, true, 1.f)
-                                  : accept_scan<LT, SAMPLE, QL>(A, b, true, c);
-    if (l == 0) {
-      if (c == 0.f) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
-      A.info[b] = r;                      // c = 0 tells the draw to skip it
+    if (write && bad && lane_id() == 0) flag_error(A.device_error, SV_DEVERR_TEMPERATURE);
+    if (c == 0.f) {
+      r = accept_scan<LT, GREEDY>(A, b, write, 1.f);          // r.c = 0: nothing to draw
+      if (write && lane_id() == 0) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
+    } else {
+      r = accept_scan<LT, SAMPLE, QL>(A, b, write, c);
     }
   } else {
-    const ScanResult r = accept_scan<LT, MODE, QL>(A, b, true, A.c);
-    if (l == 0) {
-      if constexpr (MODE == GREEDY) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
-      else A.info[b] = r;
-    }
+    r = accept_scan<LT, SAMPLE, QL>(A, b, write, A.c);
   }
-  // the partials are consumed: clear them so the workspace ends all zero
-  Partial* Pb = A.partials + (long)b * (A.K + 1) * A.S;
-  for (int i = l; i < (A.K + 1) * A.S; i += kWave) Pb[i] = Partial{0.f, 0, 0.0};
+  if (write && lane_id() == 0) A.info[b] = r;                // read by verify_locate
+  return r;
 }
 
 // ----------------------------------------------------------------------------
@@ -285,8 +300,7 @@ struct DrawRow {
 };
 
 template <typename LT, bool QL>
-__device__ __forceinline__ DrawRow<LT> draw_row(const DrawArgs& A, int b) {
-  const ScanResult scan = A.sc.info[b];       // written by verify_accept
+__device__ __forceinline__ DrawRow<LT> draw_row(const DrawArgs& A, int b, const ScanResult& scan) {
   const int K = A.sc.K;
   const long V = A.sc.V;
   DrawRow<LT> r;
@@ -393,16 +407,23 @@ __device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool resid
   return ls;
 }
 
-// verify_draw: chunk cidx of sequence b stores the mass of each of its
-// tiles.  A tile is kTileLoads consecutive 512-element wave loads; each lane
-// sums its octets of the tile before one wave reduction.
-template <typename LT, bool VEC, bool QL>
+// verify_draw: wave 0 of every workgroup runs sequence b's accept scan
+// (chunk 0 writes its outputs); then chunk cidx of b stores the mass of each
+// of its tiles.  A tile is kTileLoads consecutive 512-element wave loads;
+// each lane sums its octets of the tile before one wave reduction.
+template <typename LT, int MODE, bool VEC, bool QL>
 __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
+  __shared__ ScanResult scan;
   const int C = A.C, T = A.T;
   const int b = blockIdx.x / C, cidx = blockIdx.x % C;
   const long V = A.sc.V;
   const long nocts = (V + 7) / 8;
-  const DrawRow<LT> R = draw_row<LT, QL>(A, b);
+  if (threadIdx.x < kWave) {
+    const ScanResult r = draw_scan<LT, MODE, QL>(A.sc, b, cidx == 0);
+    if (threadIdx.x == 0) scan = r;
+  }
+  __syncthreads();
+  const DrawRow<LT> R = draw_row<LT, QL>(A, b, scan);
   if (R.c == 0.f) return;                     // greedy: its token is already written
   const bool residual = R.residual;
   float* tsum_g = A.tile_sums + (long)b * T;
@@ -441,7 +462,8 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
   float ts[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) ts[j] = lo + j < hi ? ld_coherent(&tsum_g[lo + j]) : 0.f;
-  const DrawRow<LT> R = draw_row<LT, QL>(A, b);
+  const DrawRow<LT> R = draw_row<LT, QL>(A, b, A.sc.info[b]);   // written by verify_draw
+  clear_partials(A.sc, b);                    // every draw workgroup of b has read them
   if (R.c == 0.f) {                           // greedy: nothing to draw
     if (l == 0) A.sc.info[b] = ScanResult{0, 0, 0.f, 0.f, 0.0};
     return;
@@ -549,9 +571,6 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   const dim3 block(kThreads);
   const int rows_id = mode == MIXED ? SV_KERNEL_VERIFY_MIXED_ROWS
                     : mode == SAMPLE ? SV_KERNEL_VERIFY_SAMPLE_ROWS : SV_KERNEL_VERIFY_GREEDY_ROWS;
-  const int accept_id = mode == MIXED ? SV_KERNEL_VERIFY_MIXED_ACCEPT
-                      : mode == SAMPLE ? SV_KERNEL_VERIFY_SAMPLE_ACCEPT
-                                       : SV_KERNEL_VERIFY_GREEDY_ACCEPT;
 
   RowsArgs R;
   R.logits = L.logits;
@@ -597,52 +616,51 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   sc.out_num_accepted = L.out_num_accepted;
   sc.out_p_draft = L.out_p_draft;
   sc.device_error = L.device_error;
-
   sc.info = reinterpret_cast<ScanResult*>(ws + lay.info);
   const dim3 grid_acc((unsigned)((L.B + kWaves - 1) / kWaves));
-  trace_before(stream, accept_id);
-#define SV_ACCEPT(LT, MODE) hipLaunchKernelGGL((verify_accept<LT, MODE, false>), grid_acc, block, 0, stream, sc)
-  if (ql) {
-    if (L.bf16) hipLaunchKernelGGL((verify_accept<uint16_t, SAMPLE, true>), grid_acc, block, 0, stream, sc);
-    else hipLaunchKernelGGL((verify_accept<float, SAMPLE, true>), grid_acc, block, 0, stream, sc);
-  } else if (L.bf16) {
-    SV_BY_MODE(SV_ACCEPT, uint16_t);
-  } else {
-    SV_BY_MODE(SV_ACCEPT, float);
-  }
-#undef SV_ACCEPT
 #undef SV_BY_MODE
 #undef SV_ROWS
-  err = hipGetLastError();
-  trace_after(stream, accept_id);
-  if (err != hipSuccess || mode == GREEDY) return err;
+  if (mode == GREEDY) {
+    trace_before(stream, SV_KERNEL_VERIFY_GREEDY_ACCEPT);
+    if (L.bf16) hipLaunchKernelGGL((verify_accept<uint16_t>), grid_acc, block, 0, stream, sc);
+    else hipLaunchKernelGGL((verify_accept<float>), grid_acc, block, 0, stream, sc);
+    err = hipGetLastError();
+    trace_after(stream, SV_KERNEL_VERIFY_GREEDY_ACCEPT);
+    return err;
+  }
 
+  // sampling and mixed batches: the draw kernel runs the accept scan itself
   DrawArgs D;
   D.sc = sc;
   D.C = lay.C; D.T = lay.T;
   D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
   const dim3 grid3((unsigned)((long)L.B * lay.C));
-#define SV_DRAW_KERNELS(KERNEL, GRID) \
+#define SV_DRAW_KERNELS(LAUNCH) \
   do { \
     if (L.bf16) { \
-      if (L.vec) { if (ql) hipLaunchKernelGGL((KERNEL<uint16_t, true, true>), GRID, block, 0, stream, D); \
-                   else hipLaunchKernelGGL((KERNEL<uint16_t, true, false>), GRID, block, 0, stream, D); } \
-      else { if (ql) hipLaunchKernelGGL((KERNEL<uint16_t, false, true>), GRID, block, 0, stream, D); \
-             else hipLaunchKernelGGL((KERNEL<uint16_t, false, false>), GRID, block, 0, stream, D); } \
+      if (L.vec) { if (ql) LAUNCH(uint16_t, true, true); else LAUNCH(uint16_t, true, false); } \
+      else { if (ql) LAUNCH(uint16_t, false, true); else LAUNCH(uint16_t, false, false); } \
     } else { \
-      if (L.vec) { if (ql) hipLaunchKernelGGL((KERNEL<float, true, true>), GRID, block, 0, stream, D); \
-                   else hipLaunchKernelGGL((KERNEL<float, true, false>), GRID, block, 0, stream, D); } \
-      else { if (ql) hipLaunchKernelGGL((KERNEL<float, false, true>), GRID, block, 0, stream, D); \
-             else hipLaunchKernelGGL((KERNEL<float, false, false>), GRID, block, 0, stream, D); } \
+      if (L.vec) { if (ql) LAUNCH(float, true, true); else LAUNCH(float, true, false); } \
+      else { if (ql) LAUNCH(float, false, true); else LAUNCH(float, false, false); } \
     } \
   } while (0)
+  // q from the drafter logits comes with uniform-temperature sampling only
+#define SV_DRAW(LT, VEC, QL) \
+  do { \
+    if (mode == MIXED && !QL) hipLaunchKernelGGL((verify_draw<LT, MIXED, VEC, false>), grid3, block, 0, stream, D); \
+    else hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, QL>), grid3, block, 0, stream, D); \
+  } while (0)
+#define SV_LOCATE(LT, VEC, QL) hipLaunchKernelGGL((verify_locate<LT, VEC, QL>), grid_acc, block, 0, stream, D)
   trace_before(stream, SV_KERNEL_VERIFY_SAMPLE_DRAW);
-  SV_DRAW_KERNELS(verify_draw, grid3);
+  SV_DRAW_KERNELS(SV_DRAW);
   err = hipGetLastError();
   trace_after(stream, SV_KERNEL_VERIFY_SAMPLE_DRAW);
   if (err != hipSuccess) return err;
   trace_before(stream, SV_KERNEL_VERIFY_SAMPLE_LOCATE);
-  SV_DRAW_KERNELS(verify_locate, grid_acc);
+  SV_DRAW_KERNELS(SV_LOCATE);
+#undef SV_LOCATE
+#undef SV_DRAW
 #undef SV_DRAW_KERNELS
   err = hipGetLastError();
   trace_after(stream, SV_KERNEL_VERIFY_SAMPLE_LOCATE);

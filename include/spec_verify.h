@@ -446,18 +446,17 @@ SV_API void sv_step_graph_destroy(sv_step_graph* graph);
  */
 #define SV_KERNEL_VERIFY_GREEDY_ROWS 0   /* spec_verify_greedy: row max / argmax         */
 #define SV_KERNEL_VERIFY_SAMPLE_ROWS 1   /* spec_verify_sample: row max / sum of exp     */
-#define SV_KERNEL_VERIFY_SAMPLE_DRAW 2   /* spec_verify_sample: residual / bonus masses  */
+#define SV_KERNEL_VERIFY_SAMPLE_DRAW 2   /* spec_verify_sample / _mixed / _lq: the accept
+                                            scan, then residual / bonus tile masses      */
 #define SV_KERNEL_PEAGLE_BUILD 3         /* peagle_build_draft_batch                     */
 #define SV_KERNEL_VERIFY_GREEDY_ACCEPT 4 /* spec_verify_greedy: accept scan              */
-#define SV_KERNEL_VERIFY_SAMPLE_ACCEPT 5 /* spec_verify_sample: accept scan              */
-#define SV_KERNEL_VERIFY_SAMPLE_LOCATE 6 /* spec_verify_sample: locate the drawn token   */
-#define SV_KERNEL_DRAFT_SAMPLE 7         /* spec_draft_sample                            */
-#define SV_KERNEL_VERIFY_MIXED_ROWS 8    /* spec_verify_mixed: row statistics            */
-#define SV_KERNEL_VERIFY_MIXED_ACCEPT 9  /* spec_verify_mixed: accept scan (its draw and
-                                            locate kernels carry ids 2 and 6)            */
-#define SV_KERNEL_ACCEPT_METRICS 10      /* spec_accept_metrics                          */
-#define SV_KERNEL_TREE_ROWS 11           /* spec_verify_tree: row statistics             */
-#define SV_KERNEL_TREE_WALK 12           /* spec_verify_tree: the walk down the tree     */
+#define SV_KERNEL_VERIFY_SAMPLE_LOCATE 5 /* spec_verify_sample / _mixed / _lq: locate the
+                                            drawn token                                  */
+#define SV_KERNEL_DRAFT_SAMPLE 6         /* spec_draft_sample                            */
+#define SV_KERNEL_VERIFY_MIXED_ROWS 7    /* spec_verify_mixed: row statistics            */
+#define SV_KERNEL_ACCEPT_METRICS 8       /* spec_accept_metrics                          */
+#define SV_KERNEL_TREE_ROWS 9            /* spec_verify_tree: row statistics             */
+#define SV_KERNEL_TREE_WALK 10           /* spec_verify_tree: the walk down the tree     */
 
 SV_API const char* sv_kernel_name(int kernel_id);
 SV_API sv_status sv_trace_begin(int capacity, unsigned kernel_mask); /* SV_ERR_VALUE if capacity < 1 */

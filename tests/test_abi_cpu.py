@@ -180,11 +180,12 @@ def test_tracer_host_paths(lib):
     assert lib.sv_trace_read(0, None, None) == ENULL
     import draft_verification_vocab_amd as sv
     assert all(lib.sv_kernel_name(i).decode() == n for n, i in sv.KERNEL_IDS.items())
-    names = [lib.sv_kernel_name(i) for i in range(13)]
+    names = [lib.sv_kernel_name(i) for i in range(11)]
     assert names == [b"verify_greedy_rows", b"verify_sample_rows", b"verify_sample_draw",
-                     b"peagle_build", b"verify_greedy_accept", b"verify_sample_accept",
-                     b"verify_sample_locate", b"draft_sample", b"verify_mixed_rows",
-                     b"verify_mixed_accept", b"accept_metrics", b"tree_rows", b"tree_walk"]
+                     b"peagle_build", b"verify_greedy_accept", b"verify_sample_locate",
+                     b"draft_sample", b"verify_mixed_rows", b"accept_metrics", b"tree_rows",
+                     b"tree_walk"]
+    assert lib.sv_kernel_name(11) == b"unknown"
     assert lib.sv_kernel_name(17) == b"unknown"
     lib.sv_trace_end()                              # harmless when tracing is off
 
