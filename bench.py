@@ -315,8 +315,9 @@ def graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt, hid, hs
                 pd_t, ws, bouts):
     """The fused sampled step (verify, build, acceptance metrics) replayed as
     one captured HIP graph vs the same calls launched one by one, at the full
-    batch and at a small batch (the first 16 sequences) where launches
-    dominate; the metrics counters give the acceptance figures."""
+    batch and at small batches (the first 16 sequences, the first one) where
+    launches and the kernels' own latency dominate; the metrics counters give
+    the acceptance figures."""
     def run(nb):
         zz, qq, dd, uu = z[:nb], q[:nb], d[:nb], u[:nb]
         oo = {k: (v[:nb * 2 * K] if k != "sample_rows" else v[:nb]) for k, v in bouts.items()}
@@ -358,7 +359,7 @@ def graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt, hid, hs
                                                       "draft_acceptance_rate")}
         return out
     return {"note": "verify_sample + P-EAGLE build + acceptance metrics per step",
-            "full": run(B), "small": run(16)}
+            "full": run(B), "small": run(16), "single": run(1)}
 
 
 def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, out_t, acc_t,

@@ -6,14 +6,16 @@
 // of exponentials relative to it (sampling).  Nothing else: no workgroup of
 // this kernel waits for or hands anything to another.
 //
-// verify_accept: one wave per sequence (one lane per row) combines the
+// The accept scan: one wave per sequence (one lane per row) combines the
 // sequence's partials, tests every draft in parallel and takes the first
-// rejection from a wave ballot.  Greedy: it writes the argmax of row a as the
-// new token.  Sampling: it leaves (a, max and sum of row a) for the draw.
+// rejection from a wave ballot.  Greedy verify runs it in verify_accept,
+// which writes the argmax of row a as the new token.
 //
-// verify_draw (sampling): C workgroups per sequence each take a contiguous
-// chunk of row a and store the mass r = max(0, p_a - q_a) (or p_K for the
-// bonus token) of each 2048-element tile in it.
+// verify_draw (sampling, mixed batches): C workgroups per sequence each run
+// the accept scan (chunk 0 writes its outputs and leaves a, max and sum of
+// row a for the locate kernel), then take a contiguous chunk of row a and
+// store the mass r = max(0, p_a - q_a) (or p_K for the bonus token) of each
+// 2048-element tile in it.
 // verify_locate: one wave per sequence finds the tile whose running total
 // first exceeds u * S, rescans that one tile and writes the token.  Every
 // hand-off between workgroups goes through a kernel boundary.
