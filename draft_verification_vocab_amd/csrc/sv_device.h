@@ -111,15 +111,13 @@ __device__ __forceinline__ void flag_error(int32_t* device_error, int bit) {
   if (device_error) atomicOr(device_error, bit);
 }
 
-// ---------------------------------------------------------------- cross-workgroup hand-off
-// Workgroups of one launch hand results to each other through device memory.
-// The results are written and read with agent-scope atomic stores and loads,
-// which the gfx94x/gfx950 memory model keeps coherent across the XCDs' L2
-// caches by themselves; the writer waits for its stores to be performed
-// (vmcnt(0)) before it takes a ticket with an agent-scope atomic add, and the
-// reader only reads after the ticket told it every writer has arrived.  This
-// avoids the L2 write-back / invalidate that an agent-scope release / acquire
-// fence costs on every workgroup.
+// ---------------------------------------------------------------- coherent access
+// Agent-scope relaxed atomic stores and loads bypass the non-coherent
+// per-CU vector cache (and are kept coherent across the XCDs' L2 caches by
+// the gfx94x/gfx950 memory model), so a wave that rewrites values and reads
+// them back, or reads values another launch wrote, never sees a stale cached
+// copy; wait_stores_performed makes a wave wait until its stores are done.
+// None of them needs a cache write-back or invalidate instruction.
 template <typename T>
 __device__ __forceinline__ void st_coherent(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -132,9 +130,6 @@ __device__ __forceinline__ void wait_stores_performed() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt / lgkmcnt untouched
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-__device__ __forceinline__ int take_ticket(int* p) {
-  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace sv
