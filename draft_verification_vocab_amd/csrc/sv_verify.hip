@@ -346,18 +346,19 @@ __device__ __forceinline__ void octet_mass(const DrawRow<LT>& R, long o, long V,
   if constexpr (VEC) {
     const bool in = o < nocts;
     const long oc = in ? o : nocts - 1;
-    // Logit row a: cached loads; dense q row: non-temporal loads.  Measured
-    // over whole steps: the draw alone is 6% faster the other way round, but
-    // the next step's row kernel then runs 14 us slower; this split is ~5 us
-    // faster per sampled step (and 2 us faster than all non-temporal).
+    // Every row here is read once per step: non-temporal loads.  Measured
+    // over whole sampled steps (verify + build) at B=1024, V=151936: 541 us,
+    // against 546 us with cached logit loads (their 311 MB evict from the
+    // Infinity Cache the hidden states the build reads next, +6 us there)
+    // and 550 us with cached q loads.
     Raw<LT> rz;
-    raw_load<false>(R.zrow, oc, rz);
+    raw_load<true>(R.zrow, oc, rz);
     unpack(rz, z);
     if (residual) {
       if constexpr (QL) {
         if (R.dzrow) {
           Raw<LT> rd;
-          raw_load<false>(R.dzrow, oc, rd);
+          raw_load<true>(R.dzrow, oc, rd);
           float dz[8];
           unpack(rd, dz);
 #pragma unroll
