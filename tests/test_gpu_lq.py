@@ -5,8 +5,10 @@ descriptor; spec_verify_sample on the dense q and spec_verify_sample_lq on
 the drafter logits + descriptors must then agree bit for bit (tokens, accept
 counts, p_k(d_k)).  The lq results are also checked against the oracle: q from
 oracle.draft.draft_probs, then the sampled-verify oracle with its near-tie
-tolerance.  Covered: the 151936-token bf16 shape, ragged fp32 rows gathered
-through a row index with greedy-drafted sequences, and invalid drafter rows.
+tolerance.  Covered: the 151936-token bf16 shape; a ragged bf16 vocabulary
+with drafter rows gathered through a row index, greedy-drafted sequences and
+invalid drafter rows; fp32 logits at a vocabulary that is a multiple of 8 and
+one that is not (rows gathered through a row index); no drafts at all.
 """
 import numpy as np
 import pytest
@@ -93,6 +95,37 @@ def test_lq_gathered_rows_greedy_drafts_and_bad_rows(gpu):
     assert int(err_d.item()) == gpu.DEVERR_ROW_INDEX
     assert int(err_v.item()) == gpu.DEVERR_ROW_INDEX
     _same(a1, a2)
+
+
+@pytest.mark.parametrize("V", [4096, 1001])
+def test_lq_fp32(gpu, V):
+    B, K, R = 6, 4, 40
+    rng = np.random.default_rng(93 + V)
+    z = (2.5 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    # drafter rows: the target rows plus noise, stored in shuffled order
+    rows = rng.permutation(R)[:B * K].reshape(B, K).astype(np.int32)
+    zd = (2.5 * rng.standard_normal((R, V))).astype(np.float32)
+    zd[rows] = z[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32)
+    ud = rng.random((B, K), dtype=np.float32)
+    uv = rng.random((B, K + 1), dtype=np.float32)
+    Td, T = 1.1, 0.8
+    tok, q, desc, dense, lq = _chain(gpu, dev(z), dev(zd), K, Td, T, dev(ud), dev(uv),
+                                     rows=dev(rows))
+    _same(dense, lq)
+    out, acc, pd = (x.cpu().numpy() for x in lq)
+    tok = tok.cpu().numpy()
+    oq = oracle.draft.draft_probs(zd, "f32", Td, B, K, row_index=rows)
+    checked = 0
+    for b in range(B):
+        od = [oracle.draft.draft_sample_row(zd[rows[b, k]].astype(np.float64),
+                                            float(np.float32(Td)), ud[b, k])[0]
+              for k in range(K)]
+        if list(tok[b]) != od:
+            continue                      # a flagged near tie in the draft itself
+        check_sample_sequence(z[b].astype(np.float64), oq[b], tok[b], uv[b], float(np.float32(T)),
+                              out[b], acc[b], pd[b])
+        checked += 1
+    assert checked >= B - 1
 
 
 def test_lq_without_drafts(gpu):
