@@ -51,6 +51,20 @@ def test_mixed_workloads(gpu, cfg):
     _mixed_parity(gpu, vi, temps)
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 1001), ("f32", 4099)])
+def test_mixed_ragged_vocabulary(gpu, dtype, V):
+    """A vocabulary that is not a multiple of 8 (the unvectorised kernels)."""
+    from types import SimpleNamespace
+    from tests.test_gpu_verify import _random_case
+    B, K = 10, 4
+    rng = np.random.default_rng(V)
+    logits, q, d, u = _random_case(rng, B, K, V, dtype, T=0.8)
+    vi = SimpleNamespace(logits=logits, draft_probs=q, draft_tokens=d, uniforms=u,
+                         spec=SimpleNamespace(B=B, dtype=dtype))
+    temps = np.array([0.0, 0.5, 0.7, 1.0, 1.3, 0.0, 0.8, 0.0, 2.0, 0.6], dtype=np.float32)
+    _mixed_parity(gpu, vi, temps)
+
+
 def test_every_sequence_mode_in_one_batch(gpu):
     # workload 2 has 8 sequences: give them every kind of temperature
     vi = synth.make_verify_inputs(synth.verify_config(2))

@@ -4,8 +4,9 @@ Greedy trees are compared exactly (tokens, node path, accept length).
 Sampled trees: the GPU's (path, new token) must be the oracle's, or one the
 oracle lists when a test lies within 1e-6 of its threshold or the final draw
 within 1e-6 of a CDF boundary (oracle.tree.tree_outcomes).  Covered: random,
-static and chain trees; fp32 and bf16; V up to 151936; a root without
-children; invalid nodes; determinism and a clean workspace.
+static and chain trees; fp32 and bf16, each also with a vocabulary that is
+not a multiple of 8; V up to 151936; a root without children; invalid
+nodes; determinism and a clean workspace.
 """
 import numpy as np
 import pytest
@@ -142,3 +143,13 @@ def test_max_nodes_random_trees(gpu):
     ti = make_tree_inputs(spec, workers=1)
     _check_greedy(ti, *_run(gpu, ti, 0.0))
     _check_sample(ti, 1.0, *_run(gpu, ti, 1.0))
+
+
+def test_bf16_ragged_vocabulary_trees(gpu):
+    """bf16 logits with a vocabulary that is not a multiple of 8."""
+    from synth.workloads import TreeSpec
+    spec = TreeSpec("tree-ragged", 6, 9, 30011, "bf16", 3.0, "zipf-head", 0.7, 1.0, 0.7,
+                    "static", (3, 2), 26)
+    ti = make_tree_inputs(spec, workers=1)
+    _check_greedy(ti, *_run(gpu, ti, 0.0))
+    _check_sample(ti, ti.temperature, *_run(gpu, ti, ti.temperature))
