@@ -77,7 +77,10 @@ def test_ragged_vocabularies(gpu, V, dtype):
         z[:, rng.integers(0, V, size=3)] = -np.inf
     logits = synth.f32_to_bf16_bits(z) if dtype == "bf16" else z
     u = rng.random((B, K), dtype=np.float32)
-    _parity(gpu, logits, dtype, u, 0.8, B, K)
+    tok, _ = _parity(gpu, logits, dtype, u, 0.8, B, K)
+    # the tokens-only kernel (no q written) draws the same tokens
+    tok2, _ = _parity(gpu, logits, dtype, u, 0.8, B, K, want_q=False)
+    assert np.array_equal(tok, tok2)
 
 
 def test_greedy_drafting_ties_and_no_uniforms(gpu):
@@ -89,6 +92,8 @@ def test_greedy_drafting_ties_and_no_uniforms(gpu):
         z[r, idx] = 10.0
     tok, q = _parity(gpu, z, "f32", None, 0.0, B, K)
     assert np.all(q.sum(axis=2) == 1.0) and np.all(q.max(axis=2) == 1.0)
+    tok2, _ = _parity(gpu, z, "f32", None, 0.0, B, K, want_q=False)
+    assert np.array_equal(tok, tok2)
 
 
 def test_invalid_rows_and_temperatures(gpu):
