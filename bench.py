@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_verify_sample_fused_b1024.json")
+CEILING_LIB = os.path.join(ROOT, "draft_verification_vocab_amd", "libsvceiling.so")
 
 
 @contextlib.contextmanager
@@ -226,7 +227,7 @@ def ingest_counters(fetch_csv, write_csv):
     kernels = {}
     for key in sorted(fetch, key=lambda k: (k[0], -k[1])):
         name, grid = key
-        if not name.startswith(("void sv::", "sv::")):
+        if not (name.startswith(("void sv::", "sv::")) or "stream_read<" in name):
             continue
         f = sum(fetch[key]) / len(fetch[key]) * f_scale
         w = sum(write.get(key, [0.0])) / max(1, len(write.get(key, []))) * w_scale
@@ -297,7 +298,8 @@ def ingest_valu(valu_csv):
              "| kernel [grid] | VALU instr | of which exp (fp32 transcendental) | duration µs | exp/s | ALU load at 2.4 GHz |",
              "|---|---|---|---|---|---|"]
     for (name, grid), c in sorted(per.items()):
-        if not name.startswith(("void sv::", "sv::")) or not c["SQ_INSTS_VALU"]:
+        if not (name.startswith(("void sv::", "sv::")) or "stream_read<" in name) \
+                or not c["SQ_INSTS_VALU"]:
             continue
         valu = sum(c["SQ_INSTS_VALU"]) / len(c["SQ_INSTS_VALU"])
         tr = sum(c["SQ_INSTS_VALU_TRANS_F32"]) / max(1, len(c["SQ_INSTS_VALU_TRANS_F32"]))
@@ -309,6 +311,41 @@ def ingest_valu(valu_csv):
     with open(md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(md)
+
+
+def _stream_read_fn():
+    import ctypes
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} is not built (run __graft_entry__.build())")
+    fn = ctypes.CDLL(CEILING_LIB).svc_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    return fn
+
+
+def read_ceiling(torch, buf, reps):
+    """The read rate of a plain streaming kernel over the same resident device
+    buffer (8192 workgroups, 8 16-byte loads in flight per lane, nothing
+    stored), with non-temporal and with cached loads: the practical ceiling
+    the row kernel is held against, beside the nominal peak."""
+    fn = _stream_read_fn()
+    nbytes = buf.numel() * buf.element_size()
+    stream = torch.cuda.current_stream()
+    out = {"bytes": nbytes,
+           "kernel": "plain streaming read: 8192 workgroups x 256 threads, 8 x 16-byte loads "
+                     "in flight per thread, one pass over the logit buffer"}
+    for nt, key in ((1, "nontemporal_gbs"), (0, "cached_gbs")):
+        for _ in range(3):
+            if fn(buf.data_ptr(), nbytes, nt, stream.cuda_stream):
+                raise RuntimeError("svc_stream_read failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn(buf.data_ptr(), nbytes, nt, stream.cuda_stream)
+        e1.record(stream)
+        e1.synchronize()
+        out[key] = nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    return out
 
 
 def graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt, hid, hs, out_t, acc_t,
@@ -581,6 +618,13 @@ def main():
             for T in (0.0, ts.temperature):
                 sv.spec_verify_tree(tz, tp, tt, T, draft_probs=tq, uniforms=tu)
         torch.cuda.synchronize()
+        # the read-ceiling kernel over the logit buffer, non-temporal and cached
+        rd = _stream_read_fn()
+        for nt in (1, 0):
+            if rd(z.data_ptr(), z.numel() * z.element_size(), nt,
+                  torch.cuda.current_stream().cuda_stream):
+                raise RuntimeError("svc_stream_read failed")
+        torch.cuda.synchronize()
         # calibration for HBM byte counters: one plain copy of 1 GiB
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -590,7 +634,8 @@ def main():
             os.makedirs(os.path.dirname(os.path.abspath(args.hash_out)), exist_ok=True)
             with open(args.hash_out, "w") as f:
                 f.write(kernel_source_hash() + "\n")
-        print(f"profiled {args.profile_steps} steps of every kernel family and a 1 GiB copy",
+        print(f"profiled {args.profile_steps} steps of every kernel family, the read-ceiling "
+              "kernel and a 1 GiB copy",
               flush=True)
         return
 
@@ -672,9 +717,13 @@ def main():
             tr = json.load(f)
         if tr.get("source_hash") == kernel_source_hash():
             traffic = tr.get("hbm_bytes_per_launch")
+    ceil = read_ceiling(torch, z, 20)
     res["roofline"] = {"bound": "hbm", "achieved": rk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": rk["frac"], "traffic": traffic, "kernel": "verify_sample_rows",
-                       "algorithmic_bytes": vb_rows, "avg_ms": rk["avg_ms"]}
+                       "algorithmic_bytes": vb_rows, "avg_ms": rk["avg_ms"],
+                       "read_ceiling_gbs": ceil["nontemporal_gbs"],
+                       "frac_of_read_ceiling": rk["gbs"] / ceil["nontemporal_gbs"]}
+    res["read_ceiling"] = ceil
     log("sampled step timed")
     if not args.no_greedy:
         sec_g, kmsg, accg = timed(False)

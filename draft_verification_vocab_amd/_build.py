@@ -1,4 +1,6 @@
-"""Compile libspecverify.so (all HIP sources under csrc/) for gfx950, in tree."""
+"""Compile libspecverify.so (all HIP sources under csrc/) for gfx950, in tree,
+and libsvceiling.so (ceiling/read_ceiling.hip: the plain streaming-read kernel
+bench.py times as the practical HBM read ceiling)."""
 from __future__ import annotations
 
 import glob
@@ -8,6 +10,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libspecverify.so")
+CEILING_LIB = os.path.join(HERE, "libsvceiling.so")
+CEILING_SRC = os.path.join(HERE, "ceiling", "read_ceiling.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -23,10 +27,9 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompile; returns the path of the library."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *sources(), "-o", tmp]
+def _compile(srcs, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,7 +39,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompile both libraries; returns the path of the verify library."""
+    _compile(sources(), LIB, verbose)
+    _compile([CEILING_SRC], CEILING_LIB, verbose)
     return LIB
 
 

@@ -10,6 +10,8 @@
   several workloads are kept apart by grid size, the dominant kernel is the
   sampled row kernel of the largest grid, and counters recorded on other
   kernel sources are refused.
+* The read-ceiling library loads without a GPU and refuses invalid
+  arguments before launching anything.
 """
 import csv
 import json
@@ -30,6 +32,21 @@ FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id",
           "Counter_Value", "Start_Timestamp", "End_Timestamp"]
 ROWS_S = "void sv::verify_rows<unsigned short, 1, true>(sv::RowsArgs)"
 COPY = "__amd_rocclr_copyBuffer"
+
+
+def test_read_ceiling_library_exports_and_rejects_bad_arguments():
+    """The streaming-read kernel's library loads without a GPU; invalid
+    arguments are refused before anything is launched."""
+    import ctypes
+    if not os.path.exists(bench.CEILING_LIB):
+        pytest.skip("libsvceiling.so is not built")
+    fn = ctypes.CDLL(bench.CEILING_LIB).svc_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    assert fn(None, 1024, 1, None) == 1                   # no buffer
+    assert fn(16, 0, 1, None) == 1                        # no bytes
+    assert fn(16, 1000, 0, None) == 1                     # not a multiple of 16
+    assert fn(8, 1024, 0, None) == 1                      # not 16-byte aligned
 
 
 def test_more_than_one_gpu_is_refused():
