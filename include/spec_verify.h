@@ -19,10 +19,12 @@
  *
  * Conventions shared by every call
  *   - Every tensor argument is a DEVICE pointer on the current HIP device,
- *     owned by the caller; the library allocates no device memory, keeps no
- *     state between calls (the optional kernel tracer at the end of this
- *     file aside) and never synchronises.  All work is enqueued on `stream`
- *     (a hipStream_t; NULL = the default stream) in issue order.
+ *     owned by the caller; the verify, build, drafter and metrics calls
+ *     allocate no device memory, keep no state between calls and never
+ *     synchronise.  (The step graph and the kernel tracer at the end of this
+ *     file create HIP graph, stream and event objects, which they hold until
+ *     destroyed.)  All work is enqueued on `stream` (a hipStream_t; NULL =
+ *     the default stream) in issue order.
  *   - Arrays are dense and row-major with the shapes given below.
  *   - Arguments are validated on the host before anything is enqueued: on an
  *     error the call returns a nonzero sv_status and touches no memory.
