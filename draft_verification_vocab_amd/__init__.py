@@ -28,7 +28,7 @@ SV_F32, SV_BF16, SV_F16 = 0, 1, 2
 PADDING_SLOT_ID = -1
 DEVERR_DRAFT_TOKEN, DEVERR_ACCEPT_COUNT, DEVERR_BLOCK_TABLE = 1, 2, 4
 DEVERR_ROW_INDEX, DEVERR_TEMPERATURE, DEVERR_TREE = 8, 16, 32
-MAX_K = 63
+MAX_B, MAX_K, MAX_V = 1 << 20, 63, 1 << 19      # SV_MAX_B, SV_MAX_K, SV_MAX_V
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspecverify.so")

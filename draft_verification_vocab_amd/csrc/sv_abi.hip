@@ -54,7 +54,7 @@ namespace {
 
 inline bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-constexpr long kMaxB = 1L << 20;   // sequences per call
+constexpr long kMaxB = SV_MAX_B;    // sequences per call
 
 sv_status check_verify_shape(int B, int K, int V) {
   if (B < 0 || B > kMaxB || K < 0 || K > SV_MAX_K || V < 1 || V > SV_MAX_V) return SV_ERR_SHAPE;

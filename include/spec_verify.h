@@ -84,7 +84,8 @@ typedef enum {
                                      infinite or too small for 1/T to be finite:
                                      that sequence is treated as greedy (T = 0)        */
 
-/* Limits. */
+/* Limits (a call outside them returns SV_ERR_SHAPE). */
+#define SV_MAX_B (1 << 20)        /* sequences per call                               */
 #define SV_MAX_K 63               /* drafts per sequence (K+1 rows fit one wavefront) */
 #define SV_MAX_V (1 << 19)        /* vocabulary size                                  */
 #define SV_PADDING_SLOT_ID (-1)   /* slot of rows that must not write the KV cache    */
