@@ -6,6 +6,21 @@ and devices, allocate outputs with torch when the caller passes none, and call
 the library on the current HIP stream.  All computation runs in the library's
 HIP kernels; there is no other implementation to fall back to, and every call
 raises if the library is missing or returns an error.
+
+One decode round, with the drafter's distributions handed over as its logits
+and row descriptors (tensors on the GPU; shapes as in the C header)::
+
+    tok, _, desc = spec_draft_sample(drafter_logits, K, T, uniforms=u_draft,
+                                     row_index=sample_rows, want_draft_probs=False,
+                                     want_row_desc=True)
+    out, acc, _ = spec_verify_sample_lq(target_logits, drafter_logits, desc, tok,
+                                        u_verify, T, drafter_rows=sample_rows)
+    batch = peagle_build_draft_batch(out, acc, tok, start_pos, block_table,
+                                     block_size, target_hidden, h_shared, mask_id)
+
+spec_verify_greedy / spec_verify_sample / spec_verify_mixed take a dense q
+instead; spec_verify_tree verifies draft trees; StepGraph captures a verify,
+build and acceptance-metrics step as one HIP graph.
 """
 from __future__ import annotations
 
@@ -20,6 +35,8 @@ __all__ = [
     "require_library", "library_path", "sv_status_string", "spec_verify_workspace_bytes",
     "spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
     "SpecVerifyError", "SV_F32", "SV_BF16", "SV_F16", "PADDING_SLOT_ID",
+    "spec_verify_mixed", "spec_verify_sample_lq", "spec_verify_tree", "spec_draft_sample",
+    "spec_accept_metrics", "accept_metrics_buffer", "acceptance_summary", "StepGraph",
     "trace_begin", "trace_read", "trace_end",
     "DEVERR_DRAFT_TOKEN", "DEVERR_ACCEPT_COUNT", "DEVERR_BLOCK_TABLE",
 ]
