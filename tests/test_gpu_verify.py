@@ -4,8 +4,9 @@ Token ids and accept lengths are compared exactly; decisions that lie within
 1e-6 of their threshold may take either branch (the oracle enumerates the
 acceptable outcomes, see oracle.sample_outcomes); p_k(d_k) within 1e-5
 relative.  Workloads 1, 2 and 4 at full size, ragged and degenerate shapes,
-ties, -inf logits, zero draft probabilities, the residual fallback, invalid
-draft tokens, determinism, and chi-square tests of the GPU's own outputs.
+ties, -inf logits, zero draft probabilities, the residual fallback, final
+uniforms at 0 and just below 1, invalid draft tokens, determinism, and
+chi-square tests of the GPU's own outputs.
 """
 import numpy as np
 import pytest
@@ -28,7 +29,7 @@ def _greedy_parity(sv, logits, dtype, d):
     assert np.array_equal(out.cpu().numpy(), want_out)
 
 
-def _sample_parity(sv, logits, dtype, q, d, u, T, max_flag_frac=0.01):
+def _sample_parity(sv, logits, dtype, q, d, u, T, max_flag_frac=0.01, max_mismatch=None):
     out, acc, pd = sv.spec_verify_sample(dev(logits), dev(q), dev(d), dev(u), T,
                                          want_draft_target_prob=True)
     torch.cuda.synchronize()
@@ -42,6 +43,8 @@ def _sample_parity(sv, logits, dtype, q, d, u, T, max_flag_frac=0.01):
         flags += f
     assert mism <= flags          # every departure from the canonical outcome is a near tie
     assert flags <= max(2, max_flag_frac * B * (d.shape[1] + 1))
+    if max_mismatch is not None:
+        assert mism <= max_mismatch
     return out, acc
 
 
@@ -90,6 +93,24 @@ def test_ragged_shapes(gpu, dtype, B, K, V):
     logits, q, d, u = _random_case(rng, B, K, V, dtype, T=0.8, tie_heavy=True)
     _greedy_parity(gpu, logits, dtype, d)
     _sample_parity(gpu, logits, dtype, q, d, u, 0.8)
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 5000), ("bf16", 30000)])
+def test_extreme_final_uniforms(gpu, dtype, V):
+    """The final draw at u = 0 (the first token with positive mass) and at the
+    largest fp32 below 1 (u*S at or past the rounded total: the last token
+    with positive mass), for residual draws and bonus draws."""
+    rng = np.random.default_rng(V + 11)
+    B, K = 16, 3
+    logits, q, d, u = _random_case(rng, B, K, V, dtype, T=0.9)
+    top = np.nextafter(np.float32(1), np.float32(0))
+    u[:, K] = np.where(np.arange(B) % 2 == 0, np.float32(0), top)
+    u[:8, :K] = 0.0            # accept every draft with p > 0: bonus draws from p_K
+    u[8:, 0] = top             # reject draft 0 unless p/q >= 1: residual draws from row 0
+    # u*S lies within 1e-6 of the CDF's first or last boundary by construction,
+    # so every final draw is a flagged near tie; the GPU's token must still be
+    # one the oracle allows, and the oracle's own choice in all but a few
+    _sample_parity(gpu, logits, dtype, q, d, u, 0.9, max_flag_frac=1.0, max_mismatch=2)
 
 
 def test_max_vocab(gpu):
