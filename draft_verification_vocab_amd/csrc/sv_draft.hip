@@ -101,14 +101,71 @@ __device__ __forceinline__ void store_q(float* qrow, long o, long V, const float
   }
 }
 
-// Whole q row: the one-hot of g (g < 0: all zero), stores only.
+// Four consecutive logits (quad qd = elements 4qd .. 4qd+3), cached loads:
+// sweep 2 re-reads the row sweep 1 has just read.
+__device__ __forceinline__ void load_quad(const uint16_t* row, long qd, float z[4]) {
+  const uint2 w = reinterpret_cast<const uint2*>(row)[qd];
+  z[0] = __uint_as_float(w.x << 16); z[1] = __uint_as_float(w.x & 0xffff0000u);
+  z[2] = __uint_as_float(w.y << 16); z[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load_quad(const float* row, long qd, float z[4]) {
+  const f32x4 v = reinterpret_cast<const f32x4*>(row)[qd];
+  z[0] = v.x; z[1] = v.y; z[2] = v.z; z[3] = v.w;
+}
+
+constexpr int kQuadsPerLane = 8;   // one 2048-element step per wave
+
+// Sweep 2 of a sampled row with VEC (V a multiple of 8, rows 16-byte
+// aligned): q = 2^(z c - Mc) * inv_s, element for element as q_octet
+// computes it, with lane l of a wave on quad base + j*64 + l, so that each
+// 16-byte non-temporal store instruction writes 1 KB of contiguous q.  (With
+// one octet per lane, a store instruction writes 16-byte pieces with 16-byte
+// gaps, and 10% more bytes reached HBM than q holds.)
+template <typename LT, int WAVES>
+__device__ __forceinline__ void write_q_quads(const LT* zrow, float* qrow, long V, float c,
+                                              float Mc, float inv_s) {
+  const long nquads = V / 4;
+  const int w = threadIdx.x / kWave, l = lane_id();
+  for (long base = (long)w * kWave * kQuadsPerLane; base < nquads;
+       base += (long)WAVES * kWave * kQuadsPerLane) {
+    float z[kQuadsPerLane][4];
+#pragma unroll
+    for (int j = 0; j < kQuadsPerLane; ++j) {
+      const long qd = base + (long)j * kWave + l;
+      load_quad(zrow, qd < nquads ? qd : nquads - 1, z[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kQuadsPerLane; ++j) {
+      const long qd = base + (long)j * kWave + l;
+      f32x4 q;
+      q.x = __builtin_amdgcn_exp2f(fmaf(z[j][0], c, -Mc)) * inv_s;
+      q.y = __builtin_amdgcn_exp2f(fmaf(z[j][1], c, -Mc)) * inv_s;
+      q.z = __builtin_amdgcn_exp2f(fmaf(z[j][2], c, -Mc)) * inv_s;
+      q.w = __builtin_amdgcn_exp2f(fmaf(z[j][3], c, -Mc)) * inv_s;
+      if (qd < nquads) __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(qrow) + qd);
+    }
+  }
+}
+
+// Whole q row: the one-hot of g (g < 0: all zero), stores only; with VEC one
+// contiguous 16-byte quad per lane and store instruction, as above.
 template <bool VEC, int THREADS>
 __device__ void store_one_hot(float* qrow, long V, long nocts, int g) {
-  for (long o = threadIdx.x; o < nocts; o += THREADS) {
-    float q[8];
+  if constexpr (VEC) {
+    const long nquads = V / 4;
+    for (long qd = threadIdx.x; qd < nquads; qd += THREADS) {
+      const long e = qd * 4;
+      const f32x4 q{e == g ? 1.f : 0.f, e + 1 == g ? 1.f : 0.f, e + 2 == g ? 1.f : 0.f,
+                    e + 3 == g ? 1.f : 0.f};
+      __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(qrow) + qd);
+    }
+  } else {
+    for (long o = threadIdx.x; o < nocts; o += THREADS) {
+      float q[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = (o * 8 + j == g) ? 1.f : 0.f;
-    store_q<VEC>(qrow, o, V, q);
+      for (int j = 0; j < 8; ++j) q[j] = (o * 8 + j == g) ? 1.f : 0.f;
+      store_q<VEC>(qrow, o, V, q);
+    }
   }
 }
 
@@ -259,13 +316,17 @@ __global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(Draft
 
   // sweep 2 (only when q is requested): write q
   if constexpr (WQ) {
-    for (int tile = w; tile < T_tiles; tile += WAVES) {
-      float q[kTileLoads][8];
-      tile_q<LT, VEC>(zrow, tile, V, nocts, c, Mc, inv_s, q);
+    if constexpr (VEC) {
+      write_q_quads<LT, WAVES>(zrow, qrow, V, c, Mc, inv_s);
+    } else {
+      for (int tile = w; tile < T_tiles; tile += WAVES) {
+        float q[kTileLoads][8];
+        tile_q<LT, VEC>(zrow, tile, V, nocts, c, Mc, inv_s, q);
 #pragma unroll
-      for (int sl = 0; sl < kTileLoads; ++sl) {
-        const long o = ((long)tile * kTileLoads + sl) * kWave + l;
-        if (o < nocts) store_q<VEC>(qrow, o, V, q[sl]);
+        for (int sl = 0; sl < kTileLoads; ++sl) {
+          const long o = ((long)tile * kTileLoads + sl) * kWave + l;
+          if (o < nocts) store_q<VEC>(qrow, o, V, q[sl]);
+        }
       }
     }
   }
