@@ -454,6 +454,35 @@ def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, o
     return res
 
 
+def tree_walk_passes(np, parents, path, num_accepted):
+    """Row passes of the sampled tree walk, counted from its outputs.  At each
+    node on the accepted path the walk tests the node's children in index
+    order; every rejected child costs one workgroup pass over the node's logit
+    and draft-probability rows (the new residual's mass).  At the last node
+    every child was rejected; a node with no children costs one pass over its
+    logit row alone (the target distribution's tile masses for the final
+    draw).  Returns per tree (residual passes, logit-only passes).  (A
+    residual that rounds to zero mass adds one logit-only pass; it is not
+    counted here.)"""
+    B, N = parents.shape
+    res = np.zeros(B, np.int64)
+    plain = np.zeros(B, np.int64)
+    for b in range(B):
+        a = int(num_accepted[b])
+        cur = 0
+        for depth in range(a + 1):
+            kids = [i for i in range(1, N + 1) if int(parents[b, i - 1]) == cur]
+            if depth < a:
+                nxt = int(path[b, depth])
+                res[b] += sum(1 for i in kids if i < nxt)
+                cur = nxt
+            elif kids:
+                res[b] += len(kids)
+            else:
+                plain[b] += 1
+    return res, plain
+
+
 def tree_bench(sv, torch, np, synth, args):
     """Draft-tree verification on B=256 trees of 15 nodes (3 children at the
     root, 2 below each, 1 below those), V=151936 bf16 logits, T=0.7: one call
@@ -499,10 +528,24 @@ def tree_bench(sv, torch, np, synth, args):
         sv.trace_end()
         acc = outs[2].cpu().numpy()
         rb = rows * V * 2
+        kms = {k: float(np.mean(v)) for k, v in per.items()}
         res[name] = {"ms_per_call": sec * 1e3, "rows_per_s": rows / sec,
                      "logit_gbs": rb / sec / 1e9, "logit_frac": rb / sec / 1e9 / HBM_PEAK_GBS,
-                     "kernels_ms": {k: float(np.mean(v)) for k, v in per.items()},
-                     "mean_accepted": float(acc.mean())}
+                     "kernels_ms": kms, "mean_accepted": float(acc.mean())}
+        if T > 0.0:
+            # what the walk's row passes read (each pass re-reads the node's
+            # logit row, and its fp32 draft row after a rejection)
+            rp, pp = tree_walk_passes(np, ti.parents, outs[1].cpu().numpy(), acc)
+            wb = int(rp.sum()) * V * (2 + 4) + int(pp.sum()) * V * 2
+            walk_ms = kms.get("tree_walk")
+            passes = rp + pp
+            res[name]["walk"] = {
+                "passes_mean": float(passes.mean()), "passes_max": int(passes.max()),
+                "pass_bytes": wb,
+                "pass_gbs": wb / (walk_ms * 1e-3) / 1e9 if walk_ms else None,
+                "note": "bytes read by the walk's workgroup passes (a node's logit row, plus "
+                        "its fp32 draft row after a rejection); one workgroup per tree, so "
+                        "the walk lasts as long as the tree with the most passes"}
     return res
 
 

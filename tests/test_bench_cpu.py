@@ -127,3 +127,20 @@ def test_counters_from_other_sources_are_refused(tmp_path, monkeypatch):
         _run_ingest(tmp_path, monkeypatch, hash_on_disk="feedbeef")
     assert "feedbeef" in str(e.value)
     assert not os.path.exists(tmp_path / "profiles" / "traffic.json")
+
+
+def test_tree_walk_passes_hand_example():
+    """Row passes of the sampled tree walk, counted from the path: root with
+    children 1 and 2, node 1 with child 3, node 2 with child 4.  A rejected
+    child costs one residual pass; a leaf at the end of the path costs one
+    logit-only pass (the tile masses of the target distribution)."""
+    parents = np.array([[0, 0, 1, 2]] * 4, np.int32)
+    path = np.array([[-1, -1, -1, -1, -1],     # both root children rejected
+                     [2, -1, -1, -1, -1],      # 1 rejected, 2 accepted, then 4 rejected
+                     [1, 3, -1, -1, -1],       # 1 and 3 accepted, 3 is a leaf
+                     [1, -1, -1, -1, -1]],     # 1 accepted, then 3 rejected
+                    np.int32)
+    acc = np.array([0, 1, 2, 1], np.int32)
+    res, plain = bench.tree_walk_passes(np, parents, path, acc)
+    assert res.tolist() == [2, 2, 0, 1]
+    assert plain.tolist() == [0, 0, 1, 0]
