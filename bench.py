@@ -684,7 +684,8 @@ def main():
 
     def timed(sample):
         """Wall time per step with only the dominant kernel traced (two events
-        per step), then per-kernel times from a second loop tracing all."""
+        per step), then every other kernel of the step timed the same way in
+        a loop of its own."""
         dom = {"mixed": "verify_mixed_rows", True: "verify_sample_rows",
                False: "verify_greedy_rows"}[sample]
         for _ in range(args.warmup):
@@ -700,15 +701,26 @@ def main():
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
         per = {dom: [ms for _, ms in sv.trace_read()]}
-        sv.trace_begin(8 * args.steps)
-        for _ in range(args.steps):
-            step(sample)
-            build()
-        torch.cuda.synchronize()
-        for name, ms in sv.trace_read():
-            if name != dom:
-                per.setdefault(name, []).append(ms)
         sv.trace_end()
+        # the step's other kernels (named from one traced step), each timed in
+        # a loop of its own with only that kernel traced: two events per step,
+        # so no event sits between two other kernels of the step
+        sv.trace_begin(16)
+        step(sample)
+        build()
+        torch.cuda.synchronize()
+        names = [name for name, _ in sv.trace_read()]
+        sv.trace_end()
+        for name in names:
+            if name == dom:
+                continue
+            sv.trace_begin(args.steps, [name])
+            for _ in range(args.steps):
+                step(sample)
+                build()
+            torch.cuda.synchronize()
+            per[name] = [ms for _, ms in sv.trace_read()]
+            sv.trace_end()
         acc = acc_t.cpu().numpy()
         return wall / args.steps, {k: float(np.mean(v)) for k, v in per.items()}, acc
 
