@@ -59,6 +59,9 @@ def parse():
                     help="skip timing the decode round on the two q interfaces")
     ap.add_argument("--no-tree", action="store_true",
                     help="skip timing draft-tree verification")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip timing the mid-size verify, the P-EAGLE build and the "
+                         "large-vocabulary verify workloads")
     ap.add_argument("--no-draft", action="store_true",
                     help="skip timing the drafter-output sampling kernel")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -454,6 +457,124 @@ def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, o
     return res
 
 
+def wall_ms(torch, call, warmup, steps):
+    """Wall time per call (ms) of `steps` calls after `warmup` untimed ones."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    with quiet_host():
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+
+
+def kernel_times(sv, torch, np, call, steps):
+    """Average duration (ms) of each kernel that `call` launches, every kernel
+    timed in a loop of its own with only it traced (two events per call)."""
+    sv.trace_begin(16)
+    call()
+    torch.cuda.synchronize()
+    names = list(dict.fromkeys(name for name, _ in sv.trace_read()))
+    sv.trace_end()
+    out = {}
+    for name in names:
+        sv.trace_begin(4 * steps, [name])
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        out[name] = float(np.mean([ms for _, ms in sv.trace_read()]))
+        sv.trace_end()
+    return out
+
+
+def small_workloads_bench(sv, torch, np, synth, args):
+    """The three smaller workloads, each on its own: the mid-size verify
+    (B=8, K=5, V=32000 fp32, T=1: 48 logit rows, bound by launch and latency),
+    the P-EAGLE build (B=64, K=7, H=2880 bf16: 8 MB of data movement), and the
+    large-vocabulary verify (B=64, K=7, V=201088 bf16, T=0.7: 206 MB of logits,
+    under the 256 MB Infinity Cache, so the calls rotate over four copies of
+    the logits and draft probabilities).  Per call: the host-loop wall time,
+    each kernel's duration, and the algorithmic bytes over the kernels' time."""
+    dev = torch.device("cuda:0")
+    steps = max(args.steps, 100)
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    def entry(call, nbytes):
+        ms = wall_ms(torch, call, args.warmup, steps)
+        kms = kernel_times(sv, torch, np, call, steps)
+        gpu_ms = sum(kms.values())
+        return {"ms_per_call": ms, "kernels_ms": kms, "algorithmic_bytes": nbytes,
+                "gbs_over_kernel_time": nbytes / (gpu_ms * 1e-3) / 1e9,
+                "frac_over_kernel_time": nbytes / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+    res = {}
+    for n, copies in ((2, 1), (4, 4)):
+        vi = synth.make_verify_inputs(synth.verify_config(n), workers=args.workers)
+        B, K, V = vi.spec.B, vi.spec.K, vi.spec.V
+        zsize = 2 if vi.spec.dtype == "bf16" else 4
+        zs = [up(vi.logits)]
+        qs = [up(vi.draft_probs)]
+        for _ in range(copies - 1):
+            zs.append(zs[0].clone())
+            qs.append(qs[0].clone())
+        d, u = up(vi.draft_tokens), up(vi.uniforms)
+        out_t = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        acc_t = torch.empty(B, dtype=torch.int32, device=dev)
+        pd_t = torch.empty((B, K), dtype=torch.float32, device=dev)
+        ws = torch.zeros(sv.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+        turn = [0]
+
+        def sample():
+            i = turn[0] = (turn[0] + 1) % copies
+            sv.spec_verify_sample(zs[i], qs[i], d, u, vi.temperature, out_tokens=out_t,
+                                  out_num_accepted=acc_t, out_draft_target_prob=pd_t,
+                                  workspace=ws)
+
+        def greedy():
+            i = turn[0] = (turn[0] + 1) % copies
+            sv.spec_verify_greedy(zs[i], d, out_tokens=out_t, out_num_accepted=acc_t,
+                                  workspace=ws)
+
+        r = {"workload": f"{synth.CONFIG_NAMES[n]}: B={B} K={K} V={V} {vi.spec.dtype} logits, "
+                         f"T={vi.temperature}" + (f"; {copies} rotating input copies" if
+                                                  copies > 1 else "")}
+        for name, fn, smp in (("sample", sample, True), ("greedy", greedy, False)):
+            fn()
+            torch.cuda.synchronize()
+            rb, sb = verify_bytes(B, K, V, zsize, acc_t.cpu().numpy(), sample=smp)
+            r[name] = entry(fn, rb + sb)
+        if copies == 1:
+            g = sv.StepGraph("sample", dict(target_logits=zs[0], draft_probs=qs[0],
+                                            draft_tokens=d, uniforms=u,
+                                            temperature=vi.temperature, out_tokens=out_t,
+                                            out_num_accepted=acc_t, out_draft_target_prob=pd_t,
+                                            workspace=ws))
+            r["sample"]["graph_ms_per_call"] = wall_ms(torch, g.launch, args.warmup, steps)
+            g.close()
+        res[synth.CONFIG_NAMES[n]] = r
+        del zs, qs
+    bi = synth.make_build_inputs(synth.build_config(3))
+    B, K, H = bi.spec.B, bi.spec.K, bi.spec.H
+    o, a, d = up(bi.out_tokens), up(bi.num_accepted), up(bi.draft_tokens)
+    L, bt, hid, hs = up(bi.start_pos), up(bi.block_table), up(bi.target_hidden), up(bi.h_shared)
+    bouts = sv.peagle_build_draft_batch(o, a, d, L, bt, bi.spec.block_size, hid, hs,
+                                        bi.mask_token_id)
+
+    def build():
+        sv.peagle_build_draft_batch(o, a, d, L, bt, bi.spec.block_size, hid, hs,
+                                    bi.mask_token_id, outputs=bouts)
+
+    res[synth.CONFIG_NAMES[3]] = {"workload": f"{synth.CONFIG_NAMES[3]}: B={B} K={K} H={H} bf16",
+                                  "build": entry(build, build_bytes(B, K, H, 2))}
+    return res
+
+
 def tree_walk_passes(np, parents, path, num_accepted):
     """Row passes of the sampled tree walk, counted from its outputs.  At each
     node on the accepted path the walk tests the node's children in index
@@ -842,6 +963,9 @@ def main():
     if not args.no_tree:
         res["tree_verify"] = tree_bench(sv, torch, np, synth, args)
         log("tree verify timed")
+    if not args.no_small:
+        res["small_workloads"] = small_workloads_bench(sv, torch, np, synth, args)
+        log("smaller workloads timed")
     if args.cpu_budget > 0:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(vi, bi, args.cpu_budget)

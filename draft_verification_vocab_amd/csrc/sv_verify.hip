@@ -65,9 +65,17 @@ int verify_splits(int B, int K, int V) {
   return s < 1 ? 1 : (int)s;
 }
 
+// Draw workgroups per sequence: about one round of resident workgroups over
+// the whole chip (256 CUs x 5 draw workgroups of 82 VGPRs per lane), since
+// every workgroup first waits on its sequence's accept scan.  Measured draw
+// times (V=151936 bf16 unless noted): B=64 (V=201088) 21 us at 20 chunks vs
+// 29 us at 64; B=128 27 vs 35 us at 32; B=256 45 vs 51 us at 16; B=1024
+// 154-156 us for every count from 1 to 6.
+constexpr long kDrawWorkgroups = 1280;
+
 static int draw_chunks(int B, int V) {
   const long tiles = (V + kTileElems - 1) / kTileElems;
-  long c = (4096 + B - 1) / B;
+  long c = (kDrawWorkgroups + B / 2) / B;
   if (c > tiles) c = tiles;
   return c < 1 ? 1 : (int)c;
 }
