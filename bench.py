@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--ingest-valu", default=None, metavar="VALU_CSV",
                     help="write profiles/valu_counters_fused_b1024.md from a --pmc SQ_INSTS_VALU "
                          "SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE run")
+    ap.add_argument("--ingest-trace", nargs="+", metavar="FILE",
+                    help="write the kernel trace summary under profiles/ from a rocprofv3 "
+                         "kernel-trace CSV (and the log of a bench run on the same sources)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE runs of --profile-steps) into the traffic record and exit")
@@ -268,6 +271,96 @@ def ingest_counters(fetch_csv, write_csv):
         f.write("\n".join(lines) + "\n")
     print(json.dumps({"traffic_file": TRAFFIC_FILE, "summary": md,
                       "dominant_hbm_bytes_per_launch": rec["hbm_bytes_per_launch"]}))
+
+
+def ingest_trace(trace_csv, bench_log=None):
+    """Kernel trace summary from rocprofv3's per-dispatch records: average,
+    minimum and maximum duration per kernel and grid size (one kernel serves
+    several workloads), the run's kernel source hash (--hash-out
+    source_hash.txt next to the CSV), and, given the log of a `python
+    bench.py` run on the same sources, its tracer's per-kernel times."""
+    import csv
+    import collections
+
+    here = kernel_source_hash()
+    hp = os.path.join(os.path.dirname(trace_csv), "source_hash.txt")
+    if not os.path.exists(hp):
+        sys.exit(f"{hp} is missing: cannot tell which kernels this trace measured")
+    got = open(hp).read().strip()
+    if got != here:
+        sys.exit(f"the trace in {trace_csv} was taken on kernel sources {got}, not the current {here}")
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        name = r["Kernel_Name"]
+        if not (name.startswith(("void sv::", "sv::")) or "stream_read<" in name
+                or "copyBuffer" in name):
+            continue                 # torch's own kernels (input uploads, fills)
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        per[(name, grid)].append(us)
+    rows = sorted(per.items(), key=lambda kv: -sum(kv[1]) / len(kv[1]))
+    tdir = os.path.dirname(trace_csv)
+    to = os.path.basename(trace_csv).split("_kernel_trace")[0]
+    lines = ["# Kernel trace: fused high-concurrency step (B=1024, K=7, V=151936 bf16; build H=2048)\n",
+             "Commands (from /tmp with TMPDIR=/tmp; REPO = the repository root):\n",
+             "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/{tdir} -o {to} -- "
+             f"python3 $REPO/bench.py --profile-steps 5 --hash-out $REPO/{tdir}/source_hash.txt",
+             f"python bench.py --ingest-trace {trace_csv}" + (f" {bench_log}" if bench_log else ""),
+             "```\n",
+             "`--profile-steps 5` runs, five times on the workload-5 inputs: a sampled, a greedy and "
+             "a mixed verify each followed by the build, the drafter sampling with dense q and with "
+             "row descriptors, the verify from drafter logits and the acceptance metrics; then five "
+             "greedy and five sampled tree verifications (64 trees of 15 nodes, V=151936 bf16), one "
+             "pass each of the read-ceiling kernel (`stream_read<true>` non-temporal, "
+             "`stream_read<false>` cached) over the 2.49 GB logit buffer, and one 1 GiB copy (the "
+             "counter calibration).\n",
+             f"Kernel source hash (bench.py `kernel_source_hash`): `{here}`\n",
+             "Per kernel and grid size (threads), from the per-dispatch records of the run "
+             "(the `--stats` table averages one kernel over every grid it ran at):\n",
+             "| kernel | grid | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|---|"]
+    for (name, grid), v in rows:
+        lines.append(f"| `{name}` | {grid} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | "
+                     f"{max(v):.1f} |")
+    dom = [v for (name, grid), v in per.items()
+           if "verify_rows<unsigned short, 1, true>" in name and grid == 2097152]
+    if dom:
+        lines.append(f"\nDominant kernel (`verify_rows<unsigned short, 1, true>`, the 8192-row fused "
+                     f"batch): {sum(dom[0]) / len(dom[0]):.1f} µs average over {len(dom[0])} "
+                     "dispatches (sampled verify and verify from drafter logits).")
+    if bench_log:
+        res = json.loads([ln for ln in open(bench_log) if ln.startswith("{")][-1])
+        if res.get("kernel_source_hash") != here:
+            sys.exit(f"{bench_log} was measured on other kernel sources")
+        lines += ["\nSame sources, bench.py's tracer (HIP events on the kernels' stream, one "
+                  f"kernel traced per loop, {res['steps']} timed steps of `python bench.py`):\n",
+                  "| kernel | avg µs | algorithmic GB | GB/s | % of 8 TB/s |", "|---|---|---|---|---|"]
+        for k, v in res["kernels"].items():
+            lines.append(f"| {k} | {v['avg_ms'] * 1e3:.1f} | {v['algorithmic_bytes'] / 1e9:.4f} | "
+                         f"{v['gbs']:.0f} | {v['frac'] * 100:.1f} |")
+        g = res.get("greedy_step")
+        if g:
+            r = g["verify_greedy_rows"]
+            lines.append(f"| verify_greedy_rows | {r['avg_ms'] * 1e3:.1f} | "
+                         f"{r['algorithmic_bytes'] / 1e9:.4f} | {r['gbs']:.0f} | "
+                         f"{r['frac'] * 100:.1f} |")
+            lines.append(f"| verify_greedy_accept | {g['verify_greedy_accept_ms'] * 1e3:.1f} | | | |")
+        lines.append(f"\nSampled step: {res['ms_per_step']:.3f} ms, {res['value'] / 1e6:.2f} M "
+                     f"verified logit rows/s, {res['step_hbm_gbs']:.0f} GB/s algorithmic "
+                     f"({res['step_hbm_frac'] * 100:.1f}% of 8 TB/s)" +
+                     (f"; greedy step: {g['ms_per_step']:.3f} ms, {g['value'] / 1e6:.2f} M rows/s "
+                      f"({g['step_hbm_frac'] * 100:.1f}%)." if g else "."))
+        c = res.get("read_ceiling")
+        if c:
+            lines.append(f"\nRead ceiling (the plain streaming-read kernel over the same 2.489 GB "
+                         f"logit buffer): non-temporal loads {c['nontemporal_gbs']:.0f} GB/s, cached "
+                         f"loads {c['cached_gbs']:.0f} GB/s; the sampled row kernel reaches "
+                         f"{res['roofline']['frac_of_read_ceiling'] * 100:.1f}% of the non-temporal "
+                         "rate.")
+    md = os.path.join(ROOT, "profiles", "kernel_trace_fused_b1024.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"summary": md, "kernels": len(rows)}))
 
 
 def ingest_valu(valu_csv):
@@ -677,6 +770,9 @@ def main():
         return
     if args.ingest_valu:
         ingest_valu(args.ingest_valu)
+        return
+    if args.ingest_trace:
+        ingest_trace(*args.ingest_trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -144,3 +144,30 @@ def test_tree_walk_passes_hand_example():
     res, plain = bench.tree_walk_passes(np, parents, path, acc)
     assert res.tolist() == [2, 2, 0, 1]
     assert plain.tolist() == [0, 0, 1, 0]
+
+
+def test_trace_ingestion_summarises_per_kernel_and_grid(tmp_path, monkeypatch):
+    """The kernel trace summary averages each (kernel, grid size) pair over
+    its dispatches, refuses a trace taken on other kernel sources, and names
+    the dominant kernel's average."""
+    os.makedirs(tmp_path / "profiles")
+    os.makedirs(tmp_path / "t")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc123")
+    path = tmp_path / "t" / "st_kernel_trace.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z",
+                    "Start_Timestamp", "End_Timestamp"])
+        w.writerow([ROWS_S, 2097152, 1, 1, 0, 360000])       # ns
+        w.writerow([ROWS_S, 2097152, 1, 1, 400000, 770000])
+        w.writerow([ROWS_S, 524288, 1, 1, 800000, 850000])   # the same kernel, a smaller batch
+    (tmp_path / "t" / "source_hash.txt").write_text("other\n")
+    with pytest.raises(SystemExit):
+        bench.ingest_trace(str(path))
+    (tmp_path / "t" / "source_hash.txt").write_text("abc123\n")
+    bench.ingest_trace(str(path))
+    md = (tmp_path / "profiles" / "kernel_trace_fused_b1024.md").read_text()
+    assert f"| `{ROWS_S}` | 2097152 | 2 | 365.0 | 360.0 | 370.0 |" in md
+    assert f"| `{ROWS_S}` | 524288 | 1 | 50.0 | 50.0 | 50.0 |" in md
+    assert "365.0 µs average over 2 dispatches" in md
