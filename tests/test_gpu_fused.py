@@ -5,7 +5,10 @@ probabilities (4.36 GB), verified on the device, then the P-EAGLE batch (H=2048
 bf16, prompt lengths U{64..8192}) built from the verify outputs on the same
 stream with no host round trip.  Every sequence is checked for well-formed
 output and the build invariants; a seeded sample of sequences is checked
-against the oracle one by one (the oracle's cost limits the sample).
+against the oracle one by one (the oracle's cost limits the sample), and every
+sequence against the greedy definition (numpy argmax chain) and against
+properties of rejection sampling (each accept test, the drawn token in the
+support of its distribution).
 """
 import numpy as np
 import pytest
@@ -71,6 +74,85 @@ def _well_formed(vi, out, acc):
         assert np.array_equal(out[b, :a], vi.draft_tokens[b, :a])
         assert 0 <= out[b, a] < V
         assert np.all(out[b, a + 1:] == -1)
+
+
+def _widened(vi, lo, hi):
+    """Logit rows of sequences lo..hi-1 as float32 (bf16 widened exactly)."""
+    return (vi.logits[lo:hi].astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _all_row_argmax(vi, chunk=64):
+    """Lowest-index argmax of every logit row of the batch, [B][K+1]."""
+    B = vi.spec.B
+    g = np.empty((B, vi.spec.K + 1), np.int64)
+    for lo in range(0, B, chunk):
+        g[lo:lo + chunk] = np.argmax(_widened(vi, lo, min(B, lo + chunk)), axis=-1)
+    return g
+
+
+def test_fused_greedy_every_sequence(gpu, fused):
+    """Every sequence of the full batch against the definition of greedy
+    verification: drafts accepted while each equals its row's lowest-index
+    argmax (numpy), then the argmax of the first mismatching row (or of row K)."""
+    vi, bi, t, picks = fused
+    B, K = vi.spec.B, vi.spec.K
+    out_t, acc_t = gpu.spec_verify_greedy(t["z"], t["d"])
+    torch.cuda.synchronize()
+    out, acc = out_t.cpu().numpy(), acc_t.cpu().numpy()
+    g = _all_row_argmax(vi)
+    match = vi.draft_tokens == g[:, :K]
+    want_a = np.where(match.all(axis=1), K, np.argmin(match, axis=1))
+    assert np.array_equal(acc, want_a)
+    rows = np.arange(B)
+    assert np.array_equal(out[rows, acc], g[rows, acc])
+    _well_formed(vi, out, acc)
+
+
+def test_fused_sample_every_sequence(gpu, fused):
+    """Every sequence of the full batch against properties of rejection
+    sampling that hold at any size, with p computed here in fp64 from each
+    row's max and sum of exponentials: draft k < a passed its test u_k <
+    p_k(d_k) / q_k(d_k) and draft a (a < K) failed it, except where u_k lies
+    within 1e-5 (relative) of the ratio; the new token lies in the support of
+    the distribution it was drawn from: max(0, p_a - q_a) for a < K (p_a(c) >
+    q_a(c), up to the fp32 rounding of p), p_K for a = K."""
+    vi, bi, t, picks = fused
+    B, K, T = vi.spec.B, vi.spec.K, vi.temperature
+    out_t, acc_t, _ = gpu.spec_verify_sample(t["z"], t["q"], t["d"], t["u"], T)
+    torch.cuda.synchronize()
+    out, acc = out_t.cpu().numpy(), acc_t.cpu().numpy()
+    _well_formed(vi, out, acc)
+    rows = np.arange(B)
+    c = out[rows, acc]
+    d, u = vi.draft_tokens, vi.uniforms.astype(np.float64)
+    p_d = np.empty((B, K))          # p_k(d_k)
+    p_c = np.empty(B)               # p_a(c)
+    chunk = 32
+    for lo in range(0, B, chunk):
+        hi = min(B, lo + chunk)
+        z = _widened(vi, lo, hi).astype(np.float64)            # [n][K+1][V]
+        m = z.max(axis=-1, keepdims=True)
+        lse = np.log(np.exp((z - m) / T).sum(axis=-1))          # [n][K+1]
+        n = np.arange(hi - lo)
+        zd = z[n[:, None], np.arange(K)[None, :], d[lo:hi]]
+        p_d[lo:hi] = np.exp((zd - m[:, :K, 0]) / T - lse[:, :K])
+        a = acc[lo:hi]
+        p_c[lo:hi] = np.exp((z[n, a, c[lo:hi]] - m[n, a, 0]) / T - lse[n, a])
+    q_d = np.take_along_axis(vi.draft_probs, d[:, :, None].astype(np.int64), axis=2)[:, :, 0]
+    q_d = q_d.astype(np.float64)
+    ratio = np.where(q_d > 0, p_d / np.where(q_d > 0, q_d, 1.0), np.where(p_d > 0, np.inf, 0.0))
+    passed = u[:, :K] < ratio
+    near = np.abs(u[:, :K] - ratio) <= 1e-5 * np.maximum(1.0, ratio)
+    k = np.arange(K)[None, :]
+    must_pass = k < acc[:, None]
+    must_fail = k == acc[:, None]
+    bad = (must_pass & ~passed & ~near) | (must_fail & passed & ~near)
+    assert not bad.any(), np.argwhere(bad)[:10]
+    rej = acc < K
+    q_c = vi.draft_probs[rows[rej], acc[rej], c[rej]].astype(np.float64)
+    assert np.all(p_c[rej] > q_c * (1 - 1e-5)), np.flatnonzero(rej)[p_c[rej] <= q_c * (1 - 1e-5)]
+    assert np.all(p_c[~rej] > 0)
+    print(f"[fused] {int(near.sum())} accept tests within 1e-5 of their ratio", flush=True)
 
 
 def test_fused_greedy_then_build(gpu, fused):
