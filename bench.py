@@ -972,16 +972,20 @@ def main():
         "kernels": {
             "verify_sample_rows": kinfo("verify_sample_rows", vb_rows),
             "verify_sample_draw": kinfo("verify_sample_draw", vb_draw,
-                                        "the accept scan, then the residual tile masses; "
-                                        "algorithmic bytes count the scan's reads and writes "
-                                        "once and the drafter rows a_b; the kernel also "
-                                        "re-reads logit row a"),
-            "verify_sample_locate": kinfo("verify_sample_locate", B * 4),
+                                        "the accept scan, the residual tile masses, and "
+                                        "(one workgroup per sequence) the draw of the new "
+                                        "token; algorithmic bytes count the scan's reads and "
+                                        "writes once and the drafter rows a_b; the kernel "
+                                        "also re-reads logit row a"),
             "peagle_build": kinfo("peagle_build", bb),
         },
         "acceptance": {"mean_accepted": float(acc.mean()),
                        "rate": float(acc.sum() / np.minimum(acc + 1, K).sum())},
     }
+    if "verify_sample_locate" in kms:
+        # a separate locate kernel runs only when several draw workgroups
+        # share a sequence (smaller batches)
+        res["kernels"]["verify_sample_locate"] = kinfo("verify_sample_locate", B * 4)
     rk = res["kernels"]["verify_sample_rows"]
     traffic = None
     if os.path.exists(TRAFFIC_FILE):

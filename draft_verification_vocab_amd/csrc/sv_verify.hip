@@ -66,16 +66,22 @@ int verify_splits(int B, int K, int V) {
 }
 
 // Draw workgroups per sequence: about one round of resident workgroups over
-// the whole chip (256 CUs x 5 draw workgroups of 82 VGPRs per lane), since
+// the whole chip (256 CUs x 5 resident draw workgroups of 4 waves), since
 // every workgroup first waits on its sequence's accept scan.  Measured draw
 // times (V=151936 bf16 unless noted): B=64 (V=201088) 21 us at 20 chunks vs
 // 29 us at 64; B=128 27 vs 35 us at 32; B=256 45 vs 51 us at 16; B=1024
 // 154-156 us for every count from 1 to 6.
 constexpr long kDrawWorkgroups = 1280;
 
-static int draw_chunks(int B, int V) {
+// In a mixed batch the greedy sequences' workgroups stop after the scan, so
+// at least 4 chunks per sequence let the sampled sequences' rows spread over
+// the CUs those leave idle (B=1024 with 199 greedy sequences: draw + locate
+// 144 us at 4 chunks, 149 us for the draw alone at one workgroup per
+// sequence).
+static int draw_chunks(int B, int V, bool mixed = false) {
   const long tiles = (V + kTileElems - 1) / kTileElems;
   long c = (kDrawWorkgroups + B / 2) / B;
+  if (mixed && c < 4) c = 4;
   if (c > tiles) c = tiles;
   return c < 1 ? 1 : (int)c;
 }
@@ -277,7 +283,8 @@ __global__ __launch_bounds__(kThreads) void verify_accept(ScanArgs A) {
 // the accept outputs, the greedy token of a greedy sequence of a mixed batch,
 // and the result for verify_locate.
 template <typename LT, int MODE, bool QL>
-__device__ __forceinline__ ScanResult draw_scan(const ScanArgs& A, int b, bool write) {
+__device__ __forceinline__ ScanResult draw_scan(const ScanArgs& A, int b, bool write,
+                                                bool handoff) {
   ScanResult r;
   if constexpr (MODE == MIXED) {
     bool bad;
@@ -292,7 +299,7 @@ __device__ __forceinline__ ScanResult draw_scan(const ScanArgs& A, int b, bool w
   } else {
     r = accept_scan<LT, SAMPLE, QL>(A, b, write, A.c);
   }
-  if (write && lane_id() == 0) A.info[b] = r;                // read by verify_locate
+  if (handoff && lane_id() == 0) A.info[b] = r;              // read by verify_locate
   return r;
 }
 
@@ -419,18 +426,26 @@ __device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool resid
 }
 
 // verify_draw: wave 0 of every workgroup runs sequence b's accept scan
-// (chunk 0 writes its outputs); then chunk cidx of b stores the mass of each
-// of its tiles.  A tile is kTileLoads consecutive 512-element wave loads;
-// each lane sums its octets of the tile before one wave reduction.
+// (chunk 0 writes its outputs); then chunk cidx of b computes the mass of
+// each of its tiles.  A tile is kTileLoads consecutive 512-element wave
+// loads; each lane sums its octets of the tile before one wave reduction.
+// With several chunks per sequence the masses go to the workspace for
+// verify_locate.  With one (C = 1: large batches, or rows of one tile) the
+// workgroup holds every mass of row a in LDS and wave 0 draws the token
+// itself, so no locate kernel runs; the workgroup is then the only reader of
+// the sequence's row partials and clears them after its scan.
 template <typename LT, int MODE, bool VEC, bool QL>
 __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
   __shared__ ScanResult scan;
+  __shared__ float s_tsum[kMaxTiles];
   const int C = A.C, T = A.T;
   const int b = blockIdx.x / C, cidx = blockIdx.x % C;
+  const bool whole = C == 1;
   const long V = A.sc.V;
   const long nocts = (V + 7) / 8;
   if (threadIdx.x < kWave) {
-    const ScanResult r = draw_scan<LT, MODE, QL>(A.sc, b, cidx == 0);
+    const ScanResult r = draw_scan<LT, MODE, QL>(A.sc, b, cidx == 0, !whole);
+    if (whole) clear_partials(A.sc, b);
     if (threadIdx.x == 0) scan = r;
   }
   __syncthreads();
@@ -448,37 +463,42 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
 #pragma unroll
     for (int j = 0; j < kTileUnroll; ++j) {
       const float ts = wave_sum_f(ls[j]);
-      if (l == 0 && t0 + j < t_hi) tsum_g[t0 + j] = ts;   // read by verify_locate
+      if (l == 0 && t0 + j < t_hi) {
+        if (whole) s_tsum[t0 + j] = ts;
+        else tsum_g[t0 + j] = ts;             // read by verify_locate
+      }
     }
   }
-}
-
-// verify_locate: one wave per sequence draws the token from the tile masses.
-template <typename LT, bool VEC, bool QL>
-__global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
-  constexpr int kPer = kMaxTiles / kWave;     // tiles per lane at most
-  const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
-  if (b >= A.sc.B) return;
-  const int T = A.T, K = A.sc.K;
-  const long V = A.sc.V;
-  const long nocts = (V + 7) / 8;
-  const int l = lane_id();
-  float* tsum_g = A.tile_sums + (long)b * T;
-  // this sequence's tile masses, lanes owning contiguous runs of tiles; the
-  // loads go out before the scan result is read.  They are agent-coherent
-  // loads: the rare path below rewrites the masses from this wave and reads
-  // them back.
+  if (!whole) return;
+  __syncthreads();
+  if (w != 0) return;
+  constexpr int kPer = kMaxTiles / kWave;
   const int per = (T + kWave - 1) / kWave;
   const int lo = min(T, l * per), hi = min(T, (l + 1) * per);
   float ts[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) ts[j] = lo + j < hi ? ld_coherent(&tsum_g[lo + j]) : 0.f;
-  const DrawRow<LT> R = draw_row<LT, QL>(A, b, A.sc.info[b]);   // written by verify_draw
-  clear_partials(A.sc, b);                    // every draw workgroup of b has read them
-  if (R.c == 0.f) {                           // greedy: nothing to draw
-    if (l == 0) A.sc.info[b] = ScanResult{0, 0, 0.f, 0.f, 0.0};
-    return;
-  }
+  for (int j = 0; j < kPer; ++j) ts[j] = lo + j < hi ? s_tsum[lo + j] : 0.f;
+  const int K = A.sc.K;
+  const int pick = locate_in_masses<LT, VEC, QL, true>(
+      R, A.sc.uniforms[(long)b * (K + 1) + K], T, V, nocts, ts, s_tsum);
+  if (l == 0) A.sc.out_tokens[(long)b * (K + 1) + R.a] = pick;
+}
+
+// The token drawn from row a of one sequence by one wave, given the row's T
+// tile masses: lane l holds the masses of its contiguous run of tiles [lo,
+// hi) in ts (loaded by the caller).  u * S (S = the sum of the masses) picks
+// the tile, then the element inside it (pick_in_tile).  In the rare case
+// that the residual has no mass (the drafter row sums to more than p_a) the
+// wave recomputes every tile mass of p_a into `masses` (global memory with
+// agent-coherent stores and loads, or LDS) and draws from p_a.
+template <typename LT, bool VEC, bool QL, bool IN_LDS>
+__device__ __forceinline__ int locate_in_masses(const DrawRow<LT>& R, float u, int T, long V,
+                                                long nocts, float (&ts)[kMaxTiles / kWave],
+                                                float* masses) {
+  constexpr int kPer = kMaxTiles / kWave;
+  const int l = lane_id();
+  const int per = (T + kWave - 1) / kWave;
+  const int lo = min(T, l * per), hi = min(T, (l + 1) * per);
   bool residual = R.residual;
   double part = 0.0;
 #pragma unroll
@@ -486,24 +506,26 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
   double incl = wave_inclusive_scan(part);
   double S = __shfl(incl, kWave - 1);
   if (residual && !(S > 0.0)) {
-    // r sums to 0 (only when the drafter's row sums to more than p): draw
-    // from p_a instead; this wave recomputes every tile mass
     residual = false;
     for (int t = 0; t < T; ++t) {
       const float m = wave_sum_f(lane_tile_mass<LT, VEC, QL>(R, false, t, V, nocts));
-      if (l == 0) st_coherent(&tsum_g[t], m);
+      if (l == 0) {
+        if constexpr (IN_LDS) masses[t] = m;
+        else st_coherent(&masses[t], m);
+      }
     }
-    wait_stores_performed();
+    if constexpr (!IN_LDS) wait_stores_performed();
     part = 0.0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      ts[j] = lo + j < hi ? ld_coherent(&tsum_g[lo + j]) : 0.f;
+      if constexpr (IN_LDS) ts[j] = lo + j < hi ? masses[lo + j] : 0.f;
+      else ts[j] = lo + j < hi ? ld_coherent(&masses[lo + j]) : 0.f;
       part += (double)ts[j];
     }
     incl = wave_inclusive_scan(part);
     S = __shfl(incl, kWave - 1);
   }
-  const double target = (double)A.sc.uniforms[(long)b * (K + 1) + K] * S;
+  const double target = (double)u * S;
 
   // the tile that holds u * S
   double run = __shfl_up(incl, 1);
@@ -539,7 +561,39 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
     const long o = ((long)tile * kTileLoads + sl) * kWave + l;
     octet_mass<LT, VEC, QL>(R, o, V, nocts, residual, r[sl]);
   }
-  const int pick = pick_in_tile(r, tile, pre, target, fallback);
+  return pick_in_tile(r, tile, pre, target, fallback);
+}
+
+// verify_locate: one wave per sequence draws the token from the tile masses
+// the draw kernel's workgroups stored (batches with several workgroups per
+// sequence).
+template <typename LT, bool VEC, bool QL>
+__global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
+  constexpr int kPer = kMaxTiles / kWave;     // tiles per lane at most
+  const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (b >= A.sc.B) return;
+  const int T = A.T, K = A.sc.K;
+  const long V = A.sc.V;
+  const long nocts = (V + 7) / 8;
+  const int l = lane_id();
+  float* tsum_g = A.tile_sums + (long)b * T;
+  // this sequence's tile masses, lanes owning contiguous runs of tiles; the
+  // loads go out before the scan result is read.  They are agent-coherent
+  // loads: the rare path rewrites the masses from this wave and reads them
+  // back.
+  const int per = (T + kWave - 1) / kWave;
+  const int lo = min(T, l * per), hi = min(T, (l + 1) * per);
+  float ts[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) ts[j] = lo + j < hi ? ld_coherent(&tsum_g[lo + j]) : 0.f;
+  const DrawRow<LT> R = draw_row<LT, QL>(A, b, A.sc.info[b]);   // written by verify_draw
+  clear_partials(A.sc, b);                    // every draw workgroup of b has read them
+  if (R.c == 0.f) {                           // greedy: nothing to draw
+    if (l == 0) A.sc.info[b] = ScanResult{0, 0, 0.f, 0.f, 0.0};
+    return;
+  }
+  const int pick = locate_in_masses<LT, VEC, QL, false>(
+      R, A.sc.uniforms[(long)b * (K + 1) + K], T, V, nocts, ts, tsum_g);
   if (l == 0) A.sc.out_tokens[(long)b * (K + 1) + R.a] = pick;
   // leave this sequence's part of the workspace cleared
   for (int i = l; i < T; i += kWave) st_coherent(&tsum_g[i], 0.f);
@@ -643,9 +697,10 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   // sampling and mixed batches: the draw kernel runs the accept scan itself
   DrawArgs D;
   D.sc = sc;
-  D.C = lay.C; D.T = lay.T;
+  D.C = mode == MIXED ? draw_chunks(L.B, L.V, true) : lay.C;
+  D.T = lay.T;
   D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
-  const dim3 grid3((unsigned)((long)L.B * lay.C));
+  const dim3 grid3((unsigned)((long)L.B * D.C));
 #define SV_DRAW_KERNELS(LAUNCH) \
   do { \
     if (L.bf16) { \
@@ -667,7 +722,7 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   SV_DRAW_KERNELS(SV_DRAW);
   err = hipGetLastError();
   trace_after(stream, SV_KERNEL_VERIFY_SAMPLE_DRAW);
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || D.C == 1) return err;     // C = 1: the draw drew the tokens
   trace_before(stream, SV_KERNEL_VERIFY_SAMPLE_LOCATE);
   SV_DRAW_KERNELS(SV_LOCATE);
 #undef SV_LOCATE

@@ -162,7 +162,9 @@ SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
  * acceptance ratio; results agree with an fp64 evaluation except when a
  * decision lies within ~1e-6 of its threshold.  Three kernels are enqueued:
  * row statistics; the accept scan with the residual / bonus masses of row a;
- * the draw of the new token from them.
+ * the draw of the new token from them.  When one workgroup covers each
+ * sequence's row a (B >= 854, or V <= 2048) the second kernel also draws the
+ * token and two kernels are enqueued.
  */
 SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
                                     const float* draft_probs,
@@ -189,8 +191,8 @@ SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
  *                    and counts as q = 0.
  *   drafter_desc     [B][K] sv_draft_row, as written by spec_draft_sample for
  *                    the same rows (desc b*K+k describes draft k of sequence b).
- *   Other arguments as for spec_verify_sample.  Three kernels are enqueued,
- *                    as for spec_verify_sample.
+ *   Other arguments as for spec_verify_sample.  The kernels are enqueued as
+ *                    for spec_verify_sample.
  */
 SV_API sv_status spec_verify_sample_lq(const void* target_logits, int logits_dtype,
                                        const void* drafter_logits, int64_t n_drafter_rows,
@@ -221,8 +223,9 @@ SV_API sv_status spec_verify_sample_lq(const void* target_logits, int logits_dty
  *                    sequences; for greedy ones 1 where d[b][k] is row k's
  *                    lowest-index argmax and 0 elsewhere (the T -> 0 limit).
  * Results equal those of spec_verify_greedy / spec_verify_sample on each
- * sequence alone.  The same three kernels as spec_verify_sample are enqueued;
- * the draw and locate kernels stop after the accept scan for greedy sequences.
+ * sequence alone.  The same kernels as spec_verify_sample are enqueued (the
+ * separate draw kernel whenever V > 2048); the draw and locate kernels stop
+ * after the accept scan for greedy sequences.
  */
 SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
                                    const float* draft_probs, const int32_t* draft_tokens,
