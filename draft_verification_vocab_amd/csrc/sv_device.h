@@ -11,6 +11,7 @@ constexpr int kOct = 8;                 // elements per lane per load group ("oc
 constexpr int kTile = kWave * kOct;     // 512 elements: granularity of the draw's CDF
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- bf16 / fp32
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -20,6 +21,12 @@ template <bool NT>
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   else return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x2 ld8(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  else return *reinterpret_cast<const u32x2*>(p);
 }
 
 // Element e of a logit row as fp32 (exact widening).

@@ -348,140 +348,165 @@ __device__ __forceinline__ DrawRow<LT> draw_row(const DrawArgs& A, int b, const 
   return r;
 }
 
-// Mass of octet o of the draw row: max(0, p - q) (residual) or p.  q comes
-// from the dense q row, or (QL) from the drafter logit row and descriptor.
-// With VEC the address is clamped into the row and the values past V are
-// masked, so the loads carry no branch.
-template <typename LT, bool VEC, bool QL>
-__device__ __forceinline__ void octet_mass(const DrawRow<LT>& R, long o, long V, long nocts,
-                                           bool residual, float r[8]) {
-  float z[8], q[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) q[j] = 0.f;
-  if constexpr (VEC) {
-    const bool in = o < nocts;
-    const long oc = in ? o : nocts - 1;
-    // Every row here is read once per step: non-temporal loads.  Measured
-    // over whole sampled steps (verify + build) at B=1024, V=151936: 541 us,
-    // against 546 us with cached logit loads (their 311 MB evict from the
-    // Infinity Cache the hidden states the build reads next, +6 us there)
-    // and 550 us with cached q loads.
-    Raw<LT> rz;
-    raw_load<true>(R.zrow, oc, rz);
-    unpack(rz, z);
-    if (residual) {
-      if constexpr (QL) {
-        if (R.dzrow) {
-          Raw<LT> rd;
-          raw_load<true>(R.dzrow, oc, rd);
-          float dz[8];
-          unpack(rd, dz);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) q[j] = drafter_q(R.desc, dz[j], oc * 8 + j);
-        }
-      } else {
-        Raw<float> rq;
-        raw_load<true>(R.qrow, oc, rq);
-        unpack(rq, q);
-      }
-    }
-    if (!in) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) { z[j] = -INFINITY; q[j] = 0.f; }
-    }
-  } else {
-    load_octet<false>(R.zrow, o, V, false, -INFINITY, z);
-    if (residual) {
-      if constexpr (QL) {
-        if (R.dzrow) {
-          float dz[8];
-          load_octet<false>(R.dzrow, o, V, false, 0.f, dz);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const long e = o * 8 + j;
-            q[j] = e < V ? drafter_q(R.desc, dz[j], e) : 0.f;
-          }
-        }
-      } else {
-        load_octet<false>(R.qrow, o, V, false, 0.f, q);
-      }
-    }
-  }
-  mass_octet(z, q, residual, R.c, R.Mc32, R.inv_s, r);
+// Element layout of the draw's CDF tiles.  A wave load g covers the 512
+// elements [512 g, 512 g + 512) of a row; lane l holds the quads (4
+// consecutive elements) starting at 512 g + 4 l (half 0) and 512 g + 256 +
+// 4 l (half 1), so each load instruction of the wave reads one contiguous
+// block: 512 B of bf16 logits, 1 KB of fp32 q.  (With one 8-element octet
+// per lane the fp32 q loads of a lane were two 16-byte loads 32 bytes apart,
+// and the workload-5 draw took 160 instead of 150 us.)  r[4 h + j] is the
+// mass of element 512 g + 256 h + 4 l + j.
+template <typename LT> struct Quad;
+template <> struct Quad<uint16_t> { u32x2 w; };
+template <> struct Quad<float> { u32x4 w; };
+
+__device__ __forceinline__ void load_quad(const uint16_t* row, long e, Quad<uint16_t>& q) {
+  q.w = ld8<true>(row + e);
+}
+__device__ __forceinline__ void load_quad(const float* row, long e, Quad<float>& q) {
+  q.w = ld16<true>(row + e);
+}
+__device__ __forceinline__ void unpack(const Quad<uint16_t>& q, float v[4]) {
+  v[0] = bf16_lo(q.w.x); v[1] = bf16_hi(q.w.x); v[2] = bf16_lo(q.w.y); v[3] = bf16_hi(q.w.y);
+}
+__device__ __forceinline__ void unpack(const Quad<float>& q, float v[4]) {
+  v[0] = __uint_as_float(q.w.x); v[1] = __uint_as_float(q.w.y);
+  v[2] = __uint_as_float(q.w.z); v[3] = __uint_as_float(q.w.w);
 }
 
-// Mass of tile t seen by one lane: the sum of its kTileLoads octets.
+// Masses of this lane's 8 elements of wave load g of the draw row: max(0,
+// p - q) (residual) or p.  q comes from the dense q row, or (QL) from the
+// drafter logit row and descriptor.  Every row here is read once per step:
+// non-temporal loads (measured over whole sampled steps at B=1024,
+// V=151936: 541 us, against 546 us with cached logit loads, whose 311 MB
+// evict from the Infinity Cache the hidden states the build reads next, and
+// 550 us with cached q loads).  VEC: V is a multiple of 8 and the rows 16-byte
+// aligned, so a quad lies wholly inside or wholly past the row; a quad past
+// it loads from the row's start and is masked.
+template <typename LT, bool VEC, bool QL>
+__device__ __forceinline__ void wave_load_mass(const DrawRow<LT>& R, long g, long V,
+                                               bool residual, float r[8]) {
+  const int l = lane_id();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const long e = g * kTile + h * (kTile / 2) + 4 * l;   // 512 g + 256 h + 4 l
+    float z[4], q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = 0.f;
+    if constexpr (VEC) {
+      const bool in = e < V;
+      const long ec = in ? e : 0;
+      Quad<LT> qz;
+      load_quad(R.zrow, ec, qz);
+      unpack(qz, z);
+      if (residual) {
+        if constexpr (QL) {
+          if (R.dzrow) {
+            Quad<LT> qd;
+            load_quad(R.dzrow, ec, qd);
+            float dz[4];
+            unpack(qd, dz);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) q[j] = drafter_q(R.desc, dz[j], ec + j);
+          }
+        } else {
+          Quad<float> qq;
+          load_quad(R.qrow, ec, qq);
+          unpack(qq, q);
+        }
+      }
+      if (!in) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { z[j] = -INFINITY; q[j] = 0.f; }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long ej = e + j;
+        z[j] = ej < V ? logit_at(R.zrow, ej) : -INFINITY;
+        if (residual && ej < V) {
+          if constexpr (QL) {
+            if (R.dzrow) q[j] = drafter_q(R.desc, logit_at(R.dzrow, ej), ej);
+          } else {
+            q[j] = R.qrow[ej];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(z[j], R.c, -R.Mc32)) * R.inv_s;
+      r[4 * h + j] = residual ? fmaxf(0.f, p - q[j]) : p;
+    }
+  }
+}
+
+// Mass of tile t seen by one lane: the sum of its masses in the tile's
+// kTileLoads wave loads.
 template <typename LT, bool VEC, bool QL>
 __device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool residual, int t, long V,
                                                 long nocts) {
+  (void)nocts;
   float ls = 0.f;
 #pragma unroll
   for (int sl = 0; sl < kTileLoads; ++sl) {
     float r[8];
-    const long o = ((long)t * kTileLoads + sl) * kWave + lane_id();
-    octet_mass<LT, VEC, QL>(R, o, V, nocts, residual, r);
+    wave_load_mass<LT, VEC, QL>(R, (long)t * kTileLoads + sl, V, residual, r);
     ls += tree_sum8(r);
   }
   return ls;
 }
 
-// verify_draw: wave 0 of every workgroup runs sequence b's accept scan
-// (chunk 0 writes its outputs); then chunk cidx of b computes the mass of
-// each of its tiles.  A tile is kTileLoads consecutive 512-element wave
-// loads; each lane sums its octets of the tile before one wave reduction.
-// With several chunks per sequence the masses go to the workspace for
-// verify_locate.  With one (C = 1: large batches, or rows of one tile) the
-// workgroup holds every mass of row a in LDS and wave 0 draws the token
-// itself, so no locate kernel runs; the workgroup is then the only reader of
-// the sequence's row partials and clears them after its scan.
-template <typename LT, int MODE, bool VEC, bool QL>
-__global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
-  __shared__ ScanResult scan;
-  __shared__ float s_tsum[kMaxTiles];
-  const int C = A.C, T = A.T;
-  const int b = blockIdx.x / C, cidx = blockIdx.x % C;
-  const bool whole = C == 1;
-  const long V = A.sc.V;
-  const long nocts = (V + 7) / 8;
-  if (threadIdx.x < kWave) {
-    const ScanResult r = draw_scan<LT, MODE, QL>(A.sc, b, cidx == 0, !whole);
-    if (whole) clear_partials(A.sc, b);
-    if (threadIdx.x == 0) scan = r;
-  }
-  __syncthreads();
-  const DrawRow<LT> R = draw_row<LT, QL>(A, b, scan);
-  if (R.c == 0.f) return;                     // greedy: its token is already written
-  const bool residual = R.residual;
-  float* tsum_g = A.tile_sums + (long)b * T;
-  const int t_lo = (int)((long)cidx * T / C), t_hi = (int)((long)(cidx + 1) * T / C);
-  const int w = threadIdx.x / kWave, l = lane_id();
-  for (int t0 = t_lo + w * kTileUnroll; t0 < t_hi; t0 += kWaves * kTileUnroll) {
-    float ls[kTileUnroll];
+// The token drawn inside tile `tile` of the draw row, whose masses this lane
+// holds in the layout above (r[sl]: wave load tile * kTileLoads + sl).  The
+// halves of the wave loads are walked in vocabulary order; tpre is the
+// running total before the tile and target = u * S.  Returns (on every lane)
+// the first element whose running total exceeds target; with `fallback`, or
+// when rounding leaves no crossing in the tile, its last element with
+// positive mass (0 if it has none).  Running totals are fp64.
+__device__ __forceinline__ int pick_in_draw_tile(const float (&r)[kTileLoads][8], long tile,
+                                                 double tpre, double target, bool fallback) {
+  const int l = lane_id();
+  int pick = -1, lastpos = -1;
+  double run0 = tpre;                // running total before the current half
 #pragma unroll
-    for (int j = 0; j < kTileUnroll; ++j)
-      ls[j] = lane_tile_mass<LT, VEC, QL>(R, residual, t0 + j, V, nocts);
+  for (int sl = 0; sl < kTileLoads; ++sl) {
 #pragma unroll
-    for (int j = 0; j < kTileUnroll; ++j) {
-      const float ts = wave_sum_f(ls[j]);
-      if (l == 0 && t0 + j < t_hi) {
-        if (whole) s_tsum[t0 + j] = ts;
-        else tsum_g[t0 + j] = ts;             // read by verify_locate
+    for (int h = 0; h < 2; ++h) {
+      const long e0 = (tile * kTileLoads + sl) * (long)kTile + h * (kTile / 2) + 4 * l;
+      const float* m = &r[sl][4 * h];
+      int lastj = -1;
+      for (int j = 3; j >= 0; --j) if (m[j] > 0.f) { lastj = (int)(e0 + j); break; }
+      const unsigned long long anyp = __ballot(lastj >= 0);
+      if (anyp) lastpos = __shfl(lastj, 63 - __clzll((long long)anyp));
+      if (fallback || pick >= 0) continue;
+      const double ls = (double)((m[0] + m[1]) + (m[2] + m[3]));
+      const double lincl = wave_inclusive_scan(ls);
+      double lexcl = __shfl_up(lincl, 1);
+      if (l == 0) lexcl = 0.0;
+      const unsigned long long cross = __ballot(run0 + lincl > target);
+      if (cross) {
+        const int src = __ffsll((long long)cross) - 1;
+        int mine = -1;
+        if (l == src) {
+          double lrun = run0 + lexcl;
+          for (int j = 0; j < 4; ++j) {
+            lrun += (double)m[j];
+            if (m[j] > 0.f && lrun > target) { mine = (int)(e0 + j); break; }
+          }
+          if (mine < 0)
+            for (int j = 3; j >= 0; --j) if (m[j] > 0.f) { mine = (int)(e0 + j); break; }
+        }
+        const unsigned long long got = __ballot(mine >= 0);
+        pick = got ? __shfl(mine, __ffsll((long long)got) - 1) : lastpos;
+        if (pick < 0) pick = 0;
       }
+      run0 += __shfl(lincl, kWave - 1);
     }
   }
-  if (!whole) return;
-  __syncthreads();
-  if (w != 0) return;
-  constexpr int kPer = kMaxTiles / kWave;
-  const int per = (T + kWave - 1) / kWave;
-  const int lo = min(T, l * per), hi = min(T, (l + 1) * per);
-  float ts[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) ts[j] = lo + j < hi ? s_tsum[lo + j] : 0.f;
-  const int K = A.sc.K;
-  const int pick = locate_in_masses<LT, VEC, QL, true>(
-      R, A.sc.uniforms[(long)b * (K + 1) + K], T, V, nocts, ts, s_tsum);
-  if (l == 0) A.sc.out_tokens[(long)b * (K + 1) + R.a] = pick;
+  // rounding left u*S at or past the tile's total: its last positive element
+  if (pick < 0) pick = lastpos >= 0 ? lastpos : 0;
+  return pick;
 }
 
 // The token drawn from row a of one sequence by one wave, given the row's T
@@ -557,11 +582,68 @@ __device__ __forceinline__ int locate_in_masses(const DrawRow<LT>& R, float u, i
   // rescan the tile: load its kTileLoads wave loads at once, then walk them
   float r[kTileLoads][8];
 #pragma unroll
-  for (int sl = 0; sl < kTileLoads; ++sl) {
-    const long o = ((long)tile * kTileLoads + sl) * kWave + l;
-    octet_mass<LT, VEC, QL>(R, o, V, nocts, residual, r[sl]);
+  for (int sl = 0; sl < kTileLoads; ++sl)
+    wave_load_mass<LT, VEC, QL>(R, (long)tile * kTileLoads + sl, V, residual, r[sl]);
+  return pick_in_draw_tile(r, tile, pre, target, fallback);
+}
+
+// verify_draw: wave 0 of every workgroup runs sequence b's accept scan
+// (chunk 0 writes its outputs); then chunk cidx of b computes the mass of
+// each of its tiles.  A tile is kTileLoads consecutive 512-element wave
+// loads; each lane sums its octets of the tile before one wave reduction.
+// With several chunks per sequence the masses go to the workspace for
+// verify_locate.  With one (C = 1: large batches, or rows of one tile) the
+// workgroup holds every mass of row a in LDS and wave 0 draws the token
+// itself, so no locate kernel runs; the workgroup is then the only reader of
+// the sequence's row partials and clears them after its scan.
+template <typename LT, int MODE, bool VEC, bool QL>
+__global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
+  __shared__ ScanResult scan;
+  __shared__ float s_tsum[kMaxTiles];
+  const int C = A.C, T = A.T;
+  const int b = blockIdx.x / C, cidx = blockIdx.x % C;
+  const bool whole = C == 1;
+  const long V = A.sc.V;
+  const long nocts = (V + 7) / 8;
+  if (threadIdx.x < kWave) {
+    const ScanResult r = draw_scan<LT, MODE, QL>(A.sc, b, cidx == 0, !whole);
+    if (whole) clear_partials(A.sc, b);
+    if (threadIdx.x == 0) scan = r;
   }
-  return pick_in_tile(r, tile, pre, target, fallback);
+  __syncthreads();
+  const DrawRow<LT> R = draw_row<LT, QL>(A, b, scan);
+  if (R.c == 0.f) return;                     // greedy: its token is already written
+  const bool residual = R.residual;
+  float* tsum_g = A.tile_sums + (long)b * T;
+  const int t_lo = (int)((long)cidx * T / C), t_hi = (int)((long)(cidx + 1) * T / C);
+  const int w = threadIdx.x / kWave, l = lane_id();
+  for (int t0 = t_lo + w * kTileUnroll; t0 < t_hi; t0 += kWaves * kTileUnroll) {
+    float ls[kTileUnroll];
+#pragma unroll
+    for (int j = 0; j < kTileUnroll; ++j)
+      ls[j] = lane_tile_mass<LT, VEC, QL>(R, residual, t0 + j, V, nocts);
+#pragma unroll
+    for (int j = 0; j < kTileUnroll; ++j) {
+      const float ts = wave_sum_f(ls[j]);
+      if (l == 0 && t0 + j < t_hi) {
+        if (whole) s_tsum[t0 + j] = ts;
+        else tsum_g[t0 + j] = ts;             // read by verify_locate
+      }
+    }
+  }
+  if (!whole) return;
+  __syncthreads();
+  if (w != 0) return;
+  constexpr int kPer = kMaxTiles / kWave;
+  const int per = (T + kWave - 1) / kWave;
+  const int lo = min(T, l * per), hi = min(T, (l + 1) * per);
+  float ts[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) ts[j] = lo + j < hi ? s_tsum[lo + j] : 0.f;
+  const int K = A.sc.K;
+  const int pick = locate_in_masses<LT, VEC, QL, true>(
+      R, A.sc.uniforms[(long)b * (K + 1) + K], T, V, nocts, ts, s_tsum);
+  if (l == 0) A.sc.out_tokens[(long)b * (K + 1) + R.a] = pick;
 }
 
 // verify_locate: one wave per sequence draws the token from the tile masses
