@@ -284,4 +284,85 @@ __device__ __forceinline__ int pick_in_tile(const float (&r)[kTileLoads][8], lon
   return pick;
 }
 
+// ---------------------------------------------------------------- quad layout
+// Element layout of the CDF tiles of the verify draw and the tree walk.  A
+// wave load g covers the 512 elements [512 g, 512 g + 512) of a row; lane l
+// holds the quads (4 consecutive elements) starting at 512 g + 4 l (half 0)
+// and 512 g + 256 + 4 l (half 1), so each load instruction of the wave reads
+// one contiguous block: 512 B of bf16 logits, 1 KB of fp32 q.  (With one
+// 8-element octet per lane the fp32 loads of a lane are two 16-byte loads 32
+// bytes apart: the workload-5 draw took 160 instead of 151 us.)
+template <typename LT> struct Quad;
+template <> struct Quad<uint16_t> { u32x2 w; };
+template <> struct Quad<float> { u32x4 w; };
+
+template <bool NT>
+__device__ __forceinline__ void load_quad(const uint16_t* row, long e, Quad<uint16_t>& q) {
+  q.w = ld8<NT>(row + e);
+}
+template <bool NT>
+__device__ __forceinline__ void load_quad(const float* row, long e, Quad<float>& q) {
+  q.w = ld16<NT>(row + e);
+}
+__device__ __forceinline__ void unpack(const Quad<uint16_t>& q, float v[4]) {
+  v[0] = bf16_lo(q.w.x); v[1] = bf16_hi(q.w.x); v[2] = bf16_lo(q.w.y); v[3] = bf16_hi(q.w.y);
+}
+__device__ __forceinline__ void unpack(const Quad<float>& q, float v[4]) {
+  v[0] = __uint_as_float(q.w.x); v[1] = __uint_as_float(q.w.y);
+  v[2] = __uint_as_float(q.w.z); v[3] = __uint_as_float(q.w.w);
+}
+
+// The token drawn inside CDF tile `tile` of a row whose masses this lane
+// holds in the quad layout (r[sl][4 h + j]: element 512 g + 256 h + 4 l + j
+// of wave load g = tile * kTileLoads + sl).  The
+// halves of the wave loads are walked in vocabulary order; tpre is the
+// running total before the tile and target = u * S.  Returns (on every lane)
+// the first element whose running total exceeds target; with `fallback`, or
+// when rounding leaves no crossing in the tile, its last element with
+// positive mass (0 if it has none).  Running totals are fp64.
+__device__ __forceinline__ int pick_in_quad_tile(const float (&r)[kTileLoads][8], long tile,
+                                                 double tpre, double target, bool fallback) {
+  const int l = lane_id();
+  int pick = -1, lastpos = -1;
+  double run0 = tpre;                // running total before the current half
+#pragma unroll
+  for (int sl = 0; sl < kTileLoads; ++sl) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const long e0 = (tile * kTileLoads + sl) * (long)kTile + h * (kTile / 2) + 4 * l;
+      const float* m = &r[sl][4 * h];
+      int lastj = -1;
+      for (int j = 3; j >= 0; --j) if (m[j] > 0.f) { lastj = (int)(e0 + j); break; }
+      const unsigned long long anyp = __ballot(lastj >= 0);
+      if (anyp) lastpos = __shfl(lastj, 63 - __clzll((long long)anyp));
+      if (fallback || pick >= 0) continue;
+      const double ls = (double)((m[0] + m[1]) + (m[2] + m[3]));
+      const double lincl = wave_inclusive_scan(ls);
+      double lexcl = __shfl_up(lincl, 1);
+      if (l == 0) lexcl = 0.0;
+      const unsigned long long cross = __ballot(run0 + lincl > target);
+      if (cross) {
+        const int src = __ffsll((long long)cross) - 1;
+        int mine = -1;
+        if (l == src) {
+          double lrun = run0 + lexcl;
+          for (int j = 0; j < 4; ++j) {
+            lrun += (double)m[j];
+            if (m[j] > 0.f && lrun > target) { mine = (int)(e0 + j); break; }
+          }
+          if (mine < 0)
+            for (int j = 3; j >= 0; --j) if (m[j] > 0.f) { mine = (int)(e0 + j); break; }
+        }
+        const unsigned long long got = __ballot(mine >= 0);
+        pick = got ? __shfl(mine, __ffsll((long long)got) - 1) : lastpos;
+        if (pick < 0) pick = 0;
+      }
+      run0 += __shfl(lincl, kWave - 1);
+    }
+  }
+  // rounding left u*S at or past the tile's total: its last positive element
+  if (pick < 0) pick = lastpos >= 0 ? lastpos : 0;
+  return pick;
+}
+
 }  // namespace sv

@@ -16,7 +16,8 @@
 //            rejection suffices; an accepted child becomes the current node;
 //            when every child is rejected, or the node is a leaf, the new
 //            token is drawn from the residual by inverse CDF (tile masses in
-//            LDS, then the in-tile search the chain draw uses).
+//            LDS, then the in-tile search the chain draw uses, over the same
+//            quad layout of elements across lanes).
 // All threads of a workgroup take the same decisions from the same values,
 // so the workgroup-wide passes sit in uniform control flow.
 #include "sv_device.h"
@@ -39,38 +40,54 @@ struct TreeArgs {
   float c;                 // log2(e) / T (sampled)
 };
 
-// Residual masses of the kTileLoads octets of tile t seen by this lane:
-// max(0, p - w q) with p = 2^(z c - Mc) * inv_s (residual = false: p).
+// Residual masses of this lane's elements of CDF tile t in the quad layout
+// (r[sl][4 h + j]: element 512 g + 256 h + 4 l + j of wave load g = t *
+// kTileLoads + sl): max(0, p - w q) with p = 2^(z c - Mc) * inv_s
+// (residual = false: p).  Cached loads: a node's rows are read again for
+// every rejection at that node.  VEC: V is a multiple of 8 and the rows
+// 16-byte aligned, so a quad lies wholly inside or wholly past the row; a
+// quad past it loads from the row's start and is masked.
 template <typename LT, bool VEC>
 __device__ __forceinline__ void tile_residual(const LT* zrow, const float* qrow, bool residual,
-                                              int t, long V, long nocts, float c, float Mc,
-                                              float inv_s, float w, float (&r)[kTileLoads][8]) {
+                                              int t, long V, float c, float Mc, float inv_s,
+                                              float w, float (&r)[kTileLoads][8]) {
   const int l = lane_id();
 #pragma unroll
   for (int sl = 0; sl < kTileLoads; ++sl) {
-    const long o = ((long)t * kTileLoads + sl) * kWave + l;
-    float z[8], q[8];
-    if constexpr (VEC) {
-      const long oc = o < nocts ? o : nocts - 1;
-      Raw<LT> rz;
-      raw_load<false>(zrow, oc, rz);
-      unpack(rz, z);
-      if (residual) {
-        Raw<float> rq;
-        raw_load<false>(qrow, oc, rq);
-        unpack(rq, q);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const long e = ((long)t * kTileLoads + sl) * kTile + h * (kTile / 2) + 4 * l;
+      float z[4], q[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[j] = 0.f;
+      if constexpr (VEC) {
+        const bool in = e < V;
+        const long ec = in ? e : 0;
+        Quad<LT> qz;
+        load_quad<false>(zrow, ec, qz);
+        unpack(qz, z);
+        if (residual) {
+          Quad<float> qq;
+          load_quad<false>(qrow, ec, qq);
+          unpack(qq, q);
+        }
+        if (!in) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { z[j] = -INFINITY; q[j] = 0.f; }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const long ej = e + j;
+          z[j] = ej < V ? logit_at(zrow, ej) : -INFINITY;
+          if (residual && ej < V) q[j] = qrow[ej];
+        }
       }
-      if (o >= nocts)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) z[j] = -INFINITY;
-    } else {
-      load_octet<false>(zrow, o, V, false, -INFINITY, z);
-      if (residual) load_octet<false>(qrow, o, V, false, 0.f, q);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(z[j], c, -Mc)) * inv_s;
-      r[sl][j] = residual ? fmaxf(0.f, fmaf(-w, q[j], p)) : p;
+      for (int j = 0; j < 4; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(z[j], c, -Mc)) * inv_s;
+        r[sl][4 * h + j] = residual ? fmaxf(0.f, fmaf(-w, q[j], p)) : p;
+      }
     }
   }
 }
@@ -79,13 +96,13 @@ __device__ __forceinline__ void tile_residual(const LT* zrow, const float* qrow,
 // same on every thread.  Called in uniform control flow.
 template <typename LT, bool VEC, int WAVES>
 __device__ __forceinline__ double residual_tiles(const LT* zrow, const float* qrow, bool residual,
-                                                 float w, long V, long nocts, int T_tiles, float c,
+                                                 float w, long V, int T_tiles, float c,
                                                  float Mc, float inv_s, float* tsum, double* red) {
   const int wv = threadIdx.x / kWave, l = lane_id();
   double part = 0.0;
   for (int t = wv; t < T_tiles; t += WAVES) {
     float r[kTileLoads][8];
-    tile_residual<LT, VEC>(zrow, qrow, residual, t, V, nocts, c, Mc, inv_s, w, r);
+    tile_residual<LT, VEC>(zrow, qrow, residual, t, V, c, Mc, inv_s, w, r);
     float ls = 0.f;
 #pragma unroll
     for (int sl = 0; sl < kTileLoads; ++sl) ls += tree_sum8(r[sl]);
@@ -112,7 +129,7 @@ __global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
 
   const TreeLaunch& L = A.L;
   const int b = blockIdx.x, N = L.N, t = threadIdx.x, S = A.S;
-  const long V = L.V, nocts = (V + 7) / 8;
+  const long V = L.V;
   const int T_tiles = (int)((V + kTileElems - 1) / kTileElems);
   if (t < N) {
     // node i = t + 1: its parent must precede it and its token lie in [0, V)
@@ -189,7 +206,7 @@ __global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
           final_pass = true;               // w = 0 here: the tiles of p
         }
         const double tot = residual_tiles<LT, VEC, WAVES>(zrow, qrow, w > 0.0, (float)w, V,
-                                                          nocts, T_tiles, c, Mc, inv_s, tsum, red);
+                                                          T_tiles, c, Mc, inv_s, tsum, red);
         if (final_pass) break;
         Sr = tot;
         tiles = true;
@@ -230,8 +247,8 @@ __global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
             fallback = true;
           }
           float r[kTileLoads][8];
-          tile_residual<LT, VEC>(zrow, qrow, residual, tile, V, nocts, c, Mc, inv_s, (float)w, r);
-          const int pick = pick_in_tile(r, tile, pre, target, fallback);
+          tile_residual<LT, VEC>(zrow, qrow, residual, tile, V, c, Mc, inv_s, (float)w, r);
+          const int pick = pick_in_quad_tile(r, tile, pre, target, fallback);
           if (l == 0) out[depth] = pick;
         }
         break;

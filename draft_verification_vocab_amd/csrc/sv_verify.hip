@@ -348,33 +348,8 @@ __device__ __forceinline__ DrawRow<LT> draw_row(const DrawArgs& A, int b, const 
   return r;
 }
 
-// Element layout of the draw's CDF tiles.  A wave load g covers the 512
-// elements [512 g, 512 g + 512) of a row; lane l holds the quads (4
-// consecutive elements) starting at 512 g + 4 l (half 0) and 512 g + 256 +
-// 4 l (half 1), so each load instruction of the wave reads one contiguous
-// block: 512 B of bf16 logits, 1 KB of fp32 q.  (With one 8-element octet
-// per lane the fp32 q loads of a lane were two 16-byte loads 32 bytes apart,
-// and the workload-5 draw took 160 instead of 150 us.)  r[4 h + j] is the
-// mass of element 512 g + 256 h + 4 l + j.
-template <typename LT> struct Quad;
-template <> struct Quad<uint16_t> { u32x2 w; };
-template <> struct Quad<float> { u32x4 w; };
-
-__device__ __forceinline__ void load_quad(const uint16_t* row, long e, Quad<uint16_t>& q) {
-  q.w = ld8<true>(row + e);
-}
-__device__ __forceinline__ void load_quad(const float* row, long e, Quad<float>& q) {
-  q.w = ld16<true>(row + e);
-}
-__device__ __forceinline__ void unpack(const Quad<uint16_t>& q, float v[4]) {
-  v[0] = bf16_lo(q.w.x); v[1] = bf16_hi(q.w.x); v[2] = bf16_lo(q.w.y); v[3] = bf16_hi(q.w.y);
-}
-__device__ __forceinline__ void unpack(const Quad<float>& q, float v[4]) {
-  v[0] = __uint_as_float(q.w.x); v[1] = __uint_as_float(q.w.y);
-  v[2] = __uint_as_float(q.w.z); v[3] = __uint_as_float(q.w.w);
-}
-
-// Masses of this lane's 8 elements of wave load g of the draw row: max(0,
+// Masses of this lane's 8 elements of wave load g of the draw row (the quad
+// layout: r[4 h + j] is element 512 g + 256 h + 4 l + j): max(0,
 // p - q) (residual) or p.  q comes from the dense q row, or (QL) from the
 // drafter logit row and descriptor.  Every row here is read once per step:
 // non-temporal loads (measured over whole sampled steps at B=1024,
@@ -397,13 +372,13 @@ __device__ __forceinline__ void wave_load_mass(const DrawRow<LT>& R, long g, lon
       const bool in = e < V;
       const long ec = in ? e : 0;
       Quad<LT> qz;
-      load_quad(R.zrow, ec, qz);
+      load_quad<true>(R.zrow, ec, qz);
       unpack(qz, z);
       if (residual) {
         if constexpr (QL) {
           if (R.dzrow) {
             Quad<LT> qd;
-            load_quad(R.dzrow, ec, qd);
+            load_quad<true>(R.dzrow, ec, qd);
             float dz[4];
             unpack(qd, dz);
 #pragma unroll
@@ -411,7 +386,7 @@ __device__ __forceinline__ void wave_load_mass(const DrawRow<LT>& R, long g, lon
           }
         } else {
           Quad<float> qq;
-          load_quad(R.qrow, ec, qq);
+          load_quad<true>(R.qrow, ec, qq);
           unpack(qq, q);
         }
       }
@@ -457,62 +432,10 @@ __device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool resid
   return ls;
 }
 
-// The token drawn inside tile `tile` of the draw row, whose masses this lane
-// holds in the layout above (r[sl]: wave load tile * kTileLoads + sl).  The
-// halves of the wave loads are walked in vocabulary order; tpre is the
-// running total before the tile and target = u * S.  Returns (on every lane)
-// the first element whose running total exceeds target; with `fallback`, or
-// when rounding leaves no crossing in the tile, its last element with
-// positive mass (0 if it has none).  Running totals are fp64.
-__device__ __forceinline__ int pick_in_draw_tile(const float (&r)[kTileLoads][8], long tile,
-                                                 double tpre, double target, bool fallback) {
-  const int l = lane_id();
-  int pick = -1, lastpos = -1;
-  double run0 = tpre;                // running total before the current half
-#pragma unroll
-  for (int sl = 0; sl < kTileLoads; ++sl) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const long e0 = (tile * kTileLoads + sl) * (long)kTile + h * (kTile / 2) + 4 * l;
-      const float* m = &r[sl][4 * h];
-      int lastj = -1;
-      for (int j = 3; j >= 0; --j) if (m[j] > 0.f) { lastj = (int)(e0 + j); break; }
-      const unsigned long long anyp = __ballot(lastj >= 0);
-      if (anyp) lastpos = __shfl(lastj, 63 - __clzll((long long)anyp));
-      if (fallback || pick >= 0) continue;
-      const double ls = (double)((m[0] + m[1]) + (m[2] + m[3]));
-      const double lincl = wave_inclusive_scan(ls);
-      double lexcl = __shfl_up(lincl, 1);
-      if (l == 0) lexcl = 0.0;
-      const unsigned long long cross = __ballot(run0 + lincl > target);
-      if (cross) {
-        const int src = __ffsll((long long)cross) - 1;
-        int mine = -1;
-        if (l == src) {
-          double lrun = run0 + lexcl;
-          for (int j = 0; j < 4; ++j) {
-            lrun += (double)m[j];
-            if (m[j] > 0.f && lrun > target) { mine = (int)(e0 + j); break; }
-          }
-          if (mine < 0)
-            for (int j = 3; j >= 0; --j) if (m[j] > 0.f) { mine = (int)(e0 + j); break; }
-        }
-        const unsigned long long got = __ballot(mine >= 0);
-        pick = got ? __shfl(mine, __ffsll((long long)got) - 1) : lastpos;
-        if (pick < 0) pick = 0;
-      }
-      run0 += __shfl(lincl, kWave - 1);
-    }
-  }
-  // rounding left u*S at or past the tile's total: its last positive element
-  if (pick < 0) pick = lastpos >= 0 ? lastpos : 0;
-  return pick;
-}
-
 // The token drawn from row a of one sequence by one wave, given the row's T
 // tile masses: lane l holds the masses of its contiguous run of tiles [lo,
 // hi) in ts (loaded by the caller).  u * S (S = the sum of the masses) picks
-// the tile, then the element inside it (pick_in_tile).  In the rare case
+// the tile, then the element inside it (pick_in_quad_tile).  In the rare case
 // that the residual has no mass (the drafter row sums to more than p_a) the
 // wave recomputes every tile mass of p_a into `masses` (global memory with
 // agent-coherent stores and loads, or LDS) and draws from p_a.
@@ -584,7 +507,7 @@ __device__ __forceinline__ int locate_in_masses(const DrawRow<LT>& R, float u, i
 #pragma unroll
   for (int sl = 0; sl < kTileLoads; ++sl)
     wave_load_mass<LT, VEC, QL>(R, (long)tile * kTileLoads + sl, V, residual, r[sl]);
-  return pick_in_draw_tile(r, tile, pre, target, fallback);
+  return pick_in_quad_tile(r, tile, pre, target, fallback);
 }
 
 // verify_draw: wave 0 of every workgroup runs sequence b's accept scan
