@@ -63,6 +63,34 @@ __device__ __forceinline__ void unpack(const Raw<float>& r, float v[8]) {
   v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
 }
 
+// ---------------------------------------------------------------- quad layout
+// Element layout of the CDF tiles of the verify draw and the tree walk.  A
+// wave load g covers the 512 elements [512 g, 512 g + 512) of a row; lane l
+// holds the quads (4 consecutive elements) starting at 512 g + 4 l (half 0)
+// and 512 g + 256 + 4 l (half 1), so each load instruction of the wave reads
+// one contiguous block: 512 B of bf16 logits, 1 KB of fp32 q.  (With one
+// 8-element octet per lane the fp32 loads of a lane are two 16-byte loads 32
+// bytes apart: the workload-5 draw took 160 instead of 151 us.)
+template <typename LT> struct Quad;
+template <> struct Quad<uint16_t> { u32x2 w; };
+template <> struct Quad<float> { u32x4 w; };
+
+template <bool NT>
+__device__ __forceinline__ void load_quad(const uint16_t* row, long e, Quad<uint16_t>& q) {
+  q.w = ld8<NT>(row + e);
+}
+template <bool NT>
+__device__ __forceinline__ void load_quad(const float* row, long e, Quad<float>& q) {
+  q.w = ld16<NT>(row + e);
+}
+__device__ __forceinline__ void unpack(const Quad<uint16_t>& q, float v[4]) {
+  v[0] = bf16_lo(q.w.x); v[1] = bf16_hi(q.w.x); v[2] = bf16_lo(q.w.y); v[3] = bf16_hi(q.w.y);
+}
+__device__ __forceinline__ void unpack(const Quad<float>& q, float v[4]) {
+  v[0] = __uint_as_float(q.w.x); v[1] = __uint_as_float(q.w.y);
+  v[2] = __uint_as_float(q.w.z); v[3] = __uint_as_float(q.w.w);
+}
+
 // ---------------------------------------------------------------- row-slice state
 struct SliceState {
   float best = -INFINITY;   // greedy: running max ...
@@ -87,8 +115,20 @@ __device__ __forceinline__ float tree_sum8(const float e[8]) {
 // form adds a 64-bit index and bound test, ~3x the instructions, and a search
 // runs on most steps because some lane of the wave almost always finds a new
 // maximum.
-template <int MODE, int N, int OSTRIDE, bool RANGED = true>
-__device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, long V, float c) {
+// Element offset of slot j (0..7) of an 8-element group from the group's
+// first octet o0: the octet's own elements, or (QUAD) lane l's two quads at
+// 4 l and 256 + 4 l of the wave's 512-element block starting at octet o0.
+// Either way the offsets grow with j, so a thread still meets its elements
+// in increasing index order.
+template <bool QUAD>
+__device__ __forceinline__ int slot_elem(int j, int l) {
+  if constexpr (QUAD) return j < 4 ? 4 * l + j : 252 + 4 * l + j;
+  else return j;
+}
+
+template <int MODE, int N, int OSTRIDE, bool RANGED = true, bool QUAD = false>
+__device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, long V, float c,
+                                     int l = 0) {
   float mt = v[0][0];
 #pragma unroll
   for (int u = 0; u < N; ++u)
@@ -102,7 +142,7 @@ __device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, l
         for (int u = N - 1; u >= 0; --u)
 #pragma unroll
           for (int j = 7; j >= 0; --j) {
-            const long e = (o0 + (long)u * OSTRIDE) * 8 + j;
+            const long e = (o0 + (long)u * OSTRIDE) * 8 + slot_elem<QUAD>(j, l);
             if (e < V && v[u][j] == mt) found = (int)e;
           }
       } else {
@@ -116,7 +156,8 @@ __device__ __forceinline__ void fold(SliceState& s, float (&v)[N][8], long o0, l
             if (v[u][j] == mt) su = u * 8 + j;
           slot = min(slot, su);
         }
-        if (slot < 64) found = (int)(o0 * 8) + (slot >> 3) * (OSTRIDE * 8) + (slot & 7);
+        if (slot < 64)
+          found = (int)(o0 * 8) + (slot >> 3) * (OSTRIDE * 8) + slot_elem<QUAD>(slot & 7, l);
       }
       if (found != INT32_MAX) { s.best = mt; s.idx = found; }
     }
@@ -156,6 +197,33 @@ __device__ __forceinline__ Partial slice_stats(const LT* row, long o_lo, long o_
   const int t = threadIdx.x;
   SliceState st;
   long base = o_lo + t;
+  if constexpr (VEC && sizeof(LT) == 4) {
+    // fp32 rows: the quad layout, so that each load instruction of a wave
+    // reads one contiguous kilobyte (with one octet per lane a lane's two
+    // 16-byte loads were 32 bytes apart, and the row kernel read fp32 logits
+    // at 6.1 TB/s against 6.9 TB/s for bf16).  The wave steps together while
+    // its whole block of each of the step's U wave loads lies in the slice;
+    // the rest of the slice goes through the per-octet loops below.
+    const int l = lane_id();
+    long wbase = base - l;                  // the wave's first octet of the step
+    for (; wbase + (kWave - 1) + (long)(U - 1) * THREADS < o_hi; wbase += (long)U * THREADS) {
+      Quad<LT> qa[U], qb[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const long e = (wbase + (long)u * THREADS) * 8 + 4 * l;
+        load_quad<NT>(row, e, qa[u]);
+        load_quad<NT>(row, e + kTile / 2, qb[u]);
+      }
+      float v[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        unpack(qa[u], &v[u][0]);
+        unpack(qb[u], &v[u][4]);
+      }
+      fold<MODE, U, THREADS, RANGED, true>(st, v, wbase, V, c, l);
+    }
+    base = wbase + l;
+  }
   if constexpr (VEC) {
     for (; base + (long)(U - 1) * THREADS < o_hi; base += (long)U * THREADS) {
       Raw<LT> raw[U];
@@ -282,34 +350,6 @@ __device__ __forceinline__ int pick_in_tile(const float (&r)[kTileLoads][8], lon
   // rounding left u*S at or past the tile's total: its last positive element
   if (pick < 0) pick = lastpos >= 0 ? lastpos : 0;
   return pick;
-}
-
-// ---------------------------------------------------------------- quad layout
-// Element layout of the CDF tiles of the verify draw and the tree walk.  A
-// wave load g covers the 512 elements [512 g, 512 g + 512) of a row; lane l
-// holds the quads (4 consecutive elements) starting at 512 g + 4 l (half 0)
-// and 512 g + 256 + 4 l (half 1), so each load instruction of the wave reads
-// one contiguous block: 512 B of bf16 logits, 1 KB of fp32 q.  (With one
-// 8-element octet per lane the fp32 loads of a lane are two 16-byte loads 32
-// bytes apart: the workload-5 draw took 160 instead of 151 us.)
-template <typename LT> struct Quad;
-template <> struct Quad<uint16_t> { u32x2 w; };
-template <> struct Quad<float> { u32x4 w; };
-
-template <bool NT>
-__device__ __forceinline__ void load_quad(const uint16_t* row, long e, Quad<uint16_t>& q) {
-  q.w = ld8<NT>(row + e);
-}
-template <bool NT>
-__device__ __forceinline__ void load_quad(const float* row, long e, Quad<float>& q) {
-  q.w = ld16<NT>(row + e);
-}
-__device__ __forceinline__ void unpack(const Quad<uint16_t>& q, float v[4]) {
-  v[0] = bf16_lo(q.w.x); v[1] = bf16_hi(q.w.x); v[2] = bf16_lo(q.w.y); v[3] = bf16_hi(q.w.y);
-}
-__device__ __forceinline__ void unpack(const Quad<float>& q, float v[4]) {
-  v[0] = __uint_as_float(q.w.x); v[1] = __uint_as_float(q.w.y);
-  v[2] = __uint_as_float(q.w.z); v[3] = __uint_as_float(q.w.w);
 }
 
 // The token drawn inside CDF tile `tile` of a row whose masses this lane

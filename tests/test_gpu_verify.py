@@ -120,6 +120,21 @@ def test_max_vocab(gpu):
     _sample_parity(gpu, logits, "bf16", q, d, u, 1.3)
 
 
+@pytest.mark.parametrize("V", [8992, 16392, 16387])
+def test_fp32_rows_wave_blocks(gpu, V):
+    """fp32 logits on rows long enough for the row kernel's wave-block loop
+    (B(K+1) = 2048 rows, one workgroup per row; each lane holds two quads of
+    a wave's 512-element block): the lowest-index argmax of every row on
+    tie-heavy logits, and sampling against the oracle.  V = 8992 leaves a
+    partial step for the per-octet loop, V = 16387 (not a multiple of 8) takes
+    the per-element loads."""
+    rng = np.random.default_rng(V)
+    B, K = 256, 7
+    logits, q, d, u = _random_case(rng, B, K, V, "f32", T=0.9, tie_heavy=True)
+    _greedy_parity(gpu, logits, "f32", d)
+    _sample_parity(gpu, logits, "f32", q, d, u, 0.9)
+
+
 def test_greedy_lowest_index_across_splits(gpu):
     B, K, V = 2, 1, 32000               # several workgroups share a row
     z = np.full((B, K + 1, V), -5.0, np.float32)
