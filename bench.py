@@ -60,8 +60,8 @@ def parse():
     ap.add_argument("--no-tree", action="store_true",
                     help="skip timing draft-tree verification")
     ap.add_argument("--no-small", action="store_true",
-                    help="skip timing the mid-size verify, the P-EAGLE build and the "
-                         "large-vocabulary verify workloads")
+                    help="skip timing the mid-size verify, the P-EAGLE build, the "
+                         "large-vocabulary verify workloads and the fp32-logit verify")
     ap.add_argument("--no-draft", action="store_true",
                     help="skip timing the drafter-output sampling kernel")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -668,6 +668,37 @@ def small_workloads_bench(sv, torch, np, synth, args):
     return res
 
 
+def fp32_bench(sv, torch, np, args, vi, z, q, d, u, ws):
+    """The workload-5 verify with its logits widened to fp32 (the same values,
+    4.98 GB): engines often hand the sampler fp32 logits."""
+    B, K, V = vi.spec.B, vi.spec.K, vi.spec.V
+    z32 = z.float()
+    out_t = torch.empty((B, K + 1), dtype=torch.int32, device=z.device)
+    acc_t = torch.empty(B, dtype=torch.int32, device=z.device)
+    res = {"workload": f"B={B} K={K} V={V} fp32 logits (the bf16 batch widened), "
+                       f"T={vi.temperature}"}
+
+    def sample():
+        sv.spec_verify_sample(z32, q, d, u, vi.temperature, out_tokens=out_t,
+                              out_num_accepted=acc_t, workspace=ws)
+
+    def greedy():
+        sv.spec_verify_greedy(z32, d, out_tokens=out_t, out_num_accepted=acc_t, workspace=ws)
+
+    for name, fn, smp, rows_k in (("sample", sample, True, "verify_sample_rows"),
+                                  ("greedy", greedy, False, "verify_greedy_rows")):
+        ms = wall_ms(torch, fn, args.warmup, args.steps)
+        kms = kernel_times(sv, torch, np, fn, args.steps)
+        rb, sb = verify_bytes(B, K, V, 4, acc_t.cpu().numpy(), sample=smp)
+        rk = kms[rows_k]
+        res[name] = {"ms_per_call": ms, "kernels_ms": kms, "algorithmic_bytes": rb + sb,
+                     "call_gbs": (rb + sb) / (ms * 1e-3) / 1e9,
+                     "rows_gbs": rb / (rk * 1e-3) / 1e9,
+                     "rows_frac": rb / (rk * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del z32
+    return res
+
+
 def tree_walk_passes(np, parents, path, num_accepted):
     """Row passes of the sampled tree walk, counted from its outputs.  At each
     node on the accepted path the walk tests the node's children in index
@@ -1066,6 +1097,8 @@ def main():
     if not args.no_small:
         res["small_workloads"] = small_workloads_bench(sv, torch, np, synth, args)
         log("smaller workloads timed")
+        res["fp32_logits"] = fp32_bench(sv, torch, np, args, vi, z, q, d, u, ws)
+        log("fp32 logits timed")
     if args.cpu_budget > 0:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(vi, bi, args.cpu_budget)
