@@ -103,12 +103,12 @@ __device__ __forceinline__ void store_q(float* qrow, long o, long V, const float
 
 // Four consecutive logits (quad qd = elements 4qd .. 4qd+3), cached loads:
 // sweep 2 re-reads the row sweep 1 has just read.
-__device__ __forceinline__ void load_quad(const uint16_t* row, long qd, float z[4]) {
+__device__ __forceinline__ void quad_at(const uint16_t* row, long qd, float z[4]) {
   const uint2 w = reinterpret_cast<const uint2*>(row)[qd];
   z[0] = __uint_as_float(w.x << 16); z[1] = __uint_as_float(w.x & 0xffff0000u);
   z[2] = __uint_as_float(w.y << 16); z[3] = __uint_as_float(w.y & 0xffff0000u);
 }
-__device__ __forceinline__ void load_quad(const float* row, long qd, float z[4]) {
+__device__ __forceinline__ void quad_at(const float* row, long qd, float z[4]) {
   const f32x4 v = reinterpret_cast<const f32x4*>(row)[qd];
   z[0] = v.x; z[1] = v.y; z[2] = v.z; z[3] = v.w;
 }
@@ -132,7 +132,7 @@ __device__ __forceinline__ void write_q_quads(const LT* zrow, float* qrow, long 
 #pragma unroll
     for (int j = 0; j < kQuadsPerLane; ++j) {
       const long qd = base + (long)j * kWave + l;
-      load_quad(zrow, qd < nquads ? qd : nquads - 1, z[j]);
+      quad_at(zrow, qd < nquads ? qd : nquads - 1, z[j]);
     }
 #pragma unroll
     for (int j = 0; j < kQuadsPerLane; ++j) {
