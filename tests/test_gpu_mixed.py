@@ -102,3 +102,29 @@ def test_invalid_temperatures_are_greedy_and_flagged(gpu):
         assert acc[b] == w_acc[b] and np.array_equal(out[b], w_out[b]), b
     # the clean workspace: a sampled call afterwards is unaffected
     _mixed_parity(gpu, vi, np.full(vi.spec.B, 0.9, np.float32))
+
+
+@pytest.mark.parametrize("V", [1000, 5000])
+def test_mixed_leaves_workspace_clear(gpu, V):
+    """Greedy and sampled sequences in one batch leave the workspace all zero,
+    with one draw workgroup per sequence (V = 1000: rows of one CDF tile, the
+    greedy sequences' workgroups stop after the scan) and with several (V =
+    5000, and the locate kernel)."""
+    from tests.test_gpu_verify import _random_case
+    rng = np.random.default_rng(V + 3)
+    B, K = 12, 5
+    logits, q, d, u = _random_case(rng, B, K, V, "f32", T=0.8)
+    temps = np.array([0.0, 0.8, 0.0, 1.2, 0.5, 0.0, 0.7, 0.9, 0.0, 1.0, 0.0, 0.6], np.float32)
+    ws = torch.zeros(gpu.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(2):
+        out, acc, _ = gpu.spec_verify_mixed(dev(logits), dev(q), dev(d), dev(u), dev(temps),
+                                            workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero().item()) == 0
+        outs.append((out.cpu().numpy(), acc.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    w_out, w_acc, _ = oracle.verify_mixed(logits, "f32", q, d, u, temps)
+    greedy = temps == 0
+    assert np.array_equal(outs[0][1][greedy], w_acc[greedy])
+    assert np.array_equal(outs[0][0][greedy], w_out[greedy])

@@ -182,9 +182,12 @@ def test_zero_draft_probability(gpu):
     assert acc[0] >= 1 and acc[2] >= 1 and acc[3] >= 1
 
 
-def test_residual_fallback_to_p(gpu):
-    # q = 2p: every test accepts with probability 1/2 and the residual is zero
-    B, K, V = 64, 3, 40
+@pytest.mark.parametrize("V", [40, 5000])
+def test_residual_fallback_to_p(gpu, V):
+    # q = 2p: every test accepts with probability 1/2 and the residual is zero.
+    # V = 40: one CDF tile, the draw workgroup searches the masses in LDS;
+    # V = 5000: several draw workgroups per sequence and the locate kernel.
+    B, K = 64, 3
     rng = np.random.default_rng(6)
     z = (2 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
     p = softmax(z.astype(np.float64), axis=2)
@@ -234,16 +237,27 @@ def test_empty_batch(gpu):
     assert out.shape == (0, 4) and acc.shape == (0,)
 
 
-def test_determinism_poison_and_clean_workspace(gpu):
-    vi = synth.make_verify_inputs(synth.verify_config(4), seqs=range(16))
-    args = [dev(vi.logits), dev(vi.draft_probs), dev(vi.draft_tokens), dev(vi.uniforms)]
-    ws = torch.zeros(gpu.spec_verify_workspace_bytes(16, 7, 201088), dtype=torch.uint8, device=DEV)
+@pytest.mark.parametrize("whole", [False, True])
+def test_determinism_poison_and_clean_workspace(gpu, whole):
+    """Two runs on poisoned outputs give identical bytes and leave the
+    workspace all zero: with several draw workgroups per sequence (and the
+    locate kernel), and with one draw workgroup per sequence (rows of one CDF
+    tile, V = 1000), where the draw workgroup clears the row partials."""
+    if whole:
+        rng = np.random.default_rng(12)
+        logits, q, d, u = _random_case(rng, 16, 7, 1000, "f32", T=0.7)
+        args, V, T = [dev(logits), dev(q), dev(d), dev(u)], 1000, 0.7
+    else:
+        vi = synth.make_verify_inputs(synth.verify_config(4), seqs=range(16))
+        args = [dev(vi.logits), dev(vi.draft_probs), dev(vi.draft_tokens), dev(vi.uniforms)]
+        V, T = 201088, vi.temperature
+    ws = torch.zeros(gpu.spec_verify_workspace_bytes(16, 7, V), dtype=torch.uint8, device=DEV)
     res = []
     for poison in (0x7F7F7F7F, -0x10101011):
         out = torch.full((16, 8), poison, dtype=torch.int32, device=DEV)
         acc = torch.full((16,), poison, dtype=torch.int32, device=DEV)
         pd = torch.full((16, 7), float("nan"), device=DEV)
-        gpu.spec_verify_sample(*args, vi.temperature, out_tokens=out, out_num_accepted=acc,
+        gpu.spec_verify_sample(*args, T, out_tokens=out, out_num_accepted=acc,
                                out_draft_target_prob=pd, workspace=ws)
         torch.cuda.synchronize()
         assert int(ws.count_nonzero().item()) == 0        # tickets reset by the kernel
