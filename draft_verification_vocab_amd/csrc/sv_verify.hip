@@ -17,8 +17,10 @@
 // store the mass r = max(0, p_a - q_a) (or p_K for the bonus token) of each
 // 2048-element tile in it.
 // verify_locate: one wave per sequence finds the tile whose running total
-// first exceeds u * S, rescans that one tile and writes the token.  Every
-// hand-off between workgroups goes through a kernel boundary.
+// first exceeds u * S, rescans that one tile and writes the token.  With one
+// draw workgroup per sequence (C = 1) that workgroup keeps the tile masses in
+// LDS and runs the same search itself, and no locate kernel is launched.
+// Every hand-off between workgroups goes through a kernel boundary.
 //
 // The verify flow is that of "Project 14 - speculative decoding inference
 // server", section 架构 (architecture): accept the prefix, resample the
@@ -419,9 +421,8 @@ __device__ __forceinline__ void wave_load_mass(const DrawRow<LT>& R, long g, lon
 // Mass of tile t seen by one lane: the sum of its masses in the tile's
 // kTileLoads wave loads.
 template <typename LT, bool VEC, bool QL>
-__device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool residual, int t, long V,
-                                                long nocts) {
-  (void)nocts;
+__device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool residual, int t,
+                                                long V) {
   float ls = 0.f;
 #pragma unroll
   for (int sl = 0; sl < kTileLoads; ++sl) {
@@ -441,8 +442,7 @@ __device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool resid
 // agent-coherent stores and loads, or LDS) and draws from p_a.
 template <typename LT, bool VEC, bool QL, bool IN_LDS>
 __device__ __forceinline__ int locate_in_masses(const DrawRow<LT>& R, float u, int T, long V,
-                                                long nocts, float (&ts)[kMaxTiles / kWave],
-                                                float* masses) {
+                                                float (&ts)[kMaxTiles / kWave], float* masses) {
   constexpr int kPer = kMaxTiles / kWave;
   const int l = lane_id();
   const int per = (T + kWave - 1) / kWave;
@@ -456,7 +456,7 @@ __device__ __forceinline__ int locate_in_masses(const DrawRow<LT>& R, float u, i
   if (residual && !(S > 0.0)) {
     residual = false;
     for (int t = 0; t < T; ++t) {
-      const float m = wave_sum_f(lane_tile_mass<LT, VEC, QL>(R, false, t, V, nocts));
+      const float m = wave_sum_f(lane_tile_mass<LT, VEC, QL>(R, false, t, V));
       if (l == 0) {
         if constexpr (IN_LDS) masses[t] = m;
         else st_coherent(&masses[t], m);
@@ -527,7 +527,6 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
   const int b = blockIdx.x / C, cidx = blockIdx.x % C;
   const bool whole = C == 1;
   const long V = A.sc.V;
-  const long nocts = (V + 7) / 8;
   if (threadIdx.x < kWave) {
     const ScanResult r = draw_scan<LT, MODE, QL>(A.sc, b, cidx == 0, !whole);
     if (whole) clear_partials(A.sc, b);
@@ -544,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
     float ls[kTileUnroll];
 #pragma unroll
     for (int j = 0; j < kTileUnroll; ++j)
-      ls[j] = lane_tile_mass<LT, VEC, QL>(R, residual, t0 + j, V, nocts);
+      ls[j] = lane_tile_mass<LT, VEC, QL>(R, residual, t0 + j, V);
 #pragma unroll
     for (int j = 0; j < kTileUnroll; ++j) {
       const float ts = wave_sum_f(ls[j]);
@@ -565,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
   for (int j = 0; j < kPer; ++j) ts[j] = lo + j < hi ? s_tsum[lo + j] : 0.f;
   const int K = A.sc.K;
   const int pick = locate_in_masses<LT, VEC, QL, true>(
-      R, A.sc.uniforms[(long)b * (K + 1) + K], T, V, nocts, ts, s_tsum);
+      R, A.sc.uniforms[(long)b * (K + 1) + K], T, V, ts, s_tsum);
   if (l == 0) A.sc.out_tokens[(long)b * (K + 1) + R.a] = pick;
 }
 
@@ -579,7 +578,6 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
   if (b >= A.sc.B) return;
   const int T = A.T, K = A.sc.K;
   const long V = A.sc.V;
-  const long nocts = (V + 7) / 8;
   const int l = lane_id();
   float* tsum_g = A.tile_sums + (long)b * T;
   // this sequence's tile masses, lanes owning contiguous runs of tiles; the
@@ -598,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
     return;
   }
   const int pick = locate_in_masses<LT, VEC, QL, false>(
-      R, A.sc.uniforms[(long)b * (K + 1) + K], T, V, nocts, ts, tsum_g);
+      R, A.sc.uniforms[(long)b * (K + 1) + K], T, V, ts, tsum_g);
   if (l == 0) A.sc.out_tokens[(long)b * (K + 1) + R.a] = pick;
   // leave this sequence's part of the workspace cleared
   for (int i = l; i < T; i += kWave) st_coherent(&tsum_g[i], 0.f);
