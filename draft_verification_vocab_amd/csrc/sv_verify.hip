@@ -67,8 +67,10 @@ int verify_splits(int B, int K, int V) {
   return s < 1 ? 1 : (int)s;
 }
 
-// Draw workgroups per sequence: about one round of resident workgroups over
-// the whole chip (256 CUs x 5 resident draw workgroups of 4 waves), since
+// Draw workgroups per sequence (for the batches below 256 sequences, and
+// mixed batches; see launch_verify for the rest): about one round of
+// resident workgroups over the whole chip (256 CUs x 5 resident draw
+// workgroups of 4 waves), since
 // every workgroup first waits on its sequence's accept scan.  Measured draw
 // times (V=151936 bf16 unless noted): B=64 (V=201088) 21 us at 20 chunks vs
 // 29 us at 64; B=128 27 vs 35 us at 32; B=256 45 vs 51 us at 16; B=1024
@@ -519,8 +521,9 @@ __device__ __forceinline__ int locate_in_masses(const DrawRow<LT>& R, float u, i
 // workgroup holds every mass of row a in LDS and wave 0 draws the token
 // itself, so no locate kernel runs; the workgroup is then the only reader of
 // the sequence's row partials and clears them after its scan.
-template <typename LT, int MODE, bool VEC, bool QL>
-__global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
+template <typename LT, int MODE, bool VEC, bool QL, int THREADS = kThreads>
+__global__ __launch_bounds__(THREADS) void verify_draw(DrawArgs A) {
+  constexpr int kDrawWaves = THREADS / kWave;
   __shared__ ScanResult scan;
   __shared__ float s_tsum[kMaxTiles];
   const int C = A.C, T = A.T;
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void verify_draw(DrawArgs A) {
   float* tsum_g = A.tile_sums + (long)b * T;
   const int t_lo = (int)((long)cidx * T / C), t_hi = (int)((long)(cidx + 1) * T / C);
   const int w = threadIdx.x / kWave, l = lane_id();
-  for (int t0 = t_lo + w * kTileUnroll; t0 < t_hi; t0 += kWaves * kTileUnroll) {
+  for (int t0 = t_lo + w * kTileUnroll; t0 < t_hi; t0 += kDrawWaves * kTileUnroll) {
     float ls[kTileUnroll];
 #pragma unroll
     for (int j = 0; j < kTileUnroll; ++j)
@@ -701,6 +704,14 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   DrawArgs D;
   D.sc = sc;
   D.C = mode == MIXED ? draw_chunks(L.B, L.V, true) : lay.C;
+  // From B = 256 (every CU gets a sequence) until the 256-thread rule above
+  // reaches one workgroup per sequence, one 1024-thread workgroup per
+  // sequence draws the token itself: measured at V = 151936 bf16 (wall time
+  // of the sampled verify) 146 against 154 us at B = 256 and 277 against
+  // 285 us at B = 512; at B = 128 the two are equal, and below that the
+  // chunked draw with its locate kernel is faster (B = 64: 54 against 59 us).
+  const bool wide = mode != MIXED && D.C > 1 && L.B >= 256;
+  if (wide) D.C = 1;
   D.T = lay.T;
   D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
   const dim3 grid3((unsigned)((long)L.B * D.C));
@@ -718,6 +729,7 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
 #define SV_DRAW(LT, VEC, QL) \
   do { \
     if (mode == MIXED && !QL) hipLaunchKernelGGL((verify_draw<LT, MIXED, VEC, false>), grid3, block, 0, stream, D); \
+    else if (wide) hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, QL, 4 * kThreads>), grid3, dim3(4 * kThreads), 0, stream, D); \
     else hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, QL>), grid3, block, 0, stream, D); \
   } while (0)
 #define SV_LOCATE(LT, VEC, QL) hipLaunchKernelGGL((verify_locate<LT, VEC, QL>), grid_acc, block, 0, stream, D)

@@ -163,7 +163,7 @@ SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
  * decision lies within ~1e-6 of its threshold.  Three kernels are enqueued:
  * row statistics; the accept scan with the residual / bonus masses of row a;
  * the draw of the new token from them.  When one workgroup covers each
- * sequence's row a (B >= 854, or V <= 2048) the second kernel also draws the
+ * sequence's row a (B >= 256, or V <= 2048) the second kernel also draws the
  * token and two kernels are enqueued.
  */
 SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
@@ -224,8 +224,8 @@ SV_API sv_status spec_verify_sample_lq(const void* target_logits, int logits_dty
  *                    lowest-index argmax and 0 elsewhere (the T -> 0 limit).
  * Results equal those of spec_verify_greedy / spec_verify_sample on each
  * sequence alone.  The same kernels as spec_verify_sample are enqueued (the
- * separate draw kernel whenever V > 2048); the draw and locate kernels stop
- * after the accept scan for greedy sequences.
+ * separate locate kernel whenever V > 2048, at every batch size); the draw
+ * and locate kernels stop after the accept scan for greedy sequences.
  */
 SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
                                    const float* draft_probs, const int32_t* draft_tokens,

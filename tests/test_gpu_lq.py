@@ -138,3 +138,20 @@ def test_lq_without_drafts(gpu):
     o2, a2, _ = gpu.spec_verify_sample(z, torch.zeros((3, 0, 64), device=DEV), d, u, 1.0)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(a1, a2)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 5000), ("f32", 4099)])
+def test_lq_matches_dense_mid_batch(gpu, dtype, V):
+    """B = 300 (one 1024-thread draw workgroup per sequence, which searches
+    the token itself): the drafter-logit verify equals the dense-q verify bit
+    for bit."""
+    B, K = 300, 3
+    rng = np.random.default_rng(V)
+    z = (3 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    zd = (3 * rng.standard_normal((B * K, V))).astype(np.float32)
+    if dtype == "bf16":
+        z, zd = synth.f32_to_bf16_bits(z), synth.f32_to_bf16_bits(zd)
+    ud = rng.random((B, K), dtype=np.float32)
+    uv = rng.random((B, K + 1), dtype=np.float32)
+    _, _, _, dense, lq = _chain(gpu, dev(z), dev(zd), K, 0.8, 0.9, dev(ud), dev(uv))
+    _same(dense, lq)

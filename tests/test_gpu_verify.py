@@ -322,3 +322,22 @@ def test_workspace_reuse_across_shapes(gpu):
         for b in range(0, B, max(1, B // 16)):
             check_sample_sequence(oracle.decode_logits(logits[b], dtype), q[b], d[b], u[b], 1.0,
                                   out[b].cpu().numpy(), acc[b].item())
+
+
+@pytest.mark.parametrize("dtype,B,V", [("bf16", 300, 5000), ("f32", 260, 4099)])
+def test_one_wide_draw_workgroup_per_sequence(gpu, dtype, B, V):
+    """Mid-size batches (256 <= B < 854) with rows of several CDF tiles: one
+    1024-thread draw workgroup per sequence searches the token itself (no
+    locate kernel); parity with the oracle, run-to-run identical outputs and
+    a workspace left all zero.  V = 4099 takes the per-element loads."""
+    rng = np.random.default_rng(B + V)
+    K = 3
+    logits, q, d, u = _random_case(rng, B, K, V, dtype, T=0.9)
+    _sample_parity(gpu, logits, dtype, q, d, u, 0.9)
+    ws = torch.zeros(gpu.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=DEV)
+    out, acc, _ = gpu.spec_verify_sample(dev(logits), dev(q), dev(d), dev(u), 0.9, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero().item()) == 0
+    out2, acc2, _ = gpu.spec_verify_sample(dev(logits), dev(q), dev(d), dev(u), 0.9, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(acc, acc2)
