@@ -341,3 +341,40 @@ def test_one_wide_draw_workgroup_per_sequence(gpu, dtype, B, V):
     out2, acc2, _ = gpu.spec_verify_sample(dev(logits), dev(q), dev(d), dev(u), 0.9, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(acc, acc2)
+
+
+def test_max_batch(gpu):
+    """B = SV_MAX_B sequences (K = 1, V = 16, fp32): every sequence against
+    the greedy definition (numpy lowest-index argmax) and, sampled, against
+    well-formedness and the support of the drawn token; a seeded sample of
+    sequences against the oracle."""
+    B, K, V, T = gpu.MAX_B, 1, 16, 1.0
+    rng = np.random.default_rng(20)
+    z = (2 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    q = softmax(z[:, :K].astype(np.float64) + rng.standard_normal((B, K, V)), axis=2)
+    cdf = np.cumsum(q[:, 0], axis=1)
+    d = np.minimum((cdf < rng.random((B, 1))).sum(axis=1), V - 1).astype(np.int32)[:, None]
+    q32 = q.astype(np.float32)
+    u = rng.random((B, K + 1), dtype=np.float32)
+    out, acc = gpu.spec_verify_greedy(dev(z), dev(d))
+    torch.cuda.synchronize()
+    out, acc = out.cpu().numpy(), acc.cpu().numpy()
+    g = np.argmax(z, axis=2)
+    want_a = (d[:, 0] == g[:, 0]).astype(np.int32)
+    assert np.array_equal(acc, want_a)
+    rows = np.arange(B)
+    assert np.array_equal(out[rows, acc], g[rows, acc])
+    assert np.all(out[acc == 0, 1] == -1)
+    out, acc, _ = gpu.spec_verify_sample(dev(z), dev(q32), dev(d), dev(u), T)
+    torch.cuda.synchronize()
+    out, acc = out.cpu().numpy(), acc.cpu().numpy()
+    assert np.all((acc == 0) | (acc == 1))
+    assert np.array_equal(out[acc == 1, 0], d[acc == 1, 0])
+    c = out[rows, acc]
+    assert np.all((c >= 0) & (c < V)) and np.all(out[acc == 0, 1] == -1)
+    p = softmax(z.astype(np.float64) / T, axis=2)
+    pc = p[rows, acc, c]
+    qc = np.where(acc == 0, q32[rows, 0, c].astype(np.float64), 0.0)
+    assert np.all(pc > qc * (1 - 1e-5))              # the residual's support (p for the bonus)
+    for b in rng.choice(B, 64, replace=False):
+        check_sample_sequence(z[b].astype(np.float64), q32[b], d[b], u[b], T, out[b], acc[b])
