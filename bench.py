@@ -49,7 +49,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-greedy", action="store_true")
@@ -550,6 +550,13 @@ def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, o
     return res
 
 
+def percentiles(np, xs):
+    """p10 / p50 / p90 of a list of times (ms)."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90))}
+
+
 def wall_ms(torch, call, warmup, steps):
     """Wall time per call (ms) of `steps` calls after `warmup` untimed ones."""
     for _ in range(warmup):
@@ -950,6 +957,17 @@ def main():
             wall = time.perf_counter() - t0
         per = {dom: [ms for _, ms in sv.trace_read()]}
         sv.trace_end()
+        # per-step GPU times: one event at every step boundary on the stream
+        # the library enqueues on
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        with quiet_host():
+            for i in range(args.steps):
+                evs[i].record()
+                step(sample)
+                build()
+            evs[-1].record()
+            torch.cuda.synchronize()
+        step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
         # the step's other kernels (named from one traced step), each timed in
         # a loop of its own with only that kernel traced: two events per step,
         # so no event sits between two other kernels of the step
@@ -970,9 +988,10 @@ def main():
             per[name] = [ms for _, ms in sv.trace_read()]
             sv.trace_end()
         acc = acc_t.cpu().numpy()
-        return wall / args.steps, {k: float(np.mean(v)) for k, v in per.items()}, acc
+        pct = {"step_ms": percentiles(np, step_ms), dom + "_ms": percentiles(np, per[dom])}
+        return wall / args.steps, {k: float(np.mean(v)) for k, v in per.items()}, acc, pct
 
-    sec_sample, kms, acc = timed(True)
+    sec_sample, kms, acc, pct_sample = timed(True)
     vb_rows, vb_draw = verify_bytes(B, K, V, 2, acc, sample=True)
     bb = build_bytes(B, K, H, 2)
     rows = B * (K + 1)
@@ -1010,6 +1029,7 @@ def main():
                                         "also re-reads logit row a"),
             "peagle_build": kinfo("peagle_build", bb),
         },
+        "percentiles": pct_sample,
         "acceptance": {"mean_accepted": float(acc.mean()),
                        "rate": float(acc.sum() / np.minimum(acc + 1, K).sum())},
     }
@@ -1033,7 +1053,7 @@ def main():
     res["read_ceiling"] = ceil
     log("sampled step timed")
     if not args.no_greedy:
-        sec_g, kmsg, accg = timed(False)
+        sec_g, kmsg, accg, pct_g = timed(False)
         vg_rows, vg_scan = verify_bytes(B, K, V, 2, accg, sample=False)
         g_ms = kmsg["verify_greedy_rows"]
         res["greedy_step"] = {"value": rows / sec_g, "unit": "verified logit rows/s",
@@ -1042,11 +1062,12 @@ def main():
                                                      "gbs": vg_rows / (g_ms * 1e-3) / 1e9,
                                                      "frac": vg_rows / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
                               "verify_greedy_accept_ms": kmsg["verify_greedy_accept"],
+                              "percentiles": pct_g,
                               "peagle_build_ms": kmsg["peagle_build"],
                               "step_hbm_gbs": (vg_rows + vg_scan + bb) / sec_g / 1e9,
                               "step_hbm_frac": (vg_rows + vg_scan + bb) / sec_g / 1e9 / HBM_PEAK_GBS}
     if not args.no_greedy:
-        sec_m, kmsm, accm = timed("mixed")
+        sec_m, kmsm, accm, _ = timed("mixed")
         sampled = temps_np > 0
         vm_rows, _ = verify_bytes(B, K, V, 2, accm, sample=True)
         # scan bytes: greedy sequences as in greedy mode, sampled ones as in sampling
