@@ -1124,6 +1124,11 @@ def main():
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(vi, bi, args.cpu_budget)
         res["cpu_baseline_all_cores"] = cpu_all
+        # the same algorithmic bytes per sequence as the GPU step
+        per_seq = res["step_bytes"] / B
+        for key in ("cpu_baseline", "cpu_baseline_all_cores"):
+            if res.get(key):
+                res[key]["gbs_algorithmic"] = res[key]["value"] / (K + 1) * per_seq / 1e9
     res["kernel_source_hash"] = kernel_source_hash()
     print(json.dumps(res), flush=True)
 
