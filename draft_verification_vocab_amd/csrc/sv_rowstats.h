@@ -1,6 +1,8 @@
-// Row statistics and CDF-tile helpers shared by the verify and drafter
+// Row statistics and CDF-tile helpers shared by the verify, drafter and tree
 // kernels (gfx950, wave64): the per-slice max / argmax / sum of exponentials,
-// and the search for a drawn token inside one CDF tile.
+// the quad layout of CDF tiles, and the search for a drawn token inside one
+// CDF tile (octet layout in the drafter, quad layout in the verify draw and
+// the tree walk).
 #pragma once
 
 #include <math.h>
@@ -286,16 +288,6 @@ __device__ __forceinline__ float wave_sum_f(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
   return x;
-}
-
-// Residual / bonus mass of one octet: r = max(0, p - q) or p, p = 2^(z c - Mc) * inv_s.
-__device__ __forceinline__ void mass_octet(const float z[8], const float q[8], bool residual,
-                                           float c, float Mc, float inv_s, float r[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(z[j], c, -Mc)) * inv_s;
-    r[j] = residual ? fmaxf(0.f, p - q[j]) : p;
-  }
 }
 
 // q(x) of a drafted row from its drafter logit z(x) and its descriptor: the
