@@ -135,6 +135,17 @@ def test_fp32_rows_wave_blocks(gpu, V):
     _sample_parity(gpu, logits, "f32", q, d, u, 0.9)
 
 
+def test_fp32_split_rows_wave_blocks(gpu):
+    """fp32 rows split over 16 workgroups (B(K+1) = 4 rows) whose slices of
+    ~2050 octets start at octets that are not multiples of 64: the wave-block
+    loop on unaligned slice starts, then the per-octet tail."""
+    rng = np.random.default_rng(262440)
+    B, K, V = 2, 1, 262440
+    logits, q, d, u = _random_case(rng, B, K, V, "f32", T=1.1, tie_heavy=True)
+    _greedy_parity(gpu, logits, "f32", d)
+    _sample_parity(gpu, logits, "f32", q, d, u, 1.1)
+
+
 def test_greedy_lowest_index_across_splits(gpu):
     B, K, V = 2, 1, 32000               # several workgroups share a row
     z = np.full((B, K + 1, V), -5.0, np.float32)
