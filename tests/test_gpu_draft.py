@@ -83,9 +83,11 @@ def test_ragged_vocabularies(gpu, V, dtype):
     assert np.array_equal(tok, tok2)
 
 
-def test_greedy_drafting_ties_and_no_uniforms(gpu):
+@pytest.mark.parametrize("V", [5000, 40000])
+def test_greedy_drafting_ties_and_no_uniforms(gpu, V):
+    # V = 40000 (fp32): long enough for the row statistics' wave-block loop
     rng = np.random.default_rng(3)
-    B, K, V = 3, 4, 5000
+    B, K = 3, 4
     z = rng.standard_normal((B * K, V)).astype(np.float32)
     for r in range(B * K):                 # ties at the max, across octets and tiles
         idx = rng.choice(V, size=3, replace=False)
