@@ -170,3 +170,36 @@ def test_metrics_at_max_drafts(gpu):
     got = m.cpu().numpy()
     assert np.array_equal(got[gpu.METRICS_HIST:], want["hist"])
     assert got[gpu.METRICS_ACCEPTED] == want["accepted"]
+
+
+@pytest.mark.parametrize("B", [300, 900])
+def test_step_graph_one_draw_workgroup_per_sequence(gpu, B):
+    """Sampled step graphs whose draw runs one workgroup per sequence and
+    draws the token itself (B = 300: 1024-thread workgroups; B = 900:
+    256-thread workgroups): replays with new uniforms equal the eager step."""
+    from tests.test_gpu_verify import _random_case
+    K, V, T = 3, 5000, 0.9
+    rng = np.random.default_rng(B)
+    logits, q, d, u = _random_case(rng, B, K, V, "f32", T=T)
+    inp = dict(z=dev(logits), q=dev(q), d=dev(d), u=dev(u), T=T)
+    b = _build_inputs(B, K, V)
+    og, oe = _outputs(B, K, V, 512), _outputs(B, K, V, 512)
+    ws_g = torch.zeros(gpu.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=DEV)
+    ws_e = torch.zeros_like(ws_g)
+    mg, me = gpu.accept_metrics_buffer(K, DEV), gpu.accept_metrics_buffer(K, DEV)
+    verify = dict(target_logits=inp["z"], draft_tokens=inp["d"], out_tokens=og["tok"],
+                  out_num_accepted=og["acc"], workspace=ws_g, draft_probs=inp["q"],
+                  uniforms=inp["u"], out_draft_target_prob=og["pd"], temperature=T)
+    graph = gpu.StepGraph("sample", verify, dict(b, outputs=og["build"]), metrics=mg)
+    for rep in range(3):
+        inp["u"].copy_(dev(rng.random((B, K + 1), dtype=np.float32)))
+        graph.launch()
+        _eager(gpu, "sample", inp, b, oe, ws_e, me)
+        torch.cuda.synchronize()
+        assert torch.equal(og["tok"], oe["tok"]) and torch.equal(og["acc"], oe["acc"]), rep
+        assert torch.equal(og["pd"].view(torch.int32), oe["pd"].view(torch.int32)), rep
+        for k in og["build"]:
+            assert torch.equal(og["build"][k], oe["build"][k]), (rep, k)
+    assert torch.equal(mg, me)
+    assert int(ws_g.count_nonzero().item()) == 0
+    graph.close()
