@@ -118,8 +118,14 @@ def test_fused_sample_every_sequence(gpu, fused):
     q_a(c), up to the fp32 rounding of p), p_K for a = K."""
     vi, bi, t, picks = fused
     B, K, T = vi.spec.B, vi.spec.K, vi.temperature
-    out_t, acc_t, _ = gpu.spec_verify_sample(t["z"], t["q"], t["d"], t["u"], T)
+    out_t, acc_t, pd_t = gpu.spec_verify_sample(t["z"], t["q"], t["d"], t["u"], T,
+                                                want_draft_target_prob=True)
+    out2, acc2, pd2 = gpu.spec_verify_sample(t["z"], t["q"], t["d"], t["u"], T,
+                                             want_draft_target_prob=True)
     torch.cuda.synchronize()
+    # run to run: bitwise identical (no floating-point atomics anywhere)
+    assert torch.equal(out_t, out2) and torch.equal(acc_t, acc2)
+    assert torch.equal(pd_t.view(torch.int32), pd2.view(torch.int32))
     out, acc = out_t.cpu().numpy(), acc_t.cpu().numpy()
     _well_formed(vi, out, acc)
     rows = np.arange(B)
