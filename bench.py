@@ -308,7 +308,7 @@ def ingest_trace(trace_csv, bench_log=None):
              f"python3 $REPO/bench.py --profile-steps 5 --hash-out $REPO/{tdir}/source_hash.txt",
              f"python bench.py --ingest-trace {trace_csv}" + (f" {bench_log}" if bench_log else ""),
              "```\n",
-             "`--profile-steps 5` runs, five times on the workload-5 inputs: a sampled, a greedy and "
+             "`--profile-steps 5` runs, five times on the B=1024 K=7 V=151936 bf16 inputs: a sampled, a greedy and "
              "a mixed verify each followed by the build, the drafter sampling with dense q and with "
              "row descriptors, the verify from drafter logits and the acceptance metrics; then five "
              "greedy and five sampled tree verifications (64 trees of 15 nodes, V=151936 bf16), one "
@@ -676,7 +676,7 @@ def small_workloads_bench(sv, torch, np, synth, args):
 
 
 def fp32_bench(sv, torch, np, args, vi, z, q, d, u, ws):
-    """The workload-5 verify with its logits widened to fp32 (the same values,
+    """The B=1024 K=7 V=151936 verify with its logits widened to fp32 (the same values,
     4.98 GB): engines often hand the sampler fp32 logits."""
     B, K, V = vi.spec.B, vi.spec.K, vi.spec.V
     z32 = z.float()

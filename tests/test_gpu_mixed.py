@@ -66,7 +66,7 @@ def test_mixed_ragged_vocabulary(gpu, dtype, V):
 
 
 def test_every_sequence_mode_in_one_batch(gpu):
-    # workload 2 has 8 sequences: give them every kind of temperature
+    # the mid-size verify batch (B=8, V=32000): every kind of temperature
     vi = synth.make_verify_inputs(synth.verify_config(2))
     temps = np.array([0.0, 0.5, 1.0, 0.0, 1.3, 0.7, 0.0, 2.0], dtype=np.float32)
     _mixed_parity(gpu, vi, temps)

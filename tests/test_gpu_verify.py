@@ -3,7 +3,8 @@
 Token ids and accept lengths are compared exactly; decisions that lie within
 1e-6 of their threshold may take either branch (the oracle enumerates the
 acceptable outcomes, see oracle.sample_outcomes); p_k(d_k) within 1e-5
-relative.  Workloads 1, 2 and 4 at full size, ragged and degenerate shapes,
+relative.  The tiny (B=1, V=32), mid-size (B=8, V=32000) and large-vocabulary
+(B=64, V=201088) workloads at full size, ragged and degenerate shapes,
 ties, -inf logits, zero draft probabilities, the residual fallback, final
 uniforms at 0 and just below 1, invalid draft tokens, determinism, and
 chi-square tests of the GPU's own outputs.
