@@ -704,14 +704,20 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   DrawArgs D;
   D.sc = sc;
   D.C = mode == MIXED ? draw_chunks(L.B, L.V, true) : lay.C;
-  // From B = 256 (every CU gets a sequence) until the 256-thread rule above
-  // reaches one workgroup per sequence, one 1024-thread workgroup per
-  // sequence draws the token itself: measured at V = 151936 bf16 (wall time
-  // of the sampled verify) 146 against 154 us at B = 256 and 277 against
-  // 285 us at B = 512; at B = 128 the two are equal, and below that the
-  // chunked draw with its locate kernel is faster (B = 64: 54 against 59 us).
-  const bool wide = mode != MIXED && D.C > 1 && L.B >= 256;
-  if (wide) D.C = 1;
+  // From B = 256 (every CU gets a sequence) one workgroup per sequence draws
+  // the token itself: measured at V = 151936 bf16 (wall time of the sampled
+  // verify) 146 against 154 us at B = 256 and 277 against 285 us at B = 512;
+  // at B = 128 the two are equal, and below that the chunked draw with its
+  // locate kernel is faster (B = 64: 54 against 59 us).  The workgroup is as
+  // wide as lets every draw workgroup be resident at once (the draw holds 5
+  // waves per SIMD, 20 per CU): 16 waves up to B = 256, 8 up to B = 512, 4
+  // above.  Draw kernel at V = 151936 bf16, 1024 / 512 / 256 threads:
+  // 46.8 / 48.3 / 61.2 us at B = 256, 70.3 / 67.6 / 71.3 at B = 384,
+  // 83.9 / 81.4 / 82.4 at B = 512, 106.4 / 119.6 / 101.3 at B = 640,
+  // 118.8 / 125.5 / 115.4 at B = 768.
+  const bool one = mode != MIXED && D.C > 1 && L.B >= 256;
+  const int dthreads = !one ? kThreads : L.B <= 256 ? 4 * kThreads : L.B <= 512 ? 2 * kThreads : kThreads;
+  if (one) D.C = 1;
   D.T = lay.T;
   D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
   const dim3 grid3((unsigned)((long)L.B * D.C));
@@ -729,7 +735,8 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
 #define SV_DRAW(LT, VEC, QL) \
   do { \
     if (mode == MIXED && !QL) hipLaunchKernelGGL((verify_draw<LT, MIXED, VEC, false>), grid3, block, 0, stream, D); \
-    else if (wide) hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, QL, 4 * kThreads>), grid3, dim3(4 * kThreads), 0, stream, D); \
+    else if (dthreads == 4 * kThreads) hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, QL, 4 * kThreads>), grid3, dim3(4 * kThreads), 0, stream, D); \
+    else if (dthreads == 2 * kThreads) hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, QL, 2 * kThreads>), grid3, dim3(2 * kThreads), 0, stream, D); \
     else hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, QL>), grid3, block, 0, stream, D); \
   } while (0)
 #define SV_LOCATE(LT, VEC, QL) hipLaunchKernelGGL((verify_locate<LT, VEC, QL>), grid_acc, block, 0, stream, D)

@@ -175,7 +175,7 @@ def test_metrics_at_max_drafts(gpu):
 @pytest.mark.parametrize("B", [300, 900])
 def test_step_graph_one_draw_workgroup_per_sequence(gpu, B):
     """Sampled step graphs whose draw runs one workgroup per sequence and
-    draws the token itself (B = 300: 1024-thread workgroups; B = 900:
+    draws the token itself (B = 300: 512-thread workgroups; B = 900:
     256-thread workgroups): replays with new uniforms equal the eager step."""
     from tests.test_gpu_verify import _random_case
     K, V, T = 3, 5000, 0.9

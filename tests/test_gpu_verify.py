@@ -336,12 +336,15 @@ def test_workspace_reuse_across_shapes(gpu):
                                   out[b].cpu().numpy(), acc[b].item())
 
 
-@pytest.mark.parametrize("dtype,B,V", [("bf16", 300, 5000), ("f32", 260, 4099)])
+@pytest.mark.parametrize("dtype,B,V", [("bf16", 256, 5000), ("f32", 256, 4099),
+                                        ("bf16", 300, 5000), ("f32", 260, 4099),
+                                        ("bf16", 700, 5000)])
 def test_one_wide_draw_workgroup_per_sequence(gpu, dtype, B, V):
     """Mid-size batches (256 <= B < 854) with rows of several CDF tiles: one
-    1024-thread draw workgroup per sequence searches the token itself (no
-    locate kernel); parity with the oracle, run-to-run identical outputs and
-    a workspace left all zero.  V = 4099 takes the per-element loads."""
+    draw workgroup per sequence searches the token itself (no locate
+    kernel), 1024 threads wide at B = 256, 512 at B = 300 and 260, 256 at
+    B = 700; parity with the oracle, run-to-run identical outputs and a
+    workspace left all zero.  V = 4099 takes the per-element loads."""
     rng = np.random.default_rng(B + V)
     K = 3
     logits, q, d, u = _random_case(rng, B, K, V, dtype, T=0.9)
