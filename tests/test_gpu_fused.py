@@ -8,7 +8,9 @@ output and the build invariants; a seeded sample of sequences is checked
 against the oracle one by one (the oracle's cost limits the sample), and every
 sequence against the greedy definition (numpy argmax chain) and against
 properties of rejection sampling (each accept test, the drawn token in the
-support of its distribution).
+support of its distribution).  The decode round with the drafter's q handed
+over as drafter logits + row descriptors is checked against the dense-q round
+bit for bit on every sequence.
 """
 import numpy as np
 import pytest
@@ -245,3 +247,47 @@ def test_fused_draft_sample(gpu, fused):
             assert np.allclose(qb[k], q, rtol=1e-5, atol=1e-30), (b, k)
             if tok[b, k] != d:
                 assert int(tok[b, k]) in oracle.draft_outcomes(z64, vi.temperature, u[b, k]), (b, k)
+
+
+def test_fused_lq_round(gpu, fused):
+    """A decode round at the bench shape with the drafter's q handed over as
+    logits + row descriptors: drafter sampling (the first K logit rows of each
+    sequence gathered through a row index, T = 0.7), then the verify from
+    drafter logits, which equals the dense-q verify for every sequence bit for
+    bit; sampled sequences checked against the oracle (q from the oracle's
+    drafter softmax, drafts from the oracle's drafter sampler)."""
+    vi, bi, t, picks = fused
+    B, K, V = vi.spec.B, vi.spec.K, vi.spec.V
+    rows = (np.arange(B, dtype=np.int32)[:, None] * (K + 1) + np.arange(K, dtype=np.int32)).copy()
+    ud = np.random.default_rng(7).random((B, K), dtype=np.float32)
+    zd, rows_t = t["z"].view(B * (K + 1), V), dev(rows)
+    tok_t, q_t, desc_t = gpu.spec_draft_sample(zd, K, vi.temperature, uniforms=dev(ud),
+                                               row_index=rows_t, want_row_desc=True)
+    dense = gpu.spec_verify_sample(t["z"], q_t, tok_t, t["u"], vi.temperature,
+                                   want_draft_target_prob=True)
+    del q_t
+    lq = gpu.spec_verify_sample_lq(t["z"], zd, desc_t, tok_t, t["u"], vi.temperature,
+                                   drafter_rows=rows_t, want_draft_target_prob=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dense[0], lq[0]) and torch.equal(dense[1], lq[1])
+    assert torch.equal(dense[2].view(torch.int32), lq[2].view(torch.int32))
+    tok = tok_t.cpu().numpy()
+    out, acc, pd = (x.cpu().numpy() for x in lq)
+    assert np.all((acc >= 0) & (acc <= K))
+    for b in range(B):
+        a = acc[b]
+        assert np.array_equal(out[b, :a], tok[b, :a]) and 0 <= out[b, a] < V
+        assert np.all(out[b, a + 1:] == -1)
+    Td = float(np.float32(vi.temperature))
+    checked = 0
+    for b in picks:
+        zq = [oracle.decode_logits(vi.logits[b, k], "bf16") for k in range(K)]
+        drafted = [oracle.draft.draft_sample_row(zq[k], Td, ud[b, k]) for k in range(K)]
+        od = np.array([x[0] for x in drafted], np.int32)
+        if not np.array_equal(tok[b], od):
+            continue                      # a flagged near tie in the draft itself
+        oq = np.stack([x[1] for x in drafted])
+        check_sample_sequence(oracle.decode_logits(vi.logits[b], "bf16"), oq, od, vi.uniforms[b],
+                              vi.temperature, out[b], acc[b], pd[b])
+        checked += 1
+    assert checked >= len(picks) - 1
