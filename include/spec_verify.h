@@ -81,8 +81,9 @@ typedef enum {
                                      precede it or whose token is outside [0, V): the
                                      node is treated as absent                         */
 #define SV_DEVERR_TEMPERATURE 16  /* a per-sequence temperature that is negative, NaN,
-                                     infinite or too small for 1/T to be finite:
-                                     that sequence is treated as greedy (T = 0)        */
+                                     infinite or too small for log2(e)/T to be a
+                                     finite fp32 (T < ~4.24e-39): that sequence is
+                                     treated as greedy (T = 0)                         */
 
 /* Limits (a call outside them returns SV_ERR_SHAPE). */
 #define SV_MAX_B (1 << 20)        /* sequences per call                               */
@@ -153,14 +154,18 @@ SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
  *   draft_probs      [B][K][V] fp32, the drafter's probabilities of each draft.
  *   draft_tokens     [B][K] int32, d[b][k] drawn from draft_probs[b][k].
  *   uniforms         [B][K+1] fp32 in [0, 1): [:, k<K] tests, [:, K] the draw.
- *   temperature      > 0 and finite, with 1/T finite in fp32; applies to the
- *                    target logits only.
+ *   temperature      > 0 and finite, with log2(e)/T finite in fp32 (T >= ~4.24e-39;
+ *                    smaller values return SV_ERR_VALUE); applies to the target
+ *                    logits only.
  *   out_tokens, out_num_accepted: as for spec_verify_greedy.
  *   out_draft_target_prob  optional [B][K] fp32: p_k(d[b][k]) for every k
  *                    (NULL = not written).
  * Arithmetic: fp32 exponentials, fp64 accumulation of every sum and of the
  * acceptance ratio; results agree with an fp64 evaluation except when a
- * decision lies within ~1e-6 of its threshold.  Three kernels are enqueued:
+ * decision lies within ~1e-6 of its threshold.  A logit whose |z|*log2(e)/T
+ * exceeds the fp32 range (possible only for T within a few powers of ten of
+ * the lower limit above) gives an unspecified but in-range token, like a NaN
+ * logit.  Three kernels are enqueued:
  * row statistics; the accept scan with the residual / bonus masses of row a;
  * the draw of the new token from them.  When one workgroup covers each
  * sequence's row a (B >= 256, or V <= 2048) the second kernel also draws the
@@ -217,8 +222,8 @@ SV_API sv_status spec_verify_sample_lq(const void* target_logits, int logits_dty
  *   out_num_accepted, workspace: as for spec_verify_sample; the draft_probs
  *                    rows and uniforms of greedy sequences are not read.
  *   temperatures     [B] fp32 device array.  A value that is negative, NaN,
- *                    infinite or too small for 1/T to be finite sets
- *                    SV_DEVERR_TEMPERATURE and verifies that sequence greedily.
+ *                    infinite or too small for log2(e)/T to be a finite fp32
+ *                    sets SV_DEVERR_TEMPERATURE and verifies that sequence greedily.
  *   out_draft_target_prob  optional [B][K]: p_k(d[b][k]) for sampled
  *                    sequences; for greedy ones 1 where d[b][k] is row k's
  *                    lowest-index argmax and 0 elsewhere (the T -> 0 limit).

@@ -16,9 +16,12 @@ Readings (the pages give no per-request interface):
       (``verify.verify_greedy_seq``); temperatures[b] > 0 selects rejection
       sampling at that temperature (``verify.verify_sample_seq``).  Draft
       probabilities and uniforms of greedy sequences are not used.
-* M2  a temperature that is negative, NaN, infinite, or so small that its
-      reciprocal overflows fp32 is invalid: that sequence is verified
-      greedily and flagged.
+* M2  a temperature that is negative, NaN or infinite is invalid, and so is
+      one so small that the exponent scale log2(e)/T, the factor with which
+      softmax(z/T) is evaluated as powers of two, is not a finite fp32
+      number (T below about 4.24e-39, a subnormal): that sequence is verified
+      greedily and flagged.  The pages fix no lower limit; this one is the
+      point below which z/T cannot be formed in fp32 at all.
 * M3  p_draft of a greedy sequence is the T -> 0 limit of p_k(d_k): 1 where
       d_k is row k's lowest-index argmax, else 0.
 """
@@ -40,7 +43,7 @@ def is_greedy(T: float) -> bool:
         return True                         # invalid (M2)
     with np.errstate(over="ignore"):
         c = np.float32(LOG2E / np.float64(T32))
-    return not np.isfinite(c)               # 1/T overflows fp32 (M2)
+    return not np.isfinite(c)               # log2(e)/T overflows fp32 (M2)
 
 
 def is_valid(T: float) -> bool:

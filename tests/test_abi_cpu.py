@@ -121,7 +121,12 @@ def test_verify_validation(lib):
     assert sample(lib, T=-1.0) == EVALUE
     assert sample(lib, T=float("inf")) == EVALUE
     assert sample(lib, T=float("nan")) == EVALUE
-    assert sample(lib, T=1e-45) == EVALUE           # 1/T overflows fp32
+    assert sample(lib, T=1e-45) == EVALUE           # log2(e)/T overflows fp32
+    # the boundary of that rule: log2(e)/3.5e-39 = 4.1e38 overflows (1/T = 2.9e38
+    # would not); log2(e)/4.5e-39 = 3.2e38 is finite (accepted: B = 0 is a no-op)
+    assert sample(lib, T=3.5e-39) == EVALUE
+    assert sample(lib, B=0, T=4.5e-39, logits=None, q=None, d=None, u=None, out=None, acc=None,
+                  ws=None, wsb=0) == OK
     assert sample(lib, q=None) == ENULL
     assert sample(lib, u=None) == ENULL
     assert sample(lib, u=FAKE + 2) == EALIGN

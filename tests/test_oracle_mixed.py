@@ -4,7 +4,7 @@
   different temperatures: within each temperature group the first emitted
   token follows scipy's softmax(z_0 / T) (chi-square), and the greedy group
   emits exactly numpy's argmax chain, whatever its uniforms.
-* M2's invalid temperatures (negative, NaN, infinite, 1/T overflowing fp32)
+* M2's invalid temperatures (negative, NaN, infinite, log2(e)/T overflowing fp32)
   verify greedily; the fp32 boundary of the overflow is checked directly.
 * M3: p_draft of a greedy sequence is 1 exactly where the draft is the
   lowest-index argmax of its row, by brute force.
@@ -75,13 +75,16 @@ def check_module(m):
             fails.append("sampled p_draft")
             break
     # invalid temperatures verify greedily
-    bad = np.array([-1.0, np.nan, np.inf, 1e-39, 1e-38], dtype=np.float32)
-    want_greedy = [True, True, True, True, False]
-    zb = np.broadcast_to(z, (5, K + 1, V))
-    db = np.broadcast_to(np.array(g[:K], np.int32), (5, K)).copy()
+    # 3.5e-39 is invalid under M2 (log2(e)/T = 4.1e38 > FLT_MAX = 3.40e38)
+    # although 1/T = 2.9e38 is finite; 4.5e-39 is valid (log2(e)/T = 3.2e38)
+    bad = np.array([-1.0, np.nan, np.inf, 1e-39, 1e-38, 3.5e-39, 4.5e-39], dtype=np.float32)
+    want_greedy = [True, True, True, True, False, True, False]
+    nb = len(bad)
+    zb = np.broadcast_to(z, (nb, K + 1, V))
+    db = np.broadcast_to(np.array(g[:K], np.int32), (nb, K)).copy()
     db[:, 0] = (g[0] + 1) % V            # row 0 rejected by the greedy rule
-    ub = np.full((5, K + 1), 0.999, np.float32)
-    outb, accb, _ = m.verify_mixed(zb, "f32", np.broadcast_to(q, (5, K, V)), db, ub, bad)
+    ub = np.full((nb, K + 1), 0.999, np.float32)
+    outb, accb, _ = m.verify_mixed(zb, "f32", np.broadcast_to(q, (nb, K, V)), db, ub, bad)
     for i, wg in enumerate(want_greedy):
         if m.is_greedy(bad[i]) != wg:
             fails.append(f"is_greedy({bad[i]})")

@@ -160,7 +160,9 @@ MIXED_MUTANTS = [
      "if T32 < 0.0:"),
     ("greedy p_draft always 1", ["verify_mixed_seq"],
      "1.0 if int(d[k]) == first_argmax(z_rows[k]) else 0.0", "1.0"),
-    ("overflowing 1/T sampled", ["is_greedy"], "return not np.isfinite(c)", "return False"),
+    ("overflowing log2(e)/T sampled", ["is_greedy"], "return not np.isfinite(c)", "return False"),
+    ("reciprocal rule instead of the exponent scale", ["is_greedy"],
+     "c = np.float32(LOG2E / np.float64(T32))", "c = np.float32(1.0 / np.float64(T32))"),
 ]
 
 
@@ -225,3 +227,32 @@ def test_tree_mutant_fails_pins(label, funcs, old, new):
     except (AssertionError, IndexError, KeyError, ValueError, ZeroDivisionError):
         fails = ["raised"]
     assert fails, f"mutant '{label}' passed the tree pins"
+
+
+OUTCOME_MUTANTS = [
+    ("near accept tie only walks on", ["sample_outcomes"],
+     "            walk(k + 1)\n            final(k)\n", "            walk(k + 1)\n"),
+    ("near accept tie only rejects", ["sample_outcomes"],
+     "            walk(k + 1)\n            final(k)\n", "            final(k)\n"),
+    ("accept-test flags never counted", ["sample_outcomes"],
+     "            flags += 1\n            walk(k + 1)", "            walk(k + 1)"),
+    ("draw flags never counted", ["sample_outcomes"],
+     "        if len(cands) > 1:\n            flags += 1", "        if False:\n            flags += 1"),
+    ("draw band ignored", ["_draw_candidates"], "if tol <= 0.0:", "if True:"),
+    ("draw band one-sided", ["_draw_candidates"], "(lo - tol <= target)", "(lo <= target)"),
+    ("zero-mass neighbours admitted", ["_draw_candidates"], "ok = (mass > 0.0) & ", "ok = "),
+    ("near test on the ratio's reciprocal", ["sample_outcomes"], "abs(uk - ratio) < tol",
+     "abs(uk - 1.0 / ratio) < tol"),
+]
+
+
+@pytest.mark.parametrize("label,funcs,old,new", OUTCOME_MUTANTS,
+                         ids=[m[0] for m in OUTCOME_MUTANTS])
+def test_outcome_mutant_fails_pins(label, funcs, old, new):
+    from tests.test_oracle_sample_exact import check_outcomes
+    m = _mutant_module(overify, funcs, old, new)
+    try:
+        fails = check_outcomes(m)
+    except (AssertionError, IndexError, ValueError, ZeroDivisionError):
+        fails = ["raised"]
+    assert fails, f"mutant '{label}' passed the near-tie enumerator pins"
