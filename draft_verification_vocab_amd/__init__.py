@@ -35,7 +35,8 @@ __all__ = [
     "require_library", "library_path", "sv_status_string", "spec_verify_workspace_bytes",
     "spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
     "SpecVerifyError", "SV_F32", "SV_BF16", "SV_F16", "PADDING_SLOT_ID",
-    "spec_verify_mixed", "spec_verify_sample_lq", "spec_verify_tree", "spec_draft_sample",
+    "spec_verify_mixed", "spec_verify_sample_lq", "spec_verify_sample_noalloc",
+    "noalloc_scratch_bytes", "spec_verify_tree", "spec_draft_sample",
     "spec_accept_metrics", "accept_metrics_buffer", "acceptance_summary", "StepGraph",
     "trace_begin", "trace_read", "trace_end",
     "DEVERR_DRAFT_TOKEN", "DEVERR_ACCEPT_COUNT", "DEVERR_BLOCK_TABLE",
@@ -62,6 +63,9 @@ _SIGS = {
                                 ctypes.c_size_t, _p, _p]),
     "peagle_build_draft_batch": (_i, [_p, _p, _p, _p, _p, _i, _i, _p, _p, _i, ctypes.c_int32,
                                       _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
+    "spec_verify_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "spec_verify_sample_noalloc": (_i, [_p, _i, _p, _p, _p, ctypes.c_float, _i, _i, _i, _p, _p,
+                                        _p, _p, _p]),
     "spec_verify_mixed": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p,
                                ctypes.c_size_t, _p, _p]),
     "spec_draft_sample": (_i, [_p, _i, ctypes.c_int64, _p, _p, ctypes.c_float, _p, _i, _i, _i,
@@ -275,6 +279,46 @@ def spec_verify_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor,
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _ptr(device_error), _stream(dev))
     _check(st, "spec_verify_sample")
+    return out_tokens, out_num_accepted, out_draft_target_prob
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the fixed scratch array spec_verify_sample_noalloc uses per GPU."""
+    return int(require_library().spec_verify_noalloc_scratch_bytes())
+
+
+def spec_verify_sample_noalloc(target_logits: torch.Tensor, draft_probs: torch.Tensor,
+                               draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                               temperature: float,
+                               out_tokens: torch.Tensor, out_num_accepted: torch.Tensor,
+                               out_draft_target_prob: Optional[torch.Tensor] = None,
+                               device_error: Optional[torch.Tensor] = None):
+    """spec_verify_sample without a workspace (see spec_verify_sample_noalloc in
+    include/spec_verify.h): the library takes its scratch from a fixed device
+    array, and the caller passes every output, so the call allocates nothing."""
+    lib = require_library()
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    _dev(target_logits, "target_logits")
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("target_logits must be float32 or bfloat16")
+    _dev(draft_probs, "draft_probs", torch.float32, (B, K, V), dev)
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _dev(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    _dev(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+    _dev(out_num_accepted, "out_num_accepted", torch.int32, (B,), dev)
+    if out_draft_target_prob is not None:
+        _dev(out_draft_target_prob, "out_draft_target_prob", torch.float32, (B, K), dev)
+    if device_error is not None:
+        _dev(device_error, "device_error", torch.int32, (1,), dev)
+    st = lib.spec_verify_sample_noalloc(
+        _ptr(target_logits), _DTYPES[target_logits.dtype], _ptr(draft_probs), _ptr(draft_tokens),
+        _ptr(uniforms), float(temperature), B, K, V, _ptr(out_tokens), _ptr(out_num_accepted),
+        _ptr(out_draft_target_prob), _ptr(device_error), _stream(dev))
+    _check(st, "spec_verify_sample_noalloc")
     return out_tokens, out_num_accepted, out_draft_target_prob
 
 

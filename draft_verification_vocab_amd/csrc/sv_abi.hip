@@ -75,6 +75,7 @@ SV_API const char* sv_status_string(int status) {
     case SV_ERR_WORKSPACE: return "workspace missing or too small";
     case SV_ERR_ALIGN: return "pointer not aligned to its element size";
     case SV_ERR_HIP: return "HIP launch failed";
+    case SV_ERR_SCRATCH: return "call needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -135,13 +136,20 @@ SV_API size_t spec_verify_workspace_bytes(int B, int K, int V) {
   return sv::verify_workspace_bytes(B, K, V);
 }
 
-// sample: 0 greedy, 1 one temperature, 2 per-sequence temperatures (mixed)
-static sv_status verify_common(const void* logits, int dtype, const float* draft_probs,
-                               const int32_t* draft_tokens, const float* uniforms,
-                               float temperature, const float* temperatures, int sample, int B,
-                               int K, int V, int32_t* out_tokens, int32_t* out_num_accepted,
-                               float* out_p_draft, void* workspace, size_t workspace_bytes,
-                               int32_t* device_error, void* stream) {
+}  // extern "C"
+
+namespace sv {
+
+// sample: 0 greedy, 1 one temperature, 2 per-sequence temperatures (mixed).
+// launch = false: validate every argument but the workspace and enqueue
+// nothing (the no-allocation entry point checks its call before it sets up
+// its scratch).
+sv_status verify_common(const void* logits, int dtype, const float* draft_probs,
+                        const int32_t* draft_tokens, const float* uniforms, float temperature,
+                        const float* temperatures, int sample, int B, int K, int V,
+                        int32_t* out_tokens, int32_t* out_num_accepted, float* out_p_draft,
+                        void* workspace, size_t workspace_bytes, int32_t* device_error,
+                        void* stream, bool launch) {
   sv_status st = check_verify_shape(B, K, V);
   if (st != SV_OK) return st;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
@@ -153,17 +161,18 @@ static sv_status verify_common(const void* logits, int dtype, const float* draft
   if (temperatures && !aligned(temperatures, 4)) return SV_ERR_ALIGN;
   if (!logits || !out_tokens || !out_num_accepted || (K > 0 && !draft_tokens)) return SV_ERR_NULL;
   if (sample && (!uniforms || (K > 0 && !draft_probs))) return SV_ERR_NULL;
-  if (!workspace) return SV_ERR_WORKSPACE;
-  if (workspace_bytes < sv::verify_workspace_bytes(B, K, V)) return SV_ERR_WORKSPACE;
+  if (launch && !workspace) return SV_ERR_WORKSPACE;
+  if (launch && workspace_bytes < sv::verify_workspace_bytes(B, K, V)) return SV_ERR_WORKSPACE;
   const size_t esz = dtype == SV_BF16 ? 2 : 4;
   if (!aligned(logits, esz) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
-      (draft_tokens && !aligned(draft_tokens, 4)) || !aligned(workspace, 16) ||
+      (draft_tokens && !aligned(draft_tokens, 4)) || (launch && !aligned(workspace, 16)) ||
       (device_error && !aligned(device_error, 4)))
     return SV_ERR_ALIGN;
   if (sample && (!aligned(uniforms, 4) || (draft_probs && !aligned(draft_probs, 4)) ||
                  (out_p_draft && !aligned(out_p_draft, 4))))
     return SV_ERR_ALIGN;
   if ((long)B * (K + 1) * sv::verify_splits(B, K, V) > 0x7fffffffL) return SV_ERR_SHAPE;
+  if (!launch) return SV_OK;
 
   sv::VerifyLaunch L;
   L.logits = logits;
@@ -189,14 +198,18 @@ static sv_status verify_common(const void* logits, int dtype, const float* draft
   return sv::launch_verify(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+}  // namespace sv
+
+extern "C" {
+
 SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
                                     const int32_t* draft_tokens, int B, int K, int V,
                                     int32_t* out_tokens, int32_t* out_num_accepted,
                                     void* workspace, size_t workspace_bytes,
                                     int32_t* device_error, void* stream) {
-  return verify_common(target_logits, logits_dtype, nullptr, draft_tokens, nullptr, 1.0f, nullptr,
-                       0, B, K, V, out_tokens, out_num_accepted, nullptr, workspace,
-                       workspace_bytes, device_error, stream);
+  return sv::verify_common(target_logits, logits_dtype, nullptr, draft_tokens, nullptr, 1.0f,
+                           nullptr, 0, B, K, V, out_tokens, out_num_accepted, nullptr, workspace,
+                           workspace_bytes, device_error, stream, true);
 }
 
 SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
@@ -205,9 +218,10 @@ SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
                                     int32_t* out_tokens, int32_t* out_num_accepted,
                                     float* out_draft_target_prob, void* workspace,
                                     size_t workspace_bytes, int32_t* device_error, void* stream) {
-  return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, uniforms,
-                       temperature, nullptr, 1, B, K, V, out_tokens, out_num_accepted,
-                       out_draft_target_prob, workspace, workspace_bytes, device_error, stream);
+  return sv::verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, uniforms,
+                           temperature, nullptr, 1, B, K, V, out_tokens, out_num_accepted,
+                           out_draft_target_prob, workspace, workspace_bytes, device_error, stream,
+                           true);
 }
 
 SV_API sv_status spec_verify_sample_lq(const void* target_logits, int logits_dtype,
@@ -275,9 +289,10 @@ SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
                                    int V, int32_t* out_tokens, int32_t* out_num_accepted,
                                    float* out_draft_target_prob, void* workspace,
                                    size_t workspace_bytes, int32_t* device_error, void* stream) {
-  return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, uniforms, 1.0f,
-                       temperatures, 2, B, K, V, out_tokens, out_num_accepted,
-                       out_draft_target_prob, workspace, workspace_bytes, device_error, stream);
+  return sv::verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, uniforms, 1.0f,
+                           temperatures, 2, B, K, V, out_tokens, out_num_accepted,
+                           out_draft_target_prob, workspace, workspace_bytes, device_error, stream,
+                           true);
 }
 
 SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,

@@ -58,7 +58,9 @@ typedef enum {
   SV_ERR_VALUE = 4,     /* scalar out of range (temperature <= 0 or not finite)*/
   SV_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required             */
   SV_ERR_ALIGN = 6,     /* pointer not aligned to its element size             */
-  SV_ERR_HIP = 7        /* the HIP runtime rejected a launch                   */
+  SV_ERR_HIP = 7,       /* the HIP runtime rejected a launch                   */
+  SV_ERR_SCRATCH = 8    /* the call needs more scratch than the no-allocation
+                           entry point holds (SV_NOALLOC_SCRATCH_BYTES)         */
 } sv_status;
 
 typedef enum {
@@ -180,6 +182,32 @@ SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
                                     float* out_draft_target_prob,
                                     void* workspace, size_t workspace_bytes,
                                     int32_t* device_error, void* stream);
+
+/*
+ * spec_verify_sample without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * must not allocate, harnesses that forbid hipMalloc.  Arguments, results and
+ * kernels are those of spec_verify_sample; the workspace is a fixed array of
+ * SV_NOALLOC_SCRATCH_BYTES in device memory that the library holds on each
+ * GPU it runs on until the process ends.  A call whose
+ * spec_verify_workspace_bytes(B, K, V) exceeds that size returns
+ * SV_ERR_SCRATCH and enqueues nothing.  The call allocates no memory: the
+ * first call on a device looks the array up and enqueues one fill kernel
+ * that clears it on `stream`; the verify kernels leave it all zero again.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams or threads without ordering between them)
+ * race and give undefined results; calls on one stream are ordered.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+SV_API size_t spec_verify_noalloc_scratch_bytes(void);   /* SV_NOALLOC_SCRATCH_BYTES */
+SV_API sv_status spec_verify_sample_noalloc(const void* target_logits, int logits_dtype,
+                                            const float* draft_probs,
+                                            const int32_t* draft_tokens,
+                                            const float* uniforms, float temperature,
+                                            int B, int K, int V,
+                                            int32_t* out_tokens, int32_t* out_num_accepted,
+                                            float* out_draft_target_prob,
+                                            int32_t* device_error, void* stream);
 
 /*
  * Sampled verify that takes the drafter's distributions as its logits plus a

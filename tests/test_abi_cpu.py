@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
               "spec_draft_sample", "spec_verify_mixed", "spec_verify_workspace_bytes",
               "sv_status_string", "spec_accept_metrics", "spec_accept_metrics_words",
               "sv_step_graph_create", "sv_step_graph_launch", "sv_step_graph_destroy",
-              "spec_verify_tree", "spec_verify_sample_lq"):
+              "spec_verify_tree", "spec_verify_sample_lq", "spec_verify_sample_noalloc",
+              "spec_verify_noalloc_scratch_bytes"):
         assert n in names
 
 
@@ -55,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = lib.sv_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
     assert lib.sv_status_string(OK) == b"ok"
@@ -354,3 +355,44 @@ def test_sample_lq_validation(lib):
     assert lq(lib, desc=FAKE + 8) == EALIGN
     assert lq(lib, dl=FAKE + 1) == EALIGN
     assert lq(lib, rows=FAKE + 2) == EALIGN
+
+
+ESCRATCH = 8
+
+
+def noalloc(lib, logits=FAKE, dtype=1, q=FAKE, d=FAKE, u=FAKE, T=1.0, B=2, K=3, V=64, out=FAKE,
+            acc=FAKE, pd=None, err=None):
+    return lib.spec_verify_sample_noalloc(logits, dtype, q, d, u, T, B, K, V, out, acc, pd, err,
+                                          None)
+
+
+def test_noalloc_validation(lib):
+    """The no-allocation sampled verify checks its arguments as spec_verify_sample
+    does, and rejects a call whose workspace would exceed its fixed scratch, all
+    before any HIP call (none of these reach the GPU)."""
+    assert lib.spec_verify_noalloc_scratch_bytes() == 8 << 20
+    assert noalloc(lib, B=-1) == ESHAPE
+    assert noalloc(lib, V=0) == ESHAPE
+    assert noalloc(lib, dtype=2) == EDTYPE
+    assert noalloc(lib, logits=None) == ENULL
+    assert noalloc(lib, q=None) == ENULL
+    assert noalloc(lib, u=None) == ENULL
+    assert noalloc(lib, out=None) == ENULL
+    assert noalloc(lib, T=0.0) == EVALUE
+    assert noalloc(lib, T=3.5e-39) == EVALUE
+    assert noalloc(lib, logits=FAKE + 1) == EALIGN
+    assert noalloc(lib, pd=FAKE + 2) == EALIGN
+    assert noalloc(lib, B=0, logits=None, q=None, d=None, u=None, out=None, acc=None) == OK
+    # the largest batch at K=7, V=151936 whose workspace fits, and the next one
+    cap = lib.spec_verify_noalloc_scratch_bytes()
+    lo, hi = 1, 1 << 20
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if lib.spec_verify_workspace_bytes(mid, 7, 151936) <= cap:
+            lo = mid
+        else:
+            hi = mid
+    assert lib.spec_verify_workspace_bytes(lo, 7, 151936) <= cap
+    assert lo >= 4096                     # far above the 1024-sequence serving batch
+    assert noalloc(lib, B=hi, K=7, V=151936) == ESCRATCH
+    assert lib.sv_status_string(ESCRATCH).startswith(b"call needs more scratch")
