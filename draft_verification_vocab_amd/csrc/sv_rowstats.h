@@ -22,7 +22,7 @@ enum Mode { GREEDY = 0, SAMPLE = 1, MIXED = 2 };   // MIXED: per-sequence temper
 
 // Exponent scale c = log2(e) / T of a sequence's temperature T, or 0 for a
 // greedy sequence: T = 0, or a temperature that is negative, NaN, infinite or
-// so small that 1/T overflows fp32 (`bad` is then set).
+// so small that c itself overflows fp32 (`bad` is then set).
 __device__ __forceinline__ float seq_scale(float T, bool& bad) {
   bad = false;
   if (T == 0.f) return 0.f;
