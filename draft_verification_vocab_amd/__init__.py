@@ -98,6 +98,9 @@ def library_path() -> str:
 def require_library():
     """Load libspecverify.so (raises if it has not been built)."""
     global _lib
+    lib = _lib
+    if lib is not None:
+        return lib
     with _lock:
         if _lib is None:
             if not os.path.exists(_LIB_PATH):
@@ -116,8 +119,15 @@ def sv_status_string(status: int) -> str:
     return require_library().sv_status_string(status).decode()
 
 
+_ws_bytes = {}
+
+
 def spec_verify_workspace_bytes(B: int, K: int, V: int) -> int:
-    return int(require_library().spec_verify_workspace_bytes(B, K, V))
+    key = (B, K, V)
+    n = _ws_bytes.get(key)
+    if n is None:
+        n = _ws_bytes[key] = int(require_library().spec_verify_workspace_bytes(B, K, V))
+    return n
 
 
 def _check(status: int, what: str):
@@ -158,28 +168,36 @@ def trace_end():
 _DTYPES = {torch.float32: SV_F32, torch.bfloat16: SV_BF16, torch.float16: SV_F16}
 
 
+# The checks below run on every call, so they use the cheapest tensor
+# queries (a small verify call spends more time here than on the GPU).
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if device is not None and t.device != device:
+    if device is not None and t.get_device() != device.index:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if dtype is not None and t.dtype != dtype:
+    if dtype is not None and t.dtype is not dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
 
 
-def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device):
+    """The current HIP stream of `device` (the library enqueues on it)."""
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 _ws_cache = {}

@@ -114,6 +114,17 @@ __device__ __forceinline__ void wave_argmax(float& m, int& g) {
   }
 }
 
+// 2^x for an fp64 argument x <= 0 with fp32 accuracy: 2^floor(x) exactly,
+// times the hardware fp32 exponential of the fraction (relative error ~1e-7,
+// that of every per-element exponential of the row statistics), at a few
+// instructions instead of the ~40 of an fp64 exp2.  Used to bring partial
+// sums of exponentials to a common reference.
+__device__ __forceinline__ double exp2_split(double x) {
+  if (!(x > -1074.0)) return 0.0;             // also -inf and NaN
+  const double n = floor(x);
+  return ldexp((double)__builtin_amdgcn_exp2f((float)(x - n)), (int)n);
+}
+
 __device__ __forceinline__ void flag_error(int32_t* device_error, int bit) {
   if (device_error) atomicOr(device_error, bit);
 }

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
 #pragma unroll
       for (int j = 0; j < kTreeSplits; ++j)
         if (j < S && pk[j].acc != 0.0)
-          s += pk[j].acc * exp2(((double)pk[j].m - (double)M) * (double)c);
+          s += pk[j].acc * exp2_split(((double)pk[j].m - (double)M) * (double)c);
     }
     const LT* zrow = zb + (long)cur * V;
     int nxt = -1;

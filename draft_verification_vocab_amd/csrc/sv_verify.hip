@@ -206,7 +206,7 @@ __device__ __forceinline__ ScanResult accept_scan(const ScanArgs& A, int b, bool
 #pragma unroll
       for (int j = 0; j < kMaxSplits; ++j)
         if (j < S && pk[j].acc != 0.0)
-          s_k += pk[j].acc * exp2(((double)pk[j].m - (double)M) * (double)c);
+          s_k += pk[j].acc * exp2_split(((double)pk[j].m - (double)M) * (double)c);
     }
   }
   int d = -1;
@@ -442,9 +442,19 @@ __device__ __forceinline__ float lane_tile_mass(const DrawRow<LT>& R, bool resid
 // that the residual has no mass (the drafter row sums to more than p_a) the
 // wave recomputes every tile mass of p_a into `masses` (global memory with
 // agent-coherent stores and loads, or LDS) and draws from p_a.
+struct TileChoice {
+  int tile;            // the CDF tile that holds u * S
+  int residual;        // the masses are those of the residual (else of p: the bonus,
+                       // or a residual that has no mass)
+  int fallback;        // rounding left u * S at or past the total: the tile's last
+                       // element with positive mass
+  double pre;          // running total before the tile
+  double target;       // u * S
+};
+
 template <typename LT, bool VEC, bool QL, bool IN_LDS>
-__device__ __forceinline__ int locate_in_masses(const DrawRow<LT>& R, float u, int T, long V,
-                                                float (&ts)[kMaxTiles / kWave], float* masses) {
+__device__ __forceinline__ TileChoice locate_tile(const DrawRow<LT>& R, float u, int T, long V,
+                                                  float (&ts)[kMaxTiles / kWave], float* masses) {
   constexpr int kPer = kMaxTiles / kWave;
   const int l = lane_id();
   const int per = (T + kWave - 1) / kWave;
@@ -503,13 +513,70 @@ __device__ __forceinline__ int locate_in_masses(const DrawRow<LT>& R, float u, i
     tile = anyp ? __shfl(last, 63 - __clzll((long long)anyp)) : 0;
     fallback = true;
   }
+  return TileChoice{tile, residual ? 1 : 0, fallback ? 1 : 0, pre, target};
+}
 
-  // rescan the tile: load its kTileLoads wave loads at once, then walk them
+// The drawn token inside the chosen tile: its kTileLoads wave loads are
+// loaded again (all at once) and walked.
+template <typename LT, bool VEC, bool QL>
+__device__ __forceinline__ int pick_in_choice(const DrawRow<LT>& R, const TileChoice& ch, long V) {
   float r[kTileLoads][8];
 #pragma unroll
   for (int sl = 0; sl < kTileLoads; ++sl)
-    wave_load_mass<LT, VEC, QL>(R, (long)tile * kTileLoads + sl, V, residual, r[sl]);
-  return pick_in_quad_tile(r, tile, pre, target, fallback);
+    wave_load_mass<LT, VEC, QL>(R, (long)ch.tile * kTileLoads + sl, V, ch.residual != 0, r[sl]);
+  return pick_in_quad_tile(r, ch.tile, ch.pre, ch.target, ch.fallback != 0);
+}
+
+template <typename LT, bool VEC, bool QL, bool IN_LDS>
+__device__ __forceinline__ int locate_in_masses(const DrawRow<LT>& R, float u, int T, long V,
+                                                float (&ts)[kMaxTiles / kWave], float* masses) {
+  const TileChoice ch = locate_tile<LT, VEC, QL, IN_LDS>(R, u, T, V, ts, masses);
+  return pick_in_choice<LT, VEC, QL>(R, ch, V);
+}
+
+// Rows of at most as many CDF tiles as a draw workgroup has waves: wave w
+// computes the masses of tile w once and keeps them in registers; wave 0
+// chooses the tile from their sums (in LDS), and the wave holding that tile
+// walks it without loading it again (unless the residual had no mass and
+// the choice fell back to p, whose masses wave 0 loads).  Lanes hold the
+// tile sums as locate_in_masses reads them (one tile per lane here), so the
+// choice and the token are those of that function.
+template <typename LT, bool VEC, bool QL, int THREADS>
+__device__ __forceinline__ void draw_from_tiles_in_registers(const DrawRow<LT>& R, float u, int T,
+                                                             long V, float* s_tsum,
+                                                             TileChoice* s_choice,
+                                                             int32_t* out_token) {
+  constexpr int kPer = kMaxTiles / kWave;
+  const int w = threadIdx.x / kWave, l = lane_id();
+  float r[kTileLoads][8];
+  if (w < T) {
+    float ls = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kTileLoads; ++sl) {
+      wave_load_mass<LT, VEC, QL>(R, (long)w * kTileLoads + sl, V, R.residual, r[sl]);
+      ls += tree_sum8(r[sl]);
+    }
+    const float ts = wave_sum_f(ls);
+    if (l == 0) s_tsum[w] = ts;
+  }
+  __syncthreads();
+  if (w == 0) {
+    float ts[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) ts[j] = j == 0 && l < T ? s_tsum[l] : 0.f;
+    const TileChoice ch = locate_tile<LT, VEC, QL, true>(R, u, T, V, ts, s_tsum);
+    if (l == 0) *s_choice = ch;
+    if (ch.residual != (R.residual ? 1 : 0)) {
+      const int pick = pick_in_choice<LT, VEC, QL>(R, ch, V);
+      if (l == 0) *out_token = pick;
+    }
+  }
+  __syncthreads();
+  const TileChoice ch = *s_choice;
+  if (ch.residual == (R.residual ? 1 : 0) && w == ch.tile) {
+    const int pick = pick_in_quad_tile(r, ch.tile, ch.pre, ch.target, ch.fallback != 0);
+    if (l == 0) *out_token = pick;
+  }
 }
 
 // verify_draw: wave 0 of every workgroup runs sequence b's accept scan
@@ -521,7 +588,11 @@ __device__ __forceinline__ int locate_in_masses(const DrawRow<LT>& R, float u, i
 // workgroup holds every mass of row a in LDS and wave 0 draws the token
 // itself, so no locate kernel runs; the workgroup is then the only reader of
 // the sequence's row partials and clears them after its scan.
-template <typename LT, int MODE, bool VEC, bool QL, int THREADS = kThreads>
+//
+// REG (rows of at most THREADS / 64 CDF tiles, one workgroup per sequence):
+// the tiles stay in registers and the token is drawn without loading any of
+// them again (draw_from_tiles_in_registers).
+template <typename LT, int MODE, bool VEC, bool QL, int THREADS = kThreads, bool REG = false>
 __global__ __launch_bounds__(THREADS) void verify_draw(DrawArgs A) {
   constexpr int kDrawWaves = THREADS / kWave;
   __shared__ ScanResult scan;
@@ -538,6 +609,14 @@ __global__ __launch_bounds__(THREADS) void verify_draw(DrawArgs A) {
   __syncthreads();
   const DrawRow<LT> R = draw_row<LT, QL>(A, b, scan);
   if (R.c == 0.f) return;                     // greedy: its token is already written
+  if constexpr (REG) {
+    __shared__ TileChoice s_choice;
+    const int K = A.sc.K;
+    draw_from_tiles_in_registers<LT, VEC, QL, THREADS>(
+        R, A.sc.uniforms[(long)b * (K + 1) + K], T, V, s_tsum, &s_choice,
+        &A.sc.out_tokens[(long)b * (K + 1) + R.a]);
+    return;
+  }
   const bool residual = R.residual;
   float* tsum_g = A.tile_sums + (long)b * T;
   const int t_lo = (int)((long)cidx * T / C), t_hi = (int)((long)(cidx + 1) * T / C);
@@ -704,6 +783,45 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   DrawArgs D;
   D.sc = sc;
   D.C = mode == MIXED ? draw_chunks(L.B, L.V, true) : lay.C;
+  D.T = lay.T;
+  D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
+  // Rows of at most 8 CDF tiles (V <= 16384), or 16 (V <= 32768) when the
+  // rows are vectorised (and not fp32 rows with q from the drafter logits,
+  // whose 1024-thread form would spill): one workgroup per sequence with a
+  // wave per tile draws the token from tiles kept in registers.
+  const bool reg16 = L.vec && !(ql && !L.bf16);
+  if (lay.T <= 8 || (lay.T <= 16 && reg16)) {
+    D.C = 1;
+    const int th = lay.T <= 4 ? kThreads : lay.T <= 8 ? 2 * kThreads : 4 * kThreads;
+    const dim3 grid3((unsigned)L.B);
+#define SV_DRAW_REG(LT, VEC, TH) \
+  do { \
+    if (mode == MIXED) hipLaunchKernelGGL((verify_draw<LT, MIXED, VEC, false, TH, true>), grid3, dim3(TH), 0, stream, D); \
+    else if (ql) hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, true, TH, true>), grid3, dim3(TH), 0, stream, D); \
+    else hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, false, TH, true>), grid3, dim3(TH), 0, stream, D); \
+  } while (0)
+#define SV_DRAW_REG_SMALL(LT, VEC) \
+  do { \
+    if (th == kThreads) SV_DRAW_REG(LT, VEC, kThreads); \
+    else SV_DRAW_REG(LT, VEC, 2 * kThreads); \
+  } while (0)
+    trace_before(stream, SV_KERNEL_VERIFY_SAMPLE_DRAW);
+    if (th == 4 * kThreads) {                // vectorised rows only (reg16)
+      constexpr int TH = 4 * kThreads;
+      if (L.bf16) SV_DRAW_REG(uint16_t, true, TH);
+      else if (mode == MIXED) hipLaunchKernelGGL((verify_draw<float, MIXED, true, false, TH, true>), grid3, dim3(TH), 0, stream, D);
+      else hipLaunchKernelGGL((verify_draw<float, SAMPLE, true, false, TH, true>), grid3, dim3(TH), 0, stream, D);
+    } else if (L.bf16) {
+      if (L.vec) SV_DRAW_REG_SMALL(uint16_t, true); else SV_DRAW_REG_SMALL(uint16_t, false);
+    } else {
+      if (L.vec) SV_DRAW_REG_SMALL(float, true); else SV_DRAW_REG_SMALL(float, false);
+    }
+#undef SV_DRAW_REG_SMALL
+#undef SV_DRAW_REG
+    err = hipGetLastError();
+    trace_after(stream, SV_KERNEL_VERIFY_SAMPLE_DRAW);
+    return err;
+  }
   // From B = 256 (every CU gets a sequence) one workgroup per sequence draws
   // the token itself: measured at V = 151936 bf16 (wall time of the sampled
   // verify) 146 against 154 us at B = 256 and 277 against 285 us at B = 512;
@@ -718,8 +836,6 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   const bool one = mode != MIXED && D.C > 1 && L.B >= 256;
   const int dthreads = !one ? kThreads : L.B <= 256 ? 4 * kThreads : L.B <= 512 ? 2 * kThreads : kThreads;
   if (one) D.C = 1;
-  D.T = lay.T;
-  D.tile_sums = reinterpret_cast<float*>(ws + lay.tile);
   const dim3 grid3((unsigned)((long)L.B * D.C));
 #define SV_DRAW_KERNELS(LAUNCH) \
   do { \

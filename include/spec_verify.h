@@ -170,8 +170,9 @@ SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
  * logit.  Three kernels are enqueued:
  * row statistics; the accept scan with the residual / bonus masses of row a;
  * the draw of the new token from them.  When one workgroup covers each
- * sequence's row a (B >= 256, or V <= 2048) the second kernel also draws the
- * token and two kernels are enqueued.
+ * sequence's row a (B >= 256, or rows of at most 8 CDF tiles of 2048
+ * elements, 16 for 16-byte-aligned rows with V a multiple of 8) the second
+ * kernel also draws the token and two kernels are enqueued.
  */
 SV_API sv_status spec_verify_sample(const void* target_logits, int logits_dtype,
                                     const float* draft_probs,

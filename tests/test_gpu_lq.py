@@ -140,12 +140,13 @@ def test_lq_without_drafts(gpu):
     assert torch.equal(o1, o2) and torch.equal(a1, a2)
 
 
-@pytest.mark.parametrize("dtype,V,B", [("bf16", 5000, 300), ("f32", 4099, 300),
-                                        ("bf16", 5000, 256), ("f32", 4099, 700)])
+@pytest.mark.parametrize("dtype,V,B", [("bf16", 40000, 300), ("f32", 40001, 300),
+                                        ("bf16", 40000, 256), ("f32", 40001, 700)])
 def test_lq_matches_dense_mid_batch(gpu, dtype, V, B):
-    """Mid-size batches, one draw workgroup per sequence which searches the
-    token itself (1024 threads at B = 256, 512 at B = 300, 256 at B = 700):
-    the drafter-logit verify equals the dense-q verify bit for bit."""
+    """Mid-size batches with rows of more than 16 CDF tiles, one draw
+    workgroup per sequence which searches the token itself (1024 threads at
+    B = 256, 512 at B = 300, 256 at B = 700): the drafter-logit verify equals
+    the dense-q verify bit for bit."""
     K = 3
     rng = np.random.default_rng(V + B)
     z = (3 * rng.standard_normal((B, K + 1, V))).astype(np.float32)

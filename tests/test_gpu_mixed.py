@@ -104,12 +104,12 @@ def test_invalid_temperatures_are_greedy_and_flagged(gpu):
     _mixed_parity(gpu, vi, np.full(vi.spec.B, 0.9, np.float32))
 
 
-@pytest.mark.parametrize("V", [1000, 5000])
+@pytest.mark.parametrize("V", [1000, 5000, 40000])
 def test_mixed_leaves_workspace_clear(gpu, V):
     """Greedy and sampled sequences in one batch leave the workspace all zero,
-    with one draw workgroup per sequence (V = 1000: rows of one CDF tile, the
-    greedy sequences' workgroups stop after the scan) and with several (V =
-    5000, and the locate kernel)."""
+    with one draw workgroup per sequence (V = 1000 and 5000: rows of one and
+    three CDF tiles kept in registers; the greedy sequences' workgroups stop
+    after the scan) and with several (V = 40000, and the locate kernel)."""
     from tests.test_gpu_verify import _random_case
     rng = np.random.default_rng(V + 3)
     B, K = 12, 5
