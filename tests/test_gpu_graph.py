@@ -5,9 +5,11 @@
   counts flagged and clamped.
 * A step graph (verify, build, metrics) replayed several times with new
   inputs copied into its buffers and eager calls on other buffers in
-  between: every replay must equal the eager step on the same inputs bit for
-  bit, and the metrics must equal the oracle's counters of all replays.
-  Greedy, sampled and mixed graphs.
+  between: every replay must match the oracle on that replay's inputs (the
+  verify outputs of every sequence, greedy ones exactly and sampled ones up
+  to 1e-6 near ties; the build bit for bit), equal the eager step on the
+  same inputs bit for bit, and the metrics must equal the oracle's counters
+  of all replays.  Greedy, sampled and mixed graphs.
 """
 import numpy as np
 import pytest
@@ -16,7 +18,7 @@ import torch
 import oracle
 import synth
 from synth.workloads import BuildSpec
-from tests.gpu_util import DEV, dev
+from tests.gpu_util import DEV, check_sample_sequence, dev, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +59,32 @@ def _build_inputs(B, K, V):
     bi = synth.make_build_inputs(BuildSpec(0, B, K, 512, V, 16, 700, 16, 77, False))
     return dict(start_pos=dev(bi.start_pos), block_table=dev(bi.block_table),
                 block_size=bi.spec.block_size, target_hidden=dev(bi.target_hidden),
-                h_shared=dev(bi.h_shared), mask_token_id=bi.mask_token_id)
+                h_shared=dev(bi.h_shared), mask_token_id=bi.mask_token_id, host=bi)
+
+
+def _replay_matches_oracle(mode, logits, dtype, q, d, u, T, temps, o, bi):
+    """One replay's outputs against the oracle on the inputs it read: every
+    sequence's verify outputs, then the build from those outputs bit for bit."""
+    tok, acc, pd = o["tok"].cpu().numpy(), o["acc"].cpu().numpy(), o["pd"].cpu().numpy()
+    B = logits.shape[0]
+    if mode == "greedy":
+        w_out, w_acc = oracle.verify_greedy(logits, dtype, d)
+        assert np.array_equal(acc, w_acc) and np.array_equal(tok, w_out)
+    for b in range(B if mode != "greedy" else 0):
+        Tb = T if mode == "sample" else float(temps[b])
+        if mode == "mixed" and oracle.mixed.is_greedy(temps[b]):
+            w_out, w_acc, w_pd = oracle.verify_mixed(logits[b:b + 1], dtype, q[b:b + 1],
+                                                     d[b:b + 1], u[b:b + 1], temps[b:b + 1])
+            assert acc[b] == w_acc[0] and np.array_equal(tok[b], w_out[0]), b
+            assert np.array_equal(pd[b], w_pd[0].astype(np.float32)), b
+        else:
+            check_sample_sequence(oracle.decode_logits(logits[b], dtype), q[b], d[b], u[b], Tb,
+                                  tok[b], acc[b], pd[b])
+    want = oracle.build_draft_batch(tok, acc, d, bi.start_pos, bi.block_table, bi.spec.block_size,
+                                    bi.target_hidden, bi.h_shared, bi.mask_token_id)
+    for key, v in o["build"].items():
+        got = host_bits(v) if key == "hidden" else v.cpu().numpy()
+        assert np.array_equal(got, want[key]), key
 
 
 def _outputs(B, K, V, H):
@@ -98,6 +125,7 @@ def test_step_graph_replays_match_eager(gpu, mode):
     inp = dict(z=dev(vi.logits), q=dev(vi.draft_probs), d=dev(vi.draft_tokens),
                u=dev(vi.uniforms), T=vi.temperature, temps=dev(temps))
     b = _build_inputs(B, K, V)
+    bi = b.pop("host")
     og, oe = _outputs(B, K, V, 512), _outputs(B, K, V, 512)
     ws_g = torch.zeros(gpu.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=DEV)
     ws_e = torch.zeros_like(ws_g)
@@ -121,6 +149,9 @@ def test_step_graph_replays_match_eager(gpu, mode):
         inp["u"].copy_(dev(u_new))
         inp["d"].copy_(dev(d_new))
         graph.launch()
+        torch.cuda.synchronize()
+        _replay_matches_oracle(mode, vi.logits, vi.spec.dtype, vi.draft_probs, d_new, u_new,
+                               vi.temperature, temps, og, bi)
         _eager(gpu, mode, inp, b, oe, ws_e, me)
         torch.cuda.synchronize()
         assert torch.equal(og["tok"], oe["tok"]) and torch.equal(og["acc"], oe["acc"]), rep
@@ -172,17 +203,21 @@ def test_metrics_at_max_drafts(gpu):
     assert got[gpu.METRICS_ACCEPTED] == want["accepted"]
 
 
-@pytest.mark.parametrize("B", [300, 900])
-def test_step_graph_one_draw_workgroup_per_sequence(gpu, B):
+@pytest.mark.parametrize("B,V,dtype", [(300, 40000, "bf16"), (900, 40001, "f32"),
+                                        (900, 5000, "f32")])
+def test_step_graph_one_draw_workgroup_per_sequence(gpu, B, V, dtype):
     """Sampled step graphs whose draw runs one workgroup per sequence and
-    draws the token itself (B = 300: 512-thread workgroups; B = 900:
-    256-thread workgroups): replays with new uniforms equal the eager step."""
+    draws the token itself (B = 300, V = 40000: 512-thread workgroups; B =
+    900, V = 40001: 256-thread workgroups; V = 5000: the row's three CDF tiles
+    kept in registers): every replay with new uniforms matches the oracle and
+    equals the eager step."""
     from tests.test_gpu_verify import _random_case
-    K, V, T = 3, 5000, 0.9
+    K, T = 3, 0.9
     rng = np.random.default_rng(B)
-    logits, q, d, u = _random_case(rng, B, K, V, "f32", T=T)
+    logits, q, d, u = _random_case(rng, B, K, V, dtype, T=T)
     inp = dict(z=dev(logits), q=dev(q), d=dev(d), u=dev(u), T=T)
     b = _build_inputs(B, K, V)
+    bi = b.pop("host")
     og, oe = _outputs(B, K, V, 512), _outputs(B, K, V, 512)
     ws_g = torch.zeros(gpu.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=DEV)
     ws_e = torch.zeros_like(ws_g)
@@ -192,8 +227,11 @@ def test_step_graph_one_draw_workgroup_per_sequence(gpu, B):
                   uniforms=inp["u"], out_draft_target_prob=og["pd"], temperature=T)
     graph = gpu.StepGraph("sample", verify, dict(b, outputs=og["build"]), metrics=mg)
     for rep in range(3):
-        inp["u"].copy_(dev(rng.random((B, K + 1), dtype=np.float32)))
+        u_new = rng.random((B, K + 1), dtype=np.float32)
+        inp["u"].copy_(dev(u_new))
         graph.launch()
+        torch.cuda.synchronize()
+        _replay_matches_oracle("sample", logits, dtype, q, d, u_new, T, None, og, bi)
         _eager(gpu, "sample", inp, b, oe, ws_e, me)
         torch.cuda.synchronize()
         assert torch.equal(og["tok"], oe["tok"]) and torch.equal(og["acc"], oe["acc"]), rep
