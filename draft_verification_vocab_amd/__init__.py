@@ -650,8 +650,11 @@ def spec_accept_metrics(num_accepted: torch.Tensor, K: int, metrics: torch.Tenso
 
 
 def acceptance_summary(metrics: torch.Tensor) -> dict:
-    """Host-side view of the counters (synchronises): the counts and the
-    acceptance length, tokens per round and draft acceptance rate."""
+    """Host-side view of the counters (synchronises): reads back the integer
+    counters that spec_accept_metrics accumulated on the device and divides
+    them into the acceptance length, tokens per round and draft acceptance
+    rate.  A reporting convenience, not part of the path: every count is
+    taken on the GPU, and the three ratios are plain quotients of them."""
     m = [int(x) for x in metrics.cpu().tolist()]
     rounds, proposed, accepted, emitted = (m[METRICS_ROUNDS], m[METRICS_PROPOSED],
                                            m[METRICS_ACCEPTED], m[METRICS_EMITTED])

@@ -119,8 +119,10 @@ SV_API const char* sv_status_string(int status);
 SV_API size_t spec_verify_workspace_bytes(int B, int K, int V);
 
 /*
- * Greedy verify.  For sequence b, g_k = the lowest index of the maximum of
- * logit row k.  a_b = the first k < K with draft_tokens[b][k] != g_k, or K.
+ * Greedy verify.  Source: "Project 14", section 概念 (concepts): the target
+ * checks the drafts in one forward and the accepted prefix replaces its own
+ * greedy continuation, so the emitted tokens are the target's greedy path.
+ * For sequence b, g_k = the lowest index of the maximum of logit row k.  a_b = the first k < K with draft_tokens[b][k] != g_k, or K.
  * Emitted tokens: the a_b accepted drafts, then c_b = g_{a_b}.
  *
  *   target_logits    [B][K+1][V], dtype SV_F32 or SV_BF16; row k is the
@@ -144,6 +146,9 @@ SV_API sv_status spec_verify_greedy(const void* target_logits, int logits_dtype,
 
 /*
  * Sampled verify (rejection sampling against the drafter's distribution).
+ * Source: "Project 14", section 架构 (architecture): accept the verified
+ * prefix, resample the rejected suffix; the rskf.cn survey, sections 1 and
+ * 2.2: the output follows the target's distribution exactly.
  * p_k = softmax(row k / T); q_k = draft_probs[b][k] used as given.
  * Draft k is accepted iff u[b][k] < p_k(x)/q_k(x), x = draft_tokens[b][k]
  * (q_k(x) = 0: accepted iff p_k(x) > 0).  a_b = the first rejected k, or K.
@@ -310,7 +315,13 @@ SV_API sv_status spec_verify_tree(const void* target_logits, int logits_dtype,
                                   int32_t* device_error, void* stream);
 
 /*
- * P-EAGLE drafter batch.  Each sequence b owns the 2K rows [2Kb, 2Kb+2K).
+ * P-EAGLE drafter batch.  Source: the P-EAGLE / TorchSpec blog summary,
+ * section 并行架构的核心创新 (one drafter forward predicts all K drafts
+ * from the NTP row and K-1 MASK rows carrying h_shared) and section TorchSpec
+ * 集成与工程优化 (the batch is rebuilt on the GPU: copy, insert MASK slots,
+ * remap positions, PADDING_SLOT_ID = -1 for rejected tokens, hidden states
+ * broadcast by a dedicated copy).  Each sequence b owns the 2K rows
+ * [2Kb, 2Kb+2K).
  * With a = num_accepted[b], c = verify_out_tokens[b][a], L = start_pos[b]
  * (position of verify slot 0) and h[i] = target_hidden row b*(K+1)+i (the
  * target's hidden state at verify slot i):
