@@ -589,14 +589,45 @@ def kernel_times(sv, torch, np, call, steps):
     return out
 
 
+def gpu_us_per_call(torch, call, n=100, reps=5):
+    """The GPU's own time per call: n calls captured in one graph (the
+    library enqueues on torch's current stream, the capture stream), replayed
+    reps times; no host work between the calls."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    e1.synchronize()
+    us = e0.elapsed_time(e1) / (reps * n) * 1e3
+    del g
+    return us
+
+
 def small_workloads_bench(sv, torch, np, synth, args):
-    """The three smaller workloads, each on its own: the mid-size verify
-    (B=8, K=5, V=32000 fp32, T=1: 48 logit rows, bound by launch and latency),
-    the P-EAGLE build (B=64, K=7, H=2880 bf16: 8 MB of data movement), and the
-    large-vocabulary verify (B=64, K=7, V=201088 bf16, T=0.7: 206 MB of logits,
-    under the 256 MB Infinity Cache, so the calls rotate over four copies of
-    the logits and draft probabilities).  Per call: the host-loop wall time,
-    each kernel's duration, and the algorithmic bytes over the kernels' time."""
+    """The smaller workloads, each on its own: the tiny verify (B=1, K=3,
+    V=32 fp32: launch latency), the mid-size verify (B=8, K=5, V=32000 fp32,
+    T=1: 48 logit rows, bound by latency), the P-EAGLE build (B=64, K=7,
+    H=2880 bf16: 8 MB of data movement), and the large-vocabulary verify
+    (B=64, K=7, V=201088 bf16, T=0.7: 206 MB of logits, under the 256 MB
+    Infinity Cache, so the calls rotate over four copies of the logits and
+    draft probabilities; the same calls on one resident copy are timed too).
+    Per call: the host-loop wall time, the GPU's own time (calls captured in
+    one graph), each kernel's duration, and the algorithmic bytes over the
+    kernels' time."""
     dev = torch.device("cuda:0")
     steps = max(args.steps, 100)
 
@@ -614,7 +645,7 @@ def small_workloads_bench(sv, torch, np, synth, args):
                 "frac_over_kernel_time": nbytes / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
     res = {}
-    for n, copies in ((2, 1), (4, 4)):
+    for n, copies in ((1, 1), (2, 1), (4, 4)):
         vi = synth.make_verify_inputs(synth.verify_config(n), workers=args.workers)
         B, K, V = vi.spec.B, vi.spec.K, vi.spec.V
         zsize = 2 if vi.spec.dtype == "bf16" else 4
@@ -649,6 +680,18 @@ def small_workloads_bench(sv, torch, np, synth, args):
             torch.cuda.synchronize()
             rb, sb = verify_bytes(B, K, V, zsize, acc_t.cpu().numpy(), sample=smp)
             r[name] = entry(fn, rb + sb)
+            r[name]["gpu_us_per_call"] = gpu_us_per_call(torch, fn)
+        if copies > 1:
+            # the same calls on one resident copy: the Infinity Cache then
+            # holds all 206 MB of logits between calls
+            def one_copy():
+                sv.spec_verify_sample(zs[0], qs[0], d, u, vi.temperature, out_tokens=out_t,
+                                      out_num_accepted=acc_t, out_draft_target_prob=pd_t,
+                                      workspace=ws)
+            r["sample_one_resident_copy"] = {
+                "ms_per_call": wall_ms(torch, one_copy, args.warmup, steps),
+                "kernels_ms": kernel_times(sv, torch, np, one_copy, steps),
+                "gpu_us_per_call": gpu_us_per_call(torch, one_copy)}
         if copies == 1:
             g = sv.StepGraph("sample", dict(target_logits=zs[0], draft_probs=qs[0],
                                             draft_tokens=d, uniforms=u,
@@ -656,6 +699,10 @@ def small_workloads_bench(sv, torch, np, synth, args):
                                             out_num_accepted=acc_t, out_draft_target_prob=pd_t,
                                             workspace=ws))
             r["sample"]["graph_ms_per_call"] = wall_ms(torch, g.launch, args.warmup, steps)
+            g.close()
+            g = sv.StepGraph("greedy", dict(target_logits=zs[0], draft_tokens=d, out_tokens=out_t,
+                                            out_num_accepted=acc_t, workspace=ws))
+            r["greedy"]["graph_ms_per_call"] = wall_ms(torch, g.launch, args.warmup, steps)
             g.close()
         res[synth.CONFIG_NAMES[n]] = r
         del zs, qs
@@ -672,6 +719,7 @@ def small_workloads_bench(sv, torch, np, synth, args):
 
     res[synth.CONFIG_NAMES[3]] = {"workload": f"{synth.CONFIG_NAMES[3]}: B={B} K={K} H={H} bf16",
                                   "build": entry(build, build_bytes(B, K, H, 2))}
+    res[synth.CONFIG_NAMES[3]]["build"]["gpu_us_per_call"] = gpu_us_per_call(torch, build)
     return res
 
 
