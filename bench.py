@@ -419,6 +419,53 @@ def _stream_read_fn():
     return fn
 
 
+def _ceiling_fn(name, argtypes):
+    import ctypes
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} is not built (run __graft_entry__.build())")
+    fn = getattr(ctypes.CDLL(CEILING_LIB), name)
+    fn.argtypes = argtypes
+    fn.restype = ctypes.c_int
+    return fn
+
+
+def draft_ceiling(torch, z_rows, rows, qbuf, reps):
+    """The drafter's bytes without its arithmetic: plain kernels that read
+    the gathered bf16 rows and write them back as fp32 (non-temporal and
+    ordinary stores), and that only write the fp32 rows, over the same device
+    buffers as the drafter sampling with q."""
+    import ctypes
+    vp, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    cvt = _ceiling_fn("svc_rows_to_f32", [vp, vp, i64, vp, i64, i, i, vp])
+    wr = _ceiling_fn("svc_write_rows", [vp, i64, i, i, vp])
+    n_out, V = rows.numel(), z_rows.shape[1]
+    stream = torch.cuda.current_stream()
+    calls = {
+        "rows_to_f32_nontemporal": lambda: cvt(z_rows.data_ptr(), rows.data_ptr(), z_rows.shape[0],
+                                               qbuf.data_ptr(), n_out, V, 1, stream.cuda_stream),
+        "rows_to_f32_cached": lambda: cvt(z_rows.data_ptr(), rows.data_ptr(), z_rows.shape[0],
+                                          qbuf.data_ptr(), n_out, V, 0, stream.cuda_stream),
+        "write_rows_nontemporal": lambda: wr(qbuf.data_ptr(), n_out, V, 1, stream.cuda_stream),
+        "write_rows_cached": lambda: wr(qbuf.data_ptr(), n_out, V, 0, stream.cuda_stream)}
+    out = {"kernels": "rows_to_f32: one 512-thread workgroup per output row reads the gathered "
+                      "bf16 row (16-byte non-temporal loads) and writes it as fp32; write_rows: "
+                      "the fp32 rows written alone"}
+    for key, fn in calls.items():
+        for _ in range(3):
+            if fn():
+                raise RuntimeError(f"{key} failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = n_out * V * (6 if key.startswith("rows") else 4)
+        out[key] = {"ms": ms, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9}
+    return out
+
+
 def read_ceiling(torch, buf, reps):
     """The read rate of a plain streaming kernel over the same resident device
     buffer (8192 workgroups, 8 16-byte loads in flight per lane, nothing
@@ -1154,7 +1201,8 @@ def main():
             "workload": f"drafter-output sampling B={B} K={K} V={V} bf16 T={vi.temperature}: "
                         "K draft tokens per sequence and their fp32 distributions",
             "with_probs": timed_draft(True),
-            "tokens_only": timed_draft(False)}
+            "tokens_only": timed_draft(False),
+            "copy_ceiling": draft_ceiling(torch, z_rows, d_rows, d_q, 10)}
         log("drafter sampling timed")
     if not args.no_round:
         res["decode_round"] = round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt,

@@ -1,6 +1,7 @@
 """Compile libspecverify.so (all HIP sources under csrc/) for gfx950, in tree,
-and libsvceiling.so (ceiling/read_ceiling.hip: the plain streaming-read kernel
-bench.py times as the practical HBM read ceiling)."""
+and libsvceiling.so (the HIP sources under ceiling/: plain comparison kernels
+that bench.py times beside the library -- the streaming-read ceiling, the
+drafter's bytes without its arithmetic, and the build as two kernels)."""
 from __future__ import annotations
 
 import glob
@@ -11,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libspecverify.so")
 CEILING_LIB = os.path.join(HERE, "libsvceiling.so")
-CEILING_SRC = os.path.join(HERE, "ceiling", "read_ceiling.hip")
+CEILING_DIR = os.path.join(HERE, "ceiling")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -25,6 +26,10 @@ FLAGS = [
 
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+
+
+def ceiling_sources():
+    return sorted(glob.glob(os.path.join(CEILING_DIR, "*.hip")))
 
 
 def _compile(srcs, out, verbose):
@@ -45,7 +50,7 @@ def _compile(srcs, out, verbose):
 def build(verbose: bool = False) -> str:
     """Always recompile both libraries; returns the path of the verify library."""
     _compile(sources(), LIB, verbose)
-    _compile([CEILING_SRC], CEILING_LIB, verbose)
+    _compile(ceiling_sources(), CEILING_LIB, verbose)
     return LIB
 
 

@@ -15,6 +15,14 @@
 //            q = softmax(z / T) as fp32;
 //   locate   one wave finds the tile whose running mass first exceeds u,
 //            rescans that one tile and writes the token.
+// A sampled bf16 row of up to 155648 logits (V a multiple of 8) with q
+// requested is instead held in the workgroup's registers: read once, and the
+// row max, the tile masses and q all come from the registers, so the row is
+// fetched once rather than twice.  That form is bound by the q writes, which
+// are two thirds of its bytes: at 1024 x 7 x 151936 it takes 1.34 ms
+// (1.37 ms with the second read), while a bare kernel that only reads the
+// same rows and writes them back as fp32 takes 1.38 ms (1.61 ms with
+// non-temporal stores), and writes alone run at about 5.7 TB/s.
 // Without q the row is read once with one exponential per element.  Greedy
 // rows need no exponentials: q is the one-hot of the argmax.
 // The q rows are written with non-temporal stores: the next verify reads only
@@ -29,6 +37,17 @@ namespace sv {
 // with 256 at 1024 x 7 x 151936), 256 when only tokens are drawn.
 template <bool WQ> constexpr int draft_threads() { return WQ ? 512 : 256; }
 constexpr int kDraftTilesPerStep = 2;  // sweep 1: CDF tiles per wave in flight
+// Row-resident sampled rows (RES = the workgroup size): wave w holds CDF
+// tiles w, w + W, w + 2W, ... (W waves), each as 8 quads of four bf16 logits
+// per lane (2 VGPRs a quad), up to kResTiles tiles, so V <= 76 * 2048 = 155648.
+constexpr int kResTiles = 76;
+constexpr long kResMaxV = (long)kResTiles * kTileElems;
+constexpr int kResThreads = 512;      // 1024 threads (5 slots a wave) measured the same
+template <int THREADS> constexpr int res_slots() {
+  return (kResTiles + THREADS / kWave - 1) / (THREADS / kWave);
+}
+constexpr int kQuadsPerTileLane = kTileElems / 4 / kWave;   // 8
+constexpr int kTileQuads = kTileElems / 4;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -169,14 +188,69 @@ __device__ void store_one_hot(float* qrow, long V, long nocts, int g) {
   }
 }
 
+// The max m and the sum s of 2^(z c - m c) of one bf16 CDF tile that a wave
+// holds as kQuadsPerTileLane packed quads per lane (quad k * 64 + l of the
+// tile in v[k] of lane l; quads past the row hold -inf).  Each lane sums its
+// 32 exponentials pairwise, then the wave sums the lanes.  Both the streamed
+// and the row-resident passes over bf16 rows use it, so the tile masses, and
+// with them the drawn tokens, do not depend on whether q is written.
+__device__ __forceinline__ void quad_tile_stats(const u32x2* v, float c, float& m, float& s) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kQuadsPerTileLane; ++k)
+    mx = fmaxf(mx, fmaxf(fmaxf(bf16_lo(v[k].x), bf16_hi(v[k].x)),
+                         fmaxf(bf16_lo(v[k].y), bf16_hi(v[k].y))));
+  mx = wave_max(mx);
+  float ls = 0.f;
+  if (mx != -INFINITY) {
+    const float R = mx * c;
+    float e8[kQuadsPerTileLane];
+#pragma unroll
+    for (int k = 0; k < kQuadsPerTileLane; ++k)
+      e8[k] = (__builtin_amdgcn_exp2f(fmaf(bf16_lo(v[k].x), c, -R)) +
+               __builtin_amdgcn_exp2f(fmaf(bf16_hi(v[k].x), c, -R))) +
+              (__builtin_amdgcn_exp2f(fmaf(bf16_lo(v[k].y), c, -R)) +
+               __builtin_amdgcn_exp2f(fmaf(bf16_hi(v[k].y), c, -R)));
+    ls = tree_sum8(e8);
+  }
+  m = mx;
+  s = wave_sum_f(ls);
+}
+
 // Sweep 1 of a sampled row: the max m_t and the sum s_t of 2^(z c - m_t c)
 // of every CDF tile, one wave per tile (kDraftTilesPerStep tiles in flight).
 // NT: non-temporal loads, for a row that is not read again (without q);
 // with q, sweep 2 reads the row again at once and cached loads serve it.
+// Vectorised bf16 rows are loaded as packed quads (quad_tile_stats).
 template <typename LT, bool VEC, int WAVES, bool NT>
 __device__ __forceinline__ void tile_stats(const LT* zrow, long V, long nocts, int T_tiles, float c,
                                            float* tile_m, float* tile_s) {
   const int w = threadIdx.x / kWave, l = lane_id();
+  if constexpr (VEC && sizeof(LT) == 2) {
+    const int nquads = (int)(V / 4);
+    const u32x2* zq = reinterpret_cast<const u32x2*>(zrow);
+    for (int t0 = w * kDraftTilesPerStep; t0 < T_tiles; t0 += WAVES * kDraftTilesPerStep) {
+      u32x2 v[kDraftTilesPerStep][kQuadsPerTileLane];
+#pragma unroll
+      for (int j = 0; j < kDraftTilesPerStep; ++j)
+#pragma unroll
+        for (int k = 0; k < kQuadsPerTileLane; ++k) {
+          const int qd = (t0 + j) * kTileQuads + k * kWave + l;
+          v[j][k] = ld8<NT>(zq + min(qd, nquads - 1));
+        }
+#pragma unroll
+      for (int j = 0; j < kDraftTilesPerStep; ++j) {
+#pragma unroll
+        for (int k = 0; k < kQuadsPerTileLane; ++k)
+          if ((t0 + j) * kTileQuads + k * kWave + l >= nquads)
+            v[j][k] = u32x2{0xff80ff80u, 0xff80ff80u};
+        float m, st;
+        quad_tile_stats(v[j], c, m, st);
+        if (l == 0 && t0 + j < T_tiles) { tile_m[t0 + j] = m; tile_s[t0 + j] = st; }
+      }
+    }
+    return;
+  }
   for (int t0 = w * kDraftTilesPerStep; t0 < T_tiles; t0 += WAVES * kDraftTilesPerStep) {
     float z[kDraftTilesPerStep][kTileLoads][8];
     if constexpr (VEC) {
@@ -232,11 +306,23 @@ __device__ __forceinline__ void tile_stats(const LT* zrow, long V, long nocts, i
   }
 }
 
-// WQ: q is written (out_probs non-null).
-template <typename LT, bool VEC, bool WQ>
-__global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(DraftArgs A) {
-  constexpr int THREADS = draft_threads<WQ>();
+// The row-resident path keeps each quad packed (two VGPRs for four bf16
+// logits) and unpacks it again in every pass; this empty statement, which
+// claims to change the packed words, keeps the compiler from holding the
+// unpacked fp32 values (twice the registers) from one pass to the next.
+template <int N>
+__device__ __forceinline__ void keep_packed(u32x2 (&raw)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) asm volatile("" : "+v"(raw[j].x), "+v"(raw[j].y));
+}
+
+// WQ: q is written (out_probs non-null).  RES (a workgroup size, or 0):
+// sampled rows are held in registers (bf16, VEC, WQ, V <= kResMaxV).
+template <typename LT, bool VEC, bool WQ, int RES = 0>
+__global__ __launch_bounds__(RES ? RES : draft_threads<WQ>()) void draft_sample_kernel(DraftArgs A) {
+  constexpr int THREADS = RES ? RES : draft_threads<WQ>();
   constexpr int WAVES = THREADS / kWave;
+  static_assert(!RES || (WQ && VEC && sizeof(LT) == 2), "row-resident rows: bf16 with q written");
   __shared__ float sm_f[WAVES];
   __shared__ int sm_i[WAVES];
   __shared__ double sm_d[WAVES];
@@ -285,9 +371,51 @@ __global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(Draft
     return;
   }
 
-  // sweep 1: per-tile max and sum of exponentials
   const int T_tiles = (int)((V + kTileElems - 1) / kTileElems);
-  tile_stats<LT, VEC, WAVES, !WQ>(zrow, V, nocts, T_tiles, c, tile_m, tile_s);
+  // RES: the row, once, into registers: slot i of wave w is tile w + W i, lane
+  // l holding its quads k * 64 + l (k < 8).  All loads are issued back to back
+  // (addresses past the row clamped to its last quad); then quads past the
+  // row, all in the last tile, are set to bf16 -inf, which adds nothing.
+  // Whether a slot's tile lies wholly inside the row is uniform across the
+  // wave.
+  constexpr int SLOTS = RES ? res_slots<THREADS>() : 1;
+  constexpr int NQ = SLOTS * kQuadsPerTileLane;
+  const int nquads = (int)(V / 4);
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  u32x2 raw[NQ];
+  if constexpr (RES) {
+    const u32x2* zq = reinterpret_cast<const u32x2*>(zrow);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int qd = (wv + WAVES * (j / kQuadsPerTileLane)) * kTileQuads +
+                     (j % kQuadsPerTileLane) * kWave + l;
+      raw[j] = ld8<true>(zq + min(qd, nquads - 1));
+    }
+    keep_packed(raw);
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int q0 = (wv + WAVES * i) * kTileQuads;
+      if (q0 + kTileQuads > nquads) {                // uniform
+#pragma unroll
+        for (int k = 0; k < kQuadsPerTileLane; ++k)
+          if (q0 + k * kWave + l >= nquads)
+            raw[i * kQuadsPerTileLane + k] = u32x2{0xff80ff80u, 0xff80ff80u};
+      }
+    }
+    // sweep 1 from the registers: the tile statistics tile_stats computes
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int tile = wv + WAVES * i;
+      if (tile < T_tiles) {                          // uniform
+        float m, st;
+        quad_tile_stats(raw + i * kQuadsPerTileLane, c, m, st);
+        if (l == 0) { tile_m[tile] = m; tile_s[tile] = st; }
+      }
+    }
+  } else {
+    // sweep 1: per-tile max and sum of exponentials
+    tile_stats<LT, VEC, WAVES, !WQ>(zrow, V, nocts, T_tiles, c, tile_m, tile_s);
+  }
   __syncthreads();
   // row max M; tile masses w_t = s_t 2^(m_t c - M c) replace s_t; row sum S
   if (w == 0) {
@@ -302,8 +430,8 @@ __global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(Draft
       tile_s[i] = wt;
       part += (double)wt;
     }
-    const double S = wave_sum(part);
-    if (l == 0) { row_S = S; stats.m = M; }
+    const double St = wave_sum(part);
+    if (l == 0) { row_S = St; stats.m = M; }
   }
   __syncthreads();
   const float M = stats.m;
@@ -314,8 +442,30 @@ __global__ __launch_bounds__(draft_threads<WQ>()) void draft_sample_kernel(Draft
   const float inv_s = (float)(exp2((double)Mc - (double)M * (double)c) / S);
   if (t == 0 && A.out_desc) A.out_desc[r] = sv_draft_row{c, Mc, inv_s, -1};
 
-  // sweep 2 (only when q is requested): write q
-  if constexpr (WQ) {
+  if constexpr (RES) {
+    // q from the registers, each element as the descriptor recomputes it
+    keep_packed(raw);
+    f32x4* qv = reinterpret_cast<f32x4*>(qrow);
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int q0 = (wv + WAVES * i) * kTileQuads;
+      const bool whole = q0 + kTileQuads <= nquads;  // uniform
+      if (q0 >= nquads) continue;                    // uniform
+#pragma unroll
+      for (int k = 0; k < kQuadsPerTileLane; ++k) {
+        const u32x2 v = raw[i * kQuadsPerTileLane + k];
+        const int qd = q0 + k * kWave + l;
+        if (whole || qd < nquads) {
+          const f32x4 q{__builtin_amdgcn_exp2f(fmaf(bf16_lo(v.x), c, -Mc)) * inv_s,
+                        __builtin_amdgcn_exp2f(fmaf(bf16_hi(v.x), c, -Mc)) * inv_s,
+                        __builtin_amdgcn_exp2f(fmaf(bf16_lo(v.y), c, -Mc)) * inv_s,
+                        __builtin_amdgcn_exp2f(fmaf(bf16_hi(v.y), c, -Mc)) * inv_s};
+          __builtin_nontemporal_store(q, qv + qd);
+        }
+      }
+    }
+  } else if constexpr (WQ) {
+    // sweep 2: write q
     if constexpr (VEC) {
       write_q_quads<LT, WAVES>(zrow, qrow, V, c, Mc, inv_s);
     } else {
@@ -391,7 +541,10 @@ hipError_t launch_draft(const DraftLaunch& L, hipStream_t stream) {
 #define SV_DRAFT(LT, VEC, WQ) \
   hipLaunchKernelGGL((draft_sample_kernel<LT, VEC, WQ>), grid, block, 0, stream, A)
   if (L.bf16) {
-    if (L.vec) { if (wq) SV_DRAFT(uint16_t, true, true); else SV_DRAFT(uint16_t, true, false); }
+    if (L.vec && wq && (long)L.V <= kResMaxV)
+      hipLaunchKernelGGL((draft_sample_kernel<uint16_t, true, true, kResThreads>), grid,
+                         dim3(kResThreads), 0, stream, A);
+    else if (L.vec) { if (wq) SV_DRAFT(uint16_t, true, true); else SV_DRAFT(uint16_t, true, false); }
     else { if (wq) SV_DRAFT(uint16_t, false, true); else SV_DRAFT(uint16_t, false, false); }
   } else {
     if (L.vec) { if (wq) SV_DRAFT(float, true, true); else SV_DRAFT(float, true, false); }

@@ -204,3 +204,58 @@ def test_max_drafts_per_sequence(gpu):
     u = rng.random((B, K), dtype=np.float32)
     temps = np.array([0.0, 0.8], np.float32)
     _parity(gpu, z, "f32", u, 1.0, B, K, row_index=rows, temps=temps)
+
+
+@pytest.mark.parametrize("V", [8, 2056, 4104, 151936, 155648, 155656])
+def test_row_resident_rows(gpu, V):
+    """bf16 rows with V a multiple of 8 and q written are held in registers
+    when V <= 155648 (a row of up to 76 quads per thread of a 512-thread
+    workgroup), else streamed twice.  Both sides of that limit, rows whose
+    last quads fill only part of the workgroup (2056, 4104), one-octet rows,
+    -inf logits, gathered rows, per-sequence temperatures with greedy rows,
+    an invalid row index and the q-less variant; q and the descriptor the
+    verify recomputes q from must agree element for element."""
+    rng = np.random.default_rng(V + 1)
+    B, K = 3, 3
+    n = B * K + 2
+    z = (3.0 * rng.standard_normal((n, V))).astype(np.float32)
+    z[:, :min(V, 16)] += 5.0
+    if V > 8:
+        z[:, rng.integers(0, V, size=5)] = -np.inf
+    logits = synth.f32_to_bf16_bits(z)
+    rows = rng.permutation(n)[:B * K].astype(np.int32).reshape(B, K)
+    temps = np.array([0.7, 0.0, 1.3], np.float32)
+    u = rng.random((B, K), dtype=np.float32)
+    tok, q = _parity(gpu, logits, "bf16", u, 1.0, B, K, row_index=rows, temps=temps)
+    tok2, _ = _parity(gpu, logits, "bf16", u, 1.0, B, K, row_index=rows, temps=temps,
+                      want_q=False)
+    assert np.array_equal(tok, tok2)
+    # the row descriptors reproduce q exactly as written
+    t3, q3, desc = gpu.spec_draft_sample(dev(logits), K, 1.0, uniforms=dev(u),
+                                         row_index=dev(rows), temperatures=dev(temps),
+                                         want_row_desc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(t3.cpu().numpy(), tok)
+    assert np.array_equal(q3.cpu().numpy().view(np.int32), q.view(np.int32))
+    d = desc.cpu().numpy()                       # [B, K, 4]: c, Mc, 1/S (fp32 bits), token
+    zb = logits.astype(np.uint32) << np.uint32(16)
+    for b in (0, 2):
+        for k in range(K):
+            c, mc, inv_s = d[b, k, :3].view(np.float32)
+            zr = zb[rows[b, k]].view(np.float32)
+            x = np.exp2(np.float64(np.float32(np.float64(zr) * c - mc)))
+            assert np.allclose(q[b, k], x * inv_s, rtol=2e-6, atol=1e-37)
+    # an invalid row gives token -1 and q = 0; the other rows are unaffected
+    bad = rows.copy()
+    bad[0, 1] = n
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    t4, q4 = gpu.spec_draft_sample(dev(logits), K, 1.0, uniforms=dev(u), row_index=dev(bad),
+                                   temperatures=dev(temps), device_error=err)
+    torch.cuda.synchronize()
+    t4, q4 = t4.cpu().numpy(), q4.cpu().numpy()
+    assert int(err.item()) == gpu.DEVERR_ROW_INDEX
+    assert t4[0, 1] == -1 and not q4[0, 1].any()
+    keep = np.ones((B, K), bool)
+    keep[0, 1] = False
+    assert np.array_equal(t4[keep], tok[keep])
+    assert np.array_equal(q4[keep].view(np.int32), q[keep].view(np.int32))
