@@ -466,6 +466,50 @@ def draft_ceiling(torch, z_rows, rows, qbuf, reps):
     return out
 
 
+def split_build(torch, o, a, d, L, bt, block_size, hid, hs, mask_id):
+    """The two-kernel build of the comparison library (a metadata kernel, then
+    a copy of the hidden rows through a row map) on the same inputs as
+    peagle_build_draft_batch: returns (call, outputs)."""
+    import ctypes
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    fn = _ceiling_fn("svc_build_split", [vp] * 5 + [i, i, vp, vp, ctypes.c_int32, i, i, i]
+                     + [vp] * 7)
+    B, K = d.shape
+    H = hid.shape[1]
+    dev = d.device
+    outs = {"input_ids": torch.empty(B * 2 * K, dtype=torch.int32, device=dev),
+            "positions": torch.empty(B * 2 * K, dtype=torch.int64, device=dev),
+            "slot_mapping": torch.empty(B * 2 * K, dtype=torch.int64, device=dev),
+            "hidden": torch.empty((B * 2 * K, H), dtype=hid.dtype, device=dev),
+            "sample_rows": torch.empty((B, K), dtype=torch.int32, device=dev)}
+    maps = torch.empty(2 * B * (K + 1), dtype=torch.int32, device=dev)
+
+    def call():
+        if fn(o.data_ptr(), a.data_ptr(), d.data_ptr(), L.data_ptr(), bt.data_ptr(), bt.shape[1],
+              block_size, hid.data_ptr(), hs.data_ptr(), mask_id, B, K, H,
+              outs["input_ids"].data_ptr(), outs["positions"].data_ptr(),
+              outs["slot_mapping"].data_ptr(), outs["hidden"].data_ptr(),
+              outs["sample_rows"].data_ptr(), maps.data_ptr(),
+              torch.cuda.current_stream().cuda_stream):
+            raise RuntimeError("svc_build_split failed")
+    return call, outs
+
+
+def build_compare(torch, build, bouts, split_call, souts):
+    """GPU time per call of the fused build and the two-kernel build, and
+    whether their outputs are bit for bit the same."""
+    build()
+    split_call()
+    torch.cuda.synchronize()
+    same = all(torch.equal(bouts[k].view(torch.int16) if bouts[k].dtype == torch.bfloat16
+                           else bouts[k],
+                           souts[k].view(torch.int16) if souts[k].dtype == torch.bfloat16
+                           else souts[k]) for k in souts)
+    return {"fused_gpu_us_per_call": gpu_us_per_call(torch, build),
+            "two_kernels_gpu_us_per_call": gpu_us_per_call(torch, split_call),
+            "same_outputs": same}
+
+
 def read_ceiling(torch, buf, reps):
     """The read rate of a plain streaming kernel over the same resident device
     buffer (8192 workgroups, 8 16-byte loads in flight per lane, nothing
@@ -767,6 +811,10 @@ def small_workloads_bench(sv, torch, np, synth, args):
     res[synth.CONFIG_NAMES[3]] = {"workload": f"{synth.CONFIG_NAMES[3]}: B={B} K={K} H={H} bf16",
                                   "build": entry(build, build_bytes(B, K, H, 2))}
     res[synth.CONFIG_NAMES[3]]["build"]["gpu_us_per_call"] = gpu_us_per_call(torch, build)
+    scall, souts = split_build(torch, o, a, d, L, bt, bi.spec.block_size, hid, hs,
+                               bi.mask_token_id)
+    res[synth.CONFIG_NAMES[3]]["build_vs_two_kernels"] = build_compare(torch, build, bouts, scall,
+                                                                       souts)
     return res
 
 
@@ -1003,6 +1051,36 @@ def main():
                                      out_num_accepted=acc_t, workspace=ws)
             sv.spec_accept_metrics(acc_t, K, mtr)
         torch.cuda.synchronize()
+        # the build as two kernels (metadata, then the hidden copy) on the
+        # same verify outputs, and both builds at the smaller build workload
+        scall, _ = split_build(torch, out_t, acc_t, d, L, bt, bi.spec.block_size, hid, hs,
+                               bi.mask_token_id)
+        for i in range(args.profile_steps):
+            build(); scall()
+        b3 = synth.make_build_inputs(synth.build_config(3))
+        o3, a3, d3 = up(b3.out_tokens), up(b3.num_accepted), up(b3.draft_tokens)
+        L3, bt3, h3, hs3 = (up(b3.start_pos), up(b3.block_table), up(b3.target_hidden),
+                            up(b3.h_shared))
+        scall3, _ = split_build(torch, o3, a3, d3, L3, bt3, b3.spec.block_size, h3, hs3,
+                                b3.mask_token_id)
+        for i in range(args.profile_steps):
+            sv.peagle_build_draft_batch(o3, a3, d3, L3, bt3, b3.spec.block_size, h3, hs3,
+                                        b3.mask_token_id)
+            scall3()
+        torch.cuda.synchronize()
+        # the large-vocabulary verify (B=64, V=201088), rotating over four
+        # copies of its inputs as the bench times it
+        v4 = synth.make_verify_inputs(synth.verify_config(4), workers=1)
+        z4s = [up(v4.logits) for _ in range(4)]
+        q4s = [up(v4.draft_probs) for _ in range(4)]
+        d4, u4 = up(v4.draft_tokens), up(v4.uniforms)
+        for i in range(args.profile_steps * 4):
+            sv.spec_verify_sample(z4s[i % 4], q4s[i % 4], d4, u4, v4.temperature)
+        torch.cuda.synchronize()
+        del z4s, q4s
+        # the drafter's bytes without its arithmetic (comparison kernels)
+        draft_ceiling(torch, z_rows, d_rows, d_q, 1)
+        torch.cuda.synchronize()
         ts = synth.TREE_CONFIGS["tree-large"]
         ti = synth.make_tree_inputs(ts, workers=1)
         tz, tq, tp, tt, tu = (up(ti.logits), up(ti.draft_probs), up(ti.parents), up(ti.tokens),
@@ -1027,8 +1105,8 @@ def main():
             os.makedirs(os.path.dirname(os.path.abspath(args.hash_out)), exist_ok=True)
             with open(args.hash_out, "w") as f:
                 f.write(kernel_source_hash() + "\n")
-        print(f"profiled {args.profile_steps} steps of every kernel family, the read-ceiling "
-              "kernel and a 1 GiB copy",
+        print(f"profiled {args.profile_steps} steps of every kernel family, the comparison "
+              "kernels and a 1 GiB copy",
               flush=True)
         return
 
@@ -1128,6 +1206,11 @@ def main():
         "acceptance": {"mean_accepted": float(acc.mean()),
                        "rate": float(acc.sum() / np.minimum(acc + 1, K).sum())},
     }
+    # the fused build against the same build as two kernels, on the last
+    # sampled step's verify outputs
+    res["build_vs_two_kernels"] = build_compare(
+        torch, build, bouts, *split_build(torch, out_t, acc_t, d, L, bt, bi.spec.block_size, hid,
+                                          hs, bi.mask_token_id))
     if "verify_sample_locate" in kms:
         # a separate locate kernel runs only when several draw workgroups
         # share a sequence (smaller batches)

@@ -10,7 +10,8 @@
   several workloads are kept apart by grid size, the dominant kernel is the
   sampled row kernel of the largest grid, and counters recorded on other
   kernel sources are refused.
-* The read-ceiling library loads without a GPU and refuses invalid
+* The comparison library (read ceiling, the drafter's bytes without its
+  arithmetic, the two-kernel build) loads without a GPU and refuses invalid
   arguments before launching anything.
 """
 import csv
@@ -47,6 +48,26 @@ def test_read_ceiling_library_exports_and_rejects_bad_arguments():
     assert fn(16, 0, 1, None) == 1                        # no bytes
     assert fn(16, 1000, 0, None) == 1                     # not a multiple of 16
     assert fn(8, 1024, 0, None) == 1                      # not 16-byte aligned
+    lib = ctypes.CDLL(bench.CEILING_LIB)
+    vp, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    cvt = lib.svc_rows_to_f32
+    cvt.argtypes = [vp, vp, i64, vp, i64, i, i, vp]
+    assert cvt(None, 16, 8, 16, 4, 64, 1, None) == 1       # no source rows
+    assert cvt(16, 16, 8, 16, 4, 60, 1, None) == 1         # V not a multiple of 8
+    assert cvt(16, 16, 8, 16, 0, 64, 1, None) == 1         # no output rows
+    assert cvt(8, 16, 8, 16, 4, 64, 1, None) == 1          # source not 16-byte aligned
+    wr = lib.svc_write_rows
+    wr.argtypes = [vp, i64, i, i, vp]
+    assert wr(None, 4, 64, 1, None) == 1
+    assert wr(16, 4, 62, 1, None) == 1                    # V not a multiple of 4
+    assert wr(16, -1, 64, 1, None) == 1
+    sb = lib.svc_build_split
+    sb.argtypes = [vp] * 5 + [i, i, vp, vp, ctypes.c_int32, i, i, i] + [vp] * 7
+    args = [16] * 5 + [4, 16, 16, 16, 7, 8, 7, 2048] + [16] * 6 + [None]
+    for pos, bad in ((11, 0), (11, 64), (12, 12), (10, 0), (16, None), (18, None), (7, 8)):
+        a = list(args)
+        a[pos] = bad                                      # K, H, B, an output, alignment
+        assert sb(*a) == 1, pos
 
 
 def test_more_than_one_gpu_is_refused():
