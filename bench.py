@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run only this many untimed steps (for rocprofv3) and exit; inputs are "
                          "then drawn in this process (no worker processes under a profiler)")
+    ap.add_argument("--profile-workload", choices=("fused", "large-vocab"), default="fused",
+                    help="with --profile-steps: the fused B=1024 step and the comparison kernels "
+                         "(fused), or the B=64 K=7 V=201088 bf16 verify over four rotated "
+                         "input copies (large-vocab)")
     ap.add_argument("--hash-out", default=None,
                     help="with --profile-steps: write the kernel source hash of this run here")
     ap.add_argument("--ingest-valu", default=None, metavar="VALU_CSV",
@@ -201,6 +205,23 @@ def _oracle_loop(oracle, np, vi, bi, K, t0, budget_s):
 COPY_BYTES = 1 << 30           # the calibration copy of --profile-steps
 
 
+def _library_kernel(name):
+    """A kernel of the verify library (namespace sv) or of the comparison
+    library (an anonymous namespace at file scope), not one of torch's."""
+    return (name.startswith(("void sv::", "sv::", "void (anonymous namespace)::",
+                             "(anonymous namespace)::")) and "at::" not in name)
+
+
+def _profile_record(csv_path):
+    """(kernel source hash, workload) that a profiled run wrote with
+    --hash-out into source_hash.txt next to its CSV."""
+    hp = os.path.join(os.path.dirname(csv_path), "source_hash.txt")
+    if not os.path.exists(hp):
+        sys.exit(f"{hp} is missing: cannot tell which kernels {csv_path} measured")
+    words = open(hp).read().split()
+    return words[0], (words[1] if len(words) > 1 else "fused")
+
+
 def ingest_counters(fetch_csv, write_csv):
     """Per-kernel HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the 1 GiB copy
@@ -208,13 +229,15 @@ def ingest_counters(fetch_csv, write_csv):
     profiled runs must have recorded (--hash-out source_hash.txt next to their
     CSV) the kernel source hash of the current sources."""
     here = kernel_source_hash()
+    workloads = set()
     for csv in (fetch_csv, write_csv):
-        hp = os.path.join(os.path.dirname(csv), "source_hash.txt")
-        if not os.path.exists(hp):
-            sys.exit(f"{hp} is missing: cannot tell which kernels these counters measured")
-        got = open(hp).read().strip()
+        got, wl = _profile_record(csv)
         if got != here:
             sys.exit(f"counters in {csv} were taken on kernel sources {got}, not the current {here}")
+        workloads.add(wl)
+    if len(workloads) != 1:
+        sys.exit("the FETCH_SIZE and WRITE_SIZE runs profiled different workloads")
+    workload = workloads.pop()
     import csv
     import collections
 
@@ -233,32 +256,40 @@ def ingest_counters(fetch_csv, write_csv):
     kernels = {}
     for key in sorted(fetch, key=lambda k: (k[0], -k[1])):
         name, grid = key
-        if not (name.startswith(("void sv::", "sv::")) or "stream_read<" in name):
+        if not _library_kernel(name):
             continue
         f = sum(fetch[key]) / len(fetch[key]) * f_scale
         w = sum(write.get(key, [0.0])) / max(1, len(write.get(key, []))) * w_scale
         kernels[f"{name} [grid {grid}]"] = {"fetch_bytes": f, "write_bytes": w,
                                             "hbm_bytes_per_launch": f + w,
                                             "dispatches": len(fetch[key]), "grid": grid}
-    # the sampled row kernel of the fused step: the largest grid of that kernel
+    # the sampled row kernel of the workload: the largest grid of that kernel
     dom = max((k for k in kernels if "verify_rows<unsigned short, 1, true>" in k),
               key=lambda k: kernels[k]["grid"])
     rec = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
            "kernel": dom, "hbm_bytes_per_launch": kernels[dom]["hbm_bytes_per_launch"],
            "kernels": kernels}
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
-    md = os.path.join(ROOT, "profiles", "hbm_counters_fused_b1024.md")
+    if workload == "fused":
+        # the bench line's roofline.traffic comes from this record
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        md = os.path.join(ROOT, "profiles", "hbm_counters_fused_b1024.md")
+        title = "fused step, B=1024 K=7 V=151936 bf16, H=2048"
+        extra = ""
+    else:
+        md = os.path.join(ROOT, "profiles", "hbm_counters_large_vocab_b64.md")
+        title = "large-vocabulary verify, B=64 K=7 V=201088 bf16, four rotated input copies"
+        extra = " --profile-workload large-vocab"
     # the commands that made the two CSVs: one counter per profiler run, output
     # in the directory holding each CSV
     fdir, wdir = os.path.dirname(fetch_csv), os.path.dirname(write_csv)
     fo = os.path.basename(fetch_csv).split("_counter_collection")[0]
     wo = os.path.basename(write_csv).split("_counter_collection")[0]
-    lines = ["# HBM bytes per launch from rocprofv3 counters: fused step, B=1024 K=7 V=151936 bf16, H=2048\n",
+    lines = [f"# HBM bytes per launch from rocprofv3 counters: {title}\n",
              "Commands (one counter per run, from /tmp with TMPDIR=/tmp; REPO = the repository root):\n",
              "```",
-             f"timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{fdir} -o {fo} -- python3 $REPO/bench.py --profile-steps 2 --hash-out $REPO/{fdir}/source_hash.txt",
-             f"timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{wdir} -o {wo} -- python3 $REPO/bench.py --profile-steps 2 --hash-out $REPO/{wdir}/source_hash.txt",
+             f"timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{fdir} -o {fo} -- python3 $REPO/bench.py --profile-steps 2{extra} --hash-out $REPO/{fdir}/source_hash.txt",
+             f"timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{wdir} -o {wo} -- python3 $REPO/bench.py --profile-steps 2{extra} --hash-out $REPO/{wdir}/source_hash.txt",
              f"python bench.py --ingest-counters {fetch_csv} {write_csv}",
              "```\n",
              f"Calibration (a plain 1 GiB device copy in the same runs): FETCH_SIZE x {f_scale:.4f}, "
@@ -267,10 +298,16 @@ def ingest_counters(fetch_csv, write_csv):
     for name, k in kernels.items():
         lines.append(f"| `{name}` | {k['dispatches']} | {k['fetch_bytes'] / 1e9:.4f} | "
                      f"{k['write_bytes'] / 1e9:.4f} | {k['hbm_bytes_per_launch'] / 1e9:.4f} |")
+    if workload != "fused":
+        lines.append("\nThe row kernel's algorithmic bytes are every logit row once: 64 x 8 x "
+                     "201088 x 2 B = 0.2059 GB per launch.  FETCH_SIZE counts what leaves the "
+                     "GPU's L2 for the memory fabric, so reads served by the 256 MB memory-side "
+                     "Infinity Cache count as HBM reads here; the rotation over four input copies "
+                     "(0.82 GB of logits) keeps the calls from finding their inputs cached.")
     with open(md, "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(json.dumps({"traffic_file": TRAFFIC_FILE, "summary": md,
-                      "dominant_hbm_bytes_per_launch": rec["hbm_bytes_per_launch"]}))
+    print(json.dumps({"traffic_file": TRAFFIC_FILE if workload == "fused" else None,
+                      "summary": md, "dominant_hbm_bytes_per_launch": rec["hbm_bytes_per_launch"]}))
 
 
 def ingest_trace(trace_csv, bench_log=None):
@@ -283,18 +320,14 @@ def ingest_trace(trace_csv, bench_log=None):
     import collections
 
     here = kernel_source_hash()
-    hp = os.path.join(os.path.dirname(trace_csv), "source_hash.txt")
-    if not os.path.exists(hp):
-        sys.exit(f"{hp} is missing: cannot tell which kernels this trace measured")
-    got = open(hp).read().strip()
+    got, _ = _profile_record(trace_csv)
     if got != here:
         sys.exit(f"the trace in {trace_csv} was taken on kernel sources {got}, not the current {here}")
     per = collections.defaultdict(list)
     for r in csv.DictReader(open(trace_csv)):
         us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         name = r["Kernel_Name"]
-        if not (name.startswith(("void sv::", "sv::")) or "stream_read<" in name
-                or "copyBuffer" in name):
+        if not (_library_kernel(name) or "copyBuffer" in name):
             continue                 # torch's own kernels (input uploads, fills)
         grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
         per[(name, grid)].append(us)
@@ -310,11 +343,14 @@ def ingest_trace(trace_csv, bench_log=None):
              "```\n",
              "`--profile-steps 5` runs, five times on the B=1024 K=7 V=151936 bf16 inputs: a sampled, a greedy and "
              "a mixed verify each followed by the build, the drafter sampling with dense q and with "
-             "row descriptors, the verify from drafter logits and the acceptance metrics; then five "
-             "greedy and five sampled tree verifications (64 trees of 15 nodes, V=151936 bf16), one "
-             "pass each of the read-ceiling kernel (`stream_read<true>` non-temporal, "
-             "`stream_read<false>` cached) over the 2.49 GB logit buffer, and one 1 GiB copy (the "
-             "counter calibration).\n",
+             "row descriptors, the verify from drafter logits and the acceptance metrics; then the "
+             "fused build and the two-kernel build of the comparison library (`meta_kernel`, "
+             "`copy_kernel`) five times each on the same verify outputs and at the B=64 H=2880 build "
+             "workload, the comparison library's drafter-bytes kernels (`rows_to_f32`, "
+             "`write_rows`; 4 calls each), five greedy and five sampled tree verifications (64 "
+             "trees of 15 nodes, V=151936 bf16), one pass each of the read-ceiling kernel "
+             "(`stream_read<true>` non-temporal, `stream_read<false>` cached) over the 2.49 GB "
+             "logit buffer, and one 1 GiB copy (the counter calibration).\n",
              f"Kernel source hash (bench.py `kernel_source_hash`): `{here}`\n",
              "Per kernel and grid size (threads), from the per-dispatch records of the run "
              "(the `--stats` table averages one kernel over every grid it ran at):\n",
@@ -372,8 +408,7 @@ def ingest_valu(valu_csv):
     counter run's timestamps)."""
     import csv
     import collections
-    hp = os.path.join(os.path.dirname(valu_csv), "source_hash.txt")
-    if not os.path.exists(hp) or open(hp).read().strip() != kernel_source_hash():
+    if _profile_record(valu_csv)[0] != kernel_source_hash():
         sys.exit(f"{valu_csv}: counters not taken on the current kernel sources")
     per = collections.defaultdict(lambda: collections.defaultdict(list))
     span = collections.defaultdict(dict)       # dispatch -> duration (us)
@@ -944,6 +979,49 @@ def tree_bench(sv, torch, np, synth, args):
     return res
 
 
+def profile_large_vocab(args, np, synth, log):
+    """For the profiler: the large-vocabulary verify (B=64 K=7 V=201088 bf16,
+    T=0.7), sampled and greedy, rotating over four copies of its inputs as the
+    bench times it (args.profile_steps rounds of four calls each), then the
+    read-ceiling kernel over one logit copy and the 1 GiB counter-calibration
+    copy."""
+    log("drawing the large-vocabulary inputs")
+    vi = synth.make_verify_inputs(synth.verify_config(4), workers=1)
+    import torch
+    import draft_verification_vocab_amd as sv
+    sv.require_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    zs = [up(vi.logits) for _ in range(4)]
+    qs = [up(vi.draft_probs) for _ in range(4)]
+    d, u = up(vi.draft_tokens), up(vi.uniforms)
+    for i in range(args.profile_steps * 4):
+        sv.spec_verify_sample(zs[i % 4], qs[i % 4], d, u, vi.temperature)
+    for i in range(args.profile_steps * 4):
+        sv.spec_verify_greedy(zs[i % 4], d)
+    torch.cuda.synchronize()
+    rd = _stream_read_fn()
+    if rd(zs[0].data_ptr(), zs[0].numel() * zs[0].element_size(), 1,
+          torch.cuda.current_stream().cuda_stream):
+        raise RuntimeError("svc_stream_read failed")
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    if args.hash_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.hash_out)), exist_ok=True)
+        with open(args.hash_out, "w") as f:
+            f.write(kernel_source_hash() + " large-vocab\n")
+    print(f"profiled {args.profile_steps} rounds of the large-vocabulary verify, the read-ceiling "
+          "kernel and a 1 GiB copy", flush=True)
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -965,6 +1043,9 @@ def main():
 
     # inputs are drawn before anything touches the GPU
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+    if args.profile_steps and args.profile_workload == "large-vocab":
+        profile_large_vocab(args, np, synth, log)
+        return
     log("drawing inputs")
     workers = 1 if args.profile_steps else args.workers
     vi, bi = synth.make_fused_inputs(workers=workers)
@@ -1068,16 +1149,6 @@ def main():
                                         b3.mask_token_id)
             scall3()
         torch.cuda.synchronize()
-        # the large-vocabulary verify (B=64, V=201088), rotating over four
-        # copies of its inputs as the bench times it
-        v4 = synth.make_verify_inputs(synth.verify_config(4), workers=1)
-        z4s = [up(v4.logits) for _ in range(4)]
-        q4s = [up(v4.draft_probs) for _ in range(4)]
-        d4, u4 = up(v4.draft_tokens), up(v4.uniforms)
-        for i in range(args.profile_steps * 4):
-            sv.spec_verify_sample(z4s[i % 4], q4s[i % 4], d4, u4, v4.temperature)
-        torch.cuda.synchronize()
-        del z4s, q4s
         # the drafter's bytes without its arithmetic (comparison kernels)
         draft_ceiling(torch, z_rows, d_rows, d_q, 1)
         torch.cuda.synchronize()
@@ -1104,7 +1175,7 @@ def main():
         if args.hash_out:
             os.makedirs(os.path.dirname(os.path.abspath(args.hash_out)), exist_ok=True)
             with open(args.hash_out, "w") as f:
-                f.write(kernel_source_hash() + "\n")
+                f.write(kernel_source_hash() + " fused\n")
         print(f"profiled {args.profile_steps} steps of every kernel family, the comparison "
               "kernels and a 1 GiB copy",
               flush=True)
