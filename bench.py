@@ -976,6 +976,79 @@ def tree_bench(sv, torch, np, synth, args):
                 "note": "bytes read by the walk's workgroup passes (a node's logit row, plus "
                         "its fp32 draft row after a rejection); one workgroup per tree, so "
                         "the walk lasts as long as the tree with the most passes"}
+    res["drafter_logits"] = tree_lq_bench(sv, torch, np, args, spec, z, par, tok, u, ws, outs)
+    return res
+
+
+def tree_lq_bench(sv, torch, np, args, spec, z, par, tok, u, ws, outs):
+    """The sampled tree call with the drafter's distributions handed over two
+    ways, on one drafting: stand-in drafter rows (the tree's target rows plus
+    seeded N(0, 1) noise, bf16, one per node) sampled at T=0.7 by
+    spec_draft_sample, which writes the dense q and the row descriptors; then
+    spec_verify_tree on the dense q and spec_verify_tree_lq on the drafter
+    logits + descriptors (identical outputs).  `round` adds the drafting each
+    way needs: the drafter kernel writing dense q, or only tokens and row
+    descriptors."""
+    B, N, V = spec.B, spec.N, spec.V
+    n = B * (N + 1)
+    dev = z.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(41)
+    zd = (z.view(n, V).float() + torch.randn((n, V), generator=g, device=dev)).to(z.dtype)
+    ud = torch.rand((n, 1), generator=g, device=dev)
+    _, q, desc = sv.spec_draft_sample(zd, 1, spec.temperature, uniforms=ud, want_row_desc=True)
+    q, desc = q.view(B, N + 1, V), desc.view(B, N + 1, 4)
+    T = spec.temperature
+    lq_outs = tuple(torch.empty_like(x) for x in outs)
+    calls = {
+        "dense_q": lambda: sv.spec_verify_tree(z, par, tok, T, draft_probs=q, uniforms=u,
+                                               out_tokens=outs[0], out_path=outs[1],
+                                               out_num_accepted=outs[2], workspace=ws),
+        "logit_q": lambda: sv.spec_verify_tree_lq(z, zd, desc, par, tok, u, T,
+                                                  out_tokens=lq_outs[0], out_path=lq_outs[1],
+                                                  out_num_accepted=lq_outs[2], workspace=ws)}
+    res = {"workload": f"B={B} trees of N={N} nodes, V={V} bf16, T={T}; drafter rows = target "
+                       "rows + N(0,1) noise, drafted at T=0.7"}
+    for name, call in calls.items():
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        with quiet_host():
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                call()
+            torch.cuda.synchronize()
+            sec = (time.perf_counter() - t0) / args.steps
+        sv.trace_begin(4 * args.steps)
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        per = {}
+        for k, ms in sv.trace_read():
+            per.setdefault(k, []).append(ms)
+        sv.trace_end()
+        res[name] = {"ms_per_call": sec * 1e3,
+                     "kernels_ms": {k: float(np.mean(v)) for k, v in per.items()}}
+    res["identical_outputs"] = all(torch.equal(a, b) for a, b in zip(outs, lq_outs))
+    dtok = torch.empty((n, 1), dtype=torch.int32, device=dev)
+    drafts = {
+        "dense_q": lambda: sv.spec_draft_sample(zd, 1, T, uniforms=ud, out_draft_tokens=dtok,
+                                                out_draft_probs=q.view(n, 1, V)),
+        "logit_q": lambda: sv.spec_draft_sample(zd, 1, T, uniforms=ud, out_draft_tokens=dtok,
+                                                want_draft_probs=False,
+                                                out_row_desc=desc.view(n, 1, 4))}
+    for name, call in drafts.items():
+        res[name]["drafter_ms"] = wall_ms(torch, call, args.warmup, args.steps)
+        res[name]["round_ms"] = res[name]["drafter_ms"] + res[name]["ms_per_call"]
+    acc = outs[2].cpu().numpy()
+    rp, pp = tree_walk_passes(np, par.cpu().numpy(), outs[1].cpu().numpy(), acc)
+    res["mean_accepted"] = float(acc.mean())
+    res["passes_mean"] = float((rp + pp).mean())
+    res["passes_max"] = int((rp + pp).max())
+    # bytes of the walk's passes: a node's logit row, plus after a rejection
+    # its fp32 q row (dense) or its bf16 drafter logit row (logit q)
+    res["dense_q"]["pass_bytes"] = int(rp.sum()) * V * (2 + 4) + int(pp.sum()) * V * 2
+    res["logit_q"]["pass_bytes"] = int(rp.sum()) * V * (2 + 2) + int(pp.sum()) * V * 2
     return res
 
 

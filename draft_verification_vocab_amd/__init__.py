@@ -36,7 +36,7 @@ __all__ = [
     "spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
     "SpecVerifyError", "SV_F32", "SV_BF16", "SV_F16", "PADDING_SLOT_ID",
     "spec_verify_mixed", "spec_verify_sample_lq", "spec_verify_sample_noalloc",
-    "noalloc_scratch_bytes", "spec_verify_tree", "spec_draft_sample",
+    "noalloc_scratch_bytes", "spec_verify_tree", "spec_verify_tree_lq", "spec_draft_sample",
     "spec_accept_metrics", "accept_metrics_buffer", "acceptance_summary", "StepGraph",
     "trace_begin", "trace_read", "trace_end",
     "DEVERR_DRAFT_TOKEN", "DEVERR_ACCEPT_COUNT", "DEVERR_BLOCK_TABLE",
@@ -74,6 +74,8 @@ _SIGS = {
                                    _i, _i, _i, _p, _p, _p, _p, ctypes.c_size_t, _p, _p]),
     "spec_verify_tree": (_i, [_p, _i, _p, _p, _p, _p, ctypes.c_float, _i, _i, _i, _p, _p, _p, _p,
                               ctypes.c_size_t, _p, _p]),
+    "spec_verify_tree_lq": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, _p, ctypes.c_float,
+                                 _i, _i, _i, _p, _p, _p, _p, ctypes.c_size_t, _p, _p]),
     "spec_accept_metrics_words": (ctypes.c_size_t, [_i]),
     "spec_accept_metrics": (_i, [_p, _i, _i, _p, _p, _p]),
     "sv_step_graph_create": (_i, [_p, _p]),
@@ -614,6 +616,60 @@ def spec_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens:
                               workspace.numel() * workspace.element_size(), _ptr(device_error),
                               _stream(dev))
     _check(st, "spec_verify_tree")
+    return out_tokens, out_path, out_num_accepted
+
+
+def spec_verify_tree_lq(target_logits: torch.Tensor, drafter_logits: torch.Tensor,
+                        drafter_desc: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor,
+                        uniforms: torch.Tensor, temperature: float,
+                        drafter_rows: Optional[torch.Tensor] = None,
+                        out_tokens: Optional[torch.Tensor] = None,
+                        out_path: Optional[torch.Tensor] = None,
+                        out_num_accepted: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None,
+                        device_error: Optional[torch.Tensor] = None):
+    """Sampled tree verification with q recomputed from the drafter logits
+    and the row descriptors of spec_draft_sample; see spec_verify_tree_lq in
+    include/spec_verify.h.  drafter_desc is [B, N+1, 4] int32 (sv_draft_row),
+    drafter_rows optional [B, N+1].
+
+    Returns (out_tokens [B, N+1], out_path [B, N+1], num_accepted [B])."""
+    lib = require_library()
+    if target_logits.dim() != 3 or drafter_logits.dim() != 2:
+        raise ValueError("target_logits must be [B, N+1, V] and drafter_logits [n_rows, V]")
+    B, N1, V = target_logits.shape
+    N = N1 - 1
+    dev = target_logits.device
+    _dev(target_logits, "target_logits")
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("target_logits must be float32 or bfloat16")
+    _dev(drafter_logits, "drafter_logits", target_logits.dtype, (drafter_logits.shape[0], V), dev)
+    _dev(drafter_desc, "drafter_desc", torch.int32, (B, N + 1, 4), dev)
+    _dev(parents, "parents", torch.int32, (B, N), dev)
+    _dev(tokens, "tokens", torch.int32, (B, N), dev)
+    _dev(uniforms, "uniforms", torch.float32, (B, N + 1), dev)
+    if drafter_rows is not None:
+        _dev(drafter_rows, "drafter_rows", torch.int32, (B, N + 1), dev)
+    out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev) if out_tokens is None \
+        else _dev(out_tokens, "out_tokens", torch.int32, (B, N + 1), dev)
+    out_path = torch.empty((B, N + 1), dtype=torch.int32, device=dev) if out_path is None \
+        else _dev(out_path, "out_path", torch.int32, (B, N + 1), dev)
+    out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev) if out_num_accepted is None \
+        else _dev(out_num_accepted, "out_num_accepted", torch.int32, (B,), dev)
+    need = spec_verify_workspace_bytes(B, N, V)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    _dev(workspace, "workspace", device=dev)
+    if device_error is not None:
+        _dev(device_error, "device_error", torch.int32, (1,), dev)
+    st = lib.spec_verify_tree_lq(_ptr(target_logits), _DTYPES[target_logits.dtype],
+                                 _ptr(drafter_logits), drafter_logits.shape[0],
+                                 _ptr(drafter_rows), _ptr(drafter_desc), _ptr(parents),
+                                 _ptr(tokens), _ptr(uniforms), float(temperature), B, N, V,
+                                 _ptr(out_tokens), _ptr(out_path), _ptr(out_num_accepted),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _ptr(device_error), _stream(dev))
+    _check(st, "spec_verify_tree_lq")
     return out_tokens, out_path, out_num_accepted
 
 

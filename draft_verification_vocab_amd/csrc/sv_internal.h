@@ -72,7 +72,11 @@ struct DraftLaunch {
 
 struct TreeLaunch {
   const void* logits;            // [B][N+1][V]
-  const float* draft_probs;      // [B][N+1][V] (sampled)
+  const float* draft_probs;      // [B][N+1][V] (sampled, dense q)
+  const void* dlogits;           // q from drafter logits instead: [d_rows][V], same dtype
+  long d_rows;
+  const int32_t* drows;          // optional [B][N+1] drafter row of node n (else b*(N+1)+n)
+  const sv_draft_row* ddesc;     // [B][N+1] descriptors of those rows
   const int32_t* parents;        // [B][N]
   const int32_t* tokens;         // [B][N]
   const float* uniforms;         // [B][N+1] (sampled)

@@ -315,6 +315,39 @@ SV_API sv_status spec_verify_tree(const void* target_logits, int logits_dtype,
                                   int32_t* device_error, void* stream);
 
 /*
+ * Sampled tree verification that takes the drafter's distributions as its
+ * logits plus a per-node descriptor (from spec_draft_sample), as
+ * spec_verify_sample_lq does for chains: q row n (the distribution node n's
+ * children were drawn from) is recomputed from drafter logit row
+ * drafter_rows[b][n] with descriptor drafter_desc[b][n] where the walk needs
+ * it (at each child's token, and along the node's row for a residual pass).
+ * Results are those of spec_verify_tree with draft_probs = the q that
+ * spec_draft_sample would have written for those rows (bit for bit).  Each
+ * residual pass then reads the node's drafter logit row (V * 2 bytes for
+ * bf16) instead of its fp32 q row (V * 4).  Source: as spec_verify_tree
+ * ("Project 14", section 概念).
+ *   drafter_logits   [n_drafter_rows][V], same dtype as target_logits.
+ *   drafter_rows     optional [B][N+1] int32 (NULL: row b*(N+1) + n, needs
+ *                    n_drafter_rows >= B*(N+1)); a row outside
+ *                    [0, n_drafter_rows) that the walk uses sets
+ *                    SV_DEVERR_ROW_INDEX and counts as q = 0.
+ *   drafter_desc     [B][N+1] sv_draft_row, 16-byte aligned.
+ *   temperature      > 0 (sampling only); other arguments as for
+ *                    spec_verify_tree.  The same two kernels are enqueued.
+ */
+SV_API sv_status spec_verify_tree_lq(const void* target_logits, int logits_dtype,
+                                     const void* drafter_logits, int64_t n_drafter_rows,
+                                     const int32_t* drafter_rows,
+                                     const sv_draft_row* drafter_desc,
+                                     const int32_t* parents, const int32_t* tokens,
+                                     const float* uniforms, float temperature,
+                                     int B, int N, int V,
+                                     int32_t* out_tokens, int32_t* out_path,
+                                     int32_t* out_num_accepted,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t* device_error, void* stream);
+
+/*
  * P-EAGLE drafter batch.  Source: the P-EAGLE / TorchSpec blog summary,
  * section 并行架构的核心创新 (one drafter forward predicts all K drafts
  * from the NTP row and K-1 MASK rows carrying h_shared) and section TorchSpec

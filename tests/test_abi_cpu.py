@@ -39,6 +39,7 @@ def test_header_declares_the_boundary():
               "sv_status_string", "spec_accept_metrics", "spec_accept_metrics_words",
               "sv_step_graph_create", "sv_step_graph_launch", "sv_step_graph_destroy",
               "spec_verify_tree", "spec_verify_sample_lq", "spec_verify_sample_noalloc",
+              "spec_verify_tree_lq",
               "spec_verify_noalloc_scratch_bytes"):
         assert n in names
 
@@ -355,6 +356,37 @@ def test_sample_lq_validation(lib):
     assert lq(lib, desc=FAKE + 8) == EALIGN
     assert lq(lib, dl=FAKE + 1) == EALIGN
     assert lq(lib, rows=FAKE + 2) == EALIGN
+
+
+def tree_lq(lib, logits=FAKE, dtype=1, dl=FAKE, n_rows=14, rows=None, desc=FAKE, par=FAKE,
+            tok=FAKE, u=FAKE, T=0.7, B=2, N=6, V=64, out=FAKE, path=FAKE, acc=FAKE, ws=FAKE,
+            wsb=None):
+    if wsb is None:
+        wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(N, 0), max(V, 1))
+    return lib.spec_verify_tree_lq(logits, dtype, dl, n_rows, rows, desc, par, tok, u, T, B, N, V,
+                                   out, path, acc, ws, wsb, None, None)
+
+
+def test_tree_lq_validation(lib):
+    assert tree_lq(lib, N=64) == ESHAPE
+    assert tree_lq(lib, n_rows=13) == ESHAPE            # fewer than B*(N+1) rows, no row index
+    assert tree_lq(lib, n_rows=-1, rows=FAKE) == ESHAPE
+    # a row index may name any row count (the call then stops at the workspace)
+    assert tree_lq(lib, n_rows=3, rows=FAKE, ws=None) == EWS
+    assert tree_lq(lib, dtype=2) == EDTYPE
+    for T in (0.0, -1.0, float("nan"), 1e-45):          # sampling only
+        assert tree_lq(lib, T=T) == EVALUE, T
+    assert tree_lq(lib, B=0, logits=None, dl=None, desc=None, par=None, tok=None, u=None,
+                   out=None, path=None, acc=None, ws=None, wsb=0) == OK
+    assert tree_lq(lib, dl=None) == ENULL
+    assert tree_lq(lib, desc=None) == ENULL
+    assert tree_lq(lib, u=None) == ENULL
+    assert tree_lq(lib, par=None) == ENULL
+    assert tree_lq(lib, N=0, par=None, tok=None, ws=None) == EWS   # a root alone needs no nodes
+    assert tree_lq(lib, ws=None) == EWS
+    assert tree_lq(lib, desc=FAKE + 8) == EALIGN
+    assert tree_lq(lib, dl=FAKE + 1) == EALIGN
+    assert tree_lq(lib, rows=FAKE + 2) == EALIGN
 
 
 ESCRATCH = 8
