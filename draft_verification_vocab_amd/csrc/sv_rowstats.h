@@ -93,6 +93,14 @@ __device__ __forceinline__ void unpack(const Quad<float>& q, float v[4]) {
   v[0] = __uint_as_float(q.w.x); v[1] = __uint_as_float(q.w.y);
   v[2] = __uint_as_float(q.w.z); v[3] = __uint_as_float(q.w.w);
 }
+// An empty statement that claims to change a loaded quad: placed after a
+// group of loads and before their first use, it makes every load of the group
+// go out before the first wait (without it the compiler may wait for each
+// load before issuing the next one).
+template <typename LT>
+__device__ __forceinline__ void hold(Quad<LT>& q) {
+  asm volatile("" : "+v"(q.w));
+}
 
 // ---------------------------------------------------------------- row-slice state
 struct SliceState {

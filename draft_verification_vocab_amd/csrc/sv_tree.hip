@@ -73,14 +73,6 @@ struct TileQuads {
   Quad<typename std::conditional<QL, LT, float>::type> q[G][2];
 };
 
-// An empty statement that claims to change the loaded words: every load of
-// the tile is issued before the first one is waited for (without it the
-// compiler may wait for each load before issuing the next).
-template <typename T>
-__device__ __forceinline__ void hold(T& v) {
-  asm volatile("" : "+v"(v.w));
-}
-
 // Residual masses of this lane's elements of CDF tile t in the quad layout
 // (r[sl][4 h + j]: element 512 g + 256 h + 4 l + j of wave load g = t *
 // kTileLoads + sl): max(0, p - w q) with p = 2^(z c - Mc) * inv_s
