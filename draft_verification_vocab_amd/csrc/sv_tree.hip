@@ -176,8 +176,10 @@ __device__ __forceinline__ void tile_residual(const LT* zrow, const TreeQ<LT>& Q
 // Tile masses of the residual into tsum (LDS); returns the fp64 total, the
 // same on every thread.  Called in uniform control flow.  (Two tiles in
 // flight per wave, the next tile's loads issued before the current one is
-// reduced, measured slower: 101-102 against 95.5-98 us at 256 trees x 16
-// rows x 151936 bf16.)
+// reduced, measured slower at 256 trees x 16 rows x 151936 bf16: 101-102
+// against 95.5-98 us with one buffer copied into the other, 102-103 against
+// 94.5-95 us with two buffers swapping roles, whose loads the compiler did
+// keep in flight during the reduction.)
 template <typename LT, bool VEC, bool QL, bool RESID, int WAVES>
 __device__ __forceinline__ double residual_tiles(const LT* zrow, const TreeQ<LT>& Q, float w,
                                                  long V, int T_tiles, float c, float Mc,
