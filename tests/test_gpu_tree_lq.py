@@ -9,7 +9,8 @@ distribution of its drafter row, then oracle.tree.tree_outcomes with the
 1e-6 near-tie tolerance.  Covered: V=151936 bf16 trees; fp32 trees with
 drafter rows gathered through a row index, greedy-drafted nodes and an
 invalid drafter row (flagged, q = 0 as the dense path's all-zero row); a
-bf16 vocabulary that is not a multiple of 8; a root without children.
+bf16 vocabulary that is not a multiple of 8; a root without children; trees
+of 63 nodes (the limit) and an empty batch.
 """
 import numpy as np
 import pytest
@@ -132,3 +133,33 @@ def test_tree_lq_ragged_bf16_and_bare_root(gpu):
     assert int(err.item()) & gpu.DEVERR_TREE
     _check_oracle(ti2, zd, 0.8, out, path, acc, parents=parents, skip=(2,))
     assert acc[2] == 0 and path[2, 0] == -1
+
+
+def test_tree_lq_max_nodes_and_empty_batch(gpu):
+    """Trees of N = 63 nodes (the limit; random shapes, fp32, V = 1000), each
+    node's drafter row gathered through a row index; and B = 0."""
+    rng = np.random.default_rng(63)
+    B, N, V = 4, 63, 1000
+    parents = np.stack([np.array([int(rng.integers(max(0, i - 4), i + 1)) for i in range(N)],
+                                 np.int32) for _ in range(B)])
+    spec = synth.TreeSpec(name="tree-max", B=B, N=N, V=V, dtype="f32", sigma=2.0, boost="none",
+                          temperature=0.9, draft_noise=1.0, draft_temperature=0.9,
+                          shape="random", widths=(), seed=63)
+    ti = synth.TreeInputs(spec=spec,
+                          logits=(2.0 * rng.standard_normal((B, N + 1, V))).astype(np.float32),
+                          draft_probs=np.full((B, N + 1, V), 1.0 / V, np.float32),
+                          parents=parents, tokens=rng.integers(0, V, size=(B, N)).astype(np.int32),
+                          uniforms=rng.random((B, N + 1), dtype=np.float32))
+    zd = _drafter_rows(ti, 67, scale=0.3)
+    n = B * (N + 1)
+    rows = rng.permutation(n).astype(np.int32).reshape(B, N + 1)
+    out, path, acc = _run(gpu, ti, zd, 0.9, rows=rows)
+    _check_oracle(ti, zd, 0.9, out, path, acc, rows=rows)
+    e = torch.zeros((0, N + 1, V), dtype=torch.float32, device=DEV)
+    o, p, a = gpu.spec_verify_tree_lq(e, dev(zd), torch.zeros((0, N + 1, 4), dtype=torch.int32,
+                                                               device=DEV),
+                                      torch.zeros((0, N), dtype=torch.int32, device=DEV),
+                                      torch.zeros((0, N), dtype=torch.int32, device=DEV),
+                                      torch.zeros((0, N + 1), dtype=torch.float32, device=DEV),
+                                      0.9)
+    assert o.shape == (0, N + 1) and p.shape == (0, N + 1) and a.shape == (0,)
