@@ -622,13 +622,16 @@ def graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt, hid, hs
 
 
 def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, out_t, acc_t,
-                pd_t, ws, bouts):
+                pd_t, ws, bouts, temps):
     """One decode round of the path on the two ways of handing the drafter's
     distributions to the verify: drafter sampling that writes dense fp32 q +
     spec_verify_sample, vs drafter sampling that writes only tokens and row
     descriptors + spec_verify_sample_lq; both followed by the P-EAGLE build.
     Stand-in drafter rows: the first K logit rows of the sequence B/2 places
-    away (same recipe, distinct memory), gathered through a row index."""
+    away (same recipe, distinct memory), gathered through a row index.  The
+    same pair is also timed on a mixed serving batch (per-sequence
+    temperatures, each sequence's drafter rows sampled at its own
+    temperature): spec_verify_mixed vs spec_verify_mixed_lq."""
     dev = z.device
     zr = z.view(B * (K + 1), V)
     seq = (torch.arange(B, dtype=torch.int32, device=dev) + B // 2) % B
@@ -657,9 +660,24 @@ def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, o
                                  out_num_accepted=acc_t, out_draft_target_prob=pd_t, workspace=ws)
         build()
 
+    def dense_mixed():
+        sv.spec_draft_sample(zr, K, T, uniforms=ud, row_index=rows, temperatures=temps,
+                             out_draft_tokens=tok, out_draft_probs=q)
+        sv.spec_verify_mixed(z, q, tok, u, temps, out_tokens=out_t, out_num_accepted=acc_t,
+                             out_draft_target_prob=pd_t, workspace=ws)
+        build()
+
+    def lq_mixed():
+        sv.spec_draft_sample(zr, K, T, uniforms=ud, row_index=rows, temperatures=temps,
+                             out_draft_tokens=tok, want_draft_probs=False, out_row_desc=desc)
+        sv.spec_verify_mixed_lq(z, zr, desc, tok, u, temps, drafter_rows=rows, out_tokens=out_t,
+                                out_num_accepted=acc_t, out_draft_target_prob=pd_t, workspace=ws)
+        build()
+
     res = {"workload": f"B={B} K={K} V={V} bf16: drafter sampling + sampled verify + P-EAGLE build"}
     outs = {}
-    for name, fn in (("dense_q", dense), ("logit_q", lq)):
+    for name, fn in (("dense_q", dense), ("logit_q", lq), ("mixed_dense_q", dense_mixed),
+                     ("mixed_logit_q", lq_mixed)):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
@@ -673,6 +691,10 @@ def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, o
     res["speedup"] = res["dense_q_ms_per_round"] / res["logit_q_ms_per_round"]
     res["identical_outputs"] = bool(torch.equal(outs["dense_q"][0], outs["logit_q"][0]) and
                                     torch.equal(outs["dense_q"][1], outs["logit_q"][1]))
+    res["mixed_speedup"] = res["mixed_dense_q_ms_per_round"] / res["mixed_logit_q_ms_per_round"]
+    res["mixed_identical_outputs"] = bool(
+        torch.equal(outs["mixed_dense_q"][0], outs["mixed_logit_q"][0]) and
+        torch.equal(outs["mixed_dense_q"][1], outs["mixed_logit_q"][1]))
     return res
 
 
@@ -1433,7 +1455,7 @@ def main():
         log("drafter sampling timed")
     if not args.no_round:
         res["decode_round"] = round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt,
-                                          hid, hs, out_t, acc_t, pd_t, ws, bouts)
+                                          hid, hs, out_t, acc_t, pd_t, ws, bouts, temps)
         log("decode round timed")
     if not args.no_tree:
         res["tree_verify"] = tree_bench(sv, torch, np, synth, args)

@@ -35,7 +35,8 @@ __all__ = [
     "require_library", "library_path", "sv_status_string", "spec_verify_workspace_bytes",
     "spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
     "SpecVerifyError", "SV_F32", "SV_BF16", "SV_F16", "PADDING_SLOT_ID",
-    "spec_verify_mixed", "spec_verify_sample_lq", "spec_verify_sample_noalloc",
+    "spec_verify_mixed", "spec_verify_sample_lq", "spec_verify_mixed_lq",
+    "spec_verify_sample_noalloc",
     "noalloc_scratch_bytes", "spec_verify_tree", "spec_verify_tree_lq", "spec_draft_sample",
     "spec_accept_metrics", "accept_metrics_buffer", "acceptance_summary", "StepGraph",
     "trace_begin", "trace_read", "trace_end",
@@ -72,6 +73,8 @@ _SIGS = {
                                _p, _p, _p, _p, _p]),
     "spec_verify_sample_lq": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, ctypes.c_float,
                                    _i, _i, _i, _p, _p, _p, _p, ctypes.c_size_t, _p, _p]),
+    "spec_verify_mixed_lq": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, _p,
+                                  _i, _i, _i, _p, _p, _p, _p, ctypes.c_size_t, _p, _p]),
     "spec_verify_tree": (_i, [_p, _i, _p, _p, _p, _p, ctypes.c_float, _i, _i, _i, _p, _p, _p, _p,
                               ctypes.c_size_t, _p, _p]),
     "spec_verify_tree_lq": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, _p, ctypes.c_float,
@@ -515,20 +518,9 @@ def spec_draft_sample(drafter_logits: torch.Tensor, K: int, temperature: float,
     return out_draft_tokens, out_draft_probs
 
 
-def spec_verify_sample_lq(target_logits: torch.Tensor, drafter_logits: torch.Tensor,
-                          drafter_desc: torch.Tensor, draft_tokens: torch.Tensor,
-                          uniforms: torch.Tensor, temperature: float,
-                          drafter_rows: Optional[torch.Tensor] = None,
-                          out_tokens: Optional[torch.Tensor] = None,
-                          out_num_accepted: Optional[torch.Tensor] = None,
-                          out_draft_target_prob: Optional[torch.Tensor] = None,
-                          want_draft_target_prob: bool = False,
-                          workspace: Optional[torch.Tensor] = None,
-                          device_error: Optional[torch.Tensor] = None):
-    """Sampled verify with q recomputed from the drafter logits and the row
-    descriptors of spec_draft_sample; see spec_verify_sample_lq in
-    include/spec_verify.h.  Returns (out_tokens, num_accepted, draft_target_prob
-    or None)."""
+def _verify_lq(name, target_logits, drafter_logits, drafter_desc, draft_tokens, uniforms,
+               temperature, temperatures, drafter_rows, out_tokens, out_num_accepted,
+               out_draft_target_prob, want_draft_target_prob, workspace, device_error):
     lib = require_library()
     if target_logits.dim() != 3 or drafter_logits.dim() != 2:
         raise ValueError("target_logits must be [B, K+1, V] and drafter_logits [n_rows, V]")
@@ -542,6 +534,8 @@ def spec_verify_sample_lq(target_logits: torch.Tensor, drafter_logits: torch.Ten
     _dev(drafter_desc, "drafter_desc", torch.int32, (B, K, 4), dev)
     _dev(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
     _dev(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    if temperatures is not None:
+        _dev(temperatures, "temperatures", torch.float32, (B,), dev)
     if drafter_rows is not None:
         _dev(drafter_rows, "drafter_rows", torch.int32, (B, K), dev)
     out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if out_tokens is None \
@@ -558,15 +552,58 @@ def spec_verify_sample_lq(target_logits: torch.Tensor, drafter_logits: torch.Ten
     _dev(workspace, "workspace", device=dev)
     if device_error is not None:
         _dev(device_error, "device_error", torch.int32, (1,), dev)
-    st = lib.spec_verify_sample_lq(_ptr(target_logits), _DTYPES[target_logits.dtype],
-                                   _ptr(drafter_logits), drafter_logits.shape[0],
-                                   _ptr(drafter_rows), _ptr(drafter_desc), _ptr(draft_tokens),
-                                   _ptr(uniforms), float(temperature), B, K, V, _ptr(out_tokens),
-                                   _ptr(out_num_accepted), _ptr(out_draft_target_prob),
-                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                   _ptr(device_error), _stream(dev))
-    _check(st, "spec_verify_sample_lq")
+    head = (_ptr(target_logits), _DTYPES[target_logits.dtype], _ptr(drafter_logits),
+            drafter_logits.shape[0], _ptr(drafter_rows), _ptr(drafter_desc), _ptr(draft_tokens),
+            _ptr(uniforms))
+    tail = (B, K, V, _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_draft_target_prob),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(device_error),
+            _stream(dev))
+    if name == "spec_verify_mixed_lq":
+        st = lib.spec_verify_mixed_lq(*head, _ptr(temperatures), *tail)
+    else:
+        st = lib.spec_verify_sample_lq(*head, float(temperature), *tail)
+    _check(st, name)
     return out_tokens, out_num_accepted, out_draft_target_prob
+
+
+def spec_verify_sample_lq(target_logits: torch.Tensor, drafter_logits: torch.Tensor,
+                          drafter_desc: torch.Tensor, draft_tokens: torch.Tensor,
+                          uniforms: torch.Tensor, temperature: float,
+                          drafter_rows: Optional[torch.Tensor] = None,
+                          out_tokens: Optional[torch.Tensor] = None,
+                          out_num_accepted: Optional[torch.Tensor] = None,
+                          out_draft_target_prob: Optional[torch.Tensor] = None,
+                          want_draft_target_prob: bool = False,
+                          workspace: Optional[torch.Tensor] = None,
+                          device_error: Optional[torch.Tensor] = None):
+    """Sampled verify with q recomputed from the drafter logits and the row
+    descriptors of spec_draft_sample; see spec_verify_sample_lq in
+    include/spec_verify.h.  Returns (out_tokens, num_accepted, draft_target_prob
+    or None)."""
+    return _verify_lq("spec_verify_sample_lq", target_logits, drafter_logits, drafter_desc,
+                      draft_tokens, uniforms, temperature, None, drafter_rows, out_tokens,
+                      out_num_accepted, out_draft_target_prob, want_draft_target_prob,
+                      workspace, device_error)
+
+
+def spec_verify_mixed_lq(target_logits: torch.Tensor, drafter_logits: torch.Tensor,
+                         drafter_desc: torch.Tensor, draft_tokens: torch.Tensor,
+                         uniforms: torch.Tensor, temperatures: torch.Tensor,
+                         drafter_rows: Optional[torch.Tensor] = None,
+                         out_tokens: Optional[torch.Tensor] = None,
+                         out_num_accepted: Optional[torch.Tensor] = None,
+                         out_draft_target_prob: Optional[torch.Tensor] = None,
+                         want_draft_target_prob: bool = False,
+                         workspace: Optional[torch.Tensor] = None,
+                         device_error: Optional[torch.Tensor] = None):
+    """Mixed-batch verify (per-sequence temperatures, 0 = greedy) with q
+    recomputed from the drafter logits and row descriptors; see
+    spec_verify_mixed_lq in include/spec_verify.h.  Returns (out_tokens,
+    num_accepted, draft_target_prob or None)."""
+    return _verify_lq("spec_verify_mixed_lq", target_logits, drafter_logits, drafter_desc,
+                      draft_tokens, uniforms, None, temperatures, drafter_rows, out_tokens,
+                      out_num_accepted, out_draft_target_prob, want_draft_target_prob,
+                      workspace, device_error)
 
 
 # ---------------------------------------------------------------- draft trees

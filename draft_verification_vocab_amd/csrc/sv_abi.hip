@@ -198,6 +198,66 @@ sv_status verify_common(const void* logits, int dtype, const float* draft_probs,
   return sv::launch_verify(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+// spec_verify_sample_lq (temperatures null: the scalar temperature) and
+// spec_verify_mixed_lq (per-sequence temperatures).
+sv_status verify_lq(const void* target_logits, int logits_dtype, const void* drafter_logits,
+                    int64_t n_drafter_rows, const int32_t* drafter_rows,
+                    const sv_draft_row* drafter_desc, const int32_t* draft_tokens,
+                    const float* uniforms, float temperature, const float* temperatures, int B,
+                    int K, int V, int32_t* out_tokens, int32_t* out_num_accepted,
+                    float* out_draft_target_prob, void* workspace, size_t workspace_bytes,
+                    int32_t* device_error, void* stream) {
+  sv_status st = check_verify_shape(B, K, V);
+  if (st != SV_OK) return st;
+  if (n_drafter_rows < 0 || n_drafter_rows > 0x7fffffffL) return SV_ERR_SHAPE;
+  if (!drafter_rows && n_drafter_rows < (int64_t)B * K) return SV_ERR_SHAPE;
+  if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
+  const bool mixed = temperatures != nullptr;
+  if (!mixed && !(temperature > 0.0f && isfinite(temperature) &&
+                  isfinite((float)(1.4426950408889634 / (double)temperature))))
+    return SV_ERR_VALUE;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !out_tokens || !out_num_accepted || !uniforms) return SV_ERR_NULL;
+  if (K > 0 && (!draft_tokens || !drafter_logits || !drafter_desc)) return SV_ERR_NULL;
+  if (!workspace || workspace_bytes < verify_workspace_bytes(B, K, V)) return SV_ERR_WORKSPACE;
+  const size_t esz = logits_dtype == SV_BF16 ? 2 : 4;
+  if (!aligned(target_logits, esz) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+      !aligned(uniforms, 4) || !aligned(workspace, 16) ||
+      (draft_tokens && !aligned(draft_tokens, 4)) ||
+      (drafter_logits && !aligned(drafter_logits, esz)) ||
+      (drafter_rows && !aligned(drafter_rows, 4)) ||
+      (drafter_desc && !aligned(drafter_desc, 16)) ||
+      (temperatures && !aligned(temperatures, 4)) ||
+      (out_draft_target_prob && !aligned(out_draft_target_prob, 4)) ||
+      (device_error && !aligned(device_error, 4)))
+    return SV_ERR_ALIGN;
+  if ((long)B * (K + 1) * verify_splits(B, K, V) > 0x7fffffffL) return SV_ERR_SHAPE;
+  VerifyLaunch L;
+  L.logits = target_logits;
+  L.draft_probs = nullptr;
+  L.draft_tokens = draft_tokens;
+  L.uniforms = uniforms;
+  L.temperature = mixed ? 1.0f : temperature;
+  L.B = B; L.K = K; L.V = V;
+  L.bf16 = logits_dtype == SV_BF16;
+  L.sample = 1;
+  L.mixed = mixed ? 1 : 0;
+  L.temperatures = temperatures;
+  // a valid pointer for K = 0 (nothing is read from it then)
+  L.dlogits = drafter_logits ? drafter_logits : target_logits;
+  L.d_rows = (long)n_drafter_rows;
+  L.drows = drafter_rows;
+  L.ddesc = drafter_desc;
+  L.vec = (V % 8 == 0) && aligned(target_logits, 16) &&
+          (!drafter_logits || aligned(drafter_logits, 16));
+  L.out_tokens = out_tokens;
+  L.out_num_accepted = out_num_accepted;
+  L.out_p_draft = out_draft_target_prob;
+  L.workspace = workspace;
+  L.device_error = device_error;
+  return launch_verify(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 }  // namespace sv
 
 extern "C" {
@@ -234,53 +294,29 @@ SV_API sv_status spec_verify_sample_lq(const void* target_logits, int logits_dty
                                        float* out_draft_target_prob, void* workspace,
                                        size_t workspace_bytes, int32_t* device_error,
                                        void* stream) {
-  sv_status st = check_verify_shape(B, K, V);
-  if (st != SV_OK) return st;
-  if (n_drafter_rows < 0 || n_drafter_rows > 0x7fffffffL) return SV_ERR_SHAPE;
-  if (!drafter_rows && n_drafter_rows < (int64_t)B * K) return SV_ERR_SHAPE;
-  if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
-  if (!(temperature > 0.0f && isfinite(temperature) &&
-        isfinite((float)(1.4426950408889634 / (double)temperature))))
-    return SV_ERR_VALUE;
-  if (B == 0) return SV_OK;
-  if (!target_logits || !out_tokens || !out_num_accepted || !uniforms) return SV_ERR_NULL;
-  if (K > 0 && (!draft_tokens || !drafter_logits || !drafter_desc)) return SV_ERR_NULL;
-  if (!workspace || workspace_bytes < sv::verify_workspace_bytes(B, K, V)) return SV_ERR_WORKSPACE;
-  const size_t esz = logits_dtype == SV_BF16 ? 2 : 4;
-  if (!aligned(target_logits, esz) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
-      !aligned(uniforms, 4) || !aligned(workspace, 16) ||
-      (draft_tokens && !aligned(draft_tokens, 4)) ||
-      (drafter_logits && !aligned(drafter_logits, esz)) ||
-      (drafter_rows && !aligned(drafter_rows, 4)) ||
-      (drafter_desc && !aligned(drafter_desc, 16)) ||
-      (out_draft_target_prob && !aligned(out_draft_target_prob, 4)) ||
-      (device_error && !aligned(device_error, 4)))
-    return SV_ERR_ALIGN;
-  if ((long)B * (K + 1) * sv::verify_splits(B, K, V) > 0x7fffffffL) return SV_ERR_SHAPE;
-  sv::VerifyLaunch L;
-  L.logits = target_logits;
-  L.draft_probs = nullptr;
-  L.draft_tokens = draft_tokens;
-  L.uniforms = uniforms;
-  L.temperature = temperature;
-  L.B = B; L.K = K; L.V = V;
-  L.bf16 = logits_dtype == SV_BF16;
-  L.sample = 1;
-  L.mixed = 0;
-  L.temperatures = nullptr;
-  // a valid pointer for K = 0 (nothing is read from it then)
-  L.dlogits = drafter_logits ? drafter_logits : target_logits;
-  L.d_rows = (long)n_drafter_rows;
-  L.drows = drafter_rows;
-  L.ddesc = drafter_desc;
-  L.vec = (V % 8 == 0) && aligned(target_logits, 16) &&
-          (!drafter_logits || aligned(drafter_logits, 16));
-  L.out_tokens = out_tokens;
-  L.out_num_accepted = out_num_accepted;
-  L.out_p_draft = out_draft_target_prob;
-  L.workspace = workspace;
-  L.device_error = device_error;
-  return sv::launch_verify(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+  return sv::verify_lq(target_logits, logits_dtype, drafter_logits, n_drafter_rows,
+                       drafter_rows, drafter_desc, draft_tokens, uniforms, temperature, nullptr,
+                       B, K, V,
+                   out_tokens, out_num_accepted, out_draft_target_prob, workspace,
+                   workspace_bytes, device_error, stream);
+}
+
+SV_API sv_status spec_verify_mixed_lq(const void* target_logits, int logits_dtype,
+                                      const void* drafter_logits, int64_t n_drafter_rows,
+                                      const int32_t* drafter_rows,
+                                      const sv_draft_row* drafter_desc,
+                                      const int32_t* draft_tokens, const float* uniforms,
+                                      const float* temperatures, int B, int K, int V,
+                                      int32_t* out_tokens, int32_t* out_num_accepted,
+                                      float* out_draft_target_prob, void* workspace,
+                                      size_t workspace_bytes, int32_t* device_error,
+                                      void* stream) {
+  if (B > 0 && !temperatures) return SV_ERR_NULL;
+  // B = 0 with no temperatures validates as a uniform call and returns OK
+  return sv::verify_lq(target_logits, logits_dtype, drafter_logits, n_drafter_rows,
+                       drafter_rows, drafter_desc, draft_tokens, uniforms, 1.0f, temperatures,
+                       B, K, V, out_tokens, out_num_accepted, out_draft_target_prob, workspace,
+                       workspace_bytes, device_error, stream);
 }
 
 SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,

@@ -796,7 +796,8 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
     const dim3 grid3((unsigned)L.B);
 #define SV_DRAW_REG(LT, VEC, TH) \
   do { \
-    if (mode == MIXED) hipLaunchKernelGGL((verify_draw<LT, MIXED, VEC, false, TH, true>), grid3, dim3(TH), 0, stream, D); \
+    if (mode == MIXED && ql) hipLaunchKernelGGL((verify_draw<LT, MIXED, VEC, true, TH, true>), grid3, dim3(TH), 0, stream, D); \
+    else if (mode == MIXED) hipLaunchKernelGGL((verify_draw<LT, MIXED, VEC, false, TH, true>), grid3, dim3(TH), 0, stream, D); \
     else if (ql) hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, true, TH, true>), grid3, dim3(TH), 0, stream, D); \
     else hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, false, TH, true>), grid3, dim3(TH), 0, stream, D); \
   } while (0)
@@ -847,10 +848,9 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
       else { if (ql) LAUNCH(float, false, true); else LAUNCH(float, false, false); } \
     } \
   } while (0)
-  // q from the drafter logits comes with uniform-temperature sampling only
 #define SV_DRAW(LT, VEC, QL) \
   do { \
-    if (mode == MIXED && !QL) hipLaunchKernelGGL((verify_draw<LT, MIXED, VEC, false>), grid3, block, 0, stream, D); \
+    if (mode == MIXED) hipLaunchKernelGGL((verify_draw<LT, MIXED, VEC, QL>), grid3, block, 0, stream, D); \
     else if (dthreads == 4 * kThreads) hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, QL, 4 * kThreads>), grid3, dim3(4 * kThreads), 0, stream, D); \
     else if (dthreads == 2 * kThreads) hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, QL, 2 * kThreads>), grid3, dim3(2 * kThreads), 0, stream, D); \
     else hipLaunchKernelGGL((verify_draw<LT, SAMPLE, VEC, QL>), grid3, block, 0, stream, D); \

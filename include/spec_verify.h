@@ -276,6 +276,32 @@ SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
                                    int32_t* device_error, void* stream);
 
 /*
+ * A mixed serving batch (as spec_verify_mixed: per-sequence temperatures,
+ * 0 = greedy) whose drafter distributions are handed over as drafter logits
+ * plus row descriptors (as spec_verify_sample_lq).  Results equal those of
+ * spec_verify_mixed with draft_probs = the q that spec_draft_sample would have
+ * written for those rows (bit for bit).  Sources: "Project 14", section 架构
+ * (one verify pass over every request, each with its own sampling settings).
+ *   temperatures     [B] fp32 device array, as for spec_verify_mixed (bad
+ *                    values: SV_DEVERR_TEMPERATURE, verified greedily); the
+ *                    drafter rows and descriptors of greedy sequences are not
+ *                    read.
+ *   Other arguments as for spec_verify_sample_lq.  The kernels are enqueued
+ *   as for spec_verify_mixed.
+ */
+SV_API sv_status spec_verify_mixed_lq(const void* target_logits, int logits_dtype,
+                                      const void* drafter_logits, int64_t n_drafter_rows,
+                                      const int32_t* drafter_rows,
+                                      const sv_draft_row* drafter_desc,
+                                      const int32_t* draft_tokens,
+                                      const float* uniforms, const float* temperatures,
+                                      int B, int K, int V,
+                                      int32_t* out_tokens, int32_t* out_num_accepted,
+                                      float* out_draft_target_prob,
+                                      void* workspace, size_t workspace_bytes,
+                                      int32_t* device_error, void* stream);
+
+/*
  * Verification of a draft tree per sequence.  "Project 14", section 概念:
  * P-EAGLE's parallel speculation forms deeper draft trees (the pages give no
  * tree shape; any shape of up to SV_MAX_K nodes is accepted).  Node 0 is the

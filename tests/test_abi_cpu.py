@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
               "sv_status_string", "spec_accept_metrics", "spec_accept_metrics_words",
               "sv_step_graph_create", "sv_step_graph_launch", "sv_step_graph_destroy",
               "spec_verify_tree", "spec_verify_sample_lq", "spec_verify_sample_noalloc",
-              "spec_verify_tree_lq",
+              "spec_verify_tree_lq", "spec_verify_mixed_lq",
               "spec_verify_noalloc_scratch_bytes"):
         assert n in names
 
@@ -356,6 +356,28 @@ def test_sample_lq_validation(lib):
     assert lq(lib, desc=FAKE + 8) == EALIGN
     assert lq(lib, dl=FAKE + 1) == EALIGN
     assert lq(lib, rows=FAKE + 2) == EALIGN
+
+
+def mixed_lq(lib, logits=FAKE, dtype=1, dl=FAKE, n_rows=6, rows=None, desc=FAKE, d=FAKE, u=FAKE,
+             temps=FAKE, B=2, K=3, V=64, out=FAKE, acc=FAKE, pd=None, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(K, 0), max(V, 1))
+    return lib.spec_verify_mixed_lq(logits, dtype, dl, n_rows, rows, desc, d, u, temps, B, K, V,
+                                    out, acc, pd, ws, wsb, None, None)
+
+
+def test_mixed_lq_validation(lib):
+    assert mixed_lq(lib, K=64) == ESHAPE
+    assert mixed_lq(lib, n_rows=5) == ESHAPE             # fewer than B*K rows, no row index
+    assert mixed_lq(lib, dtype=2) == EDTYPE
+    assert mixed_lq(lib, temps=None) == ENULL            # per-sequence temperatures required
+    assert mixed_lq(lib, B=0, logits=None, dl=None, desc=None, d=None, u=None, temps=None,
+                    out=None, acc=None, ws=None, wsb=0) == OK
+    assert mixed_lq(lib, dl=None) == ENULL
+    assert mixed_lq(lib, desc=None) == ENULL
+    assert mixed_lq(lib, ws=None) == EWS
+    assert mixed_lq(lib, temps=FAKE + 2) == EALIGN
+    assert mixed_lq(lib, desc=FAKE + 8) == EALIGN
 
 
 def tree_lq(lib, logits=FAKE, dtype=1, dl=FAKE, n_rows=14, rows=None, desc=FAKE, par=FAKE,

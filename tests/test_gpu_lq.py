@@ -8,7 +8,9 @@ oracle.draft.draft_probs, then the sampled-verify oracle with its near-tie
 tolerance.  Covered: the 151936-token bf16 shape; a ragged bf16 vocabulary
 with drafter rows gathered through a row index, greedy-drafted sequences and
 invalid drafter rows; fp32 logits at a vocabulary that is a multiple of 8 and
-one that is not (rows gathered through a row index); no drafts at all.
+one that is not (rows gathered through a row index); no drafts at all; and
+mixed serving batches (spec_verify_mixed_lq against spec_verify_mixed on the
+dense q and against the oracle).
 """
 import numpy as np
 import pytest
@@ -157,3 +159,57 @@ def test_lq_matches_dense_mid_batch(gpu, dtype, V, B):
     uv = rng.random((B, K + 1), dtype=np.float32)
     _, _, _, dense, lq = _chain(gpu, dev(z), dev(zd), K, 0.8, 0.9, dev(ud), dev(uv))
     _same(dense, lq)
+
+
+@pytest.mark.parametrize("dtype,V,B", [("bf16", 151936, 24), ("bf16", 32000, 40),
+                                       ("f32", 4099, 40)])
+def test_mixed_lq_matches_mixed_and_oracle(gpu, dtype, V, B):
+    """A mixed serving batch (target temperatures per sequence from {0, 0.5,
+    0.7, 1.0, 1.3}) drafted at per-sequence drafter temperatures (greedy
+    drafting included): spec_verify_mixed on the dense q and
+    spec_verify_mixed_lq on the drafter logits + descriptors agree bit for
+    bit, and every sequence matches the oracle (greedy ones exactly)."""
+    K = 5
+    rng = np.random.default_rng(V + B)
+    z = (3.0 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    z[:, :, :8] += 6.0
+    zd = (z[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32)).reshape(B * K, V)
+    if dtype == "bf16":
+        z, zd = synth.f32_to_bf16_bits(z), synth.f32_to_bf16_bits(zd)
+    temps_d = synth.make_temperatures(B, 71)
+    temps_v = synth.make_temperatures(B, 72)
+    assert (temps_v == 0).any() and (temps_v > 0).any() and (temps_d == 0).any()
+    ud = rng.random((B, K), dtype=np.float32)
+    uv = rng.random((B, K + 1), dtype=np.float32)
+    tok, q, desc = gpu.spec_draft_sample(dev(zd), K, 1.0, uniforms=dev(ud),
+                                         temperatures=dev(temps_d), want_row_desc=True)
+    dense = gpu.spec_verify_mixed(dev(z), q, tok, dev(uv), dev(temps_v),
+                                  want_draft_target_prob=True)
+    lq = gpu.spec_verify_mixed_lq(dev(z), dev(zd), desc, tok, dev(uv), dev(temps_v),
+                                  want_draft_target_prob=True)
+    torch.cuda.synchronize()
+    _same(dense, lq)
+    out, acc, pd = (x.cpu().numpy() for x in lq)
+    tok = tok.cpu().numpy()
+    oq = oracle.draft.draft_probs(zd, dtype, 1.0, B, K, temperatures=temps_d)
+    checked = mism = flags = 0
+    for b in range(B):
+        od = [oracle.draft.draft_sample_row(oracle.decode_logits(zd[b * K + k], dtype),
+                                            float(temps_d[b]), ud[b, k])[0] for k in range(K)]
+        if list(tok[b]) != od:
+            continue                      # a flagged near tie in the draft itself
+        z64 = oracle.decode_logits(z[b], dtype)
+        if oracle.mixed.is_greedy(temps_v[b]):
+            w_out, w_acc, w_pd = oracle.verify_mixed(z[b:b + 1], dtype, oq[b:b + 1],
+                                                     tok[b:b + 1], uv[b:b + 1],
+                                                     temps_v[b:b + 1])
+            assert acc[b] == w_acc[0] and np.array_equal(out[b], w_out[0]), b
+            assert np.array_equal(pd[b], w_pd[0].astype(np.float32)), b
+        else:
+            same, f = check_sample_sequence(z64, oq[b], tok[b], uv[b], float(temps_v[b]), out[b],
+                                            acc[b], pd[b])
+            mism += not same
+            flags += f
+        checked += 1
+    assert mism <= flags
+    assert checked >= B - 2
