@@ -343,12 +343,16 @@ def ingest_trace(trace_csv, bench_log=None):
              "```\n",
              "`--profile-steps 5` runs, five times on the B=1024 K=7 V=151936 bf16 inputs: a sampled, a greedy and "
              "a mixed verify each followed by the build, the drafter sampling with dense q and with "
-             "row descriptors, the verify from drafter logits and the acceptance metrics; then the "
+             "row descriptors, the verify from drafter logits, the drafter sampling at per-sequence "
+             "temperatures with row descriptors, the mixed verify from drafter logits and the "
+             "acceptance metrics; then the "
              "fused build and the two-kernel build of the comparison library (`meta_kernel`, "
              "`copy_kernel`) five times each on the same verify outputs and at the B=64 H=2880 build "
              "workload, the comparison library's drafter-bytes kernels (`rows_to_f32`, "
              "`write_rows`; 4 calls each), five greedy and five sampled tree verifications (64 "
-             "trees of 15 nodes, V=151936 bf16), one pass each of the read-ceiling kernel "
+             "trees of 15 nodes, V=151936 bf16), one drafter sampling of one row per tree node "
+             "with row descriptors and five tree verifications from those drafter logits, "
+             "one pass each of the read-ceiling kernel "
              "(`stream_read<true>` non-temporal, `stream_read<false>` cached) over the 2.49 GB "
              "logit buffer, and one 1 GiB copy (the counter calibration).\n",
              f"Kernel source hash (bench.py `kernel_source_hash`): `{here}`\n",
@@ -1213,9 +1217,10 @@ def main():
     if args.profile_steps:
         # every kernel family once per step, for the profiler: sampled, greedy
         # and mixed verify with the build, drafter sampling with q and with
-        # row descriptors, the verify from drafter logits, acceptance metrics,
-        # and (below) tree verification
+        # row descriptors, the verify from drafter logits (uniform and mixed
+        # temperatures), acceptance metrics, and (below) tree verification
         d_desc = torch.empty((B, K, 4), dtype=torch.int32, device=dev)
+        m_desc = torch.empty((B, K, 4), dtype=torch.int32, device=dev)
         mtr = sv.accept_metrics_buffer(K, dev)
         for i in range(args.profile_steps):
             step(True); build(); step(False); build(); step("mixed"); build(); draft()
@@ -1225,6 +1230,11 @@ def main():
             sv.spec_verify_sample_lq(z, z_rows, d_desc, d_tok, u, vi.temperature,
                                      drafter_rows=d_rows, out_tokens=out_t,
                                      out_num_accepted=acc_t, workspace=ws)
+            sv.spec_draft_sample(z_rows, K, vi.temperature, uniforms=d_u, row_index=d_rows,
+                                 temperatures=temps, out_draft_tokens=d_tok,
+                                 want_draft_probs=False, out_row_desc=m_desc)
+            sv.spec_verify_mixed_lq(z, z_rows, m_desc, d_tok, u, temps, drafter_rows=d_rows,
+                                    out_tokens=out_t, out_num_accepted=acc_t, workspace=ws)
             sv.spec_accept_metrics(acc_t, K, mtr)
         torch.cuda.synchronize()
         # the build as two kernels (metadata, then the hidden copy) on the
@@ -1254,6 +1264,20 @@ def main():
         for i in range(args.profile_steps):
             for T in (0.0, ts.temperature):
                 sv.spec_verify_tree(tz, tp, tt, T, draft_probs=tq, uniforms=tu)
+        # the same trees with q from drafter logits: node (b, n) drafted from
+        # the target row of node n of tree b+1 (distinct rows, so that some
+        # children are rejected and the walk makes residual passes)
+        nt_ = ts.B * (ts.N + 1)
+        tzr = tz.view(nt_, ts.V)
+        trows = ((torch.arange(nt_, dtype=torch.int32, device=dev) + ts.N + 1) % nt_).view(
+            ts.B, ts.N + 1).contiguous()
+        tud = up(np.random.default_rng(9).random((nt_, 1), dtype=np.float32))
+        _, _, tdesc = sv.spec_draft_sample(tzr, 1, ts.temperature, uniforms=tud,
+                                           row_index=trows.view(nt_, 1), want_draft_probs=False,
+                                           want_row_desc=True)
+        for i in range(args.profile_steps):
+            sv.spec_verify_tree_lq(tz, tzr, tdesc.view(ts.B, ts.N + 1, 4), tp, tt, tu,
+                                   ts.temperature, drafter_rows=trows)
         torch.cuda.synchronize()
         # the read-ceiling kernel over the logit buffer, non-temporal and cached
         rd = _stream_read_fn()
