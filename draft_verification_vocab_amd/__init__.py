@@ -774,7 +774,9 @@ class _StepDesc(ctypes.Structure):
                 ("hidden_dtype", ctypes.c_int), ("mask_token_id", ctypes.c_int32),
                 ("H", ctypes.c_int), ("out_input_ids", _p), ("out_positions", _p),
                 ("out_slot_mapping", _p), ("out_hidden", _p), ("out_sample_rows", _p),
-                ("metrics", _p), ("device_error", _p)]
+                ("metrics", _p), ("device_error", _p),
+                ("drafter_logits", _p), ("n_drafter_rows", ctypes.c_int64),
+                ("drafter_rows", _p), ("drafter_desc", _p)]
 
 
 class StepGraph:
@@ -787,7 +789,10 @@ class StepGraph:
     verify: dict with target_logits, draft_tokens, out_tokens,
       out_num_accepted, workspace, and for sampling draft_probs, uniforms and
       temperature (mode "sample") or temperatures (mode "mixed"); optional
-      out_draft_target_prob.
+      out_draft_target_prob.  For sampling with q from the drafter logits,
+      drafter_logits ([n_rows, V]) and drafter_desc ([B, K, 4] int32, from
+      spec_draft_sample) replace draft_probs, with an optional drafter_rows
+      ([B, K] int32).
     build: None, or dict with start_pos, block_table, block_size,
       target_hidden, h_shared, mask_token_id and outputs (as returned by
       peagle_build_draft_batch or preallocated).
@@ -818,8 +823,20 @@ class StepGraph:
         d.target_logits = ptr(z, "target_logits")
         d.logits_dtype = _DTYPES[z.dtype]
         d.draft_tokens = ptr(verify["draft_tokens"], "draft_tokens", torch.int32, (B, K))
+        zd = verify.get("drafter_logits")
+        if zd is not None:
+            if mode == "greedy" or verify.get("draft_probs") is not None:
+                raise ValueError("drafter_logits replaces draft_probs, for sampling only")
+            if zd.dim() != 2 or zd.shape[1] != V or zd.dtype != z.dtype:
+                raise ValueError("drafter_logits must be [n_rows, V] in the target's dtype")
+            d.drafter_logits = ptr(zd, "drafter_logits")
+            d.n_drafter_rows = zd.shape[0]
+            d.drafter_rows = ptr(verify.get("drafter_rows"), "drafter_rows", torch.int32, (B, K))
+            d.drafter_desc = ptr(verify["drafter_desc"], "drafter_desc", torch.int32, (B, K, 4))
         if mode != "greedy":
-            d.draft_probs = ptr(verify["draft_probs"], "draft_probs", torch.float32, (B, K, V))
+            if zd is None:
+                d.draft_probs = ptr(verify["draft_probs"], "draft_probs", torch.float32,
+                                    (B, K, V))
             d.uniforms = ptr(verify["uniforms"], "uniforms", torch.float32, (B, K + 1))
         if mode == "sample":
             d.temperature = float(verify["temperature"])

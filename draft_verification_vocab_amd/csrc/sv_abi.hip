@@ -556,28 +556,43 @@ struct sv_step_graph {
 
 namespace {
 
-// The calls of one step, in order, on stream s (each validates its arguments).
-sv_status enqueue_step(const sv_step_desc* d, hipStream_t s) {
-  sv_status st;
+// The step's verify call, on the dense q or on the drafter logits (each call
+// validates its own arguments).
+sv_status enqueue_verify(const sv_step_desc* d, hipStream_t s) {
+  if (d->drafter_logits) {
+    if (d->mode == SV_STEP_SAMPLE)
+      return spec_verify_sample_lq(d->target_logits, d->logits_dtype, d->drafter_logits,
+                                   d->n_drafter_rows, d->drafter_rows, d->drafter_desc,
+                                   d->draft_tokens, d->uniforms, d->temperature, d->B, d->K, d->V,
+                                   d->out_tokens, d->out_num_accepted, d->out_draft_target_prob,
+                                   d->workspace, d->workspace_bytes, d->device_error, s);
+    return spec_verify_mixed_lq(d->target_logits, d->logits_dtype, d->drafter_logits,
+                                d->n_drafter_rows, d->drafter_rows, d->drafter_desc,
+                                d->draft_tokens, d->uniforms, d->temperatures, d->B, d->K, d->V,
+                                d->out_tokens, d->out_num_accepted, d->out_draft_target_prob,
+                                d->workspace, d->workspace_bytes, d->device_error, s);
+  }
   switch (d->mode) {
     case SV_STEP_GREEDY:
-      st = spec_verify_greedy(d->target_logits, d->logits_dtype, d->draft_tokens, d->B, d->K,
-                              d->V, d->out_tokens, d->out_num_accepted, d->workspace,
-                              d->workspace_bytes, d->device_error, s);
-      break;
+      return spec_verify_greedy(d->target_logits, d->logits_dtype, d->draft_tokens, d->B, d->K,
+                                d->V, d->out_tokens, d->out_num_accepted, d->workspace,
+                                d->workspace_bytes, d->device_error, s);
     case SV_STEP_SAMPLE:
-      st = spec_verify_sample(d->target_logits, d->logits_dtype, d->draft_probs, d->draft_tokens,
-                              d->uniforms, d->temperature, d->B, d->K, d->V, d->out_tokens,
-                              d->out_num_accepted, d->out_draft_target_prob, d->workspace,
-                              d->workspace_bytes, d->device_error, s);
-      break;
+      return spec_verify_sample(d->target_logits, d->logits_dtype, d->draft_probs,
+                                d->draft_tokens, d->uniforms, d->temperature, d->B, d->K, d->V,
+                                d->out_tokens, d->out_num_accepted, d->out_draft_target_prob,
+                                d->workspace, d->workspace_bytes, d->device_error, s);
     default:
-      st = spec_verify_mixed(d->target_logits, d->logits_dtype, d->draft_probs, d->draft_tokens,
-                             d->uniforms, d->temperatures, d->B, d->K, d->V, d->out_tokens,
-                             d->out_num_accepted, d->out_draft_target_prob, d->workspace,
-                             d->workspace_bytes, d->device_error, s);
-      break;
+      return spec_verify_mixed(d->target_logits, d->logits_dtype, d->draft_probs,
+                               d->draft_tokens, d->uniforms, d->temperatures, d->B, d->K, d->V,
+                               d->out_tokens, d->out_num_accepted, d->out_draft_target_prob,
+                               d->workspace, d->workspace_bytes, d->device_error, s);
   }
+}
+
+// The calls of one step, in order, on stream s (each validates its arguments).
+sv_status enqueue_step(const sv_step_desc* d, hipStream_t s) {
+  sv_status st = enqueue_verify(d, s);
   if (st != SV_OK) return st;
   if (d->out_hidden) {
     st = peagle_build_draft_batch(d->out_tokens, d->out_num_accepted, d->draft_tokens,
@@ -601,6 +616,9 @@ SV_API sv_status sv_step_graph_create(const sv_step_desc* desc, sv_step_graph** 
   if (!desc || !out) return SV_ERR_NULL;
   *out = nullptr;
   if (desc->mode != SV_STEP_GREEDY && desc->mode != SV_STEP_SAMPLE && desc->mode != SV_STEP_MIXED)
+    return SV_ERR_VALUE;
+  // q from the drafter logits replaces the dense q, and only for sampling
+  if (desc->drafter_logits && (desc->mode == SV_STEP_GREEDY || desc->draft_probs))
     return SV_ERR_VALUE;
   if (desc->metrics && (desc->K < 1 || desc->K > SV_MAX_K)) return SV_ERR_SHAPE;
   hipStream_t s = nullptr;

@@ -501,9 +501,14 @@ SV_API sv_status spec_accept_metrics(const int32_t* num_accepted, int B, int K, 
  * section TorchSpec 集成与工程优化); each replay reads whatever the buffers
  * hold at that time.  The buffers must stay allocated while the graph exists.
  * Fields mirror the arguments of the calls above; the build is skipped when
- * out_hidden is NULL and the metrics when metrics is NULL.  Argument errors
- * of the captured calls are returned by sv_step_graph_create, which then
- * creates nothing.  Kernel tracing is paused during capture.
+ * out_hidden is NULL and the metrics when metrics is NULL.  With
+ * drafter_logits set (sample / mixed only) the captured verify is
+ * spec_verify_sample_lq or spec_verify_mixed_lq on drafter_logits,
+ * n_drafter_rows, drafter_rows and drafter_desc, and draft_probs must be NULL
+ * (SV_ERR_VALUE otherwise; SV_ERR_VALUE too for drafter_logits in greedy
+ * mode).  Argument errors of the captured calls are returned by
+ * sv_step_graph_create, which then creates nothing.  Kernel tracing is paused
+ * during capture.
  */
 #define SV_STEP_GREEDY 0
 #define SV_STEP_SAMPLE 1
@@ -538,6 +543,10 @@ typedef struct sv_step_desc {
   int32_t* out_sample_rows;               /* optional                            */
   uint64_t* metrics;                      /* NULL: no metrics                    */
   int32_t* device_error;                  /* optional                            */
+  const void* drafter_logits;             /* NULL: dense draft_probs             */
+  int64_t n_drafter_rows;                 /* with drafter_logits                 */
+  const int32_t* drafter_rows;            /* optional, with drafter_logits       */
+  const sv_draft_row* drafter_desc;       /* with drafter_logits                 */
 } sv_step_desc;
 
 typedef struct sv_step_graph sv_step_graph;   /* opaque */

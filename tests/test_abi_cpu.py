@@ -275,6 +275,12 @@ def test_metrics_and_graph_validation(lib):
     assert lib.sv_step_graph_create(ctypes.byref(d), ctypes.byref(g)) == EVALUE
     d.mode, d.metrics, d.K = 1, FAKE, 0
     assert lib.sv_step_graph_create(ctypes.byref(d), ctypes.byref(g)) == ESHAPE
+    # q from drafter logits: sampling only, and never beside a dense q
+    d.metrics, d.K, d.drafter_logits = None, 3, FAKE
+    d.mode, d.draft_probs = 0, None
+    assert lib.sv_step_graph_create(ctypes.byref(d), ctypes.byref(g)) == EVALUE
+    d.mode, d.draft_probs = 2, FAKE
+    assert lib.sv_step_graph_create(ctypes.byref(d), ctypes.byref(g)) == EVALUE
     assert lib.sv_step_graph_launch(None, None) == ENULL
     lib.sv_step_graph_destroy(None)
 

@@ -9,7 +9,8 @@
   verify outputs of every sequence, greedy ones exactly and sampled ones up
   to 1e-6 near ties; the build bit for bit), equal the eager step on the
   same inputs bit for bit, and the metrics must equal the oracle's counters
-  of all replays.  Greedy, sampled and mixed graphs.
+  of all replays.  Greedy, sampled and mixed graphs, and sampled and mixed
+  graphs with q from the drafter logits.
 """
 import numpy as np
 import pytest
@@ -233,6 +234,84 @@ def test_step_graph_one_draw_workgroup_per_sequence(gpu, B, V, dtype):
         torch.cuda.synchronize()
         _replay_matches_oracle("sample", logits, dtype, q, d, u_new, T, None, og, bi)
         _eager(gpu, "sample", inp, b, oe, ws_e, me)
+        torch.cuda.synchronize()
+        assert torch.equal(og["tok"], oe["tok"]) and torch.equal(og["acc"], oe["acc"]), rep
+        assert torch.equal(og["pd"].view(torch.int32), oe["pd"].view(torch.int32)), rep
+        for k in og["build"]:
+            assert torch.equal(og["build"][k], oe["build"][k]), (rep, k)
+    assert torch.equal(mg, me)
+    assert int(ws_g.count_nonzero().item()) == 0
+    graph.close()
+
+
+@pytest.mark.parametrize("mode", ["sample", "mixed"])
+def test_step_graph_lq_replays_match_oracle(gpu, mode):
+    """Step graphs whose verify recomputes q from the drafter logits (sampled,
+    with the drafter rows gathered through a row index; mixed, drafted at the
+    requests' own temperatures).  Before each replay the drafter sampling
+    writes new draft tokens and row descriptors into the captured buffers
+    (fresh drafter uniforms) and new verify uniforms are copied in.  Every
+    replay matches the oracle (q from oracle.draft.draft_probs of the drafter
+    rows; the build bit for bit) and equals the eager step on the dense q of
+    the same drafting bit for bit; the metrics equal the eager ones."""
+    vi = synth.make_verify_inputs(synth.verify_config(2))       # B=8, K=5, V=32000 fp32
+    B, K, V, dt = vi.spec.B, vi.spec.K, vi.spec.V, vi.spec.dtype
+    rng = np.random.default_rng(74)
+    base = oracle.decode_logits(vi.logits[:, :K].reshape(B * K, V), dt)
+    zd = (base + rng.standard_normal(base.shape)).astype(np.float32)
+    zd[~np.isfinite(base)] = base[~np.isfinite(base)]
+    perm = rng.permutation(B * K).astype(np.int32).reshape(B, K) if mode == "sample" else None
+    if perm is not None:                 # drafter row (b, k) stored at perm[b, k]
+        stored = np.empty_like(zd)
+        stored[perm.reshape(-1)] = zd
+        zd = stored
+    if dt == "bf16":
+        zd = synth.f32_to_bf16_bits(zd)
+    temps = np.array([0.0, 0.5, 1.0, 0.0, 1.3, 0.7, 0.0, 2.0], dtype=np.float32)
+    Td = 0.8
+    oq = oracle.draft.draft_probs(zd, dt, Td, B, K, row_index=perm,
+                                  temperatures=temps if mode == "mixed" else None)
+    z_t, zd_t, temps_t = dev(vi.logits), dev(zd), dev(temps)
+    rows_t = None if perm is None else dev(perm)
+    d_t = torch.empty((B, K), dtype=torch.int32, device=DEV)
+    desc_t = torch.empty((B, K, 4), dtype=torch.int32, device=DEV)
+    q_e = torch.empty((B, K, V), dtype=torch.float32, device=DEV)
+    u_t = torch.empty((B, K + 1), dtype=torch.float32, device=DEV)
+    ud_t = torch.empty((B, K), dtype=torch.float32, device=DEV)
+
+    def draft(ud):
+        ud_t.copy_(dev(ud))
+        gpu.spec_draft_sample(zd_t, K, Td, uniforms=ud_t, row_index=rows_t,
+                              temperatures=temps_t if mode == "mixed" else None,
+                              out_draft_tokens=d_t, out_draft_probs=q_e, out_row_desc=desc_t)
+
+    draft(rng.random((B, K), dtype=np.float32))
+    b = _build_inputs(B, K, V)
+    bi = b.pop("host")
+    og, oe = _outputs(B, K, V, 512), _outputs(B, K, V, 512)
+    ws_g = torch.zeros(gpu.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=DEV)
+    ws_e = torch.zeros_like(ws_g)
+    mg, me = gpu.accept_metrics_buffer(K, DEV), gpu.accept_metrics_buffer(K, DEV)
+    verify = dict(target_logits=z_t, draft_tokens=d_t, out_tokens=og["tok"],
+                  out_num_accepted=og["acc"], workspace=ws_g, uniforms=u_t,
+                  out_draft_target_prob=og["pd"], drafter_logits=zd_t, drafter_desc=desc_t,
+                  drafter_rows=rows_t)
+    if mode == "sample":
+        verify["temperature"] = vi.temperature
+    else:
+        verify["temperatures"] = temps_t
+    graph = gpu.StepGraph(mode, verify, dict(b, outputs=og["build"]), metrics=mg)
+    inp = dict(z=z_t, q=q_e, d=d_t, u=u_t, T=vi.temperature, temps=temps_t)
+    for rep in range(4):
+        draft(rng.random((B, K), dtype=np.float32))
+        u_new = rng.random((B, K + 1), dtype=np.float32)
+        u_t.copy_(dev(u_new))
+        graph.launch()
+        torch.cuda.synchronize()
+        d_host = d_t.cpu().numpy()
+        _replay_matches_oracle(mode, vi.logits, dt, oq, d_host, u_new, vi.temperature, temps,
+                               og, bi)
+        _eager(gpu, mode, inp, b, oe, ws_e, me)
         torch.cuda.synchronize()
         assert torch.equal(og["tok"], oe["tok"]) and torch.equal(og["acc"], oe["acc"]), rep
         assert torch.equal(og["pd"].view(torch.int32), oe["pd"].view(torch.int32)), rep
