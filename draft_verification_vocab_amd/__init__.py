@@ -89,6 +89,7 @@ _SIGS = {
     "sv_trace_count": (_i, []),
     "sv_trace_read": (_i, [_i, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)]),
     "sv_trace_end": (None, []),
+    "sv_trace_enable": (None, [_i]),
 }
 
 
@@ -167,6 +168,11 @@ def trace_read():
 
 def trace_end():
     require_library().sv_trace_end()
+
+
+def trace_enable(on: bool):
+    """Pause (False) or resume (True) the active trace of this host thread."""
+    require_library().sv_trace_enable(1 if on else 0)
 
 
 # ---------------------------------------------------------------- helpers

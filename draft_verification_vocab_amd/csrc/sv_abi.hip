@@ -130,6 +130,10 @@ SV_API sv_status sv_trace_read(int i, int* kernel_id, float* ms) {
 
 SV_API void sv_trace_end(void) { sv::tracer.destroy(); }
 
+SV_API void sv_trace_enable(int on) {
+  if (sv::tracer.cap > 0) sv::tracer.on = on != 0;
+}
+
 SV_API size_t spec_verify_workspace_bytes(int B, int K, int V) {
   if (check_verify_shape(B, K, V) != SV_OK) return 0;
   if (B == 0) return 0;

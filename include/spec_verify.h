@@ -563,6 +563,10 @@ SV_API void sv_step_graph_destroy(sv_step_graph* graph);
  * the kernel's id and its duration in milliseconds.  sv_trace_begin creates
  * the events (it may be called again to start over); sv_trace_end destroys
  * them.  Tracing adds two event records per traced launch and nothing else.
+ * sv_trace_enable(0) pauses an active trace (launches enqueued meanwhile are
+ * neither traced nor counted against `capacity`) and sv_trace_enable(1)
+ * resumes it, so that a caller can trace a sample of a loop's launches; it
+ * does nothing when no trace is active.
  */
 #define SV_KERNEL_VERIFY_GREEDY_ROWS 0   /* spec_verify_greedy: row max / argmax         */
 #define SV_KERNEL_VERIFY_SAMPLE_ROWS 1   /* spec_verify_sample: row max / sum of exp     */
@@ -583,6 +587,7 @@ SV_API sv_status sv_trace_begin(int capacity, unsigned kernel_mask); /* SV_ERR_V
 SV_API int sv_trace_count(void);                     /* launches traced so far         */
 SV_API sv_status sv_trace_read(int i, int* kernel_id, float* ms);  /* waits for entry i */
 SV_API void sv_trace_end(void);
+SV_API void sv_trace_enable(int on);                 /* pause (0) / resume (1)        */
 
 #ifdef __cplusplus
 }

@@ -194,6 +194,9 @@ def test_tracer_host_paths(lib):
                      b"tree_walk"]
     assert lib.sv_kernel_name(11) == b"unknown"
     assert lib.sv_kernel_name(17) == b"unknown"
+    lib.sv_trace_enable(1)                          # no trace active: nothing happens
+    lib.sv_trace_enable(0)
+    assert lib.sv_trace_count() == 0
     lib.sv_trace_end()                              # harmless when tracing is off
 
 
