@@ -8,9 +8,10 @@ oracle.draft.draft_probs, then the sampled-verify oracle with its near-tie
 tolerance.  Covered: the 151936-token bf16 shape; a ragged bf16 vocabulary
 with drafter rows gathered through a row index, greedy-drafted sequences and
 invalid drafter rows; fp32 logits at a vocabulary that is a multiple of 8 and
-one that is not (rows gathered through a row index); no drafts at all; and
+one that is not (rows gathered through a row index); no drafts at all;
 mixed serving batches (spec_verify_mixed_lq against spec_verify_mixed on the
-dense q and against the oracle).
+dense q and against the oracle); and the vocabularies of the shape sweep
+around multiples of the CDF tile, uniform and mixed.
 """
 import numpy as np
 import pytest
@@ -20,6 +21,7 @@ import oracle
 import synth
 from synth.workloads import DRAFT_CONFIGS, make_draft_inputs
 from tests.gpu_util import DEV, check_sample_sequence, dev
+from tests.test_gpu_shapes import VOCABS
 
 pytestmark = pytest.mark.gpu
 
@@ -213,3 +215,57 @@ def test_mixed_lq_matches_mixed_and_oracle(gpu, dtype, V, B):
         checked += 1
     assert mism <= flags
     assert checked >= B - 2
+
+
+@pytest.mark.parametrize("i", range(len(VOCABS)))
+def test_lq_boundary_shapes(gpu, i):
+    """q from the drafter logits over the vocabularies of the shape sweep
+    (just below, at and just above multiples of the 2048-element CDF tile),
+    with random B and K, both dtypes, and uniform and mixed temperatures in
+    turn, so that every draw form (tiles in registers, one workgroup per
+    sequence, chunks with the locate kernel) meets the drafter-logit loads:
+    bit for bit the dense verify on the same drafting, and every sequence
+    against the oracle (q from oracle.draft.draft_probs)."""
+    rng = np.random.default_rng(9100 + i)
+    V = VOCABS[i]
+    B = int(rng.integers(1, 24))
+    K = int(rng.integers(1, 10))
+    dtype = ("bf16", "f32")[i % 2]
+    mixed = i % 3 == 0
+    z = (3.0 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    z[:, :, :8] += 6.0
+    zd = (z[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32)).reshape(B * K, V)
+    if dtype == "bf16":
+        z, zd = synth.f32_to_bf16_bits(z), synth.f32_to_bf16_bits(zd)
+    ud = rng.random((B, K), dtype=np.float32)
+    uv = rng.random((B, K + 1), dtype=np.float32)
+    Td, T = 0.8, 0.9
+    temps_d = synth.make_temperatures(B, 7 + i) if mixed else None
+    temps_v = synth.make_temperatures(B, 17 + i) if mixed else None
+    tok, q, desc = gpu.spec_draft_sample(dev(zd), K, Td, uniforms=dev(ud),
+                                         temperatures=None if temps_d is None else dev(temps_d),
+                                         want_row_desc=True)
+    if mixed:
+        dense = gpu.spec_verify_mixed(dev(z), q, tok, dev(uv), dev(temps_v),
+                                      want_draft_target_prob=True)
+        lq = gpu.spec_verify_mixed_lq(dev(z), dev(zd), desc, tok, dev(uv), dev(temps_v),
+                                      want_draft_target_prob=True)
+    else:
+        dense = gpu.spec_verify_sample(dev(z), q, tok, dev(uv), T, want_draft_target_prob=True)
+        lq = gpu.spec_verify_sample_lq(dev(z), dev(zd), desc, tok, dev(uv), T,
+                                       want_draft_target_prob=True)
+    torch.cuda.synchronize()
+    _same(dense, lq)
+    out, acc, pd = (x.cpu().numpy() for x in lq)
+    tok = tok.cpu().numpy()
+    oq = oracle.draft.draft_probs(zd, dtype, Td, B, K, temperatures=temps_d)
+    for b in range(B):
+        z64 = oracle.decode_logits(z[b], dtype)
+        if mixed and oracle.mixed.is_greedy(temps_v[b]):
+            w_out, w_acc, w_pd = oracle.verify_mixed(z[b:b + 1], dtype, oq[b:b + 1], tok[b:b + 1],
+                                                     uv[b:b + 1], temps_v[b:b + 1])
+            assert acc[b] == w_acc[0] and np.array_equal(out[b], w_out[0]), b
+            assert np.array_equal(pd[b], w_pd[0].astype(np.float32)), b
+        else:
+            Tb = float(temps_v[b]) if mixed else T
+            check_sample_sequence(z64, oq[b], tok[b], uv[b], Tb, out[b], acc[b], pd[b])
