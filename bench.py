@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-small", action="store_true",
                     help="skip timing the mid-size verify, the P-EAGLE build, the "
                          "large-vocabulary verify workloads and the fp32-logit verify")
+    ap.add_argument("--no-early-exit", action="store_true",
+                    help="skip the early-exit verify comparison")
     ap.add_argument("--no-draft", action="store_true",
                     help="skip timing the drafter-output sampling kernel")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -624,6 +626,54 @@ def graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt, hid, hs
         return out
     return {"note": "verify_sample + P-EAGLE build + acceptance metrics per step",
             "full": run(B), "small": run(16), "single": run(1)}
+
+
+def early_exit_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, temps, L, bt, hid, hs,
+                     ws, bouts):
+    """The fused step with the early-exit verify forms against the full ones
+    (each + P-EAGLE build, same inputs): wall time per step, the row
+    statistics launches, the logit rows read, and whether tokens and accept
+    counts are identical.  Not the headline figure: these forms skip the rows
+    past each sequence's first rejection."""
+    dev = z.device
+    T = vi.temperature
+    outs = {}
+    res = {"workload": f"B={B} K={K} V={V} bf16 + P-EAGLE build H={hid.shape[1]}; the early-exit "
+                       "forms read only the rows up to each sequence's first rejection "
+                       "(draft positions in launch ranges [0,1), [1,2), [2,4), [4,8))"}
+    calls = {
+        "greedy": (sv.spec_verify_greedy, sv.spec_verify_greedy_early_exit, (z, d), {}),
+        "sample": (sv.spec_verify_sample, sv.spec_verify_sample_early_exit, (z, q, d, u, T), {}),
+        "mixed": (sv.spec_verify_mixed, sv.spec_verify_mixed_early_exit, (z, q, d, u, temps), {}),
+    }
+    for mode, (full, ee, a, kw) in calls.items():
+        for name, fn in (("full", full), ("early_exit", ee)):
+            ot = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+            oa = torch.empty((B,), dtype=torch.int32, device=dev)
+
+            def step():
+                fn(*a, out_tokens=ot, out_num_accepted=oa, workspace=ws)
+                sv.peagle_build_draft_batch(ot, oa, d, L, bt, bi.spec.block_size, hid, hs,
+                                            bi.mask_token_id, outputs=bouts)
+            ms = wall_ms(torch, step, args.warmup, args.steps)
+            sv.trace_begin(64)
+            step()
+            torch.cuda.synchronize()
+            kern = [(k, m) for k, m in sv.trace_read()]
+            sv.trace_end()
+            rows_launches = [m for k, m in kern if k.endswith("_rows")]
+            outs[(mode, name)] = (ot.clone(), oa.clone())
+            res[f"{mode}_{name}_ms_per_step"] = ms
+            res[f"{mode}_{name}_rows_launch_ms"] = rows_launches
+        acc = outs[(mode, "full")][1].long()
+        res[f"{mode}_rows_needed"] = int((acc + 1).clamp(max=K + 1).sum().item())
+        res[f"{mode}_speedup"] = (res[f"{mode}_full_ms_per_step"]
+                                  / res[f"{mode}_early_exit_ms_per_step"])
+        res[f"{mode}_identical_outputs"] = bool(
+            torch.equal(outs[(mode, "full")][0], outs[(mode, "early_exit")][0])
+            and torch.equal(outs[(mode, "full")][1], outs[(mode, "early_exit")][1]))
+    res["rows_total"] = B * (K + 1)
+    return res
 
 
 def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, out_t, acc_t,
@@ -1462,6 +1512,10 @@ def main():
             "step_hbm_gbs": (vm_rows + vm_draw + bb) / sec_m / 1e9,
             "step_hbm_frac": (vm_rows + vm_draw + bb) / sec_m / 1e9 / HBM_PEAK_GBS}
         log("mixed step timed")
+    if not args.no_early_exit:
+        res["early_exit"] = early_exit_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u,
+                                             temps, L, bt, hid, hs, ws, bouts)
+        log("early-exit verify timed")
     if not args.no_graph:
         res["graph_step"] = graph_bench(sv, torch, np, args, B, K, V, vi, bi, z, q, d, u, L, bt,
                                         hid, hs, out_t, acc_t, pd_t, ws, bouts)

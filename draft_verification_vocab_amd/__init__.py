@@ -36,7 +36,8 @@ __all__ = [
     "spec_verify_greedy", "spec_verify_sample", "peagle_build_draft_batch",
     "SpecVerifyError", "SV_F32", "SV_BF16", "SV_F16", "PADDING_SLOT_ID",
     "spec_verify_mixed", "spec_verify_sample_lq", "spec_verify_mixed_lq",
-    "spec_verify_sample_noalloc",
+    "spec_verify_sample_noalloc", "spec_verify_greedy_early_exit",
+    "spec_verify_sample_early_exit", "spec_verify_mixed_early_exit",
     "noalloc_scratch_bytes", "spec_verify_tree", "spec_verify_tree_lq", "spec_draft_sample",
     "spec_accept_metrics", "accept_metrics_buffer", "acceptance_summary", "StepGraph",
     "trace_begin", "trace_read", "trace_end",
@@ -69,6 +70,12 @@ _SIGS = {
                                         _p, _p, _p]),
     "spec_verify_mixed": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p,
                                ctypes.c_size_t, _p, _p]),
+    "spec_verify_greedy_early_exit": (_i, [_p, _i, _p, _i, _i, _i, _p, _p, _p, ctypes.c_size_t,
+                                           _p, _p]),
+    "spec_verify_sample_early_exit": (_i, [_p, _i, _p, _p, _p, ctypes.c_float, _i, _i, _i, _p,
+                                           _p, _p, _p, ctypes.c_size_t, _p, _p]),
+    "spec_verify_mixed_early_exit": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p,
+                                          ctypes.c_size_t, _p, _p]),
     "spec_draft_sample": (_i, [_p, _i, ctypes.c_int64, _p, _p, ctypes.c_float, _p, _i, _i, _i,
                                _p, _p, _p, _p, _p]),
     "spec_verify_sample_lq": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, ctypes.c_float,
@@ -230,7 +237,8 @@ def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor,
                        out_tokens: Optional[torch.Tensor] = None,
                        out_num_accepted: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None,
-                       device_error: Optional[torch.Tensor] = None):
+                       device_error: Optional[torch.Tensor] = None,
+                       _symbol: str = "spec_verify_greedy"):
     """Greedy verify; see spec_verify_greedy in include/spec_verify.h.
 
     target_logits [B, K+1, V] float32/bfloat16, draft_tokens [B, K] int32.
@@ -256,11 +264,12 @@ def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor,
     _dev(workspace, "workspace", device=dev)
     if device_error is not None:
         _dev(device_error, "device_error", torch.int32, (1,), dev)
-    st = lib.spec_verify_greedy(_ptr(target_logits), _DTYPES[target_logits.dtype], _ptr(draft_tokens),
-                                B, K, V, _ptr(out_tokens), _ptr(out_num_accepted), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _ptr(device_error),
-                                _stream(dev))
-    _check(st, "spec_verify_greedy")
+    st = getattr(lib, _symbol)(_ptr(target_logits), _DTYPES[target_logits.dtype],
+                               _ptr(draft_tokens), B, K, V, _ptr(out_tokens),
+                               _ptr(out_num_accepted), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(device_error),
+                               _stream(dev))
+    _check(st, _symbol)
     return out_tokens, out_num_accepted
 
 
@@ -271,7 +280,8 @@ def spec_verify_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor,
                        out_draft_target_prob: Optional[torch.Tensor] = None,
                        want_draft_target_prob: bool = False,
                        workspace: Optional[torch.Tensor] = None,
-                       device_error: Optional[torch.Tensor] = None):
+                       device_error: Optional[torch.Tensor] = None,
+                       _symbol: str = "spec_verify_sample"):
     """Rejection-sampling verify; see spec_verify_sample in include/spec_verify.h.
 
     Returns (out_tokens, num_accepted, draft_target_prob or None).
@@ -302,12 +312,12 @@ def spec_verify_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor,
     _dev(workspace, "workspace", device=dev)
     if device_error is not None:
         _dev(device_error, "device_error", torch.int32, (1,), dev)
-    st = lib.spec_verify_sample(_ptr(target_logits), _DTYPES[target_logits.dtype], _ptr(draft_probs),
+    st = getattr(lib, _symbol)(_ptr(target_logits), _DTYPES[target_logits.dtype], _ptr(draft_probs),
                                 _ptr(draft_tokens), _ptr(uniforms), float(temperature), B, K, V,
                                 _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_draft_target_prob),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _ptr(device_error), _stream(dev))
-    _check(st, "spec_verify_sample")
+    _check(st, _symbol)
     return out_tokens, out_num_accepted, out_draft_target_prob
 
 
@@ -359,7 +369,8 @@ def spec_verify_mixed(target_logits: torch.Tensor, draft_probs: torch.Tensor,
                       out_draft_target_prob: Optional[torch.Tensor] = None,
                       want_draft_target_prob: bool = False,
                       workspace: Optional[torch.Tensor] = None,
-                      device_error: Optional[torch.Tensor] = None):
+                      device_error: Optional[torch.Tensor] = None,
+                      _symbol: str = "spec_verify_mixed"):
     """Verify with a temperature per sequence (0 = greedy); see
     spec_verify_mixed in include/spec_verify.h.
 
@@ -392,13 +403,35 @@ def spec_verify_mixed(target_logits: torch.Tensor, draft_probs: torch.Tensor,
     _dev(workspace, "workspace", device=dev)
     if device_error is not None:
         _dev(device_error, "device_error", torch.int32, (1,), dev)
-    st = lib.spec_verify_mixed(_ptr(target_logits), _DTYPES[target_logits.dtype], _ptr(draft_probs),
-                               _ptr(draft_tokens), _ptr(uniforms), _ptr(temperatures), B, K, V,
-                               _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_draft_target_prob),
+    st = getattr(lib, _symbol)(_ptr(target_logits), _DTYPES[target_logits.dtype],
+                               _ptr(draft_probs), _ptr(draft_tokens), _ptr(uniforms),
+                               _ptr(temperatures), B, K, V, _ptr(out_tokens),
+                               _ptr(out_num_accepted), _ptr(out_draft_target_prob),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _ptr(device_error), _stream(dev))
-    _check(st, "spec_verify_mixed")
+    _check(st, _symbol)
     return out_tokens, out_num_accepted, out_draft_target_prob
+
+
+def spec_verify_greedy_early_exit(*args, **kw):
+    """spec_verify_greedy computing only the rows up to each sequence's first
+    rejection; see spec_verify_greedy_early_exit in include/spec_verify.h.
+    Arguments and results as spec_verify_greedy."""
+    return spec_verify_greedy(*args, _symbol="spec_verify_greedy_early_exit", **kw)
+
+
+def spec_verify_sample_early_exit(*args, **kw):
+    """spec_verify_sample computing only the rows up to each sequence's first
+    rejection; see spec_verify_sample_early_exit in include/spec_verify.h.
+    Arguments as spec_verify_sample; draft_target_prob is 0 past num_accepted."""
+    return spec_verify_sample(*args, _symbol="spec_verify_sample_early_exit", **kw)
+
+
+def spec_verify_mixed_early_exit(*args, **kw):
+    """spec_verify_mixed computing only the rows up to each sequence's first
+    rejection; see spec_verify_mixed_early_exit in include/spec_verify.h.
+    Arguments as spec_verify_mixed; draft_target_prob is 0 past num_accepted."""
+    return spec_verify_mixed(*args, _symbol="spec_verify_mixed_early_exit", **kw)
 
 
 # ---------------------------------------------------------------- P-EAGLE

@@ -153,7 +153,7 @@ sv_status verify_common(const void* logits, int dtype, const float* draft_probs,
                         const float* temperatures, int sample, int B, int K, int V,
                         int32_t* out_tokens, int32_t* out_num_accepted, float* out_p_draft,
                         void* workspace, size_t workspace_bytes, int32_t* device_error,
-                        void* stream, bool launch) {
+                        void* stream, bool launch, bool early_exit) {
   sv_status st = check_verify_shape(B, K, V);
   if (st != SV_OK) return st;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
@@ -199,6 +199,7 @@ sv_status verify_common(const void* logits, int dtype, const float* draft_probs,
   L.out_p_draft = sample ? out_p_draft : nullptr;
   L.workspace = workspace;
   L.device_error = device_error;
+  L.early_exit = early_exit ? 1 : 0;
   return sv::launch_verify(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -333,6 +334,44 @@ SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
                            temperatures, 2, B, K, V, out_tokens, out_num_accepted,
                            out_draft_target_prob, workspace, workspace_bytes, device_error, stream,
                            true);
+}
+
+SV_API sv_status spec_verify_greedy_early_exit(const void* target_logits, int logits_dtype,
+                                               const int32_t* draft_tokens, int B, int K, int V,
+                                               int32_t* out_tokens, int32_t* out_num_accepted,
+                                               void* workspace, size_t workspace_bytes,
+                                               int32_t* device_error, void* stream) {
+  return sv::verify_common(target_logits, logits_dtype, nullptr, draft_tokens, nullptr, 1.0f,
+                           nullptr, 0, B, K, V, out_tokens, out_num_accepted, nullptr, workspace,
+                           workspace_bytes, device_error, stream, true, true);
+}
+
+SV_API sv_status spec_verify_sample_early_exit(const void* target_logits, int logits_dtype,
+                                               const float* draft_probs,
+                                               const int32_t* draft_tokens, const float* uniforms,
+                                               float temperature, int B, int K, int V,
+                                               int32_t* out_tokens, int32_t* out_num_accepted,
+                                               float* out_draft_target_prob, void* workspace,
+                                               size_t workspace_bytes, int32_t* device_error,
+                                               void* stream) {
+  return sv::verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, uniforms,
+                           temperature, nullptr, 1, B, K, V, out_tokens, out_num_accepted,
+                           out_draft_target_prob, workspace, workspace_bytes, device_error, stream,
+                           true, true);
+}
+
+SV_API sv_status spec_verify_mixed_early_exit(const void* target_logits, int logits_dtype,
+                                              const float* draft_probs,
+                                              const int32_t* draft_tokens, const float* uniforms,
+                                              const float* temperatures, int B, int K, int V,
+                                              int32_t* out_tokens, int32_t* out_num_accepted,
+                                              float* out_draft_target_prob, void* workspace,
+                                              size_t workspace_bytes, int32_t* device_error,
+                                              void* stream) {
+  return sv::verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, uniforms, 1.0f,
+                           temperatures, 2, B, K, V, out_tokens, out_num_accepted,
+                           out_draft_target_prob, workspace, workspace_bytes, device_error, stream,
+                           true, true);
 }
 
 SV_API sv_status peagle_build_draft_batch(const int32_t* verify_out_tokens,

@@ -31,6 +31,9 @@ struct VerifyLaunch {
   float* out_p_draft;            // may be NULL
   void* workspace;
   int32_t* device_error;         // may be NULL
+  // statistics only of the rows up to the first rejection, one launch per
+  // draft position (spec_verify_*_early_exit)
+  int early_exit = 0;
 };
 
 struct BuildLaunch {
@@ -108,14 +111,14 @@ void trace_before(hipStream_t stream, int kernel_id);
 void trace_after(hipStream_t stream, int kernel_id);
 size_t verify_workspace_bytes(int B, int K, int V);
 // Argument checks and launches of spec_verify_greedy / _sample / _mixed
-// (sample: 0, 1, 2); launch = false checks every argument but the workspace
-// and enqueues nothing.
+// (sample: 0, 1, 2) and their _early_exit forms; launch = false checks every
+// argument but the workspace and enqueues nothing.
 sv_status verify_common(const void* logits, int dtype, const float* draft_probs,
                         const int32_t* draft_tokens, const float* uniforms, float temperature,
                         const float* temperatures, int sample, int B, int K, int V,
                         int32_t* out_tokens, int32_t* out_num_accepted, float* out_p_draft,
                         void* workspace, size_t workspace_bytes, int32_t* device_error,
-                        void* stream, bool launch);
+                        void* stream, bool launch, bool early_exit = false);
 hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream);
 hipError_t launch_build(const BuildLaunch& L, hipStream_t stream);
 hipError_t launch_draft(const DraftLaunch& L, hipStream_t stream);

@@ -137,6 +137,7 @@ struct ScanArgs {          // what an accept scan reads and writes
   int32_t* out_num_accepted;
   float* out_p_draft;
   int32_t* device_error;
+  int prefix_only;         // early exit: rows past the first rejection hold no statistics
 };
 
 struct DrawArgs {
@@ -257,7 +258,8 @@ __device__ __forceinline__ ScanResult accept_scan(const ScanArgs& A, int b, bool
   if (write) {
     if (k <= K && k != r.a) A.out_tokens[(long)b * (K + 1) + k] = k < r.a ? d : -1;
     if (k == 0) A.out_num_accepted[b] = r.a;
-    if (k < K && A.out_p_draft) A.out_p_draft[(long)b * K + k] = pdraft;
+    if (k < K && A.out_p_draft)
+      A.out_p_draft[(long)b * K + k] = A.prefix_only && k > r.a ? 0.f : pdraft;
   }
   return r;
 }
@@ -305,6 +307,60 @@ __device__ __forceinline__ ScanResult draw_scan(const ScanArgs& A, int b, bool w
   }
   if (handoff && lane_id() == 0) A.info[b] = r;              // read by verify_locate
   return r;
+}
+
+// ----------------------------------------------------------------------------
+// Early exit: the statistics of rows k0 .. k1-1 of every sequence whose
+// drafts 0..k0-1 were all accepted.  A draft is tested only if every earlier
+// one was accepted (speculative sampling's acceptance is sequential: Project
+// 14, 架构), so the rows past a sequence's first rejection never enter its
+// outputs.  The launches cover the draft positions in ranges [0,1), [1,2),
+// [2,4), [4,8), ...: one launch per position would make every deep position
+// cost a full row pass by a single workgroup (~21 us at V = 151936), while a
+// range reads, for the few sequences still undecided, some rows that turn
+// out not to be needed.  Wave 0 of each workgroup first runs the sequence's
+// accept scan over the statistics written by the earlier launches, with the
+// arithmetic of the final scan, so both take the same decisions: rows are
+// computed iff the scan's first rejection lies at or past k0 (rows from k0
+// on hold no statistics yet, or are being written by this launch, and sit
+// at or past k0, so their lanes cannot move a first rejection that lies
+// before it).  Grid: B * (k1 - k0) * S workgroups.
+template <typename LT, int MODE, bool VEC, bool QL>
+__global__ __launch_bounds__(kThreads) void verify_rows_level(RowsArgs A, ScanArgs sc, int k0,
+                                                              int k1) {
+  __shared__ float sm_f[kWaves];
+  __shared__ int sm_i[kWaves];
+  __shared__ double sm_d[kWaves];
+  __shared__ int s_go;
+
+  const int S = A.S;
+  const long V = A.V;
+  const int n = k1 - k0;
+  const int b = blockIdx.x / (n * S);
+  const int k = k0 + (int)(blockIdx.x / S % n), s = blockIdx.x % S;
+  if (k0 > 0) {
+    if (threadIdx.x < kWave) {
+      int a;
+      if constexpr (MODE == GREEDY) a = accept_scan<LT, GREEDY>(sc, b, false, 1.f).a;
+      else a = draw_scan<LT, MODE, QL>(sc, b, false, false).a;
+      if (threadIdx.x == 0) s_go = a >= k0;
+    }
+    __syncthreads();
+    if (!s_go) return;
+  }
+  const long rowi = (long)b * (A.K + 1) + k;
+  const LT* row = static_cast<const LT*>(A.logits) + rowi * V;
+  const long o_lo = (long)s * A.octets / S, o_hi = (long)(s + 1) * A.octets / S;
+  Partial P;
+  if constexpr (MODE == MIXED) {
+    bool bad;
+    const float c = seq_scale(A.temperatures[b], bad);
+    if (c == 0.f) P = slice_stats<LT, GREEDY, VEC, kThreads>(row, o_lo, o_hi, V, 1.f, sm_f, sm_i, sm_d);
+    else P = slice_stats<LT, SAMPLE, VEC, kThreads>(row, o_lo, o_hi, V, c, sm_f, sm_i, sm_d);
+  } else {
+    P = slice_stats<LT, MODE, VEC, kThreads>(row, o_lo, o_hi, V, A.c, sm_f, sm_i, sm_d);
+  }
+  if (threadIdx.x == 0) A.partials[rowi * S + s] = P;   // read by the next launches
 }
 
 // ----------------------------------------------------------------------------
@@ -729,24 +785,6 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   R.K = L.K; R.V = L.V; R.S = lay.S;
   R.octets = (L.V + 7) / 8;
   R.partials = partials;
-  const dim3 grid1((unsigned)((long)L.B * (L.K + 1) * lay.S));
-  trace_before(stream, rows_id);
-#define SV_ROWS(LT, MODE) \
-  do { \
-    if (L.vec) hipLaunchKernelGGL((verify_rows<LT, MODE, true>), grid1, block, 0, stream, R); \
-    else hipLaunchKernelGGL((verify_rows<LT, MODE, false>), grid1, block, 0, stream, R); \
-  } while (0)
-#define SV_BY_MODE(M, LT) \
-  do { \
-    if (mode == MIXED) M(LT, MIXED); \
-    else if (mode == SAMPLE) M(LT, SAMPLE); \
-    else M(LT, GREEDY); \
-  } while (0)
-  if (L.bf16) SV_BY_MODE(SV_ROWS, uint16_t);
-  else SV_BY_MODE(SV_ROWS, float);
-  hipError_t err = hipGetLastError();
-  trace_after(stream, rows_id);
-  if (err != hipSuccess) return err;
 
   const bool ql = L.dlogits != nullptr;       // q from the drafter logits (sampling)
   ScanArgs sc;
@@ -767,9 +805,57 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   sc.out_p_draft = L.out_p_draft;
   sc.device_error = L.device_error;
   sc.info = reinterpret_cast<ScanResult*>(ws + lay.info);
-  const dim3 grid_acc((unsigned)((L.B + kWaves - 1) / kWaves));
-#undef SV_BY_MODE
+  sc.prefix_only = L.early_exit;
+
+#define SV_BY_MODE(M, LT) \
+  do { \
+    if (mode == MIXED) M(LT, MIXED); \
+    else if (mode == SAMPLE) M(LT, SAMPLE); \
+    else M(LT, GREEDY); \
+  } while (0)
+  hipError_t err = hipSuccess;
+  if (L.early_exit) {
+    // draft positions [0,1), [1,2), [2,4), [4,8), ...; each launch skips the
+    // sequences already decided
+#define SV_LEVEL(LT, MODE) \
+  do { \
+    if (MODE != GREEDY && ql) { \
+      if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, true>), gridl, block, 0, stream, R, sc, k0, k1); \
+      else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, true>), gridl, block, 0, stream, R, sc, k0, k1); \
+    } else { \
+      if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, false>), gridl, block, 0, stream, R, sc, k0, k1); \
+      else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, false>), gridl, block, 0, stream, R, sc, k0, k1); \
+    } \
+  } while (0)
+    for (int k0 = 0; k0 <= L.K && err == hipSuccess;) {
+      const int k1 = k0 == 0 ? 1 : (2 * k0 < L.K + 1 ? 2 * k0 : L.K + 1);
+      const dim3 gridl((unsigned)((long)L.B * (k1 - k0) * lay.S));
+      trace_before(stream, rows_id);
+      if (L.bf16) SV_BY_MODE(SV_LEVEL, uint16_t);
+      else SV_BY_MODE(SV_LEVEL, float);
+      err = hipGetLastError();
+      trace_after(stream, rows_id);
+      k0 = k1;
+    }
+#undef SV_LEVEL
+  } else {
+    const dim3 grid1((unsigned)((long)L.B * (L.K + 1) * lay.S));
+    trace_before(stream, rows_id);
+#define SV_ROWS(LT, MODE) \
+  do { \
+    if (L.vec) hipLaunchKernelGGL((verify_rows<LT, MODE, true>), grid1, block, 0, stream, R); \
+    else hipLaunchKernelGGL((verify_rows<LT, MODE, false>), grid1, block, 0, stream, R); \
+  } while (0)
+    if (L.bf16) SV_BY_MODE(SV_ROWS, uint16_t);
+    else SV_BY_MODE(SV_ROWS, float);
 #undef SV_ROWS
+    err = hipGetLastError();
+    trace_after(stream, rows_id);
+  }
+#undef SV_BY_MODE
+  if (err != hipSuccess) return err;
+
+  const dim3 grid_acc((unsigned)((L.B + kWaves - 1) / kWaves));
   if (mode == GREEDY) {
     trace_before(stream, SV_KERNEL_VERIFY_GREEDY_ACCEPT);
     if (L.bf16) hipLaunchKernelGGL((verify_accept<uint16_t>), grid_acc, block, 0, stream, sc);

@@ -276,6 +276,47 @@ SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
                                    int32_t* device_error, void* stream);
 
 /*
+ * Early-exit forms of spec_verify_greedy, spec_verify_sample and
+ * spec_verify_mixed.  Drafts are tested in order and the first rejection
+ * ends a sequence's round ("Project 14", section 架构: the verified prefix
+ * is kept and the rest resampled), so the target rows past it never enter
+ * the sequence's outputs.  These forms compute row statistics over the
+ * draft positions in ranges [0,1), [1,2), [2,4), [4,8), ... (one launch
+ * each), a range only for the sequences whose drafts before it were all
+ * accepted, then run the usual accept scan and draw: a sequence that
+ * accepts a drafts has at most 2a+1 of its K+1 logit rows read (all of them
+ * only when a range reaches past its first rejection), at the cost of about
+ * log2(K+1) more launches.  Arguments, validation, workspace and device
+ * flags are those of the corresponding call; out_tokens and
+ * out_num_accepted are identical to its outputs bit for bit (the row
+ * statistics are computed by the same arithmetic).  out_draft_target_prob
+ * [b][k] equals the full call's value for k <= num_accepted[b] and is 0
+ * past it.  The launches per call are the row-statistics kernels of the
+ * ranges, then the kernels that follow them in the full call.
+ */
+SV_API sv_status spec_verify_greedy_early_exit(const void* target_logits, int logits_dtype,
+                                               const int32_t* draft_tokens, int B, int K, int V,
+                                               int32_t* out_tokens, int32_t* out_num_accepted,
+                                               void* workspace, size_t workspace_bytes,
+                                               int32_t* device_error, void* stream);
+SV_API sv_status spec_verify_sample_early_exit(const void* target_logits, int logits_dtype,
+                                               const float* draft_probs,
+                                               const int32_t* draft_tokens, const float* uniforms,
+                                               float temperature, int B, int K, int V,
+                                               int32_t* out_tokens, int32_t* out_num_accepted,
+                                               float* out_draft_target_prob, void* workspace,
+                                               size_t workspace_bytes, int32_t* device_error,
+                                               void* stream);
+SV_API sv_status spec_verify_mixed_early_exit(const void* target_logits, int logits_dtype,
+                                              const float* draft_probs,
+                                              const int32_t* draft_tokens, const float* uniforms,
+                                              const float* temperatures, int B, int K, int V,
+                                              int32_t* out_tokens, int32_t* out_num_accepted,
+                                              float* out_draft_target_prob, void* workspace,
+                                              size_t workspace_bytes, int32_t* device_error,
+                                              void* stream);
+
+/*
  * A mixed serving batch (as spec_verify_mixed: per-sequence temperatures,
  * 0 = greedy) whose drafter distributions are handed over as drafter logits
  * plus row descriptors (as spec_verify_sample_lq).  Results equal those of

@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
               "sv_step_graph_create", "sv_step_graph_launch", "sv_step_graph_destroy",
               "spec_verify_tree", "spec_verify_sample_lq", "spec_verify_sample_noalloc",
               "spec_verify_tree_lq", "spec_verify_mixed_lq",
-              "spec_verify_noalloc_scratch_bytes"):
+              "spec_verify_noalloc_scratch_bytes", "spec_verify_greedy_early_exit",
+              "spec_verify_sample_early_exit", "spec_verify_mixed_early_exit"):
         assert n in names
 
 
@@ -459,3 +460,47 @@ def test_noalloc_validation(lib):
     assert lo >= 4096                     # far above the 1024-sequence serving batch
     assert noalloc(lib, B=hi, K=7, V=151936) == ESCRATCH
     assert lib.sv_status_string(ESCRATCH).startswith(b"call needs more scratch")
+
+
+def test_early_exit_validation(lib):
+    """The early-exit forms validate exactly as the full calls, before any
+    launch (every case here is an error or an empty batch)."""
+    def g(**kw):
+        a = dict(logits=FAKE, dtype=1, d=FAKE, B=2, K=3, V=64, out=FAKE, acc=FAKE, ws=FAKE,
+                 wsb=None, err=None)
+        a.update(kw)
+        wsb = a["wsb"] if a["wsb"] is not None else lib.spec_verify_workspace_bytes(
+            max(a["B"], 1), max(a["K"], 0), max(a["V"], 1))
+        return lib.spec_verify_greedy_early_exit(a["logits"], a["dtype"], a["d"], a["B"], a["K"],
+                                                 a["V"], a["out"], a["acc"], a["ws"], wsb,
+                                                 a["err"], None)
+
+    def s(fn, **kw):
+        a = dict(logits=FAKE, dtype=0, q=FAKE, d=FAKE, u=FAKE, T=1.0, temps=FAKE, B=2, K=3, V=64,
+                 out=FAKE, acc=FAKE, pd=None, ws=FAKE, wsb=None)
+        a.update(kw)
+        wsb = a["wsb"] if a["wsb"] is not None else lib.spec_verify_workspace_bytes(
+            max(a["B"], 1), max(a["K"], 0), max(a["V"], 1))
+        if fn == "sample":
+            return lib.spec_verify_sample_early_exit(a["logits"], a["dtype"], a["q"], a["d"],
+                                                     a["u"], a["T"], a["B"], a["K"], a["V"],
+                                                     a["out"], a["acc"], a["pd"], a["ws"], wsb,
+                                                     None, None)
+        return lib.spec_verify_mixed_early_exit(a["logits"], a["dtype"], a["q"], a["d"], a["u"],
+                                                a["temps"], a["B"], a["K"], a["V"], a["out"],
+                                                a["acc"], a["pd"], a["ws"], wsb, None, None)
+
+    assert g(B=-1) == ESHAPE and g(K=64) == ESHAPE and g(V=0) == ESHAPE
+    assert g(dtype=2) == EDTYPE
+    assert g(B=0, logits=None, d=None, out=None, acc=None, ws=None, wsb=0) == OK
+    assert g(logits=None) == ENULL and g(d=None) == ENULL and g(acc=None) == ENULL
+    assert g(ws=None) == EWS and g(wsb=16) == EWS
+    assert g(logits=FAKE + 1) == EALIGN and g(err=FAKE + 1) == EALIGN
+    for fn in ("sample", "mixed"):
+        assert s(fn, B=-1) == ESHAPE and s(fn, K=64) == ESHAPE
+        assert s(fn, dtype=5) == EDTYPE
+        assert s(fn, q=None) == ENULL and s(fn, u=None) == ENULL
+        assert s(fn, wsb=16) == EWS
+        assert s(fn, q=FAKE + 2) == EALIGN and s(fn, pd=FAKE + 1) == EALIGN
+    assert s("sample", T=0.0) == EVALUE and s("sample", T=float("nan")) == EVALUE
+    assert s("mixed", temps=None) == ENULL and s("mixed", temps=FAKE + 2) == EALIGN

@@ -1,0 +1,158 @@
+"""GPU: the early-exit verify forms (spec_verify_greedy_early_exit,
+spec_verify_sample_early_exit, spec_verify_mixed_early_exit).
+
+Each computes a sequence's row statistics only up to its first rejection,
+one launch per draft position.  Its tokens, accept counts and device flags
+must equal the full call's bit for bit, p_k(d_k) must equal the full call's
+for k <= a and be 0 past it, and the workspace must be left all zero.
+Covered: the tiny, mid and large-vocabulary workloads, a 48-sequence slice
+of the 1024-sequence batch, 300 sequences (one draw workgroup per
+sequence), the ragged shapes of the verify tests (K = 0 and 63, V = 1, V
+not a multiple of 8), every draft accepted, every sequence rejected at its
+first draft, invalid draft tokens, mixed batches with greedy sequences; and
+the oracle directly on the mid workload.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import DEV, check_sample_sequence, dev
+from tests.test_gpu_verify import RAGGED, _random_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _ws(sv, B, K, V):
+    return torch.zeros(max(1, sv.spec_verify_workspace_bytes(B, K, V)), dtype=torch.uint8,
+                       device=DEV)
+
+
+def _prefix_equal(full, ee):
+    """Tokens and counts equal; p_k(d_k) equal for k <= a and 0 past it."""
+    out, acc, pd = full
+    eo, ea, ep = ee
+    assert torch.equal(out, eo) and torch.equal(acc, ea)
+    K = pd.shape[1]
+    keep = torch.arange(K, device=DEV)[None, :] <= acc.long()[:, None]
+    want = torch.where(keep, pd, torch.zeros_like(pd))
+    assert torch.equal(want.view(torch.int32), ep.view(torch.int32))
+
+
+def _compare(sv, logits, dtype, q, d, u, T, temps=None):
+    """Greedy, sampled and (with temps) mixed calls, full and early exit."""
+    B, K1, V = logits.shape
+    K = K1 - 1
+    z, qd, dd, ud = dev(logits), dev(q), dev(d), dev(u)
+    errs = [torch.zeros(1, dtype=torch.int32, device=DEV) for _ in range(6)]
+    ws = [_ws(sv, B, K, V) for _ in range(6)]
+    g_full = sv.spec_verify_greedy(z, dd, workspace=ws[0], device_error=errs[0])
+    g_ee = sv.spec_verify_greedy_early_exit(z, dd, workspace=ws[1], device_error=errs[1])
+    s_full = sv.spec_verify_sample(z, qd, dd, ud, T, want_draft_target_prob=True,
+                                   workspace=ws[2], device_error=errs[2])
+    s_ee = sv.spec_verify_sample_early_exit(z, qd, dd, ud, T, want_draft_target_prob=True,
+                                            workspace=ws[3], device_error=errs[3])
+    if temps is not None:
+        tt = dev(temps)
+        m_full = sv.spec_verify_mixed(z, qd, dd, ud, tt, want_draft_target_prob=True,
+                                      workspace=ws[4], device_error=errs[4])
+        m_ee = sv.spec_verify_mixed_early_exit(z, qd, dd, ud, tt, want_draft_target_prob=True,
+                                               workspace=ws[5], device_error=errs[5])
+    torch.cuda.synchronize()
+    assert torch.equal(g_full[0], g_ee[0]) and torch.equal(g_full[1], g_ee[1])
+    _prefix_equal(s_full, s_ee)
+    if temps is not None:
+        _prefix_equal(m_full, m_ee)
+    n = 6 if temps is not None else 4
+    for i in range(0, n, 2):
+        assert int(errs[i].item()) == int(errs[i + 1].item()), i
+    for w in ws[:n]:
+        assert int(w.count_nonzero().item()) == 0
+    return g_ee, s_ee
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_workloads(gpu, cfg):
+    vi = synth.make_verify_inputs(synth.verify_config(cfg))
+    temps = synth.make_temperatures(vi.spec.B, 40 + cfg)
+    _compare(gpu, vi.logits, vi.spec.dtype, vi.draft_probs, vi.draft_tokens, vi.uniforms,
+             vi.temperature, temps)
+
+
+def test_large_batch_slice(gpu):
+    vi = synth.make_verify_inputs(synth.verify_config(5), seqs=range(48))
+    _, (out, acc, _) = _compare(gpu, vi.logits, vi.spec.dtype, vi.draft_probs, vi.draft_tokens,
+                                vi.uniforms, vi.temperature, synth.make_temperatures(48, 45))
+    assert 0 < int(acc.sum().item()) < 48 * vi.spec.K
+
+
+def test_one_draw_workgroup_per_sequence(gpu):
+    rng = np.random.default_rng(301)
+    logits, q, d, u = _random_case(rng, 300, 4, 40000, "bf16", T=0.8)
+    _compare(gpu, logits, "bf16", q, d, u, 0.8, synth.make_temperatures(300, 46))
+
+
+@pytest.mark.parametrize("dtype,B,K,V", RAGGED)
+def test_ragged_shapes(gpu, dtype, B, K, V):
+    rng = np.random.default_rng(B * 1000 + K * 10 + V + 5)
+    logits, q, d, u = _random_case(rng, B, K, V, dtype, T=0.8, tie_heavy=True)
+    _compare(gpu, logits, dtype, q, d, u, 0.8, synth.make_temperatures(B, 47))
+
+
+def test_all_accepted_and_first_rejected(gpu):
+    rng = np.random.default_rng(302)
+    B, K, V = 12, 7, 5000
+    logits, q, d, u = _random_case(rng, B, K, V, "f32", T=1.0)
+    z = logits[:, :K]
+    top = np.argmax(z, axis=2).astype(np.int32)          # unique maxima for N(0, 2.5^2) logits
+    # every draft is the row's argmax with q = one-hot and u = 0: accepted by
+    # the greedy rule and by rejection sampling (u < p / q since p > 0)
+    q1 = np.zeros_like(q)
+    np.put_along_axis(q1, top[:, :, None], 1.0, axis=2)
+    u0 = u.copy()
+    u0[:, :K] = 0.0
+    (go, ga), (so, sa, _) = _compare(gpu, logits, "f32", q1, top, u0, 1.0)
+    assert ga.cpu().tolist() == [K] * B and sa.cpu().tolist() == [K] * B
+    # the first draft never the argmax, with q = one-hot on it and u just
+    # below 1: rejected at once by both rules (p / q < 1 there)
+    d1 = top.copy()
+    d1[:, 0] = (top[:, 0] + 1) % V
+    q2 = q1.copy()
+    q2[:, 0] = 0.0
+    q2[np.arange(B), 0, d1[:, 0]] = 1.0
+    u1 = u0.copy()
+    u1[:, 0] = np.float32(1.0) - np.float32(2.0 ** -24)
+    (go, ga), (so, sa, _) = _compare(gpu, logits, "f32", q2, d1, u1, 1.0)
+    assert ga.cpu().tolist() == [0] * B and sa.cpu().tolist() == [0] * B
+
+
+def test_invalid_draft_tokens(gpu):
+    rng = np.random.default_rng(303)
+    logits, q, d, u = _random_case(rng, 6, 5, 3000, "bf16", T=0.9)
+    d[1, 0] = -3                       # rejected at the first draft, flagged
+    d[2, 3] = 3000                     # past the vocabulary
+    d[4, 4] = 1 << 30
+    _compare(gpu, logits, "bf16", q, d, u, 0.9, synth.make_temperatures(6, 48))
+
+
+def test_sample_matches_oracle(gpu):
+    """The sampled early-exit call against the oracle on the mid workload:
+    outcomes within the 1e-6 near-tie rule, p_k(d_k) for k <= a."""
+    vi = synth.make_verify_inputs(synth.verify_config(2))
+    out, acc, pd = gpu.spec_verify_sample_early_exit(dev(vi.logits), dev(vi.draft_probs),
+                                                     dev(vi.draft_tokens), dev(vi.uniforms),
+                                                     vi.temperature, want_draft_target_prob=True)
+    torch.cuda.synchronize()
+    out, acc, pd = out.cpu().numpy(), acc.cpu().numpy(), pd.cpu().numpy()
+    for b in range(vi.spec.B):
+        z64 = oracle.decode_logits(vi.logits[b], vi.spec.dtype)
+        check_sample_sequence(z64, vi.draft_probs[b], vi.draft_tokens[b], vi.uniforms[b],
+                              vi.temperature, out[b], acc[b])
+        a = int(acc[b])
+        for k in range(vi.spec.K):
+            want = oracle.target_distribution(z64[k], vi.temperature)[int(vi.draft_tokens[b, k])]
+            if k <= a:
+                assert np.isclose(pd[b, k], want, rtol=1e-5, atol=1e-30), (b, k)
+            else:
+                assert pd[b, k] == 0.0
