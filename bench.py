@@ -686,7 +686,8 @@ def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, o
     away (same recipe, distinct memory), gathered through a row index.  The
     same pair is also timed on a mixed serving batch (per-sequence
     temperatures, each sequence's drafter rows sampled at its own
-    temperature): spec_verify_mixed vs spec_verify_mixed_lq."""
+    temperature): spec_verify_mixed vs spec_verify_mixed_lq.  One more
+    round pairs the drafter-logit interface with the early-exit verify."""
     dev = z.device
     zr = z.view(B * (K + 1), V)
     seq = (torch.arange(B, dtype=torch.int32, device=dev) + B // 2) % B
@@ -715,6 +716,14 @@ def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, o
                                  out_num_accepted=acc_t, out_draft_target_prob=pd_t, workspace=ws)
         build()
 
+    def lq_ee():
+        sv.spec_draft_sample(zr, K, T, uniforms=ud, row_index=rows, out_draft_tokens=tok,
+                             want_draft_probs=False, out_row_desc=desc)
+        sv.spec_verify_sample_lq_early_exit(z, zr, desc, tok, u, T, drafter_rows=rows,
+                                            out_tokens=out_t, out_num_accepted=acc_t,
+                                            out_draft_target_prob=pd_t, workspace=ws)
+        build()
+
     def dense_mixed():
         sv.spec_draft_sample(zr, K, T, uniforms=ud, row_index=rows, temperatures=temps,
                              out_draft_tokens=tok, out_draft_probs=q)
@@ -731,8 +740,8 @@ def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, o
 
     res = {"workload": f"B={B} K={K} V={V} bf16: drafter sampling + sampled verify + P-EAGLE build"}
     outs = {}
-    for name, fn in (("dense_q", dense), ("logit_q", lq), ("mixed_dense_q", dense_mixed),
-                     ("mixed_logit_q", lq_mixed)):
+    for name, fn in (("dense_q", dense), ("logit_q", lq), ("logit_q_early_exit", lq_ee),
+                     ("mixed_dense_q", dense_mixed), ("mixed_logit_q", lq_mixed)):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
@@ -746,6 +755,9 @@ def round_bench(sv, torch, np, args, B, K, V, vi, bi, z, d, u, L, bt, hid, hs, o
     res["speedup"] = res["dense_q_ms_per_round"] / res["logit_q_ms_per_round"]
     res["identical_outputs"] = bool(torch.equal(outs["dense_q"][0], outs["logit_q"][0]) and
                                     torch.equal(outs["dense_q"][1], outs["logit_q"][1]))
+    res["early_exit_identical_outputs"] = bool(
+        torch.equal(outs["dense_q"][0], outs["logit_q_early_exit"][0]) and
+        torch.equal(outs["dense_q"][1], outs["logit_q_early_exit"][1]))
     res["mixed_speedup"] = res["mixed_dense_q_ms_per_round"] / res["mixed_logit_q_ms_per_round"]
     res["mixed_identical_outputs"] = bool(
         torch.equal(outs["mixed_dense_q"][0], outs["mixed_logit_q"][0]) and

@@ -38,6 +38,7 @@ __all__ = [
     "spec_verify_mixed", "spec_verify_sample_lq", "spec_verify_mixed_lq",
     "spec_verify_sample_noalloc", "spec_verify_greedy_early_exit",
     "spec_verify_sample_early_exit", "spec_verify_mixed_early_exit",
+    "spec_verify_sample_lq_early_exit", "spec_verify_mixed_lq_early_exit",
     "noalloc_scratch_bytes", "spec_verify_tree", "spec_verify_tree_lq", "spec_draft_sample",
     "spec_accept_metrics", "accept_metrics_buffer", "acceptance_summary", "StepGraph",
     "trace_begin", "trace_read", "trace_end",
@@ -82,6 +83,12 @@ _SIGS = {
                                    _i, _i, _i, _p, _p, _p, _p, ctypes.c_size_t, _p, _p]),
     "spec_verify_mixed_lq": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, _p,
                                   _i, _i, _i, _p, _p, _p, _p, ctypes.c_size_t, _p, _p]),
+    "spec_verify_sample_lq_early_exit": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p,
+                                              ctypes.c_float, _i, _i, _i, _p, _p, _p, _p,
+                                              ctypes.c_size_t, _p, _p]),
+    "spec_verify_mixed_lq_early_exit": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, _p,
+                                             _i, _i, _i, _p, _p, _p, _p, ctypes.c_size_t, _p,
+                                             _p]),
     "spec_verify_tree": (_i, [_p, _i, _p, _p, _p, _p, ctypes.c_float, _i, _i, _i, _p, _p, _p, _p,
                               ctypes.c_size_t, _p, _p]),
     "spec_verify_tree_lq": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, _p, ctypes.c_float,
@@ -597,10 +604,10 @@ def _verify_lq(name, target_logits, drafter_logits, drafter_desc, draft_tokens, 
     tail = (B, K, V, _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_draft_target_prob),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(device_error),
             _stream(dev))
-    if name == "spec_verify_mixed_lq":
-        st = lib.spec_verify_mixed_lq(*head, _ptr(temperatures), *tail)
+    if name.startswith("spec_verify_mixed_lq"):
+        st = getattr(lib, name)(*head, _ptr(temperatures), *tail)
     else:
-        st = lib.spec_verify_sample_lq(*head, float(temperature), *tail)
+        st = getattr(lib, name)(*head, float(temperature), *tail)
     _check(st, name)
     return out_tokens, out_num_accepted, out_draft_target_prob
 
@@ -643,6 +650,34 @@ def spec_verify_mixed_lq(target_logits: torch.Tensor, drafter_logits: torch.Tens
                       draft_tokens, uniforms, None, temperatures, drafter_rows, out_tokens,
                       out_num_accepted, out_draft_target_prob, want_draft_target_prob,
                       workspace, device_error)
+
+
+def spec_verify_sample_lq_early_exit(target_logits, drafter_logits, drafter_desc, draft_tokens,
+                                     uniforms, temperature, drafter_rows=None, out_tokens=None,
+                                     out_num_accepted=None, out_draft_target_prob=None,
+                                     want_draft_target_prob=False, workspace=None,
+                                     device_error=None):
+    """spec_verify_sample_lq computing only the rows up to each sequence's
+    first rejection; see spec_verify_sample_lq_early_exit in
+    include/spec_verify.h.  draft_target_prob is 0 past num_accepted."""
+    return _verify_lq("spec_verify_sample_lq_early_exit", target_logits, drafter_logits,
+                      drafter_desc, draft_tokens, uniforms, temperature, None, drafter_rows,
+                      out_tokens, out_num_accepted, out_draft_target_prob,
+                      want_draft_target_prob, workspace, device_error)
+
+
+def spec_verify_mixed_lq_early_exit(target_logits, drafter_logits, drafter_desc, draft_tokens,
+                                    uniforms, temperatures, drafter_rows=None, out_tokens=None,
+                                    out_num_accepted=None, out_draft_target_prob=None,
+                                    want_draft_target_prob=False, workspace=None,
+                                    device_error=None):
+    """spec_verify_mixed_lq computing only the rows up to each sequence's
+    first rejection; see spec_verify_mixed_lq_early_exit in
+    include/spec_verify.h.  draft_target_prob is 0 past num_accepted."""
+    return _verify_lq("spec_verify_mixed_lq_early_exit", target_logits, drafter_logits,
+                      drafter_desc, draft_tokens, uniforms, None, temperatures, drafter_rows,
+                      out_tokens, out_num_accepted, out_draft_target_prob,
+                      want_draft_target_prob, workspace, device_error)
 
 
 # ---------------------------------------------------------------- draft trees
@@ -815,7 +850,7 @@ class _StepDesc(ctypes.Structure):
                 ("out_slot_mapping", _p), ("out_hidden", _p), ("out_sample_rows", _p),
                 ("metrics", _p), ("device_error", _p),
                 ("drafter_logits", _p), ("n_drafter_rows", ctypes.c_int64),
-                ("drafter_rows", _p), ("drafter_desc", _p)]
+                ("drafter_rows", _p), ("drafter_desc", _p), ("early_exit", ctypes.c_int)]
 
 
 class StepGraph:
@@ -836,11 +871,12 @@ class StepGraph:
       target_hidden, h_shared, mask_token_id and outputs (as returned by
       peagle_build_draft_batch or preallocated).
     metrics: None, or a counter array from accept_metrics_buffer.
+    early_exit: capture the _early_exit form of the verify.
     """
 
     def __init__(self, mode: str, verify: dict, build: Optional[dict] = None,
                  metrics: Optional[torch.Tensor] = None,
-                 device_error: Optional[torch.Tensor] = None):
+                 device_error: Optional[torch.Tensor] = None, early_exit: bool = False):
         lib = require_library()
         z = verify["target_logits"]
         if z.dim() != 3:
@@ -850,6 +886,7 @@ class StepGraph:
         dev = z.device
         d = _StepDesc()
         d.mode = {"greedy": STEP_GREEDY, "sample": STEP_SAMPLE, "mixed": STEP_MIXED}[mode]
+        d.early_exit = 1 if early_exit else 0
         keep = [z]
 
         def ptr(t, name, dtype=None, shape=None):

@@ -204,14 +204,15 @@ sv_status verify_common(const void* logits, int dtype, const float* draft_probs,
 }
 
 // spec_verify_sample_lq (temperatures null: the scalar temperature) and
-// spec_verify_mixed_lq (per-sequence temperatures).
+// spec_verify_mixed_lq (per-sequence temperatures), and their _early_exit
+// forms.
 sv_status verify_lq(const void* target_logits, int logits_dtype, const void* drafter_logits,
                     int64_t n_drafter_rows, const int32_t* drafter_rows,
                     const sv_draft_row* drafter_desc, const int32_t* draft_tokens,
                     const float* uniforms, float temperature, const float* temperatures, int B,
                     int K, int V, int32_t* out_tokens, int32_t* out_num_accepted,
                     float* out_draft_target_prob, void* workspace, size_t workspace_bytes,
-                    int32_t* device_error, void* stream) {
+                    int32_t* device_error, void* stream, bool early_exit) {
   sv_status st = check_verify_shape(B, K, V);
   if (st != SV_OK) return st;
   if (n_drafter_rows < 0 || n_drafter_rows > 0x7fffffffL) return SV_ERR_SHAPE;
@@ -260,6 +261,7 @@ sv_status verify_lq(const void* target_logits, int logits_dtype, const void* dra
   L.out_p_draft = out_draft_target_prob;
   L.workspace = workspace;
   L.device_error = device_error;
+  L.early_exit = early_exit ? 1 : 0;
   return launch_verify(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -301,9 +303,8 @@ SV_API sv_status spec_verify_sample_lq(const void* target_logits, int logits_dty
                                        void* stream) {
   return sv::verify_lq(target_logits, logits_dtype, drafter_logits, n_drafter_rows,
                        drafter_rows, drafter_desc, draft_tokens, uniforms, temperature, nullptr,
-                       B, K, V,
-                   out_tokens, out_num_accepted, out_draft_target_prob, workspace,
-                   workspace_bytes, device_error, stream);
+                       B, K, V, out_tokens, out_num_accepted, out_draft_target_prob,
+                       workspace, workspace_bytes, device_error, stream, false);
 }
 
 SV_API sv_status spec_verify_mixed_lq(const void* target_logits, int logits_dtype,
@@ -321,7 +322,32 @@ SV_API sv_status spec_verify_mixed_lq(const void* target_logits, int logits_dtyp
   return sv::verify_lq(target_logits, logits_dtype, drafter_logits, n_drafter_rows,
                        drafter_rows, drafter_desc, draft_tokens, uniforms, 1.0f, temperatures,
                        B, K, V, out_tokens, out_num_accepted, out_draft_target_prob, workspace,
-                       workspace_bytes, device_error, stream);
+                       workspace_bytes, device_error, stream, false);
+}
+
+SV_API sv_status spec_verify_sample_lq_early_exit(
+    const void* target_logits, int logits_dtype, const void* drafter_logits,
+    int64_t n_drafter_rows, const int32_t* drafter_rows, const sv_draft_row* drafter_desc,
+    const int32_t* draft_tokens, const float* uniforms, float temperature, int B, int K, int V,
+    int32_t* out_tokens, int32_t* out_num_accepted, float* out_draft_target_prob,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream) {
+  return sv::verify_lq(target_logits, logits_dtype, drafter_logits, n_drafter_rows,
+                       drafter_rows, drafter_desc, draft_tokens, uniforms, temperature, nullptr,
+                       B, K, V, out_tokens, out_num_accepted, out_draft_target_prob, workspace,
+                       workspace_bytes, device_error, stream, true);
+}
+
+SV_API sv_status spec_verify_mixed_lq_early_exit(
+    const void* target_logits, int logits_dtype, const void* drafter_logits,
+    int64_t n_drafter_rows, const int32_t* drafter_rows, const sv_draft_row* drafter_desc,
+    const int32_t* draft_tokens, const float* uniforms, const float* temperatures, int B, int K,
+    int V, int32_t* out_tokens, int32_t* out_num_accepted, float* out_draft_target_prob,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream) {
+  if (B > 0 && !temperatures) return SV_ERR_NULL;
+  return sv::verify_lq(target_logits, logits_dtype, drafter_logits, n_drafter_rows,
+                       drafter_rows, drafter_desc, draft_tokens, uniforms, 1.0f, temperatures,
+                       B, K, V, out_tokens, out_num_accepted, out_draft_target_prob, workspace,
+                       workspace_bytes, device_error, stream, true);
 }
 
 SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
@@ -599,37 +625,39 @@ struct sv_step_graph {
 
 namespace {
 
-// The step's verify call, on the dense q or on the drafter logits (each call
-// validates its own arguments).
+// The step's verify call, on the dense q or on the drafter logits, full or
+// early exit (each call validates its own arguments).
 sv_status enqueue_verify(const sv_step_desc* d, hipStream_t s) {
+  const bool ee = d->early_exit != 0;
   if (d->drafter_logits) {
-    if (d->mode == SV_STEP_SAMPLE)
-      return spec_verify_sample_lq(d->target_logits, d->logits_dtype, d->drafter_logits,
-                                   d->n_drafter_rows, d->drafter_rows, d->drafter_desc,
-                                   d->draft_tokens, d->uniforms, d->temperature, d->B, d->K, d->V,
-                                   d->out_tokens, d->out_num_accepted, d->out_draft_target_prob,
-                                   d->workspace, d->workspace_bytes, d->device_error, s);
-    return spec_verify_mixed_lq(d->target_logits, d->logits_dtype, d->drafter_logits,
-                                d->n_drafter_rows, d->drafter_rows, d->drafter_desc,
-                                d->draft_tokens, d->uniforms, d->temperatures, d->B, d->K, d->V,
-                                d->out_tokens, d->out_num_accepted, d->out_draft_target_prob,
-                                d->workspace, d->workspace_bytes, d->device_error, s);
+    auto* lq = d->mode == SV_STEP_SAMPLE
+        ? (ee ? spec_verify_sample_lq_early_exit : spec_verify_sample_lq) : nullptr;
+    if (lq)
+      return lq(d->target_logits, d->logits_dtype, d->drafter_logits, d->n_drafter_rows,
+                d->drafter_rows, d->drafter_desc, d->draft_tokens, d->uniforms, d->temperature,
+                d->B, d->K, d->V, d->out_tokens, d->out_num_accepted, d->out_draft_target_prob,
+                d->workspace, d->workspace_bytes, d->device_error, s);
+    auto* mlq = ee ? spec_verify_mixed_lq_early_exit : spec_verify_mixed_lq;
+    return mlq(d->target_logits, d->logits_dtype, d->drafter_logits, d->n_drafter_rows,
+               d->drafter_rows, d->drafter_desc, d->draft_tokens, d->uniforms, d->temperatures,
+               d->B, d->K, d->V, d->out_tokens, d->out_num_accepted, d->out_draft_target_prob,
+               d->workspace, d->workspace_bytes, d->device_error, s);
   }
   switch (d->mode) {
     case SV_STEP_GREEDY:
-      return spec_verify_greedy(d->target_logits, d->logits_dtype, d->draft_tokens, d->B, d->K,
-                                d->V, d->out_tokens, d->out_num_accepted, d->workspace,
-                                d->workspace_bytes, d->device_error, s);
+      return (ee ? spec_verify_greedy_early_exit : spec_verify_greedy)(
+          d->target_logits, d->logits_dtype, d->draft_tokens, d->B, d->K, d->V, d->out_tokens,
+          d->out_num_accepted, d->workspace, d->workspace_bytes, d->device_error, s);
     case SV_STEP_SAMPLE:
-      return spec_verify_sample(d->target_logits, d->logits_dtype, d->draft_probs,
-                                d->draft_tokens, d->uniforms, d->temperature, d->B, d->K, d->V,
-                                d->out_tokens, d->out_num_accepted, d->out_draft_target_prob,
-                                d->workspace, d->workspace_bytes, d->device_error, s);
+      return (ee ? spec_verify_sample_early_exit : spec_verify_sample)(
+          d->target_logits, d->logits_dtype, d->draft_probs, d->draft_tokens, d->uniforms,
+          d->temperature, d->B, d->K, d->V, d->out_tokens, d->out_num_accepted,
+          d->out_draft_target_prob, d->workspace, d->workspace_bytes, d->device_error, s);
     default:
-      return spec_verify_mixed(d->target_logits, d->logits_dtype, d->draft_probs,
-                               d->draft_tokens, d->uniforms, d->temperatures, d->B, d->K, d->V,
-                               d->out_tokens, d->out_num_accepted, d->out_draft_target_prob,
-                               d->workspace, d->workspace_bytes, d->device_error, s);
+      return (ee ? spec_verify_mixed_early_exit : spec_verify_mixed)(
+          d->target_logits, d->logits_dtype, d->draft_probs, d->draft_tokens, d->uniforms,
+          d->temperatures, d->B, d->K, d->V, d->out_tokens, d->out_num_accepted,
+          d->out_draft_target_prob, d->workspace, d->workspace_bytes, d->device_error, s);
   }
 }
 

@@ -343,6 +343,26 @@ SV_API sv_status spec_verify_mixed_lq(const void* target_logits, int logits_dtyp
                                       int32_t* device_error, void* stream);
 
 /*
+ * Early-exit forms of spec_verify_sample_lq and spec_verify_mixed_lq: the
+ * row statistics only up to each sequence's first rejection, as
+ * spec_verify_sample_early_exit does for the dense q.  Arguments, validation
+ * and results as the corresponding call, out_draft_target_prob 0 past
+ * num_accepted[b].
+ */
+SV_API sv_status spec_verify_sample_lq_early_exit(
+    const void* target_logits, int logits_dtype, const void* drafter_logits,
+    int64_t n_drafter_rows, const int32_t* drafter_rows, const sv_draft_row* drafter_desc,
+    const int32_t* draft_tokens, const float* uniforms, float temperature, int B, int K, int V,
+    int32_t* out_tokens, int32_t* out_num_accepted, float* out_draft_target_prob,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
+SV_API sv_status spec_verify_mixed_lq_early_exit(
+    const void* target_logits, int logits_dtype, const void* drafter_logits,
+    int64_t n_drafter_rows, const int32_t* drafter_rows, const sv_draft_row* drafter_desc,
+    const int32_t* draft_tokens, const float* uniforms, const float* temperatures, int B, int K,
+    int V, int32_t* out_tokens, int32_t* out_num_accepted, float* out_draft_target_prob,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
+
+/*
  * Verification of a draft tree per sequence.  "Project 14", section 概念:
  * P-EAGLE's parallel speculation forms deeper draft trees (the pages give no
  * tree shape; any shape of up to SV_MAX_K nodes is accepted).  Node 0 is the
@@ -547,9 +567,10 @@ SV_API sv_status spec_accept_metrics(const int32_t* num_accepted, int B, int K, 
  * spec_verify_sample_lq or spec_verify_mixed_lq on drafter_logits,
  * n_drafter_rows, drafter_rows and drafter_desc, and draft_probs must be NULL
  * (SV_ERR_VALUE otherwise; SV_ERR_VALUE too for drafter_logits in greedy
- * mode).  Argument errors of the captured calls are returned by
- * sv_step_graph_create, which then creates nothing.  Kernel tracing is paused
- * during capture.
+ * mode).  early_exit != 0 captures the _early_exit form of the verify (row
+ * statistics only up to each sequence's first rejection).  Argument errors
+ * of the captured calls are returned by sv_step_graph_create, which then
+ * creates nothing.  Kernel tracing is paused during capture.
  */
 #define SV_STEP_GREEDY 0
 #define SV_STEP_SAMPLE 1
@@ -588,6 +609,7 @@ typedef struct sv_step_desc {
   int64_t n_drafter_rows;                 /* with drafter_logits                 */
   const int32_t* drafter_rows;            /* optional, with drafter_logits       */
   const sv_draft_row* drafter_desc;       /* with drafter_logits                 */
+  int early_exit;                         /* 0: full verify; else _early_exit    */
 } sv_step_desc;
 
 typedef struct sv_step_graph sv_step_graph;   /* opaque */

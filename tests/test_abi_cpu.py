@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
               "spec_verify_tree", "spec_verify_sample_lq", "spec_verify_sample_noalloc",
               "spec_verify_tree_lq", "spec_verify_mixed_lq",
               "spec_verify_noalloc_scratch_bytes", "spec_verify_greedy_early_exit",
-              "spec_verify_sample_early_exit", "spec_verify_mixed_early_exit"):
+              "spec_verify_sample_early_exit", "spec_verify_mixed_early_exit",
+              "spec_verify_sample_lq_early_exit", "spec_verify_mixed_lq_early_exit"):
         assert n in names
 
 
@@ -343,14 +344,22 @@ def test_tree_validation(lib):
 
 
 def lq(lib, logits=FAKE, dtype=1, dl=FAKE, n_rows=6, rows=None, desc=FAKE, d=FAKE, u=FAKE, T=0.7,
-       B=2, K=3, V=64, out=FAKE, acc=FAKE, pd=None, ws=FAKE, wsb=None):
+       B=2, K=3, V=64, out=FAKE, acc=FAKE, pd=None, ws=FAKE, wsb=None,
+       fn="spec_verify_sample_lq"):
     if wsb is None:
         wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(K, 0), max(V, 1))
-    return lib.spec_verify_sample_lq(logits, dtype, dl, n_rows, rows, desc, d, u, T, B, K, V, out,
-                                     acc, pd, ws, wsb, None, None)
+    return getattr(lib, fn)(logits, dtype, dl, n_rows, rows, desc, d, u, T, B, K, V, out, acc, pd,
+                            ws, wsb, None, None)
 
 
-def test_sample_lq_validation(lib):
+@pytest.mark.parametrize("fn", ["spec_verify_sample_lq", "spec_verify_sample_lq_early_exit"])
+def test_sample_lq_validation(lib, fn):
+    import functools
+    lq_ = functools.partial(lq, fn=fn)
+    _sample_lq_cases(lib, lq_)
+
+
+def _sample_lq_cases(lib, lq):
     assert lq(lib, K=64) == ESHAPE
     assert lq(lib, n_rows=5) == ESHAPE                 # fewer than B*K rows, no row index
     assert lq(lib, n_rows=-1, rows=FAKE) == ESHAPE
@@ -369,14 +378,21 @@ def test_sample_lq_validation(lib):
 
 
 def mixed_lq(lib, logits=FAKE, dtype=1, dl=FAKE, n_rows=6, rows=None, desc=FAKE, d=FAKE, u=FAKE,
-             temps=FAKE, B=2, K=3, V=64, out=FAKE, acc=FAKE, pd=None, ws=FAKE, wsb=None):
+             temps=FAKE, B=2, K=3, V=64, out=FAKE, acc=FAKE, pd=None, ws=FAKE, wsb=None,
+             fn="spec_verify_mixed_lq"):
     if wsb is None:
         wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(K, 0), max(V, 1))
-    return lib.spec_verify_mixed_lq(logits, dtype, dl, n_rows, rows, desc, d, u, temps, B, K, V,
-                                    out, acc, pd, ws, wsb, None, None)
+    return getattr(lib, fn)(logits, dtype, dl, n_rows, rows, desc, d, u, temps, B, K, V, out, acc,
+                            pd, ws, wsb, None, None)
 
 
-def test_mixed_lq_validation(lib):
+@pytest.mark.parametrize("fn", ["spec_verify_mixed_lq", "spec_verify_mixed_lq_early_exit"])
+def test_mixed_lq_validation(lib, fn):
+    import functools
+    _mixed_lq_cases(lib, functools.partial(mixed_lq, fn=fn))
+
+
+def _mixed_lq_cases(lib, mixed_lq):
     assert mixed_lq(lib, K=64) == ESHAPE
     assert mixed_lq(lib, n_rows=5) == ESHAPE             # fewer than B*K rows, no row index
     assert mixed_lq(lib, dtype=2) == EDTYPE

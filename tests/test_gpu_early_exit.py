@@ -156,3 +156,54 @@ def test_sample_matches_oracle(gpu):
                 assert np.isclose(pd[b, k], want, rtol=1e-5, atol=1e-30), (b, k)
             else:
                 assert pd[b, k] == 0.0
+
+
+@pytest.mark.parametrize("dtype,B,K,V", [("bf16", 40, 7, 151936), ("f32", 9, 5, 4099),
+                                         ("bf16", 300, 3, 40000)])
+def test_drafter_logit_forms(gpu, dtype, B, K, V):
+    """spec_verify_sample_lq_early_exit and spec_verify_mixed_lq_early_exit
+    against the full drafter-logit calls on the same drafting (drafter rows
+    gathered through a row index, one of them invalid at a sampled sequence's
+    first draft: the same flag)."""
+    rng = np.random.default_rng(B + K + V)
+    z = (3.0 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    z[:, :, :8] += 6.0
+    n = B * K
+    zd = np.concatenate([(z[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32))
+                         .reshape(n, V), np.zeros((2, V), np.float32)])
+    if dtype == "bf16":
+        z, zd = synth.f32_to_bf16_bits(z), synth.f32_to_bf16_bits(zd)
+    rows = rng.permutation(n).astype(np.int32).reshape(B, K)
+    ud = rng.random((B, K), dtype=np.float32)
+    uv = rng.random((B, K + 1), dtype=np.float32)
+    temps = synth.make_temperatures(B, 49)
+    zt, zdt, rt, uvt = dev(z), dev(zd), dev(rows), dev(uv)
+    for mixed in (False, True):
+        tok, _, desc = gpu.spec_draft_sample(zdt, K, 0.8, uniforms=dev(ud), row_index=rt,
+                                             temperatures=dev(temps) if mixed else None,
+                                             want_draft_probs=False, want_row_desc=True)
+        bad = rows.copy()
+        bb = int(np.argmax(temps > 0))                         # a sampled sequence
+        bad[bb, 0] = n + 7                                     # no such drafter row
+        badt = dev(bad)
+        errs = [torch.zeros(1, dtype=torch.int32, device=DEV) for _ in range(2)]
+        wss = [_ws(gpu, B, K, V) for _ in range(2)]
+        if mixed:
+            args = (zt, zdt, desc, tok, uvt, dev(temps))
+            full = gpu.spec_verify_mixed_lq(*args, drafter_rows=badt, want_draft_target_prob=True,
+                                            workspace=wss[0], device_error=errs[0])
+            ee = gpu.spec_verify_mixed_lq_early_exit(*args, drafter_rows=badt,
+                                                     want_draft_target_prob=True,
+                                                     workspace=wss[1], device_error=errs[1])
+        else:
+            args = (zt, zdt, desc, tok, uvt, 0.9)
+            full = gpu.spec_verify_sample_lq(*args, drafter_rows=badt, want_draft_target_prob=True,
+                                             workspace=wss[0], device_error=errs[0])
+            ee = gpu.spec_verify_sample_lq_early_exit(*args, drafter_rows=badt,
+                                                      want_draft_target_prob=True,
+                                                      workspace=wss[1], device_error=errs[1])
+        torch.cuda.synchronize()
+        _prefix_equal(full, ee)
+        assert int(errs[0].item()) == int(errs[1].item()) != 0
+        for w in wss:
+            assert int(w.count_nonzero().item()) == 0

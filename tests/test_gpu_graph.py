@@ -320,3 +320,59 @@ def test_step_graph_lq_replays_match_oracle(gpu, mode):
     assert torch.equal(mg, me)
     assert int(ws_g.count_nonzero().item()) == 0
     graph.close()
+
+
+@pytest.mark.parametrize("mode", ["sample", "greedy", "mixed"])
+def test_step_graph_early_exit(gpu, mode):
+    """A step graph capturing the early-exit verify: every replay (new
+    uniforms and drafts copied in) matches the oracle on its inputs and
+    equals the eager full step in tokens, accept counts and the build;
+    p_k(d_k) equals the full step's up to the first rejection and is 0 past
+    it; the metrics equal the eager ones."""
+    vi = synth.make_verify_inputs(synth.verify_config(2))
+    B, K, V = vi.spec.B, vi.spec.K, vi.spec.V
+    rng = np.random.default_rng(76)
+    temps = np.array([0.0, 0.5, 1.0, 0.0, 1.3, 0.7, 0.0, 2.0], dtype=np.float32)
+    inp = dict(z=dev(vi.logits), q=dev(vi.draft_probs), d=dev(vi.draft_tokens),
+               u=dev(vi.uniforms), T=vi.temperature, temps=dev(temps))
+    b = _build_inputs(B, K, V)
+    bi = b.pop("host")
+    og, oe = _outputs(B, K, V, 512), _outputs(B, K, V, 512)
+    ws_g = torch.zeros(gpu.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=DEV)
+    ws_e = torch.zeros_like(ws_g)
+    mg, me = gpu.accept_metrics_buffer(K, DEV), gpu.accept_metrics_buffer(K, DEV)
+    verify = dict(target_logits=inp["z"], draft_tokens=inp["d"], out_tokens=og["tok"],
+                  out_num_accepted=og["acc"], workspace=ws_g)
+    if mode != "greedy":
+        verify.update(draft_probs=inp["q"], uniforms=inp["u"], out_draft_target_prob=og["pd"])
+    if mode == "sample":
+        verify["temperature"] = vi.temperature
+    if mode == "mixed":
+        verify["temperatures"] = inp["temps"]
+    graph = gpu.StepGraph(mode, verify, dict(b, outputs=og["build"]), metrics=mg,
+                          early_exit=True)
+    for rep in range(3):
+        u_new = rng.random((B, K + 1), dtype=np.float32)
+        d_new = vi.draft_tokens.copy()
+        if rep % 2:
+            d_new[:, rep % K] = rng.integers(0, V, size=B)
+        inp["u"].copy_(dev(u_new))
+        inp["d"].copy_(dev(d_new))
+        graph.launch()
+        torch.cuda.synchronize()
+        _eager(gpu, mode, inp, b, oe, ws_e, me)
+        torch.cuda.synchronize()
+        # the replay's tokens, counts and build against the oracle (p_k(d_k)
+        # past the first rejection is not computed here: the full step's)
+        _replay_matches_oracle(mode, vi.logits, vi.spec.dtype, vi.draft_probs, d_new, u_new,
+                               vi.temperature, temps, dict(og, pd=oe["pd"]), bi)
+        assert torch.equal(og["tok"], oe["tok"]) and torch.equal(og["acc"], oe["acc"]), rep
+        if mode != "greedy":
+            keep = torch.arange(K, device=DEV)[None, :] <= oe["acc"].long()[:, None]
+            want = torch.where(keep, oe["pd"], torch.zeros_like(oe["pd"]))
+            assert torch.equal(og["pd"].view(torch.int32), want.view(torch.int32)), rep
+        for k in og["build"]:
+            assert torch.equal(og["build"][k], oe["build"][k]), (rep, k)
+    assert torch.equal(mg, me)
+    assert int(ws_g.count_nonzero().item()) == 0
+    graph.close()
