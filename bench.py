@@ -347,8 +347,9 @@ def ingest_trace(trace_csv, bench_log=None):
              "`--profile-steps 5` runs, five times on the B=1024 K=7 V=151936 bf16 inputs: a sampled, a greedy and "
              "a mixed verify each followed by the build, the drafter sampling with dense q and with "
              "row descriptors, the verify from drafter logits, the drafter sampling at per-sequence "
-             "temperatures with row descriptors, the mixed verify from drafter logits and the "
-             "acceptance metrics; then the "
+             "temperatures with row descriptors, the mixed verify from drafter logits, the "
+             "early-exit sampled and greedy verify (`verify_rows_level`, four launches each) and "
+             "the acceptance metrics; then the "
              "fused build and the two-kernel build of the comparison library (`meta_kernel`, "
              "`copy_kernel`) five times each on the same verify outputs and at the B=64 H=2880 build "
              "workload, the comparison library's drafter-bytes kernels (`rows_to_f32`, "
@@ -1281,7 +1282,8 @@ def main():
         # every kernel family once per step, for the profiler: sampled, greedy
         # and mixed verify with the build, drafter sampling with q and with
         # row descriptors, the verify from drafter logits (uniform and mixed
-        # temperatures), acceptance metrics, and (below) tree verification
+        # temperatures), the early-exit sampled and greedy verify, acceptance
+        # metrics, and (below) tree verification
         d_desc = torch.empty((B, K, 4), dtype=torch.int32, device=dev)
         m_desc = torch.empty((B, K, 4), dtype=torch.int32, device=dev)
         mtr = sv.accept_metrics_buffer(K, dev)
@@ -1298,6 +1300,10 @@ def main():
                                  want_draft_probs=False, out_row_desc=m_desc)
             sv.spec_verify_mixed_lq(z, z_rows, m_desc, d_tok, u, temps, drafter_rows=d_rows,
                                     out_tokens=out_t, out_num_accepted=acc_t, workspace=ws)
+            sv.spec_verify_sample_early_exit(z, q, d, u, vi.temperature, out_tokens=out_t,
+                                             out_num_accepted=acc_t, workspace=ws)
+            sv.spec_verify_greedy_early_exit(z, d, out_tokens=out_t, out_num_accepted=acc_t,
+                                             workspace=ws)
             sv.spec_accept_metrics(acc_t, K, mtr)
         torch.cuda.synchronize()
         # the build as two kernels (metadata, then the hidden copy) on the
