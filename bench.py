@@ -897,6 +897,21 @@ def small_workloads_bench(sv, torch, np, synth, args):
             rb, sb = verify_bytes(B, K, V, zsize, acc_t.cpu().numpy(), sample=smp)
             r[name] = entry(fn, rb + sb)
             r[name]["gpu_us_per_call"] = gpu_us_per_call(torch, fn)
+
+        # the early-exit forms (row statistics only up to each sequence's
+        # first rejection): GPU time per call, to show where they pay
+        def sample_ee():
+            i = turn[0] = (turn[0] + 1) % copies
+            sv.spec_verify_sample_early_exit(zs[i], qs[i], d, u, vi.temperature,
+                                             out_tokens=out_t, out_num_accepted=acc_t,
+                                             out_draft_target_prob=pd_t, workspace=ws)
+
+        def greedy_ee():
+            i = turn[0] = (turn[0] + 1) % copies
+            sv.spec_verify_greedy_early_exit(zs[i], d, out_tokens=out_t, out_num_accepted=acc_t,
+                                             workspace=ws)
+        r["early_exit_gpu_us_per_call"] = {"sample": gpu_us_per_call(torch, sample_ee),
+                                           "greedy": gpu_us_per_call(torch, greedy_ee)}
         if copies > 1:
             # the same calls on one resident copy: the Infinity Cache then
             # holds all 206 MB of logits between calls

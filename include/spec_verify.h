@@ -292,7 +292,10 @@ SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
  * statistics are computed by the same arithmetic).  out_draft_target_prob
  * [b][k] equals the full call's value for k <= num_accepted[b] and is 0
  * past it.  The launches per call are the row-statistics kernels of the
- * ranges, then the kernels that follow them in the full call.
+ * ranges, then the kernels that follow them in the full call.  The ranges
+ * are dependent launches: for small batches, bound by latency, these forms
+ * are slower than the full calls; they pay for large batches, bound by the
+ * bytes of the logits.
  */
 SV_API sv_status spec_verify_greedy_early_exit(const void* target_logits, int logits_dtype,
                                                const int32_t* draft_tokens, int B, int K, int V,
