@@ -9,8 +9,9 @@ Covered: the tiny, mid and large-vocabulary workloads, a 48-sequence slice
 of the 1024-sequence batch, 300 sequences (one draw workgroup per
 sequence), the ragged shapes of the verify tests (K = 0 and 63, V = 1, V
 not a multiple of 8), every draft accepted, every sequence rejected at its
-first draft, invalid draft tokens, mixed batches with greedy sequences; and
-the oracle directly on the mid workload.
+first draft, invalid draft tokens, mixed batches with greedy sequences,
+SV_MAX_B sequences, the drafter-logit forms; and the oracle directly on the
+mid workload.
 """
 import numpy as np
 import pytest
@@ -207,3 +208,16 @@ def test_drafter_logit_forms(gpu, dtype, B, K, V):
         assert int(errs[0].item()) == int(errs[1].item()) != 0
         for w in wss:
             assert int(w.count_nonzero().item()) == 0
+
+
+def test_max_batch(gpu):
+    """B = SV_MAX_B sequences (K = 1, V = 16, fp32; K = 3 with V = 8 for the
+    ranges [1,2) and [2,4)): the early-exit forms equal the full calls."""
+    for K, V in ((1, 16), (3, 8)):
+        B = gpu.MAX_B if K == 1 else gpu.MAX_B // 4
+        rng = np.random.default_rng(21 + K)
+        z = (2 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+        q = np.full((B, K, V), 1.0 / V, np.float32)
+        d = rng.integers(0, V, size=(B, K)).astype(np.int32)
+        u = rng.random((B, K + 1), dtype=np.float32)
+        _compare(gpu, z, "f32", q, d, u, 1.0)
