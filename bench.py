@@ -1081,6 +1081,20 @@ def tree_bench(sv, torch, np, synth, args):
                 "note": "bytes read by the walk's workgroup passes (a node's logit row, plus "
                         "its fp32 draft row after a rejection); one workgroup per tree, so "
                         "the walk lasts as long as the tree with the most passes"}
+        # the early-exit form: no row kernel, the walk computes the statistics
+        # of the rows it visits (same inputs, same definitions)
+        ref = [x.clone() for x in outs]
+
+        def call_ee():
+            sv.spec_verify_tree_early_exit(z, par, tok, T, draft_probs=q, uniforms=u,
+                                           out_tokens=outs[0], out_path=outs[1],
+                                           out_num_accepted=outs[2], workspace=ws)
+        ee_ms = wall_ms(torch, call_ee, args.warmup, args.steps)
+        same = sum(bool(torch.equal(outs[0][b], ref[0][b]) and torch.equal(outs[1][b], ref[1][b]))
+                   for b in range(B))
+        res[name]["early_exit"] = {
+            "ms_per_call": ee_ms, "speedup": sec * 1e3 / ee_ms, "trees_identical": same,
+            "rows_visited": int(outs[2].long().sum().item()) + B}
     res["drafter_logits"] = tree_lq_bench(sv, torch, np, args, spec, z, par, tok, u, ws, outs)
     return res
 

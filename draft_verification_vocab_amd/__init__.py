@@ -39,6 +39,7 @@ __all__ = [
     "spec_verify_sample_noalloc", "spec_verify_greedy_early_exit",
     "spec_verify_sample_early_exit", "spec_verify_mixed_early_exit",
     "spec_verify_sample_lq_early_exit", "spec_verify_mixed_lq_early_exit",
+    "spec_verify_tree_early_exit", "spec_verify_tree_lq_early_exit",
     "noalloc_scratch_bytes", "spec_verify_tree", "spec_verify_tree_lq", "spec_draft_sample",
     "spec_accept_metrics", "accept_metrics_buffer", "acceptance_summary", "StepGraph",
     "trace_begin", "trace_read", "trace_end",
@@ -93,6 +94,11 @@ _SIGS = {
                               ctypes.c_size_t, _p, _p]),
     "spec_verify_tree_lq": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, _p, ctypes.c_float,
                                  _i, _i, _i, _p, _p, _p, _p, ctypes.c_size_t, _p, _p]),
+    "spec_verify_tree_early_exit": (_i, [_p, _i, _p, _p, _p, _p, ctypes.c_float, _i, _i, _i, _p,
+                                         _p, _p, _p, ctypes.c_size_t, _p, _p]),
+    "spec_verify_tree_lq_early_exit": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, _p,
+                                            ctypes.c_float, _i, _i, _i, _p, _p, _p, _p,
+                                            ctypes.c_size_t, _p, _p]),
     "spec_accept_metrics_words": (ctypes.c_size_t, [_i]),
     "spec_accept_metrics": (_i, [_p, _i, _i, _p, _p, _p]),
     "sv_step_graph_create": (_i, [_p, _p]),
@@ -688,7 +694,8 @@ def spec_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens:
                      out_path: Optional[torch.Tensor] = None,
                      out_num_accepted: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None,
-                     device_error: Optional[torch.Tensor] = None):
+                     device_error: Optional[torch.Tensor] = None,
+                     _symbol: str = "spec_verify_tree"):
     """Verify a draft tree per sequence (temperature 0 = greedy); see
     spec_verify_tree in include/spec_verify.h.
 
@@ -719,14 +726,14 @@ def spec_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens:
     _dev(workspace, "workspace", device=dev)
     if device_error is not None:
         _dev(device_error, "device_error", torch.int32, (1,), dev)
-    st = lib.spec_verify_tree(_ptr(target_logits), _DTYPES[target_logits.dtype],
+    st = getattr(lib, _symbol)(_ptr(target_logits), _DTYPES[target_logits.dtype],
                               _ptr(draft_probs if temperature > 0 else None), _ptr(parents),
                               _ptr(tokens), _ptr(uniforms if temperature > 0 else None),
                               float(temperature), B, N, V, _ptr(out_tokens), _ptr(out_path),
                               _ptr(out_num_accepted), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _ptr(device_error),
                               _stream(dev))
-    _check(st, "spec_verify_tree")
+    _check(st, _symbol)
     return out_tokens, out_path, out_num_accepted
 
 
@@ -738,7 +745,8 @@ def spec_verify_tree_lq(target_logits: torch.Tensor, drafter_logits: torch.Tenso
                         out_path: Optional[torch.Tensor] = None,
                         out_num_accepted: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None,
-                        device_error: Optional[torch.Tensor] = None):
+                        device_error: Optional[torch.Tensor] = None,
+                        _symbol: str = "spec_verify_tree_lq"):
     """Sampled tree verification with q recomputed from the drafter logits
     and the row descriptors of spec_draft_sample; see spec_verify_tree_lq in
     include/spec_verify.h.  drafter_desc is [B, N+1, 4] int32 (sv_draft_row),
@@ -773,15 +781,28 @@ def spec_verify_tree_lq(target_logits: torch.Tensor, drafter_logits: torch.Tenso
     _dev(workspace, "workspace", device=dev)
     if device_error is not None:
         _dev(device_error, "device_error", torch.int32, (1,), dev)
-    st = lib.spec_verify_tree_lq(_ptr(target_logits), _DTYPES[target_logits.dtype],
+    st = getattr(lib, _symbol)(_ptr(target_logits), _DTYPES[target_logits.dtype],
                                  _ptr(drafter_logits), drafter_logits.shape[0],
                                  _ptr(drafter_rows), _ptr(drafter_desc), _ptr(parents),
                                  _ptr(tokens), _ptr(uniforms), float(temperature), B, N, V,
                                  _ptr(out_tokens), _ptr(out_path), _ptr(out_num_accepted),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _ptr(device_error), _stream(dev))
-    _check(st, "spec_verify_tree_lq")
+    _check(st, _symbol)
     return out_tokens, out_path, out_num_accepted
+
+
+def spec_verify_tree_early_exit(*args, **kw):
+    """spec_verify_tree with the walk computing the statistics of the rows it
+    visits only; see spec_verify_tree_early_exit in include/spec_verify.h.
+    Arguments and results as spec_verify_tree."""
+    return spec_verify_tree(*args, _symbol="spec_verify_tree_early_exit", **kw)
+
+
+def spec_verify_tree_lq_early_exit(*args, **kw):
+    """spec_verify_tree_lq with the walk computing the statistics of the rows
+    it visits only; see spec_verify_tree_lq_early_exit in include/spec_verify.h."""
+    return spec_verify_tree_lq(*args, _symbol="spec_verify_tree_lq_early_exit", **kw)
 
 
 # ---------------------------------------------------------------- acceptance metrics

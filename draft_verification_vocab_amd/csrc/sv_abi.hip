@@ -265,6 +265,108 @@ sv_status verify_lq(const void* target_logits, int logits_dtype, const void* dra
   return launch_verify(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+// spec_verify_tree / spec_verify_tree_lq, and their _early_exit forms (lazy:
+// the walk computes the statistics of the rows it visits).
+sv_status tree_dense(const void* target_logits, int logits_dtype, const float* draft_probs,
+                     const int32_t* parents, const int32_t* tokens, const float* uniforms,
+                     float temperature, int B, int N, int V, int32_t* out_tokens,
+                     int32_t* out_path, int32_t* out_num_accepted, void* workspace,
+                     size_t workspace_bytes, int32_t* device_error, void* stream, bool lazy) {
+  sv_status st = check_verify_shape(B, N, V);
+  if (st != SV_OK) return st;
+  if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (!(temperature >= 0.0f && isfinite(temperature))) return SV_ERR_VALUE;
+  const bool sample = temperature > 0.0f;
+  if (sample && !isfinite((float)(1.4426950408889634 / (double)temperature))) return SV_ERR_VALUE;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !out_tokens || !out_path || !out_num_accepted) return SV_ERR_NULL;
+  if (N > 0 && (!parents || !tokens)) return SV_ERR_NULL;
+  if (sample && (!draft_probs || !uniforms)) return SV_ERR_NULL;
+  if (!workspace || workspace_bytes < sv::verify_workspace_bytes(B, N, V)) return SV_ERR_WORKSPACE;
+  const size_t esz = logits_dtype == SV_BF16 ? 2 : 4;
+  if (!aligned(target_logits, esz) || !aligned(out_tokens, 4) || !aligned(out_path, 4) ||
+      !aligned(out_num_accepted, 4) || !aligned(workspace, 16) ||
+      (parents && !aligned(parents, 4)) || (tokens && !aligned(tokens, 4)) ||
+      (draft_probs && !aligned(draft_probs, 4)) || (uniforms && !aligned(uniforms, 4)) ||
+      (device_error && !aligned(device_error, 4)))
+    return SV_ERR_ALIGN;
+  if ((long)B * (N + 1) * sv::verify_splits(B, N, V) > 0x7fffffffL) return SV_ERR_SHAPE;
+  sv::TreeLaunch L;
+  L.logits = target_logits;
+  L.draft_probs = sample ? draft_probs : nullptr;
+  L.dlogits = nullptr;
+  L.d_rows = 0;
+  L.drows = nullptr;
+  L.ddesc = nullptr;
+  L.parents = parents;
+  L.tokens = tokens;
+  L.uniforms = uniforms;
+  L.temperature = temperature;
+  L.B = B; L.N = N; L.V = V;
+  L.bf16 = logits_dtype == SV_BF16;
+  L.vec = (V % 8 == 0) && aligned(target_logits, 16) &&
+          (!sample || aligned(draft_probs, 16));
+  L.out_tokens = out_tokens;
+  L.out_path = out_path;
+  L.out_num_accepted = out_num_accepted;
+  L.workspace = workspace;
+  L.device_error = device_error;
+  L.lazy = lazy ? 1 : 0;
+  return sv::launch_tree(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status tree_lq(const void* target_logits, int logits_dtype, const void* drafter_logits,
+                  int64_t n_drafter_rows, const int32_t* drafter_rows,
+                  const sv_draft_row* drafter_desc, const int32_t* parents,
+                  const int32_t* tokens, const float* uniforms, float temperature, int B, int N,
+                  int V, int32_t* out_tokens, int32_t* out_path, int32_t* out_num_accepted,
+                  void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream,
+                  bool lazy) {
+  sv_status st = check_verify_shape(B, N, V);
+  if (st != SV_OK) return st;
+  if (n_drafter_rows < 0 || n_drafter_rows > 0x7fffffffL) return SV_ERR_SHAPE;
+  if (!drafter_rows && n_drafter_rows < (int64_t)B * (N + 1)) return SV_ERR_SHAPE;
+  if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (!(temperature > 0.0f && isfinite(temperature) &&
+        isfinite((float)(1.4426950408889634 / (double)temperature))))
+    return SV_ERR_VALUE;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !out_tokens || !out_path || !out_num_accepted || !uniforms ||
+      !drafter_logits || !drafter_desc)
+    return SV_ERR_NULL;
+  if (N > 0 && (!parents || !tokens)) return SV_ERR_NULL;
+  if (!workspace || workspace_bytes < sv::verify_workspace_bytes(B, N, V)) return SV_ERR_WORKSPACE;
+  const size_t esz = logits_dtype == SV_BF16 ? 2 : 4;
+  if (!aligned(target_logits, esz) || !aligned(drafter_logits, esz) || !aligned(out_tokens, 4) ||
+      !aligned(out_path, 4) || !aligned(out_num_accepted, 4) || !aligned(workspace, 16) ||
+      !aligned(uniforms, 4) || !aligned(drafter_desc, 16) ||
+      (drafter_rows && !aligned(drafter_rows, 4)) || (parents && !aligned(parents, 4)) ||
+      (tokens && !aligned(tokens, 4)) || (device_error && !aligned(device_error, 4)))
+    return SV_ERR_ALIGN;
+  if ((long)B * (N + 1) * sv::verify_splits(B, N, V) > 0x7fffffffL) return SV_ERR_SHAPE;
+  sv::TreeLaunch L;
+  L.logits = target_logits;
+  L.draft_probs = nullptr;
+  L.dlogits = drafter_logits;
+  L.d_rows = (long)n_drafter_rows;
+  L.drows = drafter_rows;
+  L.ddesc = drafter_desc;
+  L.parents = parents;
+  L.tokens = tokens;
+  L.uniforms = uniforms;
+  L.temperature = temperature;
+  L.B = B; L.N = N; L.V = V;
+  L.bf16 = logits_dtype == SV_BF16;
+  L.vec = (V % 8 == 0) && aligned(target_logits, 16) && aligned(drafter_logits, 16);
+  L.out_tokens = out_tokens;
+  L.out_path = out_path;
+  L.out_num_accepted = out_num_accepted;
+  L.workspace = workspace;
+  L.device_error = device_error;
+  L.lazy = lazy ? 1 : 0;
+  return sv::launch_tree(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 }  // namespace sv
 
 extern "C" {
@@ -501,46 +603,22 @@ SV_API sv_status spec_verify_tree(const void* target_logits, int logits_dtype,
                                   int B, int N, int V, int32_t* out_tokens, int32_t* out_path,
                                   int32_t* out_num_accepted, void* workspace,
                                   size_t workspace_bytes, int32_t* device_error, void* stream) {
-  sv_status st = check_verify_shape(B, N, V);
-  if (st != SV_OK) return st;
-  if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
-  if (!(temperature >= 0.0f && isfinite(temperature))) return SV_ERR_VALUE;
-  const bool sample = temperature > 0.0f;
-  if (sample && !isfinite((float)(1.4426950408889634 / (double)temperature))) return SV_ERR_VALUE;
-  if (B == 0) return SV_OK;
-  if (!target_logits || !out_tokens || !out_path || !out_num_accepted) return SV_ERR_NULL;
-  if (N > 0 && (!parents || !tokens)) return SV_ERR_NULL;
-  if (sample && (!draft_probs || !uniforms)) return SV_ERR_NULL;
-  if (!workspace || workspace_bytes < sv::verify_workspace_bytes(B, N, V)) return SV_ERR_WORKSPACE;
-  const size_t esz = logits_dtype == SV_BF16 ? 2 : 4;
-  if (!aligned(target_logits, esz) || !aligned(out_tokens, 4) || !aligned(out_path, 4) ||
-      !aligned(out_num_accepted, 4) || !aligned(workspace, 16) ||
-      (parents && !aligned(parents, 4)) || (tokens && !aligned(tokens, 4)) ||
-      (draft_probs && !aligned(draft_probs, 4)) || (uniforms && !aligned(uniforms, 4)) ||
-      (device_error && !aligned(device_error, 4)))
-    return SV_ERR_ALIGN;
-  if ((long)B * (N + 1) * sv::verify_splits(B, N, V) > 0x7fffffffL) return SV_ERR_SHAPE;
-  sv::TreeLaunch L;
-  L.logits = target_logits;
-  L.draft_probs = sample ? draft_probs : nullptr;
-  L.dlogits = nullptr;
-  L.d_rows = 0;
-  L.drows = nullptr;
-  L.ddesc = nullptr;
-  L.parents = parents;
-  L.tokens = tokens;
-  L.uniforms = uniforms;
-  L.temperature = temperature;
-  L.B = B; L.N = N; L.V = V;
-  L.bf16 = logits_dtype == SV_BF16;
-  L.vec = (V % 8 == 0) && aligned(target_logits, 16) &&
-          (!sample || aligned(draft_probs, 16));
-  L.out_tokens = out_tokens;
-  L.out_path = out_path;
-  L.out_num_accepted = out_num_accepted;
-  L.workspace = workspace;
-  L.device_error = device_error;
-  return sv::launch_tree(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+  return sv::tree_dense(target_logits, logits_dtype, draft_probs, parents, tokens, uniforms,
+                        temperature, B, N, V, out_tokens, out_path, out_num_accepted, workspace,
+                        workspace_bytes, device_error, stream, false);
+}
+
+SV_API sv_status spec_verify_tree_early_exit(const void* target_logits, int logits_dtype,
+                                             const float* draft_probs, const int32_t* parents,
+                                             const int32_t* tokens, const float* uniforms,
+                                             float temperature, int B, int N, int V,
+                                             int32_t* out_tokens, int32_t* out_path,
+                                             int32_t* out_num_accepted, void* workspace,
+                                             size_t workspace_bytes, int32_t* device_error,
+                                             void* stream) {
+  return sv::tree_dense(target_logits, logits_dtype, draft_probs, parents, tokens, uniforms,
+                        temperature, B, N, V, out_tokens, out_path, out_num_accepted, workspace,
+                        workspace_bytes, device_error, stream, true);
 }
 
 SV_API sv_status spec_verify_tree_lq(const void* target_logits, int logits_dtype,
@@ -553,48 +631,22 @@ SV_API sv_status spec_verify_tree_lq(const void* target_logits, int logits_dtype
                                      int32_t* out_num_accepted, void* workspace,
                                      size_t workspace_bytes, int32_t* device_error,
                                      void* stream) {
-  sv_status st = check_verify_shape(B, N, V);
-  if (st != SV_OK) return st;
-  if (n_drafter_rows < 0 || n_drafter_rows > 0x7fffffffL) return SV_ERR_SHAPE;
-  if (!drafter_rows && n_drafter_rows < (int64_t)B * (N + 1)) return SV_ERR_SHAPE;
-  if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
-  if (!(temperature > 0.0f && isfinite(temperature) &&
-        isfinite((float)(1.4426950408889634 / (double)temperature))))
-    return SV_ERR_VALUE;
-  if (B == 0) return SV_OK;
-  if (!target_logits || !out_tokens || !out_path || !out_num_accepted || !uniforms ||
-      !drafter_logits || !drafter_desc)
-    return SV_ERR_NULL;
-  if (N > 0 && (!parents || !tokens)) return SV_ERR_NULL;
-  if (!workspace || workspace_bytes < sv::verify_workspace_bytes(B, N, V)) return SV_ERR_WORKSPACE;
-  const size_t esz = logits_dtype == SV_BF16 ? 2 : 4;
-  if (!aligned(target_logits, esz) || !aligned(drafter_logits, esz) || !aligned(out_tokens, 4) ||
-      !aligned(out_path, 4) || !aligned(out_num_accepted, 4) || !aligned(workspace, 16) ||
-      !aligned(uniforms, 4) || !aligned(drafter_desc, 16) ||
-      (drafter_rows && !aligned(drafter_rows, 4)) || (parents && !aligned(parents, 4)) ||
-      (tokens && !aligned(tokens, 4)) || (device_error && !aligned(device_error, 4)))
-    return SV_ERR_ALIGN;
-  if ((long)B * (N + 1) * sv::verify_splits(B, N, V) > 0x7fffffffL) return SV_ERR_SHAPE;
-  sv::TreeLaunch L;
-  L.logits = target_logits;
-  L.draft_probs = nullptr;
-  L.dlogits = drafter_logits;
-  L.d_rows = (long)n_drafter_rows;
-  L.drows = drafter_rows;
-  L.ddesc = drafter_desc;
-  L.parents = parents;
-  L.tokens = tokens;
-  L.uniforms = uniforms;
-  L.temperature = temperature;
-  L.B = B; L.N = N; L.V = V;
-  L.bf16 = logits_dtype == SV_BF16;
-  L.vec = (V % 8 == 0) && aligned(target_logits, 16) && aligned(drafter_logits, 16);
-  L.out_tokens = out_tokens;
-  L.out_path = out_path;
-  L.out_num_accepted = out_num_accepted;
-  L.workspace = workspace;
-  L.device_error = device_error;
-  return sv::launch_tree(L, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+  return sv::tree_lq(target_logits, logits_dtype, drafter_logits, n_drafter_rows, drafter_rows,
+                     drafter_desc, parents, tokens, uniforms, temperature, B, N, V, out_tokens,
+                     out_path, out_num_accepted, workspace, workspace_bytes, device_error, stream,
+                     false);
+}
+
+SV_API sv_status spec_verify_tree_lq_early_exit(
+    const void* target_logits, int logits_dtype, const void* drafter_logits,
+    int64_t n_drafter_rows, const int32_t* drafter_rows, const sv_draft_row* drafter_desc,
+    const int32_t* parents, const int32_t* tokens, const float* uniforms, float temperature,
+    int B, int N, int V, int32_t* out_tokens, int32_t* out_path, int32_t* out_num_accepted,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream) {
+  return sv::tree_lq(target_logits, logits_dtype, drafter_logits, n_drafter_rows, drafter_rows,
+                     drafter_desc, parents, tokens, uniforms, temperature, B, N, V, out_tokens,
+                     out_path, out_num_accepted, workspace, workspace_bytes, device_error, stream,
+                     true);
 }
 
 SV_API size_t spec_accept_metrics_words(int K) {

@@ -92,6 +92,9 @@ struct TreeLaunch {
   int32_t* out_num_accepted;     // [B]
   void* workspace;
   int32_t* device_error;
+  // row statistics computed by the walk for the nodes it visits only
+  // (spec_verify_tree*_early_exit), instead of by the row kernel for all
+  int lazy = 0;
 };
 
 // The row-statistics partials of a verify workspace: [B][K+1][S] entries.

@@ -204,7 +204,11 @@ __device__ __forceinline__ double residual_tiles(const LT* zrow, const TreeQ<LT>
   return tot;
 }
 
-template <typename LT, int MODE, bool VEC, bool QL = false>
+// LAZY: the statistics of a node's row are computed by the walk itself when
+// it reaches the node (one workgroup pass, `slice_stats` over the whole row),
+// so only the rows of the visited nodes are read; otherwise they come from
+// the row kernel's partials of every row.
+template <typename LT, int MODE, bool VEC, bool QL = false, bool LAZY = false>
 __global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
   constexpr int THREADS = tree_threads<MODE>();
   constexpr int WAVES = THREADS / kWave;
@@ -212,6 +216,10 @@ __global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
   __shared__ int s_tok[SV_MAX_K + 1];
   __shared__ float tsum[kMaxTiles];
   __shared__ double red[WAVES];
+  __shared__ float sm_f[LAZY ? WAVES : 1];
+  __shared__ int sm_i[LAZY ? WAVES : 1];
+  __shared__ double sm_d[LAZY ? WAVES : 1];
+  __shared__ Partial s_stat;
 
   const TreeLaunch& L = A.L;
   const int b = blockIdx.x, N = L.N, t = threadIdx.x, S = A.S;
@@ -235,27 +243,39 @@ __global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
   const float c = A.c;
   int cur = 0, depth = 0;
   for (;;) {
-    // statistics of row cur from its S partials (same order on every thread)
     float M = -INFINITY;
     int g = INT32_MAX;
     double s = 0.0;
-    // all of the row's partials loaded at once (at most kTreeSplits of them)
-    Partial pk[kTreeSplits];
-#pragma unroll
-    for (int j = 0; j < kTreeSplits; ++j)
-      if (j < S) pk[j] = Pb[cur * S + j];
-    if constexpr (MODE == GREEDY) {
-#pragma unroll
-      for (int j = 0; j < kTreeSplits; ++j)
-        if (j < S && (j == 0 || pk[j].m > M)) { M = pk[j].m; g = pk[j].g; }
+    if constexpr (LAZY) {
+      // statistics of row cur by one pass of the workgroup, then shared
+      const Partial P = slice_stats<LT, MODE, VEC, THREADS>(zb + (long)cur * V, 0,
+                                                            (V + 7) / 8, V, c, sm_f, sm_i, sm_d);
+      if (t == 0) s_stat = P;
+      __syncthreads();
+      M = s_stat.m;
+      g = s_stat.g;
+      s = s_stat.acc;
+      __syncthreads();                     // s_stat is written again at the next node
     } else {
+      // statistics of row cur from its S partials (same order on every
+      // thread), all of them loaded at once (at most kTreeSplits)
+      Partial pk[kTreeSplits];
 #pragma unroll
       for (int j = 0; j < kTreeSplits; ++j)
-        if (j < S) M = fmaxf(M, pk[j].m);
+        if (j < S) pk[j] = Pb[cur * S + j];
+      if constexpr (MODE == GREEDY) {
 #pragma unroll
-      for (int j = 0; j < kTreeSplits; ++j)
-        if (j < S && pk[j].acc != 0.0)
-          s += pk[j].acc * exp2_split(((double)pk[j].m - (double)M) * (double)c);
+        for (int j = 0; j < kTreeSplits; ++j)
+          if (j < S && (j == 0 || pk[j].m > M)) { M = pk[j].m; g = pk[j].g; }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kTreeSplits; ++j)
+          if (j < S) M = fmaxf(M, pk[j].m);
+#pragma unroll
+        for (int j = 0; j < kTreeSplits; ++j)
+          if (j < S && pk[j].acc != 0.0)
+            s += pk[j].acc * exp2_split(((double)pk[j].m - (double)M) * (double)c);
+      }
     }
     const LT* zrow = zb + (long)cur * V;
     int nxt = -1;
@@ -373,14 +393,17 @@ __global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
   for (int j = depth + t; j <= N; j += THREADS) path[j] = -1;
   if (t == 0) L.out_num_accepted[b] = depth;
   // the partials are consumed: clear them so the workspace ends all zero
-  for (int i = t; i < (N + 1) * S; i += THREADS) Pb[i] = Partial{0.f, 0, 0.0};
+  if constexpr (!LAZY)
+    for (int i = t; i < (N + 1) * S; i += THREADS) Pb[i] = Partial{0.f, 0, 0.0};
 }
 
 hipError_t launch_tree(const TreeLaunch& L, hipStream_t stream) {
   const bool sample = L.temperature > 0.f;
   const float c = sample ? (float)(1.4426950408889634 / (double)L.temperature) : 1.0f;
-  hipError_t err = launch_row_stats(L.logits, L.bf16, L.vec, sample, c, L.B, L.N, L.V, L.workspace,
-                                    SV_KERNEL_TREE_ROWS, stream);
+  hipError_t err = hipSuccess;
+  if (!L.lazy)
+    err = launch_row_stats(L.logits, L.bf16, L.vec, sample, c, L.B, L.N, L.V, L.workspace,
+                           SV_KERNEL_TREE_ROWS, stream);
   if (err != hipSuccess) return err;
   const RowPartials rp = row_partials(L.workspace, L.B, L.N, L.V);
   TreeArgs A{L, static_cast<Partial*>(rp.partials), rp.S, c};
@@ -389,8 +412,13 @@ hipError_t launch_tree(const TreeLaunch& L, hipStream_t stream) {
   trace_before(stream, SV_KERNEL_TREE_WALK);
 #define SV_TREE(LT, MODE, QL) \
   do { \
-    if (L.vec) hipLaunchKernelGGL((tree_walk<LT, MODE, true, QL>), grid, block, 0, stream, A); \
-    else hipLaunchKernelGGL((tree_walk<LT, MODE, false, QL>), grid, block, 0, stream, A); \
+    if (L.lazy) { \
+      if (L.vec) hipLaunchKernelGGL((tree_walk<LT, MODE, true, QL, true>), grid, block, 0, stream, A); \
+      else hipLaunchKernelGGL((tree_walk<LT, MODE, false, QL, true>), grid, block, 0, stream, A); \
+    } else { \
+      if (L.vec) hipLaunchKernelGGL((tree_walk<LT, MODE, true, QL>), grid, block, 0, stream, A); \
+      else hipLaunchKernelGGL((tree_walk<LT, MODE, false, QL>), grid, block, 0, stream, A); \
+    } \
   } while (0)
   if (L.bf16) {
     if (ql) SV_TREE(uint16_t, SAMPLE, true);

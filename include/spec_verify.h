@@ -438,6 +438,34 @@ SV_API sv_status spec_verify_tree_lq(const void* target_logits, int logits_dtype
                                      int32_t* device_error, void* stream);
 
 /*
+ * Early-exit forms of spec_verify_tree and spec_verify_tree_lq: no row
+ * kernel; the walk computes the statistics of a node's row (one workgroup
+ * pass) when it reaches the node, so only the rows of the nodes on the
+ * accepted path and of the node where the walk stops are read, instead of
+ * all B*(N+1).  Same arguments, validation, workspace and flags as the
+ * corresponding call; the outcomes are those of the same definitions (the
+ * greedy walk's bit for bit), while a row's sum of exponentials is added in
+ * a different order than the row kernel's, so a sampled decision within
+ * rounding of its threshold may differ from the full call's (the 1e-6
+ * near-tie rule).  The walks are one workgroup per tree: these forms pay
+ * for batches of at least about one tree per CU.
+ */
+SV_API sv_status spec_verify_tree_early_exit(const void* target_logits, int logits_dtype,
+                                             const float* draft_probs, const int32_t* parents,
+                                             const int32_t* tokens, const float* uniforms,
+                                             float temperature, int B, int N, int V,
+                                             int32_t* out_tokens, int32_t* out_path,
+                                             int32_t* out_num_accepted, void* workspace,
+                                             size_t workspace_bytes, int32_t* device_error,
+                                             void* stream);
+SV_API sv_status spec_verify_tree_lq_early_exit(
+    const void* target_logits, int logits_dtype, const void* drafter_logits,
+    int64_t n_drafter_rows, const int32_t* drafter_rows, const sv_draft_row* drafter_desc,
+    const int32_t* parents, const int32_t* tokens, const float* uniforms, float temperature,
+    int B, int N, int V, int32_t* out_tokens, int32_t* out_path, int32_t* out_num_accepted,
+    void* workspace, size_t workspace_bytes, int32_t* device_error, void* stream);
+
+/*
  * P-EAGLE drafter batch.  Source: the P-EAGLE / TorchSpec blog summary,
  * section 并行架构的核心创新 (one drafter forward predicts all K drafts
  * from the NTP row and K-1 MASK rows carrying h_shared) and section TorchSpec

@@ -42,7 +42,8 @@ def test_header_declares_the_boundary():
               "spec_verify_tree_lq", "spec_verify_mixed_lq",
               "spec_verify_noalloc_scratch_bytes", "spec_verify_greedy_early_exit",
               "spec_verify_sample_early_exit", "spec_verify_mixed_early_exit",
-              "spec_verify_sample_lq_early_exit", "spec_verify_mixed_lq_early_exit"):
+              "spec_verify_sample_lq_early_exit", "spec_verify_mixed_lq_early_exit",
+              "spec_verify_tree_early_exit", "spec_verify_tree_lq_early_exit"):
         assert n in names
 
 
@@ -317,14 +318,20 @@ def test_step_desc_layout_matches_header():
 
 
 def tree(lib, logits=FAKE, dtype=1, q=FAKE, par=FAKE, tok=FAKE, u=FAKE, T=0.7, B=2, N=6, V=64,
-         out=FAKE, path=FAKE, acc=FAKE, ws=FAKE, wsb=None):
+         out=FAKE, path=FAKE, acc=FAKE, ws=FAKE, wsb=None, fn="spec_verify_tree"):
     if wsb is None:
         wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(N, 0), max(V, 1))
-    return lib.spec_verify_tree(logits, dtype, q, par, tok, u, T, B, N, V, out, path, acc, ws, wsb,
-                                None, None)
+    return getattr(lib, fn)(logits, dtype, q, par, tok, u, T, B, N, V, out, path, acc, ws, wsb,
+                            None, None)
 
 
-def test_tree_validation(lib):
+@pytest.mark.parametrize("fn", ["spec_verify_tree", "spec_verify_tree_early_exit"])
+def test_tree_validation(lib, fn):
+    import functools
+    _tree_cases(lib, functools.partial(tree, fn=fn))
+
+
+def _tree_cases(lib, tree):
     assert tree(lib, N=64) == ESHAPE
     assert tree(lib, N=-1) == ESHAPE
     assert tree(lib, V=0) == ESHAPE
@@ -408,14 +415,20 @@ def _mixed_lq_cases(lib, mixed_lq):
 
 def tree_lq(lib, logits=FAKE, dtype=1, dl=FAKE, n_rows=14, rows=None, desc=FAKE, par=FAKE,
             tok=FAKE, u=FAKE, T=0.7, B=2, N=6, V=64, out=FAKE, path=FAKE, acc=FAKE, ws=FAKE,
-            wsb=None):
+            wsb=None, fn="spec_verify_tree_lq"):
     if wsb is None:
         wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(N, 0), max(V, 1))
-    return lib.spec_verify_tree_lq(logits, dtype, dl, n_rows, rows, desc, par, tok, u, T, B, N, V,
-                                   out, path, acc, ws, wsb, None, None)
+    return getattr(lib, fn)(logits, dtype, dl, n_rows, rows, desc, par, tok, u, T, B, N, V, out,
+                            path, acc, ws, wsb, None, None)
 
 
-def test_tree_lq_validation(lib):
+@pytest.mark.parametrize("fn", ["spec_verify_tree_lq", "spec_verify_tree_lq_early_exit"])
+def test_tree_lq_validation(lib, fn):
+    import functools
+    _tree_lq_cases(lib, functools.partial(tree_lq, fn=fn))
+
+
+def _tree_lq_cases(lib, tree_lq):
     assert tree_lq(lib, N=64) == ESHAPE
     assert tree_lq(lib, n_rows=13) == ESHAPE            # fewer than B*(N+1) rows, no row index
     assert tree_lq(lib, n_rows=-1, rows=FAKE) == ESHAPE
