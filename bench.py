@@ -354,7 +354,9 @@ def ingest_trace(trace_csv, bench_log=None):
              "`copy_kernel`) five times each on the same verify outputs and at the B=64 H=2880 build "
              "workload, the comparison library's drafter-bytes kernels (`rows_to_f32`, "
              "`write_rows`; 4 calls each), five greedy and five sampled tree verifications (64 "
-             "trees of 15 nodes, V=151936 bf16), one drafter sampling of one row per tree node "
+             "trees of 15 nodes, V=151936 bf16), each also in its early-exit form "
+             "(`tree_walk<…, true>` as the last template argument: no row kernel), one drafter "
+             "sampling of one row per tree node "
              "with row descriptors and five tree verifications from those drafter logits, "
              "one pass each of the read-ceiling kernel "
              "(`stream_read<true>` non-temporal, `stream_read<false>` cached) over the 2.49 GB "
@@ -1362,6 +1364,7 @@ def main():
         for i in range(args.profile_steps):
             for T in (0.0, ts.temperature):
                 sv.spec_verify_tree(tz, tp, tt, T, draft_probs=tq, uniforms=tu)
+                sv.spec_verify_tree_early_exit(tz, tp, tt, T, draft_probs=tq, uniforms=tu)
         # the same trees with q from drafter logits: node (b, n) drafted from
         # the target row of node n of tree b+1 (distinct rows, so that some
         # children are rejected and the walk makes residual passes)
