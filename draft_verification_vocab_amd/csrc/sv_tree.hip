@@ -36,7 +36,10 @@ namespace sv {
 // a row (at 256 trees x 16 rows x 151936: 119 us with 512 threads, 181 with
 // 256; 1024 would be 106 but spills registers); the greedy walk only reads
 // partials.
-template <int MODE> constexpr int tree_threads() { return MODE == SAMPLE ? 512 : 256; }
+// A greedy walk that computes its rows' statistics itself (LAZY) is a chain
+// of whole-row passes by one workgroup, so it takes the widest workgroup.
+template <int MODE, bool LAZY = false>
+constexpr int tree_threads() { return MODE == SAMPLE ? 512 : (LAZY ? 1024 : 256); }
 constexpr int kTreeSplits = 16;        // workgroups per row at most (the row kernel's limit)
 
 struct TreeArgs {
@@ -209,8 +212,8 @@ __device__ __forceinline__ double residual_tiles(const LT* zrow, const TreeQ<LT>
 // so only the rows of the visited nodes are read; otherwise they come from
 // the row kernel's partials of every row.
 template <typename LT, int MODE, bool VEC, bool QL = false, bool LAZY = false>
-__global__ __launch_bounds__(tree_threads<MODE>()) void tree_walk(TreeArgs A) {
-  constexpr int THREADS = tree_threads<MODE>();
+__global__ __launch_bounds__((tree_threads<MODE, LAZY>())) void tree_walk(TreeArgs A) {
+  constexpr int THREADS = tree_threads<MODE, LAZY>();
   constexpr int WAVES = THREADS / kWave;
   __shared__ int s_par[SV_MAX_K + 1];
   __shared__ int s_tok[SV_MAX_K + 1];
@@ -407,7 +410,9 @@ hipError_t launch_tree(const TreeLaunch& L, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const RowPartials rp = row_partials(L.workspace, L.B, L.N, L.V);
   TreeArgs A{L, static_cast<Partial*>(rp.partials), rp.S, c};
-  const dim3 grid((unsigned)L.B), block(sample ? tree_threads<SAMPLE>() : tree_threads<GREEDY>());
+  const dim3 grid((unsigned)L.B);
+  const dim3 block(sample ? tree_threads<SAMPLE>()
+                          : (L.lazy ? tree_threads<GREEDY, true>() : tree_threads<GREEDY>()));
   const bool ql = sample && L.dlogits != nullptr;
   trace_before(stream, SV_KERNEL_TREE_WALK);
 #define SV_TREE(LT, MODE, QL) \
