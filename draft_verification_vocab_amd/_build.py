@@ -6,8 +6,11 @@ from __future__ import annotations
 
 import glob
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libspecverify.so")
@@ -16,7 +19,7 @@ CEILING_DIR = os.path.join(HERE, "ceiling")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fvisibility=hidden",
     # no packed-fp32 instructions in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,9 +35,7 @@ def ceiling_sources():
     return sorted(glob.glob(os.path.join(CEILING_DIR, "*.hip")))
 
 
-def _compile(srcs, out, verbose):
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,7 +45,24 @@ def _compile(srcs, out, verbose):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, out)
+
+
+def _compile(srcs, out, verbose):
+    """One object per source, compiled in parallel (every source is a
+    self-contained translation unit: no device code crosses files), then one
+    shared library."""
+    tmpdir = tempfile.mkdtemp(prefix="svbuild-")
+    try:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in srcs]
+        jobs = max(1, min(len(srcs), os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]], verbose),
+                        zip(srcs, objs)))
+        tmp = out + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, out)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
 
 
 def build(verbose: bool = False) -> str:
