@@ -1097,6 +1097,18 @@ def tree_bench(sv, torch, np, synth, args):
         res[name]["early_exit"] = {
             "ms_per_call": ee_ms, "speedup": sec * 1e3 / ee_ms, "trees_identical": same,
             "rows_visited": int(outs[2].long().sum().item()) + B}
+    # a mixed serving batch of trees: per-tree temperatures from {0, 0.5, 0.7,
+    # 1.0, 1.3}, full and early-exit forms
+    temps_np = synth.make_temperatures(B, 62)
+    temps = up(temps_np)
+    res["mixed"] = {"greedy_trees": int((temps_np == 0).sum()), "sampled_trees": int(
+        (temps_np > 0).sum())}
+    for name, fn in (("full", sv.spec_verify_tree_mixed),
+                     ("early_exit", sv.spec_verify_tree_mixed_early_exit)):
+        def call_m():
+            fn(z, par, tok, temps, q, u, out_tokens=outs[0], out_path=outs[1],
+               out_num_accepted=outs[2], workspace=ws)
+        res["mixed"][f"{name}_ms_per_call"] = wall_ms(torch, call_m, args.warmup, args.steps)
     res["drafter_logits"] = tree_lq_bench(sv, torch, np, args, spec, z, par, tok, u, ws, outs)
     return res
 

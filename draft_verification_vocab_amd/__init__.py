@@ -39,7 +39,8 @@ __all__ = [
     "spec_verify_sample_noalloc", "spec_verify_greedy_early_exit",
     "spec_verify_sample_early_exit", "spec_verify_mixed_early_exit",
     "spec_verify_sample_lq_early_exit", "spec_verify_mixed_lq_early_exit",
-    "spec_verify_tree_early_exit", "spec_verify_tree_lq_early_exit",
+    "spec_verify_tree_early_exit", "spec_verify_tree_lq_early_exit", "spec_verify_tree_mixed",
+    "spec_verify_tree_mixed_early_exit",
     "noalloc_scratch_bytes", "spec_verify_tree", "spec_verify_tree_lq", "spec_draft_sample",
     "spec_accept_metrics", "accept_metrics_buffer", "acceptance_summary", "StepGraph",
     "trace_begin", "trace_read", "trace_end",
@@ -99,6 +100,10 @@ _SIGS = {
     "spec_verify_tree_lq_early_exit": (_i, [_p, _i, _p, ctypes.c_int64, _p, _p, _p, _p, _p,
                                             ctypes.c_float, _i, _i, _i, _p, _p, _p, _p,
                                             ctypes.c_size_t, _p, _p]),
+    "spec_verify_tree_mixed": (_i, [_p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p,
+                                    ctypes.c_size_t, _p, _p]),
+    "spec_verify_tree_mixed_early_exit": (_i, [_p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p,
+                                               _p, _p, ctypes.c_size_t, _p, _p]),
     "spec_accept_metrics_words": (ctypes.c_size_t, [_i]),
     "spec_accept_metrics": (_i, [_p, _i, _i, _p, _p, _p]),
     "sv_step_graph_create": (_i, [_p, _p]),
@@ -695,12 +700,15 @@ def spec_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens:
                      out_num_accepted: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None,
                      device_error: Optional[torch.Tensor] = None,
-                     _symbol: str = "spec_verify_tree"):
+                     _symbol: str = "spec_verify_tree", _temperatures=None):
     """Verify a draft tree per sequence (temperature 0 = greedy); see
     spec_verify_tree in include/spec_verify.h.
 
     Returns (out_tokens [B, N+1], out_path [B, N+1], num_accepted [B])."""
     lib = require_library()
+    mixed = _temperatures is not None
+    if mixed:
+        temperature = 1.0                  # per-tree temperatures instead
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [B, N+1, V]")
     B, N1, V = target_logits.shape
@@ -726,15 +734,36 @@ def spec_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens:
     _dev(workspace, "workspace", device=dev)
     if device_error is not None:
         _dev(device_error, "device_error", torch.int32, (1,), dev)
-    st = getattr(lib, _symbol)(_ptr(target_logits), _DTYPES[target_logits.dtype],
-                              _ptr(draft_probs if temperature > 0 else None), _ptr(parents),
-                              _ptr(tokens), _ptr(uniforms if temperature > 0 else None),
-                              float(temperature), B, N, V, _ptr(out_tokens), _ptr(out_path),
-                              _ptr(out_num_accepted), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _ptr(device_error),
-                              _stream(dev))
+    head = (_ptr(target_logits), _DTYPES[target_logits.dtype],
+            _ptr(draft_probs if temperature > 0 else None), _ptr(parents), _ptr(tokens),
+            _ptr(uniforms if temperature > 0 else None))
+    tail = (B, N, V, _ptr(out_tokens), _ptr(out_path), _ptr(out_num_accepted), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(device_error), _stream(dev))
+    if mixed:
+        _dev(_temperatures, "temperatures", torch.float32, (B,), dev)
+        st = getattr(lib, _symbol)(*head, _ptr(_temperatures), *tail)
+    else:
+        st = getattr(lib, _symbol)(*head, float(temperature), *tail)
     _check(st, _symbol)
     return out_tokens, out_path, out_num_accepted
+
+
+def spec_verify_tree_mixed(target_logits, parents, tokens, temperatures, draft_probs, uniforms,
+                           **kw):
+    """Verify a mixed batch of draft trees (per-tree temperatures, 0 =
+    greedy); see spec_verify_tree_mixed in include/spec_verify.h.  Keyword
+    arguments and results as spec_verify_tree."""
+    return spec_verify_tree(target_logits, parents, tokens, 1.0, draft_probs, uniforms,
+                            _symbol="spec_verify_tree_mixed", _temperatures=temperatures, **kw)
+
+
+def spec_verify_tree_mixed_early_exit(target_logits, parents, tokens, temperatures,
+                                      draft_probs, uniforms, **kw):
+    """spec_verify_tree_mixed with the walk computing the statistics of the
+    rows it visits only; see spec_verify_tree_mixed_early_exit."""
+    return spec_verify_tree(target_logits, parents, tokens, 1.0, draft_probs, uniforms,
+                            _symbol="spec_verify_tree_mixed_early_exit",
+                            _temperatures=temperatures, **kw)
 
 
 def spec_verify_tree_lq(target_logits: torch.Tensor, drafter_logits: torch.Tensor,

@@ -267,18 +267,24 @@ sv_status verify_lq(const void* target_logits, int logits_dtype, const void* dra
 
 // spec_verify_tree / spec_verify_tree_lq, and their _early_exit forms (lazy:
 // the walk computes the statistics of the rows it visits).
+// temperatures != NULL: per-tree temperatures (spec_verify_tree_mixed*), the
+// scalar temperature unused.
 sv_status tree_dense(const void* target_logits, int logits_dtype, const float* draft_probs,
                      const int32_t* parents, const int32_t* tokens, const float* uniforms,
-                     float temperature, int B, int N, int V, int32_t* out_tokens,
-                     int32_t* out_path, int32_t* out_num_accepted, void* workspace,
-                     size_t workspace_bytes, int32_t* device_error, void* stream, bool lazy) {
+                     float temperature, const float* temperatures, int B, int N, int V,
+                     int32_t* out_tokens, int32_t* out_path, int32_t* out_num_accepted,
+                     void* workspace, size_t workspace_bytes, int32_t* device_error,
+                     void* stream, bool lazy) {
   sv_status st = check_verify_shape(B, N, V);
   if (st != SV_OK) return st;
   if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
-  if (!(temperature >= 0.0f && isfinite(temperature))) return SV_ERR_VALUE;
-  const bool sample = temperature > 0.0f;
-  if (sample && !isfinite((float)(1.4426950408889634 / (double)temperature))) return SV_ERR_VALUE;
+  const bool mixed = temperatures != nullptr;
+  if (!mixed && !(temperature >= 0.0f && isfinite(temperature))) return SV_ERR_VALUE;
+  const bool sample = mixed || temperature > 0.0f;
+  if (!mixed && sample && !isfinite((float)(1.4426950408889634 / (double)temperature)))
+    return SV_ERR_VALUE;
   if (B == 0) return SV_OK;
+  if (mixed && !aligned(temperatures, 4)) return SV_ERR_ALIGN;
   if (!target_logits || !out_tokens || !out_path || !out_num_accepted) return SV_ERR_NULL;
   if (N > 0 && (!parents || !tokens)) return SV_ERR_NULL;
   if (sample && (!draft_probs || !uniforms)) return SV_ERR_NULL;
@@ -301,7 +307,8 @@ sv_status tree_dense(const void* target_logits, int logits_dtype, const float* d
   L.parents = parents;
   L.tokens = tokens;
   L.uniforms = uniforms;
-  L.temperature = temperature;
+  L.temperature = mixed ? 1.0f : temperature;
+  L.temperatures = temperatures;
   L.B = B; L.N = N; L.V = V;
   L.bf16 = logits_dtype == SV_BF16;
   L.vec = (V % 8 == 0) && aligned(target_logits, 16) &&
@@ -604,8 +611,8 @@ SV_API sv_status spec_verify_tree(const void* target_logits, int logits_dtype,
                                   int32_t* out_num_accepted, void* workspace,
                                   size_t workspace_bytes, int32_t* device_error, void* stream) {
   return sv::tree_dense(target_logits, logits_dtype, draft_probs, parents, tokens, uniforms,
-                        temperature, B, N, V, out_tokens, out_path, out_num_accepted, workspace,
-                        workspace_bytes, device_error, stream, false);
+                        temperature, nullptr, B, N, V, out_tokens, out_path, out_num_accepted,
+                        workspace, workspace_bytes, device_error, stream, false);
 }
 
 SV_API sv_status spec_verify_tree_early_exit(const void* target_logits, int logits_dtype,
@@ -617,8 +624,34 @@ SV_API sv_status spec_verify_tree_early_exit(const void* target_logits, int logi
                                              size_t workspace_bytes, int32_t* device_error,
                                              void* stream) {
   return sv::tree_dense(target_logits, logits_dtype, draft_probs, parents, tokens, uniforms,
-                        temperature, B, N, V, out_tokens, out_path, out_num_accepted, workspace,
-                        workspace_bytes, device_error, stream, true);
+                        temperature, nullptr, B, N, V, out_tokens, out_path, out_num_accepted,
+                        workspace, workspace_bytes, device_error, stream, true);
+}
+
+SV_API sv_status spec_verify_tree_mixed(const void* target_logits, int logits_dtype,
+                                        const float* draft_probs, const int32_t* parents,
+                                        const int32_t* tokens, const float* uniforms,
+                                        const float* temperatures, int B, int N, int V,
+                                        int32_t* out_tokens, int32_t* out_path,
+                                        int32_t* out_num_accepted, void* workspace,
+                                        size_t workspace_bytes, int32_t* device_error,
+                                        void* stream) {
+  if (B > 0 && !temperatures) return SV_ERR_NULL;
+  return sv::tree_dense(target_logits, logits_dtype, draft_probs, parents, tokens, uniforms,
+                        1.0f, temperatures, B, N, V, out_tokens, out_path, out_num_accepted,
+                        workspace, workspace_bytes, device_error, stream, false);
+}
+
+SV_API sv_status spec_verify_tree_mixed_early_exit(
+    const void* target_logits, int logits_dtype, const float* draft_probs,
+    const int32_t* parents, const int32_t* tokens, const float* uniforms,
+    const float* temperatures, int B, int N, int V, int32_t* out_tokens, int32_t* out_path,
+    int32_t* out_num_accepted, void* workspace, size_t workspace_bytes, int32_t* device_error,
+    void* stream) {
+  if (B > 0 && !temperatures) return SV_ERR_NULL;
+  return sv::tree_dense(target_logits, logits_dtype, draft_probs, parents, tokens, uniforms,
+                        1.0f, temperatures, B, N, V, out_tokens, out_path, out_num_accepted,
+                        workspace, workspace_bytes, device_error, stream, true);
 }
 
 SV_API sv_status spec_verify_tree_lq(const void* target_logits, int logits_dtype,

@@ -95,6 +95,9 @@ struct TreeLaunch {
   // row statistics computed by the walk for the nodes it visits only
   // (spec_verify_tree*_early_exit), instead of by the row kernel for all
   int lazy = 0;
+  // per-tree temperatures (spec_verify_tree_mixed*): tree b greedy when 0,
+  // else sampled at its own; NULL: `temperature` for every tree
+  const float* temperatures = nullptr;
 };
 
 // The row-statistics partials of a verify workspace: [B][K+1][S] entries.
@@ -105,8 +108,11 @@ struct RowPartials {
 
 int verify_splits(int B, int K, int V);
 RowPartials row_partials(void* workspace, int B, int K, int V);
-hipError_t launch_row_stats(const void* logits, int bf16, int vec, int sample, float c, int B,
-                            int K, int V, void* workspace, int trace_id, hipStream_t stream);
+// Row statistics of B*(K+1) rows into the workspace's partials: greedy,
+// sampled at scale c, or (temperatures != NULL) each sequence by its own rule.
+hipError_t launch_row_stats(const void* logits, int bf16, int vec, int sample, float c,
+                            const float* temperatures, int B, int K, int V, void* workspace,
+                            int trace_id, hipStream_t stream);
 hipError_t launch_tree(const TreeLaunch& L, hipStream_t stream);
 
 // Kernel tracing (per host thread): bracket a launch with events on its stream.

@@ -39,7 +39,7 @@ namespace sv {
 // A greedy walk that computes its rows' statistics itself (LAZY) is a chain
 // of whole-row passes by one workgroup, so it takes the widest workgroup.
 template <int MODE, bool LAZY = false>
-constexpr int tree_threads() { return MODE == SAMPLE ? 512 : (LAZY ? 1024 : 256); }
+constexpr int tree_threads() { return MODE != GREEDY ? 512 : (LAZY ? 1024 : 256); }
 constexpr int kTreeSplits = 16;        // workgroups per row at most (the row kernel's limit)
 
 struct TreeArgs {
@@ -210,7 +210,9 @@ __device__ __forceinline__ double residual_tiles(const LT* zrow, const TreeQ<LT>
 // LAZY: the statistics of a node's row are computed by the walk itself when
 // it reaches the node (one workgroup pass, `slice_stats` over the whole row),
 // so only the rows of the visited nodes are read; otherwise they come from
-// the row kernel's partials of every row.
+// the row kernel's partials of every row.  MIXED: each tree by its own
+// temperature, greedily when it is 0 (or invalid: flagged), as the chain
+// verify treats a mixed batch.
 template <typename LT, int MODE, bool VEC, bool QL = false, bool LAZY = false>
 __global__ __launch_bounds__((tree_threads<MODE, LAZY>())) void tree_walk(TreeArgs A) {
   constexpr int THREADS = tree_threads<MODE, LAZY>();
@@ -243,7 +245,14 @@ __global__ __launch_bounds__((tree_threads<MODE, LAZY>())) void tree_walk(TreeAr
   Partial* Pb = A.partials + (long)b * (N + 1) * S;
   int32_t* out = L.out_tokens + (long)b * (N + 1);
   int32_t* path = L.out_path + (long)b * (N + 1);
-  const float c = A.c;
+  float c = A.c;
+  bool greedy = MODE == GREEDY;
+  if constexpr (MODE == MIXED) {
+    bool bad;
+    c = seq_scale(L.temperatures[b], bad);
+    if (bad && t == 0) flag_error(L.device_error, SV_DEVERR_TEMPERATURE);
+    greedy = c == 0.f;
+  }
   int cur = 0, depth = 0;
   for (;;) {
     float M = -INFINITY;
@@ -251,8 +260,15 @@ __global__ __launch_bounds__((tree_threads<MODE, LAZY>())) void tree_walk(TreeAr
     double s = 0.0;
     if constexpr (LAZY) {
       // statistics of row cur by one pass of the workgroup, then shared
-      const Partial P = slice_stats<LT, MODE, VEC, THREADS>(zb + (long)cur * V, 0,
-                                                            (V + 7) / 8, V, c, sm_f, sm_i, sm_d);
+      const LT* row = zb + (long)cur * V;
+      const long oct = (V + 7) / 8;
+      Partial P;
+      if constexpr (MODE == MIXED) {
+        if (greedy) P = slice_stats<LT, GREEDY, VEC, THREADS>(row, 0, oct, V, 1.f, sm_f, sm_i, sm_d);
+        else P = slice_stats<LT, SAMPLE, VEC, THREADS>(row, 0, oct, V, c, sm_f, sm_i, sm_d);
+      } else {
+        P = slice_stats<LT, MODE, VEC, THREADS>(row, 0, oct, V, c, sm_f, sm_i, sm_d);
+      }
       if (t == 0) s_stat = P;
       __syncthreads();
       M = s_stat.m;
@@ -266,7 +282,7 @@ __global__ __launch_bounds__((tree_threads<MODE, LAZY>())) void tree_walk(TreeAr
 #pragma unroll
       for (int j = 0; j < kTreeSplits; ++j)
         if (j < S) pk[j] = Pb[cur * S + j];
-      if constexpr (MODE == GREEDY) {
+      if (greedy) {
 #pragma unroll
         for (int j = 0; j < kTreeSplits; ++j)
           if (j < S && (j == 0 || pk[j].m > M)) { M = pk[j].m; g = pk[j].g; }
@@ -282,7 +298,7 @@ __global__ __launch_bounds__((tree_threads<MODE, LAZY>())) void tree_walk(TreeAr
     }
     const LT* zrow = zb + (long)cur * V;
     int nxt = -1;
-    if constexpr (MODE == GREEDY) {
+    if (greedy) {
       if (g < 0 || g >= V) g = 0;          // a NaN row: any in-range token
       for (int i = 1; i <= N; ++i)
         if (s_par[i] == cur && s_tok[i] == g) { nxt = i; break; }
@@ -403,16 +419,17 @@ __global__ __launch_bounds__((tree_threads<MODE, LAZY>())) void tree_walk(TreeAr
 hipError_t launch_tree(const TreeLaunch& L, hipStream_t stream) {
   const bool sample = L.temperature > 0.f;
   const float c = sample ? (float)(1.4426950408889634 / (double)L.temperature) : 1.0f;
+  const bool mixed = L.temperatures != nullptr;
   hipError_t err = hipSuccess;
   if (!L.lazy)
-    err = launch_row_stats(L.logits, L.bf16, L.vec, sample, c, L.B, L.N, L.V, L.workspace,
-                           SV_KERNEL_TREE_ROWS, stream);
+    err = launch_row_stats(L.logits, L.bf16, L.vec, sample, c, L.temperatures, L.B, L.N, L.V,
+                           L.workspace, SV_KERNEL_TREE_ROWS, stream);
   if (err != hipSuccess) return err;
   const RowPartials rp = row_partials(L.workspace, L.B, L.N, L.V);
   TreeArgs A{L, static_cast<Partial*>(rp.partials), rp.S, c};
   const dim3 grid((unsigned)L.B);
-  const dim3 block(sample ? tree_threads<SAMPLE>()
-                          : (L.lazy ? tree_threads<GREEDY, true>() : tree_threads<GREEDY>()));
+  const dim3 block(sample || mixed ? tree_threads<SAMPLE>()
+                                   : (L.lazy ? tree_threads<GREEDY, true>() : tree_threads<GREEDY>()));
   const bool ql = sample && L.dlogits != nullptr;
   trace_before(stream, SV_KERNEL_TREE_WALK);
 #define SV_TREE(LT, MODE, QL) \
@@ -426,11 +443,13 @@ hipError_t launch_tree(const TreeLaunch& L, hipStream_t stream) {
     } \
   } while (0)
   if (L.bf16) {
-    if (ql) SV_TREE(uint16_t, SAMPLE, true);
+    if (mixed) SV_TREE(uint16_t, MIXED, false);
+    else if (ql) SV_TREE(uint16_t, SAMPLE, true);
     else if (sample) SV_TREE(uint16_t, SAMPLE, false);
     else SV_TREE(uint16_t, GREEDY, false);
   } else {
-    if (ql) SV_TREE(float, SAMPLE, true);
+    if (mixed) SV_TREE(float, MIXED, false);
+    else if (ql) SV_TREE(float, SAMPLE, true);
     else if (sample) SV_TREE(float, SAMPLE, false);
     else SV_TREE(float, GREEDY, false);
   }

@@ -742,12 +742,13 @@ __global__ __launch_bounds__(kThreads) void verify_locate(DrawArgs A) {
 }
 
 // ----------------------------------------------------------------------------
-hipError_t launch_row_stats(const void* logits, int bf16, int vec, int sample, float c, int B,
-                            int K, int V, void* workspace, int trace_id, hipStream_t stream) {
+hipError_t launch_row_stats(const void* logits, int bf16, int vec, int sample, float c,
+                            const float* temperatures, int B, int K, int V, void* workspace,
+                            int trace_id, hipStream_t stream) {
   const Layout lay = layout(B, K, V);
   RowsArgs R;
   R.logits = logits;
-  R.temperatures = nullptr;
+  R.temperatures = temperatures;
   R.c = c;
   R.K = K; R.V = V; R.S = lay.S;
   R.octets = (V + 7) / 8;
@@ -756,10 +757,12 @@ hipError_t launch_row_stats(const void* logits, int bf16, int vec, int sample, f
   trace_before(stream, trace_id);
 #define SV_ROWS(LT, MODE, VEC) hipLaunchKernelGGL((verify_rows<LT, MODE, VEC>), grid1, block, 0, stream, R)
   if (bf16) {
-    if (sample) { if (vec) SV_ROWS(uint16_t, SAMPLE, true); else SV_ROWS(uint16_t, SAMPLE, false); }
+    if (temperatures) { if (vec) SV_ROWS(uint16_t, MIXED, true); else SV_ROWS(uint16_t, MIXED, false); }
+    else if (sample) { if (vec) SV_ROWS(uint16_t, SAMPLE, true); else SV_ROWS(uint16_t, SAMPLE, false); }
     else { if (vec) SV_ROWS(uint16_t, GREEDY, true); else SV_ROWS(uint16_t, GREEDY, false); }
   } else {
-    if (sample) { if (vec) SV_ROWS(float, SAMPLE, true); else SV_ROWS(float, SAMPLE, false); }
+    if (temperatures) { if (vec) SV_ROWS(float, MIXED, true); else SV_ROWS(float, MIXED, false); }
+    else if (sample) { if (vec) SV_ROWS(float, SAMPLE, true); else SV_ROWS(float, SAMPLE, false); }
     else { if (vec) SV_ROWS(float, GREEDY, true); else SV_ROWS(float, GREEDY, false); }
   }
 #undef SV_ROWS

@@ -458,6 +458,34 @@ SV_API sv_status spec_verify_tree_early_exit(const void* target_logits, int logi
                                              int32_t* out_num_accepted, void* workspace,
                                              size_t workspace_bytes, int32_t* device_error,
                                              void* stream);
+
+/*
+ * Tree verification of a mixed serving batch: tree b is walked greedily when
+ * temperatures[b] = 0 and by rejection sampling at temperatures[b] when it is
+ * > 0, as spec_verify_mixed treats a chain batch ("Project 14", section 架构:
+ * each request with its own sampling settings in one target pass; section
+ * 概念: trees).  Arguments as spec_verify_tree with temperatures [B] fp32 in
+ * place of the scalar temperature; draft_probs and uniforms are required
+ * (the rows of greedy trees are not read).  A temperature that is negative,
+ * NaN, infinite or too small for log2(e)/T to be a finite fp32 sets
+ * SV_DEVERR_TEMPERATURE and walks that tree greedily.  Results equal those
+ * of spec_verify_tree on each tree alone at its temperature.  The
+ * _early_exit form is that of spec_verify_tree_early_exit.
+ */
+SV_API sv_status spec_verify_tree_mixed(const void* target_logits, int logits_dtype,
+                                        const float* draft_probs, const int32_t* parents,
+                                        const int32_t* tokens, const float* uniforms,
+                                        const float* temperatures, int B, int N, int V,
+                                        int32_t* out_tokens, int32_t* out_path,
+                                        int32_t* out_num_accepted, void* workspace,
+                                        size_t workspace_bytes, int32_t* device_error,
+                                        void* stream);
+SV_API sv_status spec_verify_tree_mixed_early_exit(
+    const void* target_logits, int logits_dtype, const float* draft_probs,
+    const int32_t* parents, const int32_t* tokens, const float* uniforms,
+    const float* temperatures, int B, int N, int V, int32_t* out_tokens, int32_t* out_path,
+    int32_t* out_num_accepted, void* workspace, size_t workspace_bytes, int32_t* device_error,
+    void* stream);
 SV_API sv_status spec_verify_tree_lq_early_exit(
     const void* target_logits, int logits_dtype, const void* drafter_logits,
     int64_t n_drafter_rows, const int32_t* drafter_rows, const sv_draft_row* drafter_desc,

@@ -43,7 +43,8 @@ def test_header_declares_the_boundary():
               "spec_verify_noalloc_scratch_bytes", "spec_verify_greedy_early_exit",
               "spec_verify_sample_early_exit", "spec_verify_mixed_early_exit",
               "spec_verify_sample_lq_early_exit", "spec_verify_mixed_lq_early_exit",
-              "spec_verify_tree_early_exit", "spec_verify_tree_lq_early_exit"):
+              "spec_verify_tree_early_exit", "spec_verify_tree_lq_early_exit",
+              "spec_verify_tree_mixed", "spec_verify_tree_mixed_early_exit"):
         assert n in names
 
 
@@ -533,3 +534,21 @@ def test_early_exit_validation(lib):
         assert s(fn, q=FAKE + 2) == EALIGN and s(fn, pd=FAKE + 1) == EALIGN
     assert s("sample", T=0.0) == EVALUE and s("sample", T=float("nan")) == EVALUE
     assert s("mixed", temps=None) == ENULL and s("mixed", temps=FAKE + 2) == EALIGN
+
+
+@pytest.mark.parametrize("fn", ["spec_verify_tree_mixed", "spec_verify_tree_mixed_early_exit"])
+def test_tree_mixed_validation(lib, fn):
+    def tm(logits=FAKE, dtype=1, q=FAKE, par=FAKE, tok=FAKE, u=FAKE, temps=FAKE, B=2, N=6, V=64,
+           out=FAKE, path=FAKE, acc=FAKE, ws=FAKE, wsb=None):
+        if wsb is None:
+            wsb = lib.spec_verify_workspace_bytes(max(B, 1), max(N, 0), max(V, 1))
+        return getattr(lib, fn)(logits, dtype, q, par, tok, u, temps, B, N, V, out, path, acc, ws,
+                                wsb, None, None)
+    assert tm(N=64) == ESHAPE and tm(V=0) == ESHAPE
+    assert tm(dtype=2) == EDTYPE
+    assert tm(temps=None) == ENULL                      # per-tree temperatures required
+    assert tm(B=0, logits=None, q=None, par=None, tok=None, u=None, temps=None, out=None,
+              path=None, acc=None, ws=None, wsb=0) == OK
+    assert tm(q=None) == ENULL and tm(u=None) == ENULL and tm(par=None) == ENULL
+    assert tm(ws=None) == EWS
+    assert tm(temps=FAKE + 2) == EALIGN and tm(q=FAKE + 1) == EALIGN
