@@ -41,9 +41,12 @@ def _resource_usage(src):
 @pytest.mark.skipif(not os.path.exists(_build.HIPCC) and shutil.which("hipcc") is None,
                     reason="hipcc not available")
 def test_kernels_use_no_scratch():
+    from concurrent.futures import ThreadPoolExecutor
     seen = {}
-    for src in _build.sources():
-        seen.update(_resource_usage(src))
+    srcs = _build.sources()
+    with ThreadPoolExecutor(max_workers=max(1, min(len(srcs), os.cpu_count() or 1, 8))) as ex:
+        for usage in ex.map(_resource_usage, srcs):
+            seen.update(usage)
     for name in EXPECTED:
         assert any(name in k for k in seen), f"no kernel named like {name}"
     for k, usage in seen.items():
