@@ -355,7 +355,8 @@ def ingest_trace(trace_csv, bench_log=None):
              "workload, the comparison library's drafter-bytes kernels (`rows_to_f32`, "
              "`write_rows`; 4 calls each), five greedy and five sampled tree verifications (64 "
              "trees of 15 nodes, V=151936 bf16), each also in its early-exit form "
-             "(`tree_walk<…, true>` as the last template argument: no row kernel), one drafter "
+             "(`tree_walk<…, true>` as the last template argument: no row kernel), five mixed "
+             "tree verifications (per-tree temperatures, `tree_walk<…, 2, …>`), one drafter "
              "sampling of one row per tree node "
              "with row descriptors and five tree verifications from those drafter logits, "
              "one pass each of the read-ceiling kernel "
@@ -1377,6 +1378,8 @@ def main():
             for T in (0.0, ts.temperature):
                 sv.spec_verify_tree(tz, tp, tt, T, draft_probs=tq, uniforms=tu)
                 sv.spec_verify_tree_early_exit(tz, tp, tt, T, draft_probs=tq, uniforms=tu)
+            ttemps = up(synth.make_temperatures(ts.B, 62))
+            sv.spec_verify_tree_mixed(tz, tp, tt, ttemps, tq, tu)
         # the same trees with q from drafter logits: node (b, n) drafted from
         # the target row of node n of tree b+1 (distinct rows, so that some
         # children are rejected and the walk makes residual passes)
