@@ -470,7 +470,8 @@ SV_API sv_status spec_verify_tree_early_exit(const void* target_logits, int logi
  * NaN, infinite or too small for log2(e)/T to be a finite fp32 sets
  * SV_DEVERR_TEMPERATURE and walks that tree greedily.  Results equal those
  * of spec_verify_tree on each tree alone at its temperature.  The
- * _early_exit form is that of spec_verify_tree_early_exit.
+ * _early_exit form is that of spec_verify_tree_early_exit.  These take the
+ * dense q; the drafter-logit tree calls take one temperature for the batch.
  */
 SV_API sv_status spec_verify_tree_mixed(const void* target_logits, int logits_dtype,
                                         const float* draft_probs, const int32_t* parents,
