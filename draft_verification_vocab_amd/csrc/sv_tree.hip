@@ -4,7 +4,9 @@
 // logit row per node (row 0 = the root, the last committed token).
 //
 // Row statistics of all B * (N+1) rows come from the verify row kernel (one
-// pass over every logit).  Then one workgroup per sequence walks the tree:
+// pass over every logit), or, in the early-exit form, are computed by the
+// walk for the nodes it visits.  One workgroup per sequence walks the tree
+// (in a mixed batch each tree by its own temperature):
 //   greedy   move to the lowest-index child whose token is the row's argmax;
 //            emit the argmax when none matches;
 //   sampled  test the children of the current node in index order against
