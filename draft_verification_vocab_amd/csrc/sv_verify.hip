@@ -47,11 +47,13 @@ constexpr int kThreads = 256;           // 4 waves
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxSplits = 16;          // workgroups per logit row at most
 constexpr int kTileUnroll = 1;          // draw: tiles per wave per step
+constexpr int kLevelSlots = 64;         // early exit: ranges after the first (<= 7 for K < 64)
 
 // ---------------------------------------------------------------- workspace
-// scan results [B] | tile sums [B][T] | partials [B][K+1][S]
+// scan results [B] | tile sums [B][T] | partials [B][K+1][S] |
+// early-exit range counters [kLevelSlots] and sequence list [B]
 struct Layout {
-  size_t info, tile, partials, total;
+  size_t info, tile, partials, levels, total;
   int S, C, T;
 };
 
@@ -99,6 +101,7 @@ static Layout layout(int B, int K, int V) {
   L.info = off;     off = align256(off + (size_t)B * sizeof(ScanResult));
   L.tile = off;     off = align256(off + (size_t)B * L.T * sizeof(float));
   L.partials = off; off = align256(off + (size_t)B * (K + 1) * L.S * sizeof(Partial));
+  L.levels = off;   off = align256(off + (kLevelSlots + (size_t)B) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -138,7 +141,18 @@ struct ScanArgs {          // what an accept scan reads and writes
   float* out_p_draft;
   int32_t* device_error;
   int prefix_only;         // early exit: rows past the first rejection hold no statistics
+  int* level_counts;       // early exit: the gates' counters [kLevelSlots] and their
+                           // sequence list [B], cleared by the call's last kernel (else null)
 };
+
+// The call's last kernel leaves the early-exit counters and list zero for the
+// next call: workgroup 0 clears the counters, and the thread that `owns`
+// sequence b its list entry.
+__device__ __forceinline__ void clear_level_state(const ScanArgs& A, int b, bool owns) {
+  if (!A.level_counts) return;
+  if (blockIdx.x == 0 && threadIdx.x < kLevelSlots) A.level_counts[threadIdx.x] = 0;
+  if (owns) A.level_counts[kLevelSlots + b] = 0;
+}
 
 struct DrawArgs {
   ScanArgs sc;
@@ -276,8 +290,9 @@ __device__ __forceinline__ void clear_partials(const ScanArgs& A, int b) {
 template <typename LT>
 __global__ __launch_bounds__(kThreads) void verify_accept(ScanArgs A) {
   const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
-  if (b >= A.B) return;
   const int l = lane_id();
+  clear_level_state(A, b, b < A.B && l == 0);
+  if (b >= A.B) return;
   const ScanResult r = accept_scan<LT, GREEDY>(A, b, true, 1.f);
   if (l == 0) A.out_tokens[(long)b * (A.K + 1) + r.a] = r.g_a;
   clear_partials(A, b);
@@ -318,36 +333,41 @@ __device__ __forceinline__ ScanResult draw_scan(const ScanArgs& A, int b, bool w
 // [2,4), [4,8), ...: one launch per position would make every deep position
 // cost a full row pass by a single workgroup (~21 us at V = 151936), while a
 // range reads, for the few sequences still undecided, some rows that turn
-// out not to be needed.  Wave 0 of each workgroup first runs the sequence's
-// accept scan over the statistics written by the earlier launches, with the
-// arithmetic of the final scan, so both take the same decisions: rows are
-// computed iff the scan's first rejection lies at or past k0 (rows from k0
-// on hold no statistics yet, or are being written by this launch, and sit
-// at or past k0, so their lanes cannot move a first rejection that lies
-// before it).  Grid: B * (k1 - k0) * S workgroups.
-template <typename LT, int MODE, bool VEC, bool QL>
-__global__ __launch_bounds__(kThreads) void verify_rows_level(RowsArgs A, ScanArgs sc, int k0,
-                                                              int k1) {
-  __shared__ float sm_f[kWaves];
-  __shared__ int sm_i[kWaves];
-  __shared__ double sm_d[kWaves];
-  __shared__ int s_go;
+// out not to be needed.
+//
+// verify_level_gate (before every range but the first): one wave per
+// sequence runs the accept scan over the statistics written by the earlier
+// launches, with the arithmetic of the final scan, so both take the same
+// decisions, and appends b to the range's list when the first rejection
+// lies at or past k0 (rows from k0 on hold no statistics yet, and sit at or
+// past k0, so their lanes cannot move a first rejection that lies before
+// it).  The list's order follows the atomics; it decides only which
+// workgroup of the range computes which row, not any value.
+template <typename LT, int MODE, bool QL>
+__global__ __launch_bounds__(kThreads) void verify_level_gate(ScanArgs sc, int k0, int* count,
+                                                              int32_t* list) {
+  const int b = blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (b >= sc.B) return;
+  int a;
+  if constexpr (MODE == GREEDY) a = accept_scan<LT, GREEDY>(sc, b, false, 1.f).a;
+  else a = draw_scan<LT, MODE, QL>(sc, b, false, false).a;
+  if (lane_id() == 0 && a >= k0) list[atomicAdd(count, 1)] = b;
+}
 
+// verify_rows_level: the row statistics of one range, for every sequence
+// (the first range, one workgroup per item) or for the gate's list (LISTED:
+// the grid strides over the items, whose count the host does not know at
+// launch).  Work item i is (sequence i / (n S), row k0 + i / S % n, split
+// i % S).  THREADS: the greedy ranges after the first, where few sequences
+// are still undecided and a row pass is bound by one workgroup's loads in
+// flight, take 1024-thread workgroups (a greedy row's maximum and lowest
+// argmax do not depend on how the row is split among threads; a sampled
+// row's sum would, so sampled ranges keep the full call's 256).
+template <typename LT, int MODE, bool VEC, int THREADS>
+__device__ __forceinline__ void level_item(const RowsArgs& A, int b, int k, int s, float* sm_f,
+                                           int* sm_i, double* sm_d) {
   const int S = A.S;
   const long V = A.V;
-  const int n = k1 - k0;
-  const int b = blockIdx.x / (n * S);
-  const int k = k0 + (int)(blockIdx.x / S % n), s = blockIdx.x % S;
-  if (k0 > 0) {
-    if (threadIdx.x < kWave) {
-      int a;
-      if constexpr (MODE == GREEDY) a = accept_scan<LT, GREEDY>(sc, b, false, 1.f).a;
-      else a = draw_scan<LT, MODE, QL>(sc, b, false, false).a;
-      if (threadIdx.x == 0) s_go = a >= k0;
-    }
-    __syncthreads();
-    if (!s_go) return;
-  }
   const long rowi = (long)b * (A.K + 1) + k;
   const LT* row = static_cast<const LT*>(A.logits) + rowi * V;
   const long o_lo = (long)s * A.octets / S, o_hi = (long)(s + 1) * A.octets / S;
@@ -355,12 +375,34 @@ __global__ __launch_bounds__(kThreads) void verify_rows_level(RowsArgs A, ScanAr
   if constexpr (MODE == MIXED) {
     bool bad;
     const float c = seq_scale(A.temperatures[b], bad);
-    if (c == 0.f) P = slice_stats<LT, GREEDY, VEC, kThreads>(row, o_lo, o_hi, V, 1.f, sm_f, sm_i, sm_d);
-    else P = slice_stats<LT, SAMPLE, VEC, kThreads>(row, o_lo, o_hi, V, c, sm_f, sm_i, sm_d);
+    if (c == 0.f) P = slice_stats<LT, GREEDY, VEC, THREADS>(row, o_lo, o_hi, V, 1.f, sm_f, sm_i, sm_d);
+    else P = slice_stats<LT, SAMPLE, VEC, THREADS>(row, o_lo, o_hi, V, c, sm_f, sm_i, sm_d);
   } else {
-    P = slice_stats<LT, MODE, VEC, kThreads>(row, o_lo, o_hi, V, A.c, sm_f, sm_i, sm_d);
+    P = slice_stats<LT, MODE, VEC, THREADS>(row, o_lo, o_hi, V, A.c, sm_f, sm_i, sm_d);
   }
   if (threadIdx.x == 0) A.partials[rowi * S + s] = P;   // read by the next launches
+}
+
+template <typename LT, int MODE, bool VEC, bool LISTED, int THREADS = kThreads>
+__global__ __launch_bounds__(THREADS) void verify_rows_level(RowsArgs A, int k0, int k1,
+                                                             const int* count,
+                                                             const int32_t* list) {
+  __shared__ float sm_f[THREADS / kWave];
+  __shared__ int sm_i[THREADS / kWave];
+  __shared__ double sm_d[THREADS / kWave];
+  const int S = A.S;
+  const int n = k1 - k0;
+  if constexpr (!LISTED) {
+    const int i = blockIdx.x;
+    level_item<LT, MODE, VEC, THREADS>(A, i / (n * S), k0 + i / S % n, i % S, sm_f, sm_i, sm_d);
+  } else {
+    const int items = *count * n * S;          // written by the gate
+    for (int i = blockIdx.x; i < items; i += gridDim.x) {
+      level_item<LT, MODE, VEC, THREADS>(A, list[i / (n * S)], k0 + i / S % n, i % S, sm_f, sm_i,
+                                         sm_d);
+      __syncthreads();                         // the next item reuses the shared arrays
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -657,6 +699,7 @@ __global__ __launch_bounds__(THREADS) void verify_draw(DrawArgs A) {
   const int b = blockIdx.x / C, cidx = blockIdx.x % C;
   const bool whole = C == 1;
   const long V = A.sc.V;
+  clear_level_state(A.sc, b, cidx == 0 && threadIdx.x == 0);
   if (threadIdx.x < kWave) {
     const ScanResult r = draw_scan<LT, MODE, QL>(A.sc, b, cidx == 0, !whole);
     if (whole) clear_partials(A.sc, b);
@@ -809,6 +852,7 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   sc.device_error = L.device_error;
   sc.info = reinterpret_cast<ScanResult*>(ws + lay.info);
   sc.prefix_only = L.early_exit;
+  sc.level_counts = L.early_exit ? reinterpret_cast<int*>(ws + lay.levels) : nullptr;
 
 #define SV_BY_MODE(M, LT) \
   do { \
@@ -818,21 +862,46 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   } while (0)
   hipError_t err = hipSuccess;
   if (L.early_exit) {
-    // draft positions [0,1), [1,2), [2,4), [4,8), ...; each launch skips the
-    // sequences already decided
+    // draft positions [0,1), [1,2), [2,4), [4,8), ...; before each range but
+    // the first a gate lists the sequences still undecided
+    int* counts = sc.level_counts;
+    int32_t* list = reinterpret_cast<int32_t*>(counts + kLevelSlots);
+    const dim3 grid_gate((unsigned)((L.B + kWaves - 1) / kWaves));
+#define SV_GATE(LT, MODE) \
+  do { \
+    if (MODE != GREEDY && ql) hipLaunchKernelGGL((verify_level_gate<LT, MODE, true>), grid_gate, block, 0, stream, sc, k0, cnt, list); \
+    else hipLaunchKernelGGL((verify_level_gate<LT, MODE, false>), grid_gate, block, 0, stream, sc, k0, cnt, list); \
+  } while (0)
 #define SV_LEVEL(LT, MODE) \
   do { \
-    if (MODE != GREEDY && ql) { \
-      if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, true>), gridl, block, 0, stream, R, sc, k0, k1); \
-      else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, true>), gridl, block, 0, stream, R, sc, k0, k1); \
+    if (k0 == 0) { \
+      if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, false>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
+      else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, false>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
+    } else if (MODE == GREEDY) { \
+      const dim3 wide(4 * kThreads); \
+      if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, GREEDY, true, true, 4 * kThreads>), gridl, wide, 0, stream, R, k0, k1, cnt, list); \
+      else hipLaunchKernelGGL((verify_rows_level<LT, GREEDY, false, true, 4 * kThreads>), gridl, wide, 0, stream, R, k0, k1, cnt, list); \
     } else { \
-      if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, false>), gridl, block, 0, stream, R, sc, k0, k1); \
-      else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, false>), gridl, block, 0, stream, R, sc, k0, k1); \
+      if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, true>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
+      else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, true>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
     } \
   } while (0)
-    for (int k0 = 0; k0 <= L.K && err == hipSuccess;) {
+    for (int k0 = 0, level = 0; k0 <= L.K && err == hipSuccess; ++level) {
       const int k1 = k0 == 0 ? 1 : (2 * k0 < L.K + 1 ? 2 * k0 : L.K + 1);
-      const dim3 gridl((unsigned)((long)L.B * (k1 - k0) * lay.S));
+      int* cnt = k0 == 0 ? nullptr : counts + (level - 1);
+      if (k0 > 0) {
+        trace_before(stream, rows_id);
+        if (L.bf16) SV_BY_MODE(SV_GATE, uint16_t);
+        else SV_BY_MODE(SV_GATE, float);
+        err = hipGetLastError();
+        trace_after(stream, rows_id);
+        if (err != hipSuccess) break;
+      }
+      // the first range: one workgroup per item; later ones: at most about
+      // two rounds of resident workgroups, striding over the listed items
+      const long all = (long)L.B * (k1 - k0) * lay.S;
+      const long cap = mode == GREEDY ? 512 : 2048;
+      const dim3 gridl((unsigned)(k0 == 0 || all < cap ? all : cap));
       trace_before(stream, rows_id);
       if (L.bf16) SV_BY_MODE(SV_LEVEL, uint16_t);
       else SV_BY_MODE(SV_LEVEL, float);
@@ -841,6 +910,7 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
       k0 = k1;
     }
 #undef SV_LEVEL
+#undef SV_GATE
   } else {
     const dim3 grid1((unsigned)((long)L.B * (L.K + 1) * lay.S));
     trace_before(stream, rows_id);

@@ -15,7 +15,7 @@ import pytest
 
 from draft_verification_vocab_amd import _build
 
-EXPECTED = ("verify_rows", "verify_accept", "verify_draw", "verify_locate",
+EXPECTED = ("verify_rows", "verify_rows_level", "verify_accept", "verify_draw", "verify_locate",
             "draft_sample_kernel", "build_kernel", "tree_walk", "accept_metrics_kernel")
 
 
