@@ -55,6 +55,7 @@ constexpr int kLevelSlots = 64;         // early exit: ranges after the first (<
 struct Layout {
   size_t info, tile, partials, levels, total;
   int S, C, T;
+  int Sg;            // splits of the greedy early-exit form (partials sized for max(S, Sg))
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -67,6 +68,20 @@ int verify_splits(int B, int K, int V) {
   long cap = octets / 256;
   if (s > cap) s = cap;
   return s < 1 ? 1 : (int)s;
+}
+
+// Splits per row of the greedy early-exit form: at least as many as the full
+// call's, and enough that the few rows of a later range still spread over
+// the chip (about 4096 workgroups for the first range).  A greedy row's
+// maximum and lowest argmax do not depend on the split, so its outputs are
+// those of the full call.
+static int greedy_ee_splits(int B, int K, int V) {
+  const int S = verify_splits(B, K, V);
+  long s = (4096 + (long)B - 1) / (B > 0 ? B : 1);
+  if (s > kMaxSplits) s = kMaxSplits;
+  const long cap = ((long)V + 7) / 8 / 256;
+  if (s > cap) s = cap;
+  return s > S ? (int)s : S;
 }
 
 // Draw workgroups per sequence (for the batches below 256 sequences, and
@@ -95,12 +110,13 @@ static int draw_chunks(int B, int V, bool mixed = false) {
 static Layout layout(int B, int K, int V) {
   Layout L;
   L.S = verify_splits(B, K, V);
+  L.Sg = greedy_ee_splits(B, K, V);
   L.C = draw_chunks(B, V);
   L.T = (V + kTileElems - 1) / kTileElems;
   size_t off = 0;
   L.info = off;     off = align256(off + (size_t)B * sizeof(ScanResult));
   L.tile = off;     off = align256(off + (size_t)B * L.T * sizeof(float));
-  L.partials = off; off = align256(off + (size_t)B * (K + 1) * L.S * sizeof(Partial));
+  L.partials = off; off = align256(off + (size_t)B * (K + 1) * (L.S > L.Sg ? L.S : L.Sg) * sizeof(Partial));
   L.levels = off;   off = align256(off + (kLevelSlots + (size_t)B) * sizeof(int32_t));
   L.total = off;
   return L;
@@ -358,11 +374,10 @@ __global__ __launch_bounds__(kThreads) void verify_level_gate(ScanArgs sc, int k
 // (the first range, one workgroup per item) or for the gate's list (LISTED:
 // the grid strides over the items, whose count the host does not know at
 // launch).  Work item i is (sequence i / (n S), row k0 + i / S % n, split
-// i % S).  THREADS: the greedy ranges after the first, where few sequences
-// are still undecided and a row pass is bound by one workgroup's loads in
-// flight, take 1024-thread workgroups (a greedy row's maximum and lowest
-// argmax do not depend on how the row is split among threads; a sampled
-// row's sum would, so sampled ranges keep the full call's 256).
+// i % S).  The greedy form splits rows finer than the full call (S from
+// greedy_ee_splits), so that the few rows of a later range spread over more
+// workgroups; a sampled row keeps the full call's split, on which its sum's
+// rounding depends.
 template <typename LT, int MODE, bool VEC, int THREADS>
 __device__ __forceinline__ void level_item(const RowsArgs& A, int b, int k, int s, float* sm_f,
                                            int* sm_i, double* sm_d) {
@@ -383,22 +398,22 @@ __device__ __forceinline__ void level_item(const RowsArgs& A, int b, int k, int 
   if (threadIdx.x == 0) A.partials[rowi * S + s] = P;   // read by the next launches
 }
 
-template <typename LT, int MODE, bool VEC, bool LISTED, int THREADS = kThreads>
-__global__ __launch_bounds__(THREADS) void verify_rows_level(RowsArgs A, int k0, int k1,
-                                                             const int* count,
-                                                             const int32_t* list) {
-  __shared__ float sm_f[THREADS / kWave];
-  __shared__ int sm_i[THREADS / kWave];
-  __shared__ double sm_d[THREADS / kWave];
+template <typename LT, int MODE, bool VEC, bool LISTED>
+__global__ __launch_bounds__(kThreads) void verify_rows_level(RowsArgs A, int k0, int k1,
+                                                            const int* count,
+                                                            const int32_t* list) {
+  __shared__ float sm_f[kWaves];
+  __shared__ int sm_i[kWaves];
+  __shared__ double sm_d[kWaves];
   const int S = A.S;
   const int n = k1 - k0;
   if constexpr (!LISTED) {
     const int i = blockIdx.x;
-    level_item<LT, MODE, VEC, THREADS>(A, i / (n * S), k0 + i / S % n, i % S, sm_f, sm_i, sm_d);
+    level_item<LT, MODE, VEC, kThreads>(A, i / (n * S), k0 + i / S % n, i % S, sm_f, sm_i, sm_d);
   } else {
     const int items = *count * n * S;          // written by the gate
     for (int i = blockIdx.x; i < items; i += gridDim.x) {
-      level_item<LT, MODE, VEC, THREADS>(A, list[i / (n * S)], k0 + i / S % n, i % S, sm_f, sm_i,
+      level_item<LT, MODE, VEC, kThreads>(A, list[i / (n * S)], k0 + i / S % n, i % S, sm_f, sm_i,
                                          sm_d);
       __syncthreads();                         // the next item reuses the shared arrays
     }
@@ -824,11 +839,13 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   const int rows_id = mode == MIXED ? SV_KERNEL_VERIFY_MIXED_ROWS
                     : mode == SAMPLE ? SV_KERNEL_VERIFY_SAMPLE_ROWS : SV_KERNEL_VERIFY_GREEDY_ROWS;
 
+  // the greedy early-exit form splits rows finer than the full call
+  const int S = L.early_exit && mode == GREEDY ? lay.Sg : lay.S;
   RowsArgs R;
   R.logits = L.logits;
   R.temperatures = L.temperatures;
   R.c = c;
-  R.K = L.K; R.V = L.V; R.S = lay.S;
+  R.K = L.K; R.V = L.V; R.S = S;
   R.octets = (L.V + 7) / 8;
   R.partials = partials;
 
@@ -844,7 +861,7 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   sc.draft_tokens = L.draft_tokens;
   sc.uniforms = L.uniforms;
   sc.c = c;
-  sc.B = L.B; sc.K = L.K; sc.V = L.V; sc.S = lay.S;
+  sc.B = L.B; sc.K = L.K; sc.V = L.V; sc.S = S;
   sc.partials = partials;
   sc.out_tokens = L.out_tokens;
   sc.out_num_accepted = L.out_num_accepted;
@@ -877,10 +894,6 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
     if (k0 == 0) { \
       if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, false>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
       else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, false>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
-    } else if (MODE == GREEDY) { \
-      const dim3 wide(4 * kThreads); \
-      if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, GREEDY, true, true, 4 * kThreads>), gridl, wide, 0, stream, R, k0, k1, cnt, list); \
-      else hipLaunchKernelGGL((verify_rows_level<LT, GREEDY, false, true, 4 * kThreads>), gridl, wide, 0, stream, R, k0, k1, cnt, list); \
     } else { \
       if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, true>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
       else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, true>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
@@ -899,8 +912,8 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
       }
       // the first range: one workgroup per item; later ones: at most about
       // two rounds of resident workgroups, striding over the listed items
-      const long all = (long)L.B * (k1 - k0) * lay.S;
-      const long cap = mode == GREEDY ? 512 : 2048;
+      const long all = (long)L.B * (k1 - k0) * S;
+      const long cap = 2048;
       const dim3 gridl((unsigned)(k0 == 0 || all < cap ? all : cap));
       trace_before(stream, rows_id);
       if (L.bf16) SV_BY_MODE(SV_LEVEL, uint16_t);

@@ -283,16 +283,19 @@ SV_API sv_status spec_verify_mixed(const void* target_logits, int logits_dtype,
  * the sequence's outputs.  These forms compute row statistics over the
  * draft positions in ranges [0,1), [1,2), [2,4), [4,8), ... (one launch
  * each), a range only for the sequences whose drafts before it were all
- * accepted, then run the usual accept scan and draw: a sequence that
- * accepts a drafts has at most 2a+1 of its K+1 logit rows read (all of them
- * only when a range reaches past its first rejection), at the cost of about
- * log2(K+1) more launches.  Arguments, validation, workspace and device
+ * accepted (a gate kernel before each range but the first lists them),
+ * then run the usual accept scan and draw: a sequence that accepts a drafts
+ * has at most 2a+1 of its K+1 logit rows read (all of them only when a
+ * range reaches past its first rejection), at the cost of about
+ * 2 log2(K+1) more launches.  Arguments, validation, workspace and device
  * flags are those of the corresponding call; out_tokens and
- * out_num_accepted are identical to its outputs bit for bit (the row
- * statistics are computed by the same arithmetic).  out_draft_target_prob
+ * out_num_accepted are identical to its outputs bit for bit (a sampled
+ * row's statistics are computed by the same arithmetic; a greedy row's
+ * maximum and lowest argmax do not depend on how the row is split, and the
+ * greedy form splits rows finer).  out_draft_target_prob
  * [b][k] equals the full call's value for k <= num_accepted[b] and is 0
- * past it.  The launches per call are the row-statistics kernels of the
- * ranges, then the kernels that follow them in the full call.  The ranges
+ * past it.  The launches per call are the gates and row-statistics kernels
+ * of the ranges, then the kernels that follow them in the full call.  The ranges
  * are dependent launches: for small batches, bound by latency, these forms
  * are slower than the full calls; they pay for large batches, bound by the
  * bytes of the logits.
