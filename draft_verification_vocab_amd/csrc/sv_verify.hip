@@ -47,7 +47,15 @@ constexpr int kThreads = 256;           // 4 waves
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxSplits = 16;          // workgroups per logit row at most
 constexpr int kTileUnroll = 1;          // draw: tiles per wave per step
-constexpr int kLevelSlots = 64;         // early exit: ranges after the first (<= 7 for K < 64)
+constexpr int kLevelSlots = 64;         // early exit: ranges after the first (<= 6 for K < 64)
+// Early exit: gate kernels from these batch sizes on (below, ranges with the
+// scan in every workgroup).  GPU time per call at K = 7, V = 151936 bf16,
+// inline against listed: greedy 30.5 / 34.5 us at B = 64 (V = 201088), 39.7 /
+// 36.8 at B = 128, 81.6 / 49.0 at B = 256; sampled 63.6 / 68.9 at B = 64,
+// 84.6 / 91.1 at B = 128, 125.1 / 125.2 at B = 256, 187.8 / 181.5 at B = 512,
+// 326.7 / 312.1 at B = 1024 (mixed batches alike).
+constexpr int kListedMinBatchGreedy = 128;
+constexpr int kListedMinBatchSampled = 512;
 
 // ---------------------------------------------------------------- workspace
 // scan results [B] | tile sums [B][T] | partials [B][K+1][S] |
@@ -370,14 +378,20 @@ __global__ __launch_bounds__(kThreads) void verify_level_gate(ScanArgs sc, int k
   if (lane_id() == 0 && a >= k0) list[atomicAdd(count, 1)] = b;
 }
 
-// verify_rows_level: the row statistics of one range, for every sequence
-// (the first range, one workgroup per item) or for the gate's list (LISTED:
-// the grid strides over the items, whose count the host does not know at
-// launch).  Work item i is (sequence i / (n S), row k0 + i / S % n, split
-// i % S).  The greedy form splits rows finer than the full call (S from
+// verify_rows_level: the row statistics of one range.  Work item i is
+// (sequence i / (n S), row k0 + i / S % n, split i % S), over
+//   kAllSeqs  every sequence, one workgroup per item (the first range);
+//   kListed   the gate's list: the grid strides over the items, whose count
+//             the host does not know at launch;
+//   kInline   every sequence, one workgroup per item, whose wave 0 first runs
+//             the gate's scan itself and returns when the sequence is decided
+//             (small batches: one launch per range instead of two, at the
+//             cost of a scan in every workgroup of the range).
+// Batches of many sequences take kListed with finer greedy splits (S from
 // greedy_ee_splits), so that the few rows of a later range spread over more
 // workgroups; a sampled row keeps the full call's split, on which its sum's
 // rounding depends.
+constexpr int kAllSeqs = 0, kListed = 1, kInline = 2;
 template <typename LT, int MODE, bool VEC, int THREADS>
 __device__ __forceinline__ void level_item(const RowsArgs& A, int b, int k, int s, float* sm_f,
                                            int* sm_i, double* sm_d) {
@@ -398,18 +412,30 @@ __device__ __forceinline__ void level_item(const RowsArgs& A, int b, int k, int 
   if (threadIdx.x == 0) A.partials[rowi * S + s] = P;   // read by the next launches
 }
 
-template <typename LT, int MODE, bool VEC, bool LISTED>
-__global__ __launch_bounds__(kThreads) void verify_rows_level(RowsArgs A, int k0, int k1,
-                                                            const int* count,
+template <typename LT, int MODE, bool VEC, int FORM, bool QL = false>
+__global__ __launch_bounds__(kThreads) void verify_rows_level(RowsArgs A, ScanArgs sc, int k0,
+                                                            int k1, const int* count,
                                                             const int32_t* list) {
   __shared__ float sm_f[kWaves];
   __shared__ int sm_i[kWaves];
   __shared__ double sm_d[kWaves];
   const int S = A.S;
   const int n = k1 - k0;
-  if constexpr (!LISTED) {
+  if constexpr (FORM != kListed) {
     const int i = blockIdx.x;
-    level_item<LT, MODE, VEC, kThreads>(A, i / (n * S), k0 + i / S % n, i % S, sm_f, sm_i, sm_d);
+    const int b = i / (n * S);
+    if constexpr (FORM == kInline) {
+      __shared__ int s_go;
+      if (threadIdx.x < kWave) {
+        int a;
+        if constexpr (MODE == GREEDY) a = accept_scan<LT, GREEDY>(sc, b, false, 1.f).a;
+        else a = draw_scan<LT, MODE, QL>(sc, b, false, false).a;
+        if (threadIdx.x == 0) s_go = a >= k0;
+      }
+      __syncthreads();
+      if (!s_go) return;
+    }
+    level_item<LT, MODE, VEC, kThreads>(A, b, k0 + i / S % n, i % S, sm_f, sm_i, sm_d);
   } else {
     const int items = *count * n * S;          // written by the gate
     for (int i = blockIdx.x; i < items; i += gridDim.x) {
@@ -839,8 +865,12 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
   const int rows_id = mode == MIXED ? SV_KERNEL_VERIFY_MIXED_ROWS
                     : mode == SAMPLE ? SV_KERNEL_VERIFY_SAMPLE_ROWS : SV_KERNEL_VERIFY_GREEDY_ROWS;
 
-  // the greedy early-exit form splits rows finer than the full call
-  const int S = L.early_exit && mode == GREEDY ? lay.Sg : lay.S;
+  // early exit: gate kernels and listed ranges for large batches (the
+  // greedy form then splits rows finer than the full call), ranges that run
+  // the gate's scan in every workgroup below
+  const bool listed =
+      L.early_exit && L.B >= (mode == GREEDY ? kListedMinBatchGreedy : kListedMinBatchSampled);
+  const int S = listed && mode == GREEDY ? lay.Sg : lay.S;
   RowsArgs R;
   R.logits = L.logits;
   R.temperatures = L.temperatures;
@@ -889,20 +919,22 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
     if (MODE != GREEDY && ql) hipLaunchKernelGGL((verify_level_gate<LT, MODE, true>), grid_gate, block, 0, stream, sc, k0, cnt, list); \
     else hipLaunchKernelGGL((verify_level_gate<LT, MODE, false>), grid_gate, block, 0, stream, sc, k0, cnt, list); \
   } while (0)
+#define SV_LEVEL_FORM(LT, MODE, FORM, QL) \
+  do { \
+    if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, FORM, QL>), gridl, block, 0, stream, R, sc, k0, k1, cnt, list); \
+    else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, FORM, QL>), gridl, block, 0, stream, R, sc, k0, k1, cnt, list); \
+  } while (0)
 #define SV_LEVEL(LT, MODE) \
   do { \
-    if (k0 == 0) { \
-      if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, false>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
-      else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, false>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
-    } else { \
-      if (L.vec) hipLaunchKernelGGL((verify_rows_level<LT, MODE, true, true>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
-      else hipLaunchKernelGGL((verify_rows_level<LT, MODE, false, true>), gridl, block, 0, stream, R, k0, k1, cnt, list); \
-    } \
+    if (k0 == 0) SV_LEVEL_FORM(LT, MODE, kAllSeqs, false); \
+    else if (listed) SV_LEVEL_FORM(LT, MODE, kListed, false); \
+    else if (MODE != GREEDY && ql) SV_LEVEL_FORM(LT, MODE, kInline, true); \
+    else SV_LEVEL_FORM(LT, MODE, kInline, false); \
   } while (0)
     for (int k0 = 0, level = 0; k0 <= L.K && err == hipSuccess; ++level) {
       const int k1 = k0 == 0 ? 1 : (2 * k0 < L.K + 1 ? 2 * k0 : L.K + 1);
       int* cnt = k0 == 0 ? nullptr : counts + (level - 1);
-      if (k0 > 0) {
+      if (k0 > 0 && listed) {
         trace_before(stream, rows_id);
         if (L.bf16) SV_BY_MODE(SV_GATE, uint16_t);
         else SV_BY_MODE(SV_GATE, float);
@@ -914,7 +946,7 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
       // two rounds of resident workgroups, striding over the listed items
       const long all = (long)L.B * (k1 - k0) * S;
       const long cap = 2048;
-      const dim3 gridl((unsigned)(k0 == 0 || all < cap ? all : cap));
+      const dim3 gridl((unsigned)(!listed || k0 == 0 || all < cap ? all : cap));
       trace_before(stream, rows_id);
       if (L.bf16) SV_BY_MODE(SV_LEVEL, uint16_t);
       else SV_BY_MODE(SV_LEVEL, float);
@@ -923,6 +955,7 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
       k0 = k1;
     }
 #undef SV_LEVEL
+#undef SV_LEVEL_FORM
 #undef SV_GATE
   } else {
     const dim3 grid1((unsigned)((long)L.B * (L.K + 1) * lay.S));

@@ -101,6 +101,18 @@ def test_ragged_shapes(gpu, dtype, B, K, V):
     _compare(gpu, logits, dtype, q, d, u, 0.8, synth.make_temperatures(B, 47))
 
 
+@pytest.mark.parametrize("dtype,B,K,V", [("bf16", 640, 7, 5003), ("f32", 520, 15, 2048),
+                                         ("bf16", 130, 5, 3001)])
+def test_gate_kernels(gpu, dtype, B, K, V):
+    """Batches large enough for the gate kernels and listed ranges (greedy
+    from 128 sequences, sampled and mixed from 512), with the greedy form's
+    finer row splits, on tie-heavy rows: identical to the full calls, and the
+    workspace (counters and list included) left zero."""
+    rng = np.random.default_rng(B * 7 + K + V)
+    logits, q, d, u = _random_case(rng, B, K, V, dtype, T=0.8, tie_heavy=True)
+    _compare(gpu, logits, dtype, q, d, u, 0.8, synth.make_temperatures(B, 50))
+
+
 def test_all_accepted_and_first_rejected(gpu):
     rng = np.random.default_rng(302)
     B, K, V = 12, 7, 5000
@@ -160,7 +172,7 @@ def test_sample_matches_oracle(gpu):
 
 
 @pytest.mark.parametrize("dtype,B,K,V", [("bf16", 40, 7, 151936), ("f32", 9, 5, 4099),
-                                         ("bf16", 300, 3, 40000)])
+                                         ("bf16", 300, 3, 40000), ("bf16", 520, 3, 3000)])
 def test_drafter_logit_forms(gpu, dtype, B, K, V):
     """spec_verify_sample_lq_early_exit and spec_verify_mixed_lq_early_exit
     against the full drafter-logit calls on the same drafting (drafter rows
