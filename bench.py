@@ -348,7 +348,8 @@ def ingest_trace(trace_csv, bench_log=None):
              "a mixed verify each followed by the build, the drafter sampling with dense q and with "
              "row descriptors, the verify from drafter logits, the drafter sampling at per-sequence "
              "temperatures with row descriptors, the mixed verify from drafter logits, the "
-             "early-exit sampled and greedy verify (`verify_rows_level`, four launches each) and "
+             "early-exit sampled and greedy verify (`verify_rows_level`, four ranges each, the "
+             "last three after a `verify_level_gate`) and "
              "the acceptance metrics; then the "
              "fused build and the two-kernel build of the comparison library (`meta_kernel`, "
              "`copy_kernel`) five times each on the same verify outputs and at the B=64 H=2880 build "
