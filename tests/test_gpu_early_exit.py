@@ -233,3 +233,57 @@ def test_max_batch(gpu):
         d = rng.integers(0, V, size=(B, K)).astype(np.int32)
         u = rng.random((B, K + 1), dtype=np.float32)
         _compare(gpu, z, "f32", q, d, u, 1.0)
+
+
+def test_gate_kernels_in_a_captured_graph(gpu):
+    """The early-exit calls with gate kernels (B = 520: greedy, sampled and
+    mixed) captured in one torch graph and replayed on new uniforms and
+    drafts, with the library's eager calls between replays: every replay
+    equals the eager full calls on its inputs (p_k(d_k) up to the first
+    rejection), and leaves the workspaces zero."""
+    B, K, V = 520, 5, 3001
+    rng = np.random.default_rng(77)
+    logits, q, d, u = _random_case(rng, B, K, V, "bf16", T=0.8)
+    temps = dev(synth.make_temperatures(B, 51))
+    z, qd, dd, ud = dev(logits), dev(q), dev(d), dev(u)
+    ws = [_ws(gpu, B, K, V) for _ in range(3)]
+    outs = [(torch.empty((B, K + 1), dtype=torch.int32, device=DEV),
+             torch.empty((B,), dtype=torch.int32, device=DEV),
+             torch.empty((B, K), dtype=torch.float32, device=DEV)) for _ in range(3)]
+
+    def calls():
+        gpu.spec_verify_greedy_early_exit(z, dd, out_tokens=outs[0][0], out_num_accepted=outs[0][1],
+                                          workspace=ws[0])
+        gpu.spec_verify_sample_early_exit(z, qd, dd, ud, 0.8, out_tokens=outs[1][0],
+                                          out_num_accepted=outs[1][1],
+                                          out_draft_target_prob=outs[1][2], workspace=ws[1])
+        gpu.spec_verify_mixed_early_exit(z, qd, dd, ud, temps, out_tokens=outs[2][0],
+                                         out_num_accepted=outs[2][1],
+                                         out_draft_target_prob=outs[2][2], workspace=ws[2])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        d_new = d.copy()
+        d_new[:, rep % K] = rng.integers(0, V, size=B)
+        dd.copy_(dev(d_new))
+        ud.copy_(dev(rng.random((B, K + 1), dtype=np.float32)))
+        g.replay()
+        torch.cuda.synchronize()
+        full = (gpu.spec_verify_greedy(z, dd),
+                gpu.spec_verify_sample(z, qd, dd, ud, 0.8, want_draft_target_prob=True),
+                gpu.spec_verify_mixed(z, qd, dd, ud, temps, want_draft_target_prob=True))
+        torch.cuda.synchronize()
+        assert torch.equal(full[0][0], outs[0][0]) and torch.equal(full[0][1], outs[0][1]), rep
+        _prefix_equal(full[1], outs[1])
+        _prefix_equal(full[2], outs[2])
+        for w in ws:
+            assert int(w.count_nonzero().item()) == 0, rep
+    del g
