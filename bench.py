@@ -370,11 +370,13 @@ def ingest_trace(trace_csv, bench_log=None):
     for (name, grid), v in rows:
         lines.append(f"| `{name}` | {grid} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | "
                      f"{max(v):.1f} |")
-    dom = [v for (name, grid), v in per.items()
-           if "verify_rows<unsigned short, 1, true>" in name and grid == 2097152]
+    # the sampled row kernel of the 8192-row batch: its largest grid
+    dom = sorted(((grid, v) for (name, grid), v in per.items()
+                  if "verify_rows<unsigned short, 1, true>" in name), key=lambda gv: -gv[0])
     if dom:
+        grid, v = dom[0]
         lines.append(f"\nDominant kernel (`verify_rows<unsigned short, 1, true>`, the 8192-row fused "
-                     f"batch): {sum(dom[0]) / len(dom[0]):.1f} µs average over {len(dom[0])} "
+                     f"batch, grid {grid}): {sum(v) / len(v):.1f} µs average over {len(v)} "
                      "dispatches (sampled verify and verify from drafter logits).")
     if bench_log:
         res = json.loads([ln for ln in open(bench_log) if ln.startswith("{")][-1])
