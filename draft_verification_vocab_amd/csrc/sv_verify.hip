@@ -942,8 +942,9 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
         trace_after(stream, rows_id);
         if (err != hipSuccess) break;
       }
-      // the first range: one workgroup per item; later ones: at most about
-      // two rounds of resident workgroups, striding over the listed items
+      // the first range and the inline ranges: one workgroup per item; the
+      // listed ranges: at most 2048 workgroups (about two rounds of resident
+      // ones), striding over the listed items
       const long all = (long)L.B * (k1 - k0) * S;
       const long cap = 2048;
       const dim3 gridl((unsigned)(!listed || k0 == 0 || all < cap ? all : cap));
