@@ -381,8 +381,11 @@ __global__ __launch_bounds__(kThreads) void verify_level_gate(ScanArgs sc, int k
 // verify_rows_level: the row statistics of one range.  Work item i is
 // (sequence i / (n S), row k0 + i / S % n, split i % S), over
 //   kAllSeqs  every sequence, one workgroup per item (the first range);
-//   kListed   the gate's list: the grid strides over the items, whose count
-//             the host does not know at launch;
+//   kListed   the gate's list: the grid covers every sequence, as the host
+//             does not know the list's length at launch, and a workgroup
+//             past the listed items returns at once (measured 2-3 us faster
+//             per sampled call than a grid of at most 2048 workgroups
+//             striding over the items, whose loop cost ~30 VGPRs);
 //   kInline   every sequence, one workgroup per item, whose wave 0 first runs
 //             the gate's scan itself and returns when the sequence is decided
 //             (small batches: one launch per range instead of two, at the
@@ -438,11 +441,10 @@ __global__ __launch_bounds__(kThreads) void verify_rows_level(RowsArgs A, ScanAr
     level_item<LT, MODE, VEC, kThreads>(A, b, k0 + i / S % n, i % S, sm_f, sm_i, sm_d);
   } else {
     const int items = *count * n * S;          // written by the gate
-    for (int i = blockIdx.x; i < items; i += gridDim.x) {
-      level_item<LT, MODE, VEC, kThreads>(A, list[i / (n * S)], k0 + i / S % n, i % S, sm_f, sm_i,
-                                         sm_d);
-      __syncthreads();                         // the next item reuses the shared arrays
-    }
+    const int i = blockIdx.x;
+    if (i >= items) return;
+    level_item<LT, MODE, VEC, kThreads>(A, list[i / (n * S)], k0 + i / S % n, i % S, sm_f, sm_i,
+                                       sm_d);
   }
 }
 
@@ -942,12 +944,9 @@ hipError_t launch_verify(const VerifyLaunch& L, hipStream_t stream) {
         trace_after(stream, rows_id);
         if (err != hipSuccess) break;
       }
-      // the first range and the inline ranges: one workgroup per item; the
-      // listed ranges: at most 2048 workgroups (about two rounds of resident
-      // ones), striding over the listed items
-      const long all = (long)L.B * (k1 - k0) * S;
-      const long cap = 2048;
-      const dim3 gridl((unsigned)(!listed || k0 == 0 || all < cap ? all : cap));
+      // one workgroup per item of every sequence (listed ranges: those past
+      // the list return at once)
+      const dim3 gridl((unsigned)((long)L.B * (k1 - k0) * S));
       trace_before(stream, rows_id);
       if (L.bf16) SV_BY_MODE(SV_LEVEL, uint16_t);
       else SV_BY_MODE(SV_LEVEL, float);
