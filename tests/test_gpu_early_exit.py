@@ -102,7 +102,8 @@ def test_ragged_shapes(gpu, dtype, B, K, V):
 
 
 @pytest.mark.parametrize("dtype,B,K,V", [("bf16", 640, 7, 5003), ("f32", 520, 15, 2048),
-                                         ("bf16", 130, 5, 3001)])
+                                         ("bf16", 130, 5, 3001), ("bf16", 130, 63, 300),
+                                         ("f32", 512, 31, 264)])
 def test_gate_kernels(gpu, dtype, B, K, V):
     """Batches large enough for the gate kernels and listed ranges (greedy
     from 128 sequences, sampled and mixed from 512), with the greedy form's
