@@ -180,9 +180,9 @@ def test_trace_ingestion_summarises_per_kernel_and_grid(tmp_path, monkeypatch):
         w = csv.writer(f)
         w.writerow(["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z",
                     "Start_Timestamp", "End_Timestamp"])
+        w.writerow([ROWS_S, 524288, 1, 1, 800000, 850000])   # the same kernel, a smaller batch
         w.writerow([ROWS_S, 2097152, 1, 1, 0, 360000])       # ns
         w.writerow([ROWS_S, 2097152, 1, 1, 400000, 770000])
-        w.writerow([ROWS_S, 524288, 1, 1, 800000, 850000])   # the same kernel, a smaller batch
     (tmp_path / "t" / "source_hash.txt").write_text("other\n")
     with pytest.raises(SystemExit):
         bench.ingest_trace(str(path))
@@ -191,4 +191,4 @@ def test_trace_ingestion_summarises_per_kernel_and_grid(tmp_path, monkeypatch):
     md = (tmp_path / "profiles" / "kernel_trace_fused_b1024.md").read_text()
     assert f"| `{ROWS_S}` | 2097152 | 2 | 365.0 | 360.0 | 370.0 |" in md
     assert f"| `{ROWS_S}` | 524288 | 1 | 50.0 | 50.0 | 50.0 |" in md
-    assert "365.0 µs average over 2 dispatches" in md
+    assert "grid 2097152): 365.0 µs average over 2 dispatches" in md   # the largest grid
