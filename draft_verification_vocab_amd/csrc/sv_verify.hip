@@ -375,7 +375,10 @@ __global__ __launch_bounds__(kThreads) void verify_level_gate(ScanArgs sc, int k
   int a;
   if constexpr (MODE == GREEDY) a = accept_scan<LT, GREEDY>(sc, b, false, 1.f).a;
   else a = draw_scan<LT, MODE, QL>(sc, b, false, false).a;
-  if (lane_id() == 0 && a >= k0) list[atomicAdd(count, 1)] = b;
+  if (lane_id() == 0 && a >= k0) {
+    const int slot = atomicAdd(count, 1);
+    if (slot < sc.B) list[slot] = b;           // always, unless the workspace was left dirty
+  }
 }
 
 // verify_rows_level: the row statistics of one range.  Work item i is
@@ -440,11 +443,11 @@ __global__ __launch_bounds__(kThreads) void verify_rows_level(RowsArgs A, ScanAr
     }
     level_item<LT, MODE, VEC, kThreads>(A, b, k0 + i / S % n, i % S, sm_f, sm_i, sm_d);
   } else {
-    const int items = *count * n * S;          // written by the gate
-    const int i = blockIdx.x;
-    if (i >= items) return;
-    level_item<LT, MODE, VEC, kThreads>(A, list[i / (n * S)], k0 + i / S % n, i % S, sm_f, sm_i,
-                                       sm_d);
+    const int i = blockIdx.x;                  // < B n S: list entry i / (n S) exists
+    if (i >= *count * n * S) return;           // count: written by the gate
+    const int b = list[i / (n * S)];
+    if ((unsigned)b >= (unsigned)sc.B) return; // only a workspace left dirty could hold one
+    level_item<LT, MODE, VEC, kThreads>(A, b, k0 + i / S % n, i % S, sm_f, sm_i, sm_d);
   }
 }
 
